@@ -1,0 +1,52 @@
+"""CPU oracle for the scaled quantized linear -- TEST INFRASTRUCTURE ONLY.
+
+This package is a plain, slow, obviously correct CPU statement of what the
+GPU path computes:
+
+    Y[M,N] = s_a[m] * s_w[n] * (A_q[M,K] . W_q[N,K]^T)      (bf16 output)
+
+plus the dynamic activation quantizer and the offline weight quantizer, for
+the three formats of the pages (FP8_Dynamic, W8A8_INT8, Block_FP8).
+
+Who may use it: only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py``.  The product path (the HIP library and
+its Python binding) never imports, calls or links anything here, and nothing
+here imports the product path: the two share no code.  Only the seeded input
+generator in ``workloads/`` serves both sides.
+
+Sources.  The pages are five web pages about the article "Building a
+High-Performance and Portable vLLM Linear Backend with Helion" (PyTorch blog):
+  * "Summary"  -- the English summary at yuxiaoba.github.io/tech/en/helion-linear/
+  * "Noticias" -- the Spanish rendering "Helion entra al backend lineal de vLLM
+                  y supera a CUTLASS en Hopper" (noticias.mechatronicstore.cl)
+  * "News"     -- "Helion Integration Boosts vLLM Inference Speed" (latestnews.news)
+Each function cites the page and section it follows.  Where the pages are
+silent (the scale formula, rounding modes, layouts, op order) the reading
+taken is stated in the docstring.
+
+Pins.  Every function here is checked in ``tests/test_oracle_*.py`` against
+something other than itself: an independent exact-rational (Fraction)
+implementation on tiny inputs, closed forms, layout one-hot probes, the OCP
+OFP8 specification's E4M3 values, torch's CPU float8 cast, and invariants of
+the method (variant order independence, quantizer bounds).  No function is
+"parity unpinned".
+"""
+
+from .fpbits import (bf16_bits_from_f32, bf16_bits_to_f32, ulp_bf16, f32)
+from .e4m3 import e4m3_encode, e4m3_decode, E4M3_MAX
+from .quant import (FMT_FP8_DYNAMIC, FMT_W8A8_INT8, FMT_BLOCK_FP8, FORMATS,
+                    qmax_of, quantize_act, quantize_weight, dequant_codes)
+from .linear import (contract_exact, contract_abs, epilogue, reference,
+                     tolerance_bound, summation_depth, check_fp8_parity,
+                     contract_split_order, contract_swap_ab,
+                     emulate_fp32_accumulation)
+
+__all__ = [
+    "bf16_bits_from_f32", "bf16_bits_to_f32", "ulp_bf16", "f32",
+    "e4m3_encode", "e4m3_decode", "E4M3_MAX",
+    "FMT_FP8_DYNAMIC", "FMT_W8A8_INT8", "FMT_BLOCK_FP8", "FORMATS",
+    "qmax_of", "quantize_act", "quantize_weight", "dequant_codes",
+    "contract_exact", "contract_abs", "epilogue", "reference",
+    "tolerance_bound", "summation_depth", "check_fp8_parity",
+    "contract_split_order", "contract_swap_ab", "emulate_fp32_accumulation",
+]
