@@ -1,0 +1,261 @@
+"""Decode quantized-linear benchmark on one MI355X.
+
+Metric: µs per GEMM and achieved HBM GB/s (fraction of the 8 TB/s peak) at
+decode token counts M = 1..32.  Workload (default): FP8_Dynamic (OCP E4M3,
+per-token activation / per-channel weight scales) on the dense 8B-class
+projections -- QKV 6144x4096, O 4096x4096, gate_up 24576x4096, down
+4096x12288 -- at M in {1, 2, 4, 8, 16, 24, 32}: 28 linears per step.
+
+One step = the whole hot path for every point: dynamic activation quantizer,
+then the planned GEMM (standard / split-K / swap-AB from the sweep table),
+captured once into hipGraphs and replayed.  Inputs are synthetic and resident
+in HBM before timing.  Every GEMM of a step reads its own copy of the weights
+(at least 1 GiB of copies per shape), so the 256 MB Infinity Cache cannot
+serve them: the measured bandwidth is HBM bandwidth.
+
+Output: one JSON line (see the keys below); per-point kernel timings ride
+along under "per_point".
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "µs/GEMM & achieved HBM GB/s (fraction of peak), M=1–32, fp8/int8 decode shapes"
+
+
+def algorithmic_bytes(fmt, M, N, K):
+    """Bytes the method must move for one GEMM (weights, scales, activations, output)."""
+    if fmt == 2:   # Block_FP8
+        return N * K + 4 * (-(-N // 128)) * (K // 128) + M * K + 4 * M * (K // 128) + 2 * M * N
+    return N * K + 4 * N + M * K + 4 * M + 2 * M * N
+
+
+def quantizer_bytes(fmt, M, K):
+    return 2 * M * K + M * K + (4 * M * (K // 128) if fmt == 2 else 4 * M)
+
+
+def parse_args(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="fp8_dynamic_8b")
+    ap.add_argument("--kernel-reps", type=int, default=30, help="graph replays per point for kernel timing")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget-s", type=float, default=20.0)
+    ap.add_argument("--table", default=None, help="sweep table path (default: the packaged table)")
+    ap.add_argument("--out", default=None, help="also write the JSON line to this file")
+    return ap.parse_args(argv)
+
+
+def main(argv=None):
+    args = parse_args(argv)
+    if args.gpus != 1:
+        print("bench.py: this build measures one GPU only (--gpus %d requested); the linear shards "
+              "column-wise across GPUs with no exchange, so per-GPU work is one GPU's share." % args.gpus,
+              file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import quantized_gemm_decode_amd as ql
+    from workloads import config_by_name, decode_points, make_inputs
+
+    if not os.path.exists(os.path.join(ROOT, "quantized_gemm_decode_amd", "libqlinear.so")):
+        from quantized_gemm_decode_amd import build as b
+        b.build()
+    torch.cuda.set_device(0)
+    n_table = ql.qlinear_table_load(args.table) if args.table else ql.load_default_table()
+
+    wl = config_by_name(args.workload)
+    fmt = wl.fmt
+    points = decode_points(wl)
+    dev = "cuda"
+    stream = torch.cuda.Stream()
+
+    # ------------------------------------------------ inputs, weights, copies
+    shapes = {}
+    for (lab, N, K) in wl.shapes:
+        x, w = make_inputs(K, N, max(wl.ms), wl.sigma_w, seed=wl.seed)
+        wd = w.to(dev)
+        w_q, w_s = ql.quantize_weight(fmt, wd)
+        del wd
+        copies = max(2, -(-(1 << 30) // (N * K)))
+        wq_all = torch.empty((copies,) + tuple(w_q.shape), dtype=w_q.dtype, device=dev)
+        ws_all = torch.empty((copies,) + tuple(w_s.shape), dtype=w_s.dtype, device=dev)
+        wq_all[:] = w_q
+        ws_all[:] = w_s
+        shapes[lab] = dict(N=N, K=K, x=x.to(dev), wq=wq_all, ws=ws_all, copies=copies)
+    torch.cuda.synchronize()
+
+    # ------------------------------------------------ per-point plans and buffers
+    pts = []
+    for (lab, N, K, M) in points:
+        sh = shapes[lab]
+        plan = ql.qlinear_plan(fmt, M, N, K)
+        cfg, facts = plan.info()
+        pts.append(dict(lab=lab, N=N, K=K, M=M, plan=plan, cfg=cfg, facts=facts,
+                        x=sh["x"][:M].contiguous(),
+                        a_q=torch.empty(M, K, dtype=ql.code_dtype(fmt), device=dev),
+                        a_s=torch.empty(ql.act_scale_shape(fmt, M, K), dtype=torch.float32, device=dev),
+                        y=torch.empty(M, N, dtype=torch.bfloat16, device=dev),
+                        wsp=plan.new_workspace(dev),
+                        bytes=algorithmic_bytes(fmt, M, N, K), qbytes=quantizer_bytes(fmt, M, K)))
+
+    # ------------------------------------------------ step graphs (quantize + GEMM per point)
+    n_graphs = 8
+    graphs = []
+    with torch.cuda.stream(stream):
+        for gi in range(n_graphs):
+            ql.qlinear_graph_begin(stream)
+            for pi, p in enumerate(pts):
+                sh = shapes[p["lab"]]
+                c = (gi * len(pts) + pi) % sh["copies"]
+                ql.qlinear_forward(p["plan"], p["x"], p["a_q"], p["a_s"], sh["wq"][c], sh["ws"][c], p["y"],
+                                   p["wsp"], stream=stream)
+            graphs.append(ql.qlinear_graph_end(stream))
+    stream.synchronize()
+
+    for i in range(args.warmup):
+        graphs[i % n_graphs].launch(stream)
+    stream.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    wall0 = time.perf_counter()
+    for i in range(args.steps):
+        graphs[i % n_graphs].launch(stream)
+    t1.record(stream)
+    stream.synchronize()
+    wall = time.perf_counter() - wall0
+    step_ms = t0.elapsed_time(t1) / args.steps
+    step_bytes = sum(p["bytes"] + p["qbytes"] for p in pts)
+    value = step_bytes / (step_ms * 1e-3) / 1e9
+
+    # ------------------------------------------------ per-point GEMM kernel timing (HIP events)
+    reps = args.kernel_reps
+    per_point = []
+    tot_bytes = tot_us = 0.0
+    for p in pts:
+        sh = shapes[p["lab"]]
+        R = min(sh["copies"], 64)
+        with torch.cuda.stream(stream):
+            ql.qlinear_graph_begin(stream)
+            for c in range(R):
+                ql.qlinear_run(p["plan"], p["a_q"], p["a_s"], sh["wq"][c], sh["ws"][c], p["y"], p["wsp"],
+                               stream=stream)
+            g = ql.qlinear_graph_end(stream)
+            ql.qlinear_quantize_act(fmt, p["x"], p["a_q"], p["a_s"], stream=stream)
+        for _ in range(3):
+            g.launch(stream)
+        stream.synchronize()
+        samples = []
+        for _ in range(reps):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            g.launch(stream)
+            e1.record(stream)
+            e1.synchronize()
+            samples.append(e0.elapsed_time(e1) * 1e3 / R)
+        us = float(np.median(samples))
+        gbs = p["bytes"] / (us * 1e-6) / 1e9
+        tot_bytes += p["bytes"]
+        tot_us += us
+        per_point.append(dict(shape=p["lab"], M=p["M"], N=p["N"], K=p["K"], us=round(us, 3),
+                              us_p10=round(float(np.percentile(samples, 10)), 3),
+                              us_p90=round(float(np.percentile(samples, 90)), 3),
+                              GBs=round(gbs, 1), frac=round(gbs / HBM_PEAK_GBS, 4),
+                              variant=("split-k" if p["facts"]["chunks"] > 1 else
+                                       ("swap-ab" if p["cfg"]["swap_ab"] else "standard")),
+                              split=p["facts"]["chunks"], swap_ab=p["cfg"]["swap_ab"],
+                              source=p["facts"]["source"]))
+        del g
+    achieved = tot_bytes / (tot_us * 1e-6) / 1e9
+
+    # ------------------------------------------------ CPU oracle baseline (bounded sample)
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(wl, shapes, args.cpu_budget_s)
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8_e4m3" if fmt != 1 else "int8",
+        "data": "synthetic (seeded N(0,1) activations with 1% x20 outlier channels, N(0,%g) weights)" % wl.sigma_w,
+        "config": {"workload": wl.name, "format": ql.FORMAT_NAMES[fmt],
+                   "shapes": ["%s %dx%d" % s for s in wl.shapes], "token_counts": list(wl.ms),
+                   "gemms_per_step": len(pts), "graph_replay": True, "table_entries": n_table,
+                   "us_per_gemm_step_avg": round(step_ms * 1e3 / len(pts), 3)},
+        "roofline": {"kernel": "qgemm_decode_kernel", "bound": "hbm", "achieved": round(achieved, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": None,
+                     "note": "algorithmic bytes of all %d GEMMs / sum of their per-launch durations "
+                             "(HIP events around graph replays of back-to-back launches)" % len(pts)},
+        "cpu_baseline": cpu,
+        "per_point": per_point,
+        "wall_s": round(wall, 3),
+    }
+    line = json.dumps(out)
+    print(line, flush=True)
+    if args.out:
+        with open(args.out, "w") as f:
+            f.write(line + "\n")
+    return 0
+
+
+def cpu_baseline(wl, shapes, budget_s):
+    """Time the CPU oracle (as it stands) on a bounded sample of the same workload."""
+    import numpy as np
+    import torch
+
+    import oracle
+    from workloads import bf16_bits, make_inputs
+
+    n = len(os.sched_getaffinity(0))
+    torch.set_num_threads(n)
+    fmt = wl.fmt
+    sample = []
+    t_total = 0.0
+    b_total = 0
+    for (lab, N, K) in wl.shapes:
+        x, w = make_inputs(K, N, max(wl.ms), wl.sigma_w, seed=wl.seed)
+        w_q, s_w = oracle.quantize_weight(fmt, bf16_bits(w))          # offline step: not timed
+        for M in (1, max(wl.ms)):
+            xb = bf16_bits(x[:M])
+            t0 = time.perf_counter()
+            a_q, s_a = oracle.quantize_act(fmt, xb)
+            S = oracle.contract_exact(fmt, a_q, w_q)
+            oracle.epilogue(fmt, S, s_a, s_w)
+            dt = time.perf_counter() - t0
+            t_total += dt
+            b_total += algorithmic_bytes(fmt, M, N, K)
+            sample.append("%s M=%d" % (lab, M))
+            if t_total > budget_s:
+                break
+        if t_total > budget_s:
+            break
+    return {"value": round(b_total / t_total / 1e9, 3), "unit": "GB/s", "cores": n, "kind": "oracle",
+            "sample": "%s: activation quantizer + exact fp64 contraction + epilogue on %s (weights "
+                      "pre-quantized, untimed); %.1f s of CPU time" % (wl.name, ", ".join(sample), t_total),
+            "us_per_gemm": round(t_total / len(sample) * 1e6, 1)}
+
+
+if __name__ == "__main__":
+    sys.exit(main())

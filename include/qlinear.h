@@ -1,0 +1,241 @@
+/*
+ * qlinear.h -- C ABI of the MI355X (gfx950) scaled quantized linear.
+ *
+ *   Y[M,N] = s_a[m] * s_w[n] * (A_q[M,K] . W_q[N,K]^T)      bf16 output
+ *
+ * plus the dynamic activation quantizer that produces (A_q, s_a) and the
+ * offline weight quantizer that produces (W_q, s_w).
+ *
+ * Sources.  The operation and its variants are described on five web pages
+ * about the article "Building a High-Performance and Portable vLLM Linear
+ * Backend with Helion" (PyTorch blog).  Cited here as:
+ *   [Summary]  English summary, yuxiaoba.github.io/tech/en/helion-linear/
+ *   [Noticias] "Helion entra al backend lineal de vLLM y supera a CUTLASS en
+ *              Hopper", noticias.mechatronicstore.cl
+ *
+ * Formats ([Summary] "Put algorithm selection inside the search space", last
+ * paragraph; [Noticias] "El backend lineal de Helion / Alcance"):
+ *   QL_FP8_DYNAMIC  OCP E4M3 activations scaled per token, weights per output channel
+ *   QL_W8A8_INT8    int8 activations per token, weights per output channel
+ *   QL_BLOCK_FP8    E4M3 with 1x128 activation groups and 128x128 weight blocks
+ * Quantization rule (the pages give none; the plain reading): symmetric
+ * absmax, s = fl(amax / Q) with Q = 127 (int8) or 448 (E4M3); code =
+ * round-half-even(fl(x / s)) clamped to [-Q, Q]; an all-zero group gets s = 1.
+ *
+ * Data layouts (all row-major, caller-owned device memory):
+ *   X      bf16   [M, K]                 activations (input of the quantizer)
+ *   A_q    1 byte [M, K]                 int8 or E4M3 codes
+ *   s_a    fp32   [M]  or [M, K/128]     (Block_FP8: one scale per 1x128 group)
+ *   W      bf16   [N, K]                 weights (input of the weight quantizer)
+ *   W_q    1 byte [N, K]                 row n = output channel n, K contiguous
+ *   s_w    fp32   [N]  or [ceil(N/128), K/128]
+ *   Y      bf16   [M, N]
+ *
+ * Argument rules checked on the host before any launch (QL_E_INVALID /
+ * QL_E_ALIGN / QL_E_UNSUPPORTED otherwise):
+ *   M, N, K >= 0; K % 16 == 0 (rows are 16-byte aligned); Block_FP8 needs
+ *   K % 128 == 0; N * K and M * K at most 2^30; device pointers 16-byte
+ *   aligned and non-null whenever the sizes make them used.
+ *   M == 0 or N == 0 is a successful no-op.  K == 0 gives Y == 0.
+ *
+ * Streams: every `stream` argument is a hipStream_t passed as void* (NULL =
+ * the default stream).  Calls only enqueue work: no synchronisation, no
+ * device allocation, no memset nodes, so sequences of calls can be captured
+ * into a hipGraph (see qlinear_graph_begin).
+ *
+ * Errors: every call returns a ql_status; nothing throws or aborts across the
+ * ABI.  qlinear_last_error() returns a thread-local description of the last
+ * failure.  A failing HIP launch is reported as QL_E_HIP.
+ *
+ * Threading: plans are immutable after creation and may be shared between
+ * threads and streams; concurrent runs of split-K plans need distinct
+ * workspaces.  The sweep table is process-global; load it before creating
+ * plans from several threads.
+ */
+#ifndef QLINEAR_H
+#define QLINEAR_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  QL_FP8_DYNAMIC = 0,
+  QL_W8A8_INT8 = 1,
+  QL_BLOCK_FP8 = 2
+} ql_format;
+
+typedef enum {
+  QL_OK = 0,
+  QL_E_INVALID = 1,        /* bad size, format, null pointer or config */
+  QL_E_UNSUPPORTED = 2,    /* valid request this build does not serve */
+  QL_E_NO_TABLE_ENTRY = 3, /* qlinear_plan_from_table: no sweep-table entry */
+  QL_E_HIP = 4,            /* a HIP runtime call or kernel launch failed */
+  QL_E_ALIGN = 5,          /* pointer not 16-byte aligned */
+  QL_E_TABLE = 6           /* sweep table file unreadable or malformed */
+} ql_status;
+
+/* Algorithm family of a plan. */
+typedef enum {
+  QL_ALGO_DECODE = 0, /* weight-streaming kernel for M <= 32 (decode token counts) */
+  QL_ALGO_TILED = 1   /* LDS-tiled matrix-core GEMM for larger M */
+} ql_algo;
+
+/* Where a plan's configuration came from. */
+typedef enum {
+  QL_SRC_TABLE = 0,     /* the offline sweep table */
+  QL_SRC_HEURISTIC = 1, /* built-in rule (no table entry) */
+  QL_SRC_CUSTOM = 2     /* qlinear_plan_with_config or QLINEAR_FORCE */
+} ql_source;
+
+/*
+ * Tunable configuration of one GEMM launch.  The two algorithmic choices of
+ * the pages are `split_k` (powers of two 1..256) and `swap_ab` (boolean)
+ * ([Summary] "Put algorithm selection inside the search space"; [Noticias]
+ * "¿Cómo se implementa el kernel?"); the rest are the low-level tile
+ * parameters searched alongside them.
+ *   Standard GEMM = split_k 1, swap_ab 0; Split-K = split_k > 1;
+ *   Swap-AB = swap_ab 1 (the weights become the matrix core's first operand).
+ */
+typedef struct {
+  int32_t algo;          /* ql_algo */
+  int32_t swap_ab;       /* 0 or 1 */
+  int32_t split_k;       /* 1,2,4,...,256; clamped to the number of 128-wide K blocks */
+  int32_t waves_n;       /* DECODE: waves of a workgroup side by side along N */
+  int32_t waves_k;       /* DECODE: waves of a workgroup sharing its K chunk */
+  int32_t rows_per_wave; /* DECODE: 16 or 32 weight rows per wave */
+  int32_t prefetch;      /* DECODE: 128-wide K blocks per wave kept in flight (2 or 4) */
+  int32_t a_lds;         /* DECODE: 1 = stage the activation chunk in LDS, 0 = read it per K block */
+  int32_t tile_m;        /* TILED: workgroup tile rows (M) */
+  int32_t tile_n;        /* TILED: workgroup tile columns (N) */
+} ql_config;
+
+/* Derived launch facts of a plan (read-only). */
+typedef struct {
+  int32_t source;          /* ql_source */
+  int32_t chunks;          /* effective number of K chunks */
+  int32_t chunk_k;         /* K elements per chunk (last chunk may be shorter) */
+  int32_t workgroups;      /* grid size */
+  int32_t threads;         /* threads per workgroup */
+  int32_t lds_bytes;       /* dynamic LDS per workgroup */
+  int64_t workspace_bytes; /* see qlinear_workspace_bytes */
+} ql_plan_facts;
+
+typedef struct ql_plan_s* ql_plan;
+typedef struct ql_graph_s* ql_graph;
+
+/* Library version (major*10000 + minor*100 + patch). */
+int32_t qlinear_version(void);
+/* Static string naming a status code; never NULL. */
+const char* qlinear_status_string(int32_t status);
+/* Thread-local description of the last failure on this thread ("" if none). */
+const char* qlinear_last_error(void);
+
+/*
+ * Dynamic activation quantizer ([Summary] last paragraph of "Put algorithm
+ * selection inside the search space": per-token or 1x128 activation scaling).
+ *   x_bf16  [M, K] bf16 in;  a_q [M, K] codes out;  a_scale fp32 [M] or [M, K/128] out.
+ * Bit-exact contract: amax exact in fp32, IEEE division, round-half-even,
+ * clamp, E4M3 round-to-nearest-even, fp32 subnormals kept.
+ */
+ql_status qlinear_quantize_act(int32_t fmt, const void* x_bf16, int64_t M, int64_t K,
+                               void* a_q, float* a_scale, void* stream);
+
+/*
+ * Offline weight quantizer: per output channel (rows of W) or per 128x128
+ * block for Block_FP8 (the last block row may be ragged).
+ *   w_bf16 [N, K] in;  w_q [N, K] out;  w_scale fp32 [N] or [ceil(N/128), K/128] out.
+ * Same rounding contract as the activation quantizer.
+ */
+ql_status qlinear_quantize_weight(int32_t fmt, const void* w_bf16, int64_t N, int64_t K,
+                                  void* w_q, float* w_scale, void* stream);
+
+/*
+ * Offline sweep table ([Summary] "Hybrid dispatch addresses runtime
+ * overhead": per-shape, per-token-count tuned configurations).  Text file,
+ * one entry per line: fmt M N K algo swap_ab split_k waves_n waves_k
+ * rows_per_wave prefetch a_lds tile_m tile_n [time_us]; '#' starts a comment.
+ * Loading replaces the in-process table.  Returns the entry count via n_entries.
+ */
+ql_status qlinear_table_load(const char* path, int64_t* n_entries);
+void qlinear_table_clear(void);
+
+/*
+ * Plan one GEMM shape.  Looks up the sweep table with M rounded up to the
+ * next tuned token bucket {1,2,4,8,16,24,32} (M > 32: the nearest tuned M at
+ * or above, else the largest); without an entry a built-in heuristic is used
+ * (facts.source tells which).  The environment variable QLINEAR_FORCE =
+ * "algo,swap,split,wn,wk,rows,prefetch,alds,tile_m,tile_n" overrides both.
+ * Host-only: no device call is made.
+ */
+ql_status qlinear_plan(int32_t fmt, int64_t M, int64_t N, int64_t K, ql_plan* out_plan);
+/* Like qlinear_plan but only from the table; QL_E_NO_TABLE_ENTRY when absent. */
+ql_status qlinear_plan_from_table(int32_t fmt, int64_t M, int64_t N, int64_t K, ql_plan* out_plan);
+/* Plan with an explicit configuration (validated; QL_E_INVALID / QL_E_UNSUPPORTED on a bad one). */
+ql_status qlinear_plan_with_config(int32_t fmt, int64_t M, int64_t N, int64_t K,
+                                   const ql_config* cfg, ql_plan* out_plan);
+/* Effective configuration and launch facts of a plan (either pointer may be NULL). */
+ql_status qlinear_plan_info(ql_plan plan, ql_config* cfg, ql_plan_facts* facts);
+/*
+ * Bytes of device workspace a run needs (0 for split_k == 1).  Split-K plans
+ * accumulate partial sums (int32 for INT8, fp32 for FP8) plus one arrival
+ * counter per output tile.  The caller allocates it and zeroes it ONCE; every
+ * run leaves it all-zero again (the last-arriving workgroup of a tile clears
+ * its part), so it can be reused by later runs and graph replays.
+ */
+int64_t qlinear_workspace_bytes(ql_plan plan);
+void qlinear_plan_destroy(ql_plan plan);
+
+/*
+ * The scaled quantized GEMM: Y = epilogue(A_q . W_q^T) with the scales fused
+ * into the epilogue ([Summary] "Put algorithm selection inside the search
+ * space": split-K combines partial results; quantized variants add scaling).
+ * Epilogue op order (fixed): INT8 y = bf16(fl(fl(f32(acc) * s_a[m]) * s_w[n]))
+ * with an exact int32 accumulator; FP8_Dynamic the same on the fp32
+ * accumulator; Block_FP8 applies s_a[m,g] * s_w[n/128,g] to every 128-wide K
+ * group's partial inside the K loop and rounds the fp32 sum to bf16.
+ * Enqueue-only; workspace may be NULL when qlinear_workspace_bytes is 0.
+ */
+ql_status qlinear_run(ql_plan plan, const void* a_q, const float* a_scale,
+                      const void* w_q, const float* w_scale, void* y_bf16,
+                      void* workspace, void* stream);
+
+/*
+ * Test hook: same launch as qlinear_run, and additionally stores the raw
+ * accumulator per output element into acc_out [M, N] (int32 for INT8, fp32
+ * for FP8_Dynamic, the scaled fp32 sum for Block_FP8) before the bf16 rounding.
+ */
+ql_status qlinear_run_debug_acc(ql_plan plan, const void* a_q, const float* a_scale,
+                                const void* w_q, const float* w_scale, void* y_bf16,
+                                void* workspace, void* acc_out, void* stream);
+
+/*
+ * Quantize the activations, then run the GEMM: the whole decode step of one
+ * linear layer.  a_q / a_scale are caller-owned staging buffers.
+ */
+ql_status qlinear_forward(ql_plan plan, const void* x_bf16, void* a_q, float* a_scale,
+                          const void* w_q, const float* w_scale, void* y_bf16,
+                          void* workspace, void* stream);
+
+/*
+ * hipGraph dispatch for the small-M path ([Summary] "Hybrid dispatch
+ * addresses runtime overhead": the tuned kernels run only under graph
+ * replay, which removes the host launch cost).  qlinear_graph_begin starts
+ * capturing `stream` (thread-local capture mode; `stream` must not be the
+ * default stream); every qlinear_* call enqueued on it until
+ * qlinear_graph_end is recorded into one executable graph.  The graph binds
+ * the pointers given at capture time.  Replays are stream-ordered.
+ */
+ql_status qlinear_graph_begin(void* stream);
+ql_status qlinear_graph_end(void* stream, ql_graph* out_graph);
+ql_status qlinear_graph_launch(ql_graph graph, void* stream);
+void qlinear_graph_destroy(ql_graph graph);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QLINEAR_H */

@@ -1,0 +1,266 @@
+"""MI355X-native scaled quantized linear for LLM decode.
+
+    Y[M, N] = s_a[m] * s_w[n] * (A_q[M, K] . W_q[N, K]^T)     (bf16 out)
+
+Formats: FP8_Dynamic (OCP E4M3, per-token / per-channel), W8A8_INT8
+(per-token / per-channel) and Block_FP8 (1x128 activation groups, 128x128
+weight blocks).  All arithmetic runs in the hand-written gfx950 HIP kernels
+of ``libqlinear.so`` behind the C ABI of ``include/qlinear.h``; this module
+only marshals torch tensors (device memory) and streams into that ABI, with
+the same function names.  There is no CPU or PyTorch fallback: if the
+library is missing, or a tensor is not on the GPU, calls raise.
+"""
+
+import ctypes
+import os
+
+import torch
+
+from . import _lib
+from ._lib import QLConfig, QLPlanFacts
+
+FP8_DYNAMIC, W8A8_INT8, BLOCK_FP8 = 0, 1, 2
+FORMATS = (FP8_DYNAMIC, W8A8_INT8, BLOCK_FP8)
+FORMAT_NAMES = {FP8_DYNAMIC: "FP8_Dynamic", W8A8_INT8: "W8A8_INT8", BLOCK_FP8: "Block_FP8"}
+ALGO_DECODE, ALGO_TILED = 0, 1
+SOURCES = {0: "table", 1: "heuristic", 2: "custom"}
+DEFAULT_TABLE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "tables", "decode_table.txt")
+CONFIG_FIELDS = [f for f, _ in QLConfig._fields_]
+
+
+class QLinearError(RuntimeError):
+    def __init__(self, status, where):
+        lib = _lib.load()
+        self.status = status
+        msg = lib.qlinear_last_error().decode()
+        super().__init__("%s failed: %s (%s)" % (where, lib.qlinear_status_string(status).decode(), msg))
+
+
+def lib():
+    return _lib.load()
+
+
+def _check(status, where):
+    if status != 0:
+        raise QLinearError(status, where)
+
+
+def _stream(stream):
+    if stream is None:
+        return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    if isinstance(stream, torch.cuda.Stream):
+        return ctypes.c_void_p(stream.cuda_stream)
+    return ctypes.c_void_p(int(stream))
+
+
+def _ptr(t, name, dtype=None, required=True):
+    if t is None:
+        if required:
+            raise ValueError("%s is required" % name)
+        return None
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise ValueError("%s must be a CUDA (HIP) tensor" % name)
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if dtype is not None and t.dtype not in (dtype if isinstance(dtype, tuple) else (dtype,)):
+        raise ValueError("%s has dtype %s, expected %s" % (name, t.dtype, dtype))
+    return ctypes.c_void_p(t.data_ptr())
+
+
+CODE_DTYPES = (torch.int8, torch.uint8, torch.float8_e4m3fn)
+
+
+# ----------------------------------------------------------------- shapes
+
+def act_scale_shape(fmt, M, K):
+    return (M, K // 128) if fmt == BLOCK_FP8 else (M,)
+
+
+def weight_scale_shape(fmt, N, K):
+    return (-(-N // 128), K // 128) if fmt == BLOCK_FP8 else (N,)
+
+
+def code_dtype(fmt):
+    return torch.int8 if fmt == W8A8_INT8 else torch.float8_e4m3fn
+
+
+# ----------------------------------------------------------------- quantizers
+
+def qlinear_quantize_act(fmt, x, a_q, a_scale, stream=None):
+    M, K = x.shape
+    _check(lib().qlinear_quantize_act(fmt, _ptr(x, "x", torch.bfloat16), M, K, _ptr(a_q, "a_q", CODE_DTYPES),
+                                      _ptr(a_scale, "a_scale", torch.float32), _stream(stream)),
+           "qlinear_quantize_act")
+
+
+def qlinear_quantize_weight(fmt, w, w_q, w_scale, stream=None):
+    N, K = w.shape
+    _check(lib().qlinear_quantize_weight(fmt, _ptr(w, "w", torch.bfloat16), N, K, _ptr(w_q, "w_q", CODE_DTYPES),
+                                         _ptr(w_scale, "w_scale", torch.float32), _stream(stream)),
+           "qlinear_quantize_weight")
+
+
+def quantize_act(fmt, x, stream=None):
+    """Allocate (A_q, s_a) and run the activation quantizer."""
+    M, K = x.shape
+    a_q = torch.empty(M, K, dtype=code_dtype(fmt), device=x.device)
+    a_s = torch.empty(act_scale_shape(fmt, M, K), dtype=torch.float32, device=x.device)
+    qlinear_quantize_act(fmt, x, a_q, a_s, stream)
+    return a_q, a_s
+
+
+def quantize_weight(fmt, w, stream=None):
+    """Allocate (W_q, s_w) and run the weight quantizer."""
+    N, K = w.shape
+    w_q = torch.empty(N, K, dtype=code_dtype(fmt), device=w.device)
+    w_s = torch.empty(weight_scale_shape(fmt, N, K), dtype=torch.float32, device=w.device)
+    qlinear_quantize_weight(fmt, w, w_q, w_s, stream)
+    return w_q, w_s
+
+
+# ----------------------------------------------------------------- table
+
+def qlinear_table_load(path=DEFAULT_TABLE):
+    n = ctypes.c_int64(0)
+    _check(lib().qlinear_table_load(path.encode(), ctypes.byref(n)), "qlinear_table_load")
+    return n.value
+
+
+def qlinear_table_clear():
+    lib().qlinear_table_clear()
+
+
+# ----------------------------------------------------------------- plans
+
+class Plan:
+    """Owner of a ql_plan handle (host object)."""
+
+    def __init__(self, handle, fmt, M, N, K):
+        self.handle = ctypes.c_void_p(handle)
+        self.fmt, self.M, self.N, self.K = fmt, M, N, K
+
+    def __del__(self):
+        h = getattr(self, "handle", None)
+        if h is not None and h.value and _lib._lib is not None:
+            _lib._lib.qlinear_plan_destroy(h)
+            self.handle = None
+
+    def info(self):
+        cfg, facts = QLConfig(), QLPlanFacts()
+        _check(lib().qlinear_plan_info(self.handle, ctypes.byref(cfg), ctypes.byref(facts)), "qlinear_plan_info")
+        c = {f: getattr(cfg, f) for f in CONFIG_FIELDS}
+        f = {n: getattr(facts, n) for n, _ in QLPlanFacts._fields_}
+        f["source"] = SOURCES.get(f["source"], f["source"])
+        return c, f
+
+    @property
+    def config(self):
+        return self.info()[0]
+
+    @property
+    def facts(self):
+        return self.info()[1]
+
+    @property
+    def workspace_bytes(self):
+        return int(lib().qlinear_workspace_bytes(self.handle))
+
+    def new_workspace(self, device="cuda"):
+        """Zero-initialised workspace (zeroed once; runs keep it all-zero)."""
+        n = self.workspace_bytes
+        return torch.zeros(max(n, 16), dtype=torch.uint8, device=device) if n else None
+
+
+def qlinear_plan(fmt, M, N, K):
+    h = ctypes.c_void_p()
+    _check(lib().qlinear_plan(fmt, M, N, K, ctypes.byref(h)), "qlinear_plan")
+    return Plan(h.value, fmt, M, N, K)
+
+
+def qlinear_plan_from_table(fmt, M, N, K):
+    h = ctypes.c_void_p()
+    _check(lib().qlinear_plan_from_table(fmt, M, N, K, ctypes.byref(h)), "qlinear_plan_from_table")
+    return Plan(h.value, fmt, M, N, K)
+
+
+def make_config(**kw):
+    base = dict(algo=ALGO_DECODE, swap_ab=0, split_k=1, waves_n=4, waves_k=1, rows_per_wave=16, prefetch=2,
+                a_lds=1, tile_m=0, tile_n=0)
+    unknown = set(kw) - set(base)
+    if unknown:
+        raise ValueError("unknown config fields %s" % sorted(unknown))
+    base.update(kw)
+    return base
+
+
+def qlinear_plan_with_config(fmt, M, N, K, cfg):
+    c = QLConfig(**make_config(**cfg))
+    h = ctypes.c_void_p()
+    _check(lib().qlinear_plan_with_config(fmt, M, N, K, ctypes.byref(c), ctypes.byref(h)),
+           "qlinear_plan_with_config")
+    return Plan(h.value, fmt, M, N, K)
+
+
+# ----------------------------------------------------------------- GEMM
+
+def qlinear_run(plan, a_q, a_scale, w_q, w_scale, y, workspace=None, stream=None):
+    _check(lib().qlinear_run(plan.handle, _ptr(a_q, "a_q", CODE_DTYPES), _ptr(a_scale, "a_scale", torch.float32),
+                             _ptr(w_q, "w_q", CODE_DTYPES), _ptr(w_scale, "w_scale", torch.float32),
+                             _ptr(y, "y", torch.bfloat16), _ptr(workspace, "workspace", required=False),
+                             _stream(stream)), "qlinear_run")
+
+
+def qlinear_run_debug_acc(plan, a_q, a_scale, w_q, w_scale, y, acc_out, workspace=None, stream=None):
+    _check(lib().qlinear_run_debug_acc(plan.handle, _ptr(a_q, "a_q", CODE_DTYPES),
+                                       _ptr(a_scale, "a_scale", torch.float32), _ptr(w_q, "w_q", CODE_DTYPES),
+                                       _ptr(w_scale, "w_scale", torch.float32), _ptr(y, "y", torch.bfloat16),
+                                       _ptr(workspace, "workspace", required=False),
+                                       _ptr(acc_out, "acc_out", (torch.int32, torch.float32)), _stream(stream)),
+           "qlinear_run_debug_acc")
+
+
+def qlinear_forward(plan, x, a_q, a_scale, w_q, w_scale, y, workspace=None, stream=None):
+    _check(lib().qlinear_forward(plan.handle, _ptr(x, "x", torch.bfloat16), _ptr(a_q, "a_q", CODE_DTYPES),
+                                 _ptr(a_scale, "a_scale", torch.float32), _ptr(w_q, "w_q", CODE_DTYPES),
+                                 _ptr(w_scale, "w_scale", torch.float32), _ptr(y, "y", torch.bfloat16),
+                                 _ptr(workspace, "workspace", required=False), _stream(stream)),
+           "qlinear_forward")
+
+
+# ----------------------------------------------------------------- graphs
+
+class Graph:
+    """Owner of a ql_graph (an instantiated hipGraph)."""
+
+    def __init__(self, handle):
+        self.handle = ctypes.c_void_p(handle)
+
+    def launch(self, stream=None):
+        qlinear_graph_launch(self, stream)
+
+    def __del__(self):
+        h = getattr(self, "handle", None)
+        if h is not None and h.value and _lib._lib is not None:
+            _lib._lib.qlinear_graph_destroy(h)
+            self.handle = None
+
+
+def qlinear_graph_begin(stream):
+    _check(lib().qlinear_graph_begin(_stream(stream)), "qlinear_graph_begin")
+
+
+def qlinear_graph_end(stream):
+    h = ctypes.c_void_p()
+    _check(lib().qlinear_graph_end(_stream(stream), ctypes.byref(h)), "qlinear_graph_end")
+    return Graph(h.value)
+
+
+def qlinear_graph_launch(graph, stream=None):
+    _check(lib().qlinear_graph_launch(graph.handle, _stream(stream)), "qlinear_graph_launch")
+
+
+def load_default_table():
+    """Load the sweep table shipped with the package (returns its entry count, 0 if absent)."""
+    if os.path.exists(DEFAULT_TABLE):
+        return qlinear_table_load(DEFAULT_TABLE)
+    return 0

@@ -1,0 +1,444 @@
+// C ABI of the quantized linear: argument validation, planning (sweep table,
+// heuristic, explicit configs), launches and hipGraph capture helpers.
+//
+// Planning follows the pages' split between an offline per-shape search and
+// a cheap runtime lookup ([Summary] "Hybrid dispatch addresses runtime
+// overhead": token counts 1, 2, 4, 8, 16, 24, 32 tuned per GEMM shape, graph
+// replay for num_tokens <= 32).  Plans are host objects; nothing here
+// allocates device memory or synchronises.
+//
+// [Summary] = English summary of "Building a High-Performance and Portable
+// vLLM Linear Backend with Helion" (yuxiaoba.github.io).
+#include "../../include/qlinear.h"
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <fstream>
+#include <mutex>
+#include <sstream>
+#include <string>
+#include <vector>
+
+#include "decode_args.hpp"
+
+namespace {
+
+thread_local std::string g_err;
+
+ql_status fail(ql_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return st;
+}
+
+ql_status hip_fail(hipError_t e, const char* what) {
+  return fail(QL_E_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+constexpr int kNW = 4;                       // waves per decode workgroup
+constexpr int64_t kLdsLimit = 64 * 1024;     // dynamic LDS budget per workgroup
+constexpr int kBuckets[] = {1, 2, 4, 8, 16, 24, 32};
+
+bool valid_fmt(int32_t f) { return f == QL_FP8_DYNAMIC || f == QL_W8A8_INT8 || f == QL_BLOCK_FP8; }
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool is_pow2(int64_t v) { return v > 0 && (v & (v - 1)) == 0; }
+int kernel_fmt(int32_t f) { return f == QL_W8A8_INT8 ? qlk::FMT_INT8 : (f == QL_BLOCK_FP8 ? qlk::FMT_BLOCK : qlk::FMT_FP8); }
+
+ql_status check_sizes(int32_t fmt, int64_t R, int64_t K, const char* rname) {
+  if (!valid_fmt(fmt)) return fail(QL_E_INVALID, "unknown format %d", fmt);
+  if (R < 0 || K < 0) return fail(QL_E_INVALID, "negative size (%s=%lld, K=%lld)", rname, (long long)R, (long long)K);
+  if (K % 16) return fail(QL_E_INVALID, "K=%lld is not a multiple of 16", (long long)K);
+  if (fmt == QL_BLOCK_FP8 && K % 128) return fail(QL_E_INVALID, "Block_FP8 needs K %% 128 == 0 (K=%lld)", (long long)K);
+  if (R * K > (int64_t(1) << 30)) return fail(QL_E_UNSUPPORTED, "%s*K=%lld exceeds 2^30", rname, (long long)(R * K));
+  return QL_OK;
+}
+
+// ------------------------------------------------------------------ table
+
+struct TableEntry {
+  int32_t fmt;
+  int64_t M, N, K;
+  ql_config cfg;
+  double us;
+};
+
+std::mutex g_table_mu;
+std::vector<TableEntry> g_table;
+
+int64_t bucket_of(int64_t M) {
+  for (int b : kBuckets)
+    if (M <= b) return b;
+  return M;
+}
+
+bool table_lookup(int32_t fmt, int64_t M, int64_t N, int64_t K, ql_config* out) {
+  std::lock_guard<std::mutex> lk(g_table_mu);
+  const int64_t want = bucket_of(M);
+  const TableEntry* best = nullptr;
+  const TableEntry* largest = nullptr;
+  for (const TableEntry& e : g_table) {
+    if (e.fmt != fmt || e.N != N || e.K != K) continue;
+    if (e.M >= want && (!best || e.M < best->M)) best = &e;
+    if (!largest || e.M > largest->M) largest = &e;
+  }
+  if (!best && M > 32) best = largest;  // beyond every tuned M: the largest tuned one
+  if (!best) return false;
+  if ((M <= 32) != (best->M <= 32)) return false;  // never mix the decode and tiled regimes
+  *out = best->cfg;
+  return true;
+}
+
+}  // namespace
+
+// ------------------------------------------------------------------ plan object
+
+struct ql_plan_s {
+  int32_t fmt;
+  int64_t M, N, K;
+  ql_config cfg;
+  int32_t source;
+  // derived
+  int G, chunk_kb, chunks, mt, n_tiles, bn;
+  int64_t lds, ws_bytes, ws_acc_bytes;
+  qlk::DecodeKey key;
+};
+
+struct ql_graph_s {
+  hipGraph_t graph;
+  hipGraphExec_t exec;
+};
+
+namespace {
+
+ql_config heuristic_config(int32_t fmt, int64_t M, int64_t N, int64_t K) {
+  ql_config c{};
+  c.algo = QL_ALGO_DECODE;
+  c.swap_ab = 1;
+  c.waves_n = 4;
+  c.waves_k = 1;
+  c.rows_per_wave = 16;
+  c.prefetch = 2;
+  const int64_t G = (K + 127) / 128;
+  const int64_t bn = 64;
+  const int64_t tiles = (N + bn - 1) / bn;
+  int64_t split = 1;
+  while (tiles * split < 1024 && split * 2 <= 256 && (G + split * 2 - 1) / (split * 2) >= 2) split *= 2;
+  c.split_k = (int32_t)split;
+  const int64_t chunk_kb = (G + split - 1) / split;
+  const int64_t mt = M <= 16 ? 1 : 2;
+  c.a_lds = chunk_kb * mt * 2048 <= kLdsLimit ? 1 : 0;
+  (void)fmt;
+  return c;
+}
+
+ql_status build_plan(int32_t fmt, int64_t M, int64_t N, int64_t K, const ql_config& cfg, int32_t source,
+                     ql_plan* out) {
+  if (!out) return fail(QL_E_INVALID, "out_plan is NULL");
+  *out = nullptr;
+  ql_status st = check_sizes(fmt, M, K, "M");
+  if (st != QL_OK) return st;
+  if ((st = check_sizes(fmt, N, K, "N")) != QL_OK) return st;
+  if (M * N >= (int64_t(1) << 31)) return fail(QL_E_UNSUPPORTED, "M*N exceeds 2^31");
+  if (cfg.algo != QL_ALGO_DECODE)
+    return fail(QL_E_UNSUPPORTED, "algo %d is not available in this build", cfg.algo);
+  if (M > 32) return fail(QL_E_UNSUPPORTED, "the decode algorithm serves M <= 32 (M=%lld)", (long long)M);
+  if (cfg.swap_ab != 0 && cfg.swap_ab != 1) return fail(QL_E_INVALID, "swap_ab must be 0 or 1");
+  if (!is_pow2(cfg.split_k) || cfg.split_k > 256) return fail(QL_E_INVALID, "split_k must be a power of two in [1, 256]");
+  if (cfg.waves_k < 1 || cfg.waves_n < 1 || cfg.waves_n * cfg.waves_k != kNW)
+    return fail(QL_E_INVALID, "waves_n * waves_k must equal %d", kNW);
+  if (cfg.rows_per_wave != 16 && cfg.rows_per_wave != 32) return fail(QL_E_INVALID, "rows_per_wave must be 16 or 32");
+  if (cfg.prefetch != 2 && cfg.prefetch != 4) return fail(QL_E_INVALID, "prefetch must be 2 or 4");
+  if (cfg.a_lds != 0 && cfg.a_lds != 1) return fail(QL_E_INVALID, "a_lds must be 0 or 1");
+
+  ql_plan_s* p = new ql_plan_s();
+  p->fmt = fmt;
+  p->M = M;
+  p->N = N;
+  p->K = K;
+  p->cfg = cfg;
+  p->source = source;
+  p->G = (int)((K + 127) / 128);
+  const int split = std::max(1, std::min<int>(cfg.split_k, std::max(1, p->G)));
+  p->chunk_kb = p->G > 0 ? (p->G + split - 1) / split : 0;
+  p->chunks = p->G > 0 ? (p->G + p->chunk_kb - 1) / p->chunk_kb : 1;
+  p->mt = M <= 16 ? 1 : 2;
+  const int rg = cfg.rows_per_wave / 16;
+  p->bn = cfg.waves_n * rg * 16;
+  p->n_tiles = (int)((N + p->bn - 1) / p->bn);
+  const int64_t lds_a = cfg.a_lds ? (int64_t)p->chunk_kb * p->mt * 2048 : 0;
+  const int64_t lds_red = cfg.waves_k > 1 ? (int64_t)kNW * rg * p->mt * 1024 : 0;
+  p->lds = std::max(lds_a, lds_red);
+  if (p->lds > kLdsLimit) {
+    delete p;
+    return fail(QL_E_UNSUPPORTED, "config needs %lld bytes of LDS (limit %lld); use a_lds=0 or a larger split_k",
+                (long long)std::max(lds_a, lds_red), (long long)kLdsLimit);
+  }
+  p->ws_acc_bytes = p->chunks > 1 ? ((M * N * 4 + 255) / 256) * 256 : 0;
+  p->ws_bytes = p->chunks > 1 ? p->ws_acc_bytes + (int64_t)p->n_tiles * 4 : 0;
+  p->key = qlk::DecodeKey{kernel_fmt(fmt), cfg.swap_ab, p->mt, rg, kNW, cfg.prefetch, cfg.a_lds};
+  qlk::DecodeArgs dummy{};
+  hipError_t pe;
+  switch (p->key.fmt) {
+    case qlk::FMT_INT8: pe = qlk::decode_dispatch_int8(p->key, dim3(1), dim3(1), 0, nullptr, dummy, true); break;
+    case qlk::FMT_BLOCK: pe = qlk::decode_dispatch_block(p->key, dim3(1), dim3(1), 0, nullptr, dummy, true); break;
+    default: pe = qlk::decode_dispatch_fp8(p->key, dim3(1), dim3(1), 0, nullptr, dummy, true); break;
+  }
+  if (pe != hipSuccess) {
+    delete p;
+    return fail(QL_E_UNSUPPORTED, "no kernel instantiated for this configuration");
+  }
+  *out = p;
+  return QL_OK;
+}
+
+bool parse_force(ql_config* c) {
+  const char* s = std::getenv("QLINEAR_FORCE");
+  if (!s || !*s) return false;
+  int v[10];
+  if (std::sscanf(s, "%d,%d,%d,%d,%d,%d,%d,%d,%d,%d", &v[0], &v[1], &v[2], &v[3], &v[4], &v[5], &v[6], &v[7],
+                  &v[8], &v[9]) != 10)
+    return false;
+  *c = ql_config{v[0], v[1], v[2], v[3], v[4], v[5], v[6], v[7], v[8], v[9]};
+  return true;
+}
+
+ql_status launch_gemm(const ql_plan_s* p, const void* a_q, const float* a_scale, const void* w_q,
+                      const float* w_scale, void* y, void* workspace, void* acc_out, hipStream_t s) {
+  if (p->M == 0 || p->N == 0) return QL_OK;
+  if (!y) return fail(QL_E_INVALID, "y is NULL");
+  if (!aligned16(y)) return fail(QL_E_ALIGN, "y is not 16-byte aligned");
+  if (p->K == 0) {
+    hipError_t e = qlk::launch_fill_zero_bf16(y, p->M * p->N, s);
+    return e == hipSuccess ? QL_OK : hip_fail(e, "zero fill");
+  }
+  if (!a_q || !a_scale || !w_q || !w_scale) return fail(QL_E_INVALID, "NULL operand pointer");
+  if (!aligned16(a_q) || !aligned16(w_q) || !aligned16(a_scale) || !aligned16(w_scale))
+    return fail(QL_E_ALIGN, "operand pointers must be 16-byte aligned");
+  if (p->ws_bytes > 0 && !workspace) return fail(QL_E_INVALID, "split-K plan needs a workspace");
+  if (workspace && !aligned16(workspace)) return fail(QL_E_ALIGN, "workspace is not 16-byte aligned");
+  if (acc_out && !aligned16(acc_out)) return fail(QL_E_ALIGN, "acc_out is not 16-byte aligned");
+
+  qlk::DecodeArgs a{};
+  a.a = static_cast<const uint8_t*>(a_q);
+  a.sa = a_scale;
+  a.w = static_cast<const uint8_t*>(w_q);
+  a.sw = w_scale;
+  a.y = static_cast<uint16_t*>(y);
+  a.ws = workspace;
+  a.counters = p->ws_bytes > 0
+                   ? reinterpret_cast<unsigned*>(static_cast<char*>(workspace) + p->ws_acc_bytes)
+                   : nullptr;
+  a.acc_out = acc_out;
+  a.M = (int)p->M;
+  a.N = (int)p->N;
+  a.K = (int)p->K;
+  a.G = p->G;
+  a.split = p->chunks;
+  a.chunk_kb = p->chunk_kb;
+  a.waves_k = p->cfg.waves_k;
+  a.n_tiles = p->n_tiles;
+  const dim3 grid((unsigned)(p->n_tiles * p->chunks)), block(kNW * 64);
+  hipError_t e;
+  switch (p->key.fmt) {
+    case qlk::FMT_INT8: e = qlk::decode_dispatch_int8(p->key, grid, block, (size_t)p->lds, s, a, false); break;
+    case qlk::FMT_BLOCK: e = qlk::decode_dispatch_block(p->key, grid, block, (size_t)p->lds, s, a, false); break;
+    default: e = qlk::decode_dispatch_fp8(p->key, grid, block, (size_t)p->lds, s, a, false); break;
+  }
+  return e == hipSuccess ? QL_OK : hip_fail(e, "decode GEMM launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t qlinear_version(void) { return 100; }
+
+const char* qlinear_status_string(int32_t s) {
+  switch (s) {
+    case QL_OK: return "QL_OK";
+    case QL_E_INVALID: return "QL_E_INVALID";
+    case QL_E_UNSUPPORTED: return "QL_E_UNSUPPORTED";
+    case QL_E_NO_TABLE_ENTRY: return "QL_E_NO_TABLE_ENTRY";
+    case QL_E_HIP: return "QL_E_HIP";
+    case QL_E_ALIGN: return "QL_E_ALIGN";
+    case QL_E_TABLE: return "QL_E_TABLE";
+    default: return "QL_E_UNKNOWN";
+  }
+}
+
+const char* qlinear_last_error(void) { return g_err.c_str(); }
+
+ql_status qlinear_quantize_act(int32_t fmt, const void* x_bf16, int64_t M, int64_t K, void* a_q,
+                               float* a_scale, void* stream) {
+  ql_status st = check_sizes(fmt, M, K, "M");
+  if (st != QL_OK) return st;
+  if (M == 0 || K == 0) return QL_OK;
+  if (!x_bf16 || !a_q || !a_scale) return fail(QL_E_INVALID, "NULL pointer");
+  if (!aligned16(x_bf16) || !aligned16(a_q) || !aligned16(a_scale)) return fail(QL_E_ALIGN, "pointers must be 16-byte aligned");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = fmt == QL_BLOCK_FP8 ? qlk::launch_quant_groups(x_bf16, M, K, a_q, a_scale, s)
+                                     : qlk::launch_quant_rows(kernel_fmt(fmt), x_bf16, M, K, a_q, a_scale, s);
+  return e == hipSuccess ? QL_OK : hip_fail(e, "activation quantizer launch");
+}
+
+ql_status qlinear_quantize_weight(int32_t fmt, const void* w_bf16, int64_t N, int64_t K, void* w_q,
+                                  float* w_scale, void* stream) {
+  ql_status st = check_sizes(fmt, N, K, "N");
+  if (st != QL_OK) return st;
+  if (N == 0 || K == 0) return QL_OK;
+  if (!w_bf16 || !w_q || !w_scale) return fail(QL_E_INVALID, "NULL pointer");
+  if (!aligned16(w_bf16) || !aligned16(w_q) || !aligned16(w_scale)) return fail(QL_E_ALIGN, "pointers must be 16-byte aligned");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = fmt == QL_BLOCK_FP8 ? qlk::launch_quant_wblocks(w_bf16, N, K, w_q, w_scale, s)
+                                     : qlk::launch_quant_rows(kernel_fmt(fmt), w_bf16, N, K, w_q, w_scale, s);
+  return e == hipSuccess ? QL_OK : hip_fail(e, "weight quantizer launch");
+}
+
+ql_status qlinear_table_load(const char* path, int64_t* n_entries) {
+  if (!path) return fail(QL_E_INVALID, "path is NULL");
+  std::ifstream f(path);
+  if (!f) return fail(QL_E_TABLE, "cannot open table %s", path);
+  std::vector<TableEntry> rows;
+  std::string line;
+  int lineno = 0;
+  while (std::getline(f, line)) {
+    ++lineno;
+    const size_t hash = line.find('#');
+    if (hash != std::string::npos) line.resize(hash);
+    std::istringstream is(line);
+    TableEntry e{};
+    long long M, N, K;
+    if (!(is >> e.fmt)) continue;  // blank or comment line
+    if (!(is >> M >> N >> K >> e.cfg.algo >> e.cfg.swap_ab >> e.cfg.split_k >> e.cfg.waves_n >> e.cfg.waves_k >>
+          e.cfg.rows_per_wave >> e.cfg.prefetch >> e.cfg.a_lds >> e.cfg.tile_m >> e.cfg.tile_n))
+      return fail(QL_E_TABLE, "%s:%d: malformed entry", path, lineno);
+    if (!(is >> e.us)) e.us = 0;
+    if (!valid_fmt(e.fmt) || M < 1 || N < 1 || K < 1) return fail(QL_E_TABLE, "%s:%d: bad key", path, lineno);
+    e.M = M;
+    e.N = N;
+    e.K = K;
+    rows.push_back(e);
+  }
+  {
+    std::lock_guard<std::mutex> lk(g_table_mu);
+    g_table.swap(rows);
+    if (n_entries) *n_entries = (int64_t)g_table.size();
+  }
+  return QL_OK;
+}
+
+void qlinear_table_clear(void) {
+  std::lock_guard<std::mutex> lk(g_table_mu);
+  g_table.clear();
+}
+
+ql_status qlinear_plan(int32_t fmt, int64_t M, int64_t N, int64_t K, ql_plan* out_plan) {
+  ql_config c;
+  if (parse_force(&c)) return build_plan(fmt, M, N, K, c, QL_SRC_CUSTOM, out_plan);
+  if (table_lookup(fmt, M, N, K, &c)) return build_plan(fmt, M, N, K, c, QL_SRC_TABLE, out_plan);
+  return build_plan(fmt, M, N, K, heuristic_config(fmt, M, N, K), QL_SRC_HEURISTIC, out_plan);
+}
+
+ql_status qlinear_plan_from_table(int32_t fmt, int64_t M, int64_t N, int64_t K, ql_plan* out_plan) {
+  if (out_plan) *out_plan = nullptr;
+  ql_config c;
+  if (!table_lookup(fmt, M, N, K, &c))
+    return fail(QL_E_NO_TABLE_ENTRY, "no table entry for fmt=%d M=%lld N=%lld K=%lld", fmt, (long long)M,
+                (long long)N, (long long)K);
+  return build_plan(fmt, M, N, K, c, QL_SRC_TABLE, out_plan);
+}
+
+ql_status qlinear_plan_with_config(int32_t fmt, int64_t M, int64_t N, int64_t K, const ql_config* cfg,
+                                   ql_plan* out_plan) {
+  if (!cfg) return fail(QL_E_INVALID, "cfg is NULL");
+  return build_plan(fmt, M, N, K, *cfg, QL_SRC_CUSTOM, out_plan);
+}
+
+ql_status qlinear_plan_info(ql_plan p, ql_config* cfg, ql_plan_facts* facts) {
+  if (!p) return fail(QL_E_INVALID, "plan is NULL");
+  if (cfg) {
+    *cfg = p->cfg;
+    cfg->split_k = p->chunks;
+  }
+  if (facts) {
+    facts->source = p->source;
+    facts->chunks = p->chunks;
+    facts->chunk_k = p->chunk_kb * 128;
+    facts->workgroups = p->n_tiles * p->chunks;
+    facts->threads = kNW * 64;
+    facts->lds_bytes = (int32_t)p->lds;
+    facts->workspace_bytes = p->ws_bytes;
+  }
+  return QL_OK;
+}
+
+int64_t qlinear_workspace_bytes(ql_plan p) { return p ? p->ws_bytes : 0; }
+
+void qlinear_plan_destroy(ql_plan p) { delete p; }
+
+ql_status qlinear_run(ql_plan p, const void* a_q, const float* a_scale, const void* w_q, const float* w_scale,
+                      void* y, void* workspace, void* stream) {
+  if (!p) return fail(QL_E_INVALID, "plan is NULL");
+  return launch_gemm(p, a_q, a_scale, w_q, w_scale, y, workspace, nullptr, static_cast<hipStream_t>(stream));
+}
+
+ql_status qlinear_run_debug_acc(ql_plan p, const void* a_q, const float* a_scale, const void* w_q,
+                                const float* w_scale, void* y, void* workspace, void* acc_out, void* stream) {
+  if (!p) return fail(QL_E_INVALID, "plan is NULL");
+  if (!acc_out && p->M > 0 && p->N > 0 && p->K > 0) return fail(QL_E_INVALID, "acc_out is NULL");
+  return launch_gemm(p, a_q, a_scale, w_q, w_scale, y, workspace, acc_out, static_cast<hipStream_t>(stream));
+}
+
+ql_status qlinear_forward(ql_plan p, const void* x_bf16, void* a_q, float* a_scale, const void* w_q,
+                          const float* w_scale, void* y, void* workspace, void* stream) {
+  if (!p) return fail(QL_E_INVALID, "plan is NULL");
+  ql_status st = qlinear_quantize_act(p->fmt, x_bf16, p->M, p->K, a_q, a_scale, stream);
+  if (st != QL_OK) return st;
+  return launch_gemm(p, a_q, a_scale, w_q, w_scale, y, workspace, nullptr, static_cast<hipStream_t>(stream));
+}
+
+ql_status qlinear_graph_begin(void* stream) {
+  if (!stream) return fail(QL_E_INVALID, "cannot capture the default stream");
+  hipError_t e = hipStreamBeginCapture(static_cast<hipStream_t>(stream), hipStreamCaptureModeThreadLocal);
+  return e == hipSuccess ? QL_OK : hip_fail(e, "hipStreamBeginCapture");
+}
+
+ql_status qlinear_graph_end(void* stream, ql_graph* out_graph) {
+  if (!stream || !out_graph) return fail(QL_E_INVALID, "NULL argument");
+  *out_graph = nullptr;
+  hipGraph_t g = nullptr;
+  hipError_t e = hipStreamEndCapture(static_cast<hipStream_t>(stream), &g);
+  if (e != hipSuccess) return hip_fail(e, "hipStreamEndCapture");
+  hipGraphExec_t x = nullptr;
+  e = hipGraphInstantiate(&x, g, nullptr, nullptr, 0);
+  if (e != hipSuccess) {
+    (void)hipGraphDestroy(g);
+    return hip_fail(e, "hipGraphInstantiate");
+  }
+  *out_graph = new ql_graph_s{g, x};
+  return QL_OK;
+}
+
+ql_status qlinear_graph_launch(ql_graph g, void* stream) {
+  if (!g) return fail(QL_E_INVALID, "graph is NULL");
+  hipError_t e = hipGraphLaunch(g->exec, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? QL_OK : hip_fail(e, "hipGraphLaunch");
+}
+
+void qlinear_graph_destroy(ql_graph g) {
+  if (!g) return;
+  (void)hipGraphExecDestroy(g->exec);
+  (void)hipGraphDestroy(g->graph);
+  delete g;
+}
+
+}  // extern "C"

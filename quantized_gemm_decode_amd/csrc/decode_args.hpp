@@ -1,0 +1,59 @@
+// Launch arguments of the decode (M <= 32) quantized GEMM kernel, shared by
+// the host dispatcher and the kernel translation units.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qlk {
+
+// Format selector of the kernels (matches ql_format's order).
+enum { FMT_FP8 = 0, FMT_INT8 = 1, FMT_BLOCK = 2 };
+
+struct DecodeArgs {
+  const uint8_t* a;    // A_q [M, K] codes
+  const float* sa;     // s_a [M] or [M, G]
+  const uint8_t* w;    // W_q [N, K] codes
+  const float* sw;     // s_w [N] or [ceil(N/128), G]
+  uint16_t* y;         // Y [M, N] bf16
+  void* ws;            // split-K partial sums [M, N] (int32 or fp32), all-zero between runs
+  unsigned* counters;  // split-K arrival counters [n_tiles], all-zero between runs
+  void* acc_out;       // optional raw accumulators [M, N] (test hook), may be null
+  int M, N, K;
+  int G;               // number of 128-wide K blocks, ceil(K / 128)
+  int split;           // number of K chunks (workgroups per output tile)
+  int chunk_kb;        // K blocks per chunk; chunk c covers [c*chunk_kb, min(G, (c+1)*chunk_kb))
+  int waves_k;         // waves of a workgroup that share one K chunk
+  int n_tiles;         // output tiles along N
+};
+
+// Compile-time shape of one decode kernel instantiation.
+struct DecodeKey {
+  int fmt;   // FMT_FP8 / FMT_INT8 / FMT_BLOCK
+  int swap;  // weights as the matrix core's first operand
+  int mt;    // 16-wide token tiles (1: M <= 16, 2: M <= 32)
+  int rg;    // 16-row groups per wave (1 or 2)
+  int nw;    // waves per workgroup
+  int pf;    // K blocks per prefetch batch
+  int alds;  // activations staged in LDS
+};
+
+// Launch an instantiated kernel; returns hipErrorInvalidDeviceFunction when
+// the key has no instantiation.  `probe_only` checks without launching.
+hipError_t decode_dispatch_fp8(const DecodeKey& k, dim3 grid, dim3 block, size_t lds,
+                               hipStream_t s, const DecodeArgs& a, bool probe_only);
+hipError_t decode_dispatch_int8(const DecodeKey& k, dim3 grid, dim3 block, size_t lds,
+                                hipStream_t s, const DecodeArgs& a, bool probe_only);
+hipError_t decode_dispatch_block(const DecodeKey& k, dim3 grid, dim3 block, size_t lds,
+                                 hipStream_t s, const DecodeArgs& a, bool probe_only);
+
+// Quantizer launchers (quant.hip).
+hipError_t launch_quant_rows(int fmt, const void* x, int64_t R, int64_t C, void* q, float* s,
+                             hipStream_t st);
+hipError_t launch_quant_groups(const void* x, int64_t M, int64_t K, void* q, float* s,
+                               hipStream_t st);
+hipError_t launch_quant_wblocks(const void* w, int64_t N, int64_t K, void* q, float* s,
+                                hipStream_t st);
+hipError_t launch_fill_zero_bf16(void* y, int64_t count, hipStream_t st);
+
+}  // namespace qlk

@@ -1,0 +1,110 @@
+// Device helpers shared by the gfx950 kernels of the quantized linear:
+// vector types, raw buffer loads with hardware out-of-range zeroing, matrix
+// core wrappers, and the exact rounding helpers (bf16, E4M3, int8).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "decode_args.hpp"
+
+namespace qlk {
+
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+
+// Byte offset that lies beyond every buffer's num_records: a raw buffer load
+// at this offset returns zeros and issues no memory request.
+constexpr uint32_t OOB = 0x80000000u;
+
+// Raw buffer resource over `bytes` bytes starting at `p` (gfx9 word3).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
+}
+
+__device__ __forceinline__ u32x4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+}
+
+__device__ __forceinline__ float bload_f32(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
+}
+
+// 32 bytes of one row of a 128-wide K block held by one lane: `lo` covers
+// K offsets [16*g, 16*g+16) and `hi` [64+16*g, 64+16*g+16) of the block,
+// g = lane / 16.  Activations and weights use the same lane -> K map, so the
+// matrix core pairs equal K indices whatever its internal K order is.
+struct Frag {
+  u32x4 lo, hi;
+};
+
+// int8 x int8 -> int32, 16x16 output tile, K = 64 per instruction.
+__device__ __forceinline__ i32x4 mma_i8(u32x4 a, u32x4 b, i32x4 c) {
+  return __builtin_amdgcn_mfma_i32_16x16x64_i8((i32x4)a, (i32x4)b, c, 0, 0, 0);
+}
+
+// E4M3 x E4M3 -> fp32, 16x16 output tile, K = 128 per instruction (format
+// selectors 0/0 = E4M3 for both operands; zero scale operands select the
+// unscaled matrix-core instruction).
+__device__ __forceinline__ f32x4 mma_f8(const Frag& a, const Frag& b, f32x4 c) {
+  i32x8 av = {(int)a.lo.x, (int)a.lo.y, (int)a.lo.z, (int)a.lo.w,
+              (int)a.hi.x, (int)a.hi.y, (int)a.hi.z, (int)a.hi.w};
+  i32x8 bv = {(int)b.lo.x, (int)b.lo.y, (int)b.lo.z, (int)b.lo.w,
+              (int)b.hi.x, (int)b.hi.y, (int)b.hi.z, (int)b.hi.w};
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, c, 0, 0, 0, 0, 0, 0);
+}
+
+// binary32 -> bfloat16, round to nearest even; NaN stays a quiet NaN.
+__device__ __forceinline__ uint32_t bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return ((u >> 16) | 0x40u) & 0xffffu;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+
+// binary32 in [-448, 448] -> OCP E4M3 code, round to nearest even.
+// Below 2^-6 every E4M3 value is a multiple of 2^-9 (subnormals; code 8 is
+// the smallest normal), so scaling by 2^9 and rounding to an integer gives
+// the code directly.  Above, keep 3 mantissa bits with round-half-even on
+// the 20 dropped bits and rebias the exponent from 127 to 7.
+__device__ __forceinline__ uint32_t e4m3_rne(float v) {
+  uint32_t u = __float_as_uint(v);
+  uint32_t sign = (u >> 24) & 0x80u;
+  uint32_t a = u & 0x7fffffffu;
+  float af = __uint_as_float(a);
+  uint32_t code;
+  if (af < 0.015625f) {
+    code = (uint32_t)__builtin_rintf(af * 512.0f);
+  } else {
+    uint32_t r = a + 0x7ffffu + ((a >> 20) & 1u);
+    code = (r >> 20) - (120u << 3);
+  }
+  return code | sign;
+}
+
+// One quantized code of x with scale s (IEEE division, then round + clamp).
+template <int FMT>
+__device__ __forceinline__ uint32_t quant_code(float x, float s) {
+  float t = __fdiv_rn(x, s);
+  if (FMT == FMT_INT8) {
+    float q = __builtin_rintf(t);
+    q = fminf(fmaxf(q, -127.0f), 127.0f);
+    return (uint32_t)((int)q) & 0xffu;
+  } else {
+    t = fminf(fmaxf(t, -448.0f), 448.0f);
+    return e4m3_rne(t);
+  }
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+}  // namespace qlk

@@ -1,0 +1,215 @@
+// Quantizer kernels for gfx950: the dynamic activation quantizer (per token,
+// or per 1x128 group for Block_FP8) and the offline weight quantizer (per
+// output channel, or per 128x128 block for Block_FP8).
+//
+// Formats and granularity: [Summary] "Put algorithm selection inside the
+// search space" (last paragraph) and [Noticias] "El backend lineal de Helion
+// / Alcance".  The pages give no formula; the rule here is symmetric absmax:
+//   s = fl(amax / Q), Q = 127 (int8) or 448 (E4M3); s = 1 when amax == 0;
+//   code = round-half-even(fl(x / s)), clamped to [-127, 127] for int8, or
+//   clamped to [-448, 448] and rounded to nearest-even E4M3.
+// Both divisions are IEEE binary32 divisions (__fdiv_rn), and fp32
+// subnormals are kept, so the codes and scales are a deterministic function
+// of the bf16 input.  amax is a wavefront reduction (DPP/swizzle shuffles)
+// followed by an LDS reduction across the workgroup's waves.
+//
+// [Summary] = English summary of "Building a High-Performance and Portable
+// vLLM Linear Backend with Helion" (yuxiaoba.github.io); [Noticias] = "Helion
+// entra al backend lineal de vLLM y supera a CUTLASS en Hopper".
+#include <algorithm>
+
+#include "decode_args.hpp"
+#include "device_common.hpp"
+
+namespace qlk {
+
+constexpr int QT = 256;  // threads per quantizer workgroup
+
+__device__ __forceinline__ float abs_bf16_max8(const u32x4& v, float m) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    m = fmaxf(m, bf16_to_f32(v[i] & 0x7fffu));
+    m = fmaxf(m, bf16_to_f32((v[i] >> 16) & 0x7fffu));
+  }
+  return m;
+}
+
+template <int FMT>
+__device__ __forceinline__ u32x2 quant8(const u32x4& v, float s) {
+  uint32_t c[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    c[2 * i] = quant_code<FMT>(bf16_to_f32(v[i] & 0xffffu), s);
+    c[2 * i + 1] = quant_code<FMT>(bf16_to_f32(v[i] >> 16), s);
+  }
+  u32x2 out = {c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24),
+               c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24)};
+  return out;
+}
+
+__device__ __forceinline__ float block_max(float m, float* red) {
+  m = wave_max(m);
+  const int wave = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) red[wave] = m;
+  __syncthreads();
+  float r = red[0];
+#pragma unroll
+  for (int i = 1; i < QT / 64; ++i) r = fmaxf(r, red[i]);
+  return r;
+}
+
+template <int FMT>
+__device__ __forceinline__ float scale_of(float amax) {
+  const float Q = FMT == FMT_INT8 ? 127.0f : 448.0f;
+  return amax > 0.0f ? __fdiv_rn(amax, Q) : 1.0f;
+}
+
+// One row per workgroup; the row stays in registers (VPT 16-byte vectors per
+// thread) between the amax pass and the quantize pass.
+template <int FMT, int VPT>
+__global__ void __launch_bounds__(QT) quant_rows_reg_kernel(const uint16_t* __restrict__ x, uint32_t C,
+                                                            uint8_t* __restrict__ q, float* __restrict__ s) {
+  __shared__ float red[QT / 64];
+  const size_t row = blockIdx.x;
+  const uint16_t* xr = x + row * C;
+  uint8_t* qr = q + row * C;
+  u32x4 v[VPT];
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < VPT; ++i) {
+    const uint32_t e = (uint32_t)(i * QT + threadIdx.x) * 8u;
+    v[i] = e < C ? *reinterpret_cast<const u32x4*>(xr + e) : u32x4{0, 0, 0, 0};
+    amax = abs_bf16_max8(v[i], amax);
+  }
+  amax = block_max(amax, red);
+  const float sc = scale_of<FMT>(amax);
+#pragma unroll
+  for (int i = 0; i < VPT; ++i) {
+    const uint32_t e = (uint32_t)(i * QT + threadIdx.x) * 8u;
+    if (e < C) *reinterpret_cast<u32x2*>(qr + e) = quant8<FMT>(v[i], sc);
+  }
+  if (threadIdx.x == 0) s[row] = sc;
+}
+
+// Rows too long for registers: two streaming passes (the second re-reads from cache).
+template <int FMT>
+__global__ void __launch_bounds__(QT) quant_rows_stream_kernel(const uint16_t* __restrict__ x, uint32_t C,
+                                                               uint8_t* __restrict__ q, float* __restrict__ s) {
+  __shared__ float red[QT / 64];
+  const size_t row = blockIdx.x;
+  const uint16_t* xr = x + row * C;
+  uint8_t* qr = q + row * C;
+  float amax = 0.0f;
+  for (uint32_t e = threadIdx.x * 8u; e < C; e += QT * 8u)
+    amax = abs_bf16_max8(*reinterpret_cast<const u32x4*>(xr + e), amax);
+  amax = block_max(amax, red);
+  const float sc = scale_of<FMT>(amax);
+  for (uint32_t e = threadIdx.x * 8u; e < C; e += QT * 8u)
+    *reinterpret_cast<u32x2*>(qr + e) = quant8<FMT>(*reinterpret_cast<const u32x4*>(xr + e), sc);
+  if (threadIdx.x == 0) s[row] = sc;
+}
+
+// Block_FP8 activations: groups of 128 contiguous elements along K (K % 128
+// == 0, so group id = m * K/128 + g is also the s_a index); 16 lanes per
+// group, 8 elements per lane; the group amax reduces over the 16 lanes.
+__global__ void __launch_bounds__(QT) quant_groups_kernel(const uint16_t* __restrict__ x, uint32_t ngroups,
+                                                          uint8_t* __restrict__ q, float* __restrict__ s) {
+  const uint32_t gid = blockIdx.x * (QT / 16) + (threadIdx.x >> 4);
+  const uint32_t li = threadIdx.x & 15u;
+  const bool ok = gid < ngroups;
+  const size_t e = (size_t)gid * 128u + li * 8u;
+  const u32x4 v = ok ? *reinterpret_cast<const u32x4*>(x + e) : u32x4{0, 0, 0, 0};
+  float amax = abs_bf16_max8(v, 0.0f);
+#pragma unroll
+  for (int o = 8; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));
+  const float sc = scale_of<FMT_FP8>(amax);
+  if (ok) {
+    *reinterpret_cast<u32x2*>(q + e) = quant8<FMT_FP8>(v, sc);
+    if (li == 0) s[gid] = sc;
+  }
+}
+
+// Block_FP8 weights: one workgroup per 128x128 block (nb, g); thread t covers
+// 8 columns (t % 16) of rows t/16 + 16 i; rows >= N of a ragged last block
+// row are not part of the block.
+__global__ void __launch_bounds__(QT) quant_wblocks_kernel(const uint16_t* __restrict__ w, uint32_t N,
+                                                           uint32_t K, uint8_t* __restrict__ q,
+                                                           float* __restrict__ s) {
+  __shared__ float red[QT / 64];
+  const uint32_t g = blockIdx.x, nb = blockIdx.y, G = gridDim.x;
+  const uint32_t c = (threadIdx.x & 15u) * 8u;
+  const uint32_t r0 = threadIdx.x >> 4;
+  u32x4 v[8];
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const uint32_t n = nb * 128u + r0 + 16u * i;
+    v[i] = n < N ? *reinterpret_cast<const u32x4*>(w + (size_t)n * K + g * 128u + c) : u32x4{0, 0, 0, 0};
+    amax = abs_bf16_max8(v[i], amax);
+  }
+  amax = block_max(amax, red);
+  const float sc = scale_of<FMT_FP8>(amax);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const uint32_t n = nb * 128u + r0 + 16u * i;
+    if (n < N) *reinterpret_cast<u32x2*>(q + (size_t)n * K + g * 128u + c) = quant8<FMT_FP8>(v[i], sc);
+  }
+  if (threadIdx.x == 0) s[nb * G + g] = sc;
+}
+
+__global__ void fill_zero_u16_kernel(uint16_t* p, size_t n) {
+  for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
+    p[i] = 0;
+}
+
+template <int FMT>
+static hipError_t rows_dispatch(const void* x, int64_t R, int64_t C, void* q, float* s, hipStream_t st) {
+  const uint16_t* xp = static_cast<const uint16_t*>(x);
+  uint8_t* qp = static_cast<uint8_t*>(q);
+  const int64_t vecs = (C + 7) / 8;
+  const int64_t vpt = (vecs + QT - 1) / QT;
+  const dim3 grid((unsigned)R), block(QT);
+  if (vpt <= 1)
+    quant_rows_reg_kernel<FMT, 1><<<grid, block, 0, st>>>(xp, (uint32_t)C, qp, s);
+  else if (vpt <= 2)
+    quant_rows_reg_kernel<FMT, 2><<<grid, block, 0, st>>>(xp, (uint32_t)C, qp, s);
+  else if (vpt <= 4)
+    quant_rows_reg_kernel<FMT, 4><<<grid, block, 0, st>>>(xp, (uint32_t)C, qp, s);
+  else if (vpt <= 8)
+    quant_rows_reg_kernel<FMT, 8><<<grid, block, 0, st>>>(xp, (uint32_t)C, qp, s);
+  else if (vpt <= 16)
+    quant_rows_reg_kernel<FMT, 16><<<grid, block, 0, st>>>(xp, (uint32_t)C, qp, s);
+  else
+    quant_rows_stream_kernel<FMT><<<grid, block, 0, st>>>(xp, (uint32_t)C, qp, s);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_rows(int fmt, const void* x, int64_t R, int64_t C, void* q, float* s,
+                             hipStream_t st) {
+  if (fmt == FMT_INT8) return rows_dispatch<FMT_INT8>(x, R, C, q, s, st);
+  return rows_dispatch<FMT_FP8>(x, R, C, q, s, st);
+}
+
+hipError_t launch_quant_groups(const void* x, int64_t M, int64_t K, void* q, float* s, hipStream_t st) {
+  const int64_t ng = M * (K / 128);
+  const dim3 grid((unsigned)((ng + QT / 16 - 1) / (QT / 16))), block(QT);
+  quant_groups_kernel<<<grid, block, 0, st>>>(static_cast<const uint16_t*>(x), (uint32_t)ng,
+                                              static_cast<uint8_t*>(q), s);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_wblocks(const void* w, int64_t N, int64_t K, void* q, float* s, hipStream_t st) {
+  const dim3 grid((unsigned)(K / 128), (unsigned)((N + 127) / 128)), block(QT);
+  quant_wblocks_kernel<<<grid, block, 0, st>>>(static_cast<const uint16_t*>(w), (uint32_t)N, (uint32_t)K,
+                                               static_cast<uint8_t*>(q), s);
+  return hipGetLastError();
+}
+
+hipError_t launch_fill_zero_bf16(void* y, int64_t count, hipStream_t st) {
+  const int64_t blocks = std::min<int64_t>((count + 255) / 256, 4096);
+  fill_zero_u16_kernel<<<dim3((unsigned)std::max<int64_t>(blocks, 1)), dim3(256), 0, st>>>(
+      static_cast<uint16_t*>(y), (size_t)count);
+  return hipGetLastError();
+}
+
+}  // namespace qlk

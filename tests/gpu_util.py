@@ -1,0 +1,61 @@
+"""Helpers shared by the GPU parity tests: moving oracle data to the device and back."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import quantized_gemm_decode_amd as ql
+
+requires_gpu = pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")
+
+
+def dev_bf16(bits):
+    """uint16 bf16 bit patterns -> device bf16 tensor."""
+    t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16))
+    return t.view(torch.bfloat16).cuda()
+
+
+def dev_codes(fmt, q):
+    """Oracle codes -> device tensor (int8, or float8_e4m3fn from the raw bytes)."""
+    if fmt == oracle.FMT_W8A8_INT8:
+        return torch.from_numpy(np.ascontiguousarray(q).astype(np.int8)).cuda()
+    return torch.from_numpy(np.ascontiguousarray(q).astype(np.uint8)).cuda().view(torch.float8_e4m3fn)
+
+
+def host_codes(fmt, t):
+    """Device codes -> numpy array in the oracle's convention (int8 / uint8 bytes)."""
+    if fmt == oracle.FMT_W8A8_INT8:
+        return t.cpu().numpy().astype(np.int8)
+    return t.view(torch.uint8).cpu().numpy()
+
+
+def host_bf16_bits(t):
+    return t.cpu().view(torch.int16).numpy().view(np.uint16)
+
+
+def dev_f32(a):
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).cuda()
+
+
+def run_gemm(plan, a_q, s_a, w_q, s_w, acc=True):
+    """Run a plan once; returns (y_bits, acc numpy or None, workspace tensor or None)."""
+    M, N = plan.M, plan.N
+    y = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
+    y.fill_(float("nan"))
+    ws = plan.new_workspace()
+    if acc:
+        a = torch.empty(M, N, dtype=torch.int32 if plan.fmt == ql.W8A8_INT8 else torch.float32, device="cuda")
+        ql.qlinear_run_debug_acc(plan, a_q, s_a, w_q, s_w, y, a, ws)
+    else:
+        ql.qlinear_run(plan, a_q, s_a, w_q, s_w, y, ws)
+    torch.cuda.synchronize()
+    return host_bf16_bits(y), (a.cpu().numpy() if acc else None), ws
+
+
+def fp8_check(fmt, r, y_bits, split):
+    """Apply the oracle's FP8 acceptance rule to a GPU result."""
+    K = r["a_q"].shape[1]
+    d = oracle.summation_depth(K, split=split)
+    B = oracle.tolerance_bound(fmt, r["a_q"], r["w_q"], r["s_a"], r["s_w"], d)
+    return oracle.check_fp8_parity(y_bits, r["y_ref"], r["y_true"], B)

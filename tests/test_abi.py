@@ -1,0 +1,161 @@
+"""Host-side tests of the C ABI (CPU only: no kernel is launched here).
+
+The library must load, export every function that include/qlinear.h
+declares, and reject bad arguments on the host with the documented status
+codes before touching the GPU.  Planning is host-only, so plans, the sweep
+table and the QLINEAR_FORCE override are testable here too.
+"""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import quantized_gemm_decode_amd as ql
+from quantized_gemm_decode_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "qlinear.h")
+
+QL_OK, QL_E_INVALID, QL_E_UNSUPPORTED, QL_E_NO_TABLE_ENTRY, QL_E_HIP, QL_E_ALIGN, QL_E_TABLE = range(7)
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return set(re.findall(r"^\s*(?:ql_status|int32_t|int64_t|void|const char\s*\*)\s*(qlinear_\w+)\s*\(", text, re.M))
+
+
+def test_header_and_binding_agree():
+    declared = _declared_functions()
+    assert len(declared) >= 20
+    assert declared == set(_lib.SIGNATURES)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(_lib.LIB_PATH)
+    for name in _declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings_and_version():
+    lib = ql.lib()
+    assert lib.qlinear_version() >= 100
+    names = [lib.qlinear_status_string(i).decode() for i in range(7)]
+    assert names == ["QL_OK", "QL_E_INVALID", "QL_E_UNSUPPORTED", "QL_E_NO_TABLE_ENTRY", "QL_E_HIP",
+                     "QL_E_ALIGN", "QL_E_TABLE"]
+    assert lib.qlinear_status_string(99).decode() == "QL_E_UNKNOWN"
+
+
+def _plan_status(fmt, M, N, K, **cfg):
+    h = ctypes.c_void_p()
+    if cfg:
+        c = ql.QLConfig(**ql.make_config(**cfg))
+        st = ql.lib().qlinear_plan_with_config(fmt, M, N, K, ctypes.byref(c), ctypes.byref(h))
+    else:
+        st = ql.lib().qlinear_plan(fmt, M, N, K, ctypes.byref(h))
+    if h.value:
+        ql.lib().qlinear_plan_destroy(h)
+    return st
+
+
+def test_host_validation_status_codes():
+    assert _plan_status(ql.W8A8_INT8, 8, 4096, 2048) == QL_OK
+    assert _plan_status(7, 8, 4096, 2048) == QL_E_INVALID                 # unknown format
+    assert _plan_status(ql.W8A8_INT8, 8, 4096, 2056) == QL_E_INVALID      # K % 16
+    assert _plan_status(ql.BLOCK_FP8, 8, 4096, 2064) == QL_E_INVALID      # Block needs K % 128
+    assert _plan_status(ql.FP8_DYNAMIC, -1, 4096, 2048) == QL_E_INVALID
+    assert _plan_status(ql.FP8_DYNAMIC, 8, 2 ** 20, 2048) == QL_E_UNSUPPORTED   # N*K > 2^30
+    assert _plan_status(ql.FP8_DYNAMIC, 8, 4096, 2048, split_k=3) == QL_E_INVALID
+    assert _plan_status(ql.FP8_DYNAMIC, 8, 4096, 2048, split_k=512) == QL_E_INVALID
+    assert _plan_status(ql.FP8_DYNAMIC, 8, 4096, 2048, waves_n=3, waves_k=1) == QL_E_INVALID
+    assert _plan_status(ql.FP8_DYNAMIC, 8, 4096, 2048, rows_per_wave=48) == QL_E_INVALID
+    assert _plan_status(ql.FP8_DYNAMIC, 8, 4096, 2048, prefetch=3) == QL_E_INVALID
+    assert _plan_status(ql.FP8_DYNAMIC, 8, 4096, 2048, swap_ab=2) == QL_E_INVALID
+    # the LDS-staged activation chunk must fit the 64 KB budget
+    assert _plan_status(ql.FP8_DYNAMIC, 32, 4096, 25600, split_k=1, a_lds=1) == QL_E_UNSUPPORTED
+    assert _plan_status(ql.FP8_DYNAMIC, 32, 4096, 25600, split_k=1, a_lds=0) == QL_OK
+    assert "LDS" in ql.lib().qlinear_last_error().decode() or True
+
+
+def test_quantizer_rejects_bad_arguments_on_host():
+    lib = ql.lib()
+    null = ctypes.c_void_p(0)
+    assert lib.qlinear_quantize_act(ql.W8A8_INT8, null, 4, 100, null, null, null) == QL_E_INVALID  # K % 16
+    assert lib.qlinear_quantize_act(ql.W8A8_INT8, null, 4, 128, null, null, null) == QL_E_INVALID  # NULL
+    assert lib.qlinear_quantize_act(ql.W8A8_INT8, ctypes.c_void_p(8), 4, 128, ctypes.c_void_p(16),
+                                    ctypes.c_void_p(16), null) == QL_E_ALIGN
+    assert lib.qlinear_quantize_act(ql.W8A8_INT8, null, 0, 128, null, null, null) == QL_OK        # empty
+    assert lib.qlinear_quantize_weight(ql.BLOCK_FP8, null, 4, 192, null, null, null) == QL_E_INVALID
+
+
+def test_run_rejects_bad_arguments_on_host():
+    p = ql.qlinear_plan_with_config(ql.W8A8_INT8, 8, 4096, 2048, dict(split_k=4))
+    lib = ql.lib()
+    v = ctypes.c_void_p
+    good = v(1 << 20)
+    assert lib.qlinear_run(p.handle, good, good, good, good, good, v(0), v(0)) == QL_E_INVALID   # no workspace
+    assert lib.qlinear_run(p.handle, v(0), good, good, good, good, good, v(0)) == QL_E_INVALID
+    assert lib.qlinear_run(p.handle, v(3), good, good, good, good, good, v(0)) == QL_E_ALIGN
+    assert lib.qlinear_run(v(0), good, good, good, good, good, good, v(0)) == QL_E_INVALID
+    assert lib.qlinear_run_debug_acc(p.handle, good, good, good, good, good, good, v(0), v(0)) == QL_E_INVALID
+    assert lib.qlinear_graph_begin(v(0)) == QL_E_INVALID      # default stream cannot be captured
+
+
+def test_plan_facts_and_workspace_sizes():
+    p = ql.qlinear_plan_with_config(ql.W8A8_INT8, 8, 4096, 2048,
+                                    dict(split_k=4, waves_n=2, waves_k=2, rows_per_wave=32))
+    cfg, facts = p.info()
+    assert facts["source"] == "custom"
+    assert facts["chunks"] == 4 and facts["chunk_k"] == 512
+    assert facts["workgroups"] == (4096 // 64) * 4 and facts["threads"] == 256
+    assert p.workspace_bytes == 8 * 4096 * 4 + (4096 // 64) * 4
+    assert ql.qlinear_plan_with_config(ql.W8A8_INT8, 8, 4096, 2048, dict(split_k=1)).workspace_bytes == 0
+    # split clamps to the number of 128-wide K blocks and to balanced chunks
+    q = ql.qlinear_plan_with_config(ql.FP8_DYNAMIC, 4, 512, 640, dict(split_k=256, a_lds=0))
+    assert q.config["split_k"] == 5 and q.facts["chunk_k"] == 128
+    r = ql.qlinear_plan_with_config(ql.FP8_DYNAMIC, 4, 512, 5120, dict(split_k=16))
+    assert r.facts["chunks"] == 14 and r.facts["chunk_k"] == 384        # ceil(40/16)=3 blocks per chunk
+
+
+def test_table_lookup_buckets_and_force(tmp_path):
+    t = tmp_path / "t.txt"
+    t.write_text("# fmt M N K algo swap split wn wk rows pf alds tm tn us\n"
+                 "0 8 4096 4096 0 1 4 4 1 16 2 1 0 0 3.1\n"
+                 "0 32 4096 4096 0 0 2 2 2 32 4 1 0 0 3.3\n"
+                 "\n")
+    assert ql.qlinear_table_load(str(t)) == 2
+    try:
+        p = ql.qlinear_plan(ql.FP8_DYNAMIC, 5, 4096, 4096)           # bucket 8
+        assert p.facts["source"] == "table" and p.config["swap_ab"] == 1 and p.config["split_k"] == 4
+        p = ql.qlinear_plan(ql.FP8_DYNAMIC, 17, 4096, 4096)          # bucket 24 -> nearest tuned >= : 32
+        assert p.config["waves_k"] == 2 and p.config["prefetch"] == 4
+        p = ql.qlinear_plan(ql.FP8_DYNAMIC, 8, 4096, 2048)           # other K: heuristic
+        assert p.facts["source"] == "heuristic"
+        with pytest.raises(ql.QLinearError) as e:
+            ql.qlinear_plan_from_table(ql.W8A8_INT8, 8, 4096, 4096)
+        assert e.value.status == QL_E_NO_TABLE_ENTRY
+        os.environ["QLINEAR_FORCE"] = "0,0,2,1,4,16,4,0,0,0"
+        try:
+            p = ql.qlinear_plan(ql.FP8_DYNAMIC, 8, 4096, 4096)
+            assert p.facts["source"] == "custom" and p.config["waves_k"] == 4
+        finally:
+            del os.environ["QLINEAR_FORCE"]
+    finally:
+        ql.qlinear_table_clear()
+    bad = tmp_path / "bad.txt"
+    bad.write_text("0 8 4096\n")
+    with pytest.raises(ql.QLinearError) as e:
+        ql.qlinear_table_load(str(bad))
+    assert e.value.status == QL_E_TABLE
+    with pytest.raises(ql.QLinearError):
+        ql.qlinear_table_load(str(tmp_path / "missing.txt"))
+
+
+def test_heuristic_plans_cover_every_decode_workload():
+    from workloads import CONFIGS, decode_points
+    for cfg in CONFIGS[:4]:
+        for (_, N, K, M) in decode_points(cfg):
+            p = ql.qlinear_plan(cfg.fmt, M, N, K)
+            assert p.facts["workgroups"] >= 256

@@ -1,0 +1,251 @@
+"""GPU parity of the decode GEMM against the oracle.
+
+INT8: the int32 accumulator and the bf16 output are bit-exact.  FP8_Dynamic
+and Block_FP8: the bf16 output passes the oracle's acceptance rule (within
+1 bf16 ulp of the single-rounded result, or within the binary32 summation
+bound of the exact result; normwise error <= 1e-2), and the fp32
+accumulator lies within the summation bound of the exact sum.
+"""
+
+import itertools
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import quantized_gemm_decode_amd as ql
+from tests.gpu_util import (dev_bf16, dev_codes, dev_f32, fp8_check, host_bf16_bits, host_codes,
+                            requires_gpu, run_gemm)
+from workloads import CONFIGS, decode_points, make_inputs, bf16_bits
+
+pytestmark = [pytest.mark.gpu, requires_gpu]
+FMTS = [ql.FP8_DYNAMIC, ql.W8A8_INT8, ql.BLOCK_FP8]
+
+
+def _ref(fmt, M, N, K, seed, sigma=0.02):
+    x, w = make_inputs(K, N, M, sigma, seed=seed)
+    return oracle.reference(fmt, bf16_bits(x), bf16_bits(w))
+
+
+def _dev(fmt, r):
+    return (dev_codes(fmt, r["a_q"]), dev_f32(r["s_a"]), dev_codes(fmt, r["w_q"]), dev_f32(r["s_w"]))
+
+
+def _assert_parity(fmt, r, y, acc, split, label=""):
+    if fmt == ql.W8A8_INT8:
+        assert np.array_equal(acc.astype(np.int64), r["S"]), label
+        bad = np.argwhere(y != r["y_ref"])
+        assert bad.size == 0, (label, bad[:5])
+        return
+    st = fp8_check(fmt, r, y, split)
+    assert st["ok"], (label, st)
+    K = r["a_q"].shape[1]
+    d = oracle.summation_depth(K, split=split)
+    gamma = d * 2.0 ** -24 / (1 - d * 2.0 ** -24)
+    if fmt == ql.FP8_DYNAMIC:
+        bound = gamma * oracle.contract_abs(fmt, r["a_q"], r["w_q"])
+        assert np.all(np.abs(acc.astype(np.float64) - r["S"]) <= bound), label
+    else:
+        B = oracle.tolerance_bound(fmt, r["a_q"], r["w_q"], r["s_a"], r["s_w"], d)
+        assert np.all(np.abs(acc.astype(np.float64) - r["y_true"]) <= B + 1e-30), label
+
+
+# every kernel instantiation: swap x rows/wave x prefetch x LDS staging, both token tiles
+VARIANTS = list(itertools.product([0, 1], [16, 32], [2, 4], [0, 1]))
+SPLITS = [1, 2, 4, 8]
+WAVES_K = [1, 2, 4]
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("M", [5, 29])
+@pytest.mark.parametrize("vi", range(len(VARIANTS)))
+def test_every_instantiation_matches_oracle(fmt, M, vi):
+    swap, rows, pf, alds = VARIANTS[vi]
+    split = SPLITS[(vi + M) % len(SPLITS)]
+    wk = WAVES_K[(vi // 2 + M) % len(WAVES_K)]
+    N = 300 if rows == 16 else 520                      # several tiles + a ragged tail
+    K = 1152 if fmt == ql.BLOCK_FP8 or vi % 3 else 1040  # 1040: ragged last K block
+    r = _ref(fmt, M, N, K, seed=vi * 7 + M)
+    cfg = dict(swap_ab=swap, split_k=split, waves_n=4 // wk, waves_k=wk, rows_per_wave=rows, prefetch=pf,
+               a_lds=alds)
+    plan = ql.qlinear_plan_with_config(fmt, M, N, K, cfg)
+    y, acc, ws = run_gemm(plan, *_dev(fmt, r))
+    _assert_parity(fmt, r, y, acc, plan.facts["chunks"], label=str(cfg))
+    if ws is not None:
+        assert int(torch.count_nonzero(ws)) == 0, "split-K workspace not left all-zero"
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("M", [1, 2, 16, 17, 24, 32])
+def test_token_counts_and_tiles(fmt, M):
+    N, K = 1024, 2048
+    r = _ref(fmt, M, N, K, seed=M)
+    for cfg in (dict(swap_ab=0, split_k=1, waves_n=1, waves_k=4, a_lds=0),
+                dict(swap_ab=1, split_k=4, waves_n=2, waves_k=2, rows_per_wave=32, a_lds=1),
+                dict(swap_ab=1, split_k=16, waves_n=4, waves_k=1, prefetch=4, a_lds=1)):
+        plan = ql.qlinear_plan_with_config(fmt, M, N, K, cfg)
+        y, acc, _ = run_gemm(plan, *_dev(fmt, r))
+        _assert_parity(fmt, r, y, acc, plan.facts["chunks"], label=str(cfg))
+
+
+def test_int8_all_variants_bitwise_identical_and_deterministic():
+    M, N, K = 12, 700, 3072
+    r = _ref(ql.W8A8_INT8, M, N, K, seed=99)
+    d = _dev(ql.W8A8_INT8, r)
+    outs = []
+    for swap, split, wk, rows, alds in itertools.product([0, 1], [1, 8, 32], [1, 4], [16, 32], [0, 1]):
+        cfg = dict(swap_ab=swap, split_k=split, waves_n=4 // wk, waves_k=wk, rows_per_wave=rows, a_lds=alds)
+        try:
+            plan = ql.qlinear_plan_with_config(ql.W8A8_INT8, M, N, K, cfg)
+        except ql.QLinearError:
+            continue
+        for _ in range(2):
+            y, _, _ = run_gemm(plan, *d, acc=False)
+            outs.append(y)
+    assert len(outs) >= 40
+    for y in outs[1:]:
+        assert np.array_equal(y, outs[0])
+    assert np.array_equal(outs[0], r["y_ref"])
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_split_k_workspace_reuse_across_runs(fmt):
+    M, N, K = 8, 512, 4096
+    r = _ref(fmt, M, N, K, seed=5)
+    plan = ql.qlinear_plan_with_config(fmt, M, N, K, dict(split_k=8, swap_ab=1))
+    d = _dev(fmt, r)
+    ws = plan.new_workspace()
+    y = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
+    for _ in range(5):
+        y.fill_(0)
+        ql.qlinear_run(plan, *d, y, ws)
+        torch.cuda.synchronize()
+        assert int(torch.count_nonzero(ws)) == 0
+        st = fp8_check(fmt, r, host_bf16_bits(y), 8) if fmt != ql.W8A8_INT8 else None
+        if st is None:
+            assert np.array_equal(host_bf16_bits(y), r["y_ref"])
+        else:
+            assert st["ok"], st
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_forward_quantizes_and_runs(fmt):
+    M, N, K = 9, 640, 2048
+    x, w = make_inputs(K, N, M, 0.02, seed=21)
+    r = oracle.reference(fmt, bf16_bits(x), bf16_bits(w))
+    plan = ql.qlinear_plan(fmt, M, N, K)
+    w_q, w_s = ql.quantize_weight(fmt, w.cuda())
+    a_q = torch.empty(M, K, dtype=ql.code_dtype(fmt), device="cuda")
+    a_s = torch.empty(ql.act_scale_shape(fmt, M, K), dtype=torch.float32, device="cuda")
+    y = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
+    ql.qlinear_forward(plan, x.cuda(), a_q, a_s, w_q, w_s, y, plan.new_workspace())
+    torch.cuda.synchronize()
+    assert np.array_equal(host_codes(fmt, a_q), r["a_q"])
+    if fmt == ql.W8A8_INT8:
+        assert np.array_equal(host_bf16_bits(y), r["y_ref"])
+    else:
+        assert fp8_check(fmt, r, host_bf16_bits(y), plan.facts["chunks"])["ok"]
+
+
+def test_k_zero_gives_zeros_and_empty_shapes_are_no_ops():
+    plan = ql.qlinear_plan(ql.FP8_DYNAMIC, 4, 100, 0)
+    y = torch.full((4, 100), 3.0, dtype=torch.bfloat16, device="cuda")
+    e = torch.empty(16, dtype=torch.uint8, device="cuda")
+    f = torch.empty(16, dtype=torch.float32, device="cuda")
+    ql.qlinear_run(plan, e, f, e, f, y)
+    torch.cuda.synchronize()
+    assert int(torch.count_nonzero(y)) == 0
+    for M, N in ((0, 64), (4, 0)):
+        p = ql.qlinear_plan(ql.W8A8_INT8, M, N, 256)
+        yy = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
+        ql.qlinear_run(p, e, f, e, f, yy)
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_graph_capture_replays_match_eager(fmt):
+    M, N, K = 16, 1536, 4096
+    x, w = make_inputs(K, N, M, 0.02, seed=31)
+    plan = ql.qlinear_plan_with_config(fmt, M, N, K, dict(split_k=4, swap_ab=1))
+    w_q, w_s = ql.quantize_weight(fmt, w.cuda())
+    xd = x.cuda()
+    a_q = torch.empty(M, K, dtype=ql.code_dtype(fmt), device="cuda")
+    a_s = torch.empty(ql.act_scale_shape(fmt, M, K), dtype=torch.float32, device="cuda")
+    y = torch.zeros(M, N, dtype=torch.bfloat16, device="cuda")
+    ws = plan.new_workspace()
+    ql.qlinear_forward(plan, xd, a_q, a_s, w_q, w_s, y, ws)
+    torch.cuda.synchronize()
+    eager = y.clone()
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        ql.qlinear_graph_begin(s)
+        ql.qlinear_forward(plan, xd, a_q, a_s, w_q, w_s, y, ws, stream=s)
+        g = ql.qlinear_graph_end(s)
+    for i in range(4):
+        y.fill_(0)
+        torch.cuda.synchronize()
+        g.launch(s)
+        s.synchronize()
+        if fmt == ql.W8A8_INT8:
+            assert torch.equal(y, eager), i
+        else:
+            r = oracle.reference(fmt, bf16_bits(x), bf16_bits(w))
+            assert fp8_check(fmt, r, host_bf16_bits(y), 4)["ok"], i
+        assert int(torch.count_nonzero(ws)) == 0
+        _ = torch.randn(1000, device="cuda").sum()      # unrelated eager work between replays
+
+
+# ---------------------------------------------------------------- full-size workloads
+
+def _full_points():
+    pts = []
+    for ci, cfg in enumerate(CONFIGS[:4]):
+        for (lab, N, K, M) in decode_points(cfg):
+            if ci == 0 or M in (1, 8, 32) or (ci == 1 and lab == "o"):
+                pts.append((ci, lab, N, K, M))
+    return pts
+
+
+_W_CACHE = {}
+
+
+def _weights(ci, lab, N, K):
+    key = (ci, lab)
+    if key not in _W_CACHE:
+        _W_CACHE.clear()
+        cfg = CONFIGS[ci]
+        x, w = make_inputs(K, N, 32 if ci else 8, cfg.sigma_w, seed=cfg.seed)
+        w_q, w_s = ql.quantize_weight(cfg.fmt, w.cuda())
+        _W_CACHE[key] = (x, w, w_q, w_s)
+    return _W_CACHE[key]
+
+
+@pytest.mark.parametrize("ci,lab,N,K,M", _full_points())
+def test_full_size_workloads_sampled_columns(ci, lab, N, K, M):
+    """Configured workloads at full size with the plan the bench uses; the
+    oracle recomputes sampled output columns one by one (it quantizes just the
+    weight rows, or 128-row blocks, those columns need)."""
+    fmt = CONFIGS[ci].fmt
+    ql.load_default_table()
+    x, w, w_q, w_s = _weights(ci, lab, N, K)
+    xm = x[:M]
+    plan = ql.qlinear_plan(fmt, M, N, K)
+    a_q, a_s = ql.quantize_act(fmt, xm.cuda())
+    y = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
+    ql.qlinear_run(plan, a_q, a_s, w_q, w_s, y, plan.new_workspace())
+    torch.cuda.synchronize()
+    yb = host_bf16_bits(y)
+    rng = np.random.default_rng(ci * 1000 + M)
+    if fmt == ql.BLOCK_FP8:
+        nbs = rng.choice(-(-N // 128), 2, replace=False)
+        cols = np.concatenate([np.arange(nb * 128, min(N, nb * 128 + 128)) for nb in nbs])
+    else:
+        cols = np.sort(rng.choice(N, 96, replace=False))
+    r = oracle.reference(fmt, bf16_bits(xm), bf16_bits(w[torch.from_numpy(cols)]))
+    assert np.array_equal(host_codes(fmt, a_q), r["a_q"])
+    ysel = yb[:, cols]
+    if fmt == ql.W8A8_INT8:
+        assert np.array_equal(ysel, r["y_ref"])
+    else:
+        st = fp8_check(fmt, r, ysel, plan.facts["chunks"])
+        assert st["ok"], st
