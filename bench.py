@@ -198,7 +198,7 @@ def main(argv=None):
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "fp8_e4m3" if fmt != 1 else "int8",
-        "data": "synthetic (seeded N(0,1) activations with 1% x20 outlier channels, N(0,%g) weights)" % wl.sigma_w,
+        "data": "synthetic (seeded N(0,1) activations with 1%% x20 outlier channels, N(0,%g) weights)" % wl.sigma_w,
         "config": {"workload": wl.name, "format": ql.FORMAT_NAMES[fmt],
                    "shapes": ["%s %dx%d" % s for s in wl.shapes], "token_counts": list(wl.ms),
                    "gemms_per_step": len(pts), "graph_replay": True, "table_entries": n_table,

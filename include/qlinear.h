@@ -109,6 +109,11 @@ typedef struct {
   int32_t rows_per_wave; /* DECODE: 16 or 32 weight rows per wave */
   int32_t prefetch;      /* DECODE: 128-wide K blocks per wave kept in flight (2 or 4) */
   int32_t a_lds;         /* DECODE: 1 = stage the activation chunk in LDS, 0 = read it per K block */
+  int32_t w_lds;         /* DECODE, row-major weights: 1 = coalesced weight loads (8 rows x 128 B
+                            per instruction) transposed to the matrix-core layout through LDS;
+                            0 = direct loads in operand order */
+  int32_t w_layout;      /* weight layout the plan reads: 0 = row-major W_q[N,K];
+                            1 = packed tiles (qlinear_pack_weight) */
   int32_t tile_m;        /* TILED: workgroup tile rows (M) */
   int32_t tile_n;        /* TILED: workgroup tile columns (N) */
 } ql_config;
@@ -154,10 +159,25 @@ ql_status qlinear_quantize_weight(int32_t fmt, const void* w_bf16, int64_t N, in
                                   void* w_q, float* w_scale, void* stream);
 
 /*
+ * Offline weight packing (optional, for the packed-weight plans).  The
+ * packed layout stores each 16-row x 128-K block of W_q as 2 KB in the order
+ * the matrix core consumes it, with a row group's blocks adjacent, so the
+ * decode kernel streams whole contiguous kilobytes per load instruction:
+ *   tile (t, kb) at byte (t * ceil(K/128) + kb) * 2048; tile byte
+ *   h*1024 + l*16 + j = W_q[16t + l%16][128kb + 64h + 16*(l/16) + j],
+ *   zero outside N x K (h in {0,1}, l in [0,64), j in [0,16)).
+ * The scales are unchanged.  qlinear_pack_weight reads w_q [N, K] (1-byte
+ * codes, row-major) and writes qlinear_packed_weight_bytes(N, K) bytes.
+ */
+int64_t qlinear_packed_weight_bytes(int64_t N, int64_t K);
+ql_status qlinear_pack_weight(const void* w_q, int64_t N, int64_t K, void* w_packed, void* stream);
+
+/*
  * Offline sweep table ([Summary] "Hybrid dispatch addresses runtime
  * overhead": per-shape, per-token-count tuned configurations).  Text file,
  * one entry per line: fmt M N K algo swap_ab split_k waves_n waves_k
- * rows_per_wave prefetch a_lds tile_m tile_n [time_us]; '#' starts a comment.
+ * rows_per_wave prefetch a_lds w_lds w_layout tile_m tile_n [time_us]; '#'
+ * starts a comment.  Entries are looked up for the weight layout asked for.
  * Loading replaces the in-process table.  Returns the entry count via n_entries.
  */
 ql_status qlinear_table_load(const char* path, int64_t* n_entries);
@@ -168,11 +188,14 @@ void qlinear_table_clear(void);
  * next tuned token bucket {1,2,4,8,16,24,32} (M > 32: the nearest tuned M at
  * or above, else the largest); without an entry a built-in heuristic is used
  * (facts.source tells which).  The environment variable QLINEAR_FORCE =
- * "algo,swap,split,wn,wk,rows,prefetch,alds,tile_m,tile_n" overrides both.
+ * "algo,swap,split,wn,wk,rows,prefetch,alds,wlds,wlayout,tile_m,tile_n"
+ * overrides both (its w_layout must match the call).
  * Host-only: no device call is made.
  */
 ql_status qlinear_plan(int32_t fmt, int64_t M, int64_t N, int64_t K, ql_plan* out_plan);
-/* Like qlinear_plan but only from the table; QL_E_NO_TABLE_ENTRY when absent. */
+/* Like qlinear_plan, for weights packed with qlinear_pack_weight. */
+ql_status qlinear_plan_packed(int32_t fmt, int64_t M, int64_t N, int64_t K, ql_plan* out_plan);
+/* Like qlinear_plan (row-major weights) but only from the table; QL_E_NO_TABLE_ENTRY when absent. */
 ql_status qlinear_plan_from_table(int32_t fmt, int64_t M, int64_t N, int64_t K, ql_plan* out_plan);
 /* Plan with an explicit configuration (validated; QL_E_INVALID / QL_E_UNSUPPORTED on a bad one). */
 ql_status qlinear_plan_with_config(int32_t fmt, int64_t M, int64_t N, int64_t K,

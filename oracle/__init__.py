@@ -36,7 +36,7 @@ from .fpbits import (bf16_bits_from_f32, bf16_bits_to_f32, ulp_bf16, f32)
 from .e4m3 import e4m3_encode, e4m3_decode, E4M3_MAX
 from .quant import (FMT_FP8_DYNAMIC, FMT_W8A8_INT8, FMT_BLOCK_FP8, FORMATS,
                     qmax_of, quantize_act, quantize_weight, dequant_codes)
-from .linear import (contract_exact, contract_abs, epilogue, reference,
+from .linear import (contract_exact, contract_abs, epilogue, reference, MATRIX_CORE_ETA,
                      tolerance_bound, summation_depth, check_fp8_parity,
                      contract_split_order, contract_swap_ab,
                      emulate_fp32_accumulation)
@@ -47,6 +47,6 @@ __all__ = [
     "FMT_FP8_DYNAMIC", "FMT_W8A8_INT8", "FMT_BLOCK_FP8", "FORMATS",
     "qmax_of", "quantize_act", "quantize_weight", "dequant_codes",
     "contract_exact", "contract_abs", "epilogue", "reference",
-    "tolerance_bound", "summation_depth", "check_fp8_parity",
+    "tolerance_bound", "summation_depth", "MATRIX_CORE_ETA", "check_fp8_parity",
     "contract_split_order", "contract_swap_ab", "emulate_fp32_accumulation",
 ]

@@ -36,6 +36,16 @@ from .quant import (FMT_BLOCK_FP8, FMT_W8A8_INT8, GROUP, dequant_codes,
 
 U32 = 2.0 ** -24    # unit roundoff of binary32
 
+# Per-instruction error allowance of a matrix-core E4M3 dot product.  The
+# pages' kernel accumulates with the matrix instruction (the listing's hl.dot
+# into an fp32 accumulator), and such an instruction does not add its 128
+# products as a chain of binary32 additions: on gfx950 the products are
+# aligned to the largest one with a limited number of bits, so one
+# instruction's result may differ from the exact sum of its products by up
+# to ~2**-12.1 of their absolute sum (measured; single products are exact).
+# The bound below allows 2**-11 of the absolute sum per instruction.
+MATRIX_CORE_ETA = 2.0 ** -11
+
 
 def _check_exact_range(fmt, K):
     if fmt == FMT_W8A8_INT8:
@@ -139,14 +149,17 @@ def summation_depth(K, split=1, waves_k=8):
     return 128 + 3 + -(-K // GROUP) + waves_k + split
 
 
-def tolerance_bound(fmt, a_q, w_q, s_a, s_w, depth):
-    """Forward-error bound B[m, n] = gamma_d * sum_k |p_k| * scales * (1 + 4u).
+def tolerance_bound(fmt, a_q, w_q, s_a, s_w, depth, eta=MATRIX_CORE_ETA):
+    """Forward-error bound B[m, n] = (gamma_d + eta) * sum_k |p_k| * scales * (1 + 4u).
 
     gamma_d = d*u / (1 - d*u) is the classic bound for a sum evaluated with at
-    most d roundings per term (u = 2**-24); the scales multiply the absolute
-    sum (Block_FP8: per group).
+    most d binary32 roundings per term (u = 2**-24); eta is the matrix-core
+    allowance per 128-product instruction (each product belongs to exactly
+    one instruction, so the per-instruction terms add up to eta times the
+    whole absolute sum).  The scales multiply the absolute sum (Block_FP8: per
+    group).  eta=0 gives the pure binary32 bound.
     """
-    gamma = depth * U32 / (1.0 - depth * U32)
+    gamma = depth * U32 / (1.0 - depth * U32) + eta
     absS = contract_abs(fmt, a_q, w_q)
     if fmt == FMT_BLOCK_FP8:
         scaled = np.sum(absS * _block_scale(s_a, s_w, w_q.shape[0]), axis=0)

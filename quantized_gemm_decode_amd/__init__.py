@@ -118,6 +118,26 @@ def quantize_weight(fmt, w, stream=None):
     return w_q, w_s
 
 
+# ----------------------------------------------------------------- packing
+
+def qlinear_packed_weight_bytes(N, K):
+    return int(lib().qlinear_packed_weight_bytes(N, K))
+
+
+def qlinear_pack_weight(w_q, w_packed, stream=None):
+    N, K = w_q.shape
+    _check(lib().qlinear_pack_weight(_ptr(w_q, "w_q", CODE_DTYPES), N, K, _ptr(w_packed, "w_packed", CODE_DTYPES),
+                                     _stream(stream)), "qlinear_pack_weight")
+
+
+def pack_weight(w_q, stream=None):
+    """Allocate the packed buffer (same code dtype, flat) and pack row-major codes into it."""
+    N, K = w_q.shape
+    out = torch.empty(qlinear_packed_weight_bytes(N, K), dtype=w_q.dtype, device=w_q.device)
+    qlinear_pack_weight(w_q, out, stream)
+    return out
+
+
 # ----------------------------------------------------------------- table
 
 def qlinear_table_load(path=DEFAULT_TABLE):
@@ -141,9 +161,12 @@ class Plan:
 
     def __del__(self):
         h = getattr(self, "handle", None)
-        if h is not None and h.value and _lib._lib is not None:
-            _lib._lib.qlinear_plan_destroy(h)
-            self.handle = None
+        try:
+            if h is not None and h.value and _lib._lib is not None:
+                _lib._lib.qlinear_plan_destroy(h)
+        except Exception:       # interpreter shutdown: module globals may be gone
+            pass
+        self.handle = None
 
     def info(self):
         cfg, facts = QLConfig(), QLPlanFacts()
@@ -177,6 +200,13 @@ def qlinear_plan(fmt, M, N, K):
     return Plan(h.value, fmt, M, N, K)
 
 
+def qlinear_plan_packed(fmt, M, N, K):
+    """Plan for weights packed with qlinear_pack_weight."""
+    h = ctypes.c_void_p()
+    _check(lib().qlinear_plan_packed(fmt, M, N, K, ctypes.byref(h)), "qlinear_plan_packed")
+    return Plan(h.value, fmt, M, N, K)
+
+
 def qlinear_plan_from_table(fmt, M, N, K):
     h = ctypes.c_void_p()
     _check(lib().qlinear_plan_from_table(fmt, M, N, K, ctypes.byref(h)), "qlinear_plan_from_table")
@@ -185,7 +215,7 @@ def qlinear_plan_from_table(fmt, M, N, K):
 
 def make_config(**kw):
     base = dict(algo=ALGO_DECODE, swap_ab=0, split_k=1, waves_n=4, waves_k=1, rows_per_wave=16, prefetch=2,
-                a_lds=1, tile_m=0, tile_n=0)
+                a_lds=1, w_lds=0, w_layout=0, tile_m=0, tile_n=0)
     unknown = set(kw) - set(base)
     if unknown:
         raise ValueError("unknown config fields %s" % sorted(unknown))
@@ -240,9 +270,12 @@ class Graph:
 
     def __del__(self):
         h = getattr(self, "handle", None)
-        if h is not None and h.value and _lib._lib is not None:
-            _lib._lib.qlinear_graph_destroy(h)
-            self.handle = None
+        try:
+            if h is not None and h.value and _lib._lib is not None:
+                _lib._lib.qlinear_graph_destroy(h)
+        except Exception:       # interpreter shutdown: module globals may be gone
+            pass
+        self.handle = None
 
 
 def qlinear_graph_begin(stream):

@@ -38,14 +38,33 @@ def hipcc():
     raise RuntimeError("hipcc not found: the HIP library cannot be built")
 
 
+def _scratch_users(remarks):
+    """Kernels whose register allocation spilled to scratch, from the resource remarks."""
+    bad, name = [], None
+    for line in remarks.splitlines():
+        if "Function Name:" in line:
+            name = line.split("Function Name:")[1].split("[")[0].strip()
+        elif "ScratchSize [bytes/lane]:" in line and name:
+            n = int(line.split("ScratchSize [bytes/lane]:")[1].split("[")[0])
+            if n > 0:
+                bad.append((name, n))
+    return bad
+
+
 def _compile(src):
     out = os.path.join(OBJ, os.path.splitext(src)[0] + ".o")
     cmd = [hipcc()] + HIPCC_FLAGS + ["-c", os.path.join(CSRC, src), "-o", out]
     if src.endswith(".cpp"):
         cmd.insert(1, "-xhip")
+    else:
+        cmd.append("-Rpass-analysis=kernel-resource-usage")
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("compile failed: %s\n%s\n%s" % (" ".join(cmd), r.stdout, r.stderr))
+    spills = _scratch_users(r.stderr)
+    if spills:
+        raise RuntimeError("%s: kernels spill registers to scratch (not allowed on the hot path): %s"
+                           % (src, spills[:4]))
     return out
 
 

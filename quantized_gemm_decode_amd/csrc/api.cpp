@@ -80,13 +80,13 @@ int64_t bucket_of(int64_t M) {
   return M;
 }
 
-bool table_lookup(int32_t fmt, int64_t M, int64_t N, int64_t K, ql_config* out) {
+bool table_lookup(int32_t fmt, int32_t layout, int64_t M, int64_t N, int64_t K, ql_config* out) {
   std::lock_guard<std::mutex> lk(g_table_mu);
   const int64_t want = bucket_of(M);
   const TableEntry* best = nullptr;
   const TableEntry* largest = nullptr;
   for (const TableEntry& e : g_table) {
-    if (e.fmt != fmt || e.N != N || e.K != K) continue;
+    if (e.fmt != fmt || e.N != N || e.K != K || e.cfg.w_layout != layout) continue;
     if (e.M >= want && (!best || e.M < best->M)) best = &e;
     if (!largest || e.M > largest->M) largest = &e;
   }
@@ -119,8 +119,9 @@ struct ql_graph_s {
 
 namespace {
 
-ql_config heuristic_config(int32_t fmt, int64_t M, int64_t N, int64_t K) {
+ql_config heuristic_config(int32_t fmt, int32_t layout, int64_t M, int64_t N, int64_t K) {
   ql_config c{};
+  c.w_layout = layout;
   c.algo = QL_ALGO_DECODE;
   c.swap_ab = 1;
   c.waves_n = 4;
@@ -136,6 +137,7 @@ ql_config heuristic_config(int32_t fmt, int64_t M, int64_t N, int64_t K) {
   const int64_t chunk_kb = (G + split - 1) / split;
   const int64_t mt = M <= 16 ? 1 : 2;
   c.a_lds = chunk_kb * mt * 2048 <= kLdsLimit ? 1 : 0;
+  c.w_lds = 0;
   (void)fmt;
   return c;
 }
@@ -148,6 +150,8 @@ ql_status build_plan(int32_t fmt, int64_t M, int64_t N, int64_t K, const ql_conf
   if (st != QL_OK) return st;
   if ((st = check_sizes(fmt, N, K, "N")) != QL_OK) return st;
   if (M * N >= (int64_t(1) << 31)) return fail(QL_E_UNSUPPORTED, "M*N exceeds 2^31");
+  if (cfg.w_layout == 1 && qlinear_packed_weight_bytes(N, K) > (int64_t(1) << 30))
+    return fail(QL_E_UNSUPPORTED, "packed weights exceed 2^30 bytes");
   if (cfg.algo != QL_ALGO_DECODE)
     return fail(QL_E_UNSUPPORTED, "algo %d is not available in this build", cfg.algo);
   if (M > 32) return fail(QL_E_UNSUPPORTED, "the decode algorithm serves M <= 32 (M=%lld)", (long long)M);
@@ -158,6 +162,9 @@ ql_status build_plan(int32_t fmt, int64_t M, int64_t N, int64_t K, const ql_conf
   if (cfg.rows_per_wave != 16 && cfg.rows_per_wave != 32) return fail(QL_E_INVALID, "rows_per_wave must be 16 or 32");
   if (cfg.prefetch != 2 && cfg.prefetch != 4) return fail(QL_E_INVALID, "prefetch must be 2 or 4");
   if (cfg.a_lds != 0 && cfg.a_lds != 1) return fail(QL_E_INVALID, "a_lds must be 0 or 1");
+  if (cfg.w_lds != 0 && cfg.w_lds != 1) return fail(QL_E_INVALID, "w_lds must be 0 or 1");
+  if (cfg.w_layout != 0 && cfg.w_layout != 1) return fail(QL_E_INVALID, "w_layout must be 0 or 1");
+  if (cfg.w_layout == 1 && cfg.w_lds) return fail(QL_E_INVALID, "w_lds applies to row-major weights only");
 
   ql_plan_s* p = new ql_plan_s();
   p->fmt = fmt;
@@ -175,16 +182,19 @@ ql_status build_plan(int32_t fmt, int64_t M, int64_t N, int64_t K, const ql_conf
   p->bn = cfg.waves_n * rg * 16;
   p->n_tiles = (int)((N + p->bn - 1) / p->bn);
   const int64_t lds_a = cfg.a_lds ? (int64_t)p->chunk_kb * p->mt * 2048 : 0;
+  const int64_t lds_w = (cfg.w_lds && !cfg.w_layout) ? (int64_t)kNW * 2 * rg * 2048 : 0;
   const int64_t lds_red = cfg.waves_k > 1 ? (int64_t)kNW * rg * p->mt * 1024 : 0;
-  p->lds = std::max(lds_a, lds_red);
+  p->lds = std::max(lds_a + lds_w, lds_red);
   if (p->lds > kLdsLimit) {
+    const long long need = (long long)p->lds;
     delete p;
     return fail(QL_E_UNSUPPORTED, "config needs %lld bytes of LDS (limit %lld); use a_lds=0 or a larger split_k",
-                (long long)std::max(lds_a, lds_red), (long long)kLdsLimit);
+                need, (long long)kLdsLimit);
   }
   p->ws_acc_bytes = p->chunks > 1 ? ((M * N * 4 + 255) / 256) * 256 : 0;
   p->ws_bytes = p->chunks > 1 ? p->ws_acc_bytes + (int64_t)p->n_tiles * 4 : 0;
-  p->key = qlk::DecodeKey{kernel_fmt(fmt), cfg.swap_ab, p->mt, rg, kNW, cfg.prefetch, cfg.a_lds};
+  const int wm = cfg.w_layout ? qlk::W_PACKED : (cfg.w_lds ? qlk::W_LDS_TRANSPOSE : qlk::W_DIRECT);
+  p->key = qlk::DecodeKey{kernel_fmt(fmt), cfg.swap_ab, p->mt, rg, kNW, cfg.prefetch, cfg.a_lds, wm};
   qlk::DecodeArgs dummy{};
   hipError_t pe;
   switch (p->key.fmt) {
@@ -203,11 +213,11 @@ ql_status build_plan(int32_t fmt, int64_t M, int64_t N, int64_t K, const ql_conf
 bool parse_force(ql_config* c) {
   const char* s = std::getenv("QLINEAR_FORCE");
   if (!s || !*s) return false;
-  int v[10];
-  if (std::sscanf(s, "%d,%d,%d,%d,%d,%d,%d,%d,%d,%d", &v[0], &v[1], &v[2], &v[3], &v[4], &v[5], &v[6], &v[7],
-                  &v[8], &v[9]) != 10)
+  int v[12];
+  if (std::sscanf(s, "%d,%d,%d,%d,%d,%d,%d,%d,%d,%d,%d,%d", &v[0], &v[1], &v[2], &v[3], &v[4], &v[5], &v[6], &v[7],
+                  &v[8], &v[9], &v[10], &v[11]) != 12)
     return false;
-  *c = ql_config{v[0], v[1], v[2], v[3], v[4], v[5], v[6], v[7], v[8], v[9]};
+  *c = ql_config{v[0], v[1], v[2], v[3], v[4], v[5], v[6], v[7], v[8], v[9], v[10], v[11]};
   return true;
 }
 
@@ -319,7 +329,8 @@ ql_status qlinear_table_load(const char* path, int64_t* n_entries) {
     long long M, N, K;
     if (!(is >> e.fmt)) continue;  // blank or comment line
     if (!(is >> M >> N >> K >> e.cfg.algo >> e.cfg.swap_ab >> e.cfg.split_k >> e.cfg.waves_n >> e.cfg.waves_k >>
-          e.cfg.rows_per_wave >> e.cfg.prefetch >> e.cfg.a_lds >> e.cfg.tile_m >> e.cfg.tile_n))
+          e.cfg.rows_per_wave >> e.cfg.prefetch >> e.cfg.a_lds >> e.cfg.w_lds >> e.cfg.w_layout >> e.cfg.tile_m >>
+          e.cfg.tile_n))
       return fail(QL_E_TABLE, "%s:%d: malformed entry", path, lineno);
     if (!(is >> e.us)) e.us = 0;
     if (!valid_fmt(e.fmt) || M < 1 || N < 1 || K < 1) return fail(QL_E_TABLE, "%s:%d: bad key", path, lineno);
@@ -341,17 +352,43 @@ void qlinear_table_clear(void) {
   g_table.clear();
 }
 
-ql_status qlinear_plan(int32_t fmt, int64_t M, int64_t N, int64_t K, ql_plan* out_plan) {
+static ql_status plan_for_layout(int32_t fmt, int32_t layout, int64_t M, int64_t N, int64_t K, ql_plan* out_plan) {
   ql_config c;
-  if (parse_force(&c)) return build_plan(fmt, M, N, K, c, QL_SRC_CUSTOM, out_plan);
-  if (table_lookup(fmt, M, N, K, &c)) return build_plan(fmt, M, N, K, c, QL_SRC_TABLE, out_plan);
-  return build_plan(fmt, M, N, K, heuristic_config(fmt, M, N, K), QL_SRC_HEURISTIC, out_plan);
+  if (parse_force(&c)) {
+    if (c.w_layout != layout) return fail(QL_E_INVALID, "QLINEAR_FORCE names another weight layout");
+    return build_plan(fmt, M, N, K, c, QL_SRC_CUSTOM, out_plan);
+  }
+  if (table_lookup(fmt, layout, M, N, K, &c)) return build_plan(fmt, M, N, K, c, QL_SRC_TABLE, out_plan);
+  return build_plan(fmt, M, N, K, heuristic_config(fmt, layout, M, N, K), QL_SRC_HEURISTIC, out_plan);
+}
+
+ql_status qlinear_plan(int32_t fmt, int64_t M, int64_t N, int64_t K, ql_plan* out_plan) {
+  return plan_for_layout(fmt, 0, M, N, K, out_plan);
+}
+
+ql_status qlinear_plan_packed(int32_t fmt, int64_t M, int64_t N, int64_t K, ql_plan* out_plan) {
+  return plan_for_layout(fmt, 1, M, N, K, out_plan);
+}
+
+int64_t qlinear_packed_weight_bytes(int64_t N, int64_t K) {
+  if (N < 0 || K < 0) return 0;
+  return ((N + 15) / 16) * ((K + 127) / 128) * 2048;
+}
+
+ql_status qlinear_pack_weight(const void* w_q, int64_t N, int64_t K, void* w_packed, void* stream) {
+  if (N < 0 || K < 0 || K % 16) return fail(QL_E_INVALID, "bad shape (N=%lld, K=%lld)", (long long)N, (long long)K);
+  if (qlinear_packed_weight_bytes(N, K) > (int64_t(1) << 30)) return fail(QL_E_UNSUPPORTED, "packed weights exceed 2^30 bytes");
+  if (N == 0 || K == 0) return QL_OK;
+  if (!w_q || !w_packed) return fail(QL_E_INVALID, "NULL pointer");
+  if (!aligned16(w_q) || !aligned16(w_packed)) return fail(QL_E_ALIGN, "pointers must be 16-byte aligned");
+  hipError_t e = qlk::launch_pack_weight(w_q, N, K, w_packed, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? QL_OK : hip_fail(e, "weight packing launch");
 }
 
 ql_status qlinear_plan_from_table(int32_t fmt, int64_t M, int64_t N, int64_t K, ql_plan* out_plan) {
   if (out_plan) *out_plan = nullptr;
   ql_config c;
-  if (!table_lookup(fmt, M, N, K, &c))
+  if (!table_lookup(fmt, 0, M, N, K, &c))
     return fail(QL_E_NO_TABLE_ENTRY, "no table entry for fmt=%d M=%lld N=%lld K=%lld", fmt, (long long)M,
                 (long long)N, (long long)K);
   return build_plan(fmt, M, N, K, c, QL_SRC_TABLE, out_plan);

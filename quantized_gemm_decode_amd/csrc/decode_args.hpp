@@ -10,6 +10,13 @@ namespace qlk {
 // Format selector of the kernels (matches ql_format's order).
 enum { FMT_FP8 = 0, FMT_INT8 = 1, FMT_BLOCK = 2 };
 
+// How the decode kernel reads the weights.
+enum {
+  W_DIRECT = 0,         // row-major W_q[N,K], loads in matrix-core operand order
+  W_LDS_TRANSPOSE = 1,  // row-major W_q[N,K], coalesced loads + LDS transpose
+  W_PACKED = 2          // packed 2 KB tiles (see launch_pack_weight)
+};
+
 struct DecodeArgs {
   const uint8_t* a;    // A_q [M, K] codes
   const float* sa;     // s_a [M] or [M, G]
@@ -36,6 +43,7 @@ struct DecodeKey {
   int nw;    // waves per workgroup
   int pf;    // K blocks per prefetch batch
   int alds;  // activations staged in LDS
+  int wm;    // weight mode: W_DIRECT / W_LDS_TRANSPOSE / W_PACKED
 };
 
 // Launch an instantiated kernel; returns hipErrorInvalidDeviceFunction when
@@ -55,5 +63,7 @@ hipError_t launch_quant_groups(const void* x, int64_t M, int64_t K, void* q, flo
 hipError_t launch_quant_wblocks(const void* w, int64_t N, int64_t K, void* q, float* s,
                                 hipStream_t st);
 hipError_t launch_fill_zero_bf16(void* y, int64_t count, hipStream_t st);
+// Row-major W_q[N,K] -> packed 2 KB tiles (zero padding to 16 rows / 128 K).
+hipError_t launch_pack_weight(const void* w_q, int64_t N, int64_t K, void* w_packed, hipStream_t st);
 
 }  // namespace qlk

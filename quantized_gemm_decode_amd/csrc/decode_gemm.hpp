@@ -43,6 +43,12 @@ struct AccOf<FMT_INT8> {
   typedef i32x4 T;
 };
 
+// 32-bit pattern of one accumulator element.  (Element values are copied to
+// a scalar first: a bit-cast applied directly to an ext-vector element
+// lvalue has been seen to read element 0 for every index.)
+__device__ __forceinline__ int bits_of(int v) { return v; }
+__device__ __forceinline__ int bits_of(float v) { return __float_as_int(v); }
+
 // Fixed epilogue order for the per-token formats: bf16(fl(fl(acc * s_a) * s_w)).
 __device__ __forceinline__ uint32_t epilogue_scaled(float accf, float sa, float sw) {
   float t = __fmul_rn(accf, sa);
@@ -50,8 +56,10 @@ __device__ __forceinline__ uint32_t epilogue_scaled(float accf, float sa, float 
   return bf16_rne(t);
 }
 
-template <int FMT, bool SWAP, int MT, int RG, int NW, int PF, bool ALDS>
+template <int FMT, bool SWAP, int MT, int RG, int NW, int PF, bool ALDS, int WM>
 __global__ void __launch_bounds__(NW * 64) qgemm_decode_kernel(DecodeArgs p) {
+  constexpr bool WL = WM == W_LDS_TRANSPOSE;
+  constexpr bool WP = WM == W_PACKED;
   using Acc = typename AccOf<FMT>::T;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   __shared__ int s_last;
@@ -73,7 +81,8 @@ __global__ void __launch_bounds__(NW * 64) qgemm_decode_kernel(DecodeArgs p) {
   const int row_base = tile * BN + wn * RG * 16;
 
   const uint32_t M = (uint32_t)p.M, N = (uint32_t)p.N, K = (uint32_t)p.K;
-  const __amdgpu_buffer_rsrc_t rw = make_rsrc(p.w, N * K);
+  const uint32_t NT16 = (N + 15u) / 16u;  // 16-row groups (tiles along N of the packed layout)
+  const __amdgpu_buffer_rsrc_t rw = make_rsrc(p.w, WP ? NT16 * (uint32_t)p.G * 2048u : N * K);
   const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.a, M * K);
 
   // Loop-invariant lane offsets.  A row past the end gets a base of 2^31:
@@ -86,6 +95,32 @@ __global__ void __launch_bounds__(NW * 64) qgemm_decode_kernel(DecodeArgs p) {
     const uint32_t row = (uint32_t)(row_base + rg * 16 + r16);
     wbase[rg] = row < N ? row * K + glo : OOB;
   }
+  // WL (coalesced weight stream): the two loads of a (row group, K block)
+  // each cover 8 whole rows x 128 bytes -- lane l takes row 8*i + l/8 and
+  // 16-byte chunk l%8 -- and an LDS transpose hands the matrix core its
+  // operand layout afterwards.
+  const uint32_t c16 = (uint32_t)(lane & 7) * 16u;
+  uint32_t wbase_c[RG][2];
+#pragma unroll
+  for (int rg = 0; rg < RG; ++rg)
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const uint32_t row = (uint32_t)(row_base + rg * 16 + 8 * i + (lane >> 3));
+      wbase_c[rg][i] = row < N ? row * K + c16 : OOB;
+    }
+  // WP (packed tiles): tile (t, kb) is 2 KB at (t*G + kb)*2048 holding exactly
+  // the two 16-byte pieces every lane feeds the matrix core, lane l's `lo` at
+  // l*16 and `hi` at 1024 + l*16; padding rows / K are zeros in the tile.
+  uint32_t wbase_p[RG];
+#pragma unroll
+  for (int rg = 0; rg < RG; ++rg) {
+    const uint32_t t = (uint32_t)(row_base / 16 + rg);
+    wbase_p[rg] = t < NT16 ? t * (uint32_t)p.G * 2048u + (uint32_t)lane * 16u : OOB;
+  }
+  // LDS slots of the transpose: 2 per wave, each RG x 2 KB, after the
+  // staged activations.
+  const int wl_base = (ALDS ? p.chunk_kb * MT * 2048 : 0) + wave * (2 * RG * 2048);
+
   uint32_t abase[MT];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
@@ -127,10 +162,26 @@ __global__ void __launch_bounds__(NW * 64) qgemm_decode_kernel(DecodeArgs p) {
       const uint32_t rem = ok ? K - kofs : 0u;
       const bool lo_ok = glo < rem;
       const bool hi_ok = glo + 64u < rem;
+      if constexpr (WP) {
+        const uint32_t tofs = (uint32_t)kb * 2048u;
 #pragma unroll
-      for (int rg = 0; rg < RG; ++rg) {
-        wb[q][rg].lo = bload16(rw, lo_ok ? wbase[rg] + kofs : OOB);
-        wb[q][rg].hi = bload16(rw, hi_ok ? wbase[rg] + kofs + 64u : OOB);
+        for (int rg = 0; rg < RG; ++rg) {
+          wb[q][rg].lo = bload16_nt(rw, ok ? wbase_p[rg] + tofs : OOB);
+          wb[q][rg].hi = bload16_nt(rw, ok ? wbase_p[rg] + tofs + 1024u : OOB);
+        }
+      } else if constexpr (WL) {
+        const bool c_ok = c16 < rem;
+#pragma unroll
+        for (int rg = 0; rg < RG; ++rg) {
+          wb[q][rg].lo = bload16(rw, c_ok ? wbase_c[rg][0] + kofs : OOB);
+          wb[q][rg].hi = bload16(rw, c_ok ? wbase_c[rg][1] + kofs : OOB);
+        }
+      } else {
+#pragma unroll
+        for (int rg = 0; rg < RG; ++rg) {
+          wb[q][rg].lo = bload16(rw, lo_ok ? wbase[rg] + kofs : OOB);
+          wb[q][rg].hi = bload16(rw, hi_ok ? wbase[rg] + kofs + 64u : OOB);
+        }
       }
       if constexpr (!ALDS) {
 #pragma unroll
@@ -178,24 +229,44 @@ __global__ void __launch_bounds__(NW * 64) qgemm_decode_kernel(DecodeArgs p) {
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) af[mt] = ab[q][mt];
       }
+      // Weight operands.  WL: write the 8-row x 128-byte pieces to this wave's
+      // LDS slot (16-byte chunk c of row r at r*128 + (c ^ (r/2 % 8))*16, a
+      // swizzle that keeps both the writes and the operand reads free of bank
+      // conflicts), then read row l%16, chunks l/16 and 4 + l/16 back.
+      Frag wf[RG];
+#pragma unroll
+      for (int rg = 0; rg < RG; ++rg) {
+        if constexpr (WL) {
+          uint8_t* slot = smem + wl_base + (q & 1) * (RG * 2048) + rg * 2048;
+          const int wr0 = lane >> 3, wc = lane & 7;
+          *reinterpret_cast<u32x4*>(slot + wr0 * 128 + ((wc ^ ((wr0 >> 1) & 7)) << 4)) = wb[q][rg].lo;
+          const int wr1 = 8 + wr0;
+          *reinterpret_cast<u32x4*>(slot + wr1 * 128 + ((wc ^ ((wr1 >> 1) & 7)) << 4)) = wb[q][rg].hi;
+          const int sw = (r16 >> 1) & 7;
+          wf[rg].lo = *reinterpret_cast<const u32x4*>(slot + r16 * 128 + ((g ^ sw) << 4));
+          wf[rg].hi = *reinterpret_cast<const u32x4*>(slot + r16 * 128 + (((4 + g) ^ sw) << 4));
+        } else {
+          wf[rg] = wb[q][rg];
+        }
+      }
 #pragma unroll
       for (int rg = 0; rg < RG; ++rg) {
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
           if constexpr (FMT == FMT_INT8) {
             if (SWAP) {
-              acc[rg][mt] = mma_i8(wb[q][rg].lo, af[mt].lo, acc[rg][mt]);
-              acc[rg][mt] = mma_i8(wb[q][rg].hi, af[mt].hi, acc[rg][mt]);
+              acc[rg][mt] = mma_i8(wf[rg].lo, af[mt].lo, acc[rg][mt]);
+              acc[rg][mt] = mma_i8(wf[rg].hi, af[mt].hi, acc[rg][mt]);
             } else {
-              acc[rg][mt] = mma_i8(af[mt].lo, wb[q][rg].lo, acc[rg][mt]);
-              acc[rg][mt] = mma_i8(af[mt].hi, wb[q][rg].hi, acc[rg][mt]);
+              acc[rg][mt] = mma_i8(af[mt].lo, wf[rg].lo, acc[rg][mt]);
+              acc[rg][mt] = mma_i8(af[mt].hi, wf[rg].hi, acc[rg][mt]);
             }
           } else if constexpr (FMT == FMT_FP8) {
-            acc[rg][mt] = SWAP ? mma_f8(wb[q][rg], af[mt], acc[rg][mt])
-                               : mma_f8(af[mt], wb[q][rg], acc[rg][mt]);
+            acc[rg][mt] = SWAP ? mma_f8(wf[rg], af[mt], acc[rg][mt])
+                               : mma_f8(af[mt], wf[rg], acc[rg][mt]);
           } else {
             const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-            const f32x4 part = SWAP ? mma_f8(wb[q][rg], af[mt], z) : mma_f8(af[mt], wb[q][rg], z);
+            const f32x4 part = SWAP ? mma_f8(wf[rg], af[mt], z) : mma_f8(af[mt], wf[rg], z);
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
               const float f = sab[q][mt][SWAP ? 0 : r] * swb[q][rg];
@@ -212,6 +283,26 @@ __global__ void __launch_bounds__(NW * 64) qgemm_decode_kernel(DecodeArgs p) {
   // refilled right after it has been consumed.
   issue(wb0, ab0, sa0, sw0, 0);
   issue(wb1, ab1, sa1, sw1, 1);
+
+  // Scales of the per-token formats, loaded now so that their latency hides
+  // under the weight stream instead of stalling the epilogue.
+  float esa[MT][4], esw[RG][4];
+  if constexpr (FMT != FMT_BLOCK) {
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const uint32_t m = SWAP ? (uint32_t)(mt * 16 + r16) : (uint32_t)(mt * 16 + 4 * g + r);
+        esa[mt][r] = (SWAP && r > 0) ? 0.f : bload_f32(rsa, m < M ? m * 4u : OOB);
+      }
+#pragma unroll
+    for (int rg = 0; rg < RG; ++rg)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const uint32_t n = SWAP ? (uint32_t)(row_base + rg * 16 + 4 * g + r) : (uint32_t)(row_base + rg * 16 + r16);
+        esw[rg][r] = (!SWAP && r > 0) ? 0.f : bload_f32(rsw, n < N ? n * 4u : OOB);
+      }
+  }
 
   // ---- stage this chunk's activations in LDS (after the first weight
   // batches are in flight, so their HBM latency overlaps the staging): one 1 KB block per
@@ -252,7 +343,7 @@ __global__ void __launch_bounds__(NW * 64) qgemm_decode_kernel(DecodeArgs p) {
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const int i = (rg * MT + mt) * 4 + r;
-            red[(wave * NACC + i) * 64 + lane] = __builtin_bit_cast(int, acc[rg][mt][r]);
+            red[(wave * NACC + i) * 64 + lane] = bits_of(acc[rg][mt][r]);
           }
     }
     __syncthreads();
@@ -269,7 +360,7 @@ __global__ void __launch_bounds__(NW * 64) qgemm_decode_kernel(DecodeArgs p) {
               if constexpr (FMT == FMT_INT8)
                 acc[rg][mt][r] += v;
               else
-                acc[rg][mt][r] += __builtin_bit_cast(float, v);
+                acc[rg][mt][r] += __int_as_float(v);
             }
       }
     }
@@ -297,16 +388,20 @@ __global__ void __launch_bounds__(NW * 64) qgemm_decode_kernel(DecodeArgs p) {
             }
           }
     }
-    __threadfence();
+    // Every access to the workspace and the counters is a device-scope atomic
+    // read-modify-write, which the hardware performs at a point coherent for
+    // all XCDs, so no L2 write-back / invalidate (an agent-scope fence) is
+    // needed -- only that this workgroup's adds have completed before its
+    // arrival is counted: wait for every outstanding memory operation.
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     if (tid == 0) {
-      const unsigned prev = __hip_atomic_fetch_add(p.counters + tile, 1u, __ATOMIC_ACQ_REL,
+      const unsigned prev = __hip_atomic_fetch_add(p.counters + tile, 1u, __ATOMIC_RELAXED,
                                                    __HIP_MEMORY_SCOPE_AGENT);
       s_last = (prev == (unsigned)(p.split - 1));
     }
     __syncthreads();
     if (!s_last) return;
-    __threadfence();
     if (wk == 0) {
 #pragma unroll
       for (int rg = 0; rg < RG; ++rg)
@@ -323,11 +418,11 @@ __global__ void __launch_bounds__(NW * 64) qgemm_decode_kernel(DecodeArgs p) {
               if constexpr (FMT == FMT_INT8)
                 acc[rg][mt][r] = v;
               else
-                acc[rg][mt][r] = __builtin_bit_cast(float, v);
+                acc[rg][mt][r] = __int_as_float(v);
             }
           }
     }
-    if (tid == 0) __hip_atomic_store(p.counters + tile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (tid == 0) __hip_atomic_exchange(p.counters + tile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 
   if (wk != 0) return;
@@ -350,8 +445,8 @@ __global__ void __launch_bounds__(NW * 64) qgemm_decode_kernel(DecodeArgs p) {
           if (ok && p.acc_out)
             reinterpret_cast<float*>(p.acc_out)[(size_t)mm[r] * N + nn[r]] = acc[rg][mt][r];
         } else {
-          const float sa = ok ? p.sa[mm[r]] : 0.f;
-          const float sw = ok ? p.sw[nn[r]] : 0.f;
+          const float sa = esa[mt][SWAP ? 0 : r];
+          const float sw = esw[rg][SWAP ? r : 0];
           float accf;
           if constexpr (FMT == FMT_INT8)
             accf = __int2float_rn(acc[rg][mt][r]);
@@ -378,27 +473,53 @@ __global__ void __launch_bounds__(NW * 64) qgemm_decode_kernel(DecodeArgs p) {
   }
 }
 
-// Instantiation table for one format: every (swap, mt, rg, nw, pf, alds)
-// combination the planner may choose.
+// Instantiation table for one format: every (swap, mt, rg, pf, alds, weight mode)
+// combination the planner may choose.  Combinations whose registers would
+// spill (two token tiles with 32 rows per wave and four-block batches, and
+// for Block_FP8 the four-block batches of the standard orientation) are not
+// instantiated: the planner rejects them.
+template <int FMT, int SW, int MT_, int RG_, int PF_>
+constexpr bool decode_config_fits() {
+  if (MT_ == 2 && RG_ == 2 && PF_ == 4) return false;
+  if (FMT == FMT_BLOCK && MT_ == 2 && PF_ == 4 && !SW) return false;
+  return true;
+}
+
+template <int FMT, int SW, int MT_, int RG_, int PF_, int AL, int WM_>
+hipError_t decode_try(const DecodeKey& k, dim3 grid, dim3 block, size_t lds, hipStream_t s, const DecodeArgs& a,
+                      bool probe_only, bool* hit) {
+  if constexpr (decode_config_fits<FMT, SW, MT_, RG_, PF_>()) {
+    if (k.swap == SW && k.mt == MT_ && k.rg == RG_ && k.nw == 4 && k.pf == PF_ && k.alds == AL && k.wm == WM_) {
+      *hit = true;
+      if (probe_only) return hipSuccess;
+      qgemm_decode_kernel<FMT, SW != 0, MT_, RG_, 4, PF_, AL != 0, WM_><<<grid, block, lds, s>>>(a);
+      return hipGetLastError();
+    }
+  }
+  return hipSuccess;
+}
+
 template <int FMT>
 hipError_t decode_dispatch(const DecodeKey& k, dim3 grid, dim3 block, size_t lds, hipStream_t s,
                            const DecodeArgs& a, bool probe_only) {
-#define QL_TRY(SW, MT_, RG_, NW_, PF_, AL)                                                         \
-  if (k.swap == SW && k.mt == MT_ && k.rg == RG_ && k.nw == NW_ && k.pf == PF_ && k.alds == AL) { \
-    if (probe_only) return hipSuccess;                                                            \
-    qgemm_decode_kernel<FMT, SW, MT_, RG_, NW_, PF_, AL><<<grid, block, lds, s>>>(a);             \
-    return hipGetLastError();                                                                     \
-  }
-#define QL_TRY_AL(SW, MT_, RG_, NW_, PF_) QL_TRY(SW, MT_, RG_, NW_, PF_, 0) QL_TRY(SW, MT_, RG_, NW_, PF_, 1)
-#define QL_TRY_PF(SW, MT_, RG_, NW_) QL_TRY_AL(SW, MT_, RG_, NW_, 2) QL_TRY_AL(SW, MT_, RG_, NW_, 4)
-#define QL_TRY_RG(SW, MT_, NW_) QL_TRY_PF(SW, MT_, 1, NW_) QL_TRY_PF(SW, MT_, 2, NW_)
-#define QL_TRY_MT(SW, NW_) QL_TRY_RG(SW, 1, NW_) QL_TRY_RG(SW, 2, NW_)
-  QL_TRY_MT(false, 4)
-  QL_TRY_MT(true, 4)
+  bool hit = false;
+  hipError_t e = hipSuccess;
+#define QL_TRY(SW, MT_, RG_, PF_, AL, WM_)                                                       \
+  e = decode_try<FMT, SW, MT_, RG_, PF_, AL, WM_>(k, grid, block, lds, s, a, probe_only, &hit); \
+  if (hit) return e;
+#define QL_TRY_WL(SW, MT_, RG_, PF_, AL) \
+  QL_TRY(SW, MT_, RG_, PF_, AL, 0) QL_TRY(SW, MT_, RG_, PF_, AL, 1) QL_TRY(SW, MT_, RG_, PF_, AL, 2)
+#define QL_TRY_AL(SW, MT_, RG_, PF_) QL_TRY_WL(SW, MT_, RG_, PF_, 0) QL_TRY_WL(SW, MT_, RG_, PF_, 1)
+#define QL_TRY_PF(SW, MT_, RG_) QL_TRY_AL(SW, MT_, RG_, 2) QL_TRY_AL(SW, MT_, RG_, 4)
+#define QL_TRY_RG(SW, MT_) QL_TRY_PF(SW, MT_, 1) QL_TRY_PF(SW, MT_, 2)
+#define QL_TRY_MT(SW) QL_TRY_RG(SW, 1) QL_TRY_RG(SW, 2)
+  QL_TRY_MT(0)
+  QL_TRY_MT(1)
 #undef QL_TRY_MT
 #undef QL_TRY_RG
 #undef QL_TRY_PF
 #undef QL_TRY_AL
+#undef QL_TRY_WL
 #undef QL_TRY
   return hipErrorInvalidDeviceFunction;
 }

@@ -162,6 +162,31 @@ __global__ void fill_zero_u16_kernel(uint16_t* p, size_t n) {
     p[i] = 0;
 }
 
+// Packed weight tiles: tile (t, kb) -- rows 16t..16t+15, K bytes 128kb..128kb+127 --
+// is 2 KB at (t*G + kb)*2048; byte h*1024 + l*16 + j of the tile is
+// W[16t + l%16][128kb + 64h + 16(l/16) + j] (zero outside N x K).  One thread
+// moves one 16-byte piece; K % 16 == 0 keeps every piece wholly in or out.
+__global__ void __launch_bounds__(256) pack_weight_kernel(const uint8_t* __restrict__ w, uint32_t N, uint32_t K,
+                                                          uint32_t G, uint32_t pieces, uint8_t* __restrict__ out) {
+  const uint32_t pc = blockIdx.x * 256u + threadIdx.x;
+  if (pc >= pieces) return;
+  const uint32_t l = pc & 63u, h = (pc >> 6) & 1u, tk = pc >> 7;
+  const uint32_t kb = tk % G, t = tk / G;
+  const uint32_t row = t * 16u + (l & 15u);
+  const uint32_t k = kb * 128u + h * 64u + (l >> 4) * 16u;
+  u32x4 v = {0, 0, 0, 0};
+  if (row < N && k < K) v = *reinterpret_cast<const u32x4*>(w + (size_t)row * K + k);
+  *reinterpret_cast<u32x4*>(out + (size_t)pc * 16u) = v;
+}
+
+hipError_t launch_pack_weight(const void* w_q, int64_t N, int64_t K, void* w_packed, hipStream_t st) {
+  const uint32_t NT = (uint32_t)((N + 15) / 16), G = (uint32_t)((K + 127) / 128);
+  const uint32_t pieces = NT * G * 128u;
+  pack_weight_kernel<<<dim3((pieces + 255u) / 256u), dim3(256), 0, st>>>(
+      static_cast<const uint8_t*>(w_q), (uint32_t)N, (uint32_t)K, G, pieces, static_cast<uint8_t*>(w_packed));
+  return hipGetLastError();
+}
+
 template <int FMT>
 static hipError_t rows_dispatch(const void* x, int64_t R, int64_t C, void* q, float* s, hipStream_t st) {
   const uint16_t* xp = static_cast<const uint16_t*>(x);

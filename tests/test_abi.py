@@ -73,6 +73,12 @@ def test_host_validation_status_codes():
     assert _plan_status(ql.FP8_DYNAMIC, 8, 4096, 2048, rows_per_wave=48) == QL_E_INVALID
     assert _plan_status(ql.FP8_DYNAMIC, 8, 4096, 2048, prefetch=3) == QL_E_INVALID
     assert _plan_status(ql.FP8_DYNAMIC, 8, 4096, 2048, swap_ab=2) == QL_E_INVALID
+    assert _plan_status(ql.FP8_DYNAMIC, 8, 4096, 2048, w_lds=2) == QL_E_INVALID
+    assert _plan_status(ql.FP8_DYNAMIC, 8, 4096, 2048, w_layout=2) == QL_E_INVALID
+    assert _plan_status(ql.FP8_DYNAMIC, 8, 4096, 2048, w_layout=1, w_lds=1) == QL_E_INVALID
+    assert _plan_status(ql.FP8_DYNAMIC, 8, 4096, 2048, w_layout=1) == QL_OK
+    # configurations that would spill registers are not instantiated
+    assert _plan_status(ql.FP8_DYNAMIC, 32, 4096, 2048, rows_per_wave=32, prefetch=4) == QL_E_UNSUPPORTED
     # the LDS-staged activation chunk must fit the 64 KB budget
     assert _plan_status(ql.FP8_DYNAMIC, 32, 4096, 25600, split_k=1, a_lds=1) == QL_E_UNSUPPORTED
     assert _plan_status(ql.FP8_DYNAMIC, 32, 4096, 25600, split_k=1, a_lds=0) == QL_OK
@@ -121,25 +127,30 @@ def test_plan_facts_and_workspace_sizes():
 
 def test_table_lookup_buckets_and_force(tmp_path):
     t = tmp_path / "t.txt"
-    t.write_text("# fmt M N K algo swap split wn wk rows pf alds tm tn us\n"
-                 "0 8 4096 4096 0 1 4 4 1 16 2 1 0 0 3.1\n"
-                 "0 32 4096 4096 0 0 2 2 2 32 4 1 0 0 3.3\n"
+    t.write_text("# fmt M N K algo swap split wn wk rows pf alds wlds wlayout tm tn us\n"
+                 "0 8 4096 4096 0 1 4 4 1 16 2 1 0 0 0 0 3.1\n"
+                 "0 32 4096 4096 0 0 4 2 2 32 2 1 1 0 0 0 3.3\n"
+                 "0 8 4096 4096 0 0 2 1 4 16 2 0 0 1 0 0 2.2\n"
                  "\n")
-    assert ql.qlinear_table_load(str(t)) == 2
+    assert ql.qlinear_table_load(str(t)) == 3
     try:
         p = ql.qlinear_plan(ql.FP8_DYNAMIC, 5, 4096, 4096)           # bucket 8
         assert p.facts["source"] == "table" and p.config["swap_ab"] == 1 and p.config["split_k"] == 4
         p = ql.qlinear_plan(ql.FP8_DYNAMIC, 17, 4096, 4096)          # bucket 24 -> nearest tuned >= : 32
-        assert p.config["waves_k"] == 2 and p.config["prefetch"] == 4
+        assert p.config["waves_k"] == 2 and p.config["w_lds"] == 1
         p = ql.qlinear_plan(ql.FP8_DYNAMIC, 8, 4096, 2048)           # other K: heuristic
         assert p.facts["source"] == "heuristic"
+        p = ql.qlinear_plan_packed(ql.FP8_DYNAMIC, 3, 4096, 4096)    # packed-layout entry
+        assert p.facts["source"] == "table" and p.config["w_layout"] == 1 and p.config["waves_k"] == 4
+        p = ql.qlinear_plan_packed(ql.FP8_DYNAMIC, 32, 4096, 4096)   # no packed entry at/above 32
+        assert p.facts["source"] == "heuristic" and p.config["w_layout"] == 1
         with pytest.raises(ql.QLinearError) as e:
             ql.qlinear_plan_from_table(ql.W8A8_INT8, 8, 4096, 4096)
         assert e.value.status == QL_E_NO_TABLE_ENTRY
-        os.environ["QLINEAR_FORCE"] = "0,0,2,1,4,16,4,0,0,0"
+        os.environ["QLINEAR_FORCE"] = "0,0,2,1,4,16,4,0,1,0,0,0"
         try:
             p = ql.qlinear_plan(ql.FP8_DYNAMIC, 8, 4096, 4096)
-            assert p.facts["source"] == "custom" and p.config["waves_k"] == 4
+            assert p.facts["source"] == "custom" and p.config["waves_k"] == 4 and p.config["w_lds"] == 1
         finally:
             del os.environ["QLINEAR_FORCE"]
     finally:
@@ -151,6 +162,15 @@ def test_table_lookup_buckets_and_force(tmp_path):
     assert e.value.status == QL_E_TABLE
     with pytest.raises(ql.QLinearError):
         ql.qlinear_table_load(str(tmp_path / "missing.txt"))
+
+
+def test_packed_weight_sizes():
+    assert ql.qlinear_packed_weight_bytes(4096, 4096) == 4096 * 4096
+    assert ql.qlinear_packed_weight_bytes(300, 1040) == 19 * 9 * 2048
+    assert ql.qlinear_packed_weight_bytes(0, 128) == 0
+    v = ctypes.c_void_p
+    assert ql.lib().qlinear_pack_weight(v(16), 10, 100, v(16), v(0)) == QL_E_INVALID     # K % 16
+    assert ql.lib().qlinear_pack_weight(v(8), 10, 128, v(16), v(0)) == QL_E_ALIGN
 
 
 def test_heuristic_plans_cover_every_decode_workload():

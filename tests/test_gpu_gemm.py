@@ -40,9 +40,10 @@ def _assert_parity(fmt, r, y, acc, split, label=""):
         return
     st = fp8_check(fmt, r, y, split)
     assert st["ok"], (label, st)
+    assert st["frac_within_ulp"] >= 0.95, (label, st)
     K = r["a_q"].shape[1]
     d = oracle.summation_depth(K, split=split)
-    gamma = d * 2.0 ** -24 / (1 - d * 2.0 ** -24)
+    gamma = d * 2.0 ** -24 / (1 - d * 2.0 ** -24) + oracle.MATRIX_CORE_ETA
     if fmt == ql.FP8_DYNAMIC:
         bound = gamma * oracle.contract_abs(fmt, r["a_q"], r["w_q"])
         assert np.all(np.abs(acc.astype(np.float64) - r["S"]) <= bound), label
@@ -51,8 +52,10 @@ def _assert_parity(fmt, r, y, acc, split, label=""):
         assert np.all(np.abs(acc.astype(np.float64) - r["y_true"]) <= B + 1e-30), label
 
 
-# every kernel instantiation: swap x rows/wave x prefetch x LDS staging, both token tiles
-VARIANTS = list(itertools.product([0, 1], [16, 32], [2, 4], [0, 1]))
+# every kernel instantiation: swap x rows/wave x prefetch x activation LDS staging x weight mode
+# (0 row-major direct, 1 row-major through the LDS transpose, 2 packed tiles), both token tiles
+# (instantiations that would spill registers do not exist)
+VARIANTS = list(itertools.product([0, 1], [16, 32], [2, 4], [0, 1], [0, 1, 2]))
 SPLITS = [1, 2, 4, 8]
 WAVES_K = [1, 2, 4]
 
@@ -61,16 +64,24 @@ WAVES_K = [1, 2, 4]
 @pytest.mark.parametrize("M", [5, 29])
 @pytest.mark.parametrize("vi", range(len(VARIANTS)))
 def test_every_instantiation_matches_oracle(fmt, M, vi):
-    swap, rows, pf, alds = VARIANTS[vi]
+    swap, rows, pf, alds, wmode = VARIANTS[vi]
     split = SPLITS[(vi + M) % len(SPLITS)]
     wk = WAVES_K[(vi // 2 + M) % len(WAVES_K)]
     N = 300 if rows == 16 else 520                      # several tiles + a ragged tail
     K = 1152 if fmt == ql.BLOCK_FP8 or vi % 3 else 1040  # 1040: ragged last K block
     r = _ref(fmt, M, N, K, seed=vi * 7 + M)
     cfg = dict(swap_ab=swap, split_k=split, waves_n=4 // wk, waves_k=wk, rows_per_wave=rows, prefetch=pf,
-               a_lds=alds)
-    plan = ql.qlinear_plan_with_config(fmt, M, N, K, cfg)
-    y, acc, ws = run_gemm(plan, *_dev(fmt, r))
+               a_lds=alds, w_lds=int(wmode == 1), w_layout=int(wmode == 2))
+    try:
+        plan = ql.qlinear_plan_with_config(fmt, M, N, K, cfg)
+    except ql.QLinearError as e:
+        spill = M > 16 and rows == 32 and pf == 4 or (fmt == ql.BLOCK_FP8 and M > 16 and pf == 4 and not swap)
+        assert e.status == 2 and (spill or "LDS" in str(e)), e
+        pytest.skip("configuration not available: %s" % e)
+    a_q, s_a, w_q, s_w = _dev(fmt, r)
+    if wmode == 2:
+        w_q = ql.pack_weight(w_q)
+    y, acc, ws = run_gemm(plan, a_q, s_a, w_q, s_w)
     _assert_parity(fmt, r, y, acc, plan.facts["chunks"], label=str(cfg))
     if ws is not None:
         assert int(torch.count_nonzero(ws)) == 0, "split-K workspace not left all-zero"
@@ -83,10 +94,50 @@ def test_token_counts_and_tiles(fmt, M):
     r = _ref(fmt, M, N, K, seed=M)
     for cfg in (dict(swap_ab=0, split_k=1, waves_n=1, waves_k=4, a_lds=0),
                 dict(swap_ab=1, split_k=4, waves_n=2, waves_k=2, rows_per_wave=32, a_lds=1),
-                dict(swap_ab=1, split_k=16, waves_n=4, waves_k=1, prefetch=4, a_lds=1)):
+                dict(swap_ab=1, split_k=16, waves_n=4, waves_k=1, prefetch=4, a_lds=1, w_lds=1),
+                dict(swap_ab=0, split_k=1, waves_n=1, waves_k=4, rows_per_wave=32, a_lds=0, w_lds=1)):
         plan = ql.qlinear_plan_with_config(fmt, M, N, K, cfg)
         y, acc, _ = run_gemm(plan, *_dev(fmt, r))
         _assert_parity(fmt, r, y, acc, plan.facts["chunks"], label=str(cfg))
+
+
+def _pack_ref(q):
+    """The packed tile layout, restated from its definition: tile (t, kb) holds rows 16t.., K bytes
+    128kb..; tile byte h*1024 + l*16 + j = W[16t + l%16][128kb + 64h + 16(l//16) + j], zero padded."""
+    q = np.ascontiguousarray(q).view(np.uint8)
+    N, K = q.shape
+    NT, G = -(-N // 16), -(-K // 128)
+    pad = np.zeros((NT * 16, G * 128), np.uint8)
+    pad[:N, :K] = q
+    arr = pad.reshape(NT, 16, G, 128)
+    out = np.zeros((NT, G, 2, 64, 16), np.uint8)
+    for h in range(2):
+        for g in range(4):
+            out[:, :, h, 16 * g:16 * g + 16, :] = arr[:, :, :, 64 * h + 16 * g:64 * h + 16 * g + 16].transpose(0, 2, 1, 3)
+    return out.reshape(-1)
+
+
+@pytest.mark.parametrize("N,K", [(300, 1040), (16, 128), (4096, 4096), (33, 16), (1, 2064)])
+def test_pack_weight_matches_layout_definition(N, K):
+    rng = np.random.default_rng(N + K)
+    q = rng.integers(-127, 128, (N, K)).astype(np.int8)
+    packed = ql.pack_weight(torch.from_numpy(q).cuda())
+    torch.cuda.synchronize()
+    assert packed.numel() == ql.qlinear_packed_weight_bytes(N, K)
+    assert np.array_equal(packed.cpu().numpy().view(np.uint8), _pack_ref(q))
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("M", [1, 8, 32])
+def test_packed_plans_match_row_major(fmt, M):
+    """Heuristic / table plans for packed weights agree with the oracle on a multi-tile ragged shape."""
+    N, K = 1000, 3072 if fmt == ql.BLOCK_FP8 else 3088
+    r = _ref(fmt, M, N, K, seed=M + 40)
+    a_q, s_a, w_q, s_w = _dev(fmt, r)
+    plan = ql.qlinear_plan_packed(fmt, M, N, K)
+    assert plan.config["w_layout"] == 1
+    y, acc, ws = run_gemm(plan, a_q, s_a, ql.pack_weight(w_q), s_w)
+    _assert_parity(fmt, r, y, acc, plan.facts["chunks"], label=str(plan.config))
 
 
 def test_int8_all_variants_bitwise_identical_and_deterministic():
@@ -94,16 +145,20 @@ def test_int8_all_variants_bitwise_identical_and_deterministic():
     r = _ref(ql.W8A8_INT8, M, N, K, seed=99)
     d = _dev(ql.W8A8_INT8, r)
     outs = []
-    for swap, split, wk, rows, alds in itertools.product([0, 1], [1, 8, 32], [1, 4], [16, 32], [0, 1]):
-        cfg = dict(swap_ab=swap, split_k=split, waves_n=4 // wk, waves_k=wk, rows_per_wave=rows, a_lds=alds)
+    packed = ql.pack_weight(d[2])
+    for swap, split, wk, rows, alds, wmode in itertools.product([0, 1], [1, 8, 32], [1, 4], [16, 32], [0, 1],
+                                                                [0, 1, 2]):
+        cfg = dict(swap_ab=swap, split_k=split, waves_n=4 // wk, waves_k=wk, rows_per_wave=rows, a_lds=alds,
+                   w_lds=int(wmode == 1), w_layout=int(wmode == 2))
         try:
             plan = ql.qlinear_plan_with_config(ql.W8A8_INT8, M, N, K, cfg)
         except ql.QLinearError:
             continue
+        args = (d[0], d[1], packed if wmode == 2 else d[2], d[3])
         for _ in range(2):
-            y, _, _ = run_gemm(plan, *d, acc=False)
+            y, _, _ = run_gemm(plan, *args, acc=False)
             outs.append(y)
-    assert len(outs) >= 40
+    assert len(outs) >= 100
     for y in outs[1:]:
         assert np.array_equal(y, outs[0])
     assert np.array_equal(outs[0], r["y_ref"])
@@ -229,12 +284,14 @@ def test_full_size_workloads_sampled_columns(ci, lab, N, K, M):
     ql.load_default_table()
     x, w, w_q, w_s = _weights(ci, lab, N, K)
     xm = x[:M]
-    plan = ql.qlinear_plan(fmt, M, N, K)
     a_q, a_s = ql.quantize_act(fmt, xm.cuda())
-    y = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
-    ql.qlinear_run(plan, a_q, a_s, w_q, w_s, y, plan.new_workspace())
-    torch.cuda.synchronize()
-    yb = host_bf16_bits(y)
+    ys = []
+    for packed in (False, True):
+        plan = ql.qlinear_plan_packed(fmt, M, N, K) if packed else ql.qlinear_plan(fmt, M, N, K)
+        y = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
+        ql.qlinear_run(plan, a_q, a_s, ql.pack_weight(w_q) if packed else w_q, w_s, y, plan.new_workspace())
+        torch.cuda.synchronize()
+        ys.append((plan, host_bf16_bits(y)))
     rng = np.random.default_rng(ci * 1000 + M)
     if fmt == ql.BLOCK_FP8:
         nbs = rng.choice(-(-N // 128), 2, replace=False)
@@ -243,9 +300,10 @@ def test_full_size_workloads_sampled_columns(ci, lab, N, K, M):
         cols = np.sort(rng.choice(N, 96, replace=False))
     r = oracle.reference(fmt, bf16_bits(xm), bf16_bits(w[torch.from_numpy(cols)]))
     assert np.array_equal(host_codes(fmt, a_q), r["a_q"])
-    ysel = yb[:, cols]
-    if fmt == ql.W8A8_INT8:
-        assert np.array_equal(ysel, r["y_ref"])
-    else:
-        st = fp8_check(fmt, r, ysel, plan.facts["chunks"])
-        assert st["ok"], st
+    for plan, yb in ys:
+        ysel = yb[:, cols]
+        if fmt == ql.W8A8_INT8:
+            assert np.array_equal(ysel, r["y_ref"]), plan.config
+        else:
+            st = fp8_check(fmt, r, ysel, plan.facts["chunks"])
+            assert st["ok"] and st["frac_within_ulp"] >= 0.95, (plan.config, st)
