@@ -47,6 +47,8 @@ def parse_args(argv=None):
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="fp8_dynamic_8b")
+    ap.add_argument("--layout", choices=("packed", "rowmajor"), default="packed",
+                    help="weight layout: packed tiles (qlinear_pack_weight, offline) or row-major W_q[N,K]")
     ap.add_argument("--kernel-reps", type=int, default=30, help="graph replays per point for kernel timing")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=20.0)
@@ -87,6 +89,8 @@ def main(argv=None):
         x, w = make_inputs(K, N, max(wl.ms), wl.sigma_w, seed=wl.seed)
         wd = w.to(dev)
         w_q, w_s = ql.quantize_weight(fmt, wd)
+        if args.layout == "packed":
+            w_q = ql.pack_weight(w_q)          # offline, like the quantization itself
         del wd
         copies = max(2, -(-(1 << 30) // (N * K)))
         wq_all = torch.empty((copies,) + tuple(w_q.shape), dtype=w_q.dtype, device=dev)
@@ -100,7 +104,7 @@ def main(argv=None):
     pts = []
     for (lab, N, K, M) in points:
         sh = shapes[lab]
-        plan = ql.qlinear_plan(fmt, M, N, K)
+        plan = ql.qlinear_plan_packed(fmt, M, N, K) if args.layout == "packed" else ql.qlinear_plan(fmt, M, N, K)
         cfg, facts = plan.info()
         pts.append(dict(lab=lab, N=N, K=K, M=M, plan=plan, cfg=cfg, facts=facts,
                         x=sh["x"][:M].contiguous(),
@@ -202,6 +206,7 @@ def main(argv=None):
         "config": {"workload": wl.name, "format": ql.FORMAT_NAMES[fmt],
                    "shapes": ["%s %dx%d" % s for s in wl.shapes], "token_counts": list(wl.ms),
                    "gemms_per_step": len(pts), "graph_replay": True, "table_entries": n_table,
+                   "weight_layout": args.layout,
                    "us_per_gemm_step_avg": round(step_ms * 1e3 / len(pts), 3)},
         "roofline": {"kernel": "qgemm_decode_kernel", "bound": "hbm", "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),

@@ -42,7 +42,7 @@ if ROOT not in sys.path:
 
 from workloads import CONFIGS, config_by_name, make_inputs  # noqa: E402
 
-SPLITS = (1, 2, 4, 8, 16, 32, 64, 128, 256)
+SPLITS = (1, 2, 4, 8, 16, 32)
 WAVES = ((4, 1), (2, 2), (1, 4))
 
 
@@ -188,34 +188,36 @@ def main(argv=None):
     torch.cuda.set_device(0)
     stream = torch.cuda.Stream()
     t_start = time.time()
-    lines = []
-    for name in args.workloads.split(","):
-        wl = config_by_name(name)
-        ms = [int(m) for m in args.ms.split(",")] if args.ms else list(wl.ms)
-        for (lab, N, K) in wl.shapes:
-            x, w = make_inputs(K, N, max(ms), wl.sigma_w, seed=wl.seed)
-            for layout in [int(v) for v in args.layouts.split(",")]:
-                timer = Timer(wl.fmt, N, K, x, w, stream, layout=layout)
-                for M in ms:
-                    if M > 32:
-                        continue
-                    t0 = time.time()
-                    res = sweep_point(timer, wl.fmt, M, N, K)
-                    us, cfg = res[0]
-                    lines.append(table_line(wl.fmt, M, N, K, cfg, us))
-                    print("%-26s %-8s L%d M=%-3d best %.3f us (%s)  [%d cands, %.1fs]" % (
-                        wl.name, lab, layout, M, us, cfg, len(res), time.time() - t0), flush=True)
-                del timer
-                torch.cuda.empty_cache()
     hdr = ["# qlinear sweep table: fmt M N K algo swap_ab split_k waves_n waves_k rows_per_wave prefetch "
            "a_lds w_lds w_layout tile_m tile_n time_us",
            "# device: %s; hip %s; torch %s" % (torch.cuda.get_device_name(0), torch.version.hip, torch.__version__),
-           "# written %s; sweep wall time %.0f s" % (datetime.datetime.utcnow().strftime("%Y-%m-%d %H:%M UTC"),
-                                                   time.time() - t_start)]
+           "# written %s" % datetime.datetime.utcnow().strftime("%Y-%m-%d %H:%M UTC")]
     os.makedirs(os.path.dirname(os.path.abspath(args.out)), exist_ok=True)
+    n = 0
     with open(args.out, "w") as f:
-        f.write("\n".join(hdr + lines) + "\n")
-    print("wrote %d entries to %s" % (len(lines), args.out))
+        f.write("\n".join(hdr) + "\n")
+        for name in args.workloads.split(","):
+            wl = config_by_name(name)
+            ms = [int(m) for m in args.ms.split(",")] if args.ms else list(wl.ms)
+            for (lab, N, K) in wl.shapes:
+                x, w = make_inputs(K, N, max(ms), wl.sigma_w, seed=wl.seed)
+                for layout in [int(v) for v in args.layouts.split(",")]:
+                    timer = Timer(wl.fmt, N, K, x, w, stream, layout=layout)
+                    for M in ms:
+                        if M > 32:
+                            continue
+                        t0 = time.time()
+                        res = sweep_point(timer, wl.fmt, M, N, K)
+                        us, cfg = res[0]
+                        f.write(table_line(wl.fmt, M, N, K, cfg, us) + "\n")
+                        f.flush()
+                        n += 1
+                        print("%-26s %-8s L%d M=%-3d best %.3f us (%s)  [%d cands, %.1fs]" % (
+                            wl.name, lab, layout, M, us, cfg, len(res), time.time() - t0), flush=True)
+                    del timer
+                    torch.cuda.empty_cache()
+        f.write("# sweep wall time %.0f s\n" % (time.time() - t_start))
+    print("wrote %d entries to %s" % (n, args.out))
 
 
 if __name__ == "__main__":

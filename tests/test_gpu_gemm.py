@@ -8,6 +8,7 @@ accumulator lies within the summation bound of the exact sum.
 """
 
 import itertools
+import os
 
 import numpy as np
 import pytest
@@ -307,3 +308,61 @@ def test_full_size_workloads_sampled_columns(ci, lab, N, K, M):
         else:
             st = fp8_check(fmt, r, ysel, plan.facts["chunks"])
             assert st["ok"] and st["frac_within_ulp"] >= 0.95, (plan.config, st)
+
+
+def _table_entries():
+    path = ql.DEFAULT_TABLE
+    if not os.path.exists(path):
+        return []
+    out = []
+    for line in open(path):
+        f = line.split()
+        if not f or f[0].startswith("#"):
+            continue
+        v = [int(t) for t in f[:16]]
+        out.append(tuple(v))
+    return out
+
+
+_TABLE_FIELDS = ("algo", "swap_ab", "split_k", "waves_n", "waves_k", "rows_per_wave", "prefetch",
+                 "a_lds", "w_lds", "w_layout", "tile_m", "tile_n")
+
+
+def _shape_config(fmt, N, K):
+    for ci, cfg in enumerate(CONFIGS[:4]):
+        if cfg.fmt != fmt:
+            continue
+        for (lab, n, k) in cfg.shapes:
+            if (n, k) == (N, K):
+                return ci, lab
+    raise KeyError((fmt, N, K))
+
+
+@pytest.mark.parametrize("entry", _table_entries(), ids=lambda e: "f%d-M%d-N%d-K%d-L%d" % (e[0], e[1], e[2], e[3], e[13]))
+def test_every_table_entry_matches_oracle(entry):
+    """Each configuration the shipped sweep table selects, run at its own
+    (format, M, N, K) and weight layout, against the oracle on sampled columns."""
+    fmt, M, N, K = entry[:4]
+    cfg = dict(zip(_TABLE_FIELDS, entry[4:16]))
+    ci, lab = _shape_config(fmt, N, K)
+    x, w, w_q, w_s = _weights(ci, lab, N, K)
+    xm = x[:M]
+    a_q, a_s = ql.quantize_act(fmt, xm.cuda())
+    plan = ql.qlinear_plan_with_config(fmt, M, N, K, cfg)
+    y = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
+    ql.qlinear_run(plan, a_q, a_s, ql.pack_weight(w_q) if cfg["w_layout"] else w_q, w_s, y, plan.new_workspace())
+    torch.cuda.synchronize()
+    yb = host_bf16_bits(y)
+    rng = np.random.default_rng(N + 7 * M)
+    if fmt == ql.BLOCK_FP8:
+        nb = int(rng.integers(0, -(-N // 128)))
+        cols = np.arange(nb * 128, min(N, nb * 128 + 128))
+    else:
+        cols = np.sort(rng.choice(N, 64, replace=False))
+    r = oracle.reference(fmt, bf16_bits(xm), bf16_bits(w[torch.from_numpy(cols)]))
+    ysel = yb[:, cols]
+    if fmt == ql.W8A8_INT8:
+        assert np.array_equal(ysel, r["y_ref"]), cfg
+    else:
+        st = fp8_check(fmt, r, ysel, plan.facts["chunks"])
+        assert st["ok"] and st["frac_within_ulp"] >= 0.95, (cfg, st)
