@@ -41,6 +41,149 @@ def quantizer_bytes(fmt, M, K):
     return 2 * M * K + M * K + (4 * M * (K // 128) if fmt == 2 else 4 * M)
 
 
+PKG = os.path.join(ROOT, "quantized_gemm_decode_amd")
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def kernel_sources_digest():
+    """sha256 over the HIP/C++ sources and the shipped sweep table: a recorded
+    counter reading is valid only for the code (and plans) it was taken on."""
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(PKG, "csrc")
+    files = [os.path.join(csrc, f) for f in sorted(os.listdir(csrc))]
+    files.append(os.path.join(PKG, "tables", "decode_table.txt"))
+    for path in files:
+        h.update(os.path.basename(path).encode())
+        with open(path, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def traffic_file(workload, layout):
+    return os.path.join(PROFILES, "decode_gemm_%s_%s_hbm_traffic.txt" % (workload, layout))
+
+
+def recorded_traffic(workload, layout):
+    """HBM bytes (FETCH_SIZE + WRITE_SIZE, calibrated) of one launch of every GEMM
+    of the step, from the committed counter summary; None if absent or stale."""
+    path = traffic_file(workload, layout)
+    if not os.path.exists(path):
+        return None, "no counter summary"
+    kv = {}
+    for line in open(path):
+        f = line.split()
+        if len(f) == 2 and not line.startswith("#"):
+            kv[f[0]] = f[1]
+    if kv.get("kernel_sources_sha256") != kernel_sources_digest():
+        return None, "kernel sources changed since the counters were taken"
+    return int(kv["traffic_bytes_per_step"]), "rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE, copy-calibrated"
+
+
+def pmc_summary(workload, layout, fetch_csv, write_csv):
+    """Summarise two rocprofv3 --pmc runs of --profile-pass into the traffic record."""
+    import csv
+    from workloads import config_by_name, decode_points
+    wl = config_by_name(workload)
+
+    def load(path):
+        rows = list(csv.DictReader(open(path)))
+        rows.sort(key=lambda r: int(r["Dispatch_Id"]))
+        return rows
+
+    fr, wr = load(fetch_csv), load(write_csv)
+    assert len(fr) == len(wr)
+    cal = (256 << 20) / 1024.0                         # KiB read and written by each calibration copy
+    fetch_copy = sum(float(r["Counter_Value"]) for r in fr[-3:]) / 3
+    write_copy = sum(float(r["Counter_Value"]) for r in wr[-3:]) / 3
+    kf, kw = cal / fetch_copy, cal / write_copy
+    gem = [(float(a["Counter_Value"]), float(b["Counter_Value"]), a["Kernel_Name"].split("(")[0])
+           for a, b in zip(fr, wr) if "qgemm" in a["Kernel_Name"]]
+    pts = decode_points(wl)
+    gem = gem[-3 * len(pts):]
+    lines = ["# HBM traffic of the decode GEMM kernels, workload %s, %s weights" % (workload, layout),
+             "# commands (run from /tmp with TMPDIR=/tmp):",
+             "#   rocprofv3 --pmc FETCH_SIZE -f csv -d <dir_f> -o fetch -- python3 <repo>/bench.py --workload %s "
+             "--layout %s --profile-pass" % (workload, layout),
+             "#   rocprofv3 --pmc WRITE_SIZE -f csv -d <dir_w> -o write -- python3 <repo>/bench.py --workload %s "
+             "--layout %s --profile-pass" % (workload, layout),
+             "#   python3 bench.py --workload %s --layout %s --pmc-summary <dir_f>/fetch_counter_collection.csv "
+             "<dir_w>/write_counter_collection.csv" % (workload, layout),
+             "# calibration: a 256 MiB device copy reads FETCH_SIZE %.1f KiB and WRITE_SIZE %.1f KiB per dispatch"
+             % (fetch_copy, write_copy),
+             "#   -> bytes = FETCH_SIZE * %.4f KiB, WRITE_SIZE * %.4f KiB" % (kf, kw),
+             "# per GEMM: mean of 3 dispatches on distinct weight copies",
+             "# shape    M    algorithmic_B   fetched_B  written_B  traffic/alg"]
+    tot_a = tot_t = 0
+    for i, (lab, N, K, M) in enumerate(pts):
+        g = gem[3 * i:3 * i + 3]
+        fb = sum(x[0] for x in g) / 3 * 1024 * kf
+        wb = sum(x[1] for x in g) / 3 * 1024 * kw
+        ab = algorithmic_bytes(wl.fmt, M, N, K)
+        tot_a += ab
+        tot_t += fb + wb
+        lines.append("# %-8s %-4d %13d %11.0f %10.0f  %.4f" % (lab, M, ab, fb, wb, (fb + wb) / ab))
+    lines += ["kernel_sources_sha256 %s" % kernel_sources_digest(),
+              "algorithmic_bytes_per_step %d" % tot_a,
+              "traffic_bytes_per_step %d" % round(tot_t),
+              "traffic_over_algorithmic %.4f" % (tot_t / tot_a)]
+    return "\n".join(lines) + "\n"
+
+
+def trace_summary(workload, layout, trace_csv, stats_csv, bench_json):
+    """Per-point kernel durations from a rocprofv3 --kernel-trace run of this script,
+    next to the HIP-event per-launch times the same run printed."""
+    import csv
+    rows = list(csv.DictReader(open(trace_csv)))
+    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+    bench = None
+    for line in open(bench_json):
+        if line.startswith("{"):
+            bench = json.loads(line)
+    pp = bench["per_point"]
+    # the per-point timing phase ends the run: for each point a block of consecutive GEMM
+    # launches (3 warm-up replays + kernel-reps timed replays of R launches), then the quantizer
+    runs, cur = [], []
+    for r in rows:
+        if "qgemm" in r["Kernel_Name"]:
+            cur.append(r)
+        else:
+            if cur:
+                runs.append(cur)
+            cur = []
+    if cur:
+        runs.append(cur)
+    runs = runs[-len(pp):]
+    lines = ["# rocprofv3 kernel trace of the decode GEMM, workload %s, %s weights" % (workload, layout),
+             "# command (from /tmp with TMPDIR=/tmp):",
+             "#   rocprofv3 --kernel-trace --stats -f csv -d <dir> -o bench -- python3 <repo>/bench.py --workload %s "
+             "--layout %s --steps %d --warmup %d --kernel-reps %d --no-cpu-baseline"
+             % (workload, layout, bench["steps"], bench["warmup"], bench.get("kernel_reps", 5)),
+             "#   python3 bench.py --workload %s --layout %s --trace-summary <dir>/bench_kernel_trace.csv "
+             "<dir>/bench_kernel_stats.csv <stdout of the command above>" % (workload, layout),
+             "# per point: rocprof = mean kernel duration over the timed replays (last kernel-reps x R launches);",
+             "# hip_events = the same run's HIP-event time per launch (median of replays / R)",
+             "# shape    M    kernel_instantiation                                   rocprof_us  hip_events_us  ratio"]
+    tot_r = tot_e = 0.0
+    for p, run in zip(pp, runs):
+        n_timed = len(run) * 5 // 8
+        timed = run[-n_timed:]
+        us = sum(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]) for r in timed) / len(timed) / 1e3
+        name = run[0]["Kernel_Name"].split("(")[0].replace("void ", "").replace("qlk::", "")
+        tot_r += us
+        tot_e += p["us"]
+        lines.append("# %-8s %-4d %-54s %9.3f %13.3f  %.3f" % (p["shape"], p["M"], name, us, p["us"], p["us"] / us))
+    lines.append("# sum over the %d points: rocprof %.2f us, hip events %.2f us (ratio %.3f)" % (len(pp), tot_r, tot_e,
+                                                                                              tot_e / tot_r))
+    lines.append("# achieved (algorithmic bytes / rocprof durations): %.1f GB/s; bench roofline.achieved: %.1f GB/s"
+                 % (bench["roofline"]["algorithmic_bytes"] / (tot_r * 1e-6) / 1e9
+                    if "algorithmic_bytes" in bench["roofline"] else float("nan"), bench["roofline"]["achieved"]))
+    lines.append("# rocprofv3 --stats kernel summary (all launches of the run, every phase):")
+    for line in open(stats_csv):
+        lines.append("#   " + line.rstrip())
+    return "\n".join(lines) + "\n"
+
+
 def parse_args(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -54,6 +197,13 @@ def parse_args(argv=None):
     ap.add_argument("--cpu-budget-s", type=float, default=20.0)
     ap.add_argument("--table", default=None, help="sweep table path (default: the packaged table)")
     ap.add_argument("--out", default=None, help="also write the JSON line to this file")
+    ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="print the HBM-traffic record from two rocprofv3 --pmc runs of --profile-pass, and exit")
+    ap.add_argument("--trace-summary", nargs=3, metavar=("TRACE_CSV", "STATS_CSV", "BENCH_STDOUT"),
+                    help="print per-point rocprofv3 kernel durations next to the HIP-event times, and exit")
+    ap.add_argument("--profile-pass", action="store_true",
+                    help="for hardware-counter runs: launch each point's quantize+GEMM eagerly on 3 weight "
+                         "copies, then a plain 256 MiB device copy 3 times (the counters' calibration), and exit")
     return ap.parse_args(argv)
 
 
@@ -64,6 +214,13 @@ def main(argv=None):
               "column-wise across GPUs with no exchange, so per-GPU work is one GPU's share." % args.gpus,
               file=sys.stderr)
         return 2
+
+    if args.trace_summary:
+        sys.stdout.write(trace_summary(args.workload, args.layout, *args.trace_summary))
+        return 0
+    if args.pmc_summary:
+        sys.stdout.write(pmc_summary(args.workload, args.layout, *args.pmc_summary))
+        return 0
 
     import numpy as np
     import torch
@@ -113,6 +270,9 @@ def main(argv=None):
                         y=torch.empty(M, N, dtype=torch.bfloat16, device=dev),
                         wsp=plan.new_workspace(dev),
                         bytes=algorithmic_bytes(fmt, M, N, K), qbytes=quantizer_bytes(fmt, M, K)))
+
+    if args.profile_pass:
+        return profile_pass(ql, fmt, pts, shapes, stream)
 
     # ------------------------------------------------ step graphs (quantize + GEMM per point)
     n_graphs = 8
@@ -184,6 +344,7 @@ def main(argv=None):
                               source=p["facts"]["source"]))
         del g
     achieved = tot_bytes / (tot_us * 1e-6) / 1e9
+    traffic, traffic_note = recorded_traffic(wl.name, args.layout)
 
     # ------------------------------------------------ CPU oracle baseline (bounded sample)
     cpu = None
@@ -197,6 +358,7 @@ def main(argv=None):
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "kernel_reps": args.kernel_reps,
         "ms_per_step": round(step_ms, 4),
         "higher_is_better": True,
         "scaling": "weak",
@@ -210,9 +372,10 @@ def main(argv=None):
                    "us_per_gemm_step_avg": round(step_ms * 1e3 / len(pts), 3)},
         "roofline": {"kernel": "qgemm_decode_kernel", "bound": "hbm", "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": None,
-                     "note": "algorithmic bytes of all %d GEMMs / sum of their per-launch durations "
-                             "(HIP events around graph replays of back-to-back launches)" % len(pts)},
+                     "traffic": traffic, "algorithmic_bytes": int(tot_bytes), "traffic_source": traffic_note,
+                     "note": "algorithmic bytes of one launch of each of the %d GEMMs / sum of their per-launch "
+                             "durations (HIP events around graph replays of back-to-back launches); traffic is "
+                             "the HBM bytes those same %d launches moved" % (len(pts), len(pts))},
         "cpu_baseline": cpu,
         "per_point": per_point,
         "wall_s": round(wall, 3),
@@ -222,6 +385,32 @@ def main(argv=None):
     if args.out:
         with open(args.out, "w") as f:
             f.write(line + "\n")
+    return 0
+
+
+def profile_pass(ql, fmt, pts, shapes, stream):
+    """Eager launches in a fixed order for per-dispatch hardware counters.
+
+    Order: for every point, 3 x (quantize, GEMM) on weight copies 0, 1, 2;
+    then 3 plain copies of 256 MiB (read 256 MiB, write 256 MiB), whose
+    counter readings calibrate the byte counters."""
+    import torch
+    with torch.cuda.stream(stream):
+        for p in pts:
+            sh = shapes[p["lab"]]
+            for c in range(3):
+                ql.qlinear_forward(p["plan"], p["x"], p["a_q"], p["a_s"], sh["wq"][c], sh["ws"][c], p["y"],
+                                   p["wsp"], stream=stream)
+            stream.synchronize()
+            print("point %s M=%d N=%d K=%d bytes=%d" % (p["lab"], p["M"], p["N"], p["K"], p["bytes"]), flush=True)
+        src = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        src.fill_(1)
+        stream.synchronize()
+        for _ in range(3):
+            dst.copy_(src)
+        stream.synchronize()
+    print("copy bytes=%d" % (256 << 20), flush=True)
     return 0
 
 
@@ -242,7 +431,7 @@ def cpu_baseline(wl, shapes, budget_s):
     for (lab, N, K) in wl.shapes:
         x, w = make_inputs(K, N, max(wl.ms), wl.sigma_w, seed=wl.seed)
         w_q, s_w = oracle.quantize_weight(fmt, bf16_bits(w))          # offline step: not timed
-        for M in (1, max(wl.ms)):
+        for M in wl.ms:
             xb = bf16_bits(x[:M])
             t0 = time.perf_counter()
             a_q, s_a = oracle.quantize_act(fmt, xb)

@@ -44,7 +44,6 @@ ql_status hip_fail(hipError_t e, const char* what) {
   return fail(QL_E_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
-constexpr int kNW = 4;                       // waves per decode workgroup
 constexpr int64_t kLdsLimit = 64 * 1024;     // dynamic LDS budget per workgroup
 constexpr int kBuckets[] = {1, 2, 4, 8, 16, 24, 32};
 
@@ -157,10 +156,12 @@ ql_status build_plan(int32_t fmt, int64_t M, int64_t N, int64_t K, const ql_conf
   if (M > 32) return fail(QL_E_UNSUPPORTED, "the decode algorithm serves M <= 32 (M=%lld)", (long long)M);
   if (cfg.swap_ab != 0 && cfg.swap_ab != 1) return fail(QL_E_INVALID, "swap_ab must be 0 or 1");
   if (!is_pow2(cfg.split_k) || cfg.split_k > 256) return fail(QL_E_INVALID, "split_k must be a power of two in [1, 256]");
-  if (cfg.waves_k < 1 || cfg.waves_n < 1 || cfg.waves_n * cfg.waves_k != kNW)
-    return fail(QL_E_INVALID, "waves_n * waves_k must equal %d", kNW);
-  if (cfg.rows_per_wave != 16 && cfg.rows_per_wave != 32) return fail(QL_E_INVALID, "rows_per_wave must be 16 or 32");
-  if (cfg.prefetch != 2 && cfg.prefetch != 4) return fail(QL_E_INVALID, "prefetch must be 2 or 4");
+  const int nw = cfg.waves_n * cfg.waves_k;
+  if (cfg.waves_k < 1 || cfg.waves_n < 1 || (nw != 4 && nw != 8 && nw != 16))
+    return fail(QL_E_INVALID, "waves_n * waves_k must be 4, 8 or 16");
+  if (cfg.rows_per_wave != 16 && cfg.rows_per_wave != 32 && cfg.rows_per_wave != 64)
+    return fail(QL_E_INVALID, "rows_per_wave must be 16, 32 or 64");
+  if (cfg.prefetch != 1 && cfg.prefetch != 2 && cfg.prefetch != 4) return fail(QL_E_INVALID, "prefetch must be 1, 2 or 4");
   if (cfg.a_lds != 0 && cfg.a_lds != 1) return fail(QL_E_INVALID, "a_lds must be 0 or 1");
   if (cfg.w_lds != 0 && cfg.w_lds != 1) return fail(QL_E_INVALID, "w_lds must be 0 or 1");
   if (cfg.w_layout != 0 && cfg.w_layout != 1) return fail(QL_E_INVALID, "w_layout must be 0 or 1");
@@ -182,8 +183,8 @@ ql_status build_plan(int32_t fmt, int64_t M, int64_t N, int64_t K, const ql_conf
   p->bn = cfg.waves_n * rg * 16;
   p->n_tiles = (int)((N + p->bn - 1) / p->bn);
   const int64_t lds_a = cfg.a_lds ? (int64_t)p->chunk_kb * p->mt * 2048 : 0;
-  const int64_t lds_w = (cfg.w_lds && !cfg.w_layout) ? (int64_t)kNW * 2 * rg * 2048 : 0;
-  const int64_t lds_red = cfg.waves_k > 1 ? (int64_t)kNW * rg * p->mt * 1024 : 0;
+  const int64_t lds_w = (cfg.w_lds && !cfg.w_layout) ? (int64_t)nw * 2 * rg * 2048 : 0;
+  const int64_t lds_red = cfg.waves_k > 1 ? (int64_t)nw * rg * p->mt * 1024 : 0;
   p->lds = std::max(lds_a + lds_w, lds_red);
   if (p->lds > kLdsLimit) {
     const long long need = (long long)p->lds;
@@ -194,7 +195,7 @@ ql_status build_plan(int32_t fmt, int64_t M, int64_t N, int64_t K, const ql_conf
   p->ws_acc_bytes = p->chunks > 1 ? ((M * N * 4 + 255) / 256) * 256 : 0;
   p->ws_bytes = p->chunks > 1 ? p->ws_acc_bytes + (int64_t)p->n_tiles * 4 : 0;
   const int wm = cfg.w_layout ? qlk::W_PACKED : (cfg.w_lds ? qlk::W_LDS_TRANSPOSE : qlk::W_DIRECT);
-  p->key = qlk::DecodeKey{kernel_fmt(fmt), cfg.swap_ab, p->mt, rg, kNW, cfg.prefetch, cfg.a_lds, wm};
+  p->key = qlk::DecodeKey{kernel_fmt(fmt), cfg.swap_ab, p->mt, rg, nw, cfg.prefetch, cfg.a_lds, wm};
   qlk::DecodeArgs dummy{};
   hipError_t pe;
   switch (p->key.fmt) {
@@ -256,7 +257,7 @@ ql_status launch_gemm(const ql_plan_s* p, const void* a_q, const float* a_scale,
   a.chunk_kb = p->chunk_kb;
   a.waves_k = p->cfg.waves_k;
   a.n_tiles = p->n_tiles;
-  const dim3 grid((unsigned)(p->n_tiles * p->chunks)), block(kNW * 64);
+  const dim3 grid((unsigned)(p->n_tiles * p->chunks)), block((unsigned)p->key.nw * 64u);
   hipError_t e;
   switch (p->key.fmt) {
     case qlk::FMT_INT8: e = qlk::decode_dispatch_int8(p->key, grid, block, (size_t)p->lds, s, a, false); break;
@@ -411,7 +412,7 @@ ql_status qlinear_plan_info(ql_plan p, ql_config* cfg, ql_plan_facts* facts) {
     facts->chunks = p->chunks;
     facts->chunk_k = p->chunk_kb * 128;
     facts->workgroups = p->n_tiles * p->chunks;
-    facts->threads = kNW * 64;
+    facts->threads = p->key.nw * 64;
     facts->lds_bytes = (int32_t)p->lds;
     facts->workspace_bytes = p->ws_bytes;
   }

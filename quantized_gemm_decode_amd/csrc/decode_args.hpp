@@ -39,8 +39,8 @@ struct DecodeKey {
   int fmt;   // FMT_FP8 / FMT_INT8 / FMT_BLOCK
   int swap;  // weights as the matrix core's first operand
   int mt;    // 16-wide token tiles (1: M <= 16, 2: M <= 32)
-  int rg;    // 16-row groups per wave (1 or 2)
-  int nw;    // waves per workgroup
+  int rg;    // 16-row groups per wave (1, 2 or 4)
+  int nw;    // waves per workgroup (4, 8 or 16)
   int pf;    // K blocks per prefetch batch
   int alds;  // activations staged in LDS
   int wm;    // weight mode: W_DIRECT / W_LDS_TRANSPOSE / W_PACKED

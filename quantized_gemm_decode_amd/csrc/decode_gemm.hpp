@@ -473,26 +473,41 @@ __global__ void __launch_bounds__(NW * 64) qgemm_decode_kernel(DecodeArgs p) {
   }
 }
 
-// Instantiation table for one format: every (swap, mt, rg, pf, alds, weight mode)
-// combination the planner may choose.  Combinations whose registers would
-// spill (two token tiles with 32 rows per wave and four-block batches, and
-// for Block_FP8 the four-block batches of the standard orientation) are not
-// instantiated: the planner rejects them.
-template <int FMT, int SW, int MT_, int RG_, int PF_>
+// Instantiation table for one format.  Row-major weights (direct or LDS
+// transpose) and LDS-staged activations use 4-wave workgroups with 16 or 32
+// rows per wave and 2- or 4-block batches.  Packed weights additionally get
+// 8- and 16-wave workgroups, 64 rows per wave and 1-block batches.  A shape
+// whose buffers would not fit the register file of its occupancy (256
+// VGPRs a wave up to 8 waves per workgroup, 128 at 16 waves) is not
+// instantiated, and the planner rejects it.
+template <int FMT, int NW_, int SW, int MT_, int RG_, int PF_>
 constexpr bool decode_config_fits() {
-  if (MT_ == 2 && RG_ == 2 && PF_ == 4) return false;
-  if (FMT == FMT_BLOCK && MT_ == 2 && PF_ == 4 && !SW) return false;
+  if (NW_ == 4 && RG_ <= 2 && PF_ >= 2) {
+    // the original 4-wave shapes (checked one by one against the compiler)
+    if (MT_ == 2 && RG_ == 2 && PF_ == 4) return false;
+    if (FMT == FMT_BLOCK && MT_ == 2 && PF_ == 4 && !SW) return false;
+    return true;
+  }
+  // two batches of PF blocks of (RG weight + MT activation) fragments, 8 VGPRs each
+  const int buffers = 2 * PF_ * (RG_ + MT_) * 8;
+  const int scales = FMT == FMT_BLOCK ? 2 * PF_ * (4 * MT_ + RG_) : 0;
+  const int accs = RG_ * MT_ * 4;
+  const int budget = NW_ >= 16 ? 128 : 256;
+  // Block_FP8 keeps per-block partial products and scale factors live as well
+  const int estimate = (buffers + scales + accs + 40) * (FMT == FMT_BLOCK ? 135 : 100) / 100;
+  if (estimate > budget) return false;
+  if (NW_ * RG_ * MT_ > 64) return false;  // cross-wave reduction must fit 64 KB of LDS
   return true;
 }
 
-template <int FMT, int SW, int MT_, int RG_, int PF_, int AL, int WM_>
+template <int FMT, int NW_, int SW, int MT_, int RG_, int PF_, int AL, int WM_>
 hipError_t decode_try(const DecodeKey& k, dim3 grid, dim3 block, size_t lds, hipStream_t s, const DecodeArgs& a,
                       bool probe_only, bool* hit) {
-  if constexpr (decode_config_fits<FMT, SW, MT_, RG_, PF_>()) {
-    if (k.swap == SW && k.mt == MT_ && k.rg == RG_ && k.nw == 4 && k.pf == PF_ && k.alds == AL && k.wm == WM_) {
+  if constexpr (decode_config_fits<FMT, NW_, SW, MT_, RG_, PF_>()) {
+    if (k.swap == SW && k.mt == MT_ && k.rg == RG_ && k.nw == NW_ && k.pf == PF_ && k.alds == AL && k.wm == WM_) {
       *hit = true;
       if (probe_only) return hipSuccess;
-      qgemm_decode_kernel<FMT, SW != 0, MT_, RG_, 4, PF_, AL != 0, WM_><<<grid, block, lds, s>>>(a);
+      qgemm_decode_kernel<FMT, SW != 0, MT_, RG_, NW_, PF_, AL != 0, WM_><<<grid, block, lds, s>>>(a);
       return hipGetLastError();
     }
   }
@@ -504,18 +519,27 @@ hipError_t decode_dispatch(const DecodeKey& k, dim3 grid, dim3 block, size_t lds
                            const DecodeArgs& a, bool probe_only) {
   bool hit = false;
   hipError_t e = hipSuccess;
-#define QL_TRY(SW, MT_, RG_, PF_, AL, WM_)                                                       \
-  e = decode_try<FMT, SW, MT_, RG_, PF_, AL, WM_>(k, grid, block, lds, s, a, probe_only, &hit); \
+#define QL_TRY(NW_, SW, MT_, RG_, PF_, AL, WM_)                                                       \
+  e = decode_try<FMT, NW_, SW, MT_, RG_, PF_, AL, WM_>(k, grid, block, lds, s, a, probe_only, &hit); \
   if (hit) return e;
+  // 4 waves, every weight mode and activation staging
 #define QL_TRY_WL(SW, MT_, RG_, PF_, AL) \
-  QL_TRY(SW, MT_, RG_, PF_, AL, 0) QL_TRY(SW, MT_, RG_, PF_, AL, 1) QL_TRY(SW, MT_, RG_, PF_, AL, 2)
+  QL_TRY(4, SW, MT_, RG_, PF_, AL, 0) QL_TRY(4, SW, MT_, RG_, PF_, AL, 1) QL_TRY(4, SW, MT_, RG_, PF_, AL, 2)
 #define QL_TRY_AL(SW, MT_, RG_, PF_) QL_TRY_WL(SW, MT_, RG_, PF_, 0) QL_TRY_WL(SW, MT_, RG_, PF_, 1)
 #define QL_TRY_PF(SW, MT_, RG_) QL_TRY_AL(SW, MT_, RG_, 2) QL_TRY_AL(SW, MT_, RG_, 4)
 #define QL_TRY_RG(SW, MT_) QL_TRY_PF(SW, MT_, 1) QL_TRY_PF(SW, MT_, 2)
-#define QL_TRY_MT(SW) QL_TRY_RG(SW, 1) QL_TRY_RG(SW, 2)
+  // packed weights, activations from L2: wider workgroups, longer rows, 1-block batches
+#define QL_TRY_P(NW_, SW, MT_, RG_) QL_TRY(NW_, SW, MT_, RG_, 1, 0, 2) QL_TRY(NW_, SW, MT_, RG_, 2, 0, 2)
+#define QL_TRY_PN(SW, MT_)                                                                \
+  QL_TRY(4, SW, MT_, 1, 1, 0, 2) QL_TRY(4, SW, MT_, 2, 1, 0, 2) QL_TRY_P(4, SW, MT_, 4)   \
+  QL_TRY_P(8, SW, MT_, 1) QL_TRY_P(8, SW, MT_, 2) QL_TRY_P(8, SW, MT_, 4)                 \
+  QL_TRY_P(16, SW, MT_, 1) QL_TRY_P(16, SW, MT_, 2) QL_TRY_P(16, SW, MT_, 4)
+#define QL_TRY_MT(SW) QL_TRY_RG(SW, 1) QL_TRY_RG(SW, 2) QL_TRY_PN(SW, 1) QL_TRY_PN(SW, 2)
   QL_TRY_MT(0)
   QL_TRY_MT(1)
 #undef QL_TRY_MT
+#undef QL_TRY_PN
+#undef QL_TRY_P
 #undef QL_TRY_RG
 #undef QL_TRY_PF
 #undef QL_TRY_AL

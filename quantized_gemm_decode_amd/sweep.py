@@ -8,9 +8,11 @@ dispatch addresses runtime overhead"; [Noticias] "Autoajuste de los
 kernels").  Here the space is small enough to search exhaustively in two
 phases:
 
-  1. swap_ab=1, prefetch=2; every (waves_n, waves_k), rows_per_wave,
-     split_k (distinct effective chunk counts only), a_lds and w_lds;
-  2. the best few of phase 1 again with swap_ab in {0, 1} x prefetch {2, 4}.
+  1. swap_ab=1, prefetch=2 (1 where 2 is not instantiated); every
+     (waves_n, waves_k), rows_per_wave, split_k (distinct effective chunk
+     counts only), a_lds and w_lds -- for packed weights also 8- and 16-wave
+     workgroups and 64 rows per wave;
+  2. the best few of phase 1 again with swap_ab in {0, 1} x prefetch {1, 2, 4}.
 
 Every candidate is timed as a hipGraph of back-to-back launches, each on its
 own copy of the weights (>= 1 GiB of copies, so the Infinity Cache cannot
@@ -44,6 +46,8 @@ from workloads import CONFIGS, config_by_name, make_inputs  # noqa: E402
 
 SPLITS = (1, 2, 4, 8, 16, 32)
 WAVES = ((4, 1), (2, 2), (1, 4))
+# packed weights also run 8- and 16-wave workgroups and 64 rows per wave
+WAVES_PACKED = WAVES + ((1, 8), (2, 4), (1, 16))
 
 
 def _effective_chunks(K, split):
@@ -55,7 +59,8 @@ def _effective_chunks(K, split):
 
 def phase1_candidates(fmt, M, N, K, layout=0):
     seen = set()
-    for (wn, wk), rows, split, alds, wlds in itertools.product(WAVES, (16, 32), SPLITS, (1, 0),
+    waves, rows_set = (WAVES, (16, 32)) if layout == 0 else (WAVES_PACKED, (16, 32, 64))
+    for (wn, wk), rows, split, alds, wlds in itertools.product(waves, rows_set, SPLITS, (1, 0),
                                                               (1, 0) if layout == 0 else (0,)):
         ch = _effective_chunks(K, split)
         key = (wn, wk, rows, ch, alds, wlds)
@@ -137,9 +142,15 @@ def sweep_point(timer, fmt, M, N, K, log=print, top=6):
     results = []
     ref = None
     for cfg in phase1_candidates(fmt, M, N, K, timer.layout):
-        try:
-            plan = ql.qlinear_plan_with_config(fmt, M, N, K, cfg)
-        except ql.QLinearError:
+        plan = None
+        for pf in (2, 1):      # shapes too large for 2-block batches are instantiated with 1-block ones
+            try:
+                cfg = dict(cfg, prefetch=pf)
+                plan = ql.qlinear_plan_with_config(fmt, M, N, K, cfg)
+                break
+            except ql.QLinearError:
+                continue
+        if plan is None:
             continue
         cfg = dict(cfg, split_k=plan.config["split_k"])
         us, y = timer.measure(plan, M)
@@ -152,7 +163,7 @@ def sweep_point(timer, fmt, M, N, K, log=print, top=6):
     results.sort(key=lambda t: t[0])
     seen = {tuple(sorted(c.items())) for _, c in results}
     for _, base in results[:top]:
-        for swap, pf in itertools.product((0, 1), (2, 4)):
+        for swap, pf in itertools.product((0, 1), (1, 2, 4)):
             cfg = dict(base, swap_ab=swap, prefetch=pf)
             k = tuple(sorted(cfg.items()))
             if k in seen:

@@ -53,9 +53,10 @@ def run_gemm(plan, a_q, s_a, w_q, s_w, acc=True):
     return host_bf16_bits(y), (a.cpu().numpy() if acc else None), ws
 
 
-def fp8_check(fmt, r, y_bits, split):
-    """Apply the oracle's FP8 acceptance rule to a GPU result."""
+def fp8_check(fmt, r, y_bits, split, waves_k=16):
+    """Apply the oracle's FP8 acceptance rule to a GPU result (``waves_k``: the
+    partial sums a workgroup reduces, at most 16 in any plan)."""
     K = r["a_q"].shape[1]
-    d = oracle.summation_depth(K, split=split)
+    d = oracle.summation_depth(K, split=split, waves_k=waves_k)
     B = oracle.tolerance_bound(fmt, r["a_q"], r["w_q"], r["s_a"], r["s_w"], d)
     return oracle.check_fp8_parity(y_bits, r["y_ref"], r["y_true"], B)

@@ -33,17 +33,17 @@ def _dev(fmt, r):
     return (dev_codes(fmt, r["a_q"]), dev_f32(r["s_a"]), dev_codes(fmt, r["w_q"]), dev_f32(r["s_w"]))
 
 
-def _assert_parity(fmt, r, y, acc, split, label=""):
+def _assert_parity(fmt, r, y, acc, split, label="", waves_k=16):
     if fmt == ql.W8A8_INT8:
         assert np.array_equal(acc.astype(np.int64), r["S"]), label
         bad = np.argwhere(y != r["y_ref"])
         assert bad.size == 0, (label, bad[:5])
         return
-    st = fp8_check(fmt, r, y, split)
+    st = fp8_check(fmt, r, y, split, waves_k)
     assert st["ok"], (label, st)
     assert st["frac_within_ulp"] >= 0.95, (label, st)
     K = r["a_q"].shape[1]
-    d = oracle.summation_depth(K, split=split)
+    d = oracle.summation_depth(K, split=split, waves_k=waves_k)
     gamma = d * 2.0 ** -24 / (1 - d * 2.0 ** -24) + oracle.MATRIX_CORE_ETA
     if fmt == ql.FP8_DYNAMIC:
         bound = gamma * oracle.contract_abs(fmt, r["a_q"], r["w_q"])
@@ -84,6 +84,35 @@ def test_every_instantiation_matches_oracle(fmt, M, vi):
         w_q = ql.pack_weight(w_q)
     y, acc, ws = run_gemm(plan, a_q, s_a, w_q, s_w)
     _assert_parity(fmt, r, y, acc, plan.facts["chunks"], label=str(cfg))
+    if ws is not None:
+        assert int(torch.count_nonzero(ws)) == 0, "split-K workspace not left all-zero"
+
+
+# packed-weight shapes with wider workgroups: waves per workgroup x rows per wave x batch size
+WIDE = list(itertools.product([4, 8, 16], [16, 32, 64], [1, 2], [0, 1]))
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("M", [5, 29])
+@pytest.mark.parametrize("wi", range(len(WIDE)))
+def test_wide_workgroup_instantiations_match_oracle(fmt, M, wi):
+    nw, rows, pf, swap = WIDE[wi]
+    wks = [k for k in (1, 2, 4, 8, 16) if k <= nw]
+    wk = wks[(wi + M) % len(wks)]
+    split = SPLITS[(wi + 2 * M) % len(SPLITS)]
+    N = 300 + 16 * wi                                    # several tiles + a ragged tail
+    K = 1152 if fmt == ql.BLOCK_FP8 or wi % 3 else 1040  # 1040: ragged last K block
+    r = _ref(fmt, M, N, K, seed=1000 + wi * 7 + M)
+    cfg = dict(swap_ab=swap, split_k=split, waves_n=nw // wk, waves_k=wk, rows_per_wave=rows, prefetch=pf,
+               a_lds=0, w_lds=0, w_layout=1)
+    try:
+        plan = ql.qlinear_plan_with_config(fmt, M, N, K, cfg)
+    except ql.QLinearError as e:
+        assert e.status == 2, e
+        pytest.skip("configuration not available: %s" % e)
+    a_q, s_a, w_q, s_w = _dev(fmt, r)
+    y, acc, ws = run_gemm(plan, a_q, s_a, ql.pack_weight(w_q), s_w)
+    _assert_parity(fmt, r, y, acc, plan.facts["chunks"], label=str(cfg), waves_k=wk)
     if ws is not None:
         assert int(torch.count_nonzero(ws)) == 0, "split-K workspace not left all-zero"
 
