@@ -104,18 +104,22 @@ typedef struct {
   int32_t algo;          /* ql_algo */
   int32_t swap_ab;       /* 0 or 1 */
   int32_t split_k;       /* 1,2,4,...,256; clamped to the number of 128-wide K blocks */
-  int32_t waves_n;       /* DECODE: waves of a workgroup side by side along N */
+  int32_t waves_n;       /* DECODE: waves of a workgroup side by side along N;
+                            waves_n * waves_k = 4, 8 or 16 (8 and 16: packed weights) */
   int32_t waves_k;       /* DECODE: waves of a workgroup sharing its K chunk */
-  int32_t rows_per_wave; /* DECODE: 16 or 32 weight rows per wave */
-  int32_t prefetch;      /* DECODE: 128-wide K blocks per wave kept in flight (2 or 4) */
+  int32_t rows_per_wave; /* DECODE: 16, 32 or 64 weight rows per wave */
+  int32_t prefetch;      /* DECODE: 128-wide K blocks per wave and batch, two batches in flight (1, 2 or 4);
+                            TILED: 128-wide K blocks in flight per workgroup (1, 2 or 4) */
   int32_t a_lds;         /* DECODE: 1 = stage the activation chunk in LDS, 0 = read it per K block */
   int32_t w_lds;         /* DECODE, row-major weights: 1 = coalesced weight loads (8 rows x 128 B
                             per instruction) transposed to the matrix-core layout through LDS;
                             0 = direct loads in operand order */
   int32_t w_layout;      /* weight layout the plan reads: 0 = row-major W_q[N,K];
                             1 = packed tiles (qlinear_pack_weight) */
-  int32_t tile_m;        /* TILED: workgroup tile rows (M) */
-  int32_t tile_n;        /* TILED: workgroup tile columns (N) */
+  int32_t tile_m;        /* TILED: workgroup tile rows (tokens): 64, 128 or 256 */
+  int32_t tile_n;        /* TILED: workgroup tile columns (weight rows): 128 or 256;
+                            tile_m * tile_n <= 32768.  TILED reads swap_ab, split_k,
+                            w_layout, prefetch and the tile; the other fields are ignored */
 } ql_config;
 
 /* Derived launch facts of a plan (read-only). */
@@ -189,8 +193,10 @@ void qlinear_table_clear(void);
  * or above, else the largest); without an entry a built-in heuristic is used
  * (facts.source tells which).  The environment variable QLINEAR_FORCE =
  * "algo,swap,split,wn,wk,rows,prefetch,alds,wlds,wlayout,tile_m,tile_n"
- * overrides both (its w_layout must match the call).
- * Host-only: no device call is made.
+ * overrides both (its w_layout must match the call).  M <= 32 plans use the
+ * DECODE algorithm, M > 32 the TILED one.
+ * Host-only: nothing is enqueued and nothing is allocated (a TILED plan
+ * raises its kernel's dynamic LDS limit with hipFuncSetAttribute).
  */
 ql_status qlinear_plan(int32_t fmt, int64_t M, int64_t N, int64_t K, ql_plan* out_plan);
 /* Like qlinear_plan, for weights packed with qlinear_pack_weight. */

@@ -106,9 +106,11 @@ struct ql_plan_s {
   ql_config cfg;
   int32_t source;
   // derived
-  int G, chunk_kb, chunks, mt, n_tiles, bn;
+  int G, chunk_kb, chunks, mt, n_tiles, bn, tiles_n;
   int64_t lds, ws_bytes, ws_acc_bytes;
+  bool tiled;
   qlk::DecodeKey key;
+  qlk::TiledKey tkey;
 };
 
 struct ql_graph_s {
@@ -118,7 +120,30 @@ struct ql_graph_s {
 
 namespace {
 
+// Tiled (M > 32): tile rows follow M, 128 weight rows per tile; split K
+// only while the tiles alone cannot give every CU two workgroups.
+ql_config heuristic_tiled(int32_t layout, int64_t M, int64_t N, int64_t K) {
+  ql_config c{};
+  c.algo = QL_ALGO_TILED;
+  c.w_layout = layout;
+  c.swap_ab = 1;
+  c.waves_n = 4;
+  c.waves_k = 1;
+  c.rows_per_wave = 16;
+  c.prefetch = 2;
+  c.tile_m = M <= 64 ? 64 : (M <= 128 ? 128 : 256);
+  c.tile_n = 128;
+  c.prefetch = c.tile_m == 64 ? 4 : (c.tile_m == 128 ? 2 : 1);
+  const int64_t G = (K + 127) / 128;
+  const int64_t tiles = ((M + c.tile_m - 1) / c.tile_m) * ((N + c.tile_n - 1) / c.tile_n);
+  int64_t split = 1;
+  while (tiles * split < 256 && split * 2 <= 256 && G / (split * 2) >= 8) split *= 2;
+  c.split_k = (int32_t)split;
+  return c;
+}
+
 ql_config heuristic_config(int32_t fmt, int32_t layout, int64_t M, int64_t N, int64_t K) {
+  if (M > 32) return heuristic_tiled(layout, M, N, K);
   ql_config c{};
   c.w_layout = layout;
   c.algo = QL_ALGO_DECODE;
@@ -141,6 +166,58 @@ ql_config heuristic_config(int32_t fmt, int32_t layout, int64_t M, int64_t N, in
   return c;
 }
 
+constexpr int64_t kTiledLdsLimit = 160 * 1024;  // gfx950: LDS per workgroup with the per-kernel opt-in
+
+ql_status build_tiled_plan(int32_t fmt, int64_t M, int64_t N, int64_t K, const ql_config& cfg, int32_t source,
+                           ql_plan* out) {
+  if (cfg.swap_ab != 0 && cfg.swap_ab != 1) return fail(QL_E_INVALID, "swap_ab must be 0 or 1");
+  if (!is_pow2(cfg.split_k) || cfg.split_k > 256) return fail(QL_E_INVALID, "split_k must be a power of two in [1, 256]");
+  if (cfg.tile_m != 64 && cfg.tile_m != 128 && cfg.tile_m != 256) return fail(QL_E_INVALID, "tile_m must be 64, 128 or 256");
+  if (cfg.tile_n != 128 && cfg.tile_n != 256) return fail(QL_E_INVALID, "tile_n must be 128 or 256");
+  if (cfg.w_layout != 0 && cfg.w_layout != 1) return fail(QL_E_INVALID, "w_layout must be 0 or 1");
+  if (cfg.prefetch != 1 && cfg.prefetch != 2 && cfg.prefetch != 4) return fail(QL_E_INVALID, "prefetch must be 1, 2 or 4");
+  ql_plan_s* p = new ql_plan_s();
+  p->fmt = fmt;
+  p->M = M;
+  p->N = N;
+  p->K = K;
+  p->cfg = cfg;
+  p->source = source;
+  p->tiled = true;
+  p->G = (int)((K + 127) / 128);
+  const int split = std::max(1, std::min<int>(cfg.split_k, std::max(1, p->G)));
+  p->chunk_kb = p->G > 0 ? (p->G + split - 1) / split : 0;
+  p->chunks = p->G > 0 ? (p->G + p->chunk_kb - 1) / p->chunk_kb : 1;
+  p->mt = 0;
+  p->bn = cfg.tile_n;
+  p->tiles_n = (int)((N + cfg.tile_n - 1) / cfg.tile_n);
+  p->n_tiles = (int)((M + cfg.tile_m - 1) / cfg.tile_m) * p->tiles_n;
+  p->lds = 2 * (int64_t)(cfg.tile_m + cfg.tile_n) * 128;
+  if (p->lds > kTiledLdsLimit) {
+    delete p;
+    return fail(QL_E_UNSUPPORTED, "tile needs more LDS than a workgroup has");
+  }
+  p->ws_acc_bytes = p->chunks > 1 ? ((M * N * 4 + 255) / 256) * 256 : 0;
+  p->ws_bytes = p->chunks > 1 ? p->ws_acc_bytes + (int64_t)p->n_tiles * 4 : 0;
+  p->key = qlk::DecodeKey{kernel_fmt(fmt), cfg.swap_ab, 0, 0, 4, 0, 0, 0};
+  p->tkey = qlk::TiledKey{kernel_fmt(fmt), cfg.swap_ab, cfg.tile_m, cfg.tile_n,
+                          cfg.w_layout ? qlk::W_PACKED : qlk::W_DIRECT, cfg.prefetch};
+  qlk::DecodeArgs dummy{};
+  hipError_t pe;
+  switch (p->tkey.fmt) {
+    case qlk::FMT_INT8: pe = qlk::tiled_dispatch_int8(p->tkey, dim3(1), (size_t)p->lds, nullptr, dummy, true); break;
+    case qlk::FMT_BLOCK: pe = qlk::tiled_dispatch_block(p->tkey, dim3(1), (size_t)p->lds, nullptr, dummy, true); break;
+    default: pe = qlk::tiled_dispatch_fp8(p->tkey, dim3(1), (size_t)p->lds, nullptr, dummy, true); break;
+  }
+  if (pe == hipErrorInvalidDeviceFunction) {
+    delete p;
+    return fail(QL_E_UNSUPPORTED, "no tiled kernel instantiated for tile %dx%d", cfg.tile_m, cfg.tile_n);
+  }
+  // any other error: raising the LDS limit needs a GPU; the launch reports it if it matters
+  *out = p;
+  return QL_OK;
+}
+
 ql_status build_plan(int32_t fmt, int64_t M, int64_t N, int64_t K, const ql_config& cfg, int32_t source,
                      ql_plan* out) {
   if (!out) return fail(QL_E_INVALID, "out_plan is NULL");
@@ -151,8 +228,8 @@ ql_status build_plan(int32_t fmt, int64_t M, int64_t N, int64_t K, const ql_conf
   if (M * N >= (int64_t(1) << 31)) return fail(QL_E_UNSUPPORTED, "M*N exceeds 2^31");
   if (cfg.w_layout == 1 && qlinear_packed_weight_bytes(N, K) > (int64_t(1) << 30))
     return fail(QL_E_UNSUPPORTED, "packed weights exceed 2^30 bytes");
-  if (cfg.algo != QL_ALGO_DECODE)
-    return fail(QL_E_UNSUPPORTED, "algo %d is not available in this build", cfg.algo);
+  if (cfg.algo == QL_ALGO_TILED) return build_tiled_plan(fmt, M, N, K, cfg, source, out);
+  if (cfg.algo != QL_ALGO_DECODE) return fail(QL_E_INVALID, "unknown algo %d", cfg.algo);
   if (M > 32) return fail(QL_E_UNSUPPORTED, "the decode algorithm serves M <= 32 (M=%lld)", (long long)M);
   if (cfg.swap_ab != 0 && cfg.swap_ab != 1) return fail(QL_E_INVALID, "swap_ab must be 0 or 1");
   if (!is_pow2(cfg.split_k) || cfg.split_k > 256) return fail(QL_E_INVALID, "split_k must be a power of two in [1, 256]");
@@ -257,8 +334,18 @@ ql_status launch_gemm(const ql_plan_s* p, const void* a_q, const float* a_scale,
   a.chunk_kb = p->chunk_kb;
   a.waves_k = p->cfg.waves_k;
   a.n_tiles = p->n_tiles;
-  const dim3 grid((unsigned)(p->n_tiles * p->chunks)), block((unsigned)p->key.nw * 64u);
+  a.tiles_n = p->tiles_n;
   hipError_t e;
+  if (p->tiled) {
+    const dim3 tgrid((unsigned)(p->n_tiles * p->chunks));
+    switch (p->tkey.fmt) {
+      case qlk::FMT_INT8: e = qlk::tiled_dispatch_int8(p->tkey, tgrid, (size_t)p->lds, s, a, false); break;
+      case qlk::FMT_BLOCK: e = qlk::tiled_dispatch_block(p->tkey, tgrid, (size_t)p->lds, s, a, false); break;
+      default: e = qlk::tiled_dispatch_fp8(p->tkey, tgrid, (size_t)p->lds, s, a, false); break;
+    }
+    return e == hipSuccess ? QL_OK : hip_fail(e, "tiled GEMM launch");
+  }
+  const dim3 grid((unsigned)(p->n_tiles * p->chunks)), block((unsigned)p->key.nw * 64u);
   switch (p->key.fmt) {
     case qlk::FMT_INT8: e = qlk::decode_dispatch_int8(p->key, grid, block, (size_t)p->lds, s, a, false); break;
     case qlk::FMT_BLOCK: e = qlk::decode_dispatch_block(p->key, grid, block, (size_t)p->lds, s, a, false); break;
@@ -412,7 +499,7 @@ ql_status qlinear_plan_info(ql_plan p, ql_config* cfg, ql_plan_facts* facts) {
     facts->chunks = p->chunks;
     facts->chunk_k = p->chunk_kb * 128;
     facts->workgroups = p->n_tiles * p->chunks;
-    facts->threads = p->key.nw * 64;
+    facts->threads = p->tiled ? 256 : p->key.nw * 64;
     facts->lds_bytes = (int32_t)p->lds;
     facts->workspace_bytes = p->ws_bytes;
   }

@@ -31,7 +31,8 @@ struct DecodeArgs {
   int split;           // number of K chunks (workgroups per output tile)
   int chunk_kb;        // K blocks per chunk; chunk c covers [c*chunk_kb, min(G, (c+1)*chunk_kb))
   int waves_k;         // waves of a workgroup that share one K chunk
-  int n_tiles;         // output tiles along N
+  int n_tiles;         // output tiles along N (decode) / all output tiles (tiled)
+  int tiles_n;         // tiled kernel: output tiles along N
 };
 
 // Compile-time shape of one decode kernel instantiation.
@@ -46,6 +47,16 @@ struct DecodeKey {
   int wm;    // weight mode: W_DIRECT / W_LDS_TRANSPOSE / W_PACKED
 };
 
+// Compile-time shape of one tiled (M > 32) kernel instantiation.
+struct TiledKey {
+  int fmt;   // FMT_FP8 / FMT_INT8 / FMT_BLOCK
+  int swap;  // weights as the matrix core's first operand
+  int bm;    // output tile rows (tokens): 64, 128 or 256
+  int bn;    // output tile columns (weight rows): 128 or 256
+  int wm;    // weight layout: W_DIRECT (row-major) or W_PACKED
+  int pf;    // K blocks in flight in the register ring: 1, 2 or 4
+};
+
 // Launch an instantiated kernel; returns hipErrorInvalidDeviceFunction when
 // the key has no instantiation.  `probe_only` checks without launching.
 hipError_t decode_dispatch_fp8(const DecodeKey& k, dim3 grid, dim3 block, size_t lds,
@@ -54,6 +65,15 @@ hipError_t decode_dispatch_int8(const DecodeKey& k, dim3 grid, dim3 block, size_
                                 hipStream_t s, const DecodeArgs& a, bool probe_only);
 hipError_t decode_dispatch_block(const DecodeKey& k, dim3 grid, dim3 block, size_t lds,
                                  hipStream_t s, const DecodeArgs& a, bool probe_only);
+
+// Tiled kernel launchers (tiled_*.hip); `probe_only` also raises the
+// kernel's dynamic LDS limit to `lds`.
+hipError_t tiled_dispatch_fp8(const TiledKey& k, dim3 grid, size_t lds, hipStream_t s, const DecodeArgs& a,
+                              bool probe_only);
+hipError_t tiled_dispatch_int8(const TiledKey& k, dim3 grid, size_t lds, hipStream_t s, const DecodeArgs& a,
+                               bool probe_only);
+hipError_t tiled_dispatch_block(const TiledKey& k, dim3 grid, size_t lds, hipStream_t s, const DecodeArgs& a,
+                                bool probe_only);
 
 // Quantizer launchers (quant.hip).
 hipError_t launch_quant_rows(int fmt, const void* x, int64_t R, int64_t C, void* q, float* s,

@@ -106,6 +106,16 @@ __device__ __forceinline__ uint32_t quant_code(float x, float s) {
   }
 }
 
+// Workgroup barrier that orders LDS accesses only.  __syncthreads() also
+// orders global memory, which makes every wave wait for all of its
+// outstanding global loads (vmcnt 0) first; here loads issued before the
+// barrier stay in flight across it.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));

@@ -1,0 +1,123 @@
+"""GPU parity of the tiled (M > 32) GEMM against the oracle.
+
+Every instantiation (format x orientation x tile x weight layout) runs on
+ragged shapes that span several tiles, with and without split-K; INT8 must be
+bit-exact on the raw int32 accumulators and on Y, FP8 / Block_FP8 inside the
+oracle's bound.  The large-M workloads (14B-class shapes at M = 64..4096) run
+at full size with the planner's configuration, checked on sampled columns.
+"""
+
+import itertools
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import quantized_gemm_decode_amd as ql
+from tests.gpu_util import dev_codes, dev_f32, fp8_check, host_bf16_bits, host_codes, requires_gpu, run_gemm
+from tests.test_gpu_gemm import _assert_parity
+from workloads import CONFIGS, bf16_bits, make_inputs
+
+pytestmark = [pytest.mark.gpu, requires_gpu]
+FMTS = [ql.FP8_DYNAMIC, ql.W8A8_INT8, ql.BLOCK_FP8]
+TILES = [(64, 128), (64, 256), (128, 128), (128, 256), (256, 128)]
+TVARIANTS = list(itertools.product([0, 1], TILES, [0, 1], [1, 2, 4]))   # swap x tile x packed weights x ring depth
+
+
+def _ref(fmt, M, N, K, seed):
+    x, w = make_inputs(K, N, M, 0.02, seed=seed)
+    return oracle.reference(fmt, bf16_bits(x), bf16_bits(w))
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("M", [40, 200])
+@pytest.mark.parametrize("vi", range(len(TVARIANTS)))
+def test_every_tiled_instantiation_matches_oracle(fmt, M, vi):
+    swap, (bm, bn), packed, pf = TVARIANTS[vi]
+    split = [1, 2, 4][(vi + M) % 3]
+    N = 300 if bn == 128 else 520                         # several tiles + a ragged tail
+    K = 1152 if fmt == ql.BLOCK_FP8 or vi % 2 else 1040   # 1040: ragged last K block (9 blocks: ring wraps)
+    r = _ref(fmt, M, N, K, seed=3000 + vi * 5 + M)
+    cfg = dict(algo=ql.ALGO_TILED, swap_ab=swap, split_k=split, tile_m=bm, tile_n=bn, w_layout=packed, prefetch=pf)
+    try:
+        plan = ql.qlinear_plan_with_config(fmt, M, N, K, cfg)
+    except ql.QLinearError as e:
+        assert e.status == 2, e
+        pytest.skip("tile not instantiated for this format: %s" % e)
+    a_q, s_a, w_q, s_w = (dev_codes(fmt, r["a_q"]), dev_f32(r["s_a"]), dev_codes(fmt, r["w_q"]), dev_f32(r["s_w"]))
+    if packed:
+        w_q = ql.pack_weight(w_q)
+    y, acc, ws = run_gemm(plan, a_q, s_a, w_q, s_w)
+    _assert_parity(fmt, r, y, acc, plan.facts["chunks"], label=str(cfg))
+    if ws is not None:
+        assert int(torch.count_nonzero(ws)) == 0, "split-K workspace not left all-zero"
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_tiled_matches_decode_bitwise_for_int8_and_closely_for_fp8(fmt):
+    """The same M = 32 problem through both algorithms: INT8 identical bits,
+    FP8 both inside the oracle bound (their summation orders differ)."""
+    M, N, K = 32, 384, 1280
+    r = _ref(fmt, M, N, K, seed=77)
+    a_q, s_a, w_q, s_w = (dev_codes(fmt, r["a_q"]), dev_f32(r["s_a"]), dev_codes(fmt, r["w_q"]), dev_f32(r["s_w"]))
+    pd = ql.qlinear_plan_with_config(fmt, M, N, K, dict(swap_ab=1, split_k=2, a_lds=0))
+    pt = ql.qlinear_plan_with_config(fmt, M, N, K, dict(algo=ql.ALGO_TILED, swap_ab=0, split_k=1, tile_m=64,
+                                                        tile_n=128, prefetch=4))
+    yd, accd, _ = run_gemm(pd, a_q, s_a, w_q, s_w)
+    yt, acct, _ = run_gemm(pt, a_q, s_a, w_q, s_w)
+    if fmt == ql.W8A8_INT8:
+        assert np.array_equal(accd, acct) and np.array_equal(yd, yt)
+    else:
+        assert fp8_check(fmt, r, yd, 2)["ok"] and fp8_check(fmt, r, yt, 1)["ok"]
+
+
+def test_planner_routes_large_m_to_the_tiled_algorithm():
+    p = ql.qlinear_plan(ql.FP8_DYNAMIC, 33, 4096, 4096)
+    assert p.config["algo"] == ql.ALGO_TILED and p.facts["threads"] == 256
+    p = ql.qlinear_plan(ql.FP8_DYNAMIC, 32, 4096, 4096)
+    assert p.config["algo"] == ql.ALGO_DECODE
+
+
+def _large_points():
+    cfg = CONFIGS[4]
+    pts = []
+    for (lab, N, K) in cfg.shapes:
+        for M in cfg.ms:
+            if M == 4096 and lab != "qkv":
+                continue              # one 4096-token shape keeps the suite short
+            pts.append((lab, N, K, M))
+    return pts
+
+
+_LARGE = {}
+
+
+@pytest.mark.parametrize("lab,N,K,M", _large_points())
+def test_large_m_workloads_sampled_columns(lab, N, K, M):
+    """14B-class FP8 shapes at full size with the planner's configuration
+    (packed weights); the oracle recomputes 64 sampled output columns."""
+    cfg = CONFIGS[4]
+    fmt = cfg.fmt
+    key = (lab, N, K)
+    if key not in _LARGE:
+        _LARGE.clear()
+        x, w = make_inputs(K, N, max(cfg.ms), cfg.sigma_w, seed=cfg.seed)
+        w_q, w_s = ql.quantize_weight(fmt, w.cuda())
+        _LARGE[key] = (x, w, ql.pack_weight(w_q), w_s)
+    x, w, w_p, w_s = _LARGE[key]
+    xm = x[:M]
+    a_q, a_s = ql.quantize_act(fmt, xm.cuda())
+    plan = ql.qlinear_plan_packed(fmt, M, N, K)
+    assert plan.config["algo"] == ql.ALGO_TILED
+    y = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
+    ql.qlinear_run(plan, a_q, a_s, w_p, w_s, y, plan.new_workspace())
+    torch.cuda.synchronize()
+    yb = host_bf16_bits(y)
+    rng = np.random.default_rng(M + N)
+    cols = np.sort(rng.choice(N, 64, replace=False))
+    rows = np.sort(rng.choice(M, min(M, 256), replace=False))
+    r = oracle.reference(fmt, bf16_bits(xm[torch.from_numpy(rows)]), bf16_bits(w[torch.from_numpy(cols)]))
+    assert np.array_equal(host_codes(fmt, a_q)[rows], r["a_q"])
+    st = fp8_check(fmt, r, yb[np.ix_(rows, cols)], plan.facts["chunks"])
+    assert st["ok"] and st["frac_within_ulp"] >= 0.95, (plan.config, st)
