@@ -8,7 +8,12 @@ projections -- QKV 6144x4096, O 4096x4096, gate_up 24576x4096, down
 
 One step = the whole hot path for every point: dynamic activation quantizer,
 then the planned GEMM (standard / split-K / swap-AB from the sweep table),
-captured once into hipGraphs and replayed.  Inputs are synthetic and resident
+captured once into hipGraphs and replayed.  By default the weights are packed
+offline (qlinear_pack_weight) and the quantizer writes packed activations, so
+every operand load of the GEMM is a contiguous kilobyte; --layout selects the
+row-major paths instead.  --workload fp8_dynamic_14b_large_m runs the
+M = 64..4096 points through the tiled kernel and prices them against the
+matrix-core peak instead of HBM.  Inputs are synthetic and resident
 in HBM before timing.  Every GEMM of a step reads its own copy of the weights
 (at least 1 GiB of copies per shape), so the 256 MB Infinity Cache cannot
 serve them: the measured bandwidth is HBM bandwidth.
@@ -27,6 +32,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+MFMA_FP8_PEAK_TFLOPS = 5000.0   # MI355X dense e4m3 (and int8) matrix-core peak
 METRIC = "µs/GEMM & achieved HBM GB/s (fraction of peak), M=1–32, fp8/int8 decode shapes"
 
 
@@ -42,6 +48,8 @@ def quantizer_bytes(fmt, M, K):
 
 
 PKG = os.path.join(ROOT, "quantized_gemm_decode_amd")
+LAYOUT_NAMES = {"packed": "packed weights and activations", "packedw": "packed weights, row-major activations",
+                "rowmajor": "row-major weights and activations"}
 PROFILES = os.path.join(ROOT, "profiles")
 
 
@@ -101,7 +109,7 @@ def pmc_summary(workload, layout, fetch_csv, write_csv):
            for a, b in zip(fr, wr) if "qgemm" in a["Kernel_Name"]]
     pts = decode_points(wl)
     gem = gem[-3 * len(pts):]
-    lines = ["# HBM traffic of the decode GEMM kernels, workload %s, %s weights" % (workload, layout),
+    lines = ["# HBM traffic of the decode GEMM kernels, workload %s, %s" % (workload, LAYOUT_NAMES[layout]),
              "# commands (run from /tmp with TMPDIR=/tmp):",
              "#   rocprofv3 --pmc FETCH_SIZE -f csv -d <dir_f> -o fetch -- python3 <repo>/bench.py --workload %s "
              "--layout %s --profile-pass" % (workload, layout),
@@ -130,7 +138,7 @@ def pmc_summary(workload, layout, fetch_csv, write_csv):
     return "\n".join(lines) + "\n"
 
 
-def trace_summary(workload, layout, trace_csv, stats_csv, bench_json):
+def trace_summary(workload, layout, trace_csv, stats_csv, bench_json, ref_json=None):
     """Per-point kernel durations from a rocprofv3 --kernel-trace run of this script,
     next to the HIP-event per-launch times the same run printed."""
     import csv
@@ -154,13 +162,14 @@ def trace_summary(workload, layout, trace_csv, stats_csv, bench_json):
     if cur:
         runs.append(cur)
     runs = runs[-len(pp):]
-    lines = ["# rocprofv3 kernel trace of the decode GEMM, workload %s, %s weights" % (workload, layout),
+    lines = ["# rocprofv3 kernel trace of the GEMM kernels, workload %s, %s" % (workload, LAYOUT_NAMES[layout]),
              "# command (from /tmp with TMPDIR=/tmp):",
              "#   rocprofv3 --kernel-trace --stats -f csv -d <dir> -o bench -- python3 <repo>/bench.py --workload %s "
              "--layout %s --steps %d --warmup %d --kernel-reps %d --no-cpu-baseline"
              % (workload, layout, bench["steps"], bench["warmup"], bench.get("kernel_reps", 5)),
              "#   python3 bench.py --workload %s --layout %s --trace-summary <dir>/bench_kernel_trace.csv "
-             "<dir>/bench_kernel_stats.csv <stdout of the command above>" % (workload, layout),
+             "<dir>/bench_kernel_stats.csv <stdout of the command above> [--trace-ref <json of a plain run>]"
+             % (workload, layout),
              "# per point: rocprof = mean kernel duration over the timed replays (last kernel-reps x R launches);",
              "# hip_events = the same run's HIP-event time per launch (median of replays / R)",
              "# shape    M    kernel_instantiation                                   rocprof_us  hip_events_us  ratio"]
@@ -178,6 +187,13 @@ def trace_summary(workload, layout, trace_csv, stats_csv, bench_json):
     lines.append("# achieved (algorithmic bytes / rocprof durations): %.1f GB/s; bench roofline.achieved: %.1f GB/s"
                  % (bench["roofline"]["algorithmic_bytes"] / (tot_r * 1e-6) / 1e9
                     if "algorithmic_bytes" in bench["roofline"] else float("nan"), bench["roofline"]["achieved"]))
+    if ref_json:
+        ref = json.loads(open(ref_json).read().strip().splitlines()[-1])
+        ref_pp = {(q["shape"], q["M"]): q["us"] for q in ref["per_point"]}
+        tot_ref = sum(ref_pp.get((p["shape"], p["M"]), float("nan")) for p in pp)
+        lines.append("# the same bench without the profiler (%s): roofline.achieved %.1f GB/s; its per-launch "
+                     "times sum to %.2f us, %.3f x the rocprof kernel durations above"
+                     % (os.path.basename(ref_json), ref["roofline"]["achieved"], tot_ref, tot_ref / tot_r))
     lines.append("# rocprofv3 --stats kernel summary (all launches of the run, every phase):")
     for line in open(stats_csv):
         lines.append("#   " + line.rstrip())
@@ -190,8 +206,9 @@ def parse_args(argv=None):
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="fp8_dynamic_8b")
-    ap.add_argument("--layout", choices=("packed", "rowmajor"), default="packed",
-                    help="weight layout: packed tiles (qlinear_pack_weight, offline) or row-major W_q[N,K]")
+    ap.add_argument("--layout", choices=("packed", "packedw", "rowmajor"), default="packed",
+                    help="operand layouts: packed weights (qlinear_pack_weight, offline) and packed activations "
+                         "(the quantizer writes them), packed weights only, or row-major both")
     ap.add_argument("--kernel-reps", type=int, default=30, help="graph replays per point for kernel timing")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=20.0)
@@ -201,6 +218,8 @@ def parse_args(argv=None):
                     help="print the HBM-traffic record from two rocprofv3 --pmc runs of --profile-pass, and exit")
     ap.add_argument("--trace-summary", nargs=3, metavar=("TRACE_CSV", "STATS_CSV", "BENCH_STDOUT"),
                     help="print per-point rocprofv3 kernel durations next to the HIP-event times, and exit")
+    ap.add_argument("--trace-ref", default=None, metavar="BENCH_JSON",
+                    help="with --trace-summary: an unprofiled run's JSON line to set beside the trace")
     ap.add_argument("--profile-pass", action="store_true",
                     help="for hardware-counter runs: launch each point's quantize+GEMM eagerly on 3 weight "
                          "copies, then a plain 256 MiB device copy 3 times (the counters' calibration), and exit")
@@ -216,7 +235,7 @@ def main(argv=None):
         return 2
 
     if args.trace_summary:
-        sys.stdout.write(trace_summary(args.workload, args.layout, *args.trace_summary))
+        sys.stdout.write(trace_summary(args.workload, args.layout, *args.trace_summary, ref_json=args.trace_ref))
         return 0
     if args.pmc_summary:
         sys.stdout.write(pmc_summary(args.workload, args.layout, *args.pmc_summary))
@@ -246,7 +265,7 @@ def main(argv=None):
         x, w = make_inputs(K, N, max(wl.ms), wl.sigma_w, seed=wl.seed)
         wd = w.to(dev)
         w_q, w_s = ql.quantize_weight(fmt, wd)
-        if args.layout == "packed":
+        if args.layout != "rowmajor":
             w_q = ql.pack_weight(w_q)          # offline, like the quantization itself
         del wd
         copies = max(2, -(-(1 << 30) // (N * K)))
@@ -261,11 +280,12 @@ def main(argv=None):
     pts = []
     for (lab, N, K, M) in points:
         sh = shapes[lab]
-        plan = ql.qlinear_plan_packed(fmt, M, N, K) if args.layout == "packed" else ql.qlinear_plan(fmt, M, N, K)
+        w_layout, a_packed = {"packed": (1, 1), "packedw": (1, 0), "rowmajor": (0, 0)}[args.layout]
+        plan = ql.qlinear_plan_layouts(fmt, M, N, K, w_layout, a_packed)
         cfg, facts = plan.info()
         pts.append(dict(lab=lab, N=N, K=K, M=M, plan=plan, cfg=cfg, facts=facts,
                         x=sh["x"][:M].contiguous(),
-                        a_q=torch.empty(M, K, dtype=ql.code_dtype(fmt), device=dev),
+                        a_q=ql.act_buffer(plan, dev),
                         a_s=torch.empty(ql.act_scale_shape(fmt, M, K), dtype=torch.float32, device=dev),
                         y=torch.empty(M, N, dtype=torch.bfloat16, device=dev),
                         wsp=plan.new_workspace(dev),
@@ -307,7 +327,7 @@ def main(argv=None):
     # ------------------------------------------------ per-point GEMM kernel timing (HIP events)
     reps = args.kernel_reps
     per_point = []
-    tot_bytes = tot_us = 0.0
+    tot_bytes = tot_us = tot_flops = 0.0
     for p in pts:
         sh = shapes[p["lab"]]
         R = min(sh["copies"], 64)
@@ -317,7 +337,10 @@ def main(argv=None):
                 ql.qlinear_run(p["plan"], p["a_q"], p["a_s"], sh["wq"][c], sh["ws"][c], p["y"], p["wsp"],
                                stream=stream)
             g = ql.qlinear_graph_end(stream)
-            ql.qlinear_quantize_act(fmt, p["x"], p["a_q"], p["a_s"], stream=stream)
+            if p["cfg"]["a_mode"] == 2:
+                ql.qlinear_quantize_act_packed(fmt, p["x"], p["a_q"], p["a_s"], stream=stream)
+            else:
+                ql.qlinear_quantize_act(fmt, p["x"], p["a_q"], p["a_s"], stream=stream)
         for _ in range(3):
             g.launch(stream)
         stream.synchronize()
@@ -332,12 +355,15 @@ def main(argv=None):
             samples.append(e0.elapsed_time(e1) * 1e3 / R)
         us = float(np.median(samples))
         gbs = p["bytes"] / (us * 1e-6) / 1e9
+        flops = 2.0 * p["M"] * p["N"] * p["K"]
         tot_bytes += p["bytes"]
+        tot_flops += flops
         tot_us += us
         per_point.append(dict(shape=p["lab"], M=p["M"], N=p["N"], K=p["K"], us=round(us, 3),
                               us_p10=round(float(np.percentile(samples, 10)), 3),
                               us_p90=round(float(np.percentile(samples, 90)), 3),
                               GBs=round(gbs, 1), frac=round(gbs / HBM_PEAK_GBS, 4),
+                              TFLOPs=round(flops / (us * 1e-6) / 1e12, 1), algo=p["cfg"]["algo"],
                               variant=("split-k" if p["facts"]["chunks"] > 1 else
                                        ("swap-ab" if p["cfg"]["swap_ab"] else "standard")),
                               split=p["facts"]["chunks"], swap_ab=p["cfg"]["swap_ab"],
@@ -345,6 +371,24 @@ def main(argv=None):
         del g
     achieved = tot_bytes / (tot_us * 1e-6) / 1e9
     traffic, traffic_note = recorded_traffic(wl.name, args.layout)
+    if max(wl.ms) <= 32:
+        roofline = {"kernel": "qgemm_decode_kernel", "bound": "hbm", "achieved": round(achieved, 1),
+                    "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                    "traffic": traffic, "algorithmic_bytes": int(tot_bytes), "traffic_source": traffic_note,
+                    "note": "algorithmic bytes of one launch of each of the %d GEMMs / sum of their per-launch "
+                            "durations (HIP events around graph replays of back-to-back launches); traffic is "
+                            "the HBM bytes those same %d launches moved" % (len(pts), len(pts))}
+    else:
+        # token counts in the hundreds and thousands: the tiled kernel is matrix-core bound
+        big = [q for q in per_point if q["M"] >= 1024]
+        fl = sum(2.0 * q["M"] * q["N"] * q["K"] for q in big)
+        t = sum(q["us"] for q in big) * 1e-6
+        tflops = fl / t / 1e12
+        roofline = {"kernel": "qgemm_tiled_kernel", "bound": "mfma", "achieved": round(tflops, 1),
+                    "peak": MFMA_FP8_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(tflops / MFMA_FP8_PEAK_TFLOPS, 4),
+                    "traffic": traffic, "traffic_source": traffic_note,
+                    "note": "2*M*N*K of one launch of each M >= 1024 GEMM / sum of their per-launch durations; "
+                            "the M = 64 and 256 points are HBM- or ridge-bound and are reported per point"}
 
     # ------------------------------------------------ CPU oracle baseline (bounded sample)
     cpu = None
@@ -370,12 +414,7 @@ def main(argv=None):
                    "gemms_per_step": len(pts), "graph_replay": True, "table_entries": n_table,
                    "weight_layout": args.layout,
                    "us_per_gemm_step_avg": round(step_ms * 1e3 / len(pts), 3)},
-        "roofline": {"kernel": "qgemm_decode_kernel", "bound": "hbm", "achieved": round(achieved, 1),
-                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": traffic, "algorithmic_bytes": int(tot_bytes), "traffic_source": traffic_note,
-                     "note": "algorithmic bytes of one launch of each of the %d GEMMs / sum of their per-launch "
-                             "durations (HIP events around graph replays of back-to-back launches); traffic is "
-                             "the HBM bytes those same %d launches moved" % (len(pts), len(pts))},
+        "roofline": roofline,
         "cpu_baseline": cpu,
         "per_point": per_point,
         "wall_s": round(wall, 3),
@@ -432,6 +471,8 @@ def cpu_baseline(wl, shapes, budget_s):
         x, w = make_inputs(K, N, max(wl.ms), wl.sigma_w, seed=wl.seed)
         w_q, s_w = oracle.quantize_weight(fmt, bf16_bits(w))          # offline step: not timed
         for M in wl.ms:
+            if 2.0 * M * N * K > 50e9:
+                continue       # a single fp64 GEMM of minutes: outside the bounded sample
             xb = bf16_bits(x[:M])
             t0 = time.perf_counter()
             a_q, s_a = oracle.quantize_act(fmt, xb)

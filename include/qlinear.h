@@ -110,7 +110,9 @@ typedef struct {
   int32_t rows_per_wave; /* DECODE: 16, 32 or 64 weight rows per wave */
   int32_t prefetch;      /* DECODE: 128-wide K blocks per wave and batch, two batches in flight (1, 2 or 4);
                             TILED: 128-wide K blocks in flight per workgroup (1, 2 or 4) */
-  int32_t a_lds;         /* DECODE: 1 = stage the activation chunk in LDS, 0 = read it per K block */
+  int32_t a_mode;        /* activations: 0 = row-major A_q read per K block; 1 (DECODE) = row-major
+                            A_q chunk staged in LDS; 2 = packed A_q (qlinear_quantize_act_packed)
+                            read per K block */
   int32_t w_lds;         /* DECODE, row-major weights: 1 = coalesced weight loads (8 rows x 128 B
                             per instruction) transposed to the matrix-core layout through LDS;
                             0 = direct loads in operand order */
@@ -119,7 +121,8 @@ typedef struct {
   int32_t tile_m;        /* TILED: workgroup tile rows (tokens): 64, 128 or 256 */
   int32_t tile_n;        /* TILED: workgroup tile columns (weight rows): 128 or 256;
                             tile_m * tile_n <= 32768.  TILED reads swap_ab, split_k,
-                            w_layout, prefetch and the tile; the other fields are ignored */
+                            a_mode (0 or 2), w_layout, prefetch and the tile; the other
+                            fields are ignored */
 } ql_config;
 
 /* Derived launch facts of a plan (read-only). */
@@ -154,6 +157,19 @@ ql_status qlinear_quantize_act(int32_t fmt, const void* x_bf16, int64_t M, int64
                                void* a_q, float* a_scale, void* stream);
 
 /*
+ * The same quantizer writing the packed activation layout that plans with
+ * a_mode = 2 read: the weight packing below applied to A_q, i.e. 2 KB tiles
+ * (t, kb) of 16 tokens x 128 K at byte (t * ceil(K/128) + kb) * 2048, tile
+ * byte h*1024 + l*16 + j = A_q[16t + l%16][128kb + 64h + 16*(l/16) + j], zero
+ * for tokens >= M and K beyond K.  Every activation load of the GEMM then
+ * reads one contiguous kilobyte.  a_packed holds qlinear_packed_act_bytes(M, K)
+ * bytes; a_scale is as for qlinear_quantize_act.  Same codes, same scales.
+ */
+int64_t qlinear_packed_act_bytes(int64_t M, int64_t K);
+ql_status qlinear_quantize_act_packed(int32_t fmt, const void* x_bf16, int64_t M, int64_t K,
+                                      void* a_packed, float* a_scale, void* stream);
+
+/*
  * Offline weight quantizer: per output channel (rows of W) or per 128x128
  * block for Block_FP8 (the last block row may be ragged).
  *   w_bf16 [N, K] in;  w_q [N, K] out;  w_scale fp32 [N] or [ceil(N/128), K/128] out.
@@ -180,8 +196,9 @@ ql_status qlinear_pack_weight(const void* w_q, int64_t N, int64_t K, void* w_pac
  * Offline sweep table ([Summary] "Hybrid dispatch addresses runtime
  * overhead": per-shape, per-token-count tuned configurations).  Text file,
  * one entry per line: fmt M N K algo swap_ab split_k waves_n waves_k
- * rows_per_wave prefetch a_lds w_lds w_layout tile_m tile_n [time_us]; '#'
- * starts a comment.  Entries are looked up for the weight layout asked for.
+ * rows_per_wave prefetch a_mode w_lds w_layout tile_m tile_n [time_us]; '#'
+ * starts a comment.  Entries are looked up for the operand layouts asked for
+ * (w_layout, and packed activations = a_mode 2).
  * Loading replaces the in-process table.  Returns the entry count via n_entries.
  */
 ql_status qlinear_table_load(const char* path, int64_t* n_entries);
@@ -192,15 +209,23 @@ void qlinear_table_clear(void);
  * next tuned token bucket {1,2,4,8,16,24,32} (M > 32: the nearest tuned M at
  * or above, else the largest); without an entry a built-in heuristic is used
  * (facts.source tells which).  The environment variable QLINEAR_FORCE =
- * "algo,swap,split,wn,wk,rows,prefetch,alds,wlds,wlayout,tile_m,tile_n"
- * overrides both (its w_layout must match the call).  M <= 32 plans use the
- * DECODE algorithm, M > 32 the TILED one.
+ * "algo,swap,split,wn,wk,rows,prefetch,amode,wlds,wlayout,tile_m,tile_n"
+ * overrides both (its operand layouts must match the call).  M <= 32 plans
+ * use the DECODE algorithm, M > 32 the TILED one.  qlinear_plan: row-major
+ * W_q and A_q.
  * Host-only: nothing is enqueued and nothing is allocated (a TILED plan
  * raises its kernel's dynamic LDS limit with hipFuncSetAttribute).
  */
 ql_status qlinear_plan(int32_t fmt, int64_t M, int64_t N, int64_t K, ql_plan* out_plan);
-/* Like qlinear_plan, for weights packed with qlinear_pack_weight. */
+/* Like qlinear_plan, for weights packed with qlinear_pack_weight (row-major A_q). */
 ql_status qlinear_plan_packed(int32_t fmt, int64_t M, int64_t N, int64_t K, ql_plan* out_plan);
+/*
+ * Like qlinear_plan for any operand layouts: w_layout 0 = row-major W_q,
+ * 1 = packed weights; a_packed 0 = row-major A_q (qlinear_quantize_act),
+ * 1 = packed A_q (qlinear_quantize_act_packed; the plan's a_mode is 2).
+ */
+ql_status qlinear_plan_layouts(int32_t fmt, int64_t M, int64_t N, int64_t K, int32_t w_layout,
+                               int32_t a_packed, ql_plan* out_plan);
 /* Like qlinear_plan (row-major weights) but only from the table; QL_E_NO_TABLE_ENTRY when absent. */
 ql_status qlinear_plan_from_table(int32_t fmt, int64_t M, int64_t N, int64_t K, ql_plan* out_plan);
 /* Plan with an explicit configuration (validated; QL_E_INVALID / QL_E_UNSUPPORTED on a bad one). */
@@ -226,6 +251,8 @@ void qlinear_plan_destroy(ql_plan plan);
  * with an exact int32 accumulator; FP8_Dynamic the same on the fp32
  * accumulator; Block_FP8 applies s_a[m,g] * s_w[n/128,g] to every 128-wide K
  * group's partial inside the K loop and rounds the fp32 sum to bf16.
+ * a_q is in the plan's activation layout: row-major [M, K], or packed when
+ * the plan's a_mode is 2; w_q in the plan's weight layout (w_layout).
  * Enqueue-only; workspace may be NULL when qlinear_workspace_bytes is 0.
  */
 ql_status qlinear_run(ql_plan plan, const void* a_q, const float* a_scale,
@@ -243,7 +270,9 @@ ql_status qlinear_run_debug_acc(ql_plan plan, const void* a_q, const float* a_sc
 
 /*
  * Quantize the activations, then run the GEMM: the whole decode step of one
- * linear layer.  a_q / a_scale are caller-owned staging buffers.
+ * linear layer.  a_q / a_scale are caller-owned staging buffers; a_q is
+ * written in the plan's activation layout (qlinear_packed_act_bytes(M, K)
+ * bytes when a_mode is 2, else M*K).
  */
 ql_status qlinear_forward(ql_plan plan, const void* x_bf16, void* a_q, float* a_scale,
                           const void* w_q, const float* w_scale, void* y_bf16,

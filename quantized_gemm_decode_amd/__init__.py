@@ -93,6 +93,18 @@ def qlinear_quantize_act(fmt, x, a_q, a_scale, stream=None):
            "qlinear_quantize_act")
 
 
+def qlinear_packed_act_bytes(M, K):
+    return int(lib().qlinear_packed_act_bytes(M, K))
+
+
+def qlinear_quantize_act_packed(fmt, x, a_packed, a_scale, stream=None):
+    M, K = x.shape
+    _check(lib().qlinear_quantize_act_packed(fmt, _ptr(x, "x", torch.bfloat16), M, K,
+                                             _ptr(a_packed, "a_packed", CODE_DTYPES),
+                                             _ptr(a_scale, "a_scale", torch.float32), _stream(stream)),
+           "qlinear_quantize_act_packed")
+
+
 def qlinear_quantize_weight(fmt, w, w_q, w_scale, stream=None):
     N, K = w.shape
     _check(lib().qlinear_quantize_weight(fmt, _ptr(w, "w", torch.bfloat16), N, K, _ptr(w_q, "w_q", CODE_DTYPES),
@@ -107,6 +119,21 @@ def quantize_act(fmt, x, stream=None):
     a_s = torch.empty(act_scale_shape(fmt, M, K), dtype=torch.float32, device=x.device)
     qlinear_quantize_act(fmt, x, a_q, a_s, stream)
     return a_q, a_s
+
+
+def quantize_act_packed(fmt, x, stream=None):
+    """Allocate (packed A_q as a flat code buffer, s_a) and run the packed-layout quantizer."""
+    M, K = x.shape
+    a_p = torch.empty(max(qlinear_packed_act_bytes(M, K), 16), dtype=code_dtype(fmt), device=x.device)
+    a_s = torch.empty(act_scale_shape(fmt, M, K), dtype=torch.float32, device=x.device)
+    qlinear_quantize_act_packed(fmt, x, a_p, a_s, stream)
+    return a_p, a_s
+
+
+def act_buffer(plan, device="cuda"):
+    """Activation code buffer in the plan's layout (packed when its a_mode is 2)."""
+    n = qlinear_packed_act_bytes(plan.M, plan.K) if plan.config["a_mode"] == 2 else plan.M * plan.K
+    return torch.empty(max(n, 16), dtype=code_dtype(plan.fmt), device=device)
 
 
 def quantize_weight(fmt, w, stream=None):
@@ -207,6 +234,14 @@ def qlinear_plan_packed(fmt, M, N, K):
     return Plan(h.value, fmt, M, N, K)
 
 
+def qlinear_plan_layouts(fmt, M, N, K, w_layout, a_packed):
+    """Plan for the given operand layouts (w_layout: 0 row-major, 1 packed weights;
+    a_packed: 0 row-major A_q, 1 packed A_q from qlinear_quantize_act_packed)."""
+    h = ctypes.c_void_p()
+    _check(lib().qlinear_plan_layouts(fmt, M, N, K, w_layout, a_packed, ctypes.byref(h)), "qlinear_plan_layouts")
+    return Plan(h.value, fmt, M, N, K)
+
+
 def qlinear_plan_from_table(fmt, M, N, K):
     h = ctypes.c_void_p()
     _check(lib().qlinear_plan_from_table(fmt, M, N, K, ctypes.byref(h)), "qlinear_plan_from_table")
@@ -215,7 +250,7 @@ def qlinear_plan_from_table(fmt, M, N, K):
 
 def make_config(**kw):
     base = dict(algo=ALGO_DECODE, swap_ab=0, split_k=1, waves_n=4, waves_k=1, rows_per_wave=16, prefetch=2,
-                a_lds=1, w_lds=0, w_layout=0, tile_m=0, tile_n=0)
+                a_mode=0, w_lds=0, w_layout=0, tile_m=0, tile_n=0)
     unknown = set(kw) - set(base)
     if unknown:
         raise ValueError("unknown config fields %s" % sorted(unknown))

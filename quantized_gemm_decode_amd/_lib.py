@@ -11,7 +11,7 @@ c_i32, c_i64, c_vp, c_cp = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p, ctyp
 
 class QLConfig(ctypes.Structure):
     _fields_ = [(n, c_i32) for n in ("algo", "swap_ab", "split_k", "waves_n", "waves_k", "rows_per_wave",
-                                     "prefetch", "a_lds", "w_lds", "w_layout", "tile_m", "tile_n")]
+                                     "prefetch", "a_mode", "w_lds", "w_layout", "tile_m", "tile_n")]
 
 
 class QLPlanFacts(ctypes.Structure):
@@ -26,12 +26,15 @@ SIGNATURES = {
     "qlinear_last_error": (c_cp, []),
     "qlinear_quantize_act": (c_i32, [c_i32, c_vp, c_i64, c_i64, c_vp, c_vp, c_vp]),
     "qlinear_quantize_weight": (c_i32, [c_i32, c_vp, c_i64, c_i64, c_vp, c_vp, c_vp]),
+    "qlinear_packed_act_bytes": (c_i64, [c_i64, c_i64]),
+    "qlinear_quantize_act_packed": (c_i32, [c_i32, c_vp, c_i64, c_i64, c_vp, c_vp, c_vp]),
     "qlinear_packed_weight_bytes": (c_i64, [c_i64, c_i64]),
     "qlinear_pack_weight": (c_i32, [c_vp, c_i64, c_i64, c_vp, c_vp]),
     "qlinear_table_load": (c_i32, [c_cp, ctypes.POINTER(c_i64)]),
     "qlinear_table_clear": (None, []),
     "qlinear_plan": (c_i32, [c_i32, c_i64, c_i64, c_i64, ctypes.POINTER(c_vp)]),
     "qlinear_plan_packed": (c_i32, [c_i32, c_i64, c_i64, c_i64, ctypes.POINTER(c_vp)]),
+    "qlinear_plan_layouts": (c_i32, [c_i32, c_i64, c_i64, c_i64, c_i32, c_i32, ctypes.POINTER(c_vp)]),
     "qlinear_plan_from_table": (c_i32, [c_i32, c_i64, c_i64, c_i64, ctypes.POINTER(c_vp)]),
     "qlinear_plan_with_config": (c_i32, [c_i32, c_i64, c_i64, c_i64, ctypes.POINTER(QLConfig),
                                          ctypes.POINTER(c_vp)]),

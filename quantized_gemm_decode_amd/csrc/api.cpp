@@ -79,13 +79,13 @@ int64_t bucket_of(int64_t M) {
   return M;
 }
 
-bool table_lookup(int32_t fmt, int32_t layout, int64_t M, int64_t N, int64_t K, ql_config* out) {
+bool table_lookup(int32_t fmt, int32_t layout, bool a_packed, int64_t M, int64_t N, int64_t K, ql_config* out) {
   std::lock_guard<std::mutex> lk(g_table_mu);
   const int64_t want = bucket_of(M);
   const TableEntry* best = nullptr;
   const TableEntry* largest = nullptr;
   for (const TableEntry& e : g_table) {
-    if (e.fmt != fmt || e.N != N || e.K != K || e.cfg.w_layout != layout) continue;
+    if (e.fmt != fmt || e.N != N || e.K != K || e.cfg.w_layout != layout || (e.cfg.a_mode == 2) != a_packed) continue;
     if (e.M >= want && (!best || e.M < best->M)) best = &e;
     if (!largest || e.M > largest->M) largest = &e;
   }
@@ -122,10 +122,11 @@ namespace {
 
 // Tiled (M > 32): tile rows follow M, 128 weight rows per tile; split K
 // only while the tiles alone cannot give every CU two workgroups.
-ql_config heuristic_tiled(int32_t layout, int64_t M, int64_t N, int64_t K) {
+ql_config heuristic_tiled(int32_t layout, bool a_packed, int64_t M, int64_t N, int64_t K) {
   ql_config c{};
   c.algo = QL_ALGO_TILED;
   c.w_layout = layout;
+  c.a_mode = a_packed ? 2 : 0;
   c.swap_ab = 1;
   c.waves_n = 4;
   c.waves_k = 1;
@@ -142,8 +143,8 @@ ql_config heuristic_tiled(int32_t layout, int64_t M, int64_t N, int64_t K) {
   return c;
 }
 
-ql_config heuristic_config(int32_t fmt, int32_t layout, int64_t M, int64_t N, int64_t K) {
-  if (M > 32) return heuristic_tiled(layout, M, N, K);
+ql_config heuristic_config(int32_t fmt, int32_t layout, bool a_packed, int64_t M, int64_t N, int64_t K) {
+  if (M > 32) return heuristic_tiled(layout, a_packed, M, N, K);
   ql_config c{};
   c.w_layout = layout;
   c.algo = QL_ALGO_DECODE;
@@ -160,7 +161,7 @@ ql_config heuristic_config(int32_t fmt, int32_t layout, int64_t M, int64_t N, in
   c.split_k = (int32_t)split;
   const int64_t chunk_kb = (G + split - 1) / split;
   const int64_t mt = M <= 16 ? 1 : 2;
-  c.a_lds = chunk_kb * mt * 2048 <= kLdsLimit ? 1 : 0;
+  c.a_mode = a_packed ? 2 : (chunk_kb * mt * 2048 <= kLdsLimit ? 1 : 0);
   c.w_lds = 0;
   (void)fmt;
   return c;
@@ -176,6 +177,9 @@ ql_status build_tiled_plan(int32_t fmt, int64_t M, int64_t N, int64_t K, const q
   if (cfg.tile_n != 128 && cfg.tile_n != 256) return fail(QL_E_INVALID, "tile_n must be 128 or 256");
   if (cfg.w_layout != 0 && cfg.w_layout != 1) return fail(QL_E_INVALID, "w_layout must be 0 or 1");
   if (cfg.prefetch != 1 && cfg.prefetch != 2 && cfg.prefetch != 4) return fail(QL_E_INVALID, "prefetch must be 1, 2 or 4");
+  if (cfg.a_mode != 0 && cfg.a_mode != 2) return fail(QL_E_INVALID, "a_mode must be 0 or 2 for the tiled algorithm");
+  if (cfg.a_mode == 2 && qlinear_packed_act_bytes(M, K) > (int64_t(1) << 30))
+    return fail(QL_E_UNSUPPORTED, "packed activations exceed 2^30 bytes");
   ql_plan_s* p = new ql_plan_s();
   p->fmt = fmt;
   p->M = M;
@@ -201,7 +205,7 @@ ql_status build_tiled_plan(int32_t fmt, int64_t M, int64_t N, int64_t K, const q
   p->ws_bytes = p->chunks > 1 ? p->ws_acc_bytes + (int64_t)p->n_tiles * 4 : 0;
   p->key = qlk::DecodeKey{kernel_fmt(fmt), cfg.swap_ab, 0, 0, 4, 0, 0, 0};
   p->tkey = qlk::TiledKey{kernel_fmt(fmt), cfg.swap_ab, cfg.tile_m, cfg.tile_n,
-                          cfg.w_layout ? qlk::W_PACKED : qlk::W_DIRECT, cfg.prefetch};
+                          cfg.w_layout ? qlk::W_PACKED : qlk::W_DIRECT, cfg.prefetch, cfg.a_mode == 2 ? 1 : 0};
   qlk::DecodeArgs dummy{};
   hipError_t pe;
   switch (p->tkey.fmt) {
@@ -239,7 +243,10 @@ ql_status build_plan(int32_t fmt, int64_t M, int64_t N, int64_t K, const ql_conf
   if (cfg.rows_per_wave != 16 && cfg.rows_per_wave != 32 && cfg.rows_per_wave != 64)
     return fail(QL_E_INVALID, "rows_per_wave must be 16, 32 or 64");
   if (cfg.prefetch != 1 && cfg.prefetch != 2 && cfg.prefetch != 4) return fail(QL_E_INVALID, "prefetch must be 1, 2 or 4");
-  if (cfg.a_lds != 0 && cfg.a_lds != 1) return fail(QL_E_INVALID, "a_lds must be 0 or 1");
+  if (cfg.a_mode < 0 || cfg.a_mode > 2) return fail(QL_E_INVALID, "a_mode must be 0, 1 or 2");
+  if (cfg.a_mode == 2 && !cfg.w_layout) return fail(QL_E_UNSUPPORTED, "packed activations need packed weights");
+  if (cfg.a_mode == 2 && qlinear_packed_act_bytes(M, K) > (int64_t(1) << 30))
+    return fail(QL_E_UNSUPPORTED, "packed activations exceed 2^30 bytes");
   if (cfg.w_lds != 0 && cfg.w_lds != 1) return fail(QL_E_INVALID, "w_lds must be 0 or 1");
   if (cfg.w_layout != 0 && cfg.w_layout != 1) return fail(QL_E_INVALID, "w_layout must be 0 or 1");
   if (cfg.w_layout == 1 && cfg.w_lds) return fail(QL_E_INVALID, "w_lds applies to row-major weights only");
@@ -259,20 +266,20 @@ ql_status build_plan(int32_t fmt, int64_t M, int64_t N, int64_t K, const ql_conf
   const int rg = cfg.rows_per_wave / 16;
   p->bn = cfg.waves_n * rg * 16;
   p->n_tiles = (int)((N + p->bn - 1) / p->bn);
-  const int64_t lds_a = cfg.a_lds ? (int64_t)p->chunk_kb * p->mt * 2048 : 0;
+  const int64_t lds_a = cfg.a_mode == 1 ? (int64_t)p->chunk_kb * p->mt * 2048 : 0;
   const int64_t lds_w = (cfg.w_lds && !cfg.w_layout) ? (int64_t)nw * 2 * rg * 2048 : 0;
   const int64_t lds_red = cfg.waves_k > 1 ? (int64_t)nw * rg * p->mt * 1024 : 0;
   p->lds = std::max(lds_a + lds_w, lds_red);
   if (p->lds > kLdsLimit) {
     const long long need = (long long)p->lds;
     delete p;
-    return fail(QL_E_UNSUPPORTED, "config needs %lld bytes of LDS (limit %lld); use a_lds=0 or a larger split_k",
+    return fail(QL_E_UNSUPPORTED, "config needs %lld bytes of LDS (limit %lld); use a_mode 0 or 2, or a larger split_k",
                 need, (long long)kLdsLimit);
   }
   p->ws_acc_bytes = p->chunks > 1 ? ((M * N * 4 + 255) / 256) * 256 : 0;
   p->ws_bytes = p->chunks > 1 ? p->ws_acc_bytes + (int64_t)p->n_tiles * 4 : 0;
   const int wm = cfg.w_layout ? qlk::W_PACKED : (cfg.w_lds ? qlk::W_LDS_TRANSPOSE : qlk::W_DIRECT);
-  p->key = qlk::DecodeKey{kernel_fmt(fmt), cfg.swap_ab, p->mt, rg, nw, cfg.prefetch, cfg.a_lds, wm};
+  p->key = qlk::DecodeKey{kernel_fmt(fmt), cfg.swap_ab, p->mt, rg, nw, cfg.prefetch, cfg.a_mode, wm};
   qlk::DecodeArgs dummy{};
   hipError_t pe;
   switch (p->key.fmt) {
@@ -375,17 +382,34 @@ const char* qlinear_status_string(int32_t s) {
 
 const char* qlinear_last_error(void) { return g_err.c_str(); }
 
-ql_status qlinear_quantize_act(int32_t fmt, const void* x_bf16, int64_t M, int64_t K, void* a_q,
-                               float* a_scale, void* stream) {
+static ql_status quantize_act(int32_t fmt, const void* x_bf16, int64_t M, int64_t K, void* a_q, float* a_scale,
+                              bool packed, void* stream) {
   ql_status st = check_sizes(fmt, M, K, "M");
   if (st != QL_OK) return st;
+  if (packed && qlinear_packed_act_bytes(M, K) > (int64_t(1) << 30))
+    return fail(QL_E_UNSUPPORTED, "packed activations exceed 2^30 bytes");
   if (M == 0 || K == 0) return QL_OK;
   if (!x_bf16 || !a_q || !a_scale) return fail(QL_E_INVALID, "NULL pointer");
   if (!aligned16(x_bf16) || !aligned16(a_q) || !aligned16(a_scale)) return fail(QL_E_ALIGN, "pointers must be 16-byte aligned");
   hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e = fmt == QL_BLOCK_FP8 ? qlk::launch_quant_groups(x_bf16, M, K, a_q, a_scale, s)
-                                     : qlk::launch_quant_rows(kernel_fmt(fmt), x_bf16, M, K, a_q, a_scale, s);
+  hipError_t e = fmt == QL_BLOCK_FP8 ? qlk::launch_quant_groups(x_bf16, M, K, a_q, a_scale, packed, s)
+                                     : qlk::launch_quant_rows(kernel_fmt(fmt), x_bf16, M, K, a_q, a_scale, packed, s);
   return e == hipSuccess ? QL_OK : hip_fail(e, "activation quantizer launch");
+}
+
+ql_status qlinear_quantize_act(int32_t fmt, const void* x_bf16, int64_t M, int64_t K, void* a_q,
+                               float* a_scale, void* stream) {
+  return quantize_act(fmt, x_bf16, M, K, a_q, a_scale, false, stream);
+}
+
+int64_t qlinear_packed_act_bytes(int64_t M, int64_t K) {
+  if (M < 0 || K < 0) return 0;
+  return ((M + 15) / 16) * ((K + 127) / 128) * 2048;
+}
+
+ql_status qlinear_quantize_act_packed(int32_t fmt, const void* x_bf16, int64_t M, int64_t K, void* a_packed,
+                                      float* a_scale, void* stream) {
+  return quantize_act(fmt, x_bf16, M, K, a_packed, a_scale, true, stream);
 }
 
 ql_status qlinear_quantize_weight(int32_t fmt, const void* w_bf16, int64_t N, int64_t K, void* w_q,
@@ -397,7 +421,7 @@ ql_status qlinear_quantize_weight(int32_t fmt, const void* w_bf16, int64_t N, in
   if (!aligned16(w_bf16) || !aligned16(w_q) || !aligned16(w_scale)) return fail(QL_E_ALIGN, "pointers must be 16-byte aligned");
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = fmt == QL_BLOCK_FP8 ? qlk::launch_quant_wblocks(w_bf16, N, K, w_q, w_scale, s)
-                                     : qlk::launch_quant_rows(kernel_fmt(fmt), w_bf16, N, K, w_q, w_scale, s);
+                                     : qlk::launch_quant_rows(kernel_fmt(fmt), w_bf16, N, K, w_q, w_scale, false, s);
   return e == hipSuccess ? QL_OK : hip_fail(e, "weight quantizer launch");
 }
 
@@ -417,7 +441,7 @@ ql_status qlinear_table_load(const char* path, int64_t* n_entries) {
     long long M, N, K;
     if (!(is >> e.fmt)) continue;  // blank or comment line
     if (!(is >> M >> N >> K >> e.cfg.algo >> e.cfg.swap_ab >> e.cfg.split_k >> e.cfg.waves_n >> e.cfg.waves_k >>
-          e.cfg.rows_per_wave >> e.cfg.prefetch >> e.cfg.a_lds >> e.cfg.w_lds >> e.cfg.w_layout >> e.cfg.tile_m >>
+          e.cfg.rows_per_wave >> e.cfg.prefetch >> e.cfg.a_mode >> e.cfg.w_lds >> e.cfg.w_layout >> e.cfg.tile_m >>
           e.cfg.tile_n))
       return fail(QL_E_TABLE, "%s:%d: malformed entry", path, lineno);
     if (!(is >> e.us)) e.us = 0;
@@ -440,22 +464,32 @@ void qlinear_table_clear(void) {
   g_table.clear();
 }
 
-static ql_status plan_for_layout(int32_t fmt, int32_t layout, int64_t M, int64_t N, int64_t K, ql_plan* out_plan) {
+static ql_status plan_for_layout(int32_t fmt, int32_t layout, bool a_packed, int64_t M, int64_t N, int64_t K,
+                                 ql_plan* out_plan) {
+  if (layout != 0 && layout != 1) return fail(QL_E_INVALID, "w_layout must be 0 or 1");
   ql_config c;
   if (parse_force(&c)) {
-    if (c.w_layout != layout) return fail(QL_E_INVALID, "QLINEAR_FORCE names another weight layout");
+    if (c.w_layout != layout || (c.a_mode == 2) != a_packed)
+      return fail(QL_E_INVALID, "QLINEAR_FORCE names other operand layouts");
     return build_plan(fmt, M, N, K, c, QL_SRC_CUSTOM, out_plan);
   }
-  if (table_lookup(fmt, layout, M, N, K, &c)) return build_plan(fmt, M, N, K, c, QL_SRC_TABLE, out_plan);
-  return build_plan(fmt, M, N, K, heuristic_config(fmt, layout, M, N, K), QL_SRC_HEURISTIC, out_plan);
+  if (table_lookup(fmt, layout, a_packed, M, N, K, &c)) return build_plan(fmt, M, N, K, c, QL_SRC_TABLE, out_plan);
+  return build_plan(fmt, M, N, K, heuristic_config(fmt, layout, a_packed, M, N, K), QL_SRC_HEURISTIC, out_plan);
 }
 
 ql_status qlinear_plan(int32_t fmt, int64_t M, int64_t N, int64_t K, ql_plan* out_plan) {
-  return plan_for_layout(fmt, 0, M, N, K, out_plan);
+  return plan_for_layout(fmt, 0, false, M, N, K, out_plan);
 }
 
 ql_status qlinear_plan_packed(int32_t fmt, int64_t M, int64_t N, int64_t K, ql_plan* out_plan) {
-  return plan_for_layout(fmt, 1, M, N, K, out_plan);
+  return plan_for_layout(fmt, 1, false, M, N, K, out_plan);
+}
+
+ql_status qlinear_plan_layouts(int32_t fmt, int64_t M, int64_t N, int64_t K, int32_t w_layout, int32_t a_packed,
+                               ql_plan* out_plan) {
+  if (a_packed != 0 && a_packed != 1) return fail(QL_E_INVALID, "a_packed must be 0 or 1");
+  if (a_packed && !w_layout) return fail(QL_E_UNSUPPORTED, "packed activations need packed weights");
+  return plan_for_layout(fmt, w_layout, a_packed != 0, M, N, K, out_plan);
 }
 
 int64_t qlinear_packed_weight_bytes(int64_t N, int64_t K) {
@@ -476,7 +510,7 @@ ql_status qlinear_pack_weight(const void* w_q, int64_t N, int64_t K, void* w_pac
 ql_status qlinear_plan_from_table(int32_t fmt, int64_t M, int64_t N, int64_t K, ql_plan* out_plan) {
   if (out_plan) *out_plan = nullptr;
   ql_config c;
-  if (!table_lookup(fmt, 0, M, N, K, &c))
+  if (!table_lookup(fmt, 0, false, M, N, K, &c))
     return fail(QL_E_NO_TABLE_ENTRY, "no table entry for fmt=%d M=%lld N=%lld K=%lld", fmt, (long long)M,
                 (long long)N, (long long)K);
   return build_plan(fmt, M, N, K, c, QL_SRC_TABLE, out_plan);
@@ -526,7 +560,7 @@ ql_status qlinear_run_debug_acc(ql_plan p, const void* a_q, const float* a_scale
 ql_status qlinear_forward(ql_plan p, const void* x_bf16, void* a_q, float* a_scale, const void* w_q,
                           const float* w_scale, void* y, void* workspace, void* stream) {
   if (!p) return fail(QL_E_INVALID, "plan is NULL");
-  ql_status st = qlinear_quantize_act(p->fmt, x_bf16, p->M, p->K, a_q, a_scale, stream);
+  ql_status st = quantize_act(p->fmt, x_bf16, p->M, p->K, a_q, a_scale, p->cfg.a_mode == 2, stream);
   if (st != QL_OK) return st;
   return launch_gemm(p, a_q, a_scale, w_q, w_scale, y, workspace, nullptr, static_cast<hipStream_t>(stream));
 }

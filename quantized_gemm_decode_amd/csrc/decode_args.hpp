@@ -43,7 +43,7 @@ struct DecodeKey {
   int rg;    // 16-row groups per wave (1, 2 or 4)
   int nw;    // waves per workgroup (4, 8 or 16)
   int pf;    // K blocks per prefetch batch
-  int alds;  // activations staged in LDS
+  int alds;  // activations: 0 row-major from L2, 1 row-major staged in LDS, 2 packed from L2
   int wm;    // weight mode: W_DIRECT / W_LDS_TRANSPOSE / W_PACKED
 };
 
@@ -55,6 +55,7 @@ struct TiledKey {
   int bn;    // output tile columns (weight rows): 128 or 256
   int wm;    // weight layout: W_DIRECT (row-major) or W_PACKED
   int pf;    // K blocks in flight in the register ring: 1, 2 or 4
+  int ap;    // activations packed (1) or row-major (0)
 };
 
 // Launch an instantiated kernel; returns hipErrorInvalidDeviceFunction when
@@ -76,9 +77,11 @@ hipError_t tiled_dispatch_block(const TiledKey& k, dim3 grid, size_t lds, hipStr
                                 bool probe_only);
 
 // Quantizer launchers (quant.hip).
-hipError_t launch_quant_rows(int fmt, const void* x, int64_t R, int64_t C, void* q, float* s,
+// `packed`: codes in the packed activation layout (2 KB tiles of 16 rows x
+// 128 K in matrix-core operand order, zero padding), else row-major [R, C].
+hipError_t launch_quant_rows(int fmt, const void* x, int64_t R, int64_t C, void* q, float* s, bool packed,
                              hipStream_t st);
-hipError_t launch_quant_groups(const void* x, int64_t M, int64_t K, void* q, float* s,
+hipError_t launch_quant_groups(const void* x, int64_t M, int64_t K, void* q, float* s, bool packed,
                                hipStream_t st);
 hipError_t launch_quant_wblocks(const void* w, int64_t N, int64_t K, void* q, float* s,
                                 hipStream_t st);

@@ -56,8 +56,10 @@ __device__ __forceinline__ uint32_t epilogue_scaled(float accf, float sa, float 
   return bf16_rne(t);
 }
 
-template <int FMT, bool SWAP, int MT, int RG, int NW, int PF, bool ALDS, int WM>
+template <int FMT, bool SWAP, int MT, int RG, int NW, int PF, int AL, int WM>
 __global__ void __launch_bounds__(NW * 64) qgemm_decode_kernel(DecodeArgs p) {
+  constexpr bool ALDS = AL == 1;  // row-major activations staged in LDS
+  constexpr bool AP = AL == 2;    // packed activations, read per K block like packed weights
   constexpr bool WL = WM == W_LDS_TRANSPOSE;
   constexpr bool WP = WM == W_PACKED;
   using Acc = typename AccOf<FMT>::T;
@@ -83,7 +85,8 @@ __global__ void __launch_bounds__(NW * 64) qgemm_decode_kernel(DecodeArgs p) {
   const uint32_t M = (uint32_t)p.M, N = (uint32_t)p.N, K = (uint32_t)p.K;
   const uint32_t NT16 = (N + 15u) / 16u;  // 16-row groups (tiles along N of the packed layout)
   const __amdgpu_buffer_rsrc_t rw = make_rsrc(p.w, WP ? NT16 * (uint32_t)p.G * 2048u : N * K);
-  const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.a, M * K);
+  const uint32_t MT16 = (M + 15u) / 16u;
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.a, AP ? MT16 * (uint32_t)p.G * 2048u : M * K);
 
   // Loop-invariant lane offsets.  A row past the end gets a base of 2^31:
   // adding any in-range K offset (< 2^30) keeps it beyond num_records
@@ -121,11 +124,18 @@ __global__ void __launch_bounds__(NW * 64) qgemm_decode_kernel(DecodeArgs p) {
   // staged activations.
   const int wl_base = (ALDS ? p.chunk_kb * MT * 2048 : 0) + wave * (2 * RG * 2048);
 
+  // Activation lane bases.  Row-major: row m, K offset 16g of each block.
+  // Packed: lane l's two pieces of tile (mt, kb) at (mt*G + kb)*2048 + l*16
+  // (+1024).  Lanes of tokens >= M get OOB in both, so at small M a load
+  // instruction moves only the valid rows.
   uint32_t abase[MT];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
     const uint32_t m = (uint32_t)(mt * 16 + r16);
-    abase[mt] = m < M ? m * K + glo : OOB;
+    if constexpr (AP)
+      abase[mt] = m < M ? (uint32_t)mt * (uint32_t)p.G * 2048u + (uint32_t)lane * 16u : OOB;
+    else
+      abase[mt] = m < M ? m * K + glo : OOB;
   }
 
   // ---- this wave's K blocks: kb0 + wk + j*WK, j < nkw
@@ -183,7 +193,14 @@ __global__ void __launch_bounds__(NW * 64) qgemm_decode_kernel(DecodeArgs p) {
           wb[q][rg].hi = bload16(rw, hi_ok ? wbase[rg] + kofs + 64u : OOB);
         }
       }
-      if constexpr (!ALDS) {
+      if constexpr (AP) {
+        const uint32_t tofs = (uint32_t)kb * 2048u;
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+          ab[q][mt].lo = bload16(ra, ok ? abase[mt] + tofs : OOB);
+          ab[q][mt].hi = bload16(ra, ok ? abase[mt] + tofs + 1024u : OOB);
+        }
+      } else if constexpr (!ALDS) {
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
           ab[q][mt].lo = bload16(ra, lo_ok ? abase[mt] + kofs : OOB);
@@ -507,7 +524,7 @@ hipError_t decode_try(const DecodeKey& k, dim3 grid, dim3 block, size_t lds, hip
     if (k.swap == SW && k.mt == MT_ && k.rg == RG_ && k.nw == NW_ && k.pf == PF_ && k.alds == AL && k.wm == WM_) {
       *hit = true;
       if (probe_only) return hipSuccess;
-      qgemm_decode_kernel<FMT, SW != 0, MT_, RG_, NW_, PF_, AL != 0, WM_><<<grid, block, lds, s>>>(a);
+      qgemm_decode_kernel<FMT, SW != 0, MT_, RG_, NW_, PF_, AL, WM_><<<grid, block, lds, s>>>(a);
       return hipGetLastError();
     }
   }
@@ -525,13 +542,16 @@ hipError_t decode_dispatch(const DecodeKey& k, dim3 grid, dim3 block, size_t lds
   // 4 waves, every weight mode and activation staging
 #define QL_TRY_WL(SW, MT_, RG_, PF_, AL) \
   QL_TRY(4, SW, MT_, RG_, PF_, AL, 0) QL_TRY(4, SW, MT_, RG_, PF_, AL, 1) QL_TRY(4, SW, MT_, RG_, PF_, AL, 2)
-#define QL_TRY_AL(SW, MT_, RG_, PF_) QL_TRY_WL(SW, MT_, RG_, PF_, 0) QL_TRY_WL(SW, MT_, RG_, PF_, 1)
+#define QL_TRY_AL(SW, MT_, RG_, PF_) \
+  QL_TRY_WL(SW, MT_, RG_, PF_, 0) QL_TRY_WL(SW, MT_, RG_, PF_, 1) QL_TRY(4, SW, MT_, RG_, PF_, 2, 2)
 #define QL_TRY_PF(SW, MT_, RG_) QL_TRY_AL(SW, MT_, RG_, 2) QL_TRY_AL(SW, MT_, RG_, 4)
 #define QL_TRY_RG(SW, MT_) QL_TRY_PF(SW, MT_, 1) QL_TRY_PF(SW, MT_, 2)
-  // packed weights, activations from L2: wider workgroups, longer rows, 1-block batches
-#define QL_TRY_P(NW_, SW, MT_, RG_) QL_TRY(NW_, SW, MT_, RG_, 1, 0, 2) QL_TRY(NW_, SW, MT_, RG_, 2, 0, 2)
-#define QL_TRY_PN(SW, MT_)                                                                \
-  QL_TRY(4, SW, MT_, 1, 1, 0, 2) QL_TRY(4, SW, MT_, 2, 1, 0, 2) QL_TRY_P(4, SW, MT_, 4)   \
+  // packed weights, activations (row-major or packed) from L2: wider workgroups,
+  // longer rows, 1-block batches
+#define QL_TRY_PA(NW_, SW, MT_, RG_, PF_) QL_TRY(NW_, SW, MT_, RG_, PF_, 0, 2) QL_TRY(NW_, SW, MT_, RG_, PF_, 2, 2)
+#define QL_TRY_P(NW_, SW, MT_, RG_) QL_TRY_PA(NW_, SW, MT_, RG_, 1) QL_TRY_PA(NW_, SW, MT_, RG_, 2)
+#define QL_TRY_PN(SW, MT_)                                                                    \
+  QL_TRY_PA(4, SW, MT_, 1, 1) QL_TRY_PA(4, SW, MT_, 2, 1) QL_TRY_P(4, SW, MT_, 4)             \
   QL_TRY_P(8, SW, MT_, 1) QL_TRY_P(8, SW, MT_, 2) QL_TRY_P(8, SW, MT_, 4)                 \
   QL_TRY_P(16, SW, MT_, 1) QL_TRY_P(16, SW, MT_, 2) QL_TRY_P(16, SW, MT_, 4)
 #define QL_TRY_MT(SW) QL_TRY_RG(SW, 1) QL_TRY_RG(SW, 2) QL_TRY_PN(SW, 1) QL_TRY_PN(SW, 2)
@@ -540,6 +560,7 @@ hipError_t decode_dispatch(const DecodeKey& k, dim3 grid, dim3 block, size_t lds
 #undef QL_TRY_MT
 #undef QL_TRY_PN
 #undef QL_TRY_P
+#undef QL_TRY_PA
 #undef QL_TRY_RG
 #undef QL_TRY_PF
 #undef QL_TRY_AL

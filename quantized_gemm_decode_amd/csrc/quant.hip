@@ -58,6 +58,16 @@ __device__ __forceinline__ float block_max(float m, float* red) {
   return r;
 }
 
+// Byte offset of codes (row, k .. k+7) in the packed activation layout: the
+// 2 KB tile (row / 16, k / 128) at (row/16 * G + k/128) * 2048, inside it byte
+// h*1024 + l*16 + j holds row 16t + l%16, K offset 128kb + 64h + 16(l/16) + j
+// (the layout of packed weights; 8 consecutive codes stay in one 16-byte piece).
+__device__ __forceinline__ size_t packed_offset(uint32_t row, uint32_t k, uint32_t G) {
+  const uint32_t kk = k & 127u;
+  return ((size_t)(row >> 4) * G + (k >> 7)) * 2048u + (kk >> 6) * 1024u +
+         ((row & 15u) + 16u * ((kk >> 4) & 3u)) * 16u + (kk & 15u);
+}
+
 template <int FMT>
 __device__ __forceinline__ float scale_of(float amax) {
   const float Q = FMT == FMT_INT8 ? 127.0f : 448.0f;
@@ -65,20 +75,25 @@ __device__ __forceinline__ float scale_of(float amax) {
 }
 
 // One row per workgroup; the row stays in registers (VPT 16-byte vectors per
-// thread) between the amax pass and the quantize pass.
-template <int FMT, int VPT>
-__global__ void __launch_bounds__(QT) quant_rows_reg_kernel(const uint16_t* __restrict__ x, uint32_t C,
+// thread) between the amax pass and the quantize pass.  PACKED writes the
+// packed activation layout instead of row-major codes: the grid then also
+// covers the padding rows up to a multiple of 16 and the padding K up to a
+// multiple of 128, which get zero codes (and no scale).
+template <int FMT, int VPT, bool PACKED>
+__global__ void __launch_bounds__(QT) quant_rows_reg_kernel(const uint16_t* __restrict__ x, uint32_t R, uint32_t C,
                                                             uint8_t* __restrict__ q, float* __restrict__ s) {
   __shared__ float red[QT / 64];
-  const size_t row = blockIdx.x;
-  const uint16_t* xr = x + row * C;
-  uint8_t* qr = q + row * C;
+  const uint32_t row = blockIdx.x;
+  const bool real = row < R;
+  const uint16_t* xr = x + (size_t)row * C;
+  const uint32_t G = (C + 127u) / 128u;
+  const uint32_t CW = PACKED ? G * 128u : C;  // code columns written
   u32x4 v[VPT];
   float amax = 0.0f;
 #pragma unroll
   for (int i = 0; i < VPT; ++i) {
     const uint32_t e = (uint32_t)(i * QT + threadIdx.x) * 8u;
-    v[i] = e < C ? *reinterpret_cast<const u32x4*>(xr + e) : u32x4{0, 0, 0, 0};
+    v[i] = (real && e < C) ? *reinterpret_cast<const u32x4*>(xr + e) : u32x4{0, 0, 0, 0};
     amax = abs_bf16_max8(v[i], amax);
   }
   amax = block_max(amax, red);
@@ -86,33 +101,46 @@ __global__ void __launch_bounds__(QT) quant_rows_reg_kernel(const uint16_t* __re
 #pragma unroll
   for (int i = 0; i < VPT; ++i) {
     const uint32_t e = (uint32_t)(i * QT + threadIdx.x) * 8u;
-    if (e < C) *reinterpret_cast<u32x2*>(qr + e) = quant8<FMT>(v[i], sc);
+    if (e < CW) {
+      const size_t off = PACKED ? packed_offset(row, e, G) : (size_t)row * C + e;
+      *reinterpret_cast<u32x2*>(q + off) = quant8<FMT>(v[i], sc);
+    }
   }
-  if (threadIdx.x == 0) s[row] = sc;
+  if (threadIdx.x == 0 && real) s[row] = sc;
 }
 
 // Rows too long for registers: two streaming passes (the second re-reads from cache).
-template <int FMT>
-__global__ void __launch_bounds__(QT) quant_rows_stream_kernel(const uint16_t* __restrict__ x, uint32_t C,
+template <int FMT, bool PACKED>
+__global__ void __launch_bounds__(QT) quant_rows_stream_kernel(const uint16_t* __restrict__ x, uint32_t R, uint32_t C,
                                                                uint8_t* __restrict__ q, float* __restrict__ s) {
   __shared__ float red[QT / 64];
-  const size_t row = blockIdx.x;
-  const uint16_t* xr = x + row * C;
-  uint8_t* qr = q + row * C;
+  const uint32_t row = blockIdx.x;
+  const bool real = row < R;
+  const uint16_t* xr = x + (size_t)row * C;
+  const uint32_t G = (C + 127u) / 128u;
+  const uint32_t CW = PACKED ? G * 128u : C;
   float amax = 0.0f;
-  for (uint32_t e = threadIdx.x * 8u; e < C; e += QT * 8u)
-    amax = abs_bf16_max8(*reinterpret_cast<const u32x4*>(xr + e), amax);
+  if (real)
+    for (uint32_t e = threadIdx.x * 8u; e < C; e += QT * 8u)
+      amax = abs_bf16_max8(*reinterpret_cast<const u32x4*>(xr + e), amax);
   amax = block_max(amax, red);
   const float sc = scale_of<FMT>(amax);
-  for (uint32_t e = threadIdx.x * 8u; e < C; e += QT * 8u)
-    *reinterpret_cast<u32x2*>(qr + e) = quant8<FMT>(*reinterpret_cast<const u32x4*>(xr + e), sc);
-  if (threadIdx.x == 0) s[row] = sc;
+  for (uint32_t e = threadIdx.x * 8u; e < CW; e += QT * 8u) {
+    const u32x4 v = (real && e < C) ? *reinterpret_cast<const u32x4*>(xr + e) : u32x4{0, 0, 0, 0};
+    const size_t off = PACKED ? packed_offset(row, e, G) : (size_t)row * C + e;
+    *reinterpret_cast<u32x2*>(q + off) = quant8<FMT>(v, sc);
+  }
+  if (threadIdx.x == 0 && real) s[row] = sc;
 }
 
 // Block_FP8 activations: groups of 128 contiguous elements along K (K % 128
 // == 0, so group id = m * K/128 + g is also the s_a index); 16 lanes per
 // group, 8 elements per lane; the group amax reduces over the 16 lanes.
+// PACKED: codes in the packed activation layout; groups of the padding rows
+// (up to a multiple of 16 rows, `ngroups_out` in all) get zero codes.
+template <bool PACKED>
 __global__ void __launch_bounds__(QT) quant_groups_kernel(const uint16_t* __restrict__ x, uint32_t ngroups,
+                                                          uint32_t ngroups_out, uint32_t G,
                                                           uint8_t* __restrict__ q, float* __restrict__ s) {
   const uint32_t gid = blockIdx.x * (QT / 16) + (threadIdx.x >> 4);
   const uint32_t li = threadIdx.x & 15u;
@@ -123,10 +151,11 @@ __global__ void __launch_bounds__(QT) quant_groups_kernel(const uint16_t* __rest
 #pragma unroll
   for (int o = 8; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));
   const float sc = scale_of<FMT_FP8>(amax);
-  if (ok) {
-    *reinterpret_cast<u32x2*>(q + e) = quant8<FMT_FP8>(v, sc);
-    if (li == 0) s[gid] = sc;
+  if (gid < (PACKED ? ngroups_out : ngroups)) {
+    const size_t off = PACKED ? packed_offset(gid / G, (gid % G) * 128u + li * 8u, G) : e;
+    *reinterpret_cast<u32x2*>(q + off) = quant8<FMT_FP8>(v, sc);
   }
+  if (ok && li == 0) s[gid] = sc;
 }
 
 // Block_FP8 weights: one workgroup per 128x128 block (nb, g); thread t covers
@@ -187,39 +216,51 @@ hipError_t launch_pack_weight(const void* w_q, int64_t N, int64_t K, void* w_pac
   return hipGetLastError();
 }
 
-template <int FMT>
+template <int FMT, bool PACKED>
 static hipError_t rows_dispatch(const void* x, int64_t R, int64_t C, void* q, float* s, hipStream_t st) {
   const uint16_t* xp = static_cast<const uint16_t*>(x);
   uint8_t* qp = static_cast<uint8_t*>(q);
   const int64_t vecs = (C + 7) / 8;
   const int64_t vpt = (vecs + QT - 1) / QT;
-  const dim3 grid((unsigned)R), block(QT);
+  const dim3 grid((unsigned)(PACKED ? (R + 15) / 16 * 16 : R)), block(QT);
+  const uint32_t r = (uint32_t)R, c = (uint32_t)C;
   if (vpt <= 1)
-    quant_rows_reg_kernel<FMT, 1><<<grid, block, 0, st>>>(xp, (uint32_t)C, qp, s);
+    quant_rows_reg_kernel<FMT, 1, PACKED><<<grid, block, 0, st>>>(xp, r, c, qp, s);
   else if (vpt <= 2)
-    quant_rows_reg_kernel<FMT, 2><<<grid, block, 0, st>>>(xp, (uint32_t)C, qp, s);
+    quant_rows_reg_kernel<FMT, 2, PACKED><<<grid, block, 0, st>>>(xp, r, c, qp, s);
   else if (vpt <= 4)
-    quant_rows_reg_kernel<FMT, 4><<<grid, block, 0, st>>>(xp, (uint32_t)C, qp, s);
+    quant_rows_reg_kernel<FMT, 4, PACKED><<<grid, block, 0, st>>>(xp, r, c, qp, s);
   else if (vpt <= 8)
-    quant_rows_reg_kernel<FMT, 8><<<grid, block, 0, st>>>(xp, (uint32_t)C, qp, s);
+    quant_rows_reg_kernel<FMT, 8, PACKED><<<grid, block, 0, st>>>(xp, r, c, qp, s);
   else if (vpt <= 16)
-    quant_rows_reg_kernel<FMT, 16><<<grid, block, 0, st>>>(xp, (uint32_t)C, qp, s);
+    quant_rows_reg_kernel<FMT, 16, PACKED><<<grid, block, 0, st>>>(xp, r, c, qp, s);
   else
-    quant_rows_stream_kernel<FMT><<<grid, block, 0, st>>>(xp, (uint32_t)C, qp, s);
+    quant_rows_stream_kernel<FMT, PACKED><<<grid, block, 0, st>>>(xp, r, c, qp, s);
   return hipGetLastError();
 }
 
-hipError_t launch_quant_rows(int fmt, const void* x, int64_t R, int64_t C, void* q, float* s,
+hipError_t launch_quant_rows(int fmt, const void* x, int64_t R, int64_t C, void* q, float* s, bool packed,
                              hipStream_t st) {
-  if (fmt == FMT_INT8) return rows_dispatch<FMT_INT8>(x, R, C, q, s, st);
-  return rows_dispatch<FMT_FP8>(x, R, C, q, s, st);
+  if (packed) {
+    if (fmt == FMT_INT8) return rows_dispatch<FMT_INT8, true>(x, R, C, q, s, st);
+    return rows_dispatch<FMT_FP8, true>(x, R, C, q, s, st);
+  }
+  if (fmt == FMT_INT8) return rows_dispatch<FMT_INT8, false>(x, R, C, q, s, st);
+  return rows_dispatch<FMT_FP8, false>(x, R, C, q, s, st);
 }
 
-hipError_t launch_quant_groups(const void* x, int64_t M, int64_t K, void* q, float* s, hipStream_t st) {
-  const int64_t ng = M * (K / 128);
-  const dim3 grid((unsigned)((ng + QT / 16 - 1) / (QT / 16))), block(QT);
-  quant_groups_kernel<<<grid, block, 0, st>>>(static_cast<const uint16_t*>(x), (uint32_t)ng,
-                                              static_cast<uint8_t*>(q), s);
+hipError_t launch_quant_groups(const void* x, int64_t M, int64_t K, void* q, float* s, bool packed,
+                               hipStream_t st) {
+  const int64_t G = K / 128;
+  const int64_t ng = M * G;
+  const int64_t ng_out = packed ? (M + 15) / 16 * 16 * G : ng;
+  const dim3 grid((unsigned)((ng_out + QT / 16 - 1) / (QT / 16))), block(QT);
+  if (packed)
+    quant_groups_kernel<true><<<grid, block, 0, st>>>(static_cast<const uint16_t*>(x), (uint32_t)ng, (uint32_t)ng_out,
+                                                      (uint32_t)G, static_cast<uint8_t*>(q), s);
+  else
+    quant_groups_kernel<false><<<grid, block, 0, st>>>(static_cast<const uint16_t*>(x), (uint32_t)ng,
+                                                       (uint32_t)ng_out, (uint32_t)G, static_cast<uint8_t*>(q), s);
   return hipGetLastError();
 }
 

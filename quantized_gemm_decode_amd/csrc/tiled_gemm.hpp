@@ -18,8 +18,8 @@
 //     global memory into registers, and writes them into one of two LDS
 //     stages in matrix-core operand order: a 16-row x 128 group becomes a
 //     2 KB tile whose lane-l reads at l*16 and 1024 + l*16 give the lane its
-//     two 16-byte pieces (the packed weight layout is exactly this order, so
-//     packed weights copy through verbatim).  The loads for block k+1 are in
+//     two 16-byte pieces (the packed weight and activation layouts are
+//     exactly this order, so packed operands copy through verbatim).  The loads for block k+1 are in
 //     flight while the matrix cores work on block k: the workgroup barriers
 //     order LDS only, so they do not wait for outstanding global loads.
 //   * Each wave reads its TM/16 A fragments and, one at a time, its TN/16 B
@@ -50,7 +50,7 @@ struct TiledAcc<FMT_INT8> {
   typedef i32x4 T;
 };
 
-template <int FMT, bool SWAP, int BM, int BN, int WM, int PF>
+template <int FMT, bool SWAP, int BM, int BN, int WM, int PF, bool AP>
 __global__ void __launch_bounds__(256) qgemm_tiled_kernel(DecodeArgs p) {
   constexpr int TM = BM / 2, TN = BN / 2;  // wave tile
   constexpr int IM = TM / 16, IN = TN / 16;
@@ -95,7 +95,8 @@ __global__ void __launch_bounds__(256) qgemm_tiled_kernel(DecodeArgs p) {
   const int kb1 = min(p.G, kb0 + p.chunk_kb);
   const int nk = kb1 - kb0;
 
-  const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.a, M * K);
+  const uint32_t MT16 = (M + 15u) / 16u;
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.a, AP ? MT16 * G * 2048u : M * K);
   const __amdgpu_buffer_rsrc_t rw = make_rsrc(p.w, WP ? NT16 * G * 2048u : N * K);
   const __amdgpu_buffer_rsrc_t rsa = make_rsrc(p.sa, (FMT == FMT_BLOCK ? M * G : M) * 4u);
   const __amdgpu_buffer_rsrc_t rsw = make_rsrc(p.sw, (FMT == FMT_BLOCK ? ((N + 127u) / 128u) * G : N) * 4u);
@@ -109,8 +110,13 @@ __global__ void __launch_bounds__(256) qgemm_tiled_kernel(DecodeArgs p) {
 #pragma unroll
     for (int i = 0; i < PA; ++i) {
       const uint32_t q = (uint32_t)(i * 256 + tid);
-      const uint32_t m = m0 + (q >> 3), k = kofs + (q & 7u) * 16u;
-      pa[sl][i] = bload16(ra, (in && m < M && k < K) ? m * K + k : OOB);
+      if constexpr (AP) {
+        const uint32_t t = m0 / 16u + (q >> 7);
+        pa[sl][i] = bload16(ra, (in && t < MT16) ? (t * G + (uint32_t)kb) * 2048u + (q & 127u) * 16u : OOB);
+      } else {
+        const uint32_t m = m0 + (q >> 3), k = kofs + (q & 7u) * 16u;
+        pa[sl][i] = bload16(ra, (in && m < M && k < K) ? m * K + k : OOB);
+      }
     }
 #pragma unroll
     for (int i = 0; i < PB; ++i) {
@@ -131,9 +137,13 @@ __global__ void __launch_bounds__(256) qgemm_tiled_kernel(DecodeArgs p) {
 #pragma unroll
     for (int i = 0; i < PA; ++i) {
       const int q = i * 256 + tid;
-      const int row = q >> 3, c = q & 7;
-      *reinterpret_cast<u32x4*>(base + (row >> 4) * 2048 + (c >> 2) * 1024 + ((row & 15) + 16 * (c & 3)) * 16) =
-          pa[sl][i];
+      if constexpr (AP) {
+        *reinterpret_cast<u32x4*>(base + q * 16) = pa[sl][i];
+      } else {
+        const int row = q >> 3, c = q & 7;
+        *reinterpret_cast<u32x4*>(base + (row >> 4) * 2048 + (c >> 2) * 1024 + ((row & 15) + 16 * (c & 3)) * 16) =
+            pa[sl][i];
+      }
     }
     uint8_t* bbase = base + BM * 128;
 #pragma unroll
@@ -374,13 +384,13 @@ constexpr bool tiled_config_fits() {
   return BM * BN <= 128 * 256;
 }
 
-template <int FMT, int SW, int BM, int BN, int WM_, int PF>
+template <int FMT, int SW, int BM, int BN, int WM_, int PF, int AP>
 hipError_t tiled_try(const TiledKey& k, dim3 grid, size_t lds, hipStream_t s, const DecodeArgs& a, bool probe_only,
                      bool* hit) {
   if constexpr (tiled_config_fits<FMT, SW, BM, BN, PF>()) {
-    if (k.swap == SW && k.bm == BM && k.bn == BN && k.wm == WM_ && k.pf == PF) {
+    if (k.swap == SW && k.bm == BM && k.bn == BN && k.wm == WM_ && k.pf == PF && k.ap == AP) {
       *hit = true;
-      auto fn = qgemm_tiled_kernel<FMT, SW != 0, BM, BN, WM_, PF>;
+      auto fn = qgemm_tiled_kernel<FMT, SW != 0, BM, BN, WM_, PF, AP != 0>;
       if (probe_only) {
         // stages above the default 64 KB need the per-kernel opt-in (gfx950: 160 KB per workgroup)
         return hipFuncSetAttribute(reinterpret_cast<const void*>(fn), hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -398,11 +408,13 @@ hipError_t tiled_dispatch(const TiledKey& k, dim3 grid, size_t lds, hipStream_t 
                           bool probe_only) {
   bool hit = false;
   hipError_t e = hipSuccess;
-#define QL_TT(SW, BM, BN, WM_, PF)                                                  \
-  e = tiled_try<FMT, SW, BM, BN, WM_, PF>(k, grid, lds, s, a, probe_only, &hit);    \
+#define QL_TT(SW, BM, BN, WM_, PF, AP)                                                  \
+  e = tiled_try<FMT, SW, BM, BN, WM_, PF, AP>(k, grid, lds, s, a, probe_only, &hit);    \
   if (hit) return e;
-#define QL_TT_P(SW, BM, BN, WM_) QL_TT(SW, BM, BN, WM_, 1) QL_TT(SW, BM, BN, WM_, 2) QL_TT(SW, BM, BN, WM_, 4)
-#define QL_TT_W(SW, BM, BN) QL_TT_P(SW, BM, BN, 0) QL_TT_P(SW, BM, BN, 2)
+#define QL_TT_P(SW, BM, BN, WM_, AP) \
+  QL_TT(SW, BM, BN, WM_, 1, AP) QL_TT(SW, BM, BN, WM_, 2, AP) QL_TT(SW, BM, BN, WM_, 4, AP)
+  // (row-major W, row-major A), (packed W, row-major A), (packed W, packed A)
+#define QL_TT_W(SW, BM, BN) QL_TT_P(SW, BM, BN, 0, 0) QL_TT_P(SW, BM, BN, 2, 0) QL_TT_P(SW, BM, BN, 2, 1)
 #define QL_TT_S(BM, BN) QL_TT_W(0, BM, BN) QL_TT_W(1, BM, BN)
   QL_TT_S(64, 128)
   QL_TT_S(64, 256)

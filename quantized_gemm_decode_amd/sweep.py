@@ -10,9 +10,12 @@ phases:
 
   1. swap_ab=1, prefetch=2 (1 where 2 is not instantiated); every
      (waves_n, waves_k), rows_per_wave, split_k (distinct effective chunk
-     counts only), a_lds and w_lds -- for packed weights also 8- and 16-wave
+     counts only), a_mode and w_lds -- for packed weights also 8- and 16-wave
      workgroups and 64 rows per wave;
   2. the best few of phase 1 again with swap_ab in {0, 1} x prefetch {1, 2, 4}.
+For M > 32 (the tiled algorithm) the whole space -- tile, swap_ab, split_k,
+ring depth -- is timed in one phase.  Operand layouts: row-major W and A,
+packed W, packed W and A; each gets its own entries.
 
 Every candidate is timed as a hipGraph of back-to-back launches, each on its
 own copy of the weights (>= 1 GiB of copies, so the Infinity Cache cannot
@@ -57,27 +60,45 @@ def _effective_chunks(K, split):
     return -(-G // ck)
 
 
+TILES = ((64, 128), (64, 256), (128, 128), (128, 256), (256, 128))
+
+
+def tiled_candidates(M, N, K, layout):
+    """Every tiled configuration for M > 32 (tile, orientation, split, ring depth)."""
+    for (bm, bn), swap, split, pf in itertools.product(TILES, (0, 1), (1, 2, 4, 8), (1, 2, 4)):
+        if bm > 64 and bm > 2 * M:
+            continue
+        yield dict(algo=ql.ALGO_TILED, swap_ab=swap, split_k=split, tile_m=bm, tile_n=bn, prefetch=pf,
+                   a_mode=2 if layout == 2 else 0, w_layout=1 if layout >= 1 else 0)
+
+
 def phase1_candidates(fmt, M, N, K, layout=0):
+    if M > 32:
+        yield from tiled_candidates(M, N, K, layout)
+        return
     seen = set()
     waves, rows_set = (WAVES, (16, 32)) if layout == 0 else (WAVES_PACKED, (16, 32, 64))
-    for (wn, wk), rows, split, alds, wlds in itertools.product(waves, rows_set, SPLITS, (1, 0),
+    amodes = (2,) if layout == 2 else (1, 0)
+    for (wn, wk), rows, split, alds, wlds in itertools.product(waves, rows_set, SPLITS, amodes,
                                                               (1, 0) if layout == 0 else (0,)):
         ch = _effective_chunks(K, split)
         key = (wn, wk, rows, ch, alds, wlds)
         if key in seen:
             continue
         seen.add(key)
-        yield dict(swap_ab=1, split_k=split, waves_n=wn, waves_k=wk, rows_per_wave=rows, prefetch=2, a_lds=alds,
-                   w_lds=wlds, w_layout=layout)
+        yield dict(swap_ab=1, split_k=split, waves_n=wn, waves_k=wk, rows_per_wave=rows, prefetch=2, a_mode=alds,
+                   w_lds=wlds, w_layout=1 if layout >= 1 else 0)
 
 
 class Timer:
-    """Times plans for one (format, N, K, weight layout) on rotated weight copies."""
+    """Times plans for one (format, N, K, operand layouts) on rotated weight copies.
+
+    layout 0: row-major W_q and A_q; 1: packed W_q, row-major A_q; 2: packed W_q and A_q."""
 
     def __init__(self, fmt, N, K, x, w, stream, layout=0, max_copies=48):
         self.fmt, self.N, self.K, self.layout = fmt, N, K, layout
         w_q, w_s = ql.quantize_weight(fmt, w.cuda())
-        if layout == 1:
+        if layout >= 1:
             w_q = ql.pack_weight(w_q)
         self.copies = min(max_copies, max(2, -(-(1 << 30) // (N * K))))
         self.wq = torch.empty((self.copies,) + tuple(w_q.shape), dtype=w_q.dtype, device="cuda")
@@ -90,7 +111,10 @@ class Timer:
     def measure(self, plan, M, reps=5):
         """Median per-launch microseconds and the output of one launch."""
         fmt, s = self.fmt, self.stream
-        a_q, a_s = ql.quantize_act(fmt, self.x[:M].contiguous())
+        if self.layout == 2:
+            a_q, a_s = ql.quantize_act_packed(fmt, self.x[:M].contiguous())
+        else:
+            a_q, a_s = ql.quantize_act(fmt, self.x[:M].contiguous())
         y = torch.empty(M, self.N, dtype=torch.bfloat16, device="cuda")
         wsp = plan.new_workspace()
         torch.cuda.synchronize()
@@ -143,7 +167,8 @@ def sweep_point(timer, fmt, M, N, K, log=print, top=6):
     ref = None
     for cfg in phase1_candidates(fmt, M, N, K, timer.layout):
         plan = None
-        for pf in (2, 1):      # shapes too large for 2-block batches are instantiated with 1-block ones
+        # decode shapes too large for 2-block batches are instantiated with 1-block ones
+        for pf in ((cfg["prefetch"],) if cfg.get("algo") == ql.ALGO_TILED else (2, 1)):
             try:
                 cfg = dict(cfg, prefetch=pf)
                 plan = ql.qlinear_plan_with_config(fmt, M, N, K, cfg)
@@ -162,7 +187,7 @@ def sweep_point(timer, fmt, M, N, K, log=print, top=6):
         results.append((us, cfg))
     results.sort(key=lambda t: t[0])
     seen = {tuple(sorted(c.items())) for _, c in results}
-    for _, base in results[:top]:
+    for _, base in (results[:top] if M <= 32 else []):   # the tiled space is searched whole in phase 1
         for swap, pf in itertools.product((0, 1), (1, 2, 4)):
             cfg = dict(base, swap_ab=swap, prefetch=pf)
             k = tuple(sorted(cfg.items()))
@@ -184,9 +209,10 @@ def sweep_point(timer, fmt, M, N, K, log=print, top=6):
 
 
 def table_line(fmt, M, N, K, cfg, us):
+    c = ql.make_config(**cfg)
     return "%d %d %d %d %d %d %d %d %d %d %d %d %d %d %d %d %.3f" % (
-        fmt, M, N, K, ql.ALGO_DECODE, cfg["swap_ab"], cfg["split_k"], cfg["waves_n"], cfg["waves_k"],
-        cfg["rows_per_wave"], cfg["prefetch"], cfg["a_lds"], cfg["w_lds"], cfg.get("w_layout", 0), 0, 0, us)
+        fmt, M, N, K, c["algo"], c["swap_ab"], c["split_k"], c["waves_n"], c["waves_k"], c["rows_per_wave"],
+        c["prefetch"], c["a_mode"], c["w_lds"], c["w_layout"], c["tile_m"], c["tile_n"], us)
 
 
 def main(argv=None):
@@ -194,13 +220,14 @@ def main(argv=None):
     ap.add_argument("--workloads", default=",".join(c.name for c in CONFIGS[:4]))
     ap.add_argument("--out", default=ql.DEFAULT_TABLE)
     ap.add_argument("--ms", default=None, help="comma list overriding the token counts")
-    ap.add_argument("--layouts", default="0,1", help="weight layouts to tune: 0 row-major, 1 packed")
+    ap.add_argument("--layouts", default="0,1,2",
+                    help="operand layouts to tune: 0 row-major W and A, 1 packed W, 2 packed W and A")
     args = ap.parse_args(argv)
     torch.cuda.set_device(0)
     stream = torch.cuda.Stream()
     t_start = time.time()
     hdr = ["# qlinear sweep table: fmt M N K algo swap_ab split_k waves_n waves_k rows_per_wave prefetch "
-           "a_lds w_lds w_layout tile_m tile_n time_us",
+           "a_mode w_lds w_layout tile_m tile_n time_us",
            "# device: %s; hip %s; torch %s" % (torch.cuda.get_device_name(0), torch.version.hip, torch.__version__),
            "# written %s" % datetime.datetime.utcnow().strftime("%Y-%m-%d %H:%M UTC")]
     os.makedirs(os.path.dirname(os.path.abspath(args.out)), exist_ok=True)
@@ -215,8 +242,6 @@ def main(argv=None):
                 for layout in [int(v) for v in args.layouts.split(",")]:
                     timer = Timer(wl.fmt, N, K, x, w, stream, layout=layout)
                     for M in ms:
-                        if M > 32:
-                            continue
                         t0 = time.time()
                         res = sweep_point(timer, wl.fmt, M, N, K)
                         us, cfg = res[0]

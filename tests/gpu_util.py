@@ -60,3 +60,20 @@ def fp8_check(fmt, r, y_bits, split, waves_k=16):
     d = oracle.summation_depth(K, split=split, waves_k=waves_k)
     B = oracle.tolerance_bound(fmt, r["a_q"], r["w_q"], r["s_a"], r["s_w"], d)
     return oracle.check_fp8_parity(y_bits, r["y_ref"], r["y_true"], B)
+
+
+def pack_ref(q):
+    """The packed tile layout (weights and activations alike), restated from its definition:
+    tile (t, kb) holds rows 16t.., K bytes 128kb..; tile byte h*1024 + l*16 + j =
+    Q[16t + l%16][128kb + 64h + 16(l//16) + j], zero padded."""
+    q = np.ascontiguousarray(q).view(np.uint8)
+    N, K = q.shape
+    NT, G = -(-N // 16), -(-K // 128)
+    pad = np.zeros((NT * 16, G * 128), np.uint8)
+    pad[:N, :K] = q
+    arr = pad.reshape(NT, 16, G, 128)
+    out = np.zeros((NT, G, 2, 64, 16), np.uint8)
+    for h in range(2):
+        for g in range(4):
+            out[:, :, h, 16 * g:16 * g + 16, :] = arr[:, :, :, 64 * h + 16 * g:64 * h + 16 * g + 16].transpose(0, 2, 1, 3)
+    return out.reshape(-1)

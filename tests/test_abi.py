@@ -80,8 +80,8 @@ def test_host_validation_status_codes():
     # configurations that would spill registers are not instantiated
     assert _plan_status(ql.FP8_DYNAMIC, 32, 4096, 2048, rows_per_wave=32, prefetch=4) == QL_E_UNSUPPORTED
     # the LDS-staged activation chunk must fit the 64 KB budget
-    assert _plan_status(ql.FP8_DYNAMIC, 32, 4096, 25600, split_k=1, a_lds=1) == QL_E_UNSUPPORTED
-    assert _plan_status(ql.FP8_DYNAMIC, 32, 4096, 25600, split_k=1, a_lds=0) == QL_OK
+    assert _plan_status(ql.FP8_DYNAMIC, 32, 4096, 25600, split_k=1, a_mode=1) == QL_E_UNSUPPORTED
+    assert _plan_status(ql.FP8_DYNAMIC, 32, 4096, 25600, split_k=1, a_mode=0) == QL_OK
     assert "LDS" in ql.lib().qlinear_last_error().decode() or True
 
 
@@ -119,7 +119,7 @@ def test_plan_facts_and_workspace_sizes():
     assert p.workspace_bytes == 8 * 4096 * 4 + (4096 // 64) * 4
     assert ql.qlinear_plan_with_config(ql.W8A8_INT8, 8, 4096, 2048, dict(split_k=1)).workspace_bytes == 0
     # split clamps to the number of 128-wide K blocks and to balanced chunks
-    q = ql.qlinear_plan_with_config(ql.FP8_DYNAMIC, 4, 512, 640, dict(split_k=256, a_lds=0))
+    q = ql.qlinear_plan_with_config(ql.FP8_DYNAMIC, 4, 512, 640, dict(split_k=256, a_mode=0))
     assert q.config["split_k"] == 5 and q.facts["chunk_k"] == 128
     r = ql.qlinear_plan_with_config(ql.FP8_DYNAMIC, 4, 512, 5120, dict(split_k=16))
     assert r.facts["chunks"] == 14 and r.facts["chunk_k"] == 384        # ceil(40/16)=3 blocks per chunk
@@ -127,7 +127,7 @@ def test_plan_facts_and_workspace_sizes():
 
 def test_table_lookup_buckets_and_force(tmp_path):
     t = tmp_path / "t.txt"
-    t.write_text("# fmt M N K algo swap split wn wk rows pf alds wlds wlayout tm tn us\n"
+    t.write_text("# fmt M N K algo swap split wn wk rows pf amode wlds wlayout tm tn us\n"
                  "0 8 4096 4096 0 1 4 4 1 16 2 1 0 0 0 0 3.1\n"
                  "0 32 4096 4096 0 0 4 2 2 32 2 1 1 0 0 0 3.3\n"
                  "0 8 4096 4096 0 0 2 1 4 16 2 0 0 1 0 0 2.2\n"

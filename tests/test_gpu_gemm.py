@@ -16,7 +16,7 @@ import torch
 
 import oracle
 import quantized_gemm_decode_amd as ql
-from tests.gpu_util import (dev_bf16, dev_codes, dev_f32, fp8_check, host_bf16_bits, host_codes,
+from tests.gpu_util import (dev_bf16, dev_codes, dev_f32, fp8_check, host_bf16_bits, host_codes, pack_ref,
                             requires_gpu, run_gemm)
 from workloads import CONFIGS, decode_points, make_inputs, bf16_bits
 
@@ -27,6 +27,13 @@ FMTS = [ql.FP8_DYNAMIC, ql.W8A8_INT8, ql.BLOCK_FP8]
 def _ref(fmt, M, N, K, seed, sigma=0.02):
     x, w = make_inputs(K, N, M, sigma, seed=seed)
     return oracle.reference(fmt, bf16_bits(x), bf16_bits(w))
+
+
+def _dev_packed_act(fmt, r):
+    """Oracle activation codes in the packed layout (restated on the host, not by the GPU quantizer)."""
+    codes = np.asarray(r["a_q"]).view(np.uint8) if fmt != ql.W8A8_INT8 else np.asarray(r["a_q"]).astype(np.int8).view(np.uint8)
+    t = torch.from_numpy(pack_ref(codes)).cuda()
+    return t.view(torch.int8) if fmt == ql.W8A8_INT8 else t.view(torch.float8_e4m3fn)
 
 
 def _dev(fmt, r):
@@ -56,7 +63,8 @@ def _assert_parity(fmt, r, y, acc, split, label="", waves_k=16):
 # every kernel instantiation: swap x rows/wave x prefetch x activation LDS staging x weight mode
 # (0 row-major direct, 1 row-major through the LDS transpose, 2 packed tiles), both token tiles
 # (instantiations that would spill registers do not exist)
-VARIANTS = list(itertools.product([0, 1], [16, 32], [2, 4], [0, 1], [0, 1, 2]))
+VARIANTS = [v for v in itertools.product([0, 1], [16, 32], [2, 4], [0, 1, 2], [0, 1, 2])
+            if v[3] != 2 or v[4] == 2]        # packed activations (a_mode 2) go with packed weights
 SPLITS = [1, 2, 4, 8]
 WAVES_K = [1, 2, 4]
 
@@ -72,16 +80,19 @@ def test_every_instantiation_matches_oracle(fmt, M, vi):
     K = 1152 if fmt == ql.BLOCK_FP8 or vi % 3 else 1040  # 1040: ragged last K block
     r = _ref(fmt, M, N, K, seed=vi * 7 + M)
     cfg = dict(swap_ab=swap, split_k=split, waves_n=4 // wk, waves_k=wk, rows_per_wave=rows, prefetch=pf,
-               a_lds=alds, w_lds=int(wmode == 1), w_layout=int(wmode == 2))
+               a_mode=alds, w_lds=int(wmode == 1), w_layout=int(wmode == 2))
     try:
         plan = ql.qlinear_plan_with_config(fmt, M, N, K, cfg)
     except ql.QLinearError as e:
-        spill = M > 16 and rows == 32 and pf == 4 or (fmt == ql.BLOCK_FP8 and M > 16 and pf == 4 and not swap)
+        spill = (M > 16 and rows == 32 and pf == 4 or (fmt == ql.BLOCK_FP8 and M > 16 and pf == 4 and not swap)
+                 or alds == 2)   # 4-wave packed-activation shapes exist for the register-fitting ones only
         assert e.status == 2 and (spill or "LDS" in str(e)), e
         pytest.skip("configuration not available: %s" % e)
     a_q, s_a, w_q, s_w = _dev(fmt, r)
     if wmode == 2:
         w_q = ql.pack_weight(w_q)
+    if alds == 2:
+        a_q = _dev_packed_act(fmt, r)
     y, acc, ws = run_gemm(plan, a_q, s_a, w_q, s_w)
     _assert_parity(fmt, r, y, acc, plan.facts["chunks"], label=str(cfg))
     if ws is not None:
@@ -89,14 +100,14 @@ def test_every_instantiation_matches_oracle(fmt, M, vi):
 
 
 # packed-weight shapes with wider workgroups: waves per workgroup x rows per wave x batch size
-WIDE = list(itertools.product([4, 8, 16], [16, 32, 64], [1, 2], [0, 1]))
+WIDE = list(itertools.product([4, 8, 16], [16, 32, 64], [1, 2], [0, 1], [0, 2]))   # ... x activation mode
 
 
 @pytest.mark.parametrize("fmt", FMTS)
 @pytest.mark.parametrize("M", [5, 29])
 @pytest.mark.parametrize("wi", range(len(WIDE)))
 def test_wide_workgroup_instantiations_match_oracle(fmt, M, wi):
-    nw, rows, pf, swap = WIDE[wi]
+    nw, rows, pf, swap, amode = WIDE[wi]
     wks = [k for k in (1, 2, 4, 8, 16) if k <= nw]
     wk = wks[(wi + M) % len(wks)]
     split = SPLITS[(wi + 2 * M) % len(SPLITS)]
@@ -104,13 +115,15 @@ def test_wide_workgroup_instantiations_match_oracle(fmt, M, wi):
     K = 1152 if fmt == ql.BLOCK_FP8 or wi % 3 else 1040  # 1040: ragged last K block
     r = _ref(fmt, M, N, K, seed=1000 + wi * 7 + M)
     cfg = dict(swap_ab=swap, split_k=split, waves_n=nw // wk, waves_k=wk, rows_per_wave=rows, prefetch=pf,
-               a_lds=0, w_lds=0, w_layout=1)
+               a_mode=amode, w_lds=0, w_layout=1)
     try:
         plan = ql.qlinear_plan_with_config(fmt, M, N, K, cfg)
     except ql.QLinearError as e:
         assert e.status == 2, e
         pytest.skip("configuration not available: %s" % e)
     a_q, s_a, w_q, s_w = _dev(fmt, r)
+    if amode == 2:
+        a_q = _dev_packed_act(fmt, r)
     y, acc, ws = run_gemm(plan, a_q, s_a, ql.pack_weight(w_q), s_w)
     _assert_parity(fmt, r, y, acc, plan.facts["chunks"], label=str(cfg), waves_k=wk)
     if ws is not None:
@@ -122,29 +135,15 @@ def test_wide_workgroup_instantiations_match_oracle(fmt, M, wi):
 def test_token_counts_and_tiles(fmt, M):
     N, K = 1024, 2048
     r = _ref(fmt, M, N, K, seed=M)
-    for cfg in (dict(swap_ab=0, split_k=1, waves_n=1, waves_k=4, a_lds=0),
-                dict(swap_ab=1, split_k=4, waves_n=2, waves_k=2, rows_per_wave=32, a_lds=1),
-                dict(swap_ab=1, split_k=16, waves_n=4, waves_k=1, prefetch=4, a_lds=1, w_lds=1),
-                dict(swap_ab=0, split_k=1, waves_n=1, waves_k=4, rows_per_wave=32, a_lds=0, w_lds=1)):
+    for cfg in (dict(swap_ab=0, split_k=1, waves_n=1, waves_k=4, a_mode=0),
+                dict(swap_ab=1, split_k=4, waves_n=2, waves_k=2, rows_per_wave=32, a_mode=1),
+                dict(swap_ab=1, split_k=16, waves_n=4, waves_k=1, prefetch=4, a_mode=1, w_lds=1),
+                dict(swap_ab=0, split_k=1, waves_n=1, waves_k=4, rows_per_wave=32, a_mode=0, w_lds=1)):
         plan = ql.qlinear_plan_with_config(fmt, M, N, K, cfg)
         y, acc, _ = run_gemm(plan, *_dev(fmt, r))
         _assert_parity(fmt, r, y, acc, plan.facts["chunks"], label=str(cfg))
 
 
-def _pack_ref(q):
-    """The packed tile layout, restated from its definition: tile (t, kb) holds rows 16t.., K bytes
-    128kb..; tile byte h*1024 + l*16 + j = W[16t + l%16][128kb + 64h + 16(l//16) + j], zero padded."""
-    q = np.ascontiguousarray(q).view(np.uint8)
-    N, K = q.shape
-    NT, G = -(-N // 16), -(-K // 128)
-    pad = np.zeros((NT * 16, G * 128), np.uint8)
-    pad[:N, :K] = q
-    arr = pad.reshape(NT, 16, G, 128)
-    out = np.zeros((NT, G, 2, 64, 16), np.uint8)
-    for h in range(2):
-        for g in range(4):
-            out[:, :, h, 16 * g:16 * g + 16, :] = arr[:, :, :, 64 * h + 16 * g:64 * h + 16 * g + 16].transpose(0, 2, 1, 3)
-    return out.reshape(-1)
 
 
 @pytest.mark.parametrize("N,K", [(300, 1040), (16, 128), (4096, 4096), (33, 16), (1, 2064)])
@@ -154,7 +153,7 @@ def test_pack_weight_matches_layout_definition(N, K):
     packed = ql.pack_weight(torch.from_numpy(q).cuda())
     torch.cuda.synchronize()
     assert packed.numel() == ql.qlinear_packed_weight_bytes(N, K)
-    assert np.array_equal(packed.cpu().numpy().view(np.uint8), _pack_ref(q))
+    assert np.array_equal(packed.cpu().numpy().view(np.uint8), pack_ref(q))
 
 
 @pytest.mark.parametrize("fmt", FMTS)
@@ -178,7 +177,7 @@ def test_int8_all_variants_bitwise_identical_and_deterministic():
     packed = ql.pack_weight(d[2])
     for swap, split, wk, rows, alds, wmode in itertools.product([0, 1], [1, 8, 32], [1, 4], [16, 32], [0, 1],
                                                                 [0, 1, 2]):
-        cfg = dict(swap_ab=swap, split_k=split, waves_n=4 // wk, waves_k=wk, rows_per_wave=rows, a_lds=alds,
+        cfg = dict(swap_ab=swap, split_k=split, waves_n=4 // wk, waves_k=wk, rows_per_wave=rows, a_mode=alds,
                    w_lds=int(wmode == 1), w_layout=int(wmode == 2))
         try:
             plan = ql.qlinear_plan_with_config(ql.W8A8_INT8, M, N, K, cfg)
@@ -227,6 +226,31 @@ def test_forward_quantizes_and_runs(fmt):
     ql.qlinear_forward(plan, x.cuda(), a_q, a_s, w_q, w_s, y, plan.new_workspace())
     torch.cuda.synchronize()
     assert np.array_equal(host_codes(fmt, a_q), r["a_q"])
+    if fmt == ql.W8A8_INT8:
+        assert np.array_equal(host_bf16_bits(y), r["y_ref"])
+    else:
+        assert fp8_check(fmt, r, host_bf16_bits(y), plan.facts["chunks"])["ok"]
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("M", [3, 24, 40])
+def test_forward_with_packed_operands(fmt, M):
+    """qlinear_forward on a packed-weight, packed-activation plan quantizes into
+    the packed layout itself (decode and tiled algorithms)."""
+    N, K = 520, 2048
+    x, w = make_inputs(K, N, M, 0.02, seed=22 + M)
+    r = oracle.reference(fmt, bf16_bits(x), bf16_bits(w))
+    plan = ql.qlinear_plan_layouts(fmt, M, N, K, 1, 1)
+    assert plan.config["a_mode"] == 2
+    w_q, w_s = ql.quantize_weight(fmt, w.cuda())
+    a_p = ql.act_buffer(plan)
+    a_s = torch.empty(ql.act_scale_shape(fmt, M, K), dtype=torch.float32, device="cuda")
+    y = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
+    ql.qlinear_forward(plan, x.cuda(), a_p, a_s, ql.pack_weight(w_q), w_s, y, plan.new_workspace())
+    torch.cuda.synchronize()
+    n = ql.qlinear_packed_act_bytes(M, K)
+    codes = np.asarray(r["a_q"]).astype(np.int8).view(np.uint8) if fmt == ql.W8A8_INT8 else np.asarray(r["a_q"])
+    assert np.array_equal(a_p[:n].view(torch.uint8).cpu().numpy(), pack_ref(codes))
     if fmt == ql.W8A8_INT8:
         assert np.array_equal(host_bf16_bits(y), r["y_ref"])
     else:
@@ -299,7 +323,7 @@ def _weights(ci, lab, N, K):
     if key not in _W_CACHE:
         _W_CACHE.clear()
         cfg = CONFIGS[ci]
-        x, w = make_inputs(K, N, 32 if ci else 8, cfg.sigma_w, seed=cfg.seed)
+        x, w = make_inputs(K, N, max(cfg.ms), cfg.sigma_w, seed=cfg.seed)
         w_q, w_s = ql.quantize_weight(cfg.fmt, w.cuda())
         _W_CACHE[key] = (x, w, w_q, w_s)
     return _W_CACHE[key]
@@ -315,11 +339,13 @@ def test_full_size_workloads_sampled_columns(ci, lab, N, K, M):
     x, w, w_q, w_s = _weights(ci, lab, N, K)
     xm = x[:M]
     a_q, a_s = ql.quantize_act(fmt, xm.cuda())
+    a_p, _ = ql.quantize_act_packed(fmt, xm.cuda())
+    w_p = ql.pack_weight(w_q)
     ys = []
-    for packed in (False, True):
-        plan = ql.qlinear_plan_packed(fmt, M, N, K) if packed else ql.qlinear_plan(fmt, M, N, K)
+    for w_layout, a_packed in ((0, 0), (1, 0), (1, 1)):
+        plan = ql.qlinear_plan_layouts(fmt, M, N, K, w_layout, a_packed)
         y = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
-        ql.qlinear_run(plan, a_q, a_s, ql.pack_weight(w_q) if packed else w_q, w_s, y, plan.new_workspace())
+        ql.qlinear_run(plan, a_p if a_packed else a_q, a_s, w_p if w_layout else w_q, w_s, y, plan.new_workspace())
         torch.cuda.synchronize()
         ys.append((plan, host_bf16_bits(y)))
     rng = np.random.default_rng(ci * 1000 + M)
@@ -354,11 +380,11 @@ def _table_entries():
 
 
 _TABLE_FIELDS = ("algo", "swap_ab", "split_k", "waves_n", "waves_k", "rows_per_wave", "prefetch",
-                 "a_lds", "w_lds", "w_layout", "tile_m", "tile_n")
+                 "a_mode", "w_lds", "w_layout", "tile_m", "tile_n")
 
 
 def _shape_config(fmt, N, K):
-    for ci, cfg in enumerate(CONFIGS[:4]):
+    for ci, cfg in enumerate(CONFIGS):
         if cfg.fmt != fmt:
             continue
         for (lab, n, k) in cfg.shapes:
@@ -379,6 +405,8 @@ def test_every_table_entry_matches_oracle(entry):
     a_q, a_s = ql.quantize_act(fmt, xm.cuda())
     plan = ql.qlinear_plan_with_config(fmt, M, N, K, cfg)
     y = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
+    if cfg["a_mode"] == 2:
+        a_q, _ = ql.quantize_act_packed(fmt, xm.cuda())
     ql.qlinear_run(plan, a_q, a_s, ql.pack_weight(w_q) if cfg["w_layout"] else w_q, w_s, y, plan.new_workspace())
     torch.cuda.synchronize()
     yb = host_bf16_bits(y)
@@ -388,8 +416,9 @@ def test_every_table_entry_matches_oracle(entry):
         cols = np.arange(nb * 128, min(N, nb * 128 + 128))
     else:
         cols = np.sort(rng.choice(N, 64, replace=False))
-    r = oracle.reference(fmt, bf16_bits(xm), bf16_bits(w[torch.from_numpy(cols)]))
-    ysel = yb[:, cols]
+    rows = np.sort(rng.choice(M, 256, replace=False)) if M > 256 else np.arange(M)
+    r = oracle.reference(fmt, bf16_bits(xm[torch.from_numpy(rows)]), bf16_bits(w[torch.from_numpy(cols)]))
+    ysel = yb[np.ix_(rows, cols)]
     if fmt == ql.W8A8_INT8:
         assert np.array_equal(ysel, r["y_ref"]), cfg
     else:

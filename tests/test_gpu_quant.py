@@ -6,7 +6,7 @@ import torch
 
 import oracle
 import quantized_gemm_decode_amd as ql
-from tests.gpu_util import dev_bf16, host_codes, requires_gpu
+from tests.gpu_util import dev_bf16, host_codes, pack_ref, requires_gpu
 from workloads import make_inputs, bf16_bits
 
 pytestmark = [pytest.mark.gpu, requires_gpu]
@@ -18,11 +18,17 @@ def _bits(a):
 
 
 def _check_act(fmt, xb):
+    """Row-major and packed quantizer outputs against the oracle (the packed
+    layout restated independently from its definition)."""
     q_ref, s_ref = oracle.quantize_act(fmt, xb)
     a_q, a_s = ql.quantize_act(fmt, dev_bf16(xb))
+    a_p, a_ps = ql.quantize_act_packed(fmt, dev_bf16(xb))
     torch.cuda.synchronize()
     assert np.array_equal(host_codes(fmt, a_q), q_ref)
     assert np.array_equal(a_s.cpu().numpy().view(np.uint32), np.asarray(s_ref, np.float32).view(np.uint32))
+    n = ql.qlinear_packed_act_bytes(*xb.shape)
+    assert np.array_equal(a_p[:n].view(torch.uint8).cpu().numpy(), pack_ref(np.asarray(q_ref).view(np.uint8)))
+    assert np.array_equal(a_ps.cpu().numpy().view(np.uint32), np.asarray(s_ref, np.float32).view(np.uint32))
 
 
 @pytest.mark.parametrize("fmt", FMTS)

@@ -16,13 +16,14 @@ import torch
 import oracle
 import quantized_gemm_decode_amd as ql
 from tests.gpu_util import dev_codes, dev_f32, fp8_check, host_bf16_bits, host_codes, requires_gpu, run_gemm
-from tests.test_gpu_gemm import _assert_parity
+from tests.test_gpu_gemm import _assert_parity, _dev_packed_act
 from workloads import CONFIGS, bf16_bits, make_inputs
 
 pytestmark = [pytest.mark.gpu, requires_gpu]
 FMTS = [ql.FP8_DYNAMIC, ql.W8A8_INT8, ql.BLOCK_FP8]
 TILES = [(64, 128), (64, 256), (128, 128), (128, 256), (256, 128)]
-TVARIANTS = list(itertools.product([0, 1], TILES, [0, 1], [1, 2, 4]))   # swap x tile x packed weights x ring depth
+# swap x tile x (packed weights, packed activations) x ring depth
+TVARIANTS = list(itertools.product([0, 1], TILES, [(0, 0), (1, 0), (1, 1)], [1, 2, 4]))
 
 
 def _ref(fmt, M, N, K, seed):
@@ -34,12 +35,13 @@ def _ref(fmt, M, N, K, seed):
 @pytest.mark.parametrize("M", [40, 200])
 @pytest.mark.parametrize("vi", range(len(TVARIANTS)))
 def test_every_tiled_instantiation_matches_oracle(fmt, M, vi):
-    swap, (bm, bn), packed, pf = TVARIANTS[vi]
+    swap, (bm, bn), (packed, apacked), pf = TVARIANTS[vi]
     split = [1, 2, 4][(vi + M) % 3]
     N = 300 if bn == 128 else 520                         # several tiles + a ragged tail
     K = 1152 if fmt == ql.BLOCK_FP8 or vi % 2 else 1040   # 1040: ragged last K block (9 blocks: ring wraps)
     r = _ref(fmt, M, N, K, seed=3000 + vi * 5 + M)
-    cfg = dict(algo=ql.ALGO_TILED, swap_ab=swap, split_k=split, tile_m=bm, tile_n=bn, w_layout=packed, prefetch=pf)
+    cfg = dict(algo=ql.ALGO_TILED, swap_ab=swap, split_k=split, tile_m=bm, tile_n=bn, w_layout=packed, prefetch=pf,
+               a_mode=2 * apacked)
     try:
         plan = ql.qlinear_plan_with_config(fmt, M, N, K, cfg)
     except ql.QLinearError as e:
@@ -48,6 +50,8 @@ def test_every_tiled_instantiation_matches_oracle(fmt, M, vi):
     a_q, s_a, w_q, s_w = (dev_codes(fmt, r["a_q"]), dev_f32(r["s_a"]), dev_codes(fmt, r["w_q"]), dev_f32(r["s_w"]))
     if packed:
         w_q = ql.pack_weight(w_q)
+    if apacked:
+        a_q = _dev_packed_act(fmt, r)
     y, acc, ws = run_gemm(plan, a_q, s_a, w_q, s_w)
     _assert_parity(fmt, r, y, acc, plan.facts["chunks"], label=str(cfg))
     if ws is not None:
@@ -61,7 +65,7 @@ def test_tiled_matches_decode_bitwise_for_int8_and_closely_for_fp8(fmt):
     M, N, K = 32, 384, 1280
     r = _ref(fmt, M, N, K, seed=77)
     a_q, s_a, w_q, s_w = (dev_codes(fmt, r["a_q"]), dev_f32(r["s_a"]), dev_codes(fmt, r["w_q"]), dev_f32(r["s_w"]))
-    pd = ql.qlinear_plan_with_config(fmt, M, N, K, dict(swap_ab=1, split_k=2, a_lds=0))
+    pd = ql.qlinear_plan_with_config(fmt, M, N, K, dict(swap_ab=1, split_k=2, a_mode=0))
     pt = ql.qlinear_plan_with_config(fmt, M, N, K, dict(algo=ql.ALGO_TILED, swap_ab=0, split_k=1, tile_m=64,
                                                         tile_n=128, prefetch=4))
     yd, accd, _ = run_gemm(pd, a_q, s_a, w_q, s_w)
@@ -96,7 +100,8 @@ _LARGE = {}
 @pytest.mark.parametrize("lab,N,K,M", _large_points())
 def test_large_m_workloads_sampled_columns(lab, N, K, M):
     """14B-class FP8 shapes at full size with the planner's configuration
-    (packed weights); the oracle recomputes 64 sampled output columns."""
+    (packed weights and activations); the oracle recomputes 64 sampled output
+    columns."""
     cfg = CONFIGS[4]
     fmt = cfg.fmt
     key = (lab, N, K)
@@ -108,10 +113,11 @@ def test_large_m_workloads_sampled_columns(lab, N, K, M):
     x, w, w_p, w_s = _LARGE[key]
     xm = x[:M]
     a_q, a_s = ql.quantize_act(fmt, xm.cuda())
-    plan = ql.qlinear_plan_packed(fmt, M, N, K)
-    assert plan.config["algo"] == ql.ALGO_TILED
+    a_p, _ = ql.quantize_act_packed(fmt, xm.cuda())
+    plan = ql.qlinear_plan_layouts(fmt, M, N, K, 1, 1)
+    assert plan.config["algo"] == ql.ALGO_TILED and plan.config["a_mode"] == 2
     y = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
-    ql.qlinear_run(plan, a_q, a_s, w_p, w_s, y, plan.new_workspace())
+    ql.qlinear_run(plan, a_p, a_s, w_p, w_s, y, plan.new_workspace())
     torch.cuda.synchronize()
     yb = host_bf16_bits(y)
     rng = np.random.default_rng(M + N)
