@@ -92,10 +92,9 @@ __device__ __forceinline__ uint32_t e4m3_rne(float v) {
   return code | sign;
 }
 
-// One quantized code of x with scale s (IEEE division, then round + clamp).
+// Round-to-code of an already divided value t (round + clamp).
 template <int FMT>
-__device__ __forceinline__ uint32_t quant_code(float x, float s) {
-  float t = __fdiv_rn(x, s);
+__device__ __forceinline__ uint32_t code_of(float t) {
   if (FMT == FMT_INT8) {
     float q = __builtin_rintf(t);
     q = fminf(fmaxf(q, -127.0f), 127.0f);
@@ -104,6 +103,28 @@ __device__ __forceinline__ uint32_t quant_code(float x, float s) {
     t = fminf(fmaxf(t, -448.0f), 448.0f);
     return e4m3_rne(t);
   }
+}
+
+// One quantized code of x with scale s: IEEE division, then round + clamp.
+template <int FMT>
+__device__ __forceinline__ uint32_t quant_code(float x, float s) {
+  return code_of<FMT>(__fdiv_rn(x, s));
+}
+
+// The same code from r = fl(1/s) with one multiply and two fused corrections
+// on |x|: q0 = fl(|x|*r), e = fma(-q0, s, |x|) (the remainder, exact),
+// q = fma(e, r, q0), then x's sign (so -0 keeps its sign, as in -0/s).  q
+// can still differ from fl(|x|/s) by one ulp, but for every bf16 x with
+// |x| <= amax, s = fl(amax/Q) >= 2^-96, the rounded code is the same --
+// checked exhaustively over all such (|x|, amax) pairs for Q = 127 and 448.
+// Rows with a smaller scale take the division.
+constexpr float FAST_DIV_MIN_SCALE = 1.2621774483536189e-29f;  // 2^-96
+template <int FMT>
+__device__ __forceinline__ uint32_t quant_code_fast(float x, float s, float r) {
+  const float ax = __builtin_fabsf(x);
+  const float q0 = __fmul_rn(ax, r);
+  const float e = __fmaf_rn(-q0, s, ax);
+  return code_of<FMT>(__builtin_copysignf(__fmaf_rn(e, r, q0), x));
 }
 
 // Workgroup barrier that orders LDS accesses only.  __syncthreads() also

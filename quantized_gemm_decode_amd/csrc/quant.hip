@@ -34,19 +34,31 @@ __device__ __forceinline__ float abs_bf16_max8(const u32x4& v, float m) {
   return m;
 }
 
+// Eight codes of one 16-byte bf16 vector.  r = fl(1/s) selects the
+// reciprocal path (exact at the code level for s >= 2^-96, see
+// quant_code_fast); r = 0 selects the division.
 template <int FMT>
-__device__ __forceinline__ u32x2 quant8(const u32x4& v, float s) {
+__device__ __forceinline__ u32x2 quant8(const u32x4& v, float s, float r) {
   uint32_t c[8];
+  if (r != 0.0f) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    c[2 * i] = quant_code<FMT>(bf16_to_f32(v[i] & 0xffffu), s);
-    c[2 * i + 1] = quant_code<FMT>(bf16_to_f32(v[i] >> 16), s);
+    for (int i = 0; i < 4; ++i) {
+      c[2 * i] = quant_code_fast<FMT>(bf16_to_f32(v[i] & 0xffffu), s, r);
+      c[2 * i + 1] = quant_code_fast<FMT>(bf16_to_f32(v[i] >> 16), s, r);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      c[2 * i] = quant_code<FMT>(bf16_to_f32(v[i] & 0xffffu), s);
+      c[2 * i + 1] = quant_code<FMT>(bf16_to_f32(v[i] >> 16), s);
+    }
   }
   u32x2 out = {c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24),
                c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24)};
   return out;
 }
 
+template <int NT>
 __device__ __forceinline__ float block_max(float m, float* red) {
   m = wave_max(m);
   const int wave = threadIdx.x >> 6;
@@ -54,7 +66,7 @@ __device__ __forceinline__ float block_max(float m, float* red) {
   __syncthreads();
   float r = red[0];
 #pragma unroll
-  for (int i = 1; i < QT / 64; ++i) r = fmaxf(r, red[i]);
+  for (int i = 1; i < NT / 64; ++i) r = fmaxf(r, red[i]);
   return r;
 }
 
@@ -74,15 +86,20 @@ __device__ __forceinline__ float scale_of(float amax) {
   return amax > 0.0f ? __fdiv_rn(amax, Q) : 1.0f;
 }
 
+// Reciprocal for quant8: fl(1/s), or 0 (take the division) below 2^-96.
+__device__ __forceinline__ float recip_of(float s) {
+  return s >= FAST_DIV_MIN_SCALE ? __fdiv_rn(1.0f, s) : 0.0f;
+}
+
 // One row per workgroup; the row stays in registers (VPT 16-byte vectors per
 // thread) between the amax pass and the quantize pass.  PACKED writes the
 // packed activation layout instead of row-major codes: the grid then also
 // covers the padding rows up to a multiple of 16 and the padding K up to a
 // multiple of 128, which get zero codes (and no scale).
-template <int FMT, int VPT, bool PACKED>
-__global__ void __launch_bounds__(QT) quant_rows_reg_kernel(const uint16_t* __restrict__ x, uint32_t R, uint32_t C,
+template <int FMT, int VPT, bool PACKED, int NT>
+__global__ void __launch_bounds__(NT) quant_rows_reg_kernel(const uint16_t* __restrict__ x, uint32_t R, uint32_t C,
                                                             uint8_t* __restrict__ q, float* __restrict__ s) {
-  __shared__ float red[QT / 64];
+  __shared__ float red[NT / 64];
   const uint32_t row = blockIdx.x;
   const bool real = row < R;
   const uint16_t* xr = x + (size_t)row * C;
@@ -92,18 +109,19 @@ __global__ void __launch_bounds__(QT) quant_rows_reg_kernel(const uint16_t* __re
   float amax = 0.0f;
 #pragma unroll
   for (int i = 0; i < VPT; ++i) {
-    const uint32_t e = (uint32_t)(i * QT + threadIdx.x) * 8u;
+    const uint32_t e = (uint32_t)(i * NT + threadIdx.x) * 8u;
     v[i] = (real && e < C) ? *reinterpret_cast<const u32x4*>(xr + e) : u32x4{0, 0, 0, 0};
     amax = abs_bf16_max8(v[i], amax);
   }
-  amax = block_max(amax, red);
+  amax = block_max<NT>(amax, red);
   const float sc = scale_of<FMT>(amax);
+  const float rc = recip_of(sc);
 #pragma unroll
   for (int i = 0; i < VPT; ++i) {
-    const uint32_t e = (uint32_t)(i * QT + threadIdx.x) * 8u;
+    const uint32_t e = (uint32_t)(i * NT + threadIdx.x) * 8u;
     if (e < CW) {
       const size_t off = PACKED ? packed_offset(row, e, G) : (size_t)row * C + e;
-      *reinterpret_cast<u32x2*>(q + off) = quant8<FMT>(v[i], sc);
+      *reinterpret_cast<u32x2*>(q + off) = quant8<FMT>(v[i], sc, rc);
     }
   }
   if (threadIdx.x == 0 && real) s[row] = sc;
@@ -123,12 +141,13 @@ __global__ void __launch_bounds__(QT) quant_rows_stream_kernel(const uint16_t* _
   if (real)
     for (uint32_t e = threadIdx.x * 8u; e < C; e += QT * 8u)
       amax = abs_bf16_max8(*reinterpret_cast<const u32x4*>(xr + e), amax);
-  amax = block_max(amax, red);
+  amax = block_max<QT>(amax, red);
   const float sc = scale_of<FMT>(amax);
+  const float rc = recip_of(sc);
   for (uint32_t e = threadIdx.x * 8u; e < CW; e += QT * 8u) {
     const u32x4 v = (real && e < C) ? *reinterpret_cast<const u32x4*>(xr + e) : u32x4{0, 0, 0, 0};
     const size_t off = PACKED ? packed_offset(row, e, G) : (size_t)row * C + e;
-    *reinterpret_cast<u32x2*>(q + off) = quant8<FMT>(v, sc);
+    *reinterpret_cast<u32x2*>(q + off) = quant8<FMT>(v, sc, rc);
   }
   if (threadIdx.x == 0 && real) s[row] = sc;
 }
@@ -153,7 +172,7 @@ __global__ void __launch_bounds__(QT) quant_groups_kernel(const uint16_t* __rest
   const float sc = scale_of<FMT_FP8>(amax);
   if (gid < (PACKED ? ngroups_out : ngroups)) {
     const size_t off = PACKED ? packed_offset(gid / G, (gid % G) * 128u + li * 8u, G) : e;
-    *reinterpret_cast<u32x2*>(q + off) = quant8<FMT_FP8>(v, sc);
+    *reinterpret_cast<u32x2*>(q + off) = quant8<FMT_FP8>(v, sc, recip_of(sc));
   }
   if (ok && li == 0) s[gid] = sc;
 }
@@ -176,12 +195,13 @@ __global__ void __launch_bounds__(QT) quant_wblocks_kernel(const uint16_t* __res
     v[i] = n < N ? *reinterpret_cast<const u32x4*>(w + (size_t)n * K + g * 128u + c) : u32x4{0, 0, 0, 0};
     amax = abs_bf16_max8(v[i], amax);
   }
-  amax = block_max(amax, red);
+  amax = block_max<QT>(amax, red);
   const float sc = scale_of<FMT_FP8>(amax);
+  const float rc = recip_of(sc);
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const uint32_t n = nb * 128u + r0 + 16u * i;
-    if (n < N) *reinterpret_cast<u32x2*>(q + (size_t)n * K + g * 128u + c) = quant8<FMT_FP8>(v[i], sc);
+    if (n < N) *reinterpret_cast<u32x2*>(q + (size_t)n * K + g * 128u + c) = quant8<FMT_FP8>(v[i], sc, rc);
   }
   if (threadIdx.x == 0) s[nb * G + g] = sc;
 }
@@ -216,27 +236,37 @@ hipError_t launch_pack_weight(const void* w_q, int64_t N, int64_t K, void* w_pac
   return hipGetLastError();
 }
 
-template <int FMT, bool PACKED>
-static hipError_t rows_dispatch(const void* x, int64_t R, int64_t C, void* q, float* s, hipStream_t st) {
+template <int FMT, bool PACKED, int NT>
+static hipError_t rows_dispatch_nt(const void* x, int64_t R, int64_t C, void* q, float* s, hipStream_t st) {
   const uint16_t* xp = static_cast<const uint16_t*>(x);
   uint8_t* qp = static_cast<uint8_t*>(q);
   const int64_t vecs = (C + 7) / 8;
-  const int64_t vpt = (vecs + QT - 1) / QT;
-  const dim3 grid((unsigned)(PACKED ? (R + 15) / 16 * 16 : R)), block(QT);
+  const int64_t vpt = (vecs + NT - 1) / NT;
+  const dim3 grid((unsigned)(PACKED ? (R + 15) / 16 * 16 : R)), block(NT);
   const uint32_t r = (uint32_t)R, c = (uint32_t)C;
   if (vpt <= 1)
-    quant_rows_reg_kernel<FMT, 1, PACKED><<<grid, block, 0, st>>>(xp, r, c, qp, s);
+    quant_rows_reg_kernel<FMT, 1, PACKED, NT><<<grid, block, 0, st>>>(xp, r, c, qp, s);
   else if (vpt <= 2)
-    quant_rows_reg_kernel<FMT, 2, PACKED><<<grid, block, 0, st>>>(xp, r, c, qp, s);
+    quant_rows_reg_kernel<FMT, 2, PACKED, NT><<<grid, block, 0, st>>>(xp, r, c, qp, s);
   else if (vpt <= 4)
-    quant_rows_reg_kernel<FMT, 4, PACKED><<<grid, block, 0, st>>>(xp, r, c, qp, s);
+    quant_rows_reg_kernel<FMT, 4, PACKED, NT><<<grid, block, 0, st>>>(xp, r, c, qp, s);
   else if (vpt <= 8)
-    quant_rows_reg_kernel<FMT, 8, PACKED><<<grid, block, 0, st>>>(xp, r, c, qp, s);
-  else if (vpt <= 16)
-    quant_rows_reg_kernel<FMT, 16, PACKED><<<grid, block, 0, st>>>(xp, r, c, qp, s);
-  else
-    quant_rows_stream_kernel<FMT, PACKED><<<grid, block, 0, st>>>(xp, r, c, qp, s);
+    quant_rows_reg_kernel<FMT, 8, PACKED, NT><<<grid, block, 0, st>>>(xp, r, c, qp, s);
+  else if constexpr (NT == QT) {
+    if (vpt <= 16)
+      quant_rows_reg_kernel<FMT, 16, PACKED, NT><<<grid, block, 0, st>>>(xp, r, c, qp, s);
+    else
+      quant_rows_stream_kernel<FMT, PACKED><<<grid, block, 0, st>>>(xp, r, c, qp, s);
+  }
   return hipGetLastError();
+}
+
+// Few rows (activations at decode token counts): 1024 threads a row, so each
+// lane quantizes at most a few vectors; many rows (weights): 256.
+template <int FMT, bool PACKED>
+static hipError_t rows_dispatch(const void* x, int64_t R, int64_t C, void* q, float* s, hipStream_t st) {
+  if (R <= 256 && C <= 8 * 8 * 1024) return rows_dispatch_nt<FMT, PACKED, 1024>(x, R, C, q, s, st);
+  return rows_dispatch_nt<FMT, PACKED, QT>(x, R, C, q, s, st);
 }
 
 hipError_t launch_quant_rows(int fmt, const void* x, int64_t R, int64_t C, void* q, float* s, bool packed,

@@ -49,13 +49,15 @@ def test_act_quantizer_ragged_k(fmt, K):
 @pytest.mark.parametrize("fmt", FMTS)
 def test_act_quantizer_special_rows(fmt):
     K = 256
-    x = np.zeros((6, K))
+    x = np.zeros((8, K))
     x[1, :] = np.linspace(-3, 3, K)                  # ordinary
     x[2, 7] = -1e-38                                 # subnormal scale
     x[3, :] = 2.0 ** -130                            # bf16 subnormal inputs
     x[4, ::2] = -0.0                                 # negative zeros only -> zero row
     x[5, :] = 448.0 * np.sign(np.sin(np.arange(K))) # ties and max magnitudes
     x[5, 3] = 1e30
+    x[6, :] = np.linspace(-1, 1, K) * 2.0 ** -88     # smallest scales of the reciprocal path
+    x[7, :] = np.linspace(-1, 1, K) * 2.0 ** -92     # scales just below it: the division path
     _check_act(fmt, _bits(x))
 
 
