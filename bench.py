@@ -337,7 +337,7 @@ def main(argv=None):
                 ql.qlinear_run(p["plan"], p["a_q"], p["a_s"], sh["wq"][c], sh["ws"][c], p["y"], p["wsp"],
                                stream=stream)
             g = ql.qlinear_graph_end(stream)
-            if p["cfg"]["a_mode"] == 2:
+            if p["cfg"]["a_mode"] >= 2:
                 ql.qlinear_quantize_act_packed(fmt, p["x"], p["a_q"], p["a_s"], stream=stream)
             else:
                 ql.qlinear_quantize_act(fmt, p["x"], p["a_q"], p["a_s"], stream=stream)

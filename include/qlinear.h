@@ -112,10 +112,13 @@ typedef struct {
                             TILED: 128-wide K blocks in flight per workgroup (1, 2 or 4) */
   int32_t a_mode;        /* activations: 0 = row-major A_q read per K block; 1 (DECODE) = row-major
                             A_q chunk staged in LDS; 2 = packed A_q (qlinear_quantize_act_packed)
-                            read per K block */
+                            read per K block; 3 (DECODE) = packed A_q chunk staged in LDS and
+                            shared by the workgroup's waves.  2 and 3 need packed weights */
   int32_t w_lds;         /* DECODE, row-major weights: 1 = coalesced weight loads (8 rows x 128 B
                             per instruction) transposed to the matrix-core layout through LDS;
-                            0 = direct loads in operand order */
+                            0 = direct loads in operand order.  TILED, packed weights and
+                            activations: 1 = both operands go straight to an LDS ring of
+                            `prefetch` (2 or 3) stages by LDS-DMA loads; 0 = register ring */
   int32_t w_layout;      /* weight layout the plan reads: 0 = row-major W_q[N,K];
                             1 = packed tiles (qlinear_pack_weight) */
   int32_t tile_m;        /* TILED: workgroup tile rows (tokens): 64, 128 or 256 */
@@ -222,7 +225,7 @@ ql_status qlinear_plan_packed(int32_t fmt, int64_t M, int64_t N, int64_t K, ql_p
 /*
  * Like qlinear_plan for any operand layouts: w_layout 0 = row-major W_q,
  * 1 = packed weights; a_packed 0 = row-major A_q (qlinear_quantize_act),
- * 1 = packed A_q (qlinear_quantize_act_packed; the plan's a_mode is 2).
+ * 1 = packed A_q (qlinear_quantize_act_packed; the plan's a_mode is 2 or 3).
  */
 ql_status qlinear_plan_layouts(int32_t fmt, int64_t M, int64_t N, int64_t K, int32_t w_layout,
                                int32_t a_packed, ql_plan* out_plan);
@@ -252,7 +255,7 @@ void qlinear_plan_destroy(ql_plan plan);
  * accumulator; Block_FP8 applies s_a[m,g] * s_w[n/128,g] to every 128-wide K
  * group's partial inside the K loop and rounds the fp32 sum to bf16.
  * a_q is in the plan's activation layout: row-major [M, K], or packed when
- * the plan's a_mode is 2; w_q in the plan's weight layout (w_layout).
+ * the plan's a_mode is 2 or 3; w_q in the plan's weight layout (w_layout).
  * Enqueue-only; workspace may be NULL when qlinear_workspace_bytes is 0.
  */
 ql_status qlinear_run(ql_plan plan, const void* a_q, const float* a_scale,
@@ -272,7 +275,7 @@ ql_status qlinear_run_debug_acc(ql_plan plan, const void* a_q, const float* a_sc
  * Quantize the activations, then run the GEMM: the whole decode step of one
  * linear layer.  a_q / a_scale are caller-owned staging buffers; a_q is
  * written in the plan's activation layout (qlinear_packed_act_bytes(M, K)
- * bytes when a_mode is 2, else M*K).
+ * bytes when a_mode is 2 or 3, else M*K).
  */
 ql_status qlinear_forward(ql_plan plan, const void* x_bf16, void* a_q, float* a_scale,
                           const void* w_q, const float* w_scale, void* y_bf16,

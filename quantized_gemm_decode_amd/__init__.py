@@ -131,8 +131,8 @@ def quantize_act_packed(fmt, x, stream=None):
 
 
 def act_buffer(plan, device="cuda"):
-    """Activation code buffer in the plan's layout (packed when its a_mode is 2)."""
-    n = qlinear_packed_act_bytes(plan.M, plan.K) if plan.config["a_mode"] == 2 else plan.M * plan.K
+    """Activation code buffer in the plan's layout (packed when its a_mode is 2 or 3)."""
+    n = qlinear_packed_act_bytes(plan.M, plan.K) if plan.config["a_mode"] >= 2 else plan.M * plan.K
     return torch.empty(max(n, 16), dtype=code_dtype(plan.fmt), device=device)
 
 

@@ -44,7 +44,7 @@ ql_status hip_fail(hipError_t e, const char* what) {
   return fail(QL_E_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
-constexpr int64_t kLdsLimit = 64 * 1024;     // dynamic LDS budget per workgroup
+constexpr int64_t kLdsLimit = 160 * 1024;    // gfx950: LDS per workgroup (above 64 KB with the per-kernel opt-in)
 constexpr int kBuckets[] = {1, 2, 4, 8, 16, 24, 32};
 
 bool valid_fmt(int32_t f) { return f == QL_FP8_DYNAMIC || f == QL_W8A8_INT8 || f == QL_BLOCK_FP8; }
@@ -85,7 +85,7 @@ bool table_lookup(int32_t fmt, int32_t layout, bool a_packed, int64_t M, int64_t
   const TableEntry* best = nullptr;
   const TableEntry* largest = nullptr;
   for (const TableEntry& e : g_table) {
-    if (e.fmt != fmt || e.N != N || e.K != K || e.cfg.w_layout != layout || (e.cfg.a_mode == 2) != a_packed) continue;
+    if (e.fmt != fmt || e.N != N || e.K != K || e.cfg.w_layout != layout || (e.cfg.a_mode >= 2) != a_packed) continue;
     if (e.M >= want && (!best || e.M < best->M)) best = &e;
     if (!largest || e.M > largest->M) largest = &e;
   }
@@ -175,8 +175,12 @@ ql_status build_tiled_plan(int32_t fmt, int64_t M, int64_t N, int64_t K, const q
   if (!is_pow2(cfg.split_k) || cfg.split_k > 256) return fail(QL_E_INVALID, "split_k must be a power of two in [1, 256]");
   if (cfg.tile_m != 64 && cfg.tile_m != 128 && cfg.tile_m != 256) return fail(QL_E_INVALID, "tile_m must be 64, 128 or 256");
   if (cfg.tile_n != 128 && cfg.tile_n != 256) return fail(QL_E_INVALID, "tile_n must be 128 or 256");
+  if (cfg.w_lds != 0 && cfg.w_lds != 1) return fail(QL_E_INVALID, "w_lds must be 0 or 1");
+  if (cfg.w_lds && (cfg.a_mode != 2 || cfg.w_layout != 1 || (cfg.prefetch != 2 && cfg.prefetch != 3)))
+    return fail(QL_E_INVALID, "the LDS-DMA ring (w_lds=1) needs packed operands and prefetch = 2 or 3 stages");
   if (cfg.w_layout != 0 && cfg.w_layout != 1) return fail(QL_E_INVALID, "w_layout must be 0 or 1");
-  if (cfg.prefetch != 1 && cfg.prefetch != 2 && cfg.prefetch != 4) return fail(QL_E_INVALID, "prefetch must be 1, 2 or 4");
+  if (!cfg.w_lds && cfg.prefetch != 1 && cfg.prefetch != 2 && cfg.prefetch != 4)
+    return fail(QL_E_INVALID, "prefetch must be 1, 2 or 4");
   if (cfg.a_mode != 0 && cfg.a_mode != 2) return fail(QL_E_INVALID, "a_mode must be 0 or 2 for the tiled algorithm");
   if (cfg.a_mode == 2 && qlinear_packed_act_bytes(M, K) > (int64_t(1) << 30))
     return fail(QL_E_UNSUPPORTED, "packed activations exceed 2^30 bytes");
@@ -196,7 +200,7 @@ ql_status build_tiled_plan(int32_t fmt, int64_t M, int64_t N, int64_t K, const q
   p->bn = cfg.tile_n;
   p->tiles_n = (int)((N + cfg.tile_n - 1) / cfg.tile_n);
   p->n_tiles = (int)((M + cfg.tile_m - 1) / cfg.tile_m) * p->tiles_n;
-  p->lds = 2 * (int64_t)(cfg.tile_m + cfg.tile_n) * 128;
+  p->lds = (cfg.w_lds ? cfg.prefetch : 2) * (int64_t)(cfg.tile_m + cfg.tile_n) * 128;
   if (p->lds > kTiledLdsLimit) {
     delete p;
     return fail(QL_E_UNSUPPORTED, "tile needs more LDS than a workgroup has");
@@ -205,7 +209,8 @@ ql_status build_tiled_plan(int32_t fmt, int64_t M, int64_t N, int64_t K, const q
   p->ws_bytes = p->chunks > 1 ? p->ws_acc_bytes + (int64_t)p->n_tiles * 4 : 0;
   p->key = qlk::DecodeKey{kernel_fmt(fmt), cfg.swap_ab, 0, 0, 4, 0, 0, 0};
   p->tkey = qlk::TiledKey{kernel_fmt(fmt), cfg.swap_ab, cfg.tile_m, cfg.tile_n,
-                          cfg.w_layout ? qlk::W_PACKED : qlk::W_DIRECT, cfg.prefetch, cfg.a_mode == 2 ? 1 : 0};
+                          cfg.w_layout ? qlk::W_PACKED : qlk::W_DIRECT, cfg.w_lds ? 1 : cfg.prefetch,
+                          cfg.a_mode == 2 ? 1 : 0, cfg.w_lds ? cfg.prefetch : 0};
   qlk::DecodeArgs dummy{};
   hipError_t pe;
   switch (p->tkey.fmt) {
@@ -243,9 +248,9 @@ ql_status build_plan(int32_t fmt, int64_t M, int64_t N, int64_t K, const ql_conf
   if (cfg.rows_per_wave != 16 && cfg.rows_per_wave != 32 && cfg.rows_per_wave != 64)
     return fail(QL_E_INVALID, "rows_per_wave must be 16, 32 or 64");
   if (cfg.prefetch != 1 && cfg.prefetch != 2 && cfg.prefetch != 4) return fail(QL_E_INVALID, "prefetch must be 1, 2 or 4");
-  if (cfg.a_mode < 0 || cfg.a_mode > 2) return fail(QL_E_INVALID, "a_mode must be 0, 1 or 2");
-  if (cfg.a_mode == 2 && !cfg.w_layout) return fail(QL_E_UNSUPPORTED, "packed activations need packed weights");
-  if (cfg.a_mode == 2 && qlinear_packed_act_bytes(M, K) > (int64_t(1) << 30))
+  if (cfg.a_mode < 0 || cfg.a_mode > 3) return fail(QL_E_INVALID, "a_mode must be 0, 1, 2 or 3");
+  if (cfg.a_mode >= 2 && !cfg.w_layout) return fail(QL_E_UNSUPPORTED, "packed activations need packed weights");
+  if (cfg.a_mode >= 2 && qlinear_packed_act_bytes(M, K) > (int64_t(1) << 30))
     return fail(QL_E_UNSUPPORTED, "packed activations exceed 2^30 bytes");
   if (cfg.w_lds != 0 && cfg.w_lds != 1) return fail(QL_E_INVALID, "w_lds must be 0 or 1");
   if (cfg.w_layout != 0 && cfg.w_layout != 1) return fail(QL_E_INVALID, "w_layout must be 0 or 1");
@@ -266,7 +271,7 @@ ql_status build_plan(int32_t fmt, int64_t M, int64_t N, int64_t K, const ql_conf
   const int rg = cfg.rows_per_wave / 16;
   p->bn = cfg.waves_n * rg * 16;
   p->n_tiles = (int)((N + p->bn - 1) / p->bn);
-  const int64_t lds_a = cfg.a_mode == 1 ? (int64_t)p->chunk_kb * p->mt * 2048 : 0;
+  const int64_t lds_a = (cfg.a_mode == 1 || cfg.a_mode == 3) ? (int64_t)p->chunk_kb * p->mt * 2048 : 0;
   const int64_t lds_w = (cfg.w_lds && !cfg.w_layout) ? (int64_t)nw * 2 * rg * 2048 : 0;
   const int64_t lds_red = cfg.waves_k > 1 ? (int64_t)nw * rg * p->mt * 1024 : 0;
   p->lds = std::max(lds_a + lds_w, lds_red);
@@ -283,14 +288,15 @@ ql_status build_plan(int32_t fmt, int64_t M, int64_t N, int64_t K, const ql_conf
   qlk::DecodeArgs dummy{};
   hipError_t pe;
   switch (p->key.fmt) {
-    case qlk::FMT_INT8: pe = qlk::decode_dispatch_int8(p->key, dim3(1), dim3(1), 0, nullptr, dummy, true); break;
-    case qlk::FMT_BLOCK: pe = qlk::decode_dispatch_block(p->key, dim3(1), dim3(1), 0, nullptr, dummy, true); break;
-    default: pe = qlk::decode_dispatch_fp8(p->key, dim3(1), dim3(1), 0, nullptr, dummy, true); break;
+    case qlk::FMT_INT8: pe = qlk::decode_dispatch_int8(p->key, dim3(1), dim3(1), (size_t)p->lds, nullptr, dummy, true); break;
+    case qlk::FMT_BLOCK: pe = qlk::decode_dispatch_block(p->key, dim3(1), dim3(1), (size_t)p->lds, nullptr, dummy, true); break;
+    default: pe = qlk::decode_dispatch_fp8(p->key, dim3(1), dim3(1), (size_t)p->lds, nullptr, dummy, true); break;
   }
-  if (pe != hipSuccess) {
+  if (pe == hipErrorInvalidDeviceFunction) {
     delete p;
     return fail(QL_E_UNSUPPORTED, "no kernel instantiated for this configuration");
   }
+  // any other error: raising the LDS limit needs a GPU; the launch reports it if it matters
   *out = p;
   return QL_OK;
 }
@@ -469,7 +475,7 @@ static ql_status plan_for_layout(int32_t fmt, int32_t layout, bool a_packed, int
   if (layout != 0 && layout != 1) return fail(QL_E_INVALID, "w_layout must be 0 or 1");
   ql_config c;
   if (parse_force(&c)) {
-    if (c.w_layout != layout || (c.a_mode == 2) != a_packed)
+    if (c.w_layout != layout || (c.a_mode >= 2) != a_packed)
       return fail(QL_E_INVALID, "QLINEAR_FORCE names other operand layouts");
     return build_plan(fmt, M, N, K, c, QL_SRC_CUSTOM, out_plan);
   }
@@ -560,7 +566,7 @@ ql_status qlinear_run_debug_acc(ql_plan p, const void* a_q, const float* a_scale
 ql_status qlinear_forward(ql_plan p, const void* x_bf16, void* a_q, float* a_scale, const void* w_q,
                           const float* w_scale, void* y, void* workspace, void* stream) {
   if (!p) return fail(QL_E_INVALID, "plan is NULL");
-  ql_status st = quantize_act(p->fmt, x_bf16, p->M, p->K, a_q, a_scale, p->cfg.a_mode == 2, stream);
+  ql_status st = quantize_act(p->fmt, x_bf16, p->M, p->K, a_q, a_scale, p->cfg.a_mode >= 2, stream);
   if (st != QL_OK) return st;
   return launch_gemm(p, a_q, a_scale, w_q, w_scale, y, workspace, nullptr, static_cast<hipStream_t>(stream));
 }

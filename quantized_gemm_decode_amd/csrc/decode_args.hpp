@@ -56,6 +56,7 @@ struct TiledKey {
   int wm;    // weight layout: W_DIRECT (row-major) or W_PACKED
   int pf;    // K blocks in flight in the register ring: 1, 2 or 4
   int ap;    // activations packed (1) or row-major (0)
+  int ns;    // 0: register ring; 2 or 3: LDS-DMA ring of that many stages (packed operands)
 };
 
 // Launch an instantiated kernel; returns hipErrorInvalidDeviceFunction when

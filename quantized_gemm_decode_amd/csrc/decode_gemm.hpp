@@ -58,8 +58,8 @@ __device__ __forceinline__ uint32_t epilogue_scaled(float accf, float sa, float 
 
 template <int FMT, bool SWAP, int MT, int RG, int NW, int PF, int AL, int WM>
 __global__ void __launch_bounds__(NW * 64) qgemm_decode_kernel(DecodeArgs p) {
-  constexpr bool ALDS = AL == 1;  // row-major activations staged in LDS
-  constexpr bool AP = AL == 2;    // packed activations, read per K block like packed weights
+  constexpr bool ALDS = AL == 1 || AL == 3;  // activations staged in LDS (row-major 1, packed 3)
+  constexpr bool AP = AL == 2;               // packed activations, read per K block like packed weights
   constexpr bool WL = WM == W_LDS_TRANSPOSE;
   constexpr bool WP = WM == W_PACKED;
   using Acc = typename AccOf<FMT>::T;
@@ -86,7 +86,7 @@ __global__ void __launch_bounds__(NW * 64) qgemm_decode_kernel(DecodeArgs p) {
   const uint32_t NT16 = (N + 15u) / 16u;  // 16-row groups (tiles along N of the packed layout)
   const __amdgpu_buffer_rsrc_t rw = make_rsrc(p.w, WP ? NT16 * (uint32_t)p.G * 2048u : N * K);
   const uint32_t MT16 = (M + 15u) / 16u;
-  const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.a, AP ? MT16 * (uint32_t)p.G * 2048u : M * K);
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.a, (AL >= 2) ? MT16 * (uint32_t)p.G * 2048u : M * K);
 
   // Loop-invariant lane offsets.  A row past the end gets a base of 2^31:
   // adding any in-range K offset (< 2^30) keeps it beyond num_records
@@ -295,6 +295,36 @@ __global__ void __launch_bounds__(NW * 64) qgemm_decode_kernel(DecodeArgs p) {
     }
   };
 
+  // ---- stage this chunk's activations in LDS first, with LDS-DMA buffer
+  // loads (no registers; their completion is awaited below, after the first
+  // weight batches are in flight): one 1 KB block b per (K block kbl, token
+  // tile mt, half h), b = (kbl*MT + mt)*2 + h, in which lane l holds token
+  // 16*mt + l%16, K bytes [h*64 + 16*(l/16), +16) of the K block.  Packed
+  // activations hold exactly these blocks contiguously; row-major ones are
+  // gathered 16 rows x 16 bytes at a time.
+  if constexpr (ALDS) {
+    const int nblk = nkc * MT * 2;
+    for (int b = wave; b < nblk; b += NW) {
+      const int h = b & 1;
+      const int mt = (b >> 1) % MT;
+      const int kbl = (b >> 1) / MT;
+      uint32_t off;
+      if constexpr (AL == 3) {
+        off = (uint32_t)mt < MT16
+                  ? ((uint32_t)mt * (uint32_t)p.G + (uint32_t)(kb0 + kbl)) * 2048u + (uint32_t)h * 1024u +
+                        (uint32_t)lane * 16u
+                  : OOB;
+      } else {
+        const uint32_t m = (uint32_t)(mt * 16 + r16);
+        const uint32_t k = (uint32_t)(kb0 + kbl) * 128u + (uint32_t)h * 64u + (uint32_t)g * 16u;
+        off = (m < M && k < K) ? m * K + k : OOB;
+      }
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          ra, (__attribute__((address_space(3))) void*)(smem + b * 1024), 16, off, 0, 0, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+
   // Two batches in flight: the loop enters and repeats with the same pair of
   // buffers outstanding (batch b in wb0, b+1 in wb1), and each buffer is
   // refilled right after it has been consumed.
@@ -321,23 +351,14 @@ __global__ void __launch_bounds__(NW * 64) qgemm_decode_kernel(DecodeArgs p) {
       }
   }
 
-  // ---- stage this chunk's activations in LDS (after the first weight
-  // batches are in flight, so their HBM latency overlaps the staging): one 1 KB block per
-  // (K block, token tile, half); lane l of a block holds token 16*mt + l%16,
-  // K bytes [h*64 + 16*(l/16), +16) of the K block.
+  // ---- activations staged in LDS: wait for the staging copies (issued
+  // before the weight batches, and vmcnt counts in issue order) while the
+  // weight batches stay in flight, then make LDS visible workgroup-wide.
   if constexpr (ALDS) {
-    const int nblk = nkc * MT * 2;
-    for (int b = wave; b < nblk; b += NW) {
-      const int h = b & 1;
-      const int mt = (b >> 1) % MT;
-      const int kbl = (b >> 1) / MT;
-      const uint32_t m = (uint32_t)(mt * 16 + r16);
-      const uint32_t k = (uint32_t)(kb0 + kbl) * 128u + (uint32_t)h * 64u + (uint32_t)g * 16u;
-      const uint32_t off = (m < M && k < K) ? m * K + k : OOB;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          ra, (__attribute__((address_space(3))) void*)(smem + b * 1024), 16, off, 0, 0, 0);
-    }
-    __syncthreads();
+    constexpr int NW_LOADS = 2 * PF * 2 * RG;  // weight loads of the two batches: all issued after the copies
+    static_assert(NW_LOADS <= 63, "vmcnt holds 6 bits");
+    __builtin_amdgcn_s_waitcnt((NW_LOADS & 15) | (7 << 4) | (15 << 8) | ((NW_LOADS >> 4) << 14));
+    lds_barrier();
   }
 
   for (int b = 0; b < nbatch; b += 2) {
@@ -523,8 +544,15 @@ hipError_t decode_try(const DecodeKey& k, dim3 grid, dim3 block, size_t lds, hip
   if constexpr (decode_config_fits<FMT, NW_, SW, MT_, RG_, PF_>()) {
     if (k.swap == SW && k.mt == MT_ && k.rg == RG_ && k.nw == NW_ && k.pf == PF_ && k.alds == AL && k.wm == WM_) {
       *hit = true;
-      if (probe_only) return hipSuccess;
-      qgemm_decode_kernel<FMT, SW != 0, MT_, RG_, NW_, PF_, AL, WM_><<<grid, block, lds, s>>>(a);
+      auto fn = qgemm_decode_kernel<FMT, SW != 0, MT_, RG_, NW_, PF_, AL, WM_>;
+      if (probe_only) {
+        // LDS beyond the default 64 KB needs the per-kernel opt-in (gfx950: 160 KB a workgroup)
+        if (lds > 64 * 1024)
+          return hipFuncSetAttribute(reinterpret_cast<const void*>(fn), hipFuncAttributeMaxDynamicSharedMemorySize,
+                                     (int)lds);
+        return hipSuccess;
+      }
+      fn<<<grid, block, lds, s>>>(a);
       return hipGetLastError();
     }
   }
@@ -542,13 +570,15 @@ hipError_t decode_dispatch(const DecodeKey& k, dim3 grid, dim3 block, size_t lds
   // 4 waves, every weight mode and activation staging
 #define QL_TRY_WL(SW, MT_, RG_, PF_, AL) \
   QL_TRY(4, SW, MT_, RG_, PF_, AL, 0) QL_TRY(4, SW, MT_, RG_, PF_, AL, 1) QL_TRY(4, SW, MT_, RG_, PF_, AL, 2)
-#define QL_TRY_AL(SW, MT_, RG_, PF_) \
-  QL_TRY_WL(SW, MT_, RG_, PF_, 0) QL_TRY_WL(SW, MT_, RG_, PF_, 1) QL_TRY(4, SW, MT_, RG_, PF_, 2, 2)
+#define QL_TRY_AL(SW, MT_, RG_, PF_)                                                      \
+  QL_TRY_WL(SW, MT_, RG_, PF_, 0) QL_TRY_WL(SW, MT_, RG_, PF_, 1) QL_TRY(4, SW, MT_, RG_, PF_, 2, 2) \
+  QL_TRY(4, SW, MT_, RG_, PF_, 3, 2)
 #define QL_TRY_PF(SW, MT_, RG_) QL_TRY_AL(SW, MT_, RG_, 2) QL_TRY_AL(SW, MT_, RG_, 4)
 #define QL_TRY_RG(SW, MT_) QL_TRY_PF(SW, MT_, 1) QL_TRY_PF(SW, MT_, 2)
   // packed weights, activations (row-major or packed) from L2: wider workgroups,
   // longer rows, 1-block batches
-#define QL_TRY_PA(NW_, SW, MT_, RG_, PF_) QL_TRY(NW_, SW, MT_, RG_, PF_, 0, 2) QL_TRY(NW_, SW, MT_, RG_, PF_, 2, 2)
+#define QL_TRY_PA(NW_, SW, MT_, RG_, PF_) \
+  QL_TRY(NW_, SW, MT_, RG_, PF_, 0, 2) QL_TRY(NW_, SW, MT_, RG_, PF_, 2, 2) QL_TRY(NW_, SW, MT_, RG_, PF_, 3, 2)
 #define QL_TRY_P(NW_, SW, MT_, RG_) QL_TRY_PA(NW_, SW, MT_, RG_, 1) QL_TRY_PA(NW_, SW, MT_, RG_, 2)
 #define QL_TRY_PN(SW, MT_)                                                                    \
   QL_TRY_PA(4, SW, MT_, 1, 1) QL_TRY_PA(4, SW, MT_, 2, 1) QL_TRY_P(4, SW, MT_, 4)             \

@@ -50,7 +50,7 @@ struct TiledAcc<FMT_INT8> {
   typedef i32x4 T;
 };
 
-template <int FMT, bool SWAP, int BM, int BN, int WM, int PF, bool AP>
+template <int FMT, bool SWAP, int BM, int BN, int WM, int PF, bool AP, int NS>
 __global__ void __launch_bounds__(256) qgemm_tiled_kernel(DecodeArgs p) {
   constexpr int TM = BM / 2, TN = BN / 2;  // wave tile
   constexpr int IM = TM / 16, IN = TN / 16;
@@ -231,7 +231,8 @@ __global__ void __launch_bounds__(256) qgemm_tiled_kernel(DecodeArgs p) {
   };
 
   // ---- main loop: LDS stage it&1 holds K block kb0+it while blocks
-  // kb0+it+1 .. kb0+it+PF are in flight in the register ring
+  // kb0+it+1 .. kb0+it+PF are in flight in the register ring (NS == 0), or
+  // an NS-stage LDS ring filled by LDS-DMA (NS > 0)
   float sa_c[SA_N], sw_c[SW_N];
   auto take_scales = [&](int sl) {
 #pragma unroll
@@ -243,7 +244,66 @@ __global__ void __launch_bounds__(256) qgemm_tiled_kernel(DecodeArgs p) {
   // unconditionally: blocks past the chunk are zeros and add nothing, and
   // the fixed instruction stream lets the compiler wait for exactly the
   // oldest ring slot instead of draining all loads in flight.
-  if (nk > 0) {
+  if constexpr (NS > 0) {
+    // ---- packed operands straight into an NS-stage LDS ring with LDS-DMA
+    // buffer loads (no staging registers).  A stage is the A tile's BM/16
+    // and the B tile's BN/16 2 KB tiles, each copied as two 1 KB wave loads;
+    // every wave issues DW of them per stage, so "stage it has landed" is
+    // "at most (NS-2)*DW of this wave's loads outstanding" followed by a
+    // barrier.  The refill of stage it-1's buffer goes out right after that
+    // barrier, before the matrix cores start on stage it.
+    static_assert(WP && AP && FMT != FMT_BLOCK, "the LDS-DMA ring reads packed operands");
+    constexpr int TA = BM / 16, TB = BN / 16;
+    constexpr int DA = 2 * TA / 4, DB = 2 * TB / 4;
+    constexpr int DW = DA + DB;
+    constexpr int ALLOW = (NS - 2) * DW;
+    static_assert(ALLOW <= 63, "vmcnt holds 6 bits");
+    // wave w copies 1 KB halves j = w + 4i: tile j/2 = w/2 + 2i, half w%2
+    const uint32_t a_lane = (m0 / 16u + (uint32_t)(wave >> 1)) * G * 2048u + (uint32_t)(wave & 1) * 1024u +
+                            (uint32_t)lane * 16u;
+    const uint32_t b_lane = (n0 / 16u + (uint32_t)(wave >> 1)) * G * 2048u + (uint32_t)(wave & 1) * 1024u +
+                            (uint32_t)lane * 16u;
+    const int lds_wave = (wave >> 1) * 2048 + (wave & 1) * 1024;
+    auto dma_stage = [&](int kb, int buf) {
+      const bool in = kb < kb1;
+      uint8_t* base = smem + buf * STAGE + lds_wave;
+      const uint32_t kofs = (uint32_t)kb * 2048u;
+#pragma unroll
+      for (int i = 0; i < DA; ++i) {
+        const uint32_t t = m0 / 16u + (uint32_t)(wave >> 1) + 2u * (uint32_t)i;
+        const uint32_t off = (in && t < MT16) ? a_lane + (uint32_t)i * 2u * G * 2048u + kofs : OOB;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (__attribute__((address_space(3))) void*)(base + i * 4096), 16,
+                                                 off, 0, 0, 0);
+      }
+#pragma unroll
+      for (int i = 0; i < DB; ++i) {
+        const uint32_t t = n0 / 16u + (uint32_t)(wave >> 1) + 2u * (uint32_t)i;
+        const uint32_t off = (in && t < NT16) ? b_lane + (uint32_t)i * 2u * G * 2048u + kofs : OOB;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rw, (__attribute__((address_space(3))) void*)(base + BM * 128 + i * 4096), 16, off, 0, 0, 0);
+      }
+    };
+    if (nk > 0) {
+      float sa_c[SA_N], sw_c[SW_N];
+#pragma unroll
+      for (int i = 0; i < SA_N; ++i) sa_c[i] = 0.f;
+#pragma unroll
+      for (int j = 0; j < SW_N; ++j) sw_c[j] = 0.f;
+#pragma unroll
+      for (int st = 0; st < NS - 1; ++st) dma_stage(kb0 + st, st);
+      // unrolled by NS so every stage index is a constant; the loop runs a
+      // multiple of NS blocks, those past the chunk being zeros
+      for (int it0 = 0; it0 < nk; it0 += NS) {
+#pragma unroll
+        for (int q = 0; q < NS; ++q) {
+          __builtin_amdgcn_s_waitcnt((ALLOW & 15) | (7 << 4) | (15 << 8) | ((ALLOW >> 4) << 14));
+          lds_barrier();
+          dma_stage(kb0 + it0 + q + NS - 1, (q + NS - 1) % NS);
+          compute(q, sa_c, sw_c);
+        }
+      }
+    }
+  } else if (nk > 0) {
     const int nloop = (nk + PF - 1) / PF * PF;
     load_block(kb0, 0);
     load_scales(kb0, 0);
@@ -324,7 +384,28 @@ __global__ void __launch_bounds__(256) qgemm_tiled_kernel(DecodeArgs p) {
     if (tid == 0) __hip_atomic_exchange(p.counters + tile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 
-  // ---- epilogue
+  // ---- epilogue.  The per-token formats need one s_a per token row and one
+  // s_w per output column this lane holds: IM x (1 or 4) and IN x (4 or 1)
+  // values, loaded once (not per element, which would keep hundreds of
+  // loads in flight next to the accumulators).
+  constexpr int EA = FMT == FMT_BLOCK ? 1 : (SWAP ? 1 : 4), EW = FMT == FMT_BLOCK ? 1 : (SWAP ? 4 : 1);
+  float ea[IM][EA], ew[IN][EW];
+  if constexpr (FMT != FMT_BLOCK) {
+#pragma unroll
+    for (int i = 0; i < IM; ++i)
+#pragma unroll
+      for (int r = 0; r < EA; ++r) {
+        const uint32_t m = elem_m(i, r);
+        ea[i][r] = bload_f32(rsa, m < M ? m * 4u : OOB);
+      }
+#pragma unroll
+    for (int j = 0; j < IN; ++j)
+#pragma unroll
+      for (int r = 0; r < EW; ++r) {
+        const uint32_t n = elem_n(j, r);
+        ew[j][r] = bload_f32(rsw, n < N ? n * 4u : OOB);
+      }
+  }
   const bool vec4 = SWAP && (N & 3u) == 0;
 #pragma unroll
   for (int i = 0; i < IM; ++i) {
@@ -339,8 +420,8 @@ __global__ void __launch_bounds__(256) qgemm_tiled_kernel(DecodeArgs p) {
           out[r] = bf16_rne(acc[i][j][r]);
           if (ok && p.acc_out) reinterpret_cast<float*>(p.acc_out)[(size_t)m * N + n] = acc[i][j][r];
         } else {
-          const float sa = bload_f32(rsa, m < M ? m * 4u : OOB);
-          const float sw = bload_f32(rsw, n < N ? n * 4u : OOB);
+          const float sa = ea[i][EA == 4 ? r : 0];
+          const float sw = ew[j][EW == 4 ? r : 0];
           float accf;
           if constexpr (FMT == FMT_INT8)
             accf = __int2float_rn(acc[i][j][r]);
@@ -368,6 +449,9 @@ __global__ void __launch_bounds__(256) qgemm_tiled_kernel(DecodeArgs p) {
           if (m < M && n < N) p.y[(size_t)m * N + n] = (uint16_t)out[r];
         }
       }
+      // one 16x16 tile at a time: keeps the scheduler from reading many
+      // accumulator tiles out of the matrix-core registers at once
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
 }
@@ -376,21 +460,22 @@ __global__ void __launch_bounds__(256) qgemm_tiled_kernel(DecodeArgs p) {
 // accumulator tiles, at most 128 registers (256 x 256 would spill).
 // Block_FP8 in the standard orientation also keeps four token scales per
 // accumulator tile row live, so its largest tiles are left out as well.
-template <int FMT, int SW, int BM, int BN, int PF>
+template <int FMT, int SW, int BM, int BN, int PF, int NS>
 constexpr bool tiled_config_fits() {
+  if (NS > 0) return FMT != FMT_BLOCK && NS * (BM + BN) * 128 <= 160 * 1024 && BM * BN <= 128 * 256;
   if (FMT == FMT_BLOCK && !SW && BM * BN > 128 * 128) return false;
   if (PF * (BM + BN) > 768) return false;  // ring of PF K blocks: at most 96 VGPRs a lane
   if (FMT == FMT_BLOCK && BM * BN > 128 * 128 && PF > 1) return false;
   return BM * BN <= 128 * 256;
 }
 
-template <int FMT, int SW, int BM, int BN, int WM_, int PF, int AP>
+template <int FMT, int SW, int BM, int BN, int WM_, int PF, int AP, int NS>
 hipError_t tiled_try(const TiledKey& k, dim3 grid, size_t lds, hipStream_t s, const DecodeArgs& a, bool probe_only,
                      bool* hit) {
-  if constexpr (tiled_config_fits<FMT, SW, BM, BN, PF>()) {
-    if (k.swap == SW && k.bm == BM && k.bn == BN && k.wm == WM_ && k.pf == PF && k.ap == AP) {
+  if constexpr (tiled_config_fits<FMT, SW, BM, BN, PF, NS>()) {
+    if (k.swap == SW && k.bm == BM && k.bn == BN && k.wm == WM_ && k.pf == PF && k.ap == AP && k.ns == NS) {
       *hit = true;
-      auto fn = qgemm_tiled_kernel<FMT, SW != 0, BM, BN, WM_, PF, AP != 0>;
+      auto fn = qgemm_tiled_kernel<FMT, SW != 0, BM, BN, WM_, PF, AP != 0, NS>;
       if (probe_only) {
         // stages above the default 64 KB need the per-kernel opt-in (gfx950: 160 KB per workgroup)
         return hipFuncSetAttribute(reinterpret_cast<const void*>(fn), hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -409,8 +494,13 @@ hipError_t tiled_dispatch(const TiledKey& k, dim3 grid, size_t lds, hipStream_t 
   bool hit = false;
   hipError_t e = hipSuccess;
 #define QL_TT(SW, BM, BN, WM_, PF, AP)                                                  \
-  e = tiled_try<FMT, SW, BM, BN, WM_, PF, AP>(k, grid, lds, s, a, probe_only, &hit);    \
+  e = tiled_try<FMT, SW, BM, BN, WM_, PF, AP, 0>(k, grid, lds, s, a, probe_only, &hit); \
   if (hit) return e;
+  // packed operands through the LDS-DMA ring of NS stages (prefetch field = 1)
+#define QL_TD(SW, BM, BN, NS)                                                          \
+  e = tiled_try<FMT, SW, BM, BN, 2, 1, 1, NS>(k, grid, lds, s, a, probe_only, &hit);   \
+  if (hit) return e;
+#define QL_TD_S(BM, BN, NS) QL_TD(0, BM, BN, NS) QL_TD(1, BM, BN, NS)
 #define QL_TT_P(SW, BM, BN, WM_, AP) \
   QL_TT(SW, BM, BN, WM_, 1, AP) QL_TT(SW, BM, BN, WM_, 2, AP) QL_TT(SW, BM, BN, WM_, 4, AP)
   // (row-major W, row-major A), (packed W, row-major A), (packed W, packed A)
@@ -421,6 +511,14 @@ hipError_t tiled_dispatch(const TiledKey& k, dim3 grid, size_t lds, hipStream_t 
   QL_TT_S(128, 128)
   QL_TT_S(128, 256)
   QL_TT_S(256, 128)
+  QL_TD_S(128, 128, 2)
+  QL_TD_S(128, 128, 3)
+  QL_TD_S(128, 256, 2)
+  QL_TD_S(128, 256, 3)
+  QL_TD_S(256, 128, 2)
+  QL_TD_S(256, 128, 3)
+#undef QL_TD_S
+#undef QL_TD
 #undef QL_TT_S
 #undef QL_TT_W
 #undef QL_TT_P

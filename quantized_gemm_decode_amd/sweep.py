@@ -64,11 +64,13 @@ TILES = ((64, 128), (64, 256), (128, 128), (128, 256), (256, 128))
 
 
 def tiled_candidates(M, N, K, layout):
-    """Every tiled configuration for M > 32 (tile, orientation, split, ring depth)."""
-    for (bm, bn), swap, split, pf in itertools.product(TILES, (0, 1), (1, 2, 4, 8), (1, 2, 4)):
+    """Every tiled configuration for M > 32 (tile, orientation, split, register-ring depth,
+    and with packed operands the LDS-DMA ring of 2 or 3 stages)."""
+    rings = [(0, 1), (0, 2), (0, 4)] + ([(1, 2), (1, 3)] if layout == 2 else [])
+    for (bm, bn), swap, split, (dma, pf) in itertools.product(TILES, (0, 1), (1, 2, 4, 8), rings):
         if bm > 64 and bm > 2 * M:
             continue
-        yield dict(algo=ql.ALGO_TILED, swap_ab=swap, split_k=split, tile_m=bm, tile_n=bn, prefetch=pf,
+        yield dict(algo=ql.ALGO_TILED, swap_ab=swap, split_k=split, tile_m=bm, tile_n=bn, prefetch=pf, w_lds=dma,
                    a_mode=2 if layout == 2 else 0, w_layout=1 if layout >= 1 else 0)
 
 
@@ -78,7 +80,7 @@ def phase1_candidates(fmt, M, N, K, layout=0):
         return
     seen = set()
     waves, rows_set = (WAVES, (16, 32)) if layout == 0 else (WAVES_PACKED, (16, 32, 64))
-    amodes = (2,) if layout == 2 else (1, 0)
+    amodes = (3, 2) if layout == 2 else (1, 0)
     for (wn, wk), rows, split, alds, wlds in itertools.product(waves, rows_set, SPLITS, amodes,
                                                               (1, 0) if layout == 0 else (0,)):
         ch = _effective_chunks(K, split)

@@ -63,8 +63,8 @@ def _assert_parity(fmt, r, y, acc, split, label="", waves_k=16):
 # every kernel instantiation: swap x rows/wave x prefetch x activation LDS staging x weight mode
 # (0 row-major direct, 1 row-major through the LDS transpose, 2 packed tiles), both token tiles
 # (instantiations that would spill registers do not exist)
-VARIANTS = [v for v in itertools.product([0, 1], [16, 32], [2, 4], [0, 1, 2], [0, 1, 2])
-            if v[3] != 2 or v[4] == 2]        # packed activations (a_mode 2) go with packed weights
+VARIANTS = [v for v in itertools.product([0, 1], [16, 32], [2, 4], [0, 1, 2, 3], [0, 1, 2])
+            if v[3] < 2 or v[4] == 2]         # packed activations (a_mode 2, 3) go with packed weights
 SPLITS = [1, 2, 4, 8]
 WAVES_K = [1, 2, 4]
 
@@ -85,13 +85,13 @@ def test_every_instantiation_matches_oracle(fmt, M, vi):
         plan = ql.qlinear_plan_with_config(fmt, M, N, K, cfg)
     except ql.QLinearError as e:
         spill = (M > 16 and rows == 32 and pf == 4 or (fmt == ql.BLOCK_FP8 and M > 16 and pf == 4 and not swap)
-                 or alds == 2)   # 4-wave packed-activation shapes exist for the register-fitting ones only
+                 or alds >= 2)   # 4-wave packed-activation shapes exist for the register-fitting ones only
         assert e.status == 2 and (spill or "LDS" in str(e)), e
         pytest.skip("configuration not available: %s" % e)
     a_q, s_a, w_q, s_w = _dev(fmt, r)
     if wmode == 2:
         w_q = ql.pack_weight(w_q)
-    if alds == 2:
+    if alds >= 2:
         a_q = _dev_packed_act(fmt, r)
     y, acc, ws = run_gemm(plan, a_q, s_a, w_q, s_w)
     _assert_parity(fmt, r, y, acc, plan.facts["chunks"], label=str(cfg))
@@ -100,7 +100,7 @@ def test_every_instantiation_matches_oracle(fmt, M, vi):
 
 
 # packed-weight shapes with wider workgroups: waves per workgroup x rows per wave x batch size
-WIDE = list(itertools.product([4, 8, 16], [16, 32, 64], [1, 2], [0, 1], [0, 2]))   # ... x activation mode
+WIDE = list(itertools.product([4, 8, 16], [16, 32, 64], [1, 2], [0, 1], [0, 2, 3]))   # ... x activation mode
 
 
 @pytest.mark.parametrize("fmt", FMTS)
@@ -122,7 +122,7 @@ def test_wide_workgroup_instantiations_match_oracle(fmt, M, wi):
         assert e.status == 2, e
         pytest.skip("configuration not available: %s" % e)
     a_q, s_a, w_q, s_w = _dev(fmt, r)
-    if amode == 2:
+    if amode >= 2:
         a_q = _dev_packed_act(fmt, r)
     y, acc, ws = run_gemm(plan, a_q, s_a, ql.pack_weight(w_q), s_w)
     _assert_parity(fmt, r, y, acc, plan.facts["chunks"], label=str(cfg), waves_k=wk)
@@ -241,7 +241,7 @@ def test_forward_with_packed_operands(fmt, M):
     x, w = make_inputs(K, N, M, 0.02, seed=22 + M)
     r = oracle.reference(fmt, bf16_bits(x), bf16_bits(w))
     plan = ql.qlinear_plan_layouts(fmt, M, N, K, 1, 1)
-    assert plan.config["a_mode"] == 2
+    assert plan.config["a_mode"] >= 2
     w_q, w_s = ql.quantize_weight(fmt, w.cuda())
     a_p = ql.act_buffer(plan)
     a_s = torch.empty(ql.act_scale_shape(fmt, M, K), dtype=torch.float32, device="cuda")
@@ -405,7 +405,7 @@ def test_every_table_entry_matches_oracle(entry):
     a_q, a_s = ql.quantize_act(fmt, xm.cuda())
     plan = ql.qlinear_plan_with_config(fmt, M, N, K, cfg)
     y = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
-    if cfg["a_mode"] == 2:
+    if cfg["a_mode"] >= 2:
         a_q, _ = ql.quantize_act_packed(fmt, xm.cuda())
     ql.qlinear_run(plan, a_q, a_s, ql.pack_weight(w_q) if cfg["w_layout"] else w_q, w_s, y, plan.new_workspace())
     torch.cuda.synchronize()

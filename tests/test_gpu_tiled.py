@@ -58,6 +58,29 @@ def test_every_tiled_instantiation_matches_oracle(fmt, M, vi):
         assert int(torch.count_nonzero(ws)) == 0, "split-K workspace not left all-zero"
 
 
+DMA_VARIANTS = list(itertools.product([0, 1], [(128, 128), (128, 256), (256, 128)], [2, 3]))
+
+
+@pytest.mark.parametrize("fmt", [ql.FP8_DYNAMIC, ql.W8A8_INT8])
+@pytest.mark.parametrize("M", [40, 300])
+@pytest.mark.parametrize("vi", range(len(DMA_VARIANTS)))
+def test_tiled_lds_dma_ring_matches_oracle(fmt, M, vi):
+    """Packed operands streamed into an LDS ring by LDS-DMA (w_lds = 1), with
+    ragged M, N and K (a last K block of 16 bytes) and split-K."""
+    swap, (bm, bn), ns = DMA_VARIANTS[vi]
+    split = [1, 2, 4][(vi + M) % 3]
+    N, K = 520 + 16 * vi, 1040 if vi % 2 else 1152
+    r = _ref(fmt, M, N, K, seed=5000 + vi * 3 + M)
+    cfg = dict(algo=ql.ALGO_TILED, swap_ab=swap, split_k=split, tile_m=bm, tile_n=bn, w_layout=1, a_mode=2,
+               w_lds=1, prefetch=ns)
+    plan = ql.qlinear_plan_with_config(fmt, M, N, K, cfg)
+    a_q, s_a, w_q, s_w = (dev_codes(fmt, r["a_q"]), dev_f32(r["s_a"]), dev_codes(fmt, r["w_q"]), dev_f32(r["s_w"]))
+    y, acc, ws = run_gemm(plan, _dev_packed_act(fmt, r), s_a, ql.pack_weight(w_q), s_w)
+    _assert_parity(fmt, r, y, acc, plan.facts["chunks"], label=str(cfg))
+    if ws is not None:
+        assert int(torch.count_nonzero(ws)) == 0, "split-K workspace not left all-zero"
+
+
 @pytest.mark.parametrize("fmt", FMTS)
 def test_tiled_matches_decode_bitwise_for_int8_and_closely_for_fp8(fmt):
     """The same M = 32 problem through both algorithms: INT8 identical bits,
