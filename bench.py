@@ -174,6 +174,7 @@ def trace_summary(workload, layout, trace_csv, stats_csv, bench_json, ref_json=N
              "# hip_events = the same run's HIP-event time per launch (median of replays / R)",
              "# shape    M    kernel_instantiation                                   rocprof_us  hip_events_us  ratio"]
     tot_r = tot_e = 0.0
+    per_us = []
     for p, run in zip(pp, runs):
         n_timed = len(run) * 5 // 8
         timed = run[-n_timed:]
@@ -181,19 +182,28 @@ def trace_summary(workload, layout, trace_csv, stats_csv, bench_json, ref_json=N
         name = run[0]["Kernel_Name"].split("(")[0].replace("void ", "").replace("qlk::", "")
         tot_r += us
         tot_e += p["us"]
+        per_us.append(us)
         lines.append("# %-8s %-4d %-54s %9.3f %13.3f  %.3f" % (p["shape"], p["M"], name, us, p["us"], p["us"] / us))
     lines.append("# sum over the %d points: rocprof %.2f us, hip events %.2f us (ratio %.3f)" % (len(pp), tot_r, tot_e,
                                                                                               tot_e / tot_r))
-    lines.append("# achieved (algorithmic bytes / rocprof durations): %.1f GB/s; bench roofline.achieved: %.1f GB/s"
-                 % (bench["roofline"]["algorithmic_bytes"] / (tot_r * 1e-6) / 1e9
-                    if "algorithmic_bytes" in bench["roofline"] else float("nan"), bench["roofline"]["achieved"]))
+    rl = bench["roofline"]
+    if rl["unit"] == "GB/s":
+        ach = rl["algorithmic_bytes"] / (tot_r * 1e-6) / 1e9
+        what = "algorithmic bytes of every point"
+    else:
+        big = [(p, us) for p, us in zip(pp, per_us) if p["M"] >= 1024]
+        ach = sum(2.0 * p["M"] * p["N"] * p["K"] for p, _ in big) / (sum(us for _, us in big) * 1e-6) / 1e12
+        what = "2*M*N*K of the M >= 1024 points"
+    lines.append("# achieved (%s / rocprof durations): %.1f %s; bench roofline.achieved: %.1f %s"
+                 % (what, ach, rl["unit"], rl["achieved"], rl["unit"]))
     if ref_json:
         ref = json.loads(open(ref_json).read().strip().splitlines()[-1])
         ref_pp = {(q["shape"], q["M"]): q["us"] for q in ref["per_point"]}
         tot_ref = sum(ref_pp.get((p["shape"], p["M"]), float("nan")) for p in pp)
-        lines.append("# the same bench without the profiler (%s): roofline.achieved %.1f GB/s; its per-launch "
+        lines.append("# the same bench without the profiler (%s): roofline.achieved %.1f %s; its per-launch "
                      "times sum to %.2f us, %.3f x the rocprof kernel durations above"
-                     % (os.path.basename(ref_json), ref["roofline"]["achieved"], tot_ref, tot_ref / tot_r))
+                     % (os.path.basename(ref_json), ref["roofline"]["achieved"], ref["roofline"]["unit"], tot_ref,
+                        tot_ref / tot_r))
     lines.append("# rocprofv3 --stats kernel summary (all launches of the run, every phase):")
     for line in open(stats_csv):
         lines.append("#   " + line.rstrip())

@@ -44,7 +44,9 @@ ql_status hip_fail(hipError_t e, const char* what) {
   return fail(QL_E_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
-constexpr int64_t kLdsLimit = 160 * 1024;    // gfx950: LDS per workgroup (above 64 KB with the per-kernel opt-in)
+// gfx950: LDS per workgroup (above 64 KB with the per-kernel opt-in), less
+// room for the kernels' own static LDS variables
+constexpr int64_t kLdsLimit = 160 * 1024 - 256;
 constexpr int kBuckets[] = {1, 2, 4, 8, 16, 24, 32};
 
 bool valid_fmt(int32_t f) { return f == QL_FP8_DYNAMIC || f == QL_W8A8_INT8 || f == QL_BLOCK_FP8; }
@@ -167,7 +169,7 @@ ql_config heuristic_config(int32_t fmt, int32_t layout, bool a_packed, int64_t M
   return c;
 }
 
-constexpr int64_t kTiledLdsLimit = 160 * 1024;  // gfx950: LDS per workgroup with the per-kernel opt-in
+constexpr int64_t kTiledLdsLimit = 160 * 1024 - 256;  // as kLdsLimit
 
 ql_status build_tiled_plan(int32_t fmt, int64_t M, int64_t N, int64_t K, const ql_config& cfg, int32_t source,
                            ql_plan* out) {

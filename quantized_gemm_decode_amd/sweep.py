@@ -119,6 +119,9 @@ class Timer:
             a_q, a_s = ql.quantize_act(fmt, self.x[:M].contiguous())
         y = torch.empty(M, self.N, dtype=torch.bfloat16, device="cuda")
         wsp = plan.new_workspace()
+        # one eager launch first: a configuration that cannot launch fails here,
+        # not later inside a captured graph
+        ql.qlinear_run(plan, a_q, a_s, self.wq[0], self.ws[0], y, wsp)
         torch.cuda.synchronize()
         R = self.copies
         with torch.cuda.stream(s):
@@ -180,7 +183,11 @@ def sweep_point(timer, fmt, M, N, K, log=print, top=6):
         if plan is None:
             continue
         cfg = dict(cfg, split_k=plan.config["split_k"])
-        us, y = timer.measure(plan, M)
+        try:
+            us, y = timer.measure(plan, M)
+        except ql.QLinearError as e:
+            log("  SKIP (does not launch: %s): %s" % (e, cfg))
+            continue
         if ref is None:
             ref = y
         elif not _agrees(fmt, y, ref):
@@ -198,9 +205,9 @@ def sweep_point(timer, fmt, M, N, K, log=print, top=6):
             seen.add(k)
             try:
                 plan = ql.qlinear_plan_with_config(fmt, M, N, K, cfg)
+                us, y = timer.measure(plan, M)
             except ql.QLinearError:
                 continue
-            us, y = timer.measure(plan, M)
             if not _agrees(fmt, y, ref):
                 log("  DROP (disagrees): %s" % cfg)
                 continue
