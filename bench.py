@@ -9,9 +9,11 @@ projections -- QKV 6144x4096, O 4096x4096, gate_up 24576x4096, down
 One step = the whole hot path for every point: dynamic activation quantizer,
 then the planned GEMM (standard / split-K / swap-AB from the sweep table),
 captured once into hipGraphs and replayed.  By default the weights are packed
-offline (qlinear_pack_weight) and the quantizer writes packed activations, so
-every operand load of the GEMM is a contiguous kilobyte; --layout selects the
-row-major paths instead.  --workload fp8_dynamic_14b_large_m runs the
+offline (qlinear_pack_weight) and each point runs its forward plan: where the
+sweep found it faster, one launch that quantizes inside the GEMM (fused
+quantization), else the quantizer writing packed activations and then the
+GEMM -- either way every operand load of the GEMM is a contiguous kilobyte.
+--layout selects the unfused packed or the row-major paths instead.  --workload fp8_dynamic_14b_large_m runs the
 M = 64..4096 points through the tiled kernel and prices them against the
 matrix-core peak instead of HBM.  Inputs are synthetic and resident
 in HBM before timing.  Every GEMM of a step reads its own copy of the weights
@@ -43,13 +45,22 @@ def algorithmic_bytes(fmt, M, N, K):
     return N * K + 4 * N + M * K + 4 * M + 2 * M * N
 
 
+def fused_kernel_bytes(fmt, M, N, K):
+    """Bytes one fused-quantization GEMM launch must move: weights and their
+    scales, bf16 X in, the codes and scales it hands back, and Y."""
+    return N * K + 4 * N + 2 * M * K + M * K + 4 * M + 2 * M * N
+
+
 def quantizer_bytes(fmt, M, K):
     return 2 * M * K + M * K + (4 * M * (K // 128) if fmt == 2 else 4 * M)
 
 
 PKG = os.path.join(ROOT, "quantized_gemm_decode_amd")
-LAYOUT_NAMES = {"packed": "packed weights and activations", "packedw": "packed weights, row-major activations",
+LAYOUT_NAMES = {"fused": "packed weights, forward plans (quantization fused into the GEMM where faster)",
+                "packed": "packed weights and activations", "packedw": "packed weights, row-major activations",
                 "rowmajor": "row-major weights and activations"}
+# (w_layout, a_packed) of qlinear_plan_layouts per --layout
+LAYOUT_PLAN = {"fused": (1, 2), "packed": (1, 1), "packedw": (1, 0), "rowmajor": (0, 0)}
 PROFILES = os.path.join(ROOT, "profiles")
 
 
@@ -88,6 +99,14 @@ def recorded_traffic(workload, layout):
     return int(kv["traffic_bytes_per_step"]), "rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE, copy-calibrated"
 
 
+def is_fused_instantiation(name):
+    """A qgemm_decode_kernel<FMT, SWAP, MT, RG, NW, PF, AL, WM> name with AL = 4."""
+    if "qgemm_decode_kernel<" not in name:
+        return False
+    args = name.split("qgemm_decode_kernel<", 1)[1].split(">", 1)[0].split(",")
+    return len(args) == 8 and args[6].strip() == "4"
+
+
 def pmc_summary(workload, layout, fetch_csv, write_csv):
     """Summarise two rocprofv3 --pmc runs of --profile-pass into the traffic record."""
     import csv
@@ -120,14 +139,15 @@ def pmc_summary(workload, layout, fetch_csv, write_csv):
              "# calibration: a 256 MiB device copy reads FETCH_SIZE %.1f KiB and WRITE_SIZE %.1f KiB per dispatch"
              % (fetch_copy, write_copy),
              "#   -> bytes = FETCH_SIZE * %.4f KiB, WRITE_SIZE * %.4f KiB" % (kf, kw),
-             "# per GEMM: mean of 3 dispatches on distinct weight copies",
+             "# per GEMM: mean of 3 dispatches on distinct weight copies (a fused-quantization launch's",
+             "# algorithmic bytes include bf16 X in and the codes and scales out)",
              "# shape    M    algorithmic_B   fetched_B  written_B  traffic/alg"]
     tot_a = tot_t = 0
     for i, (lab, N, K, M) in enumerate(pts):
         g = gem[3 * i:3 * i + 3]
         fb = sum(x[0] for x in g) / 3 * 1024 * kf
         wb = sum(x[1] for x in g) / 3 * 1024 * kw
-        ab = algorithmic_bytes(wl.fmt, M, N, K)
+        ab = (fused_kernel_bytes if is_fused_instantiation(g[0][2]) else algorithmic_bytes)(wl.fmt, M, N, K)
         tot_a += ab
         tot_t += fb + wb
         lines.append("# %-8s %-4d %13d %11.0f %10.0f  %.4f" % (lab, M, ab, fb, wb, (fb + wb) / ab))
@@ -149,19 +169,18 @@ def trace_summary(workload, layout, trace_csv, stats_csv, bench_json, ref_json=N
         if line.startswith("{"):
             bench = json.loads(line)
     pp = bench["per_point"]
-    # the per-point timing phase ends the run: for each point a block of consecutive GEMM
-    # launches (3 warm-up replays + kernel-reps timed replays of R launches), then the quantizer
-    runs, cur = [], []
-    for r in rows:
-        if "qgemm" in r["Kernel_Name"]:
-            cur.append(r)
-        else:
-            if cur:
-                runs.append(cur)
-            cur = []
-    if cur:
-        runs.append(cur)
-    runs = runs[-len(pp):]
+    # The per-point timing phase ends the run: for each point a block of
+    # (3 warm-up + kernel-reps timed) graph replays of R GEMM launches, in
+    # point order (the unfused points' quantizer runs between blocks and is
+    # skipped).  Slice the GEMM launches by those counts from the end.
+    reps = bench.get("kernel_reps", 5)
+    gemm = [r for r in rows if "qgemm" in r["Kernel_Name"]]
+    sizes = [(3 + reps) * p["R"] for p in pp]
+    tail = gemm[-sum(sizes):]
+    runs, at = [], 0
+    for n in sizes:
+        runs.append((tail[at:at + n], n * reps // (3 + reps)))
+        at += n
     lines = ["# rocprofv3 kernel trace of the GEMM kernels, workload %s, %s" % (workload, LAYOUT_NAMES[layout]),
              "# command (from /tmp with TMPDIR=/tmp):",
              "#   rocprofv3 --kernel-trace --stats -f csv -d <dir> -o bench -- python3 <repo>/bench.py --workload %s "
@@ -175,8 +194,7 @@ def trace_summary(workload, layout, trace_csv, stats_csv, bench_json, ref_json=N
              "# shape    M    kernel_instantiation                                   rocprof_us  hip_events_us  ratio"]
     tot_r = tot_e = 0.0
     per_us = []
-    for p, run in zip(pp, runs):
-        n_timed = len(run) * 5 // 8
+    for p, (run, n_timed) in zip(pp, runs):
         timed = run[-n_timed:]
         us = sum(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]) for r in timed) / len(timed) / 1e3
         name = run[0]["Kernel_Name"].split("(")[0].replace("void ", "").replace("qlk::", "")
@@ -216,9 +234,11 @@ def parse_args(argv=None):
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="fp8_dynamic_8b")
-    ap.add_argument("--layout", choices=("packed", "packedw", "rowmajor"), default="packed",
-                    help="operand layouts: packed weights (qlinear_pack_weight, offline) and packed activations "
-                         "(the quantizer writes them), packed weights only, or row-major both")
+    ap.add_argument("--layout", choices=("fused", "packed", "packedw", "rowmajor"), default="fused",
+                    help="fused: packed weights (qlinear_pack_weight, offline) and each point's forward plan, "
+                         "with the quantizer fused into the GEMM where the sweep found that faster; packed: "
+                         "packed weights and activations (the quantizer writes them), two launches; packedw: "
+                         "packed weights only; rowmajor: row-major both")
     ap.add_argument("--kernel-reps", type=int, default=30, help="graph replays per point for kernel timing")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=20.0)
@@ -290,16 +310,18 @@ def main(argv=None):
     pts = []
     for (lab, N, K, M) in points:
         sh = shapes[lab]
-        w_layout, a_packed = {"packed": (1, 1), "packedw": (1, 0), "rowmajor": (0, 0)}[args.layout]
+        w_layout, a_packed = LAYOUT_PLAN[args.layout]
         plan = ql.qlinear_plan_layouts(fmt, M, N, K, w_layout, a_packed)
         cfg, facts = plan.info()
+        fused = cfg["algo"] == ql.ALGO_DECODE and cfg["a_mode"] == 4
         pts.append(dict(lab=lab, N=N, K=K, M=M, plan=plan, cfg=cfg, facts=facts,
                         x=sh["x"][:M].contiguous(),
                         a_q=ql.act_buffer(plan, dev),
                         a_s=torch.empty(ql.act_scale_shape(fmt, M, K), dtype=torch.float32, device=dev),
                         y=torch.empty(M, N, dtype=torch.bfloat16, device=dev),
-                        wsp=plan.new_workspace(dev),
-                        bytes=algorithmic_bytes(fmt, M, N, K), qbytes=quantizer_bytes(fmt, M, K)))
+                        wsp=plan.new_workspace(dev), fused=fused,
+                        bytes=algorithmic_bytes(fmt, M, N, K), qbytes=quantizer_bytes(fmt, M, K),
+                        kbytes=fused_kernel_bytes(fmt, M, N, K) if fused else algorithmic_bytes(fmt, M, N, K)))
 
     if args.profile_pass:
         return profile_pass(ql, fmt, pts, shapes, stream)
@@ -335,6 +357,8 @@ def main(argv=None):
     value = step_bytes / (step_ms * 1e-3) / 1e9
 
     # ------------------------------------------------ per-point GEMM kernel timing (HIP events)
+    # R back-to-back launches of the point's GEMM kernel: qlinear_run, or for a
+    # fused plan qlinear_forward (which is that one kernel launch)
     reps = args.kernel_reps
     per_point = []
     tot_bytes = tot_us = tot_flops = 0.0
@@ -344,10 +368,16 @@ def main(argv=None):
         with torch.cuda.stream(stream):
             ql.qlinear_graph_begin(stream)
             for c in range(R):
-                ql.qlinear_run(p["plan"], p["a_q"], p["a_s"], sh["wq"][c], sh["ws"][c], p["y"], p["wsp"],
-                               stream=stream)
+                if p["fused"]:
+                    ql.qlinear_forward(p["plan"], p["x"], p["a_q"], p["a_s"], sh["wq"][c], sh["ws"][c], p["y"],
+                                       p["wsp"], stream=stream)
+                else:
+                    ql.qlinear_run(p["plan"], p["a_q"], p["a_s"], sh["wq"][c], sh["ws"][c], p["y"], p["wsp"],
+                                   stream=stream)
             g = ql.qlinear_graph_end(stream)
-            if p["cfg"]["a_mode"] >= 2:
+            if p["fused"]:
+                pass
+            elif p["cfg"]["a_mode"] >= 2:
                 ql.qlinear_quantize_act_packed(fmt, p["x"], p["a_q"], p["a_s"], stream=stream)
             else:
                 ql.qlinear_quantize_act(fmt, p["x"], p["a_q"], p["a_s"], stream=stream)
@@ -364,9 +394,9 @@ def main(argv=None):
             e1.synchronize()
             samples.append(e0.elapsed_time(e1) * 1e3 / R)
         us = float(np.median(samples))
-        gbs = p["bytes"] / (us * 1e-6) / 1e9
+        gbs = p["kbytes"] / (us * 1e-6) / 1e9
         flops = 2.0 * p["M"] * p["N"] * p["K"]
-        tot_bytes += p["bytes"]
+        tot_bytes += p["kbytes"]
         tot_flops += flops
         tot_us += us
         per_point.append(dict(shape=p["lab"], M=p["M"], N=p["N"], K=p["K"], us=round(us, 3),
@@ -377,6 +407,7 @@ def main(argv=None):
                               variant=("split-k" if p["facts"]["chunks"] > 1 else
                                        ("swap-ab" if p["cfg"]["swap_ab"] else "standard")),
                               split=p["facts"]["chunks"], swap_ab=p["cfg"]["swap_ab"],
+                              fused_quant=p["fused"], kernel_bytes=int(p["kbytes"]), R=R,
                               source=p["facts"]["source"]))
         del g
     achieved = tot_bytes / (tot_us * 1e-6) / 1e9
@@ -385,9 +416,11 @@ def main(argv=None):
         roofline = {"kernel": "qgemm_decode_kernel", "bound": "hbm", "achieved": round(achieved, 1),
                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                     "traffic": traffic, "algorithmic_bytes": int(tot_bytes), "traffic_source": traffic_note,
-                    "note": "algorithmic bytes of one launch of each of the %d GEMMs / sum of their per-launch "
-                            "durations (HIP events around graph replays of back-to-back launches); traffic is "
-                            "the HBM bytes those same %d launches moved" % (len(pts), len(pts))}
+                    "note": "algorithmic bytes of one launch of each of the %d GEMM kernels (a fused-"
+                            "quantization launch also reads bf16 X and writes the codes and scales) / sum of "
+                            "their per-launch durations (HIP events around graph replays of back-to-back "
+                            "launches); traffic is the HBM bytes those same %d launches moved"
+                            % (len(pts), len(pts))}
     else:
         # token counts in the hundreds and thousands: the tiled kernel is matrix-core bound
         big = [q for q in per_point if q["M"] >= 1024]
@@ -423,6 +456,7 @@ def main(argv=None):
                    "shapes": ["%s %dx%d" % s for s in wl.shapes], "token_counts": list(wl.ms),
                    "gemms_per_step": len(pts), "graph_replay": True, "table_entries": n_table,
                    "weight_layout": args.layout,
+                   "fused_quant_points": sum(1 for p in pts if p["fused"]),
                    "us_per_gemm_step_avg": round(step_ms * 1e3 / len(pts), 3)},
         "roofline": roofline,
         "cpu_baseline": cpu,

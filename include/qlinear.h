@@ -113,7 +113,12 @@ typedef struct {
   int32_t a_mode;        /* activations: 0 = row-major A_q read per K block; 1 (DECODE) = row-major
                             A_q chunk staged in LDS; 2 = packed A_q (qlinear_quantize_act_packed)
                             read per K block; 3 (DECODE) = packed A_q chunk staged in LDS and
-                            shared by the workgroup's waves.  2 and 3 need packed weights */
+                            shared by the workgroup's waves; 4 (DECODE) = fused quantization:
+                            every workgroup quantizes the bf16 rows of X itself (row amax,
+                            then the codes of its K chunk into LDS) and the plan runs only
+                            through qlinear_forward, which then writes a_q (packed) and
+                            a_scale from inside the GEMM launch -- per-token formats,
+                            M <= 16, M*K <= 16384, K % 512 == 0.  2..4 need packed weights */
   int32_t w_lds;         /* DECODE, row-major weights: 1 = coalesced weight loads (8 rows x 128 B
                             per instruction) transposed to the matrix-core layout through LDS;
                             0 = direct loads in operand order.  TILED, packed weights and
@@ -173,6 +178,16 @@ ql_status qlinear_quantize_act_packed(int32_t fmt, const void* x_bf16, int64_t M
                                       void* a_packed, float* a_scale, void* stream);
 
 /*
+ * The E4M3 encoder every FP8 quantizer of the library applies to its
+ * quotients, on its own: codes[i] = OCP E4M3 code of x[i] clamped to
+ * [-448, 448], rounded to nearest even (signed zeros kept, subnormal codes
+ * produced).  x: n binary32 values, codes: n bytes, both device memory,
+ * 16-byte aligned; n <= 2^30.  NaN inputs are outside the contract.  Used to
+ * check the encoder against the format definition.  Enqueue-only.
+ */
+ql_status qlinear_encode_e4m3(const float* x, int64_t n, void* codes, void* stream);
+
+/*
  * Offline weight quantizer: per output channel (rows of W) or per 128x128
  * block for Block_FP8 (the last block row may be ragged).
  *   w_bf16 [N, K] in;  w_q [N, K] out;  w_scale fp32 [N] or [ceil(N/128), K/128] out.
@@ -199,9 +214,12 @@ ql_status qlinear_pack_weight(const void* w_q, int64_t N, int64_t K, void* w_pac
  * Offline sweep table ([Summary] "Hybrid dispatch addresses runtime
  * overhead": per-shape, per-token-count tuned configurations).  Text file,
  * one entry per line: fmt M N K algo swap_ab split_k waves_n waves_k
- * rows_per_wave prefetch a_mode w_lds w_layout tile_m tile_n [time_us]; '#'
- * starts a comment.  Entries are looked up for the operand layouts asked for
- * (w_layout, and packed activations = a_mode 2).
+ * rows_per_wave prefetch a_mode w_lds w_layout tile_m tile_n [time_us [fwd]];
+ * '#' starts a comment.  Entries are looked up for the operand layouts asked
+ * for (w_layout; row-major A_q = a_mode 0/1, packed A_q = a_mode 2/3).  An
+ * entry marked "fwd" (and every a_mode 4 entry) is a forward plan: the best
+ * configuration for quantize + GEMM together, fused or not, and its time
+ * covers both.
  * Loading replaces the in-process table.  Returns the entry count via n_entries.
  */
 ql_status qlinear_table_load(const char* path, int64_t* n_entries);
@@ -225,7 +243,9 @@ ql_status qlinear_plan_packed(int32_t fmt, int64_t M, int64_t N, int64_t K, ql_p
 /*
  * Like qlinear_plan for any operand layouts: w_layout 0 = row-major W_q,
  * 1 = packed weights; a_packed 0 = row-major A_q (qlinear_quantize_act),
- * 1 = packed A_q (qlinear_quantize_act_packed; the plan's a_mode is 2 or 3).
+ * 1 = packed A_q (qlinear_quantize_act_packed; the plan's a_mode is 2 or 3),
+ * 2 = a forward plan for packed weights (the table's "fwd" entry, else the
+ * packed-A_q plan): a_mode 2, 3 or 4, to be run with qlinear_forward only.
  */
 ql_status qlinear_plan_layouts(int32_t fmt, int64_t M, int64_t N, int64_t K, int32_t w_layout,
                                int32_t a_packed, ql_plan* out_plan);
@@ -275,7 +295,10 @@ ql_status qlinear_run_debug_acc(ql_plan plan, const void* a_q, const float* a_sc
  * Quantize the activations, then run the GEMM: the whole decode step of one
  * linear layer.  a_q / a_scale are caller-owned staging buffers; a_q is
  * written in the plan's activation layout (qlinear_packed_act_bytes(M, K)
- * bytes when a_mode is 2 or 3, else M*K).
+ * bytes when a_mode is 2, 3 or 4, else M*K).  With a_mode 4 this is one
+ * launch: the GEMM kernel quantizes X itself and also writes a_q / a_scale
+ * (identical to what qlinear_quantize_act_packed writes).  qlinear_run
+ * rejects an a_mode 4 plan with QL_E_INVALID.
  */
 ql_status qlinear_forward(ql_plan plan, const void* x_bf16, void* a_q, float* a_scale,
                           const void* w_q, const float* w_scale, void* y_bf16,

@@ -131,7 +131,7 @@ def quantize_act_packed(fmt, x, stream=None):
 
 
 def act_buffer(plan, device="cuda"):
-    """Activation code buffer in the plan's layout (packed when its a_mode is 2 or 3)."""
+    """Activation code buffer in the plan's layout (packed when its a_mode is 2, 3 or 4)."""
     n = qlinear_packed_act_bytes(plan.M, plan.K) if plan.config["a_mode"] >= 2 else plan.M * plan.K
     return torch.empty(max(n, 16), dtype=code_dtype(plan.fmt), device=device)
 
@@ -146,6 +146,12 @@ def quantize_weight(fmt, w, stream=None):
 
 
 # ----------------------------------------------------------------- packing
+
+def qlinear_encode_e4m3(x, codes, stream=None):
+    """The library's E4M3 encoder: codes = E4M3(clamp(x, -448, 448)), round to nearest even."""
+    _check(lib().qlinear_encode_e4m3(_ptr(x, "x", torch.float32), x.numel(), _ptr(codes, "codes", CODE_DTYPES),
+                                     _stream(stream)), "qlinear_encode_e4m3")
+
 
 def qlinear_packed_weight_bytes(N, K):
     return int(lib().qlinear_packed_weight_bytes(N, K))
@@ -236,7 +242,9 @@ def qlinear_plan_packed(fmt, M, N, K):
 
 def qlinear_plan_layouts(fmt, M, N, K, w_layout, a_packed):
     """Plan for the given operand layouts (w_layout: 0 row-major, 1 packed weights;
-    a_packed: 0 row-major A_q, 1 packed A_q from qlinear_quantize_act_packed)."""
+    a_packed: 0 row-major A_q, 1 packed A_q from qlinear_quantize_act_packed,
+    2 a forward plan -- possibly with the quantizer fused into the GEMM --
+    that runs only through qlinear_forward)."""
     h = ctypes.c_void_p()
     _check(lib().qlinear_plan_layouts(fmt, M, N, K, w_layout, a_packed, ctypes.byref(h)), "qlinear_plan_layouts")
     return Plan(h.value, fmt, M, N, K)

@@ -29,6 +29,7 @@ SIGNATURES = {
     "qlinear_packed_act_bytes": (c_i64, [c_i64, c_i64]),
     "qlinear_quantize_act_packed": (c_i32, [c_i32, c_vp, c_i64, c_i64, c_vp, c_vp, c_vp]),
     "qlinear_packed_weight_bytes": (c_i64, [c_i64, c_i64]),
+    "qlinear_encode_e4m3": (c_i32, [c_vp, c_i64, c_vp, c_vp]),
     "qlinear_pack_weight": (c_i32, [c_vp, c_i64, c_i64, c_vp, c_vp]),
     "qlinear_table_load": (c_i32, [c_cp, ctypes.POINTER(c_i64)]),
     "qlinear_table_clear": (None, []),

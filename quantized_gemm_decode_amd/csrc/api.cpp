@@ -47,6 +47,8 @@ ql_status hip_fail(hipError_t e, const char* what) {
 // gfx950: LDS per workgroup (above 64 KB with the per-kernel opt-in), less
 // room for the kernels' own static LDS variables
 constexpr int64_t kLdsLimit = 160 * 1024 - 256;
+// Fused quantization holds the workgroup's share of X in registers: 16384 bf16 values.
+constexpr int64_t kFusedMaxValues = 16384;
 constexpr int kBuckets[] = {1, 2, 4, 8, 16, 24, 32};
 
 bool valid_fmt(int32_t f) { return f == QL_FP8_DYNAMIC || f == QL_W8A8_INT8 || f == QL_BLOCK_FP8; }
@@ -70,6 +72,7 @@ struct TableEntry {
   int64_t M, N, K;
   ql_config cfg;
   double us;
+  int us_class;  // 2: a forward-only entry (its time covers quantize + GEMM), else act_class(a_mode)
 };
 
 std::mutex g_table_mu;
@@ -81,13 +84,19 @@ int64_t bucket_of(int64_t M) {
   return M;
 }
 
-bool table_lookup(int32_t fmt, int32_t layout, bool a_packed, int64_t M, int64_t N, int64_t K, ql_config* out) {
+// Activation class of a configuration: 0 row-major A_q (a_mode 0, 1), 1 packed
+// A_q (2, 3), 2 forward-only plans (fused quantization, 4).  A class-2 table
+// entry is the best plan for quantize + GEMM, fused or not.
+int act_class(int32_t a_mode) { return a_mode == 4 ? 2 : (a_mode >= 2 ? 1 : 0); }
+
+bool table_lookup(int32_t fmt, int32_t layout, int a_class, int64_t M, int64_t N, int64_t K, ql_config* out) {
   std::lock_guard<std::mutex> lk(g_table_mu);
   const int64_t want = bucket_of(M);
   const TableEntry* best = nullptr;
   const TableEntry* largest = nullptr;
   for (const TableEntry& e : g_table) {
-    if (e.fmt != fmt || e.N != N || e.K != K || e.cfg.w_layout != layout || (e.cfg.a_mode >= 2) != a_packed) continue;
+    if (e.fmt != fmt || e.N != N || e.K != K || e.cfg.w_layout != layout) continue;
+    if (a_class == 2 ? e.us_class != 2 : (e.us_class == 2 || act_class(e.cfg.a_mode) != a_class)) continue;
     if (e.M >= want && (!best || e.M < best->M)) best = &e;
     if (!largest || e.M > largest->M) largest = &e;
   }
@@ -250,8 +259,14 @@ ql_status build_plan(int32_t fmt, int64_t M, int64_t N, int64_t K, const ql_conf
   if (cfg.rows_per_wave != 16 && cfg.rows_per_wave != 32 && cfg.rows_per_wave != 64)
     return fail(QL_E_INVALID, "rows_per_wave must be 16, 32 or 64");
   if (cfg.prefetch != 1 && cfg.prefetch != 2 && cfg.prefetch != 4) return fail(QL_E_INVALID, "prefetch must be 1, 2 or 4");
-  if (cfg.a_mode < 0 || cfg.a_mode > 3) return fail(QL_E_INVALID, "a_mode must be 0, 1, 2 or 3");
+  if (cfg.a_mode < 0 || cfg.a_mode > 4) return fail(QL_E_INVALID, "a_mode must be 0, 1, 2, 3 or 4");
   if (cfg.a_mode >= 2 && !cfg.w_layout) return fail(QL_E_UNSUPPORTED, "packed activations need packed weights");
+  if (cfg.a_mode == 4) {
+    if (fmt == QL_BLOCK_FP8) return fail(QL_E_UNSUPPORTED, "fused quantization serves the per-token formats");
+    if (M > 16 || M * K > kFusedMaxValues || K % 512)
+      return fail(QL_E_UNSUPPORTED, "fused quantization needs M <= 16, M*K <= %lld and K %% 512 == 0",
+                  (long long)kFusedMaxValues);
+  }
   if (cfg.a_mode >= 2 && qlinear_packed_act_bytes(M, K) > (int64_t(1) << 30))
     return fail(QL_E_UNSUPPORTED, "packed activations exceed 2^30 bytes");
   if (cfg.w_lds != 0 && cfg.w_lds != 1) return fail(QL_E_INVALID, "w_lds must be 0 or 1");
@@ -273,7 +288,9 @@ ql_status build_plan(int32_t fmt, int64_t M, int64_t N, int64_t K, const ql_conf
   const int rg = cfg.rows_per_wave / 16;
   p->bn = cfg.waves_n * rg * 16;
   p->n_tiles = (int)((N + p->bn - 1) / p->bn);
-  const int64_t lds_a = (cfg.a_mode == 1 || cfg.a_mode == 3) ? (int64_t)p->chunk_kb * p->mt * 2048 : 0;
+  const int64_t lds_a = (cfg.a_mode == 1 || cfg.a_mode == 3) ? (int64_t)p->chunk_kb * p->mt * 2048
+                       : cfg.a_mode == 4                    ? 512 + M * ((int64_t)p->chunk_kb * 128 + 64)
+                                                            : 0;
   const int64_t lds_w = (cfg.w_lds && !cfg.w_layout) ? (int64_t)nw * 2 * rg * 2048 : 0;
   const int64_t lds_red = cfg.waves_k > 1 ? (int64_t)nw * rg * p->mt * 1024 : 0;
   p->lds = std::max(lds_a + lds_w, lds_red);
@@ -314,8 +331,14 @@ bool parse_force(ql_config* c) {
   return true;
 }
 
+// x / aq_out / sa_out: the fused plans' input X and their quantizer outputs
+// (a_q and a_scale are then unused).
 ql_status launch_gemm(const ql_plan_s* p, const void* a_q, const float* a_scale, const void* w_q,
-                      const float* w_scale, void* y, void* workspace, void* acc_out, hipStream_t s) {
+                      const float* w_scale, void* y, void* workspace, void* acc_out, hipStream_t s,
+                      bool from_forward = false, const void* x = nullptr, void* aq_out = nullptr,
+                      float* sa_out = nullptr) {
+  const bool fused = !p->tiled && p->cfg.a_mode == 4;
+  if (fused && !from_forward) return fail(QL_E_INVALID, "a fused-quantization plan runs through qlinear_forward");
   if (p->M == 0 || p->N == 0) return QL_OK;
   if (!y) return fail(QL_E_INVALID, "y is NULL");
   if (!aligned16(y)) return fail(QL_E_ALIGN, "y is not 16-byte aligned");
@@ -323,9 +346,15 @@ ql_status launch_gemm(const ql_plan_s* p, const void* a_q, const float* a_scale,
     hipError_t e = qlk::launch_fill_zero_bf16(y, p->M * p->N, s);
     return e == hipSuccess ? QL_OK : hip_fail(e, "zero fill");
   }
-  if (!a_q || !a_scale || !w_q || !w_scale) return fail(QL_E_INVALID, "NULL operand pointer");
-  if (!aligned16(a_q) || !aligned16(w_q) || !aligned16(a_scale) || !aligned16(w_scale))
-    return fail(QL_E_ALIGN, "operand pointers must be 16-byte aligned");
+  if (fused) {
+    if (!x || !aq_out || !sa_out || !w_q || !w_scale) return fail(QL_E_INVALID, "NULL operand pointer");
+    if (!aligned16(x) || !aligned16(aq_out) || !aligned16(sa_out) || !aligned16(w_q) || !aligned16(w_scale))
+      return fail(QL_E_ALIGN, "operand pointers must be 16-byte aligned");
+  } else {
+    if (!a_q || !a_scale || !w_q || !w_scale) return fail(QL_E_INVALID, "NULL operand pointer");
+    if (!aligned16(a_q) || !aligned16(w_q) || !aligned16(a_scale) || !aligned16(w_scale))
+      return fail(QL_E_ALIGN, "operand pointers must be 16-byte aligned");
+  }
   if (p->ws_bytes > 0 && !workspace) return fail(QL_E_INVALID, "split-K plan needs a workspace");
   if (workspace && !aligned16(workspace)) return fail(QL_E_ALIGN, "workspace is not 16-byte aligned");
   if (acc_out && !aligned16(acc_out)) return fail(QL_E_ALIGN, "acc_out is not 16-byte aligned");
@@ -341,6 +370,9 @@ ql_status launch_gemm(const ql_plan_s* p, const void* a_q, const float* a_scale,
                    ? reinterpret_cast<unsigned*>(static_cast<char*>(workspace) + p->ws_acc_bytes)
                    : nullptr;
   a.acc_out = acc_out;
+  a.x = static_cast<const uint16_t*>(x);
+  a.aq_out = static_cast<uint8_t*>(aq_out);
+  a.sa_out = sa_out;
   a.M = (int)p->M;
   a.N = (int)p->N;
   a.K = (int)p->K;
@@ -453,6 +485,12 @@ ql_status qlinear_table_load(const char* path, int64_t* n_entries) {
           e.cfg.tile_n))
       return fail(QL_E_TABLE, "%s:%d: malformed entry", path, lineno);
     if (!(is >> e.us)) e.us = 0;
+    std::string kind;
+    e.us_class = act_class(e.cfg.a_mode);
+    if (is >> kind) {
+      if (kind != "fwd") return fail(QL_E_TABLE, "%s:%d: unknown entry kind '%s'", path, lineno, kind.c_str());
+      e.us_class = 2;
+    }
     if (!valid_fmt(e.fmt) || M < 1 || N < 1 || K < 1) return fail(QL_E_TABLE, "%s:%d: bad key", path, lineno);
     e.M = M;
     e.N = N;
@@ -472,32 +510,45 @@ void qlinear_table_clear(void) {
   g_table.clear();
 }
 
-static ql_status plan_for_layout(int32_t fmt, int32_t layout, bool a_packed, int64_t M, int64_t N, int64_t K,
+static ql_status plan_for_layout(int32_t fmt, int32_t layout, int a_class, int64_t M, int64_t N, int64_t K,
                                  ql_plan* out_plan) {
   if (layout != 0 && layout != 1) return fail(QL_E_INVALID, "w_layout must be 0 or 1");
   ql_config c;
   if (parse_force(&c)) {
-    if (c.w_layout != layout || (c.a_mode >= 2) != a_packed)
+    const int fc = act_class(c.a_mode);
+    if (c.w_layout != layout || (a_class == 2 ? fc == 0 : fc != a_class))
       return fail(QL_E_INVALID, "QLINEAR_FORCE names other operand layouts");
     return build_plan(fmt, M, N, K, c, QL_SRC_CUSTOM, out_plan);
   }
-  if (table_lookup(fmt, layout, a_packed, M, N, K, &c)) return build_plan(fmt, M, N, K, c, QL_SRC_TABLE, out_plan);
-  return build_plan(fmt, M, N, K, heuristic_config(fmt, layout, a_packed, M, N, K), QL_SRC_HEURISTIC, out_plan);
+  if (table_lookup(fmt, layout, a_class, M, N, K, &c)) return build_plan(fmt, M, N, K, c, QL_SRC_TABLE, out_plan);
+  // a forward plan without its own entry: the packed-activation plan
+  if (a_class == 2 && table_lookup(fmt, layout, 1, M, N, K, &c))
+    return build_plan(fmt, M, N, K, c, QL_SRC_TABLE, out_plan);
+  return build_plan(fmt, M, N, K, heuristic_config(fmt, layout, a_class != 0, M, N, K), QL_SRC_HEURISTIC, out_plan);
 }
 
 ql_status qlinear_plan(int32_t fmt, int64_t M, int64_t N, int64_t K, ql_plan* out_plan) {
-  return plan_for_layout(fmt, 0, false, M, N, K, out_plan);
+  return plan_for_layout(fmt, 0, 0, M, N, K, out_plan);
 }
 
 ql_status qlinear_plan_packed(int32_t fmt, int64_t M, int64_t N, int64_t K, ql_plan* out_plan) {
-  return plan_for_layout(fmt, 1, false, M, N, K, out_plan);
+  return plan_for_layout(fmt, 1, 0, M, N, K, out_plan);
 }
 
 ql_status qlinear_plan_layouts(int32_t fmt, int64_t M, int64_t N, int64_t K, int32_t w_layout, int32_t a_packed,
                                ql_plan* out_plan) {
-  if (a_packed != 0 && a_packed != 1) return fail(QL_E_INVALID, "a_packed must be 0 or 1");
+  if (a_packed < 0 || a_packed > 2) return fail(QL_E_INVALID, "a_packed must be 0, 1 or 2");
   if (a_packed && !w_layout) return fail(QL_E_UNSUPPORTED, "packed activations need packed weights");
-  return plan_for_layout(fmt, w_layout, a_packed != 0, M, N, K, out_plan);
+  return plan_for_layout(fmt, w_layout, a_packed, M, N, K, out_plan);
+}
+
+ql_status qlinear_encode_e4m3(const float* x, int64_t n, void* codes, void* stream) {
+  if (n < 0 || n > (int64_t(1) << 30)) return fail(QL_E_INVALID, "n=%lld outside [0, 2^30]", (long long)n);
+  if (n == 0) return QL_OK;
+  if (!x || !codes) return fail(QL_E_INVALID, "NULL pointer");
+  if (!aligned16(x) || !aligned16(codes)) return fail(QL_E_ALIGN, "pointers must be 16-byte aligned");
+  hipError_t e = qlk::launch_encode_e4m3(x, n, codes, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? QL_OK : hip_fail(e, "E4M3 encoder launch");
 }
 
 int64_t qlinear_packed_weight_bytes(int64_t N, int64_t K) {
@@ -518,7 +569,7 @@ ql_status qlinear_pack_weight(const void* w_q, int64_t N, int64_t K, void* w_pac
 ql_status qlinear_plan_from_table(int32_t fmt, int64_t M, int64_t N, int64_t K, ql_plan* out_plan) {
   if (out_plan) *out_plan = nullptr;
   ql_config c;
-  if (!table_lookup(fmt, 0, false, M, N, K, &c))
+  if (!table_lookup(fmt, 0, 0, M, N, K, &c))
     return fail(QL_E_NO_TABLE_ENTRY, "no table entry for fmt=%d M=%lld N=%lld K=%lld", fmt, (long long)M,
                 (long long)N, (long long)K);
   return build_plan(fmt, M, N, K, c, QL_SRC_TABLE, out_plan);
@@ -568,6 +619,9 @@ ql_status qlinear_run_debug_acc(ql_plan p, const void* a_q, const float* a_scale
 ql_status qlinear_forward(ql_plan p, const void* x_bf16, void* a_q, float* a_scale, const void* w_q,
                           const float* w_scale, void* y, void* workspace, void* stream) {
   if (!p) return fail(QL_E_INVALID, "plan is NULL");
+  if (!p->tiled && p->cfg.a_mode == 4)
+    return launch_gemm(p, nullptr, nullptr, w_q, w_scale, y, workspace, nullptr, static_cast<hipStream_t>(stream),
+                       true, x_bf16, a_q, a_scale);
   ql_status st = quantize_act(p->fmt, x_bf16, p->M, p->K, a_q, a_scale, p->cfg.a_mode >= 2, stream);
   if (st != QL_OK) return st;
   return launch_gemm(p, a_q, a_scale, w_q, w_scale, y, workspace, nullptr, static_cast<hipStream_t>(stream));

@@ -26,6 +26,11 @@ struct DecodeArgs {
   void* ws;            // split-K partial sums [M, N] (int32 or fp32), all-zero between runs
   unsigned* counters;  // split-K arrival counters [n_tiles], all-zero between runs
   void* acc_out;       // optional raw accumulators [M, N] (test hook), may be null
+  // fused quantization (decode activation mode 4): the kernel reads X and
+  // writes the codes (packed layout) and scales it computed, if non-null
+  const uint16_t* x;   // X [M, K] bf16
+  uint8_t* aq_out;     // packed A_q, ceil(M/16) x G tiles of 2 KB
+  float* sa_out;       // s_a [M]
   int M, N, K;
   int G;               // number of 128-wide K blocks, ceil(K / 128)
   int split;           // number of K chunks (workgroups per output tile)
@@ -43,7 +48,8 @@ struct DecodeKey {
   int rg;    // 16-row groups per wave (1, 2 or 4)
   int nw;    // waves per workgroup (4, 8 or 16)
   int pf;    // K blocks per prefetch batch
-  int alds;  // activations: 0 row-major from L2, 1 row-major staged in LDS, 2 packed from L2
+  int alds;  // activations: 0 row-major from L2, 1 row-major staged in LDS, 2 packed from L2,
+             // 3 packed staged in LDS, 4 quantized from X inside the kernel (fused)
   int wm;    // weight mode: W_DIRECT / W_LDS_TRANSPOSE / W_PACKED
 };
 
@@ -87,6 +93,8 @@ hipError_t launch_quant_groups(const void* x, int64_t M, int64_t K, void* q, flo
 hipError_t launch_quant_wblocks(const void* w, int64_t N, int64_t K, void* q, float* s,
                                 hipStream_t st);
 hipError_t launch_fill_zero_bf16(void* y, int64_t count, hipStream_t st);
+// codes[i] = E4M3 code of x[i] clamped to [-448, 448], round to nearest even.
+hipError_t launch_encode_e4m3(const float* x, int64_t n, void* q, hipStream_t st);
 // Row-major W_q[N,K] -> packed 2 KB tiles (zero padding to 16 rows / 128 K).
 hipError_t launch_pack_weight(const void* w_q, int64_t N, int64_t K, void* w_packed, hipStream_t st);
 

@@ -23,6 +23,13 @@
 // every ds_read_b128 is a contiguous 1 KB wave read, or fetched per K block
 // from L2 next to the weights.
 //
+// Fused quantization (activation mode 4, small M): the workgroup reads the
+// bf16 rows of X itself, reduces each row's amax, and writes the codes of its
+// own K range into LDS -- the dynamic quantizer's arithmetic, bit for bit --
+// while its first weight batches are already in flight, so a linear is one
+// launch instead of two.  Its first workgroup per chunk range also writes the
+// codes (packed layout) and scales out, as the standalone quantizer would.
+//
 // Sources: [Summary] = English summary of "Building a High-Performance and
 // Portable vLLM Linear Backend with Helion" (yuxiaoba.github.io);
 // [Noticias] = "Helion entra al backend lineal de vLLM y supera a CUTLASS en
@@ -31,6 +38,7 @@
 
 #include "decode_args.hpp"
 #include "device_common.hpp"
+#include "quant_common.hpp"
 
 namespace qlk {
 
@@ -58,10 +66,12 @@ __device__ __forceinline__ uint32_t epilogue_scaled(float accf, float sa, float 
 
 template <int FMT, bool SWAP, int MT, int RG, int NW, int PF, int AL, int WM>
 __global__ void __launch_bounds__(NW * 64) qgemm_decode_kernel(DecodeArgs p) {
-  constexpr bool ALDS = AL == 1 || AL == 3;  // activations staged in LDS (row-major 1, packed 3)
-  constexpr bool AP = AL == 2;               // packed activations, read per K block like packed weights
+  constexpr bool FUSED = AL == 4;                     // activations quantized here from bf16 X
+  constexpr bool ALDS = AL == 1 || AL == 3 || FUSED;  // activations read from LDS
+  constexpr bool AP = AL == 2;                        // packed activations, read per K block like packed weights
   constexpr bool WL = WM == W_LDS_TRANSPOSE;
   constexpr bool WP = WM == W_PACKED;
+  static_assert(!FUSED || (MT == 1 && WP && FMT != FMT_BLOCK), "fused quantization: per-token formats, M <= 16");
   using Acc = typename AccOf<FMT>::T;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   __shared__ int s_last;
@@ -137,6 +147,18 @@ __global__ void __launch_bounds__(NW * 64) qgemm_decode_kernel(DecodeArgs p) {
     else
       abase[mt] = m < M ? m * K + glo : OOB;
   }
+
+  // Fused LDS image: the wave amax partials (64 floats) at FA_RED, s_a of the
+  // 16 tokens at FA_SC, a 16-byte zero slot at FA_ZERO, then
+  // the codes of token m at FA0 + m*CH for this chunk's K range.  CH adds 64
+  // bytes to the chunk so consecutive tokens start 16 banks apart.  Lanes of
+  // tokens >= M read the zero slot for every K block.
+  constexpr int FA_RED = 0, FA_SC = 256, FA_ZERO = 384, FA0 = 512;
+  const int CH = p.chunk_kb * 128 + 64;
+  const bool real_tok = (uint32_t)r16 < M;
+  const int fa_lane = real_tok ? FA0 + r16 * CH + g * 16 : FA_ZERO;
+  const int fa_step = real_tok ? 128 : 0;
+  const int fa_hi = real_tok ? 64 : 0;
 
   // ---- this wave's K blocks: kb0 + wk + j*WK, j < nkw
   const int nkw = nkc > wk ? (nkc - wk + WK - 1) / WK : 0;
@@ -233,7 +255,13 @@ __global__ void __launch_bounds__(NW * 64) qgemm_decode_kernel(DecodeArgs p) {
 #pragma unroll
     for (int q = 0; q < PF; ++q) {
       Frag af[MT];
-      if constexpr (ALDS) {
+      if constexpr (FUSED) {
+        const int j = batch * PF + q;
+        const int kbl = j < nkw ? wk + j * WK : 0;
+        const uint8_t* base = smem + fa_lane + kbl * fa_step;
+        af[0].lo = *reinterpret_cast<const u32x4*>(base);
+        af[0].hi = *reinterpret_cast<const u32x4*>(base + fa_hi);
+      } else if constexpr (ALDS) {
         const int j = batch * PF + q;
         const int kbl = j < nkw ? wk + j * WK : 0;
 #pragma unroll
@@ -302,7 +330,7 @@ __global__ void __launch_bounds__(NW * 64) qgemm_decode_kernel(DecodeArgs p) {
   // 16*mt + l%16, K bytes [h*64 + 16*(l/16), +16) of the K block.  Packed
   // activations hold exactly these blocks contiguously; row-major ones are
   // gathered 16 rows x 16 bytes at a time.
-  if constexpr (ALDS) {
+  if constexpr (ALDS && !FUSED) {
     const int nblk = nkc * MT * 2;
     for (int b = wave; b < nblk; b += NW) {
       const int h = b & 1;
@@ -325,11 +353,83 @@ __global__ void __launch_bounds__(NW * 64) qgemm_decode_kernel(DecodeArgs p) {
     __builtin_amdgcn_sched_barrier(0);
   }
 
+  // ---- fused quantization, part 1: X is read first, so that waiting for it
+  // below leaves the weight batches issued after it in flight.  With K a
+  // multiple of 512 each wave's 64 consecutive 16-byte pieces (one load
+  // instruction) lie in one token row; the workgroup holds XP pieces a lane,
+  // 16384 values in all.
+  constexpr int XP = FUSED ? 32 / NW : 1;
+  u32x4 xv[XP];
+  const uint32_t upr = K / 512u;  // wave pieces per token row
+  if constexpr (FUSED) {
+    const __amdgpu_buffer_rsrc_t rx = make_rsrc(p.x, M * K * 2u);
+    const uint32_t npc = M * K / 8u;
+#pragma unroll
+    for (int i = 0; i < XP; ++i) {
+      const uint32_t P = (uint32_t)(tid + NW * 64 * i);
+      xv[i] = bload16(rx, P < npc ? P * 16u : OOB);
+    }
+    if (tid < 4) reinterpret_cast<uint32_t*>(smem + FA_ZERO)[tid] = 0u;
+    __builtin_amdgcn_sched_barrier(0);
+  }
+
   // Two batches in flight: the loop enters and repeats with the same pair of
   // buffers outstanding (batch b in wb0, b+1 in wb1), and each buffer is
   // refilled right after it has been consumed.
   issue(wb0, ab0, sa0, sw0, 0);
   issue(wb1, ab1, sa1, sw1, 1);
+
+  // ---- fused quantization, part 2: wait for X only, then per token row:
+  // amax (each wave's partial, then the row's partials), s = fl(amax/Q) and
+  // fl(1/s) in every wave that holds a piece of the row, and the codes of
+  // this chunk's K range into LDS.
+  if constexpr (FUSED) {
+    constexpr int NW_LOADS = 2 * PF * 2 * RG;  // weight loads of the two batches, issued after X
+    static_assert(NW_LOADS <= 63, "vmcnt holds 6 bits");
+    __builtin_amdgcn_s_waitcnt((NW_LOADS & 15) | (7 << 4) | (15 << 8) | ((NW_LOADS >> 4) << 14));
+    float* red = reinterpret_cast<float*>(smem + FA_RED);
+    float* ssc = reinterpret_cast<float*>(smem + FA_SC);
+    const uint32_t nu = M * upr;
+#pragma unroll
+    for (int i = 0; i < XP; ++i) {
+      const uint32_t u = (uint32_t)(wave + NW * i);
+      const float m = wave_max_nonneg(abs_bf16_max8(xv[i], 0.0f));
+      if (lane == 0 && u < nu) red[u] = m;
+    }
+    lds_barrier();
+    const uint32_t k_lo = (uint32_t)kb0 * 128u, k_hi = (uint32_t)kb1 * 128u;
+#pragma unroll
+    for (int i = 0; i < XP; ++i) {
+      const uint32_t u = (uint32_t)(wave + NW * i);
+      if (u < nu) {
+        const uint32_t m = u / upr;
+        float amax = 0.0f;
+        for (uint32_t v = m * upr; v < (m + 1u) * upr; ++v) amax = fmaxf(amax, red[v]);
+        const float sc = scale_of<FMT>(amax);
+        if (lane == 0 && u == m * upr) ssc[m] = sc;
+        const uint32_t k = (u - m * upr) * 512u + (uint32_t)lane * 8u;
+        if (k >= k_lo && k < k_hi)
+          *reinterpret_cast<u32x2*>(smem + FA0 + m * (uint32_t)CH + (k - k_lo)) =
+              quant8<FMT>(xv[i], sc, recip_of(sc));
+      }
+    }
+    lds_barrier();
+    // The codes and scales leave the kernel as the standalone quantizer
+    // writes them: this chunk's packed tiles (token tile 0; rows >= M zero)
+    // spread over the chunk's workgroups, and s_a from the first workgroup.
+    if (p.aq_out) {
+      const uint32_t nunits = (uint32_t)nkc * 128u;  // 16-byte units: K block x half x lane
+      for (uint32_t u = (uint32_t)(tile * NW * 64 + tid); u < nunits; u += (uint32_t)(p.n_tiles * NW * 64)) {
+        const uint32_t kbl = u >> 7, h = (u >> 6) & 1u, l = u & 63u;
+        const uint32_t row = l & 15u;
+        const uint32_t k = kbl * 128u + h * 64u + (l >> 4) * 16u;
+        u32x4 v = {0u, 0u, 0u, 0u};
+        if (row < M) v = *reinterpret_cast<const u32x4*>(smem + FA0 + row * (uint32_t)CH + k);
+        *reinterpret_cast<u32x4*>(p.aq_out + (size_t)((uint32_t)kb0 + kbl) * 2048u + h * 1024u + l * 16u) = v;
+      }
+      if (tile == 0 && chunk == 0 && (uint32_t)tid < M) p.sa_out[tid] = ssc[tid];
+    }
+  }
 
   // Scales of the per-token formats, loaded now so that their latency hides
   // under the weight stream instead of stalling the epilogue.
@@ -340,7 +440,10 @@ __global__ void __launch_bounds__(NW * 64) qgemm_decode_kernel(DecodeArgs p) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const uint32_t m = SWAP ? (uint32_t)(mt * 16 + r16) : (uint32_t)(mt * 16 + 4 * g + r);
-        esa[mt][r] = (SWAP && r > 0) ? 0.f : bload_f32(rsa, m < M ? m * 4u : OOB);
+        if constexpr (FUSED)
+          esa[mt][r] = m < M ? reinterpret_cast<const float*>(smem + FA_SC)[m] : 0.f;
+        else
+          esa[mt][r] = (SWAP && r > 0) ? 0.f : bload_f32(rsa, m < M ? m * 4u : OOB);
       }
 #pragma unroll
     for (int rg = 0; rg < RG; ++rg)
@@ -354,7 +457,7 @@ __global__ void __launch_bounds__(NW * 64) qgemm_decode_kernel(DecodeArgs p) {
   // ---- activations staged in LDS: wait for the staging copies (issued
   // before the weight batches, and vmcnt counts in issue order) while the
   // weight batches stay in flight, then make LDS visible workgroup-wide.
-  if constexpr (ALDS) {
+  if constexpr (ALDS && !FUSED) {
     constexpr int NW_LOADS = 2 * PF * 2 * RG;  // weight loads of the two batches: all issued after the copies
     static_assert(NW_LOADS <= 63, "vmcnt holds 6 bits");
     __builtin_amdgcn_s_waitcnt((NW_LOADS & 15) | (7 << 4) | (15 << 8) | ((NW_LOADS >> 4) << 14));
@@ -538,10 +641,22 @@ constexpr bool decode_config_fits() {
   return true;
 }
 
+// Fused quantization adds 32/NW 16-byte X pieces a lane to the buffers in
+// flight; it serves one token tile, packed weights and the per-token formats.
+template <int FMT, int NW_, int SW, int MT_, int RG_, int PF_, int AL, int WM_>
+constexpr bool decode_variant_ok() {
+  if constexpr (AL == 4) {
+    if (MT_ != 1 || WM_ != W_PACKED || FMT == FMT_BLOCK) return false;
+    const int estimate = 2 * PF_ * (RG_ + MT_) * 8 + RG_ * MT_ * 4 + 40 + 4 * (32 / NW_);
+    return estimate <= (NW_ >= 16 ? 128 : 256) && decode_config_fits<FMT, NW_, SW, MT_, RG_, PF_>();
+  }
+  return decode_config_fits<FMT, NW_, SW, MT_, RG_, PF_>();
+}
+
 template <int FMT, int NW_, int SW, int MT_, int RG_, int PF_, int AL, int WM_>
 hipError_t decode_try(const DecodeKey& k, dim3 grid, dim3 block, size_t lds, hipStream_t s, const DecodeArgs& a,
                       bool probe_only, bool* hit) {
-  if constexpr (decode_config_fits<FMT, NW_, SW, MT_, RG_, PF_>()) {
+  if constexpr (decode_variant_ok<FMT, NW_, SW, MT_, RG_, PF_, AL, WM_>()) {
     if (k.swap == SW && k.mt == MT_ && k.rg == RG_ && k.nw == NW_ && k.pf == PF_ && k.alds == AL && k.wm == WM_) {
       *hit = true;
       auto fn = qgemm_decode_kernel<FMT, SW != 0, MT_, RG_, NW_, PF_, AL, WM_>;
@@ -572,13 +687,14 @@ hipError_t decode_dispatch(const DecodeKey& k, dim3 grid, dim3 block, size_t lds
   QL_TRY(4, SW, MT_, RG_, PF_, AL, 0) QL_TRY(4, SW, MT_, RG_, PF_, AL, 1) QL_TRY(4, SW, MT_, RG_, PF_, AL, 2)
 #define QL_TRY_AL(SW, MT_, RG_, PF_)                                                      \
   QL_TRY_WL(SW, MT_, RG_, PF_, 0) QL_TRY_WL(SW, MT_, RG_, PF_, 1) QL_TRY(4, SW, MT_, RG_, PF_, 2, 2) \
-  QL_TRY(4, SW, MT_, RG_, PF_, 3, 2)
+  QL_TRY(4, SW, MT_, RG_, PF_, 3, 2) QL_TRY(4, SW, MT_, RG_, PF_, 4, 2)
 #define QL_TRY_PF(SW, MT_, RG_) QL_TRY_AL(SW, MT_, RG_, 2) QL_TRY_AL(SW, MT_, RG_, 4)
 #define QL_TRY_RG(SW, MT_) QL_TRY_PF(SW, MT_, 1) QL_TRY_PF(SW, MT_, 2)
   // packed weights, activations (row-major or packed) from L2: wider workgroups,
   // longer rows, 1-block batches
-#define QL_TRY_PA(NW_, SW, MT_, RG_, PF_) \
-  QL_TRY(NW_, SW, MT_, RG_, PF_, 0, 2) QL_TRY(NW_, SW, MT_, RG_, PF_, 2, 2) QL_TRY(NW_, SW, MT_, RG_, PF_, 3, 2)
+#define QL_TRY_PA(NW_, SW, MT_, RG_, PF_)                                                      \
+  QL_TRY(NW_, SW, MT_, RG_, PF_, 0, 2) QL_TRY(NW_, SW, MT_, RG_, PF_, 2, 2) QL_TRY(NW_, SW, MT_, RG_, PF_, 3, 2) \
+  QL_TRY(NW_, SW, MT_, RG_, PF_, 4, 2)
 #define QL_TRY_P(NW_, SW, MT_, RG_) QL_TRY_PA(NW_, SW, MT_, RG_, 1) QL_TRY_PA(NW_, SW, MT_, RG_, 2)
 #define QL_TRY_PN(SW, MT_)                                                                    \
   QL_TRY_PA(4, SW, MT_, 1, 1) QL_TRY_PA(4, SW, MT_, 2, 1) QL_TRY_P(4, SW, MT_, 4)             \

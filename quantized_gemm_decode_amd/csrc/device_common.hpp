@@ -92,6 +92,19 @@ __device__ __forceinline__ uint32_t e4m3_rne(float v) {
   return code | sign;
 }
 
+// Two E4M3 codes by the conversion instruction (v_cvt_pk_fp8_f32): a and b,
+// already clamped to [-448, 448], rounded to nearest even, into byte 0 / 1
+// (HI = false) or byte 2 / 3 (HI = true) of `old`.  It agrees with e4m3_rne
+// on every clamped input, signed zeros and subnormal results included: the
+// GPU tests compare it with the oracle's encoder around every rounding
+// midpoint and on every bf16 value.
+template <bool HI>
+__device__ __forceinline__ uint32_t e4m3_pk2(float a, float b, uint32_t old) {
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, (int)old, HI);
+}
+
+__device__ __forceinline__ float clamp448(float t) { return __builtin_amdgcn_fmed3f(t, -448.0f, 448.0f); }
+
 // Round-to-code of an already divided value t (round + clamp).
 template <int FMT>
 __device__ __forceinline__ uint32_t code_of(float t) {
@@ -105,26 +118,19 @@ __device__ __forceinline__ uint32_t code_of(float t) {
   }
 }
 
-// One quantized code of x with scale s: IEEE division, then round + clamp.
-template <int FMT>
-__device__ __forceinline__ uint32_t quant_code(float x, float s) {
-  return code_of<FMT>(__fdiv_rn(x, s));
-}
-
-// The same code from r = fl(1/s) with one multiply and two fused corrections
-// on |x|: q0 = fl(|x|*r), e = fma(-q0, s, |x|) (the remainder, exact),
-// q = fma(e, r, q0), then x's sign (so -0 keeps its sign, as in -0/s).  q
-// can still differ from fl(|x|/s) by one ulp, but for every bf16 x with
-// |x| <= amax, s = fl(amax/Q) >= 2^-96, the rounded code is the same --
-// checked exhaustively over all such (|x|, amax) pairs for Q = 127 and 448.
-// Rows with a smaller scale take the division.
+// fl(x / s) at the code level from r = fl(1/s), with one multiply and two
+// fused corrections on |x|: q0 = fl(|x|*r), e = fma(-q0, s, |x|) (the
+// remainder, exact), q = fma(e, r, q0), then x's sign (so -0 keeps its sign,
+// as in -0/s).  q can still differ from fl(|x|/s) by one ulp, but for every
+// bf16 x with |x| <= amax, s = fl(amax/Q) >= 2^-96, the rounded code is the
+// same -- checked exhaustively over all such (|x|, amax) pairs for Q = 127
+// and 448.  Rows with a smaller scale take the division.
 constexpr float FAST_DIV_MIN_SCALE = 1.2621774483536189e-29f;  // 2^-96
-template <int FMT>
-__device__ __forceinline__ uint32_t quant_code_fast(float x, float s, float r) {
+__device__ __forceinline__ float div_fast(float x, float s, float r) {
   const float ax = __builtin_fabsf(x);
   const float q0 = __fmul_rn(ax, r);
   const float e = __fmaf_rn(-q0, s, ax);
-  return code_of<FMT>(__builtin_copysignf(__fmaf_rn(e, r, q0), x));
+  return __builtin_copysignf(__fmaf_rn(e, r, q0), x);
 }
 
 // Workgroup barrier that orders LDS accesses only.  __syncthreads() also
@@ -141,6 +147,19 @@ __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
   return v;
+}
+
+// Maximum over the wave of non-negative values, returned wave-uniform: DPP
+// lane swaps inside each row of 16 (xor 1, xor 2 by quad permutation, then
+// the half-row and row mirrors), then the four row results by readlane.
+__device__ __forceinline__ float wave_max_nonneg(float v) {
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xf, 0xf, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xf, 0xf, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xf, 0xf, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x140, 0xf, 0xf, false)));
+  const int b = __float_as_int(v);
+  return fmaxf(fmaxf(__int_as_float(__builtin_amdgcn_readlane(b, 0)), __int_as_float(__builtin_amdgcn_readlane(b, 16))),
+               fmaxf(__int_as_float(__builtin_amdgcn_readlane(b, 32)), __int_as_float(__builtin_amdgcn_readlane(b, 48))));
 }
 
 }  // namespace qlk

@@ -20,47 +20,15 @@
 
 #include "decode_args.hpp"
 #include "device_common.hpp"
+#include "quant_common.hpp"
 
 namespace qlk {
 
 constexpr int QT = 256;  // threads per quantizer workgroup
 
-__device__ __forceinline__ float abs_bf16_max8(const u32x4& v, float m) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    m = fmaxf(m, bf16_to_f32(v[i] & 0x7fffu));
-    m = fmaxf(m, bf16_to_f32((v[i] >> 16) & 0x7fffu));
-  }
-  return m;
-}
-
-// Eight codes of one 16-byte bf16 vector.  r = fl(1/s) selects the
-// reciprocal path (exact at the code level for s >= 2^-96, see
-// quant_code_fast); r = 0 selects the division.
-template <int FMT>
-__device__ __forceinline__ u32x2 quant8(const u32x4& v, float s, float r) {
-  uint32_t c[8];
-  if (r != 0.0f) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      c[2 * i] = quant_code_fast<FMT>(bf16_to_f32(v[i] & 0xffffu), s, r);
-      c[2 * i + 1] = quant_code_fast<FMT>(bf16_to_f32(v[i] >> 16), s, r);
-    }
-  } else {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      c[2 * i] = quant_code<FMT>(bf16_to_f32(v[i] & 0xffffu), s);
-      c[2 * i + 1] = quant_code<FMT>(bf16_to_f32(v[i] >> 16), s);
-    }
-  }
-  u32x2 out = {c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24),
-               c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24)};
-  return out;
-}
-
 template <int NT>
 __device__ __forceinline__ float block_max(float m, float* red) {
-  m = wave_max(m);
+  m = wave_max_nonneg(m);
   const int wave = threadIdx.x >> 6;
   if ((threadIdx.x & 63) == 0) red[wave] = m;
   __syncthreads();
@@ -78,17 +46,6 @@ __device__ __forceinline__ size_t packed_offset(uint32_t row, uint32_t k, uint32
   const uint32_t kk = k & 127u;
   return ((size_t)(row >> 4) * G + (k >> 7)) * 2048u + (kk >> 6) * 1024u +
          ((row & 15u) + 16u * ((kk >> 4) & 3u)) * 16u + (kk & 15u);
-}
-
-template <int FMT>
-__device__ __forceinline__ float scale_of(float amax) {
-  const float Q = FMT == FMT_INT8 ? 127.0f : 448.0f;
-  return amax > 0.0f ? __fdiv_rn(amax, Q) : 1.0f;
-}
-
-// Reciprocal for quant8: fl(1/s), or 0 (take the division) below 2^-96.
-__device__ __forceinline__ float recip_of(float s) {
-  return s >= FAST_DIV_MIN_SCALE ? __fdiv_rn(1.0f, s) : 0.0f;
 }
 
 // One row per workgroup; the row stays in registers (VPT 16-byte vectors per
@@ -298,6 +255,25 @@ hipError_t launch_quant_wblocks(const void* w, int64_t N, int64_t K, void* q, fl
   const dim3 grid((unsigned)(K / 128), (unsigned)((N + 127) / 128)), block(QT);
   quant_wblocks_kernel<<<grid, block, 0, st>>>(static_cast<const uint16_t*>(w), (uint32_t)N, (uint32_t)K,
                                                static_cast<uint8_t*>(q), s);
+  return hipGetLastError();
+}
+
+// The E4M3 encoder alone: two values per thread, clamped, by the conversion
+// instruction every FP8 quantizer uses.
+__global__ void __launch_bounds__(256) encode_e4m3_kernel(const float* __restrict__ x, uint32_t n,
+                                                          uint8_t* __restrict__ q) {
+  const uint32_t i = (blockIdx.x * 256u + threadIdx.x) * 2u;
+  if (i >= n) return;
+  const float a = clamp448(x[i]);
+  const float b = i + 1u < n ? clamp448(x[i + 1u]) : 0.0f;
+  const uint32_t c = e4m3_pk2<false>(a, b, 0u);
+  q[i] = (uint8_t)(c & 0xffu);
+  if (i + 1u < n) q[i + 1u] = (uint8_t)((c >> 8) & 0xffu);
+}
+
+hipError_t launch_encode_e4m3(const float* x, int64_t n, void* q, hipStream_t st) {
+  const int64_t blocks = (n + 511) / 512;
+  encode_e4m3_kernel<<<dim3((unsigned)blocks), dim3(256), 0, st>>>(x, (uint32_t)n, static_cast<uint8_t*>(q));
   return hipGetLastError();
 }
 

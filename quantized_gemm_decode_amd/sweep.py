@@ -15,7 +15,12 @@ phases:
   2. the best few of phase 1 again with swap_ab in {0, 1} x prefetch {1, 2, 4}.
 For M > 32 (the tiled algorithm) the whole space -- tile, swap_ab, split_k,
 ring depth -- is timed in one phase.  Operand layouts: row-major W and A,
-packed W, packed W and A; each gets its own entries.
+packed W, packed W and A; each gets its own entries.  Layout 3 tunes
+forward plans (packed W, quantize + GEMM timed together): every fused-
+quantization configuration against the packed-A plan the table already
+holds; the winner is written as a "fwd" entry (the Deep-dive page's fused
+quantization, "Understanding Helion", as one more switch of the search
+space).
 
 Every candidate is timed as a hipGraph of back-to-back launches, each on its
 own copy of the weights (>= 1 GiB of copies, so the Infinity Cache cannot
@@ -74,9 +79,24 @@ def tiled_candidates(M, N, K, layout):
                    a_mode=2 if layout == 2 else 0, w_layout=1 if layout >= 1 else 0)
 
 
+def fused_ok(fmt, M, K):
+    """Shapes the fused-quantization decode kernel serves."""
+    return fmt != ql.BLOCK_FP8 and M <= 16 and M * K <= 16384 and K % 512 == 0
+
+
 def phase1_candidates(fmt, M, N, K, layout=0):
     if M > 32:
         yield from tiled_candidates(M, N, K, layout)
+        return
+    if layout == 3:
+        seen = set()
+        for (wn, wk), rows, split in itertools.product(WAVES_PACKED, (16, 32, 64), SPLITS):
+            key = (wn, wk, rows, _effective_chunks(K, split))
+            if key in seen:
+                continue
+            seen.add(key)
+            yield dict(swap_ab=1, split_k=split, waves_n=wn, waves_k=wk, rows_per_wave=rows, prefetch=2, a_mode=4,
+                       w_lds=0, w_layout=1)
         return
     seen = set()
     waves, rows_set = (WAVES, (16, 32)) if layout == 0 else (WAVES_PACKED, (16, 32, 64))
@@ -95,7 +115,8 @@ def phase1_candidates(fmt, M, N, K, layout=0):
 class Timer:
     """Times plans for one (format, N, K, operand layouts) on rotated weight copies.
 
-    layout 0: row-major W_q and A_q; 1: packed W_q, row-major A_q; 2: packed W_q and A_q."""
+    layout 0: row-major W_q and A_q; 1: packed W_q, row-major A_q; 2: packed W_q and A_q;
+    3: packed W_q, whole forward (quantizer + GEMM, or the fused launch) timed."""
 
     def __init__(self, fmt, N, K, x, w, stream, layout=0, max_copies=48):
         self.fmt, self.N, self.K, self.layout = fmt, N, K, layout
@@ -113,21 +134,31 @@ class Timer:
     def measure(self, plan, M, reps=5):
         """Median per-launch microseconds and the output of one launch."""
         fmt, s = self.fmt, self.stream
-        if self.layout == 2:
-            a_q, a_s = ql.quantize_act_packed(fmt, self.x[:M].contiguous())
+        xm = self.x[:M].contiguous()
+        if self.layout == 3:
+            a_q = ql.act_buffer(plan)
+            a_s = torch.empty(ql.act_scale_shape(fmt, M, self.K), dtype=torch.float32, device="cuda")
+        elif self.layout == 2:
+            a_q, a_s = ql.quantize_act_packed(fmt, xm)
         else:
-            a_q, a_s = ql.quantize_act(fmt, self.x[:M].contiguous())
+            a_q, a_s = ql.quantize_act(fmt, xm)
         y = torch.empty(M, self.N, dtype=torch.bfloat16, device="cuda")
         wsp = plan.new_workspace()
+
+        def one(c, stream=None):
+            if self.layout == 3:
+                ql.qlinear_forward(plan, xm, a_q, a_s, self.wq[c], self.ws[c], y, wsp, stream=stream)
+            else:
+                ql.qlinear_run(plan, a_q, a_s, self.wq[c], self.ws[c], y, wsp, stream=stream)
         # one eager launch first: a configuration that cannot launch fails here,
         # not later inside a captured graph
-        ql.qlinear_run(plan, a_q, a_s, self.wq[0], self.ws[0], y, wsp)
+        one(0)
         torch.cuda.synchronize()
         R = self.copies
         with torch.cuda.stream(s):
             ql.qlinear_graph_begin(s)
             for c in range(R):
-                ql.qlinear_run(plan, a_q, a_s, self.wq[c], self.ws[c], y, wsp, stream=s)
+                one(c, stream=s)
             g = ql.qlinear_graph_end(s)
         g.launch(s)
         s.synchronize()
@@ -170,7 +201,11 @@ def choose(results, tie=0.02):
 def sweep_point(timer, fmt, M, N, K, log=print, top=6):
     results = []
     ref = None
-    for cfg in phase1_candidates(fmt, M, N, K, timer.layout):
+    cands = list(phase1_candidates(fmt, M, N, K, timer.layout))
+    if timer.layout == 3:
+        # the unfused contender: the packed-activation plan (table entry or heuristic)
+        cands.insert(0, dict(ql.qlinear_plan_layouts(fmt, M, N, K, 1, 1).config))
+    for cfg in cands:
         plan = None
         # decode shapes too large for 2-block batches are instantiated with 1-block ones
         for pf in ((cfg["prefetch"],) if cfg.get("algo") == ql.ALGO_TILED else (2, 1)):
@@ -217,11 +252,12 @@ def sweep_point(timer, fmt, M, N, K, log=print, top=6):
     return [chosen] + [r for r in results if r is not chosen]
 
 
-def table_line(fmt, M, N, K, cfg, us):
+def table_line(fmt, M, N, K, cfg, us, forward=False):
     c = ql.make_config(**cfg)
-    return "%d %d %d %d %d %d %d %d %d %d %d %d %d %d %d %d %.3f" % (
+    return "%d %d %d %d %d %d %d %d %d %d %d %d %d %d %d %d %.3f%s" % (
         fmt, M, N, K, c["algo"], c["swap_ab"], c["split_k"], c["waves_n"], c["waves_k"], c["rows_per_wave"],
-        c["prefetch"], c["a_mode"], c["w_lds"], c["w_layout"], c["tile_m"], c["tile_n"], us)
+        c["prefetch"], c["a_mode"], c["w_lds"], c["w_layout"], c["tile_m"], c["tile_n"], us,
+        " fwd" if forward else "")
 
 
 def main(argv=None):
@@ -229,11 +265,13 @@ def main(argv=None):
     ap.add_argument("--workloads", default=",".join(c.name for c in CONFIGS[:4]))
     ap.add_argument("--out", default=ql.DEFAULT_TABLE)
     ap.add_argument("--ms", default=None, help="comma list overriding the token counts")
-    ap.add_argument("--layouts", default="0,1,2",
-                    help="operand layouts to tune: 0 row-major W and A, 1 packed W, 2 packed W and A")
+    ap.add_argument("--layouts", default="0,1,2,3",
+                    help="operand layouts to tune: 0 row-major W and A, 1 packed W, 2 packed W and A, "
+                         "3 forward plans (packed W; fused quantization or not)")
     args = ap.parse_args(argv)
     torch.cuda.set_device(0)
     stream = torch.cuda.Stream()
+    ql.load_default_table()     # forward tuning starts from the packed-activation entries
     t_start = time.time()
     hdr = ["# qlinear sweep table: fmt M N K algo swap_ab split_k waves_n waves_k rows_per_wave prefetch "
            "a_mode w_lds w_layout tile_m tile_n time_us",
@@ -249,12 +287,15 @@ def main(argv=None):
             for (lab, N, K) in wl.shapes:
                 x, w = make_inputs(K, N, max(ms), wl.sigma_w, seed=wl.seed)
                 for layout in [int(v) for v in args.layouts.split(",")]:
+                    lms = [m for m in ms if layout != 3 or fused_ok(wl.fmt, m, K)]
+                    if not lms:
+                        continue
                     timer = Timer(wl.fmt, N, K, x, w, stream, layout=layout)
-                    for M in ms:
+                    for M in lms:
                         t0 = time.time()
                         res = sweep_point(timer, wl.fmt, M, N, K)
                         us, cfg = res[0]
-                        f.write(table_line(wl.fmt, M, N, K, cfg, us) + "\n")
+                        f.write(table_line(wl.fmt, M, N, K, cfg, us, forward=layout == 3) + "\n")
                         f.flush()
                         n += 1
                         print("%-26s %-8s L%d M=%-3d best %.3f us (%s)  [%d cands, %.1fs]" % (

@@ -179,3 +179,53 @@ def test_heuristic_plans_cover_every_decode_workload():
         for (_, N, K, M) in decode_points(cfg):
             p = ql.qlinear_plan(cfg.fmt, M, N, K)
             assert p.facts["workgroups"] >= 256
+
+
+def test_fused_quantization_plans_are_validated_on_host():
+    fused = dict(w_layout=1, a_mode=4, waves_n=1, waves_k=4)
+    assert _plan_status(ql.FP8_DYNAMIC, 4, 4096, 4096, **fused) == QL_OK
+    assert _plan_status(ql.W8A8_INT8, 1, 4096, 12288, **fused) == QL_OK
+    assert _plan_status(ql.BLOCK_FP8, 1, 4096, 4096, **fused) == QL_E_UNSUPPORTED    # per-token formats only
+    assert _plan_status(ql.FP8_DYNAMIC, 8, 4096, 4096, **fused) == QL_E_UNSUPPORTED  # M*K > 16384
+    assert _plan_status(ql.FP8_DYNAMIC, 17, 4096, 512, **fused) == QL_E_UNSUPPORTED  # one token tile
+    assert _plan_status(ql.FP8_DYNAMIC, 1, 4096, 4352, **fused) == QL_E_UNSUPPORTED  # K % 512
+    assert _plan_status(ql.FP8_DYNAMIC, 1, 4096, 4096, a_mode=4) == QL_E_UNSUPPORTED  # needs packed weights
+    assert _plan_status(ql.FP8_DYNAMIC, 1, 4096, 4096, a_mode=5, w_layout=1) == QL_E_INVALID
+    # a fused plan quantizes X itself, so it only runs through qlinear_forward
+    p = ql.qlinear_plan_with_config(ql.FP8_DYNAMIC, 2, 1024, 4096, fused)
+    assert p.facts["lds_bytes"] >= 512 + 2 * (4096 + 64)
+    v = ctypes.c_void_p
+    good = v(1 << 20)
+    assert ql.lib().qlinear_run(p.handle, good, good, good, good, good, v(0), v(0)) == QL_E_INVALID
+    assert "qlinear_forward" in ql.lib().qlinear_last_error().decode()
+    assert ql.lib().qlinear_forward(p.handle, v(0), good, good, good, good, good, v(0), v(0)) == QL_E_INVALID
+    assert ql.lib().qlinear_forward(p.handle, v(8), good, good, good, good, good, v(0), v(0)) == QL_E_ALIGN
+
+
+def test_forward_table_entries(tmp_path):
+    t = tmp_path / "t.txt"
+    t.write_text("0 4 4096 4096 0 0 1 1 4 16 2 2 0 1 0 0 5.0\n"          # packed-A_q entry
+                 "0 4 4096 4096 0 0 1 1 4 32 1 4 0 1 0 0 6.1 fwd\n"      # forward entry, fused
+                 "0 8 4096 4096 0 1 1 1 4 16 2 3 0 1 0 0 8.2 fwd\n"      # forward entry, not fused
+                 "0 16 4096 4096 0 0 2 1 4 16 2 2 0 1 0 0 6.0\n")
+    assert ql.qlinear_table_load(str(t)) == 4
+    try:
+        p = ql.qlinear_plan_layouts(ql.FP8_DYNAMIC, 3, 4096, 4096, 1, 2)
+        assert p.facts["source"] == "table" and p.config["a_mode"] == 4 and p.config["rows_per_wave"] == 32
+        p = ql.qlinear_plan_layouts(ql.FP8_DYNAMIC, 3, 4096, 4096, 1, 1)   # the packed-A_q plan ignores fwd entries
+        assert p.config["a_mode"] == 2 and p.config["rows_per_wave"] == 16
+        p = ql.qlinear_plan_layouts(ql.FP8_DYNAMIC, 8, 4096, 4096, 1, 2)
+        assert p.config["a_mode"] == 3 and p.config["swap_ab"] == 1
+        p = ql.qlinear_plan_layouts(ql.FP8_DYNAMIC, 8, 4096, 4096, 1, 1)   # no packed-A_q entry at 8: next tuned
+        assert p.config["a_mode"] == 2 and p.config["split_k"] == 2
+        p = ql.qlinear_plan_layouts(ql.FP8_DYNAMIC, 12, 4096, 4096, 1, 2)  # no fwd entry at 16: packed-A_q entry
+        assert p.facts["source"] == "table" and p.config["a_mode"] == 2 and p.config["split_k"] == 2
+        with pytest.raises(ql.QLinearError):
+            ql.qlinear_plan_layouts(ql.FP8_DYNAMIC, 4, 4096, 4096, 0, 2)   # forward plans need packed weights
+    finally:
+        ql.qlinear_table_clear()
+    bad = tmp_path / "bad.txt"
+    bad.write_text("0 4 4096 4096 0 0 1 1 4 16 2 2 0 1 0 0 5.0 xyz\n")
+    with pytest.raises(ql.QLinearError) as e:
+        ql.qlinear_table_load(str(bad))
+    assert e.value.status == QL_E_TABLE

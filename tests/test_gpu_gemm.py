@@ -375,7 +375,7 @@ def _table_entries():
         if not f or f[0].startswith("#"):
             continue
         v = [int(t) for t in f[:16]]
-        out.append(tuple(v))
+        out.append(tuple(v) + (int(len(f) > 17 and f[17] == "fwd"),))
     return out
 
 
@@ -393,10 +393,12 @@ def _shape_config(fmt, N, K):
     raise KeyError((fmt, N, K))
 
 
-@pytest.mark.parametrize("entry", _table_entries(), ids=lambda e: "f%d-M%d-N%d-K%d-L%d" % (e[0], e[1], e[2], e[3], e[13]))
+@pytest.mark.parametrize("entry", _table_entries(),
+                         ids=lambda e: "f%d-M%d-N%d-K%d-L%d%s" % (e[0], e[1], e[2], e[3], e[13], "-fwd" * e[16]))
 def test_every_table_entry_matches_oracle(entry):
     """Each configuration the shipped sweep table selects, run at its own
-    (format, M, N, K) and weight layout, against the oracle on sampled columns."""
+    (format, M, N, K) and weight layout, against the oracle on sampled columns
+    (forward entries through qlinear_forward, which also quantizes)."""
     fmt, M, N, K = entry[:4]
     cfg = dict(zip(_TABLE_FIELDS, entry[4:16]))
     ci, lab = _shape_config(fmt, N, K)
@@ -405,10 +407,18 @@ def test_every_table_entry_matches_oracle(entry):
     a_q, a_s = ql.quantize_act(fmt, xm.cuda())
     plan = ql.qlinear_plan_with_config(fmt, M, N, K, cfg)
     y = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
-    if cfg["a_mode"] >= 2:
-        a_q, _ = ql.quantize_act_packed(fmt, xm.cuda())
-    ql.qlinear_run(plan, a_q, a_s, ql.pack_weight(w_q) if cfg["w_layout"] else w_q, w_s, y, plan.new_workspace())
-    torch.cuda.synchronize()
+    w_use = ql.pack_weight(w_q) if cfg["w_layout"] else w_q
+    if entry[16]:
+        a_f = ql.act_buffer(plan)
+        s_f = torch.empty_like(a_s)
+        ql.qlinear_forward(plan, xm.cuda(), a_f, s_f, w_use, w_s, y, plan.new_workspace())
+        torch.cuda.synchronize()
+        assert torch.equal(s_f, a_s)
+    else:
+        if cfg["a_mode"] >= 2:
+            a_q, _ = ql.quantize_act_packed(fmt, xm.cuda())
+        ql.qlinear_run(plan, a_q, a_s, w_use, w_s, y, plan.new_workspace())
+        torch.cuda.synchronize()
     yb = host_bf16_bits(y)
     rng = np.random.default_rng(N + 7 * M)
     if fmt == ql.BLOCK_FP8:

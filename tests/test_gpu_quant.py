@@ -113,3 +113,37 @@ def test_quantizer_empty_inputs_are_no_ops():
     x = torch.empty(0, 256, dtype=torch.bfloat16, device="cuda")
     a_q, a_s = ql.quantize_act(ql.W8A8_INT8, x)
     assert a_q.shape == (0, 256)
+
+
+def _e4m3_probe_inputs():
+    """Every bf16 value; every binary32 within 64 ulp of each E4M3 value and of
+    each midpoint between neighbouring values (both signs); values beyond the
+    clamp; binary32 subnormals; random bit patterns."""
+    v = oracle.e4m3_decode(np.arange(128, dtype=np.uint8))
+    v = np.sort(v[np.isfinite(v)]).astype(np.float64)            # 0 .. 448, 127 values
+    pts = np.concatenate([v, (v[1:] + v[:-1]) / 2]).astype(np.float32)
+    b = pts.view(np.int32)[:, None] + np.arange(-64, 65, dtype=np.int32)[None, :]
+    near = b[b >= 0].view(np.float32)
+    allbf = (np.arange(65536, dtype=np.uint32) << 16).view(np.float32)
+    allbf = allbf[np.isfinite(allbf)]
+    rng = np.random.default_rng(11)
+    rnd = rng.integers(0, 2 ** 32, 4 << 20, dtype=np.uint64).astype(np.uint32).view(np.float32)
+    rnd = rnd[np.isfinite(rnd)]
+    extra = np.array([448.0, 448.5, 464.0, 464.5, 480.0, 1e30, np.inf, 1e-40, 1.4e-45, 0.0], np.float32)
+    x = np.concatenate([near, -near, allbf, rnd, extra, -extra])
+    return np.ascontiguousarray(x, np.float32)
+
+
+def test_e4m3_encoder_matches_the_format_definition():
+    """The conversion instruction the FP8 quantizers use, against the oracle's
+    encoder (written from the OCP E4M3 definition) on the clamped inputs."""
+    x = _e4m3_probe_inputs()
+    xd = torch.from_numpy(x).cuda()
+    codes = torch.empty(x.size, dtype=torch.uint8, device="cuda")
+    ql.qlinear_encode_e4m3(xd, codes)
+    torch.cuda.synchronize()
+    ref = oracle.e4m3_encode(np.clip(x, -448.0, 448.0))
+    got = codes.cpu().numpy()
+    bad = np.flatnonzero(got != ref)
+    assert bad.size == 0, [(float(x[i]), hex(x[i:i + 1].view(np.uint32)[0]), int(got[i]), int(ref[i]))
+                           for i in bad[:8]]
