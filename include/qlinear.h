@@ -80,7 +80,8 @@ typedef enum {
 
 /* Algorithm family of a plan. */
 typedef enum {
-  QL_ALGO_DECODE = 0, /* weight-streaming kernel for M <= 32 (decode token counts) */
+  QL_ALGO_DECODE = 0, /* weight-streaming kernel for M <= 64 (decode token counts; the planner's
+                          heuristic uses it up to 32, the sweep table may pick it up to 64) */
   QL_ALGO_TILED = 1   /* LDS-tiled matrix-core GEMM for larger M */
 } ql_algo;
 
@@ -231,8 +232,9 @@ void qlinear_table_clear(void);
  * or above, else the largest); without an entry a built-in heuristic is used
  * (facts.source tells which).  The environment variable QLINEAR_FORCE =
  * "algo,swap,split,wn,wk,rows,prefetch,amode,wlds,wlayout,tile_m,tile_n"
- * overrides both (its operand layouts must match the call).  M <= 32 plans
- * use the DECODE algorithm, M > 32 the TILED one.  qlinear_plan: row-major
+ * overrides both (its operand layouts must match the call).  Without a table
+ * entry M <= 32 plans use the DECODE algorithm and M > 32 the TILED one; the
+ * table may choose DECODE up to M = 64 (four 16-token tiles, packed weights).  qlinear_plan: row-major
  * W_q and A_q.
  * Host-only: nothing is enqueued and nothing is allocated (a TILED plan
  * raises its kernel's dynamic LDS limit with hipFuncSetAttribute).

@@ -250,7 +250,7 @@ ql_status build_plan(int32_t fmt, int64_t M, int64_t N, int64_t K, const ql_conf
     return fail(QL_E_UNSUPPORTED, "packed weights exceed 2^30 bytes");
   if (cfg.algo == QL_ALGO_TILED) return build_tiled_plan(fmt, M, N, K, cfg, source, out);
   if (cfg.algo != QL_ALGO_DECODE) return fail(QL_E_INVALID, "unknown algo %d", cfg.algo);
-  if (M > 32) return fail(QL_E_UNSUPPORTED, "the decode algorithm serves M <= 32 (M=%lld)", (long long)M);
+  if (M > 64) return fail(QL_E_UNSUPPORTED, "the decode algorithm serves M <= 64 (M=%lld)", (long long)M);
   if (cfg.swap_ab != 0 && cfg.swap_ab != 1) return fail(QL_E_INVALID, "swap_ab must be 0 or 1");
   if (!is_pow2(cfg.split_k) || cfg.split_k > 256) return fail(QL_E_INVALID, "split_k must be a power of two in [1, 256]");
   const int nw = cfg.waves_n * cfg.waves_k;
@@ -284,7 +284,7 @@ ql_status build_plan(int32_t fmt, int64_t M, int64_t N, int64_t K, const ql_conf
   const int split = std::max(1, std::min<int>(cfg.split_k, std::max(1, p->G)));
   p->chunk_kb = p->G > 0 ? (p->G + split - 1) / split : 0;
   p->chunks = p->G > 0 ? (p->G + p->chunk_kb - 1) / p->chunk_kb : 1;
-  p->mt = M <= 16 ? 1 : 2;
+  p->mt = M <= 16 ? 1 : (M <= 32 ? 2 : 4);
   const int rg = cfg.rows_per_wave / 16;
   p->bn = cfg.waves_n * rg * 16;
   p->n_tiles = (int)((N + p->bn - 1) / p->bn);

@@ -1,4 +1,4 @@
-// Launch arguments of the decode (M <= 32) quantized GEMM kernel, shared by
+// Launch arguments of the decode (M <= 64) quantized GEMM kernel, shared by
 // the host dispatcher and the kernel translation units.
 #pragma once
 
@@ -44,7 +44,7 @@ struct DecodeArgs {
 struct DecodeKey {
   int fmt;   // FMT_FP8 / FMT_INT8 / FMT_BLOCK
   int swap;  // weights as the matrix core's first operand
-  int mt;    // 16-wide token tiles (1: M <= 16, 2: M <= 32)
+  int mt;    // 16-wide token tiles (1: M <= 16, 2: M <= 32, 4: M <= 64)
   int rg;    // 16-row groups per wave (1, 2 or 4)
   int nw;    // waves per workgroup (4, 8 or 16)
   int pf;    // K blocks per prefetch batch

@@ -1,4 +1,4 @@
-// Weight-streaming quantized GEMM for decode token counts (M <= 32) on gfx950.
+// Weight-streaming quantized GEMM for decode token counts (M <= 64) on gfx950.
 //
 // What it computes: Y[m, n] = epilogue(sum_k A_q[m, k] * W_q[n, k]) with the
 // scales of the format fused in -- the scaled quantized linear of the Helion
@@ -623,7 +623,7 @@ __global__ void __launch_bounds__(NW * 64) qgemm_decode_kernel(DecodeArgs p) {
 // instantiated, and the planner rejects it.
 template <int FMT, int NW_, int SW, int MT_, int RG_, int PF_>
 constexpr bool decode_config_fits() {
-  if (NW_ == 4 && RG_ <= 2 && PF_ >= 2) {
+  if (NW_ == 4 && RG_ <= 2 && PF_ >= 2 && MT_ <= 2) {
     // the original 4-wave shapes (checked one by one against the compiler)
     if (MT_ == 2 && RG_ == 2 && PF_ == 4) return false;
     if (FMT == FMT_BLOCK && MT_ == 2 && PF_ == 4 && !SW) return false;
@@ -700,10 +700,18 @@ hipError_t decode_dispatch(const DecodeKey& k, dim3 grid, dim3 block, size_t lds
   QL_TRY_PA(4, SW, MT_, 1, 1) QL_TRY_PA(4, SW, MT_, 2, 1) QL_TRY_P(4, SW, MT_, 4)             \
   QL_TRY_P(8, SW, MT_, 1) QL_TRY_P(8, SW, MT_, 2) QL_TRY_P(8, SW, MT_, 4)                 \
   QL_TRY_P(16, SW, MT_, 1) QL_TRY_P(16, SW, MT_, 2) QL_TRY_P(16, SW, MT_, 4)
-#define QL_TRY_MT(SW) QL_TRY_RG(SW, 1) QL_TRY_RG(SW, 2) QL_TRY_PN(SW, 1) QL_TRY_PN(SW, 2)
+  // four token tiles (M <= 64): packed weights, activations from L2
+#define QL_TRY_P4(NW_, SW, RG_, PF_) QL_TRY(NW_, SW, 4, RG_, PF_, 0, 2) QL_TRY(NW_, SW, 4, RG_, PF_, 2, 2)
+#define QL_TRY_PN4(SW)                                                                            \
+  QL_TRY_P4(4, SW, 1, 1) QL_TRY_P4(4, SW, 1, 2) QL_TRY_P4(4, SW, 2, 1) QL_TRY_P4(4, SW, 2, 2)     \
+  QL_TRY_P4(4, SW, 4, 1) QL_TRY_P4(8, SW, 1, 1) QL_TRY_P4(8, SW, 1, 2) QL_TRY_P4(8, SW, 2, 1)     \
+  QL_TRY_P4(8, SW, 2, 2)
+#define QL_TRY_MT(SW) QL_TRY_RG(SW, 1) QL_TRY_RG(SW, 2) QL_TRY_PN(SW, 1) QL_TRY_PN(SW, 2) QL_TRY_PN4(SW)
   QL_TRY_MT(0)
   QL_TRY_MT(1)
 #undef QL_TRY_MT
+#undef QL_TRY_PN4
+#undef QL_TRY_P4
 #undef QL_TRY_PN
 #undef QL_TRY_P
 #undef QL_TRY_PA

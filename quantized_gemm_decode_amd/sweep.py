@@ -84,9 +84,25 @@ def fused_ok(fmt, M, K):
     return fmt != ql.BLOCK_FP8 and M <= 16 and M * K <= 16384 and K % 512 == 0
 
 
+def decode_m64_candidates(M, N, K, layout):
+    """Weight-streaming configurations with four token tiles (32 < M <= 64,
+    packed weights, activations from L2)."""
+    seen = set()
+    for (wn, wk), rows, split, amode in itertools.product(((4, 1), (2, 2), (1, 4), (2, 4), (1, 8)), (16, 32, 64),
+                                                         SPLITS, (2, 0) if layout == 2 else (0,)):
+        key = (wn, wk, rows, _effective_chunks(K, split), amode)
+        if key in seen:
+            continue
+        seen.add(key)
+        yield dict(swap_ab=1, split_k=split, waves_n=wn, waves_k=wk, rows_per_wave=rows, prefetch=2, a_mode=amode,
+                   w_lds=0, w_layout=1)
+
+
 def phase1_candidates(fmt, M, N, K, layout=0):
     if M > 32:
         yield from tiled_candidates(M, N, K, layout)
+        if M <= 64 and layout >= 1:
+            yield from decode_m64_candidates(M, N, K, layout)
         return
     if layout == 3:
         seen = set()
@@ -231,7 +247,8 @@ def sweep_point(timer, fmt, M, N, K, log=print, top=6):
         results.append((us, cfg))
     results.sort(key=lambda t: t[0])
     seen = {tuple(sorted(c.items())) for _, c in results}
-    for _, base in (results[:top] if M <= 32 else []):   # the tiled space is searched whole in phase 1
+    # the tiled space is searched whole in phase 1; decode candidates get a second pass
+    for _, base in [r for r in results if r[1].get("algo", ql.ALGO_DECODE) == ql.ALGO_DECODE][:top]:
         for swap, pf in itertools.product((0, 1), (1, 2, 4)):
             cfg = dict(base, swap_ab=swap, prefetch=pf)
             k = tuple(sorted(cfg.items()))

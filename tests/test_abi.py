@@ -229,3 +229,18 @@ def test_forward_table_entries(tmp_path):
     with pytest.raises(ql.QLinearError) as e:
         ql.qlinear_table_load(str(bad))
     assert e.value.status == QL_E_TABLE
+
+
+def test_decode_plans_reach_64_tokens():
+    cfg = dict(w_layout=1, a_mode=2, waves_n=1, waves_k=4, prefetch=1)
+    assert _plan_status(ql.FP8_DYNAMIC, 64, 4096, 4096, **cfg) == QL_OK
+    assert _plan_status(ql.W8A8_INT8, 33, 4096, 4096, **cfg) == QL_OK
+    assert _plan_status(ql.FP8_DYNAMIC, 65, 4096, 4096, **cfg) == QL_E_UNSUPPORTED
+    p = ql.qlinear_plan_with_config(ql.FP8_DYNAMIC, 50, 4096, 4096, cfg)
+    assert p.config["algo"] == ql.ALGO_DECODE and p.facts["threads"] == 256
+    # without a table entry the planner still sends M > 32 to the tiled kernel
+    ql.qlinear_table_clear()
+    try:
+        assert ql.qlinear_plan_layouts(ql.FP8_DYNAMIC, 50, 4096, 4096, 1, 1).config["algo"] == ql.ALGO_TILED
+    finally:
+        ql.load_default_table()

@@ -104,7 +104,7 @@ WIDE = list(itertools.product([4, 8, 16], [16, 32, 64], [1, 2], [0, 1], [0, 2, 3
 
 
 @pytest.mark.parametrize("fmt", FMTS)
-@pytest.mark.parametrize("M", [5, 29])
+@pytest.mark.parametrize("M", [5, 29, 61])
 @pytest.mark.parametrize("wi", range(len(WIDE)))
 def test_wide_workgroup_instantiations_match_oracle(fmt, M, wi):
     nw, rows, pf, swap, amode = WIDE[wi]

@@ -123,8 +123,8 @@ _LARGE = {}
 @pytest.mark.parametrize("lab,N,K,M", _large_points())
 def test_large_m_workloads_sampled_columns(lab, N, K, M):
     """14B-class FP8 shapes at full size with the planner's configuration
-    (packed weights and activations); the oracle recomputes 64 sampled output
-    columns."""
+    (packed weights and activations; tiled, or at M = 64 possibly the
+    weight-streaming kernel); the oracle recomputes 64 sampled output columns."""
     cfg = CONFIGS[4]
     fmt = cfg.fmt
     key = (lab, N, K)
@@ -138,7 +138,9 @@ def test_large_m_workloads_sampled_columns(lab, N, K, M):
     a_q, a_s = ql.quantize_act(fmt, xm.cuda())
     a_p, _ = ql.quantize_act_packed(fmt, xm.cuda())
     plan = ql.qlinear_plan_layouts(fmt, M, N, K, 1, 1)
-    assert plan.config["algo"] == ql.ALGO_TILED and plan.config["a_mode"] == 2
+    # the table may serve M = 64 with the weight-streaming kernel (four token tiles)
+    assert plan.config["algo"] == ql.ALGO_TILED or M <= 64
+    assert plan.config["a_mode"] == 2
     y = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
     ql.qlinear_run(plan, a_p, a_s, w_p, w_s, y, plan.new_workspace())
     torch.cuda.synchronize()
