@@ -129,7 +129,8 @@ typedef struct {
                             1 = packed tiles (qlinear_pack_weight) */
   int32_t tile_m;        /* TILED: workgroup tile rows (tokens): 64, 128 or 256 */
   int32_t tile_n;        /* TILED: workgroup tile columns (weight rows): 128 or 256;
-                            tile_m * tile_n <= 32768.  TILED reads swap_ab, split_k,
+                            tile_m * tile_n <= 32768 with 4 waves, or 256 x 256 with 8 waves
+                            (packed operands, LDS-DMA ring of 2 stages, per-token formats).  TILED reads swap_ab, split_k,
                             a_mode (0 or 2), w_layout, prefetch and the tile; the other
                             fields are ignored */
 } ql_config;

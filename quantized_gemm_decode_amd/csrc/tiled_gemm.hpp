@@ -12,7 +12,10 @@
 // threshold ([Summary] "Hybrid dispatch addresses runtime overhead"); here
 // they stay in the same library, with the same split_k / swap_ab switches.
 //
-// Structure (256 threads = 4 waves in a 2 x 2 grid, wave tile TM x TN):
+// Structure (256 threads = 4 waves in a 2 x 2 grid, wave tile TM x TN; the
+// 256 x 256 tile runs 512 threads = 8 waves in a 2 x 4 grid, wave tile
+// 128 x 64, so the LDS bytes a wave reads per flop drop by a quarter and the
+// L2 bytes per flop by half against 128 x 128):
 //   * K advances in 128-wide blocks.  Per block, every thread loads its
 //     16-byte pieces of the A tile (BM x 128) and the B tile (BN x 128) from
 //     global memory into registers, and writes them into one of two LDS
@@ -50,13 +53,22 @@ struct TiledAcc<FMT_INT8> {
   typedef i32x4 T;
 };
 
+// Waves along N of a tile's wave grid (along M there are always 2).
+template <int BM, int BN>
+constexpr int tiled_waves_n() {
+  return BM * BN >= 256 * 256 ? 4 : 2;
+}
+
 template <int FMT, bool SWAP, int BM, int BN, int WM, int PF, bool AP, int NS>
-__global__ void __launch_bounds__(256) qgemm_tiled_kernel(DecodeArgs p) {
-  constexpr int TM = BM / 2, TN = BN / 2;  // wave tile
+__global__ void __launch_bounds__((64 * 2 * tiled_waves_n<BM, BN>())) qgemm_tiled_kernel(DecodeArgs p) {
+  constexpr int WGN = tiled_waves_n<BM, BN>();
+  constexpr int NW = 2 * WGN;              // waves per workgroup
+  constexpr int NT = 64 * NW;              // threads
+  constexpr int TM = BM / 2, TN = BN / WGN;  // wave tile
   constexpr int IM = TM / 16, IN = TN / 16;
   constexpr int STAGE = (BM + BN) * 128;   // bytes of one LDS stage
-  constexpr int PA = BM * 8 / 256;         // 16-byte A pieces per thread per K block
-  constexpr int PB = BN * 8 / 256;
+  constexpr int PA = BM * 8 / NT;          // 16-byte A pieces per thread per K block
+  constexpr int PB = BN * 8 / NT;
   constexpr bool WP = WM == W_PACKED;
   using Acc = typename TiledAcc<FMT>::T;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
@@ -65,7 +77,7 @@ __global__ void __launch_bounds__(256) qgemm_tiled_kernel(DecodeArgs p) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int wy = wave >> 1, wx = wave & 1;
+  const int wy = wave / WGN, wx = wave % WGN;
   const int r16 = lane & 15, g = lane >> 4;
 
   const uint32_t M = (uint32_t)p.M, N = (uint32_t)p.N, K = (uint32_t)p.K;
@@ -109,7 +121,7 @@ __global__ void __launch_bounds__(256) qgemm_tiled_kernel(DecodeArgs p) {
     const uint32_t kofs = (uint32_t)kb * 128u;
 #pragma unroll
     for (int i = 0; i < PA; ++i) {
-      const uint32_t q = (uint32_t)(i * 256 + tid);
+      const uint32_t q = (uint32_t)(i * NT + tid);
       if constexpr (AP) {
         const uint32_t t = m0 / 16u + (q >> 7);
         pa[sl][i] = bload16(ra, (in && t < MT16) ? (t * G + (uint32_t)kb) * 2048u + (q & 127u) * 16u : OOB);
@@ -120,7 +132,7 @@ __global__ void __launch_bounds__(256) qgemm_tiled_kernel(DecodeArgs p) {
     }
 #pragma unroll
     for (int i = 0; i < PB; ++i) {
-      const uint32_t q = (uint32_t)(i * 256 + tid);
+      const uint32_t q = (uint32_t)(i * NT + tid);
       if constexpr (WP) {
         const uint32_t t = n0 / 16u + (q >> 7);
         pb[sl][i] = bload16(rw, (in && t < NT16) ? (t * G + (uint32_t)kb) * 2048u + (q & 127u) * 16u : OOB);
@@ -136,7 +148,7 @@ __global__ void __launch_bounds__(256) qgemm_tiled_kernel(DecodeArgs p) {
     uint8_t* base = smem + buf * STAGE;
 #pragma unroll
     for (int i = 0; i < PA; ++i) {
-      const int q = i * 256 + tid;
+      const int q = i * NT + tid;
       if constexpr (AP) {
         *reinterpret_cast<u32x4*>(base + q * 16) = pa[sl][i];
       } else {
@@ -148,7 +160,7 @@ __global__ void __launch_bounds__(256) qgemm_tiled_kernel(DecodeArgs p) {
     uint8_t* bbase = base + BM * 128;
 #pragma unroll
     for (int i = 0; i < PB; ++i) {
-      const int q = i * 256 + tid;
+      const int q = i * NT + tid;
       if constexpr (WP) {
         *reinterpret_cast<u32x4*>(bbase + q * 16) = pb[sl][i];
       } else {
@@ -248,17 +260,19 @@ __global__ void __launch_bounds__(256) qgemm_tiled_kernel(DecodeArgs p) {
     // ---- packed operands straight into an NS-stage LDS ring with LDS-DMA
     // buffer loads (no staging registers).  A stage is the A tile's BM/16
     // and the B tile's BN/16 2 KB tiles, each copied as two 1 KB wave loads;
-    // every wave issues DW of them per stage, so "stage it has landed" is
+    // every wave issues DW of them per stage (wave w takes the halves
+    // w, w + NW, w + 2NW, ...), so "stage it has landed" is
     // "at most (NS-2)*DW of this wave's loads outstanding" followed by a
     // barrier.  The refill of stage it-1's buffer goes out right after that
     // barrier, before the matrix cores start on stage it.
     static_assert(WP && AP && FMT != FMT_BLOCK, "the LDS-DMA ring reads packed operands");
     constexpr int TA = BM / 16, TB = BN / 16;
-    constexpr int DA = 2 * TA / 4, DB = 2 * TB / 4;
+    constexpr int DA = 2 * TA / NW, DB = 2 * TB / NW;
+    static_assert(DA * NW == 2 * TA && DB * NW == 2 * TB, "whole 1 KB halves per wave");
     constexpr int DW = DA + DB;
     constexpr int ALLOW = (NS - 2) * DW;
     static_assert(ALLOW <= 63, "vmcnt holds 6 bits");
-    // wave w copies 1 KB halves j = w + 4i: tile j/2 = w/2 + 2i, half w%2
+    // wave w copies 1 KB halves j = w + NW*i: tile j/2 = w/2 + (NW/2)*i, half w%2
     const uint32_t a_lane = (m0 / 16u + (uint32_t)(wave >> 1)) * G * 2048u + (uint32_t)(wave & 1) * 1024u +
                             (uint32_t)lane * 16u;
     const uint32_t b_lane = (n0 / 16u + (uint32_t)(wave >> 1)) * G * 2048u + (uint32_t)(wave & 1) * 1024u +
@@ -270,17 +284,17 @@ __global__ void __launch_bounds__(256) qgemm_tiled_kernel(DecodeArgs p) {
       const uint32_t kofs = (uint32_t)kb * 2048u;
 #pragma unroll
       for (int i = 0; i < DA; ++i) {
-        const uint32_t t = m0 / 16u + (uint32_t)(wave >> 1) + 2u * (uint32_t)i;
-        const uint32_t off = (in && t < MT16) ? a_lane + (uint32_t)i * 2u * G * 2048u + kofs : OOB;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (__attribute__((address_space(3))) void*)(base + i * 4096), 16,
-                                                 off, 0, 0, 0);
+        const uint32_t t = m0 / 16u + (uint32_t)(wave >> 1) + (uint32_t)(NW / 2) * (uint32_t)i;
+        const uint32_t off = (in && t < MT16) ? a_lane + (uint32_t)i * (uint32_t)(NW / 2) * G * 2048u + kofs : OOB;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (__attribute__((address_space(3))) void*)(base + i * NW * 1024),
+                                                 16, off, 0, 0, 0);
       }
 #pragma unroll
       for (int i = 0; i < DB; ++i) {
-        const uint32_t t = n0 / 16u + (uint32_t)(wave >> 1) + 2u * (uint32_t)i;
-        const uint32_t off = (in && t < NT16) ? b_lane + (uint32_t)i * 2u * G * 2048u + kofs : OOB;
+        const uint32_t t = n0 / 16u + (uint32_t)(wave >> 1) + (uint32_t)(NW / 2) * (uint32_t)i;
+        const uint32_t off = (in && t < NT16) ? b_lane + (uint32_t)i * (uint32_t)(NW / 2) * G * 2048u + kofs : OOB;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            rw, (__attribute__((address_space(3))) void*)(base + BM * 128 + i * 4096), 16, off, 0, 0, 0);
+            rw, (__attribute__((address_space(3))) void*)(base + BM * 128 + i * NW * 1024), 16, off, 0, 0, 0);
       }
     };
     if (nk > 0) {
@@ -457,11 +471,13 @@ __global__ void __launch_bounds__(256) qgemm_tiled_kernel(DecodeArgs p) {
 }
 
 // Tile shapes instantiated per format: a wave holds (BM/32) x (BN/32) 16x16
-// accumulator tiles, at most 128 registers (256 x 256 would spill).
+// accumulator tiles (4 waves), at most 128 registers; the 8-wave 256 x 256
+// tile holds 8 x 4 and exists for the LDS-DMA ring of 2 stages only.
 // Block_FP8 in the standard orientation also keeps four token scales per
 // accumulator tile row live, so its largest tiles are left out as well.
 template <int FMT, int SW, int BM, int BN, int PF, int NS>
 constexpr bool tiled_config_fits() {
+  if (BM * BN == 256 * 256) return NS == 2 && FMT != FMT_BLOCK;
   if (NS > 0) return FMT != FMT_BLOCK && NS * (BM + BN) * 128 <= 160 * 1024 && BM * BN <= 128 * 256;
   if (FMT == FMT_BLOCK && !SW && BM * BN > 128 * 128) return false;
   if (PF * (BM + BN) > 768) return false;  // ring of PF K blocks: at most 96 VGPRs a lane
@@ -481,7 +497,7 @@ hipError_t tiled_try(const TiledKey& k, dim3 grid, size_t lds, hipStream_t s, co
         return hipFuncSetAttribute(reinterpret_cast<const void*>(fn), hipFuncAttributeMaxDynamicSharedMemorySize,
                                    (int)lds);
       }
-      fn<<<grid, dim3(256), lds, s>>>(a);
+      fn<<<grid, dim3(64 * 2 * tiled_waves_n<BM, BN>()), lds, s>>>(a);
       return hipGetLastError();
     }
   }
@@ -517,6 +533,7 @@ hipError_t tiled_dispatch(const TiledKey& k, dim3 grid, size_t lds, hipStream_t 
   QL_TD_S(128, 256, 3)
   QL_TD_S(256, 128, 2)
   QL_TD_S(256, 128, 3)
+  QL_TD_S(256, 256, 2)
 #undef QL_TD_S
 #undef QL_TD
 #undef QL_TT_S

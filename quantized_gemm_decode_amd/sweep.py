@@ -72,9 +72,11 @@ def tiled_candidates(M, N, K, layout):
     """Every tiled configuration for M > 32 (tile, orientation, split, register-ring depth,
     and with packed operands the LDS-DMA ring of 2 or 3 stages)."""
     rings = [(0, 1), (0, 2), (0, 4)] + ([(1, 2), (1, 3)] if layout == 2 else [])
-    for (bm, bn), swap, split, (dma, pf) in itertools.product(TILES, (0, 1), (1, 2, 4, 8), rings):
+    for (bm, bn), swap, split, (dma, pf) in itertools.product(TILES + ((256, 256),), (0, 1), (1, 2, 4, 8), rings):
         if bm > 64 and bm > 2 * M:
             continue
+        if (bm, bn) == (256, 256) and (dma, pf) != (1, 2):
+            continue                  # the 8-wave tile runs the 2-stage LDS-DMA ring only
         yield dict(algo=ql.ALGO_TILED, swap_ab=swap, split_k=split, tile_m=bm, tile_n=bn, prefetch=pf, w_lds=dma,
                    a_mode=2 if layout == 2 else 0, w_layout=1 if layout >= 1 else 0)
 

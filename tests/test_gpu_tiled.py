@@ -58,7 +58,8 @@ def test_every_tiled_instantiation_matches_oracle(fmt, M, vi):
         assert int(torch.count_nonzero(ws)) == 0, "split-K workspace not left all-zero"
 
 
-DMA_VARIANTS = list(itertools.product([0, 1], [(128, 128), (128, 256), (256, 128)], [2, 3]))
+DMA_VARIANTS = list(itertools.product([0, 1], [(128, 128), (128, 256), (256, 128)], [2, 3])) + \
+    [(0, (256, 256), 2), (1, (256, 256), 2)]     # the 8-wave tile
 
 
 @pytest.mark.parametrize("fmt", [ql.FP8_DYNAMIC, ql.W8A8_INT8])
