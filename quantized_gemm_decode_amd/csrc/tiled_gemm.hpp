@@ -203,41 +203,63 @@ __global__ void __launch_bounds__((64 * 2 * tiled_waves_n<BM, BN>())) qgemm_tile
 #pragma unroll
     for (int j = 0; j < IN; ++j) acc[i][j] = Acc{0, 0, 0, 0};
 
+  auto mma_tile = [&](const Frag& a, const Frag& b, int i, int j, const float (&sa_c)[SA_N],
+                      const float (&sw_c)[SW_N]) {
+    if constexpr (FMT == FMT_INT8) {
+      if (SWAP) {
+        acc[i][j] = mma_i8(b.lo, a.lo, acc[i][j]);
+        acc[i][j] = mma_i8(b.hi, a.hi, acc[i][j]);
+      } else {
+        acc[i][j] = mma_i8(a.lo, b.lo, acc[i][j]);
+        acc[i][j] = mma_i8(a.hi, b.hi, acc[i][j]);
+      }
+    } else if constexpr (FMT == FMT_FP8) {
+      acc[i][j] = SWAP ? mma_f8(b, a, acc[i][j]) : mma_f8(a, b, acc[i][j]);
+    } else {
+      const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+      const f32x4 part = SWAP ? mma_f8(b, a, z) : mma_f8(a, b, z);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float f = sa_c[SWAP ? i : i * 4 + r] * sw_c[j];
+        acc[i][j][r] = __builtin_fmaf(part[r], f, acc[i][j][r]);
+      }
+    }
+  };
+  // The operand with fewer fragments stays in registers for the whole K
+  // block; the other streams through, one fragment feeding a row (or
+  // column) of matrix-core instructions, so LDS reads overlap the math.
   auto compute = [&](int buf, const float (&sa_c)[SA_N], const float (&sw_c)[SW_N]) {
     const uint8_t* as = smem + buf * STAGE + (wy * IM) * 2048 + lane * 16;
     const uint8_t* bs = smem + buf * STAGE + BM * 128 + (wx * IN) * 2048 + lane * 16;
-    Frag af[IM];
+    if constexpr (IM > IN) {
+      Frag bf[IN];
 #pragma unroll
-    for (int i = 0; i < IM; ++i) {
-      af[i].lo = *reinterpret_cast<const u32x4*>(as + i * 2048);
-      af[i].hi = *reinterpret_cast<const u32x4*>(as + i * 2048 + 1024);
-    }
-#pragma unroll
-    for (int j = 0; j < IN; ++j) {
-      Frag bf;
-      bf.lo = *reinterpret_cast<const u32x4*>(bs + j * 2048);
-      bf.hi = *reinterpret_cast<const u32x4*>(bs + j * 2048 + 1024);
+      for (int j = 0; j < IN; ++j) {
+        bf[j].lo = *reinterpret_cast<const u32x4*>(bs + j * 2048);
+        bf[j].hi = *reinterpret_cast<const u32x4*>(bs + j * 2048 + 1024);
+      }
 #pragma unroll
       for (int i = 0; i < IM; ++i) {
-        if constexpr (FMT == FMT_INT8) {
-          if (SWAP) {
-            acc[i][j] = mma_i8(bf.lo, af[i].lo, acc[i][j]);
-            acc[i][j] = mma_i8(bf.hi, af[i].hi, acc[i][j]);
-          } else {
-            acc[i][j] = mma_i8(af[i].lo, bf.lo, acc[i][j]);
-            acc[i][j] = mma_i8(af[i].hi, bf.hi, acc[i][j]);
-          }
-        } else if constexpr (FMT == FMT_FP8) {
-          acc[i][j] = SWAP ? mma_f8(bf, af[i], acc[i][j]) : mma_f8(af[i], bf, acc[i][j]);
-        } else {
-          const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-          const f32x4 part = SWAP ? mma_f8(bf, af[i], z) : mma_f8(af[i], bf, z);
+        Frag af;
+        af.lo = *reinterpret_cast<const u32x4*>(as + i * 2048);
+        af.hi = *reinterpret_cast<const u32x4*>(as + i * 2048 + 1024);
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const float f = sa_c[SWAP ? i : i * 4 + r] * sw_c[j];
-            acc[i][j][r] = __builtin_fmaf(part[r], f, acc[i][j][r]);
-          }
-        }
+        for (int j = 0; j < IN; ++j) mma_tile(af, bf[j], i, j, sa_c, sw_c);
+      }
+    } else {
+      Frag af[IM];
+#pragma unroll
+      for (int i = 0; i < IM; ++i) {
+        af[i].lo = *reinterpret_cast<const u32x4*>(as + i * 2048);
+        af[i].hi = *reinterpret_cast<const u32x4*>(as + i * 2048 + 1024);
+      }
+#pragma unroll
+      for (int j = 0; j < IN; ++j) {
+        Frag bf;
+        bf.lo = *reinterpret_cast<const u32x4*>(bs + j * 2048);
+        bf.hi = *reinterpret_cast<const u32x4*>(bs + j * 2048 + 1024);
+#pragma unroll
+        for (int i = 0; i < IM; ++i) mma_tile(af[i], bf, i, j, sa_c, sw_c);
       }
     }
   };
