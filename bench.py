@@ -259,7 +259,7 @@ def parse_args(argv=None):
 def main(argv=None):
     args = parse_args(argv)
     if args.gpus != 1:
-        print("bench.py: this build measures one GPU only (--gpus %d requested); the linear shards "
+        print("bench.py measures one GPU only (--gpus %d requested); the linear shards "
               "column-wise across GPUs with no exchange, so per-GPU work is one GPU's share." % args.gpus,
               file=sys.stderr)
         return 2

@@ -71,7 +71,7 @@ typedef enum {
 typedef enum {
   QL_OK = 0,
   QL_E_INVALID = 1,        /* bad size, format, null pointer or config */
-  QL_E_UNSUPPORTED = 2,    /* valid request this build does not serve */
+  QL_E_UNSUPPORTED = 2,    /* valid request the library does not serve */
   QL_E_NO_TABLE_ENTRY = 3, /* qlinear_plan_from_table: no sweep-table entry */
   QL_E_HIP = 4,            /* a HIP runtime call or kernel launch failed */
   QL_E_ALIGN = 5,          /* pointer not 16-byte aligned */

@@ -6,7 +6,7 @@ exponent bits with bias 7, 3 mantissa bits; exponent field 0 holds subnormals
 m * 2**-9; S.1111.111 is NaN; there are no infinities; the largest finite
 magnitude is S.1111.110 = 1.75 * 2**8 = 448.
 
-Encoding rule of this build: the caller clamps to [-448, 448] first (the
+Encoding rule used here: the caller clamps to [-448, 448] first (the
 quantizer does), then the value is rounded to the nearest E4M3 value, ties to
 even.  The sign of the input (including -0.0) is kept in bit 7.
 """

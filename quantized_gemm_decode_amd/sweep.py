@@ -50,7 +50,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
-from workloads import CONFIGS, config_by_name, make_inputs  # noqa: E402
+from workloads import config_by_name, decode_workloads, make_inputs  # noqa: E402
 
 SPLITS = (1, 2, 4, 8, 16, 32)
 WAVES = ((4, 1), (2, 2), (1, 4))
@@ -281,7 +281,7 @@ def table_line(fmt, M, N, K, cfg, us, forward=False):
 
 def main(argv=None):
     ap = argparse.ArgumentParser(description="offline per-shape sweep")
-    ap.add_argument("--workloads", default=",".join(c.name for c in CONFIGS[:4]))
+    ap.add_argument("--workloads", default=",".join(c.name for c in decode_workloads()))
     ap.add_argument("--out", default=ql.DEFAULT_TABLE)
     ap.add_argument("--ms", default=None, help="comma list overriding the token counts")
     ap.add_argument("--layouts", default="0,1,2,3",

@@ -174,8 +174,8 @@ def test_packed_weight_sizes():
 
 
 def test_heuristic_plans_cover_every_decode_workload():
-    from workloads import CONFIGS, decode_points
-    for cfg in CONFIGS[:4]:
+    from workloads import decode_points, decode_workloads
+    for cfg in decode_workloads():
         for (_, N, K, M) in decode_points(cfg):
             p = ql.qlinear_plan(cfg.fmt, M, N, K)
             assert p.facts["workgroups"] >= 256

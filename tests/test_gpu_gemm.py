@@ -18,7 +18,7 @@ import oracle
 import quantized_gemm_decode_amd as ql
 from tests.gpu_util import (dev_bf16, dev_codes, dev_f32, fp8_check, host_bf16_bits, host_codes, pack_ref,
                             requires_gpu, run_gemm)
-from workloads import CONFIGS, decode_points, make_inputs, bf16_bits
+from workloads import CONFIGS, bf16_bits, config_by_name, decode_points, decode_workloads, make_inputs
 
 pytestmark = [pytest.mark.gpu, requires_gpu]
 FMTS = [ql.FP8_DYNAMIC, ql.W8A8_INT8, ql.BLOCK_FP8]
@@ -308,35 +308,35 @@ def test_graph_capture_replays_match_eager(fmt):
 
 def _full_points():
     pts = []
-    for ci, cfg in enumerate(CONFIGS[:4]):
+    for cfg in decode_workloads():
         for (lab, N, K, M) in decode_points(cfg):
-            if ci == 0 or M in (1, 8, 32) or (ci == 1 and lab == "o"):
-                pts.append((ci, lab, N, K, M))
+            if len(cfg.shapes) == 1 or M in (1, 8, 32) or (cfg.name == "fp8_dynamic_8b" and lab == "o"):
+                pts.append((cfg.name, lab, N, K, M))
     return pts
 
 
 _W_CACHE = {}
 
 
-def _weights(ci, lab, N, K):
-    key = (ci, lab)
+def _weights(wname, lab, N, K):
+    key = (wname, lab)
     if key not in _W_CACHE:
         _W_CACHE.clear()
-        cfg = CONFIGS[ci]
+        cfg = config_by_name(wname)
         x, w = make_inputs(K, N, max(cfg.ms), cfg.sigma_w, seed=cfg.seed)
         w_q, w_s = ql.quantize_weight(cfg.fmt, w.cuda())
         _W_CACHE[key] = (x, w, w_q, w_s)
     return _W_CACHE[key]
 
 
-@pytest.mark.parametrize("ci,lab,N,K,M", _full_points())
-def test_full_size_workloads_sampled_columns(ci, lab, N, K, M):
+@pytest.mark.parametrize("wname,lab,N,K,M", _full_points())
+def test_full_size_workloads_sampled_columns(wname, lab, N, K, M):
     """Configured workloads at full size with the plan the bench uses; the
     oracle recomputes sampled output columns one by one (it quantizes just the
     weight rows, or 128-row blocks, those columns need)."""
-    fmt = CONFIGS[ci].fmt
+    fmt = config_by_name(wname).fmt
     ql.load_default_table()
-    x, w, w_q, w_s = _weights(ci, lab, N, K)
+    x, w, w_q, w_s = _weights(wname, lab, N, K)
     xm = x[:M]
     a_q, a_s = ql.quantize_act(fmt, xm.cuda())
     a_p, _ = ql.quantize_act_packed(fmt, xm.cuda())
@@ -348,7 +348,7 @@ def test_full_size_workloads_sampled_columns(ci, lab, N, K, M):
         ql.qlinear_run(plan, a_p if a_packed else a_q, a_s, w_p if w_layout else w_q, w_s, y, plan.new_workspace())
         torch.cuda.synchronize()
         ys.append((plan, host_bf16_bits(y)))
-    rng = np.random.default_rng(ci * 1000 + M)
+    rng = np.random.default_rng(sum(map(ord, wname)) * 1000 + M)
     if fmt == ql.BLOCK_FP8:
         nbs = rng.choice(-(-N // 128), 2, replace=False)
         cols = np.concatenate([np.arange(nb * 128, min(N, nb * 128 + 128)) for nb in nbs])
@@ -384,12 +384,12 @@ _TABLE_FIELDS = ("algo", "swap_ab", "split_k", "waves_n", "waves_k", "rows_per_w
 
 
 def _shape_config(fmt, N, K):
-    for ci, cfg in enumerate(CONFIGS):
+    for cfg in CONFIGS:
         if cfg.fmt != fmt:
             continue
         for (lab, n, k) in cfg.shapes:
             if (n, k) == (N, K):
-                return ci, lab
+                return cfg.name, lab
     raise KeyError((fmt, N, K))
 
 
@@ -401,8 +401,8 @@ def test_every_table_entry_matches_oracle(entry):
     (forward entries through qlinear_forward, which also quantizes)."""
     fmt, M, N, K = entry[:4]
     cfg = dict(zip(_TABLE_FIELDS, entry[4:16]))
-    ci, lab = _shape_config(fmt, N, K)
-    x, w, w_q, w_s = _weights(ci, lab, N, K)
+    wname, lab = _shape_config(fmt, N, K)
+    x, w, w_q, w_s = _weights(wname, lab, N, K)
     xm = x[:M]
     a_q, a_s = ql.quantize_act(fmt, xm.cuda())
     plan = ql.qlinear_plan_with_config(fmt, M, N, K, cfg)

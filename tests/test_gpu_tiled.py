@@ -17,7 +17,7 @@ import oracle
 import quantized_gemm_decode_amd as ql
 from tests.gpu_util import dev_codes, dev_f32, fp8_check, host_bf16_bits, host_codes, requires_gpu, run_gemm
 from tests.test_gpu_gemm import _assert_parity, _dev_packed_act
-from workloads import CONFIGS, bf16_bits, make_inputs
+from workloads import bf16_bits, config_by_name, make_inputs
 
 pytestmark = [pytest.mark.gpu, requires_gpu]
 FMTS = [ql.FP8_DYNAMIC, ql.W8A8_INT8, ql.BLOCK_FP8]
@@ -108,7 +108,7 @@ def test_planner_routes_large_m_to_the_tiled_algorithm():
 
 
 def _large_points():
-    cfg = CONFIGS[4]
+    cfg = config_by_name("fp8_dynamic_14b_large_m")
     pts = []
     for (lab, N, K) in cfg.shapes:
         for M in cfg.ms:
@@ -126,7 +126,7 @@ def test_large_m_workloads_sampled_columns(lab, N, K, M):
     """14B-class FP8 shapes at full size with the planner's configuration
     (packed weights and activations; tiled, or at M = 64 possibly the
     weight-streaming kernel); the oracle recomputes 64 sampled output columns."""
-    cfg = CONFIGS[4]
+    cfg = config_by_name("fp8_dynamic_14b_large_m")
     fmt = cfg.fmt
     key = (lab, N, K)
     if key not in _LARGE:

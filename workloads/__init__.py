@@ -6,7 +6,7 @@ of bf16 activations and weights.  Both the CPU oracle and the GPU path take
 their inputs from here.
 """
 
-from .configs import CONFIGS, Workload, decode_points, config_by_name
+from .configs import CONFIGS, Workload, config_by_name, decode_points, decode_workloads
 from .synth import make_inputs, bf16_bits
 
-__all__ = ["CONFIGS", "Workload", "decode_points", "config_by_name", "make_inputs", "bf16_bits"]
+__all__ = ["CONFIGS", "Workload", "config_by_name", "decode_points", "decode_workloads", "make_inputs", "bf16_bits"]

@@ -43,6 +43,11 @@ CONFIGS = (
 )
 
 
+def decode_workloads():
+    """The workloads whose token counts stay within the decode range (M <= 32)."""
+    return [c for c in CONFIGS if max(c.ms) <= 32]
+
+
 def config_by_name(name):
     for c in CONFIGS:
         if c.name == name:
