@@ -115,11 +115,12 @@ typedef struct {
                             A_q chunk staged in LDS; 2 = packed A_q (qlinear_quantize_act_packed)
                             read per K block; 3 (DECODE) = packed A_q chunk staged in LDS and
                             shared by the workgroup's waves; 4 (DECODE) = fused quantization:
-                            every workgroup quantizes the bf16 rows of X itself (row amax,
-                            then the codes of its K chunk into LDS) and the plan runs only
-                            through qlinear_forward, which then writes a_q (packed) and
-                            a_scale from inside the GEMM launch -- per-token formats,
-                            M <= 16, M*K <= 16384, K % 512 == 0.  2..4 need packed weights */
+                            every workgroup quantizes the bf16 rows of X itself (row or
+                            1x128-group amax, then the codes of its K chunk into LDS) and the
+                            plan runs only through qlinear_forward, which then writes a_q
+                            (packed) and a_scale from inside the GEMM launch -- M <= 16;
+                            per-token formats: M*K <= 16384, K % 512 == 0; Block_FP8:
+                            M * (K chunk) <= 16384.  2..4 need packed weights */
   int32_t w_lds;         /* DECODE, row-major weights: 1 = coalesced weight loads (8 rows x 128 B
                             per instruction) transposed to the matrix-core layout through LDS;
                             0 = direct loads in operand order.  TILED, packed weights and

@@ -261,12 +261,9 @@ ql_status build_plan(int32_t fmt, int64_t M, int64_t N, int64_t K, const ql_conf
   if (cfg.prefetch != 1 && cfg.prefetch != 2 && cfg.prefetch != 4) return fail(QL_E_INVALID, "prefetch must be 1, 2 or 4");
   if (cfg.a_mode < 0 || cfg.a_mode > 4) return fail(QL_E_INVALID, "a_mode must be 0, 1, 2, 3 or 4");
   if (cfg.a_mode >= 2 && !cfg.w_layout) return fail(QL_E_UNSUPPORTED, "packed activations need packed weights");
-  if (cfg.a_mode == 4) {
-    if (fmt == QL_BLOCK_FP8) return fail(QL_E_UNSUPPORTED, "fused quantization serves the per-token formats");
-    if (M > 16 || M * K > kFusedMaxValues || K % 512)
-      return fail(QL_E_UNSUPPORTED, "fused quantization needs M <= 16, M*K <= %lld and K %% 512 == 0",
-                  (long long)kFusedMaxValues);
-  }
+  if (cfg.a_mode == 4 && fmt != QL_BLOCK_FP8 && (M > 16 || M * K > kFusedMaxValues || K % 512))
+    return fail(QL_E_UNSUPPORTED, "fused per-token quantization needs M <= 16, M*K <= %lld and K %% 512 == 0",
+                (long long)kFusedMaxValues);
   if (cfg.a_mode >= 2 && qlinear_packed_act_bytes(M, K) > (int64_t(1) << 30))
     return fail(QL_E_UNSUPPORTED, "packed activations exceed 2^30 bytes");
   if (cfg.w_lds != 0 && cfg.w_lds != 1) return fail(QL_E_INVALID, "w_lds must be 0 or 1");
@@ -285,12 +282,20 @@ ql_status build_plan(int32_t fmt, int64_t M, int64_t N, int64_t K, const ql_conf
   p->chunk_kb = p->G > 0 ? (p->G + split - 1) / split : 0;
   p->chunks = p->G > 0 ? (p->G + p->chunk_kb - 1) / p->chunk_kb : 1;
   p->mt = M <= 16 ? 1 : (M <= 32 ? 2 : 4);
+  // Block_FP8 fused quantization reads only its K chunk: M * chunk values
+  if (cfg.a_mode == 4 && fmt == QL_BLOCK_FP8 && (M > 16 || M * p->chunk_kb * 128 > kFusedMaxValues)) {
+    const long long chunk = (long long)p->chunk_kb * 128;
+    delete p;
+    return fail(QL_E_UNSUPPORTED, "fused group quantization needs M <= 16 and M * chunk <= %lld (chunk %lld)",
+                (long long)kFusedMaxValues, chunk);
+  }
   const int rg = cfg.rows_per_wave / 16;
   p->bn = cfg.waves_n * rg * 16;
   p->n_tiles = (int)((N + p->bn - 1) / p->bn);
   const int64_t lds_a = (cfg.a_mode == 1 || cfg.a_mode == 3) ? (int64_t)p->chunk_kb * p->mt * 2048
-                       : cfg.a_mode == 4                    ? 512 + M * ((int64_t)p->chunk_kb * 128 + 64)
-                                                            : 0;
+                       : cfg.a_mode == 4 ? 512 + M * ((int64_t)p->chunk_kb * 128 + 64) +
+                                               (fmt == QL_BLOCK_FP8 ? M * (int64_t)p->chunk_kb * 4 : 0)
+                                         : 0;
   const int64_t lds_w = (cfg.w_lds && !cfg.w_layout) ? (int64_t)nw * 2 * rg * 2048 : 0;
   const int64_t lds_red = cfg.waves_k > 1 ? (int64_t)nw * rg * p->mt * 1024 : 0;
   p->lds = std::max(lds_a + lds_w, lds_red);

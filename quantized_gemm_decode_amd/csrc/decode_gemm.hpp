@@ -71,7 +71,7 @@ __global__ void __launch_bounds__(NW * 64) qgemm_decode_kernel(DecodeArgs p) {
   constexpr bool AP = AL == 2;                        // packed activations, read per K block like packed weights
   constexpr bool WL = WM == W_LDS_TRANSPOSE;
   constexpr bool WP = WM == W_PACKED;
-  static_assert(!FUSED || (MT == 1 && WP && FMT != FMT_BLOCK), "fused quantization: per-token formats, M <= 16");
+  static_assert(!FUSED || (MT == 1 && WP), "fused quantization: one token tile, packed weights");
   using Acc = typename AccOf<FMT>::T;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   __shared__ int s_last;
@@ -152,9 +152,11 @@ __global__ void __launch_bounds__(NW * 64) qgemm_decode_kernel(DecodeArgs p) {
   // 16 tokens at FA_SC, a 16-byte zero slot at FA_ZERO, then
   // the codes of token m at FA0 + m*CH for this chunk's K range.  CH adds 64
   // bytes to the chunk so consecutive tokens start 16 banks apart.  Lanes of
-  // tokens >= M read the zero slot for every K block.
+  // tokens >= M read the zero slot for every K block.  Block_FP8 keeps its
+  // group scales s_a[m, kb0 + kbl] after the codes, at FA_SB + (m*chunk_kb + kbl)*4.
   constexpr int FA_RED = 0, FA_SC = 256, FA_ZERO = 384, FA0 = 512;
   const int CH = p.chunk_kb * 128 + 64;
+  const int FA_SB = FA0 + p.M * CH;
   const bool real_tok = (uint32_t)r16 < M;
   const int fa_lane = real_tok ? FA0 + r16 * CH + g * 16 : FA_ZERO;
   const int fa_step = real_tok ? 128 : 0;
@@ -236,7 +238,10 @@ __global__ void __launch_bounds__(NW * 64) qgemm_decode_kernel(DecodeArgs p) {
 #pragma unroll
           for (int r = 0; r < (SWAP ? 1 : 4); ++r) {
             const uint32_t m = SWAP ? (uint32_t)(mt * 16 + r16) : (uint32_t)(mt * 16 + 4 * g + r);
-            sab[q][mt][r] = bload_f32(rsa, (ok && m < M) ? (m * Gu + (uint32_t)kb) * 4u : OOB);
+            if constexpr (FUSED)
+              sab[q][mt][r] = 0.f;   // read from LDS when consumed
+            else
+              sab[q][mt][r] = bload_f32(rsa, (ok && m < M) ? (m * Gu + (uint32_t)kb) * 4u : OOB);
           }
         }
 #pragma unroll
@@ -261,6 +266,15 @@ __global__ void __launch_bounds__(NW * 64) qgemm_decode_kernel(DecodeArgs p) {
         const uint8_t* base = smem + fa_lane + kbl * fa_step;
         af[0].lo = *reinterpret_cast<const u32x4*>(base);
         af[0].hi = *reinterpret_cast<const u32x4*>(base + fa_hi);
+        if constexpr (FMT == FMT_BLOCK) {
+#pragma unroll
+          for (int r = 0; r < (SWAP ? 1 : 4); ++r) {
+            const uint32_t m = SWAP ? (uint32_t)r16 : (uint32_t)(4 * g + r);
+            sab[q][0][r] = (j < nkw && m < M)
+                               ? reinterpret_cast<const float*>(smem + FA_SB)[m * (uint32_t)p.chunk_kb + (uint32_t)kbl]
+                               : 0.f;
+          }
+        }
       } else if constexpr (ALDS) {
         const int j = batch * PF + q;
         const int kbl = j < nkw ? wk + j * WK : 0;
@@ -314,8 +328,10 @@ __global__ void __launch_bounds__(NW * 64) qgemm_decode_kernel(DecodeArgs p) {
             const f32x4 part = SWAP ? mma_f8(wf[rg], af[mt], z) : mma_f8(af[mt], wf[rg], z);
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-              const float f = sab[q][mt][SWAP ? 0 : r] * swb[q][rg];
-              acc[rg][mt][r] = __builtin_fmaf(part[r], f, acc[rg][mt][r]);
+              // (P_g * s_a) * s_w: the group sum meets the activation scale
+              // first, so a tiny s_a cannot underflow a product of scales
+              const float t = __fmul_rn(part[r], sab[q][mt][SWAP ? 0 : r]);
+              acc[rg][mt][r] = __builtin_fmaf(t, swb[q][rg], acc[rg][mt][r]);
             }
           }
         }
@@ -358,16 +374,27 @@ __global__ void __launch_bounds__(NW * 64) qgemm_decode_kernel(DecodeArgs p) {
   // multiple of 512 each wave's 64 consecutive 16-byte pieces (one load
   // instruction) lie in one token row; the workgroup holds XP pieces a lane,
   // 16384 values in all.
+  // Block_FP8 needs only this chunk's K range (its 1 x 128 groups are
+  // local): pieces run row by row over the chunk, nkc*16 a row, and the 16
+  // lanes of a row of the wave hold one group.
   constexpr int XP = FUSED ? 32 / NW : 1;
   u32x4 xv[XP];
-  const uint32_t upr = K / 512u;  // wave pieces per token row
+  const uint32_t upr = K / 512u;                 // per-token: wave pieces per token row
+  const uint32_t ppr = (uint32_t)nkc * 16u;      // Block_FP8: pieces per row of the chunk
   if constexpr (FUSED) {
     const __amdgpu_buffer_rsrc_t rx = make_rsrc(p.x, M * K * 2u);
-    const uint32_t npc = M * K / 8u;
+    const uint32_t npc = FMT == FMT_BLOCK ? M * ppr : M * K / 8u;
 #pragma unroll
     for (int i = 0; i < XP; ++i) {
       const uint32_t P = (uint32_t)(tid + NW * 64 * i);
-      xv[i] = bload16(rx, P < npc ? P * 16u : OOB);
+      uint32_t off;
+      if constexpr (FMT == FMT_BLOCK) {
+        const uint32_t m = P / ppr, w = P - m * ppr;
+        off = (m * K + (uint32_t)kb0 * 128u + w * 8u) * 2u;
+      } else {
+        off = P * 16u;
+      }
+      xv[i] = bload16(rx, P < npc ? off : OOB);
     }
     if (tid < 4) reinterpret_cast<uint32_t*>(smem + FA_ZERO)[tid] = 0u;
     __builtin_amdgcn_sched_barrier(0);
@@ -383,7 +410,32 @@ __global__ void __launch_bounds__(NW * 64) qgemm_decode_kernel(DecodeArgs p) {
   // amax (each wave's partial, then the row's partials), s = fl(amax/Q) and
   // fl(1/s) in every wave that holds a piece of the row, and the codes of
   // this chunk's K range into LDS.
-  if constexpr (FUSED) {
+  if constexpr (FUSED && FMT == FMT_BLOCK) {
+    // weight loads and weight-scale loads of the two batches, issued after X
+    constexpr int NW_LOADS = 2 * PF * 3 * RG;
+    static_assert(NW_LOADS <= 63, "vmcnt holds 6 bits");
+    __builtin_amdgcn_s_waitcnt((NW_LOADS & 15) | (7 << 4) | (15 << 8) | ((NW_LOADS >> 4) << 14));
+    float* ssb = reinterpret_cast<float*>(smem + FA_SB);
+    const uint32_t npc = M * ppr;
+#pragma unroll
+    for (int i = 0; i < XP; ++i) {
+      const uint32_t P = (uint32_t)(tid + NW * 64 * i);
+      const float gmax = row16_max_nonneg(abs_bf16_max8(xv[i], 0.0f));
+      if (P < npc) {
+        const uint32_t m = P / ppr, w = P - m * ppr;
+        const float sc = scale_of<FMT>(gmax);
+        *reinterpret_cast<u32x2*>(smem + FA0 + m * (uint32_t)CH + w * 8u) = quant8<FMT>(xv[i], sc, recip_of(sc));
+        if ((w & 15u) == 0u) ssb[m * (uint32_t)p.chunk_kb + (w >> 4)] = sc;
+      }
+    }
+    lds_barrier();
+    if (p.aq_out && tile == 0) {
+      for (uint32_t v = (uint32_t)tid; v < M * (uint32_t)nkc; v += (uint32_t)(NW * 64)) {
+        const uint32_t m = v / (uint32_t)nkc, kbl = v - m * (uint32_t)nkc;
+        p.sa_out[m * (uint32_t)p.G + (uint32_t)kb0 + kbl] = ssb[m * (uint32_t)p.chunk_kb + kbl];
+      }
+    }
+  } else if constexpr (FUSED) {
     constexpr int NW_LOADS = 2 * PF * 2 * RG;  // weight loads of the two batches, issued after X
     static_assert(NW_LOADS <= 63, "vmcnt holds 6 bits");
     __builtin_amdgcn_s_waitcnt((NW_LOADS & 15) | (7 << 4) | (15 << 8) | ((NW_LOADS >> 4) << 14));
@@ -414,9 +466,12 @@ __global__ void __launch_bounds__(NW * 64) qgemm_decode_kernel(DecodeArgs p) {
       }
     }
     lds_barrier();
-    // The codes and scales leave the kernel as the standalone quantizer
-    // writes them: this chunk's packed tiles (token tile 0; rows >= M zero)
-    // spread over the chunk's workgroups, and s_a from the first workgroup.
+    if (p.aq_out && tile == 0 && chunk == 0 && (uint32_t)tid < M) p.sa_out[tid] = ssc[tid];
+  }
+  // The codes leave the kernel as the standalone quantizer writes them: this
+  // chunk's packed tiles (token tile 0; rows >= M zero), spread over the
+  // chunk's workgroups.  (The scales were written above.)
+  if constexpr (FUSED) {
     if (p.aq_out) {
       const uint32_t nunits = (uint32_t)nkc * 128u;  // 16-byte units: K block x half x lane
       for (uint32_t u = (uint32_t)(tile * NW * 64 + tid); u < nunits; u += (uint32_t)(p.n_tiles * NW * 64)) {
@@ -427,7 +482,6 @@ __global__ void __launch_bounds__(NW * 64) qgemm_decode_kernel(DecodeArgs p) {
         if (row < M) v = *reinterpret_cast<const u32x4*>(smem + FA0 + row * (uint32_t)CH + k);
         *reinterpret_cast<u32x4*>(p.aq_out + (size_t)((uint32_t)kb0 + kbl) * 2048u + h * 1024u + l * 16u) = v;
       }
-      if (tile == 0 && chunk == 0 && (uint32_t)tid < M) p.sa_out[tid] = ssc[tid];
     }
   }
 
@@ -642,11 +696,11 @@ constexpr bool decode_config_fits() {
 }
 
 // Fused quantization adds 32/NW 16-byte X pieces a lane to the buffers in
-// flight; it serves one token tile, packed weights and the per-token formats.
+// flight; it serves one token tile and packed weights.
 template <int FMT, int NW_, int SW, int MT_, int RG_, int PF_, int AL, int WM_>
 constexpr bool decode_variant_ok() {
   if constexpr (AL == 4) {
-    if (MT_ != 1 || WM_ != W_PACKED || FMT == FMT_BLOCK) return false;
+    if (MT_ != 1 || WM_ != W_PACKED) return false;
     const int estimate = 2 * PF_ * (RG_ + MT_) * 8 + RG_ * MT_ * 4 + 40 + 4 * (32 / NW_);
     return estimate <= (NW_ >= 16 ? 128 : 256) && decode_config_fits<FMT, NW_, SW, MT_, RG_, PF_>();
   }

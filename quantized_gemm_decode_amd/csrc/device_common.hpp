@@ -149,15 +149,22 @@ __device__ __forceinline__ float wave_max(float v) {
   return v;
 }
 
-// Maximum over the wave of non-negative values, returned wave-uniform: DPP
-// lane swaps inside each row of 16 (xor 1, xor 2 by quad permutation, then
-// the half-row and row mirrors), then the four row results by readlane.
-__device__ __forceinline__ float wave_max_nonneg(float v) {
+// Maximum of non-negative values over each row of 16 lanes (lanes 16a ..
+// 16a+15), returned to every lane of the row: DPP lane swaps (xor 1, xor 2
+// by quad permutation, then the half-row and row mirrors).
+__device__ __forceinline__ float row16_max_nonneg(float v) {
   v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xf, 0xf, false)));
   v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xf, 0xf, false)));
   v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xf, 0xf, false)));
   v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x140, 0xf, 0xf, false)));
-  const int b = __float_as_int(v);
+  return v;
+}
+
+// Maximum over the wave of non-negative values, returned wave-uniform: DPP
+// lane swaps inside each row of 16 (xor 1, xor 2 by quad permutation, then
+// the half-row and row mirrors), then the four row results by readlane.
+__device__ __forceinline__ float wave_max_nonneg(float v) {
+  const int b = __float_as_int(row16_max_nonneg(v));
   return fmaxf(fmaxf(__int_as_float(__builtin_amdgcn_readlane(b, 0)), __int_as_float(__builtin_amdgcn_readlane(b, 16))),
                fmaxf(__int_as_float(__builtin_amdgcn_readlane(b, 32)), __int_as_float(__builtin_amdgcn_readlane(b, 48))));
 }

@@ -220,8 +220,9 @@ __global__ void __launch_bounds__((64 * 2 * tiled_waves_n<BM, BN>())) qgemm_tile
       const f32x4 part = SWAP ? mma_f8(b, a, z) : mma_f8(a, b, z);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const float f = sa_c[SWAP ? i : i * 4 + r] * sw_c[j];
-        acc[i][j][r] = __builtin_fmaf(part[r], f, acc[i][j][r]);
+        // (P_g * s_a) * s_w, as in the decode kernel
+        const float t = __fmul_rn(part[r], sa_c[SWAP ? i : i * 4 + r]);
+        acc[i][j][r] = __builtin_fmaf(t, sw_c[j], acc[i][j][r]);
       }
     }
   };

@@ -82,8 +82,11 @@ def tiled_candidates(M, N, K, layout):
 
 
 def fused_ok(fmt, M, K):
-    """Shapes the fused-quantization decode kernel serves."""
-    return fmt != ql.BLOCK_FP8 and M <= 16 and M * K <= 16384 and K % 512 == 0
+    """Shapes the fused-quantization decode kernel can serve (Block_FP8: with a
+    large enough split; the planner rejects the candidates that do not fit)."""
+    if fmt == ql.BLOCK_FP8:
+        return M <= 16
+    return M <= 16 and M * K <= 16384 and K % 512 == 0
 
 
 def decode_m64_candidates(M, N, K, layout):

@@ -185,7 +185,10 @@ def test_fused_quantization_plans_are_validated_on_host():
     fused = dict(w_layout=1, a_mode=4, waves_n=1, waves_k=4)
     assert _plan_status(ql.FP8_DYNAMIC, 4, 4096, 4096, **fused) == QL_OK
     assert _plan_status(ql.W8A8_INT8, 1, 4096, 12288, **fused) == QL_OK
-    assert _plan_status(ql.BLOCK_FP8, 1, 4096, 4096, **fused) == QL_E_UNSUPPORTED    # per-token formats only
+    assert _plan_status(ql.BLOCK_FP8, 1, 4096, 4096, **fused) == QL_OK
+    assert _plan_status(ql.BLOCK_FP8, 16, 4096, 4096, **fused) == QL_E_UNSUPPORTED  # 16 x 4096 > 16384 ...
+    assert _plan_status(ql.BLOCK_FP8, 16, 4096, 4096, split_k=4, **fused) == QL_OK  # ... a 1024-wide chunk fits
+    assert _plan_status(ql.BLOCK_FP8, 17, 4096, 4096, split_k=8, **fused) == QL_E_UNSUPPORTED
     assert _plan_status(ql.FP8_DYNAMIC, 8, 4096, 4096, **fused) == QL_E_UNSUPPORTED  # M*K > 16384
     assert _plan_status(ql.FP8_DYNAMIC, 17, 4096, 512, **fused) == QL_E_UNSUPPORTED  # one token tile
     assert _plan_status(ql.FP8_DYNAMIC, 1, 4096, 4352, **fused) == QL_E_UNSUPPORTED  # K % 512

@@ -1,4 +1,5 @@
-"""GPU parity of the decode GEMM with fused activation quantization (a_mode 4).
+"""GPU parity of the decode GEMM with fused activation quantization (a_mode 4):
+per-token amax for FP8_Dynamic and INT8, per 1 x 128 group for Block_FP8.
 
 One launch reads bf16 X, quantizes it inside every workgroup and runs the
 GEMM.  What it writes out must be exactly what the two-launch path writes:
@@ -18,7 +19,7 @@ from tests.gpu_util import dev_bf16, fp8_check, host_bf16_bits, pack_ref, requir
 from workloads import bf16_bits, make_inputs
 
 pytestmark = [pytest.mark.gpu, requires_gpu]
-FMTS = [ql.FP8_DYNAMIC, ql.W8A8_INT8]
+FMTS = [ql.FP8_DYNAMIC, ql.W8A8_INT8, ql.BLOCK_FP8]
 
 # waves per workgroup x waves sharing K x rows per wave x batch x swap
 FVARIANTS = [v for v in itertools.product([4, 8, 16], [1, 2, 4, 8, 16], [16, 32, 64], [1, 2, 4], [0, 1])
