@@ -72,32 +72,12 @@ __device__ __forceinline__ uint32_t bf16_rne(float f) {
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
 
-// binary32 in [-448, 448] -> OCP E4M3 code, round to nearest even.
-// Below 2^-6 every E4M3 value is a multiple of 2^-9 (subnormals; code 8 is
-// the smallest normal), so scaling by 2^9 and rounding to an integer gives
-// the code directly.  Above, keep 3 mantissa bits with round-half-even on
-// the 20 dropped bits and rebias the exponent from 127 to 7.
-__device__ __forceinline__ uint32_t e4m3_rne(float v) {
-  uint32_t u = __float_as_uint(v);
-  uint32_t sign = (u >> 24) & 0x80u;
-  uint32_t a = u & 0x7fffffffu;
-  float af = __uint_as_float(a);
-  uint32_t code;
-  if (af < 0.015625f) {
-    code = (uint32_t)__builtin_rintf(af * 512.0f);
-  } else {
-    uint32_t r = a + 0x7ffffu + ((a >> 20) & 1u);
-    code = (r >> 20) - (120u << 3);
-  }
-  return code | sign;
-}
-
 // Two E4M3 codes by the conversion instruction (v_cvt_pk_fp8_f32): a and b,
 // already clamped to [-448, 448], rounded to nearest even, into byte 0 / 1
-// (HI = false) or byte 2 / 3 (HI = true) of `old`.  It agrees with e4m3_rne
-// on every clamped input, signed zeros and subnormal results included: the
-// GPU tests compare it with the oracle's encoder around every rounding
-// midpoint and on every bf16 value.
+// (HI = false) or byte 2 / 3 (HI = true) of `old`.  It agrees with the OCP
+// E4M3 definition on every clamped input, signed zeros and subnormal results
+// included: the GPU tests compare it with the oracle's encoder around every
+// rounding midpoint and on every bf16 value.
 template <bool HI>
 __device__ __forceinline__ uint32_t e4m3_pk2(float a, float b, uint32_t old) {
   return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, (int)old, HI);
@@ -105,17 +85,11 @@ __device__ __forceinline__ uint32_t e4m3_pk2(float a, float b, uint32_t old) {
 
 __device__ __forceinline__ float clamp448(float t) { return __builtin_amdgcn_fmed3f(t, -448.0f, 448.0f); }
 
-// Round-to-code of an already divided value t (round + clamp).
-template <int FMT>
-__device__ __forceinline__ uint32_t code_of(float t) {
-  if (FMT == FMT_INT8) {
-    float q = __builtin_rintf(t);
-    q = fminf(fmaxf(q, -127.0f), 127.0f);
-    return (uint32_t)((int)q) & 0xffu;
-  } else {
-    t = fminf(fmaxf(t, -448.0f), 448.0f);
-    return e4m3_rne(t);
-  }
+// int8 code of an already divided value t: round half to even, clamp to +-127.
+__device__ __forceinline__ uint32_t int8_code(float t) {
+  float q = __builtin_rintf(t);
+  q = fminf(fmaxf(q, -127.0f), 127.0f);
+  return (uint32_t)((int)q) & 0xffu;
 }
 
 // fl(x / s) at the code level from r = fl(1/s), with one multiply and two
@@ -141,12 +115,6 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-}
-
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
-  return v;
 }
 
 // Maximum of non-negative values over each row of 16 lanes (lanes 16a ..

@@ -111,7 +111,8 @@ __global__ void __launch_bounds__(QT) quant_rows_stream_kernel(const uint16_t* _
 
 // Block_FP8 activations: groups of 128 contiguous elements along K (K % 128
 // == 0, so group id = m * K/128 + g is also the s_a index); 16 lanes per
-// group, 8 elements per lane; the group amax reduces over the 16 lanes.
+// group, 8 elements per lane; the group amax reduces over the 16 lanes (one
+// DPP row: groups start at multiples of 16 lanes).
 // PACKED: codes in the packed activation layout; groups of the padding rows
 // (up to a multiple of 16 rows, `ngroups_out` in all) get zero codes.
 template <bool PACKED>
@@ -123,9 +124,7 @@ __global__ void __launch_bounds__(QT) quant_groups_kernel(const uint16_t* __rest
   const bool ok = gid < ngroups;
   const size_t e = (size_t)gid * 128u + li * 8u;
   const u32x4 v = ok ? *reinterpret_cast<const u32x4*>(x + e) : u32x4{0, 0, 0, 0};
-  float amax = abs_bf16_max8(v, 0.0f);
-#pragma unroll
-  for (int o = 8; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));
+  const float amax = row16_max_nonneg(abs_bf16_max8(v, 0.0f));   // the group's 16 lanes are a DPP row
   const float sc = scale_of<FMT_FP8>(amax);
   if (gid < (PACKED ? ngroups_out : ngroups)) {
     const size_t off = PACKED ? packed_offset(gid / G, (gid % G) * 128u + li * 8u, G) : e;

@@ -46,7 +46,7 @@ __device__ __forceinline__ u32x2 quant8(const u32x4& v, float s, float r) {
   if constexpr (FMT == FMT_INT8) {
     uint32_t c[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) c[i] = code_of<FMT_INT8>(t[i]);
+    for (int i = 0; i < 8; ++i) c[i] = int8_code(t[i]);
     u32x2 out = {c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24), c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24)};
     return out;
   } else {
