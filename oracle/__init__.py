@@ -6,7 +6,8 @@ GPU path computes:
     Y[M,N] = s_a[m] * s_w[n] * (A_q[M,K] . W_q[N,K]^T)      (bf16 output)
 
 plus the dynamic activation quantizer and the offline weight quantizer, for
-the three formats of the pages (FP8_Dynamic, W8A8_INT8, Block_FP8).
+the three formats of the pages (FP8_Dynamic, W8A8_INT8, Block_FP8), and the
+SiLU-and-mul epilogue of a merged gate/up projection (``glu``).
 
 Who may use it: only ``tests/``, ``__graft_entry__.smoke()`` and the
 ``cpu_baseline`` leg of ``bench.py``.  The product path (the HIP library and
@@ -40,6 +41,7 @@ from .linear import (contract_exact, contract_abs, epilogue, reference, MATRIX_C
                      tolerance_bound, summation_depth, check_fp8_parity,
                      contract_split_order, contract_swap_ab,
                      emulate_fp32_accumulation)
+from .glu import silu, glu_values, glu_reference, SILU_SLOPE_MAX
 
 __all__ = [
     "bf16_bits_from_f32", "bf16_bits_to_f32", "ulp_bf16", "f32",
@@ -48,5 +50,6 @@ __all__ = [
     "qmax_of", "quantize_act", "quantize_weight", "dequant_codes",
     "contract_exact", "contract_abs", "epilogue", "reference",
     "tolerance_bound", "summation_depth", "MATRIX_CORE_ETA", "check_fp8_parity",
+    "silu", "glu_values", "glu_reference", "SILU_SLOPE_MAX",
     "contract_split_order", "contract_swap_ab", "emulate_fp32_accumulation",
 ]
