@@ -145,6 +145,7 @@ typedef struct {
   int32_t threads;         /* threads per workgroup */
   int32_t lds_bytes;       /* dynamic LDS per workgroup */
   int64_t workspace_bytes; /* see qlinear_workspace_bytes */
+  int32_t epilogue;        /* 0 = Y [M, N]; 1 = SiLU-and-mul of a merged gate/up weight, Y [M, N/2] */
 } ql_plan_facts;
 
 typedef struct ql_plan_s* ql_plan;
@@ -258,6 +259,23 @@ ql_status qlinear_plan_from_table(int32_t fmt, int64_t M, int64_t N, int64_t K, 
 /* Plan with an explicit configuration (validated; QL_E_INVALID / QL_E_UNSUPPORTED on a bad one). */
 ql_status qlinear_plan_with_config(int32_t fmt, int64_t M, int64_t N, int64_t K,
                                    const ql_config* cfg, ql_plan* out_plan);
+/*
+ * SiLU-and-mul epilogue ([Deep dive] "Understanding Helion": activations
+ * such as SiLU fused into the GEMM's write-back).  The weight [N, K] is a
+ * merged gate/up projection -- rows [0, N/2) gate, rows [N/2, N) up -- and
+ * the plan's runs write, instead of the linear's output, the [M, N/2] bf16
+ * tensor H[m, i] = bf16(silu(g) * u) with g, u the binary32 epilogue values
+ * of output columns i and N/2 + i (after the scales, before any rounding),
+ * silu(g) = g / (1 + exp(-g)).  Decode algorithm only (M <= 32), packed
+ * weights, N % 32 == 0; qlinear_run (a_packed 1) or qlinear_forward
+ * (a_packed 2: the quantizer may be fused as well) drive it as usual with
+ * y_bf16 [M, N/2].  qlinear_plan_glu starts from the merged linear's planned
+ * configuration (table or heuristic) and keeps 32 rows a wave (a gate and an
+ * up group); qlinear_run_debug_acc rejects these plans.
+ */
+ql_status qlinear_plan_glu(int32_t fmt, int64_t M, int64_t N, int64_t K, int32_t a_packed, ql_plan* out_plan);
+ql_status qlinear_plan_glu_with_config(int32_t fmt, int64_t M, int64_t N, int64_t K, const ql_config* cfg,
+                                       ql_plan* out_plan);
 /* Effective configuration and launch facts of a plan (either pointer may be NULL). */
 ql_status qlinear_plan_info(ql_plan plan, ql_config* cfg, ql_plan_facts* facts);
 /*

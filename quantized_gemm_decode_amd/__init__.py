@@ -250,6 +250,23 @@ def qlinear_plan_layouts(fmt, M, N, K, w_layout, a_packed):
     return Plan(h.value, fmt, M, N, K)
 
 
+def qlinear_plan_glu(fmt, M, N, K, a_packed=1):
+    """Plan for a merged gate/up weight [N, K] (packed) whose runs write the
+    SiLU-and-mul output [M, N/2]; a_packed 1 = packed A_q (qlinear_run),
+    2 = a forward plan (qlinear_forward, quantization possibly fused)."""
+    h = ctypes.c_void_p()
+    _check(lib().qlinear_plan_glu(fmt, M, N, K, a_packed, ctypes.byref(h)), "qlinear_plan_glu")
+    return Plan(h.value, fmt, M, N, K)
+
+
+def qlinear_plan_glu_with_config(fmt, M, N, K, cfg):
+    c = QLConfig(**make_config(**cfg))
+    h = ctypes.c_void_p()
+    _check(lib().qlinear_plan_glu_with_config(fmt, M, N, K, ctypes.byref(c), ctypes.byref(h)),
+           "qlinear_plan_glu_with_config")
+    return Plan(h.value, fmt, M, N, K)
+
+
 def qlinear_plan_from_table(fmt, M, N, K):
     h = ctypes.c_void_p()
     _check(lib().qlinear_plan_from_table(fmt, M, N, K, ctypes.byref(h)), "qlinear_plan_from_table")

@@ -16,7 +16,7 @@ class QLConfig(ctypes.Structure):
 
 class QLPlanFacts(ctypes.Structure):
     _fields_ = [("source", c_i32), ("chunks", c_i32), ("chunk_k", c_i32), ("workgroups", c_i32),
-                ("threads", c_i32), ("lds_bytes", c_i32), ("workspace_bytes", c_i64)]
+                ("threads", c_i32), ("lds_bytes", c_i32), ("workspace_bytes", c_i64), ("epilogue", c_i32)]
 
 
 # name -> (restype, argtypes); exactly the functions declared in include/qlinear.h
@@ -40,6 +40,9 @@ SIGNATURES = {
     "qlinear_plan_with_config": (c_i32, [c_i32, c_i64, c_i64, c_i64, ctypes.POINTER(QLConfig),
                                          ctypes.POINTER(c_vp)]),
     "qlinear_plan_info": (c_i32, [c_vp, ctypes.POINTER(QLConfig), ctypes.POINTER(QLPlanFacts)]),
+    "qlinear_plan_glu": (c_i32, [c_i32, c_i64, c_i64, c_i64, c_i32, ctypes.POINTER(c_vp)]),
+    "qlinear_plan_glu_with_config": (c_i32, [c_i32, c_i64, c_i64, c_i64, ctypes.POINTER(QLConfig),
+                                             ctypes.POINTER(c_vp)]),
     "qlinear_workspace_bytes": (c_i64, [c_vp]),
     "qlinear_plan_destroy": (None, [c_vp]),
     "qlinear_run": (c_i32, [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp]),

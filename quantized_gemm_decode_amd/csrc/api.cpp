@@ -120,6 +120,7 @@ struct ql_plan_s {
   int G, chunk_kb, chunks, mt, n_tiles, bn, tiles_n;
   int64_t lds, ws_bytes, ws_acc_bytes;
   bool tiled;
+  bool glu;  // merged gate/up weight, SiLU-and-mul epilogue, output [M, N/2]
   qlk::DecodeKey key;
   qlk::TiledKey tkey;
 };
@@ -239,7 +240,7 @@ ql_status build_tiled_plan(int32_t fmt, int64_t M, int64_t N, int64_t K, const q
 }
 
 ql_status build_plan(int32_t fmt, int64_t M, int64_t N, int64_t K, const ql_config& cfg, int32_t source,
-                     ql_plan* out) {
+                     ql_plan* out, bool glu = false) {
   if (!out) return fail(QL_E_INVALID, "out_plan is NULL");
   *out = nullptr;
   ql_status st = check_sizes(fmt, M, K, "M");
@@ -248,6 +249,14 @@ ql_status build_plan(int32_t fmt, int64_t M, int64_t N, int64_t K, const ql_conf
   if (M * N >= (int64_t(1) << 31)) return fail(QL_E_UNSUPPORTED, "M*N exceeds 2^31");
   if (cfg.w_layout == 1 && qlinear_packed_weight_bytes(N, K) > (int64_t(1) << 30))
     return fail(QL_E_UNSUPPORTED, "packed weights exceed 2^30 bytes");
+  if (glu) {
+    if (cfg.algo != QL_ALGO_DECODE || M > 32)
+      return fail(QL_E_UNSUPPORTED, "the SiLU-and-mul epilogue runs on the decode algorithm (M <= 32)");
+    if (N % 32) return fail(QL_E_INVALID, "SiLU-and-mul needs N (gate + up rows) a multiple of 32 (N=%lld)",
+                            (long long)N);
+    if (cfg.w_layout != 1 || cfg.rows_per_wave != 32 || (cfg.a_mode != 2 && cfg.a_mode != 4))
+      return fail(QL_E_UNSUPPORTED, "SiLU-and-mul plans need packed weights, rows_per_wave 32 and a_mode 2 or 4");
+  }
   if (cfg.algo == QL_ALGO_TILED) return build_tiled_plan(fmt, M, N, K, cfg, source, out);
   if (cfg.algo != QL_ALGO_DECODE) return fail(QL_E_INVALID, "unknown algo %d", cfg.algo);
   if (M > 64) return fail(QL_E_UNSUPPORTED, "the decode algorithm serves M <= 64 (M=%lld)", (long long)M);
@@ -290,8 +299,10 @@ ql_status build_plan(int32_t fmt, int64_t M, int64_t N, int64_t K, const ql_conf
                 (long long)kFusedMaxValues, chunk);
   }
   const int rg = cfg.rows_per_wave / 16;
-  p->bn = cfg.waves_n * rg * 16;
-  p->n_tiles = (int)((N + p->bn - 1) / p->bn);
+  p->glu = glu;
+  // GLU: a tile's waves side by side cover 16 output columns each
+  p->bn = glu ? cfg.waves_n * 16 : cfg.waves_n * rg * 16;
+  p->n_tiles = (int)(((glu ? N / 2 : N) + p->bn - 1) / p->bn);
   const int64_t lds_a = (cfg.a_mode == 1 || cfg.a_mode == 3) ? (int64_t)p->chunk_kb * p->mt * 2048
                        : cfg.a_mode == 4 ? 512 + M * ((int64_t)p->chunk_kb * 128 + 64) +
                                                (fmt == QL_BLOCK_FP8 ? M * (int64_t)p->chunk_kb * 4 : 0)
@@ -308,7 +319,7 @@ ql_status build_plan(int32_t fmt, int64_t M, int64_t N, int64_t K, const ql_conf
   p->ws_acc_bytes = p->chunks > 1 ? ((M * N * 4 + 255) / 256) * 256 : 0;
   p->ws_bytes = p->chunks > 1 ? p->ws_acc_bytes + (int64_t)p->n_tiles * 4 : 0;
   const int wm = cfg.w_layout ? qlk::W_PACKED : (cfg.w_lds ? qlk::W_LDS_TRANSPOSE : qlk::W_DIRECT);
-  p->key = qlk::DecodeKey{kernel_fmt(fmt), cfg.swap_ab, p->mt, rg, nw, cfg.prefetch, cfg.a_mode, wm};
+  p->key = qlk::DecodeKey{kernel_fmt(fmt), cfg.swap_ab, p->mt, rg, nw, cfg.prefetch, cfg.a_mode, wm, glu ? 1 : 0};
   qlk::DecodeArgs dummy{};
   hipError_t pe;
   switch (p->key.fmt) {
@@ -344,6 +355,7 @@ ql_status launch_gemm(const ql_plan_s* p, const void* a_q, const float* a_scale,
                       float* sa_out = nullptr) {
   const bool fused = !p->tiled && p->cfg.a_mode == 4;
   if (fused && !from_forward) return fail(QL_E_INVALID, "a fused-quantization plan runs through qlinear_forward");
+  if (p->glu && acc_out) return fail(QL_E_UNSUPPORTED, "raw accumulators are not kept by a SiLU-and-mul plan");
   if (p->M == 0 || p->N == 0) return QL_OK;
   if (!y) return fail(QL_E_INVALID, "y is NULL");
   if (!aligned16(y)) return fail(QL_E_ALIGN, "y is not 16-byte aligned");
@@ -586,6 +598,43 @@ ql_status qlinear_plan_with_config(int32_t fmt, int64_t M, int64_t N, int64_t K,
   return build_plan(fmt, M, N, K, *cfg, QL_SRC_CUSTOM, out_plan);
 }
 
+ql_status qlinear_plan_glu_with_config(int32_t fmt, int64_t M, int64_t N, int64_t K, const ql_config* cfg,
+                                       ql_plan* out_plan) {
+  if (!cfg) return fail(QL_E_INVALID, "cfg is NULL");
+  return build_plan(fmt, M, N, K, *cfg, QL_SRC_CUSTOM, out_plan, true);
+}
+
+ql_status qlinear_plan_glu(int32_t fmt, int64_t M, int64_t N, int64_t K, int32_t a_packed, ql_plan* out_plan) {
+  if (out_plan) *out_plan = nullptr;
+  if (a_packed != 1 && a_packed != 2) return fail(QL_E_INVALID, "a_packed must be 1 or 2 for SiLU-and-mul plans");
+  // start from the merged linear's own plan (table or heuristic), then keep
+  // the fields the SiLU-and-mul kernels are instantiated for
+  ql_plan base = nullptr;
+  ql_status st = plan_for_layout(fmt, 1, a_packed, M, N, K, &base);
+  if (st != QL_OK) return st;
+  ql_config c = base->cfg;
+  const int32_t source = base->source;
+  delete base;
+  if (c.algo != QL_ALGO_DECODE) return fail(QL_E_UNSUPPORTED, "the SiLU-and-mul epilogue serves M <= 32");
+  c.rows_per_wave = 32;
+  const int nw = c.waves_n * c.waves_k;
+  if (nw != 4 && nw != 8) {
+    c.waves_n = 1;
+    c.waves_k = 4;
+  }
+  if (c.prefetch > 2) c.prefetch = 2;
+  if (c.a_mode == 3) c.a_mode = 2;
+  st = build_plan(fmt, M, N, K, c, source, out_plan, true);
+  if (st == QL_E_UNSUPPORTED) {     // that shape is not instantiated: the plain one is
+    c.swap_ab = 0;
+    c.waves_n = 1;
+    c.waves_k = 4;
+    c.prefetch = 1;
+    st = build_plan(fmt, M, N, K, c, source, out_plan, true);
+  }
+  return st;
+}
+
 ql_status qlinear_plan_info(ql_plan p, ql_config* cfg, ql_plan_facts* facts) {
   if (!p) return fail(QL_E_INVALID, "plan is NULL");
   if (cfg) {
@@ -600,6 +649,7 @@ ql_status qlinear_plan_info(ql_plan p, ql_config* cfg, ql_plan_facts* facts) {
     facts->threads = p->tiled ? (p->cfg.tile_m * p->cfg.tile_n >= 256 * 256 ? 512 : 256) : p->key.nw * 64;
     facts->lds_bytes = (int32_t)p->lds;
     facts->workspace_bytes = p->ws_bytes;
+    facts->epilogue = p->glu ? 1 : 0;
   }
   return QL_OK;
 }

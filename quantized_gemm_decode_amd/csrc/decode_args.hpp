@@ -51,6 +51,7 @@ struct DecodeKey {
   int alds;  // activations: 0 row-major from L2, 1 row-major staged in LDS, 2 packed from L2,
              // 3 packed staged in LDS, 4 quantized from X inside the kernel (fused)
   int wm;    // weight mode: W_DIRECT / W_LDS_TRANSPOSE / W_PACKED
+  int glu;   // 1: merged gate/up weight, SiLU-and-mul epilogue, output [M, N/2]
 };
 
 // Compile-time shape of one tiled (M > 32) kernel instantiation.

@@ -64,7 +64,11 @@ __device__ __forceinline__ uint32_t epilogue_scaled(float accf, float sa, float 
   return bf16_rne(t);
 }
 
-template <int FMT, bool SWAP, int MT, int RG, int NW, int PF, int AL, int WM>
+// GLU: the weight is a merged gate/up projection (rows [0, N/2) gate, rows
+// [N/2, N) up) and the output is silu(gate) * up, [M, N/2]: a wave's two
+// 16-row groups are gate rows c.. and the up rows N/2 + c.. of the same
+// output columns, so both values of an output element meet in one lane.
+template <int FMT, bool SWAP, int MT, int RG, int NW, int PF, int AL, int WM, bool GLU>
 __global__ void __launch_bounds__(NW * 64) qgemm_decode_kernel(DecodeArgs p) {
   constexpr bool FUSED = AL == 4;                     // activations quantized here from bf16 X
   constexpr bool ALDS = AL == 1 || AL == 3 || FUSED;  // activations read from LDS
@@ -72,6 +76,7 @@ __global__ void __launch_bounds__(NW * 64) qgemm_decode_kernel(DecodeArgs p) {
   constexpr bool WL = WM == W_LDS_TRANSPOSE;
   constexpr bool WP = WM == W_PACKED;
   static_assert(!FUSED || (MT == 1 && WP), "fused quantization: one token tile, packed weights");
+  static_assert(!GLU || (RG == 2 && WP), "SiLU-and-mul: a gate and an up row group per wave, packed weights");
   using Acc = typename AccOf<FMT>::T;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   __shared__ int s_last;
@@ -93,6 +98,14 @@ __global__ void __launch_bounds__(NW * 64) qgemm_decode_kernel(DecodeArgs p) {
   const int row_base = tile * BN + wn * RG * 16;
 
   const uint32_t M = (uint32_t)p.M, N = (uint32_t)p.N, K = (uint32_t)p.K;
+  // GLU: output columns obase.. of this wave; weight rows of its row groups
+  const uint32_t IH = N / 2u;
+  const int obase = tile * (NW / WK) * 16 + wn * 16;
+  auto grow = [&](int rg) -> int { return GLU ? (rg == 0 ? obase : (int)IH + obase) : row_base + rg * 16; };
+  // is the element at offset x of row group rg a real output?
+  auto rowok = [&](int rg, uint32_t x) -> bool {
+    return GLU ? (uint32_t)obase + x < IH : (uint32_t)grow(rg) + x < N;
+  };
   const uint32_t NT16 = (N + 15u) / 16u;  // 16-row groups (tiles along N of the packed layout)
   const __amdgpu_buffer_rsrc_t rw = make_rsrc(p.w, WP ? NT16 * (uint32_t)p.G * 2048u : N * K);
   const uint32_t MT16 = (M + 15u) / 16u;
@@ -105,7 +118,7 @@ __global__ void __launch_bounds__(NW * 64) qgemm_decode_kernel(DecodeArgs p) {
   uint32_t wbase[RG];
 #pragma unroll
   for (int rg = 0; rg < RG; ++rg) {
-    const uint32_t row = (uint32_t)(row_base + rg * 16 + r16);
+    const uint32_t row = (uint32_t)(grow(rg) + r16);
     wbase[rg] = row < N ? row * K + glo : OOB;
   }
   // WL (coalesced weight stream): the two loads of a (row group, K block)
@@ -118,7 +131,7 @@ __global__ void __launch_bounds__(NW * 64) qgemm_decode_kernel(DecodeArgs p) {
   for (int rg = 0; rg < RG; ++rg)
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-      const uint32_t row = (uint32_t)(row_base + rg * 16 + 8 * i + (lane >> 3));
+      const uint32_t row = (uint32_t)(grow(rg) + 8 * i + (lane >> 3));
       wbase_c[rg][i] = row < N ? row * K + c16 : OOB;
     }
   // WP (packed tiles): tile (t, kb) is 2 KB at (t*G + kb)*2048 holding exactly
@@ -127,8 +140,8 @@ __global__ void __launch_bounds__(NW * 64) qgemm_decode_kernel(DecodeArgs p) {
   uint32_t wbase_p[RG];
 #pragma unroll
   for (int rg = 0; rg < RG; ++rg) {
-    const uint32_t t = (uint32_t)(row_base / 16 + rg);
-    wbase_p[rg] = t < NT16 ? t * (uint32_t)p.G * 2048u + (uint32_t)lane * 16u : OOB;
+    const uint32_t t = (uint32_t)(grow(rg) / 16);
+    wbase_p[rg] = (t < NT16 && rowok(rg, 0)) ? t * (uint32_t)p.G * 2048u + (uint32_t)lane * 16u : OOB;
   }
   // LDS slots of the transpose: 2 per wave, each RG x 2 KB, after the
   // staged activations.
@@ -246,7 +259,7 @@ __global__ void __launch_bounds__(NW * 64) qgemm_decode_kernel(DecodeArgs p) {
         }
 #pragma unroll
         for (int rg = 0; rg < RG; ++rg) {
-          const uint32_t row0 = (uint32_t)(row_base + rg * 16);
+          const uint32_t row0 = (uint32_t)grow(rg);
           swb[q][rg] = bload_f32(rsw, (ok && row0 < N) ? ((row0 >> 7) * Gu + (uint32_t)kb) * 4u : OOB);
         }
       }
@@ -503,7 +516,7 @@ __global__ void __launch_bounds__(NW * 64) qgemm_decode_kernel(DecodeArgs p) {
     for (int rg = 0; rg < RG; ++rg)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const uint32_t n = SWAP ? (uint32_t)(row_base + rg * 16 + 4 * g + r) : (uint32_t)(row_base + rg * 16 + r16);
+        const uint32_t n = (uint32_t)grow(rg) + (SWAP ? (uint32_t)(4 * g + r) : (uint32_t)r16);
         esw[rg][r] = (!SWAP && r > 0) ? 0.f : bload_f32(rsw, n < N ? n * 4u : OOB);
       }
   }
@@ -570,10 +583,10 @@ __global__ void __launch_bounds__(NW * 64) qgemm_decode_kernel(DecodeArgs p) {
         for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            const uint32_t n = SWAP ? (uint32_t)(row_base + rg * 16 + 4 * g + r)
-                                    : (uint32_t)(row_base + rg * 16 + r16);
+            const uint32_t x = SWAP ? (uint32_t)(4 * g + r) : (uint32_t)r16;
+            const uint32_t n = (uint32_t)grow(rg) + x;
             const uint32_t m = SWAP ? (uint32_t)(mt * 16 + r16) : (uint32_t)(mt * 16 + 4 * g + r);
-            if (m < M && n < N) {
+            if (m < M && rowok(rg, x)) {
               if constexpr (FMT == FMT_INT8)
                 __hip_atomic_fetch_add(reinterpret_cast<int*>(p.ws) + (size_t)m * N + n, acc[rg][mt][r],
                                        __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -604,10 +617,10 @@ __global__ void __launch_bounds__(NW * 64) qgemm_decode_kernel(DecodeArgs p) {
         for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            const uint32_t n = SWAP ? (uint32_t)(row_base + rg * 16 + 4 * g + r)
-                                    : (uint32_t)(row_base + rg * 16 + r16);
+            const uint32_t x = SWAP ? (uint32_t)(4 * g + r) : (uint32_t)r16;
+            const uint32_t n = (uint32_t)grow(rg) + x;
             const uint32_t m = SWAP ? (uint32_t)(mt * 16 + r16) : (uint32_t)(mt * 16 + 4 * g + r);
-            if (m < M && n < N) {
+            if (m < M && rowok(rg, x)) {
               int* slot = reinterpret_cast<int*>(p.ws) + (size_t)m * N + n;
               const int v = __hip_atomic_exchange(slot, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
               if constexpr (FMT == FMT_INT8)
@@ -622,6 +635,37 @@ __global__ void __launch_bounds__(NW * 64) qgemm_decode_kernel(DecodeArgs p) {
 
   if (wk != 0) return;
 
+  // ---- SiLU-and-mul epilogue: the gate (row group 0) and up (1) values of
+  // an output element are the binary32 epilogue values of the two rows;
+  // h = g / (1 + exp(-g)) * u, rounded to bf16 once, stored to Y [M, N/2].
+  if constexpr (GLU) {
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const uint32_t x = SWAP ? (uint32_t)(4 * g + r) : (uint32_t)r16;
+        const uint32_t m = SWAP ? (uint32_t)(mt * 16 + r16) : (uint32_t)(mt * 16 + 4 * g + r);
+        float t[2];
+#pragma unroll
+        for (int rg = 0; rg < 2; ++rg) {
+          if constexpr (FMT == FMT_BLOCK) {
+            t[rg] = acc[rg][mt][r];
+          } else {
+            float accf;
+            if constexpr (FMT == FMT_INT8)
+              accf = __int2float_rn(acc[rg][mt][r]);
+            else
+              accf = acc[rg][mt][r];
+            t[rg] = __fmul_rn(__fmul_rn(accf, esa[mt][SWAP ? 0 : r]), esw[rg][SWAP ? r : 0]);
+          }
+        }
+        const float h = __fmul_rn(__fdiv_rn(t[0], 1.0f + expf(-t[0])), t[1]);
+        if (m < M && rowok(0, x)) p.y[(size_t)m * IH + (uint32_t)obase + x] = (uint16_t)bf16_rne(h);
+      }
+    }
+    return;
+  }
+
   // ---- epilogue: scales, bf16 rounding, store
   const bool vec4 = SWAP && (N & 3u) == 0;
 #pragma unroll
@@ -632,7 +676,7 @@ __global__ void __launch_bounds__(NW * 64) qgemm_decode_kernel(DecodeArgs p) {
       uint32_t nn[4], mm[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        nn[r] = SWAP ? (uint32_t)(row_base + rg * 16 + 4 * g + r) : (uint32_t)(row_base + rg * 16 + r16);
+        nn[r] = (uint32_t)grow(rg) + (SWAP ? (uint32_t)(4 * g + r) : (uint32_t)r16);
         mm[r] = SWAP ? (uint32_t)(mt * 16 + r16) : (uint32_t)(mt * 16 + 4 * g + r);
         const bool ok = mm[r] < M && nn[r] < N;
         if constexpr (FMT == FMT_BLOCK) {
@@ -707,13 +751,14 @@ constexpr bool decode_variant_ok() {
   return decode_config_fits<FMT, NW_, SW, MT_, RG_, PF_>();
 }
 
-template <int FMT, int NW_, int SW, int MT_, int RG_, int PF_, int AL, int WM_>
+template <int FMT, int NW_, int SW, int MT_, int RG_, int PF_, int AL, int WM_, int GLU = 0>
 hipError_t decode_try(const DecodeKey& k, dim3 grid, dim3 block, size_t lds, hipStream_t s, const DecodeArgs& a,
                       bool probe_only, bool* hit) {
   if constexpr (decode_variant_ok<FMT, NW_, SW, MT_, RG_, PF_, AL, WM_>()) {
-    if (k.swap == SW && k.mt == MT_ && k.rg == RG_ && k.nw == NW_ && k.pf == PF_ && k.alds == AL && k.wm == WM_) {
+    if (k.swap == SW && k.mt == MT_ && k.rg == RG_ && k.nw == NW_ && k.pf == PF_ && k.alds == AL && k.wm == WM_ &&
+        k.glu == GLU) {
       *hit = true;
-      auto fn = qgemm_decode_kernel<FMT, SW != 0, MT_, RG_, NW_, PF_, AL, WM_>;
+      auto fn = qgemm_decode_kernel<FMT, SW != 0, MT_, RG_, NW_, PF_, AL, WM_, GLU != 0>;
       if (probe_only) {
         // LDS beyond the default 64 KB needs the per-kernel opt-in (gfx950: 160 KB a workgroup)
         if (lds > 64 * 1024)
@@ -760,10 +805,22 @@ hipError_t decode_dispatch(const DecodeKey& k, dim3 grid, dim3 block, size_t lds
   QL_TRY_P4(4, SW, 1, 1) QL_TRY_P4(4, SW, 1, 2) QL_TRY_P4(4, SW, 2, 1) QL_TRY_P4(4, SW, 2, 2)     \
   QL_TRY_P4(4, SW, 4, 1) QL_TRY_P4(8, SW, 1, 1) QL_TRY_P4(8, SW, 1, 2) QL_TRY_P4(8, SW, 2, 1)     \
   QL_TRY_P4(8, SW, 2, 2)
-#define QL_TRY_MT(SW) QL_TRY_RG(SW, 1) QL_TRY_RG(SW, 2) QL_TRY_PN(SW, 1) QL_TRY_PN(SW, 2) QL_TRY_PN4(SW)
+  // SiLU-and-mul epilogue: 32 rows a wave (a gate and an up group), packed
+  // weights, activations packed from L2 or quantized in the kernel
+#define QL_TRY_G1(NW_, SW, MT_, PF_, AL)                                                        \
+  e = decode_try<FMT, NW_, SW, MT_, 2, PF_, AL, 2, 1>(k, grid, block, lds, s, a, probe_only, &hit); \
+  if (hit) return e;
+#define QL_TRY_G(SW, MT_)                                                                      \
+  QL_TRY_G1(4, SW, MT_, 1, 2) QL_TRY_G1(4, SW, MT_, 2, 2) QL_TRY_G1(8, SW, MT_, 1, 2)            \
+  QL_TRY_G1(8, SW, MT_, 2, 2) QL_TRY_G1(4, SW, MT_, 1, 4) QL_TRY_G1(4, SW, MT_, 2, 4)            \
+  QL_TRY_G1(8, SW, MT_, 1, 4) QL_TRY_G1(8, SW, MT_, 2, 4)
+#define QL_TRY_MT(SW) QL_TRY_RG(SW, 1) QL_TRY_RG(SW, 2) QL_TRY_PN(SW, 1) QL_TRY_PN(SW, 2) QL_TRY_PN4(SW) \
+  QL_TRY_G(SW, 1) QL_TRY_G(SW, 2)
   QL_TRY_MT(0)
   QL_TRY_MT(1)
 #undef QL_TRY_MT
+#undef QL_TRY_G
+#undef QL_TRY_G1
 #undef QL_TRY_PN4
 #undef QL_TRY_P4
 #undef QL_TRY_PN

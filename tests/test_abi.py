@@ -247,3 +247,30 @@ def test_decode_plans_reach_64_tokens():
         assert ql.qlinear_plan_layouts(ql.FP8_DYNAMIC, 50, 4096, 4096, 1, 1).config["algo"] == ql.ALGO_TILED
     finally:
         ql.load_default_table()
+
+
+def test_glu_plans_are_validated_on_host():
+    def glu_status(fmt, M, N, K, **cfg):
+        h = ctypes.c_void_p()
+        c = ql.QLConfig(**ql.make_config(**cfg))
+        st = ql.lib().qlinear_plan_glu_with_config(fmt, M, N, K, ctypes.byref(c), ctypes.byref(h))
+        if h.value:
+            ql.lib().qlinear_plan_destroy(h)
+        return st
+    good = dict(w_layout=1, a_mode=2, rows_per_wave=32, waves_n=1, waves_k=4, prefetch=1)
+    assert glu_status(ql.FP8_DYNAMIC, 4, 1024, 512, **good) == QL_OK
+    assert glu_status(ql.FP8_DYNAMIC, 4, 1040, 512, **good) == QL_E_INVALID                   # N % 32
+    assert glu_status(ql.FP8_DYNAMIC, 4, 1024, 512, **dict(good, rows_per_wave=16)) == QL_E_UNSUPPORTED
+    assert glu_status(ql.FP8_DYNAMIC, 4, 1024, 512, **dict(good, w_layout=0)) == QL_E_UNSUPPORTED
+    assert glu_status(ql.FP8_DYNAMIC, 40, 1024, 512, **good) == QL_E_UNSUPPORTED              # decode only
+    p = ql.qlinear_plan_glu_with_config(ql.W8A8_INT8, 4, 1024, 512, good)
+    assert p.facts["epilogue"] == 1 and p.facts["workgroups"] == 512 // 16
+    assert ql.qlinear_plan(ql.W8A8_INT8, 4, 1024, 512).facts["epilogue"] == 0
+    v = ctypes.c_void_p
+    good_ptr = v(1 << 20)
+    assert ql.lib().qlinear_run_debug_acc(p.handle, good_ptr, good_ptr, good_ptr, good_ptr, good_ptr, v(0),
+                                          good_ptr, v(0)) == QL_E_UNSUPPORTED
+    q = ql.qlinear_plan_glu(ql.FP8_DYNAMIC, 2, 24576, 4096, 2)
+    assert q.facts["epilogue"] == 1 and q.config["rows_per_wave"] == 32
+    with pytest.raises(ql.QLinearError):
+        ql.qlinear_plan_glu(ql.FP8_DYNAMIC, 2, 24576, 4096, 0)
