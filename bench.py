@@ -253,6 +253,9 @@ def parse_args(argv=None):
     ap.add_argument("--profile-pass", action="store_true",
                     help="for hardware-counter runs: launch each point's quantize+GEMM eagerly on 3 weight "
                          "copies, then a plain 256 MiB device copy 3 times (the counters' calibration), and exit")
+    ap.add_argument("--glu", action="store_true",
+                    help="time the workload's gate_up points two ways -- the forward plan writing Y [M, N], and "
+                         "the SiLU-and-mul plan writing silu(gate)*up [M, N/2] -- print one JSON line, and exit")
     return ap.parse_args(argv)
 
 
@@ -325,6 +328,8 @@ def main(argv=None):
 
     if args.profile_pass:
         return profile_pass(ql, fmt, pts, shapes, stream)
+    if args.glu:
+        return glu_pass(ql, wl, pts, shapes, stream, args)
 
     # ------------------------------------------------ step graphs (quantize + GEMM per point)
     n_graphs = 8
@@ -468,6 +473,61 @@ def main(argv=None):
     if args.out:
         with open(args.out, "w") as f:
             f.write(line + "\n")
+    return 0
+
+
+def glu_pass(ql, wl, pts, shapes, stream, args):
+    """Per-launch times of the gate_up points as a plain forward (Y [M, N]) and
+    with the SiLU-and-mul epilogue (silu(gate)*up, [M, N/2]), HIP events around
+    graph replays of R launches on distinct weight copies, as for the bench's
+    per-point timing."""
+    import numpy as np
+    import torch
+    fmt = wl.fmt
+    out = []
+    for p in pts:
+        if p["lab"] != "gate_up":
+            continue
+        sh = shapes[p["lab"]]
+        M, N, K = p["M"], p["N"], p["K"]
+        R = min(sh["copies"], 64)
+        res = {"M": M}
+        for kind in ("plain", "glu"):
+            plan = p["plan"] if kind == "plain" else ql.qlinear_plan_glu(fmt, M, N, K, 2)
+            y = torch.empty(M, N if kind == "plain" else N // 2, dtype=torch.bfloat16, device="cuda")
+            a_q = ql.act_buffer(plan)
+            a_s = torch.empty(ql.act_scale_shape(fmt, M, K), dtype=torch.float32, device="cuda")
+            wsp = plan.new_workspace()
+            with torch.cuda.stream(stream):
+                ql.qlinear_graph_begin(stream)
+                for c in range(R):
+                    ql.qlinear_forward(plan, p["x"], a_q, a_s, sh["wq"][c], sh["ws"][c], y, wsp, stream=stream)
+                g = ql.qlinear_graph_end(stream)
+            for _ in range(3):
+                g.launch(stream)
+            stream.synchronize()
+            samples = []
+            for _ in range(args.kernel_reps):
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                g.launch(stream)
+                e1.record(stream)
+                e1.synchronize()
+                samples.append(e0.elapsed_time(e1) * 1e3 / R)
+            cfg = plan.config
+            res[kind + "_us"] = round(float(np.median(samples)), 3)
+            res[kind + "_fused_quant"] = cfg["a_mode"] == 4
+            res[kind + "_config"] = "swap%d split%d waves%dx%d rows%d pf%d amode%d" % (
+                cfg["swap_ab"], cfg["split_k"], cfg["waves_n"], cfg["waves_k"], cfg["rows_per_wave"],
+                cfg["prefetch"], cfg["a_mode"])
+            del g
+        out.append(res)
+    gu = [p for p in pts if p["lab"] == "gate_up"]
+    print(json.dumps({"metric": "µs per gate_up forward: plain (Y [M, N]) vs SiLU-and-mul epilogue (silu(gate)*up, "
+                                "[M, N/2])", "unit": "us", "workload": wl.name,
+                      "shape": "gate_up %dx%d" % (gu[0]["N"], gu[0]["K"]) if gu else None,
+                      "data": "synthetic", "kernel_reps": args.kernel_reps, "per_point": out}), flush=True)
     return 0
 
 
