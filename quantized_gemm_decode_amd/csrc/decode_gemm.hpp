@@ -397,17 +397,22 @@ __global__ void __launch_bounds__(NW * 64) qgemm_decode_kernel(DecodeArgs p) {
   if constexpr (FUSED) {
     const __amdgpu_buffer_rsrc_t rx = make_rsrc(p.x, M * K * 2u);
     const uint32_t npc = FMT == FMT_BLOCK ? M * ppr : M * K / 8u;
+    // a wave issues only the loads whose pieces exist (a wave-uniform test;
+    // the wait below counts the weight loads, which are all younger)
 #pragma unroll
     for (int i = 0; i < XP; ++i) {
       const uint32_t P = (uint32_t)(tid + NW * 64 * i);
-      uint32_t off;
-      if constexpr (FMT == FMT_BLOCK) {
-        const uint32_t m = P / ppr, w = P - m * ppr;
-        off = (m * K + (uint32_t)kb0 * 128u + w * 8u) * 2u;
-      } else {
-        off = P * 16u;
+      xv[i] = u32x4{0u, 0u, 0u, 0u};
+      if ((uint32_t)(wave * 64 + NW * 64 * i) < npc) {
+        uint32_t off;
+        if constexpr (FMT == FMT_BLOCK) {
+          const uint32_t m = P / ppr, w = P - m * ppr;
+          off = (m * K + (uint32_t)kb0 * 128u + w * 8u) * 2u;
+        } else {
+          off = P * 16u;
+        }
+        xv[i] = bload16(rx, P < npc ? off : OOB);
       }
-      xv[i] = bload16(rx, P < npc ? off : OOB);
     }
     if (tid < 4) reinterpret_cast<uint32_t*>(smem + FA_ZERO)[tid] = 0u;
     __builtin_amdgcn_sched_barrier(0);
@@ -433,6 +438,7 @@ __global__ void __launch_bounds__(NW * 64) qgemm_decode_kernel(DecodeArgs p) {
 #pragma unroll
     for (int i = 0; i < XP; ++i) {
       const uint32_t P = (uint32_t)(tid + NW * 64 * i);
+      if ((uint32_t)(wave * 64 + NW * 64 * i) >= npc) continue;   // no piece of this wave
       const float gmax = row16_max_nonneg(abs_bf16_max8(xv[i], 0.0f));
       if (P < npc) {
         const uint32_t m = P / ppr, w = P - m * ppr;
@@ -458,8 +464,9 @@ __global__ void __launch_bounds__(NW * 64) qgemm_decode_kernel(DecodeArgs p) {
 #pragma unroll
     for (int i = 0; i < XP; ++i) {
       const uint32_t u = (uint32_t)(wave + NW * i);
+      if (u >= nu) continue;   // wave-uniform: no piece of this wave
       const float m = wave_max_nonneg(abs_bf16_max8(xv[i], 0.0f));
-      if (lane == 0 && u < nu) red[u] = m;
+      if (lane == 0) red[u] = m;
     }
     lds_barrier();
     const uint32_t k_lo = (uint32_t)kb0 * 128u, k_hi = (uint32_t)kb1 * 128u;
