@@ -223,7 +223,8 @@ ql_status qlinear_pack_weight(const void* w_q, int64_t N, int64_t K, void* w_pac
  * for (w_layout; row-major A_q = a_mode 0/1, packed A_q = a_mode 2/3).  An
  * entry marked "fwd" (and every a_mode 4 entry) is a forward plan: the best
  * configuration for quantize + GEMM together, fused or not, and its time
- * covers both.
+ * covers both.  An entry marked "glu" is the same for a SiLU-and-mul plan
+ * (qlinear_plan_glu) of the merged gate/up weight [N, K].
  * Loading replaces the in-process table.  Returns the entry count via n_entries.
  */
 ql_status qlinear_table_load(const char* path, int64_t* n_entries);
@@ -269,9 +270,9 @@ ql_status qlinear_plan_with_config(int32_t fmt, int64_t M, int64_t N, int64_t K,
  * silu(g) = g / (1 + exp(-g)).  Decode algorithm only (M <= 32), packed
  * weights, N % 32 == 0; qlinear_run (a_packed 1) or qlinear_forward
  * (a_packed 2: the quantizer may be fused as well) drive it as usual with
- * y_bf16 [M, N/2].  qlinear_plan_glu starts from the merged linear's planned
- * configuration (table or heuristic) and keeps 32 rows a wave (a gate and an
- * up group); qlinear_run_debug_acc rejects these plans.
+ * y_bf16 [M, N/2].  qlinear_plan_glu takes the table's "glu" entry, else the
+ * merged linear's planned configuration (table or heuristic) with 32 rows a
+ * wave (a gate and an up group); qlinear_run_debug_acc rejects these plans.
  */
 ql_status qlinear_plan_glu(int32_t fmt, int64_t M, int64_t N, int64_t K, int32_t a_packed, ql_plan* out_plan);
 ql_status qlinear_plan_glu_with_config(int32_t fmt, int64_t M, int64_t N, int64_t K, const ql_config* cfg,

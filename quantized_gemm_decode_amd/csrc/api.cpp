@@ -72,7 +72,8 @@ struct TableEntry {
   int64_t M, N, K;
   ql_config cfg;
   double us;
-  int us_class;  // 2: a forward-only entry (its time covers quantize + GEMM), else act_class(a_mode)
+  int us_class;  // 2: a forward-only entry (its time covers quantize + GEMM); 3: a SiLU-and-mul forward
+                 // entry (qlinear_plan_glu); else act_class(a_mode)
 };
 
 std::mutex g_table_mu;
@@ -96,7 +97,7 @@ bool table_lookup(int32_t fmt, int32_t layout, int a_class, int64_t M, int64_t N
   const TableEntry* largest = nullptr;
   for (const TableEntry& e : g_table) {
     if (e.fmt != fmt || e.N != N || e.K != K || e.cfg.w_layout != layout) continue;
-    if (a_class == 2 ? e.us_class != 2 : (e.us_class == 2 || act_class(e.cfg.a_mode) != a_class)) continue;
+    if (a_class >= 2 ? e.us_class != a_class : (e.us_class >= 2 || act_class(e.cfg.a_mode) != a_class)) continue;
     if (e.M >= want && (!best || e.M < best->M)) best = &e;
     if (!largest || e.M > largest->M) largest = &e;
   }
@@ -505,8 +506,9 @@ ql_status qlinear_table_load(const char* path, int64_t* n_entries) {
     std::string kind;
     e.us_class = act_class(e.cfg.a_mode);
     if (is >> kind) {
-      if (kind != "fwd") return fail(QL_E_TABLE, "%s:%d: unknown entry kind '%s'", path, lineno, kind.c_str());
-      e.us_class = 2;
+      if (kind != "fwd" && kind != "glu")
+        return fail(QL_E_TABLE, "%s:%d: unknown entry kind '%s'", path, lineno, kind.c_str());
+      e.us_class = kind == "glu" ? 3 : 2;
     }
     if (!valid_fmt(e.fmt) || M < 1 || N < 1 || K < 1) return fail(QL_E_TABLE, "%s:%d: bad key", path, lineno);
     e.M = M;
@@ -607,8 +609,14 @@ ql_status qlinear_plan_glu_with_config(int32_t fmt, int64_t M, int64_t N, int64_
 ql_status qlinear_plan_glu(int32_t fmt, int64_t M, int64_t N, int64_t K, int32_t a_packed, ql_plan* out_plan) {
   if (out_plan) *out_plan = nullptr;
   if (a_packed != 1 && a_packed != 2) return fail(QL_E_INVALID, "a_packed must be 1 or 2 for SiLU-and-mul plans");
-  // start from the merged linear's own plan (table or heuristic), then keep
-  // the fields the SiLU-and-mul kernels are instantiated for
+  // a swept SiLU-and-mul entry first (timed as a forward)
+  ql_config tc;
+  if (!std::getenv("QLINEAR_FORCE") && table_lookup(fmt, 1, 3, M, N, K, &tc)) {
+    if (a_packed == 1 && tc.a_mode == 4) tc.a_mode = 2;   // qlinear_run takes quantized activations
+    if (build_plan(fmt, M, N, K, tc, QL_SRC_TABLE, out_plan, true) == QL_OK) return QL_OK;
+  }
+  // else the merged linear's own plan (table or heuristic), keeping the
+  // fields the SiLU-and-mul kernels are instantiated for
   ql_plan base = nullptr;
   ql_status st = plan_for_layout(fmt, 1, a_packed, M, N, K, &base);
   if (st != QL_OK) return st;

@@ -109,6 +109,14 @@ def phase1_candidates(fmt, M, N, K, layout=0):
         if M <= 64 and layout >= 1:
             yield from decode_m64_candidates(M, N, K, layout)
         return
+    if layout == 4:
+        # SiLU-and-mul plans: 32 rows a wave (gate and up), packed or fused activations
+        for swap, (wn, wk), pf, split, amode in itertools.product(
+                (0, 1), ((1, 4), (2, 2), (4, 1), (1, 8), (2, 4)), (1, 2), SPLITS,
+                (2, 4) if fused_ok(fmt, M, K) else (2,)):
+            yield dict(swap_ab=swap, split_k=split, waves_n=wn, waves_k=wk, rows_per_wave=32, prefetch=pf,
+                       a_mode=amode, w_lds=0, w_layout=1)
+        return
     if layout == 3:
         seen = set()
         for (wn, wk), rows, split in itertools.product(WAVES_PACKED, (16, 32, 64), SPLITS):
@@ -137,7 +145,8 @@ class Timer:
     """Times plans for one (format, N, K, operand layouts) on rotated weight copies.
 
     layout 0: row-major W_q and A_q; 1: packed W_q, row-major A_q; 2: packed W_q and A_q;
-    3: packed W_q, whole forward (quantizer + GEMM, or the fused launch) timed."""
+    3: packed W_q, whole forward (quantizer + GEMM, or the fused launch) timed;
+    4: as 3 for SiLU-and-mul plans of a merged gate/up weight (output [M, N/2])."""
 
     def __init__(self, fmt, N, K, x, w, stream, layout=0, max_copies=48):
         self.fmt, self.N, self.K, self.layout = fmt, N, K, layout
@@ -156,18 +165,18 @@ class Timer:
         """Median per-launch microseconds and the output of one launch."""
         fmt, s = self.fmt, self.stream
         xm = self.x[:M].contiguous()
-        if self.layout == 3:
+        if self.layout >= 3:
             a_q = ql.act_buffer(plan)
             a_s = torch.empty(ql.act_scale_shape(fmt, M, self.K), dtype=torch.float32, device="cuda")
         elif self.layout == 2:
             a_q, a_s = ql.quantize_act_packed(fmt, xm)
         else:
             a_q, a_s = ql.quantize_act(fmt, xm)
-        y = torch.empty(M, self.N, dtype=torch.bfloat16, device="cuda")
+        y = torch.empty(M, self.N // 2 if self.layout == 4 else self.N, dtype=torch.bfloat16, device="cuda")
         wsp = plan.new_workspace()
 
         def one(c, stream=None):
-            if self.layout == 3:
+            if self.layout >= 3:
                 ql.qlinear_forward(plan, xm, a_q, a_s, self.wq[c], self.ws[c], y, wsp, stream=stream)
             else:
                 ql.qlinear_run(plan, a_q, a_s, self.wq[c], self.ws[c], y, wsp, stream=stream)
@@ -232,7 +241,8 @@ def sweep_point(timer, fmt, M, N, K, log=print, top=6):
         for pf in ((cfg["prefetch"],) if cfg.get("algo") == ql.ALGO_TILED else (2, 1)):
             try:
                 cfg = dict(cfg, prefetch=pf)
-                plan = ql.qlinear_plan_with_config(fmt, M, N, K, cfg)
+                plan = (ql.qlinear_plan_glu_with_config if timer.layout == 4 else ql.qlinear_plan_with_config)(
+                    fmt, M, N, K, cfg)
                 break
             except ql.QLinearError:
                 continue
@@ -261,7 +271,8 @@ def sweep_point(timer, fmt, M, N, K, log=print, top=6):
                 continue
             seen.add(k)
             try:
-                plan = ql.qlinear_plan_with_config(fmt, M, N, K, cfg)
+                plan = (ql.qlinear_plan_glu_with_config if timer.layout == 4 else ql.qlinear_plan_with_config)(
+                    fmt, M, N, K, cfg)
                 us, y = timer.measure(plan, M)
             except ql.QLinearError:
                 continue
@@ -274,12 +285,12 @@ def sweep_point(timer, fmt, M, N, K, log=print, top=6):
     return [chosen] + [r for r in results if r is not chosen]
 
 
-def table_line(fmt, M, N, K, cfg, us, forward=False):
+def table_line(fmt, M, N, K, cfg, us, kind=""):
     c = ql.make_config(**cfg)
     return "%d %d %d %d %d %d %d %d %d %d %d %d %d %d %d %d %.3f%s" % (
         fmt, M, N, K, c["algo"], c["swap_ab"], c["split_k"], c["waves_n"], c["waves_k"], c["rows_per_wave"],
         c["prefetch"], c["a_mode"], c["w_lds"], c["w_layout"], c["tile_m"], c["tile_n"], us,
-        " fwd" if forward else "")
+        (" " + kind) if kind else "")
 
 
 def main(argv=None):
@@ -287,9 +298,10 @@ def main(argv=None):
     ap.add_argument("--workloads", default=",".join(c.name for c in decode_workloads()))
     ap.add_argument("--out", default=ql.DEFAULT_TABLE)
     ap.add_argument("--ms", default=None, help="comma list overriding the token counts")
-    ap.add_argument("--layouts", default="0,1,2,3",
+    ap.add_argument("--layouts", default="0,1,2,3,4",
                     help="operand layouts to tune: 0 row-major W and A, 1 packed W, 2 packed W and A, "
-                         "3 forward plans (packed W; fused quantization or not)")
+                         "3 forward plans (packed W; fused quantization or not), 4 SiLU-and-mul forward plans "
+                         "of the gate_up shapes")
     args = ap.parse_args(argv)
     torch.cuda.set_device(0)
     stream = torch.cuda.Stream()
@@ -310,6 +322,8 @@ def main(argv=None):
                 x, w = make_inputs(K, N, max(ms), wl.sigma_w, seed=wl.seed)
                 for layout in [int(v) for v in args.layouts.split(",")]:
                     lms = [m for m in ms if layout != 3 or fused_ok(wl.fmt, m, K)]
+                    if layout == 4 and (lab != "gate_up" or N % 32):
+                        continue        # SiLU-and-mul plans: the merged gate/up projection only
                     if not lms:
                         continue
                     timer = Timer(wl.fmt, N, K, x, w, stream, layout=layout)
@@ -317,7 +331,8 @@ def main(argv=None):
                         t0 = time.time()
                         res = sweep_point(timer, wl.fmt, M, N, K)
                         us, cfg = res[0]
-                        f.write(table_line(wl.fmt, M, N, K, cfg, us, forward=layout == 3) + "\n")
+                        f.write(table_line(wl.fmt, M, N, K, cfg, us, kind={3: "fwd", 4: "glu"}.get(layout, ""))
+                                + "\n")
                         f.flush()
                         n += 1
                         print("%-26s %-8s L%d M=%-3d best %.3f us (%s)  [%d cands, %.1fs]" % (

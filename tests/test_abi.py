@@ -274,3 +274,17 @@ def test_glu_plans_are_validated_on_host():
     assert q.facts["epilogue"] == 1 and q.config["rows_per_wave"] == 32
     with pytest.raises(ql.QLinearError):
         ql.qlinear_plan_glu(ql.FP8_DYNAMIC, 2, 24576, 4096, 0)
+
+
+def test_glu_table_entries(tmp_path):
+    t = tmp_path / "t.txt"
+    t.write_text("0 4 1024 512 0 1 2 2 2 32 2 2 0 1 0 0 5.0 glu\n"
+                 "0 4 1024 512 0 0 1 1 4 16 2 2 0 1 0 0 4.0\n")
+    assert ql.qlinear_table_load(str(t)) == 2
+    try:
+        p = ql.qlinear_plan_glu(ql.FP8_DYNAMIC, 3, 1024, 512, 1)
+        assert p.facts["source"] == "table" and p.config["split_k"] == 2 and p.config["waves_n"] == 2
+        p = ql.qlinear_plan_layouts(ql.FP8_DYNAMIC, 3, 1024, 512, 1, 1)     # the plain plan ignores glu entries
+        assert p.config["rows_per_wave"] == 16 and p.facts["epilogue"] == 0
+    finally:
+        ql.qlinear_table_clear()

@@ -375,7 +375,8 @@ def _table_entries():
         if not f or f[0].startswith("#"):
             continue
         v = [int(t) for t in f[:16]]
-        out.append(tuple(v) + (int(len(f) > 17 and f[17] == "fwd"),))
+        kind = f[17] if len(f) > 17 else ""
+        out.append(tuple(v) + ({"": 0, "fwd": 1, "glu": 2}[kind],))
     return out
 
 
@@ -394,7 +395,8 @@ def _shape_config(fmt, N, K):
 
 
 @pytest.mark.parametrize("entry", _table_entries(),
-                         ids=lambda e: "f%d-M%d-N%d-K%d-L%d%s" % (e[0], e[1], e[2], e[3], e[13], "-fwd" * e[16]))
+                         ids=lambda e: "f%d-M%d-N%d-K%d-L%d%s" % (e[0], e[1], e[2], e[3], e[13],
+                                                                  ["", "-fwd", "-glu"][e[16]]))
 def test_every_table_entry_matches_oracle(entry):
     """Each configuration the shipped sweep table selects, run at its own
     (format, M, N, K) and weight layout, against the oracle on sampled columns
@@ -404,6 +406,9 @@ def test_every_table_entry_matches_oracle(entry):
     wname, lab = _shape_config(fmt, N, K)
     x, w, w_q, w_s = _weights(wname, lab, N, K)
     xm = x[:M]
+    if entry[16] == 2:
+        _check_glu_entry(fmt, M, N, K, cfg, xm, w, w_q, w_s)
+        return
     a_q, a_s = ql.quantize_act(fmt, xm.cuda())
     plan = ql.qlinear_plan_with_config(fmt, M, N, K, cfg)
     y = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
@@ -434,3 +439,27 @@ def test_every_table_entry_matches_oracle(entry):
     else:
         st = fp8_check(fmt, r, ysel, plan.facts["chunks"])
         assert st["ok"] and st["frac_within_ulp"] >= 0.95, (cfg, st)
+
+
+def _check_glu_entry(fmt, M, N, K, cfg, xm, w, w_q, w_s):
+    """A SiLU-and-mul table entry: forward with the merged gate/up weight,
+    64 sampled output columns (whole 128-row blocks for Block_FP8) against
+    the oracle's glu_reference."""
+    I = N // 2
+    plan = ql.qlinear_plan_glu_with_config(fmt, M, N, K, cfg)
+    y = torch.empty(M, I, dtype=torch.bfloat16, device="cuda")
+    a_p = ql.act_buffer(plan)
+    a_s = torch.empty(ql.act_scale_shape(fmt, M, K), dtype=torch.float32, device="cuda")
+    ql.qlinear_forward(plan, xm.cuda(), a_p, a_s, ql.pack_weight(w_q), w_s, y, plan.new_workspace())
+    torch.cuda.synchronize()
+    h = host_bf16_bits(y)
+    rng = np.random.default_rng(N + M)
+    if fmt == ql.BLOCK_FP8:
+        nb = int(rng.integers(0, I // 128))
+        cols = np.arange(nb * 128, nb * 128 + 128)
+    else:
+        cols = np.sort(rng.choice(I, 64, replace=False))
+    r = oracle.reference(fmt, bf16_bits(xm), bf16_bits(w[torch.from_numpy(np.concatenate([cols, I + cols]))]))
+    h_ref, h_true, bound = oracle.glu_reference(fmt, r, split=plan.facts["chunks"])
+    st = oracle.check_fp8_parity(h[:, cols], h_ref, h_true, bound)
+    assert st["ok"] and st["frac_within_ulp"] >= 0.95, (cfg, st)
