@@ -7,7 +7,9 @@ GPU path computes:
 
 plus the dynamic activation quantizer and the offline weight quantizer, for
 the three formats of the pages (FP8_Dynamic, W8A8_INT8, Block_FP8), and the
-SiLU-and-mul epilogue of a merged gate/up projection (``glu``).
+SiLU-and-mul epilogue of a merged gate/up projection (``glu``), and the
+MXFP8 linear (E4M3 elements with E8M0 scales per 32 values along K, the
+scales applied inside the product; ``mx``).
 
 Who may use it: only ``tests/``, ``__graft_entry__.smoke()`` and the
 ``cpu_baseline`` leg of ``bench.py``.  The product path (the HIP library and
@@ -28,8 +30,8 @@ taken is stated in the docstring.
 Pins.  Every function here is checked in ``tests/test_oracle_*.py`` against
 something other than itself: an independent exact-rational (Fraction)
 implementation on tiny inputs, closed forms, layout one-hot probes, the OCP
-OFP8 specification's E4M3 values, torch's CPU float8 cast, and invariants of
-the method (variant order independence, quantizer bounds).  No function is
+OFP8 specification's E4M3 values, torch's CPU float8 cast, the bf16 bit
+fields (MX shared exponents, exhaustively), and invariants of the method (variant order independence, quantizer bounds).  No function is
 "parity unpinned".
 """
 
@@ -42,6 +44,8 @@ from .linear import (contract_exact, contract_abs, epilogue, reference, MATRIX_C
                      contract_split_order, contract_swap_ab,
                      emulate_fp32_accumulation)
 from .glu import silu, glu_values, glu_reference, SILU_SLOPE_MAX
+from .mx import (MX_BLOCK, mx_shared_exponent, mx_quantize, mx_dequantize, mx_contract_exact,
+                 mx_contract_abs, mx_tolerance_bound, mx_reference)
 
 __all__ = [
     "bf16_bits_from_f32", "bf16_bits_to_f32", "ulp_bf16", "f32",
@@ -52,4 +56,6 @@ __all__ = [
     "tolerance_bound", "summation_depth", "MATRIX_CORE_ETA", "check_fp8_parity",
     "silu", "glu_values", "glu_reference", "SILU_SLOPE_MAX",
     "contract_split_order", "contract_swap_ab", "emulate_fp32_accumulation",
+    "MX_BLOCK", "mx_shared_exponent", "mx_quantize", "mx_dequantize", "mx_contract_exact",
+    "mx_contract_abs", "mx_tolerance_bound", "mx_reference",
 ]

@@ -99,3 +99,26 @@ def dot_int(a_row, w_row):
 
 def dot_frac(a_row, w_row):
     return sum((x * y for x, y in zip(a_row, w_row)), F(0))
+
+
+def floor_log2(a):
+    """floor(log2 a) of a positive rational, by integer comparison."""
+    e = a.numerator.bit_length() - a.denominator.bit_length()
+    while F(2) ** e > a:
+        e -= 1
+    while F(2) ** (e + 1) <= a:
+        e += 1
+    return e
+
+
+def mx_quantize_block(values, negzero):
+    """One MXFP8 block (OCP MX: shared exponent floor(log2 amax) - 8, clamped to
+    [-127, 127]; -127 for an all-zero block; elements v / 2**e clamped to
+    +-448 and rounded to E4M3).  Returns ([(value, neg)], e)."""
+    amax = max((abs(v) for v in values), default=F(0))
+    e = -127 if amax == 0 else max(-127, min(127, floor_log2(amax) - 8))
+    out = []
+    for v, nz in zip(values, negzero):
+        t = max(F(-448), min(F(448), v / F(2) ** e))
+        out.append((re4m3(t), v < 0 or (v == 0 and nz)))
+    return out, e
