@@ -320,7 +320,7 @@ def main(argv=None):
         pts.append(dict(lab=lab, N=N, K=K, M=M, plan=plan, cfg=cfg, facts=facts,
                         x=sh["x"][:M].contiguous(),
                         a_q=ql.act_buffer(plan, dev),
-                        a_s=torch.empty(ql.act_scale_shape(fmt, M, K), dtype=torch.float32, device=dev),
+                        a_s=torch.empty(ql.act_scale_shape(fmt, M, K), dtype=ql.scale_dtype(fmt), device=dev),
                         y=torch.empty(M, N, dtype=torch.bfloat16, device=dev),
                         wsp=plan.new_workspace(dev), fused=fused,
                         bytes=algorithmic_bytes(fmt, M, N, K), qbytes=quantizer_bytes(fmt, M, K),
@@ -496,7 +496,7 @@ def glu_pass(ql, wl, pts, shapes, stream, args):
             plan = p["plan"] if kind == "plain" else ql.qlinear_plan_glu(fmt, M, N, K, 2)
             y = torch.empty(M, N if kind == "plain" else N // 2, dtype=torch.bfloat16, device="cuda")
             a_q = ql.act_buffer(plan)
-            a_s = torch.empty(ql.act_scale_shape(fmt, M, K), dtype=torch.float32, device="cuda")
+            a_s = torch.empty(ql.act_scale_shape(fmt, M, K), dtype=ql.scale_dtype(fmt), device="cuda")
             wsp = plan.new_workspace()
             with torch.cuda.stream(stream):
                 ql.qlinear_graph_begin(stream)

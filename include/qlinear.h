@@ -18,23 +18,34 @@
  *   QL_FP8_DYNAMIC  OCP E4M3 activations scaled per token, weights per output channel
  *   QL_W8A8_INT8    int8 activations per token, weights per output channel
  *   QL_BLOCK_FP8    E4M3 with 1x128 activation groups and 128x128 weight blocks
+ *   QL_MXFP8        E4M3 with one E8M0 (power-of-two) scale per 32 values along K,
+ *                   activations and weights alike
  * Quantization rule (the pages give none; the plain reading): symmetric
  * absmax, s = fl(amax / Q) with Q = 127 (int8) or 448 (E4M3); code =
  * round-half-even(fl(x / s)) clamped to [-Q, Q]; an all-zero group gets s = 1.
+ * MXFP8 ([Noticias] "¿Qué son vLLM y Helion?" lists block-scaled NVFP4 among
+ * the formats linear backends serve; gfx950's counterpart is OCP
+ * microscaling, whose v1.0 rule is taken here): per block of 32 values
+ * e = floor(log2(amax)) - 8 clamped to [-127, 127] (-127 for an all-zero
+ * block), scale byte e + 127, code = E4M3 round-to-nearest-even of
+ * x * 2^-e clamped to [-448, 448].  The matrix core applies the scales inside
+ * the product: Y = bf16(sum_k 2^(ea+ew) a_k w_k), no scale epilogue.
  *
  * Data layouts (all row-major, caller-owned device memory):
  *   X      bf16   [M, K]                 activations (input of the quantizer)
  *   A_q    1 byte [M, K]                 int8 or E4M3 codes
  *   s_a    fp32   [M]  or [M, K/128]     (Block_FP8: one scale per 1x128 group)
+ *          uint8  [M, K/32]              (MXFP8: E8M0 bytes; every scale pointer of
+ *                                        this header is void* for that reason)
  *   W      bf16   [N, K]                 weights (input of the weight quantizer)
  *   W_q    1 byte [N, K]                 row n = output channel n, K contiguous
- *   s_w    fp32   [N]  or [ceil(N/128), K/128]
+ *   s_w    fp32   [N]  or [ceil(N/128), K/128];  MXFP8: uint8 [N, K/32]
  *   Y      bf16   [M, N]
  *
  * Argument rules checked on the host before any launch (QL_E_INVALID /
  * QL_E_ALIGN / QL_E_UNSUPPORTED otherwise):
- *   M, N, K >= 0; K % 16 == 0 (rows are 16-byte aligned); Block_FP8 needs
- *   K % 128 == 0; N * K and M * K at most 2^30; device pointers 16-byte
+ *   M, N, K >= 0; K % 16 == 0 (rows are 16-byte aligned); Block_FP8 and
+ *   MXFP8 need K % 128 == 0; N * K and M * K at most 2^30; device pointers 16-byte
  *   aligned and non-null whenever the sizes make them used.
  *   M == 0 or N == 0 is a successful no-op.  K == 0 gives Y == 0.
  *
@@ -65,7 +76,8 @@ extern "C" {
 typedef enum {
   QL_FP8_DYNAMIC = 0,
   QL_W8A8_INT8 = 1,
-  QL_BLOCK_FP8 = 2
+  QL_BLOCK_FP8 = 2,
+  QL_MXFP8 = 3
 } ql_format;
 
 typedef enum {
@@ -161,12 +173,15 @@ const char* qlinear_last_error(void);
 /*
  * Dynamic activation quantizer ([Summary] last paragraph of "Put algorithm
  * selection inside the search space": per-token or 1x128 activation scaling).
- *   x_bf16  [M, K] bf16 in;  a_q [M, K] codes out;  a_scale fp32 [M] or [M, K/128] out.
+ *   x_bf16  [M, K] bf16 in;  a_q [M, K] codes out;  a_scale fp32 [M] or [M, K/128]
+ *   out (MXFP8: E8M0 bytes [M, K/32]).
  * Bit-exact contract: amax exact in fp32, IEEE division, round-half-even,
- * clamp, E4M3 round-to-nearest-even, fp32 subnormals kept.
+ * clamp, E4M3 round-to-nearest-even, fp32 subnormals kept (MXFP8: the
+ * shared exponent from amax's bits, an exact power-of-two scaling, E4M3
+ * round-to-nearest-even).
  */
 ql_status qlinear_quantize_act(int32_t fmt, const void* x_bf16, int64_t M, int64_t K,
-                               void* a_q, float* a_scale, void* stream);
+                               void* a_q, void* a_scale, void* stream);
 
 /*
  * The same quantizer writing the packed activation layout that plans with
@@ -179,7 +194,7 @@ ql_status qlinear_quantize_act(int32_t fmt, const void* x_bf16, int64_t M, int64
  */
 int64_t qlinear_packed_act_bytes(int64_t M, int64_t K);
 ql_status qlinear_quantize_act_packed(int32_t fmt, const void* x_bf16, int64_t M, int64_t K,
-                                      void* a_packed, float* a_scale, void* stream);
+                                      void* a_packed, void* a_scale, void* stream);
 
 /*
  * The E4M3 encoder every FP8 quantizer of the library applies to its
@@ -194,11 +209,12 @@ ql_status qlinear_encode_e4m3(const float* x, int64_t n, void* codes, void* stre
 /*
  * Offline weight quantizer: per output channel (rows of W) or per 128x128
  * block for Block_FP8 (the last block row may be ragged).
- *   w_bf16 [N, K] in;  w_q [N, K] out;  w_scale fp32 [N] or [ceil(N/128), K/128] out.
+ *   w_bf16 [N, K] in;  w_q [N, K] out;  w_scale fp32 [N] or [ceil(N/128), K/128]
+ *   out (MXFP8: E8M0 bytes [N, K/32], the activation rule applied to rows of W).
  * Same rounding contract as the activation quantizer.
  */
 ql_status qlinear_quantize_weight(int32_t fmt, const void* w_bf16, int64_t N, int64_t K,
-                                  void* w_q, float* w_scale, void* stream);
+                                  void* w_q, void* w_scale, void* stream);
 
 /*
  * Offline weight packing (optional, for the packed-weight plans).  The
@@ -296,22 +312,26 @@ void qlinear_plan_destroy(ql_plan plan);
  * Epilogue op order (fixed): INT8 y = bf16(fl(fl(f32(acc) * s_a[m]) * s_w[n]))
  * with an exact int32 accumulator; FP8_Dynamic the same on the fp32
  * accumulator; Block_FP8 applies s_a[m,g] * s_w[n/128,g] to every 128-wide K
- * group's partial inside the K loop and rounds the fp32 sum to bf16.
+ * group's partial inside the K loop and rounds the fp32 sum to bf16; MXFP8
+ * hands the E8M0 bytes to the scaled matrix-core instruction, which applies
+ * them to every 32-wide block of products, and rounds the fp32 sum to bf16.
+ * MXFP8 plans use the decode algorithm (M <= 64) with packed weights and
+ * packed activations (a_mode 2 or 3).
  * a_q is in the plan's activation layout: row-major [M, K], or packed when
  * the plan's a_mode is 2 or 3; w_q in the plan's weight layout (w_layout).
  * Enqueue-only; workspace may be NULL when qlinear_workspace_bytes is 0.
  */
-ql_status qlinear_run(ql_plan plan, const void* a_q, const float* a_scale,
-                      const void* w_q, const float* w_scale, void* y_bf16,
+ql_status qlinear_run(ql_plan plan, const void* a_q, const void* a_scale,
+                      const void* w_q, const void* w_scale, void* y_bf16,
                       void* workspace, void* stream);
 
 /*
  * Test hook: same launch as qlinear_run, and additionally stores the raw
  * accumulator per output element into acc_out [M, N] (int32 for INT8, fp32
- * for FP8_Dynamic, the scaled fp32 sum for Block_FP8) before the bf16 rounding.
+ * for FP8_Dynamic, the scaled fp32 sum for Block_FP8 and MXFP8) before the bf16 rounding.
  */
-ql_status qlinear_run_debug_acc(ql_plan plan, const void* a_q, const float* a_scale,
-                                const void* w_q, const float* w_scale, void* y_bf16,
+ql_status qlinear_run_debug_acc(ql_plan plan, const void* a_q, const void* a_scale,
+                                const void* w_q, const void* w_scale, void* y_bf16,
                                 void* workspace, void* acc_out, void* stream);
 
 /*
@@ -323,8 +343,8 @@ ql_status qlinear_run_debug_acc(ql_plan plan, const void* a_q, const float* a_sc
  * (identical to what qlinear_quantize_act_packed writes).  qlinear_run
  * rejects an a_mode 4 plan with QL_E_INVALID.
  */
-ql_status qlinear_forward(ql_plan plan, const void* x_bf16, void* a_q, float* a_scale,
-                          const void* w_q, const float* w_scale, void* y_bf16,
+ql_status qlinear_forward(ql_plan plan, const void* x_bf16, void* a_q, void* a_scale,
+                          const void* w_q, const void* w_scale, void* y_bf16,
                           void* workspace, void* stream);
 
 /*

@@ -3,8 +3,9 @@
     Y[M, N] = s_a[m] * s_w[n] * (A_q[M, K] . W_q[N, K]^T)     (bf16 out)
 
 Formats: FP8_Dynamic (OCP E4M3, per-token / per-channel), W8A8_INT8
-(per-token / per-channel) and Block_FP8 (1x128 activation groups, 128x128
-weight blocks).  All arithmetic runs in the hand-written gfx950 HIP kernels
+(per-token / per-channel), Block_FP8 (1x128 activation groups, 128x128
+weight blocks) and MXFP8 (E4M3 with one E8M0 scale byte per 32 values along
+K, applied by the matrix core).  All arithmetic runs in the hand-written gfx950 HIP kernels
 of ``libqlinear.so`` behind the C ABI of ``include/qlinear.h``; this module
 only marshals torch tensors (device memory) and streams into that ABI, with
 the same function names.  There is no CPU or PyTorch fallback: if the
@@ -19,9 +20,9 @@ import torch
 from . import _lib
 from ._lib import QLConfig, QLPlanFacts
 
-FP8_DYNAMIC, W8A8_INT8, BLOCK_FP8 = 0, 1, 2
-FORMATS = (FP8_DYNAMIC, W8A8_INT8, BLOCK_FP8)
-FORMAT_NAMES = {FP8_DYNAMIC: "FP8_Dynamic", W8A8_INT8: "W8A8_INT8", BLOCK_FP8: "Block_FP8"}
+FP8_DYNAMIC, W8A8_INT8, BLOCK_FP8, MXFP8 = 0, 1, 2, 3
+FORMATS = (FP8_DYNAMIC, W8A8_INT8, BLOCK_FP8, MXFP8)
+FORMAT_NAMES = {FP8_DYNAMIC: "FP8_Dynamic", W8A8_INT8: "W8A8_INT8", BLOCK_FP8: "Block_FP8", MXFP8: "MXFP8"}
 ALGO_DECODE, ALGO_TILED = 0, 1
 SOURCES = {0: "table", 1: "heuristic", 2: "custom"}
 DEFAULT_TABLE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "tables", "decode_table.txt")
@@ -68,16 +69,25 @@ def _ptr(t, name, dtype=None, required=True):
 
 
 CODE_DTYPES = (torch.int8, torch.uint8, torch.float8_e4m3fn)
+SCALE_DTYPES = (torch.float32, torch.uint8)      # binary32 scales, or MXFP8's E8M0 bytes
 
 
 # ----------------------------------------------------------------- shapes
 
 def act_scale_shape(fmt, M, K):
+    if fmt == MXFP8:
+        return (M, K // 32)
     return (M, K // 128) if fmt == BLOCK_FP8 else (M,)
 
 
 def weight_scale_shape(fmt, N, K):
+    if fmt == MXFP8:
+        return (N, K // 32)
     return (-(-N // 128), K // 128) if fmt == BLOCK_FP8 else (N,)
+
+
+def scale_dtype(fmt):
+    return torch.uint8 if fmt == MXFP8 else torch.float32
 
 
 def code_dtype(fmt):
@@ -89,7 +99,7 @@ def code_dtype(fmt):
 def qlinear_quantize_act(fmt, x, a_q, a_scale, stream=None):
     M, K = x.shape
     _check(lib().qlinear_quantize_act(fmt, _ptr(x, "x", torch.bfloat16), M, K, _ptr(a_q, "a_q", CODE_DTYPES),
-                                      _ptr(a_scale, "a_scale", torch.float32), _stream(stream)),
+                                      _ptr(a_scale, "a_scale", SCALE_DTYPES), _stream(stream)),
            "qlinear_quantize_act")
 
 
@@ -101,14 +111,14 @@ def qlinear_quantize_act_packed(fmt, x, a_packed, a_scale, stream=None):
     M, K = x.shape
     _check(lib().qlinear_quantize_act_packed(fmt, _ptr(x, "x", torch.bfloat16), M, K,
                                              _ptr(a_packed, "a_packed", CODE_DTYPES),
-                                             _ptr(a_scale, "a_scale", torch.float32), _stream(stream)),
+                                             _ptr(a_scale, "a_scale", SCALE_DTYPES), _stream(stream)),
            "qlinear_quantize_act_packed")
 
 
 def qlinear_quantize_weight(fmt, w, w_q, w_scale, stream=None):
     N, K = w.shape
     _check(lib().qlinear_quantize_weight(fmt, _ptr(w, "w", torch.bfloat16), N, K, _ptr(w_q, "w_q", CODE_DTYPES),
-                                         _ptr(w_scale, "w_scale", torch.float32), _stream(stream)),
+                                         _ptr(w_scale, "w_scale", SCALE_DTYPES), _stream(stream)),
            "qlinear_quantize_weight")
 
 
@@ -116,7 +126,7 @@ def quantize_act(fmt, x, stream=None):
     """Allocate (A_q, s_a) and run the activation quantizer."""
     M, K = x.shape
     a_q = torch.empty(M, K, dtype=code_dtype(fmt), device=x.device)
-    a_s = torch.empty(act_scale_shape(fmt, M, K), dtype=torch.float32, device=x.device)
+    a_s = torch.empty(act_scale_shape(fmt, M, K), dtype=scale_dtype(fmt), device=x.device)
     qlinear_quantize_act(fmt, x, a_q, a_s, stream)
     return a_q, a_s
 
@@ -125,7 +135,7 @@ def quantize_act_packed(fmt, x, stream=None):
     """Allocate (packed A_q as a flat code buffer, s_a) and run the packed-layout quantizer."""
     M, K = x.shape
     a_p = torch.empty(max(qlinear_packed_act_bytes(M, K), 16), dtype=code_dtype(fmt), device=x.device)
-    a_s = torch.empty(act_scale_shape(fmt, M, K), dtype=torch.float32, device=x.device)
+    a_s = torch.empty(act_scale_shape(fmt, M, K), dtype=scale_dtype(fmt), device=x.device)
     qlinear_quantize_act_packed(fmt, x, a_p, a_s, stream)
     return a_p, a_s
 
@@ -140,7 +150,7 @@ def quantize_weight(fmt, w, stream=None):
     """Allocate (W_q, s_w) and run the weight quantizer."""
     N, K = w.shape
     w_q = torch.empty(N, K, dtype=code_dtype(fmt), device=w.device)
-    w_s = torch.empty(weight_scale_shape(fmt, N, K), dtype=torch.float32, device=w.device)
+    w_s = torch.empty(weight_scale_shape(fmt, N, K), dtype=scale_dtype(fmt), device=w.device)
     qlinear_quantize_weight(fmt, w, w_q, w_s, stream)
     return w_q, w_s
 
@@ -294,16 +304,16 @@ def qlinear_plan_with_config(fmt, M, N, K, cfg):
 # ----------------------------------------------------------------- GEMM
 
 def qlinear_run(plan, a_q, a_scale, w_q, w_scale, y, workspace=None, stream=None):
-    _check(lib().qlinear_run(plan.handle, _ptr(a_q, "a_q", CODE_DTYPES), _ptr(a_scale, "a_scale", torch.float32),
-                             _ptr(w_q, "w_q", CODE_DTYPES), _ptr(w_scale, "w_scale", torch.float32),
+    _check(lib().qlinear_run(plan.handle, _ptr(a_q, "a_q", CODE_DTYPES), _ptr(a_scale, "a_scale", SCALE_DTYPES),
+                             _ptr(w_q, "w_q", CODE_DTYPES), _ptr(w_scale, "w_scale", SCALE_DTYPES),
                              _ptr(y, "y", torch.bfloat16), _ptr(workspace, "workspace", required=False),
                              _stream(stream)), "qlinear_run")
 
 
 def qlinear_run_debug_acc(plan, a_q, a_scale, w_q, w_scale, y, acc_out, workspace=None, stream=None):
     _check(lib().qlinear_run_debug_acc(plan.handle, _ptr(a_q, "a_q", CODE_DTYPES),
-                                       _ptr(a_scale, "a_scale", torch.float32), _ptr(w_q, "w_q", CODE_DTYPES),
-                                       _ptr(w_scale, "w_scale", torch.float32), _ptr(y, "y", torch.bfloat16),
+                                       _ptr(a_scale, "a_scale", SCALE_DTYPES), _ptr(w_q, "w_q", CODE_DTYPES),
+                                       _ptr(w_scale, "w_scale", SCALE_DTYPES), _ptr(y, "y", torch.bfloat16),
                                        _ptr(workspace, "workspace", required=False),
                                        _ptr(acc_out, "acc_out", (torch.int32, torch.float32)), _stream(stream)),
            "qlinear_run_debug_acc")
@@ -311,8 +321,8 @@ def qlinear_run_debug_acc(plan, a_q, a_scale, w_q, w_scale, y, acc_out, workspac
 
 def qlinear_forward(plan, x, a_q, a_scale, w_q, w_scale, y, workspace=None, stream=None):
     _check(lib().qlinear_forward(plan.handle, _ptr(x, "x", torch.bfloat16), _ptr(a_q, "a_q", CODE_DTYPES),
-                                 _ptr(a_scale, "a_scale", torch.float32), _ptr(w_q, "w_q", CODE_DTYPES),
-                                 _ptr(w_scale, "w_scale", torch.float32), _ptr(y, "y", torch.bfloat16),
+                                 _ptr(a_scale, "a_scale", SCALE_DTYPES), _ptr(w_q, "w_q", CODE_DTYPES),
+                                 _ptr(w_scale, "w_scale", SCALE_DTYPES), _ptr(y, "y", torch.bfloat16),
                                  _ptr(workspace, "workspace", required=False), _stream(stream)),
            "qlinear_forward")
 

@@ -51,16 +51,19 @@ constexpr int64_t kLdsLimit = 160 * 1024 - 256;
 constexpr int64_t kFusedMaxValues = 16384;
 constexpr int kBuckets[] = {1, 2, 4, 8, 16, 24, 32};
 
-bool valid_fmt(int32_t f) { return f == QL_FP8_DYNAMIC || f == QL_W8A8_INT8 || f == QL_BLOCK_FP8; }
+bool valid_fmt(int32_t f) { return f == QL_FP8_DYNAMIC || f == QL_W8A8_INT8 || f == QL_BLOCK_FP8 || f == QL_MXFP8; }
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool is_pow2(int64_t v) { return v > 0 && (v & (v - 1)) == 0; }
-int kernel_fmt(int32_t f) { return f == QL_W8A8_INT8 ? qlk::FMT_INT8 : (f == QL_BLOCK_FP8 ? qlk::FMT_BLOCK : qlk::FMT_FP8); }
+int kernel_fmt(int32_t f) {
+  return f == QL_W8A8_INT8 ? qlk::FMT_INT8 : f == QL_BLOCK_FP8 ? qlk::FMT_BLOCK : f == QL_MXFP8 ? qlk::FMT_MX : qlk::FMT_FP8;
+}
 
 ql_status check_sizes(int32_t fmt, int64_t R, int64_t K, const char* rname) {
   if (!valid_fmt(fmt)) return fail(QL_E_INVALID, "unknown format %d", fmt);
   if (R < 0 || K < 0) return fail(QL_E_INVALID, "negative size (%s=%lld, K=%lld)", rname, (long long)R, (long long)K);
   if (K % 16) return fail(QL_E_INVALID, "K=%lld is not a multiple of 16", (long long)K);
   if (fmt == QL_BLOCK_FP8 && K % 128) return fail(QL_E_INVALID, "Block_FP8 needs K %% 128 == 0 (K=%lld)", (long long)K);
+  if (fmt == QL_MXFP8 && K % 128) return fail(QL_E_INVALID, "MXFP8 needs K %% 128 == 0 (K=%lld)", (long long)K);
   if (R * K > (int64_t(1) << 30)) return fail(QL_E_UNSUPPORTED, "%s*K=%lld exceeds 2^30", rname, (long long)(R * K));
   return QL_OK;
 }
@@ -157,7 +160,8 @@ ql_config heuristic_tiled(int32_t layout, bool a_packed, int64_t M, int64_t N, i
 }
 
 ql_config heuristic_config(int32_t fmt, int32_t layout, bool a_packed, int64_t M, int64_t N, int64_t K) {
-  if (M > 32) return heuristic_tiled(layout, a_packed, M, N, K);
+  // MXFP8 has no tiled kernel: its decode kernel serves up to 64 tokens
+  if (M > 32 && !(fmt == QL_MXFP8 && M <= 64)) return heuristic_tiled(layout, a_packed, M, N, K);
   ql_config c{};
   c.w_layout = layout;
   c.algo = QL_ALGO_DECODE;
@@ -258,6 +262,13 @@ ql_status build_plan(int32_t fmt, int64_t M, int64_t N, int64_t K, const ql_conf
     if (cfg.w_layout != 1 || cfg.rows_per_wave != 32 || (cfg.a_mode != 2 && cfg.a_mode != 4))
       return fail(QL_E_UNSUPPORTED, "SiLU-and-mul plans need packed weights, rows_per_wave 32 and a_mode 2 or 4");
   }
+  if (fmt == QL_MXFP8) {
+    if (glu) return fail(QL_E_UNSUPPORTED, "MXFP8 plans have no SiLU-and-mul epilogue");
+    if (cfg.algo != QL_ALGO_DECODE || M > 64)
+      return fail(QL_E_UNSUPPORTED, "MXFP8 runs on the decode algorithm (M <= 64)");
+    if (cfg.w_layout != 1 || (cfg.a_mode != 2 && cfg.a_mode != 3))
+      return fail(QL_E_UNSUPPORTED, "MXFP8 plans need packed weights and packed activations (a_mode 2 or 3)");
+  }
   if (cfg.algo == QL_ALGO_TILED) return build_tiled_plan(fmt, M, N, K, cfg, source, out);
   if (cfg.algo != QL_ALGO_DECODE) return fail(QL_E_INVALID, "unknown algo %d", cfg.algo);
   if (M > 64) return fail(QL_E_UNSUPPORTED, "the decode algorithm serves M <= 64 (M=%lld)", (long long)M);
@@ -326,6 +337,7 @@ ql_status build_plan(int32_t fmt, int64_t M, int64_t N, int64_t K, const ql_conf
   switch (p->key.fmt) {
     case qlk::FMT_INT8: pe = qlk::decode_dispatch_int8(p->key, dim3(1), dim3(1), (size_t)p->lds, nullptr, dummy, true); break;
     case qlk::FMT_BLOCK: pe = qlk::decode_dispatch_block(p->key, dim3(1), dim3(1), (size_t)p->lds, nullptr, dummy, true); break;
+    case qlk::FMT_MX: pe = qlk::decode_dispatch_mx(p->key, dim3(1), dim3(1), (size_t)p->lds, nullptr, dummy, true); break;
     default: pe = qlk::decode_dispatch_fp8(p->key, dim3(1), dim3(1), (size_t)p->lds, nullptr, dummy, true); break;
   }
   if (pe == hipErrorInvalidDeviceFunction) {
@@ -350,8 +362,8 @@ bool parse_force(ql_config* c) {
 
 // x / aq_out / sa_out: the fused plans' input X and their quantizer outputs
 // (a_q and a_scale are then unused).
-ql_status launch_gemm(const ql_plan_s* p, const void* a_q, const float* a_scale, const void* w_q,
-                      const float* w_scale, void* y, void* workspace, void* acc_out, hipStream_t s,
+ql_status launch_gemm(const ql_plan_s* p, const void* a_q, const void* a_scale, const void* w_q,
+                      const void* w_scale, void* y, void* workspace, void* acc_out, hipStream_t s,
                       bool from_forward = false, const void* x = nullptr, void* aq_out = nullptr,
                       float* sa_out = nullptr) {
   const bool fused = !p->tiled && p->cfg.a_mode == 4;
@@ -379,9 +391,9 @@ ql_status launch_gemm(const ql_plan_s* p, const void* a_q, const float* a_scale,
 
   qlk::DecodeArgs a{};
   a.a = static_cast<const uint8_t*>(a_q);
-  a.sa = a_scale;
+  a.sa = static_cast<const float*>(a_scale);   // MXFP8: E8M0 bytes, read as such by the kernel
   a.w = static_cast<const uint8_t*>(w_q);
-  a.sw = w_scale;
+  a.sw = static_cast<const float*>(w_scale);
   a.y = static_cast<uint16_t*>(y);
   a.ws = workspace;
   a.counters = p->ws_bytes > 0
@@ -414,6 +426,7 @@ ql_status launch_gemm(const ql_plan_s* p, const void* a_q, const float* a_scale,
   switch (p->key.fmt) {
     case qlk::FMT_INT8: e = qlk::decode_dispatch_int8(p->key, grid, block, (size_t)p->lds, s, a, false); break;
     case qlk::FMT_BLOCK: e = qlk::decode_dispatch_block(p->key, grid, block, (size_t)p->lds, s, a, false); break;
+    case qlk::FMT_MX: e = qlk::decode_dispatch_mx(p->key, grid, block, (size_t)p->lds, s, a, false); break;
     default: e = qlk::decode_dispatch_fp8(p->key, grid, block, (size_t)p->lds, s, a, false); break;
   }
   return e == hipSuccess ? QL_OK : hip_fail(e, "decode GEMM launch");
@@ -440,7 +453,7 @@ const char* qlinear_status_string(int32_t s) {
 
 const char* qlinear_last_error(void) { return g_err.c_str(); }
 
-static ql_status quantize_act(int32_t fmt, const void* x_bf16, int64_t M, int64_t K, void* a_q, float* a_scale,
+static ql_status quantize_act(int32_t fmt, const void* x_bf16, int64_t M, int64_t K, void* a_q, void* a_scale,
                               bool packed, void* stream) {
   ql_status st = check_sizes(fmt, M, K, "M");
   if (st != QL_OK) return st;
@@ -450,13 +463,18 @@ static ql_status quantize_act(int32_t fmt, const void* x_bf16, int64_t M, int64_
   if (!x_bf16 || !a_q || !a_scale) return fail(QL_E_INVALID, "NULL pointer");
   if (!aligned16(x_bf16) || !aligned16(a_q) || !aligned16(a_scale)) return fail(QL_E_ALIGN, "pointers must be 16-byte aligned");
   hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e = fmt == QL_BLOCK_FP8 ? qlk::launch_quant_groups(x_bf16, M, K, a_q, a_scale, packed, s)
-                                     : qlk::launch_quant_rows(kernel_fmt(fmt), x_bf16, M, K, a_q, a_scale, packed, s);
+  hipError_t e;
+  if (fmt == QL_MXFP8)
+    e = qlk::launch_quant_mx(x_bf16, M, K, a_q, static_cast<uint8_t*>(a_scale), packed, s);
+  else if (fmt == QL_BLOCK_FP8)
+    e = qlk::launch_quant_groups(x_bf16, M, K, a_q, static_cast<float*>(a_scale), packed, s);
+  else
+    e = qlk::launch_quant_rows(kernel_fmt(fmt), x_bf16, M, K, a_q, static_cast<float*>(a_scale), packed, s);
   return e == hipSuccess ? QL_OK : hip_fail(e, "activation quantizer launch");
 }
 
 ql_status qlinear_quantize_act(int32_t fmt, const void* x_bf16, int64_t M, int64_t K, void* a_q,
-                               float* a_scale, void* stream) {
+                               void* a_scale, void* stream) {
   return quantize_act(fmt, x_bf16, M, K, a_q, a_scale, false, stream);
 }
 
@@ -466,20 +484,25 @@ int64_t qlinear_packed_act_bytes(int64_t M, int64_t K) {
 }
 
 ql_status qlinear_quantize_act_packed(int32_t fmt, const void* x_bf16, int64_t M, int64_t K, void* a_packed,
-                                      float* a_scale, void* stream) {
+                                      void* a_scale, void* stream) {
   return quantize_act(fmt, x_bf16, M, K, a_packed, a_scale, true, stream);
 }
 
 ql_status qlinear_quantize_weight(int32_t fmt, const void* w_bf16, int64_t N, int64_t K, void* w_q,
-                                  float* w_scale, void* stream) {
+                                  void* w_scale, void* stream) {
   ql_status st = check_sizes(fmt, N, K, "N");
   if (st != QL_OK) return st;
   if (N == 0 || K == 0) return QL_OK;
   if (!w_bf16 || !w_q || !w_scale) return fail(QL_E_INVALID, "NULL pointer");
   if (!aligned16(w_bf16) || !aligned16(w_q) || !aligned16(w_scale)) return fail(QL_E_ALIGN, "pointers must be 16-byte aligned");
   hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e = fmt == QL_BLOCK_FP8 ? qlk::launch_quant_wblocks(w_bf16, N, K, w_q, w_scale, s)
-                                     : qlk::launch_quant_rows(kernel_fmt(fmt), w_bf16, N, K, w_q, w_scale, false, s);
+  hipError_t e;
+  if (fmt == QL_MXFP8)
+    e = qlk::launch_quant_mx(w_bf16, N, K, w_q, static_cast<uint8_t*>(w_scale), false, s);
+  else if (fmt == QL_BLOCK_FP8)
+    e = qlk::launch_quant_wblocks(w_bf16, N, K, w_q, static_cast<float*>(w_scale), s);
+  else
+    e = qlk::launch_quant_rows(kernel_fmt(fmt), w_bf16, N, K, w_q, static_cast<float*>(w_scale), false, s);
   return e == hipSuccess ? QL_OK : hip_fail(e, "weight quantizer launch");
 }
 
@@ -666,25 +689,25 @@ int64_t qlinear_workspace_bytes(ql_plan p) { return p ? p->ws_bytes : 0; }
 
 void qlinear_plan_destroy(ql_plan p) { delete p; }
 
-ql_status qlinear_run(ql_plan p, const void* a_q, const float* a_scale, const void* w_q, const float* w_scale,
+ql_status qlinear_run(ql_plan p, const void* a_q, const void* a_scale, const void* w_q, const void* w_scale,
                       void* y, void* workspace, void* stream) {
   if (!p) return fail(QL_E_INVALID, "plan is NULL");
   return launch_gemm(p, a_q, a_scale, w_q, w_scale, y, workspace, nullptr, static_cast<hipStream_t>(stream));
 }
 
-ql_status qlinear_run_debug_acc(ql_plan p, const void* a_q, const float* a_scale, const void* w_q,
-                                const float* w_scale, void* y, void* workspace, void* acc_out, void* stream) {
+ql_status qlinear_run_debug_acc(ql_plan p, const void* a_q, const void* a_scale, const void* w_q,
+                                const void* w_scale, void* y, void* workspace, void* acc_out, void* stream) {
   if (!p) return fail(QL_E_INVALID, "plan is NULL");
   if (!acc_out && p->M > 0 && p->N > 0 && p->K > 0) return fail(QL_E_INVALID, "acc_out is NULL");
   return launch_gemm(p, a_q, a_scale, w_q, w_scale, y, workspace, acc_out, static_cast<hipStream_t>(stream));
 }
 
-ql_status qlinear_forward(ql_plan p, const void* x_bf16, void* a_q, float* a_scale, const void* w_q,
-                          const float* w_scale, void* y, void* workspace, void* stream) {
+ql_status qlinear_forward(ql_plan p, const void* x_bf16, void* a_q, void* a_scale, const void* w_q,
+                          const void* w_scale, void* y, void* workspace, void* stream) {
   if (!p) return fail(QL_E_INVALID, "plan is NULL");
   if (!p->tiled && p->cfg.a_mode == 4)
     return launch_gemm(p, nullptr, nullptr, w_q, w_scale, y, workspace, nullptr, static_cast<hipStream_t>(stream),
-                       true, x_bf16, a_q, a_scale);
+                       true, x_bf16, a_q, static_cast<float*>(a_scale));
   ql_status st = quantize_act(p->fmt, x_bf16, p->M, p->K, a_q, a_scale, p->cfg.a_mode >= 2, stream);
   if (st != QL_OK) return st;
   return launch_gemm(p, a_q, a_scale, w_q, w_scale, y, workspace, nullptr, static_cast<hipStream_t>(stream));

@@ -7,8 +7,9 @@
 
 namespace qlk {
 
-// Format selector of the kernels (matches ql_format's order).
-enum { FMT_FP8 = 0, FMT_INT8 = 1, FMT_BLOCK = 2 };
+// Format selector of the kernels (matches ql_format's order).  FMT_MX:
+// MXFP8, E4M3 codes with one E8M0 scale byte per 32 values along K.
+enum { FMT_FP8 = 0, FMT_INT8 = 1, FMT_BLOCK = 2, FMT_MX = 3 };
 
 // How the decode kernel reads the weights.
 enum {
@@ -19,9 +20,9 @@ enum {
 
 struct DecodeArgs {
   const uint8_t* a;    // A_q [M, K] codes
-  const float* sa;     // s_a [M] or [M, G]
+  const float* sa;     // s_a [M] or [M, G]; MXFP8: E8M0 bytes [M, K/32]
   const uint8_t* w;    // W_q [N, K] codes
-  const float* sw;     // s_w [N] or [ceil(N/128), G]
+  const float* sw;     // s_w [N] or [ceil(N/128), G]; MXFP8: E8M0 bytes [N, K/32]
   uint16_t* y;         // Y [M, N] bf16
   void* ws;            // split-K partial sums [M, N] (int32 or fp32), all-zero between runs
   unsigned* counters;  // split-K arrival counters [n_tiles], all-zero between runs
@@ -74,6 +75,8 @@ hipError_t decode_dispatch_int8(const DecodeKey& k, dim3 grid, dim3 block, size_
                                 hipStream_t s, const DecodeArgs& a, bool probe_only);
 hipError_t decode_dispatch_block(const DecodeKey& k, dim3 grid, dim3 block, size_t lds,
                                  hipStream_t s, const DecodeArgs& a, bool probe_only);
+hipError_t decode_dispatch_mx(const DecodeKey& k, dim3 grid, dim3 block, size_t lds,
+                              hipStream_t s, const DecodeArgs& a, bool probe_only);
 
 // Tiled kernel launchers (tiled_*.hip); `probe_only` also raises the
 // kernel's dynamic LDS limit to `lds`.
@@ -94,6 +97,10 @@ hipError_t launch_quant_groups(const void* x, int64_t M, int64_t K, void* q, flo
 hipError_t launch_quant_wblocks(const void* w, int64_t N, int64_t K, void* q, float* s,
                                 hipStream_t st);
 hipError_t launch_fill_zero_bf16(void* y, int64_t count, hipStream_t st);
+// MXFP8 rows: x bf16 [R, C] (C % 32 == 0) -> E4M3 codes (row-major [R, C],
+// or packed tiles when `packed`) and E8M0 scale bytes [R, C/32].
+hipError_t launch_quant_mx(const void* x, int64_t R, int64_t C, void* q, uint8_t* s, bool packed,
+                           hipStream_t st);
 // codes[i] = E4M3 code of x[i] clamped to [-448, 448], round to nearest even.
 hipError_t launch_encode_e4m3(const float* x, int64_t n, void* q, hipStream_t st);
 // Row-major W_q[N,K] -> packed 2 KB tiles (zero padding to 16 rows / 128 K).

@@ -77,6 +77,7 @@ __global__ void __launch_bounds__(NW * 64) qgemm_decode_kernel(DecodeArgs p) {
   constexpr bool WP = WM == W_PACKED;
   static_assert(!FUSED || (MT == 1 && WP), "fused quantization: one token tile, packed weights");
   static_assert(!GLU || (RG == 2 && WP), "SiLU-and-mul: a gate and an up row group per wave, packed weights");
+  static_assert(FMT != FMT_MX || (!FUSED && !GLU), "MXFP8: quantized activations in, plain bf16 out");
   using Acc = typename AccOf<FMT>::T;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   __shared__ int s_last;
@@ -190,9 +191,26 @@ __global__ void __launch_bounds__(NW * 64) qgemm_decode_kernel(DecodeArgs p) {
   float sa0[PF][MT][4], sa1[PF][MT][4];
   float sw0[PF][RG], sw1[PF][RG];
 
-  const __amdgpu_buffer_rsrc_t rsa = make_rsrc(p.sa, (FMT == FMT_BLOCK ? M * (uint32_t)p.G : M) * 4u);
-  const __amdgpu_buffer_rsrc_t rsw =
-      make_rsrc(p.sw, (FMT == FMT_BLOCK ? ((N + 127u) / 128u) * (uint32_t)p.G : N) * 4u);
+  // MXFP8 scales are bytes, K/32 = 4G a row
+  const __amdgpu_buffer_rsrc_t rsa =
+      make_rsrc(p.sa, (FMT == FMT_BLOCK || FMT == FMT_MX ? M * (uint32_t)p.G : M) * 4u);
+  const __amdgpu_buffer_rsrc_t rsw = make_rsrc(
+      p.sw, (FMT == FMT_MX ? N * (uint32_t)p.G : FMT == FMT_BLOCK ? ((N + 127u) / 128u) * (uint32_t)p.G : N) * 4u);
+  // MXFP8: the scale byte lane l hands the matrix core with K block kb is that
+  // of row l%16 (token, or weight row) and 32-wide block 4*kb + l/16, at
+  // row*K/32 + 4*kb + l/16.  Rows past the end read as zeros (their operand
+  // rows are zero too).
+  uint32_t xsa[MT], xsw[RG];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+    const uint32_t m = (uint32_t)(mt * 16 + r16);
+    xsa[mt] = m < M ? m * (uint32_t)p.G * 4u + (uint32_t)g : OOB;
+  }
+#pragma unroll
+  for (int rg = 0; rg < RG; ++rg) {
+    const uint32_t row = (uint32_t)(grow(rg) + r16);
+    xsw[rg] = row < N ? row * (uint32_t)p.G * 4u + (uint32_t)g : OOB;
+  }
 
   // Issue one batch of PF K blocks.  A K block past this wave's range, or
   // the part of a ragged last block beyond K, reads as zeros: `rem` (uniform)
@@ -262,6 +280,14 @@ __global__ void __launch_bounds__(NW * 64) qgemm_decode_kernel(DecodeArgs p) {
           const uint32_t row0 = (uint32_t)grow(rg);
           swb[q][rg] = bload_f32(rsw, (ok && row0 < N) ? ((row0 >> 7) * Gu + (uint32_t)kb) * 4u : OOB);
         }
+      }
+      if constexpr (FMT == FMT_MX) {
+        // scale bytes ride in the float slots as raw bits (no arithmetic touches them)
+        const uint32_t sofs = (uint32_t)kb * 4u;
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) sab[q][mt][0] = __int_as_float(bload_u8(rsa, ok ? xsa[mt] + sofs : OOB));
+#pragma unroll
+        for (int rg = 0; rg < RG; ++rg) swb[q][rg] = __int_as_float(bload_u8(rsw, ok ? xsw[rg] + sofs : OOB));
       }
     }
     // keep the whole batch issued before the matrix-core work that follows
@@ -336,6 +362,11 @@ __global__ void __launch_bounds__(NW * 64) qgemm_decode_kernel(DecodeArgs p) {
           } else if constexpr (FMT == FMT_FP8) {
             acc[rg][mt] = SWAP ? mma_f8(wf[rg], af[mt], acc[rg][mt])
                                : mma_f8(af[mt], wf[rg], acc[rg][mt]);
+          } else if constexpr (FMT == FMT_MX) {
+            const int xa = __float_as_int(sab[q][mt][0]);
+            const int xw = __float_as_int(swb[q][rg]);
+            acc[rg][mt] = SWAP ? mma_f8_mx(wf[rg], af[mt], acc[rg][mt], xw, xa)
+                               : mma_f8_mx(af[mt], wf[rg], acc[rg][mt], xa, xw);
           } else {
             const f32x4 z = {0.f, 0.f, 0.f, 0.f};
             const f32x4 part = SWAP ? mma_f8(wf[rg], af[mt], z) : mma_f8(af[mt], wf[rg], z);
@@ -508,7 +539,7 @@ __global__ void __launch_bounds__(NW * 64) qgemm_decode_kernel(DecodeArgs p) {
   // Scales of the per-token formats, loaded now so that their latency hides
   // under the weight stream instead of stalling the epilogue.
   float esa[MT][4], esw[RG][4];
-  if constexpr (FMT != FMT_BLOCK) {
+  if constexpr (FMT != FMT_BLOCK && FMT != FMT_MX) {
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
@@ -655,7 +686,7 @@ __global__ void __launch_bounds__(NW * 64) qgemm_decode_kernel(DecodeArgs p) {
         float t[2];
 #pragma unroll
         for (int rg = 0; rg < 2; ++rg) {
-          if constexpr (FMT == FMT_BLOCK) {
+          if constexpr (FMT == FMT_BLOCK || FMT == FMT_MX) {
             t[rg] = acc[rg][mt][r];
           } else {
             float accf;
@@ -686,7 +717,7 @@ __global__ void __launch_bounds__(NW * 64) qgemm_decode_kernel(DecodeArgs p) {
         nn[r] = (uint32_t)grow(rg) + (SWAP ? (uint32_t)(4 * g + r) : (uint32_t)r16);
         mm[r] = SWAP ? (uint32_t)(mt * 16 + r16) : (uint32_t)(mt * 16 + 4 * g + r);
         const bool ok = mm[r] < M && nn[r] < N;
-        if constexpr (FMT == FMT_BLOCK) {
+        if constexpr (FMT == FMT_BLOCK || FMT == FMT_MX) {
           out[r] = bf16_rne(acc[rg][mt][r]);
           if (ok && p.acc_out)
             reinterpret_cast<float*>(p.acc_out)[(size_t)mm[r] * N + nn[r]] = acc[rg][mt][r];
@@ -736,7 +767,7 @@ constexpr bool decode_config_fits() {
   }
   // two batches of PF blocks of (RG weight + MT activation) fragments, 8 VGPRs each
   const int buffers = 2 * PF_ * (RG_ + MT_) * 8;
-  const int scales = FMT == FMT_BLOCK ? 2 * PF_ * (4 * MT_ + RG_) : 0;
+  const int scales = FMT == FMT_BLOCK ? 2 * PF_ * (4 * MT_ + RG_) : FMT == FMT_MX ? 2 * PF_ * (MT_ + RG_) : 0;
   const int accs = RG_ * MT_ * 4;
   const int budget = NW_ >= 16 ? 128 : 256;
   // Block_FP8 keeps per-block partial products and scale factors live as well
@@ -746,10 +777,27 @@ constexpr bool decode_config_fits() {
   return true;
 }
 
+// MXFP8 shapes whose register allocation spills (checked one by one against
+// the compiler's resource report): the scaled instruction keeps its
+// operands and scale bytes in VGPRs, which costs more than the unscaled E4M3
+// path, above all with two token tiles held in registers (AL == 2).
+template <int NW_, int MT_, int RG_, int PF_, int AL>
+constexpr bool mx_spills() {
+  if (NW_ == 4) return MT_ == 2 && RG_ == 1 && PF_ == 4 && AL == 2;
+  if (NW_ == 8)
+    return (MT_ == 1 && RG_ == 4 && PF_ == 2) || (MT_ == 2 && PF_ == 2 && (RG_ == 2 || AL == 2)) ||
+           (MT_ == 2 && RG_ == 4 && AL == 2) || (MT_ == 4 && (PF_ == 2 || RG_ == 2));
+  if (NW_ == 16) return MT_ == 2 && (RG_ == 2 || AL == 2);
+  return false;
+}
+
 // Fused quantization adds 32/NW 16-byte X pieces a lane to the buffers in
 // flight; it serves one token tile and packed weights.
 template <int FMT, int NW_, int SW, int MT_, int RG_, int PF_, int AL, int WM_>
 constexpr bool decode_variant_ok() {
+  if constexpr (FMT == FMT_MX) {
+    if (mx_spills<NW_, MT_, RG_, PF_, AL>()) return false;
+  }
   if constexpr (AL == 4) {
     if (MT_ != 1 || WM_ != W_PACKED) return false;
     const int estimate = 2 * PF_ * (RG_ + MT_) * 8 + RG_ * MT_ * 4 + 40 + 4 * (32 / NW_);
@@ -761,7 +809,9 @@ constexpr bool decode_variant_ok() {
 template <int FMT, int NW_, int SW, int MT_, int RG_, int PF_, int AL, int WM_, int GLU = 0>
 hipError_t decode_try(const DecodeKey& k, dim3 grid, dim3 block, size_t lds, hipStream_t s, const DecodeArgs& a,
                       bool probe_only, bool* hit) {
-  if constexpr (decode_variant_ok<FMT, NW_, SW, MT_, RG_, PF_, AL, WM_>()) {
+  // MXFP8 is served with packed weights and packed activations only
+  constexpr bool mx_ok = FMT != FMT_MX || (GLU == 0 && WM_ == W_PACKED && (AL == 2 || AL == 3));
+  if constexpr (mx_ok && decode_variant_ok<FMT, NW_, SW, MT_, RG_, PF_, AL, WM_>()) {
     if (k.swap == SW && k.mt == MT_ && k.rg == RG_ && k.nw == NW_ && k.pf == PF_ && k.alds == AL && k.wm == WM_ &&
         k.glu == GLU) {
       *hit = true;

@@ -38,10 +38,19 @@ __device__ __forceinline__ float bload_f32(__amdgpu_buffer_rsrc_t r, uint32_t of
   return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
 }
 
+__device__ __forceinline__ int bload_u8(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return (int)__builtin_amdgcn_raw_buffer_load_b8(r, off, 0, 0);
+}
+
 // 32 bytes of one row of a 128-wide K block held by one lane: `lo` covers
 // K offsets [16*g, 16*g+16) and `hi` [64+16*g, 64+16*g+16) of the block,
 // g = lane / 16.  Activations and weights use the same lane -> K map, so the
-// matrix core pairs equal K indices whatever its internal K order is.
+// unscaled matrix core pairs equal K indices whatever its internal K order
+// is.  This map is also the order in which the scaled E4M3 instruction
+// groups K: the scale byte of lane 16*b + r multiplies K offsets
+// [32*b, 32*b+32) of row r -- for b < 2 the `lo` pieces of lane groups 2b
+// and 2b+1, for b >= 2 their `hi` pieces (checked on gfx950 with one-hot
+// operands and a distinct power-of-two scale per lane group).
 struct Frag {
   u32x4 lo, hi;
 };
@@ -60,6 +69,18 @@ __device__ __forceinline__ f32x4 mma_f8(const Frag& a, const Frag& b, f32x4 c) {
   i32x8 bv = {(int)b.lo.x, (int)b.lo.y, (int)b.lo.z, (int)b.lo.w,
               (int)b.hi.x, (int)b.hi.y, (int)b.hi.z, (int)b.hi.w};
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, c, 0, 0, 0, 0, 0, 0);
+}
+
+// E4M3 x E4M3 -> fp32 with E8M0 block scales: `sa` / `sb` (low byte) are this
+// lane's scales of the first / second operand, row l%16 and 32-wide K block
+// l/16 of the 128-wide step; each product is multiplied by 2^(sa-127) *
+// 2^(sb-127).
+__device__ __forceinline__ f32x4 mma_f8_mx(const Frag& a, const Frag& b, f32x4 c, int sa, int sb) {
+  i32x8 av = {(int)a.lo.x, (int)a.lo.y, (int)a.lo.z, (int)a.lo.w,
+              (int)a.hi.x, (int)a.hi.y, (int)a.hi.z, (int)a.hi.w};
+  i32x8 bv = {(int)b.lo.x, (int)b.lo.y, (int)b.lo.z, (int)b.lo.w,
+              (int)b.hi.x, (int)b.hi.y, (int)b.hi.z, (int)b.hi.w};
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, c, 0, 0, 0, sa, 0, sb);
 }
 
 // binary32 -> bfloat16, round to nearest even; NaN stays a quiet NaN.

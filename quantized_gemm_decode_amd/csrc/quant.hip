@@ -257,6 +257,69 @@ hipError_t launch_quant_wblocks(const void* w, int64_t N, int64_t K, void* q, fl
   return hipGetLastError();
 }
 
+// MXFP8 (OCP microscaling, E4M3 elements): a block is 32 consecutive values
+// of a row; its shared exponent is e = floor(log2(amax)) - 8 (8: exponent of
+// E4M3's largest normal), clamped to [-127, 127], -127 for an all-zero block,
+// stored as the E8M0 byte e + 127; each element is x * 2^-e (exact: a power
+// of two; a product below the binary32 normals is far below E4M3's smallest
+// subnormal, so its rounding cannot change the code) clamped to +-448 and
+// rounded to E4M3.
+__device__ __forceinline__ int mx_exponent(float amax) {
+  const uint32_t u = __float_as_uint(amax);   // amax >= 0, finite
+  if (u == 0u) return -127;
+  const int fl2 = u >= 0x00800000u ? (int)(u >> 23) - 127   // normal
+                                   : (31 - (int)__clz(u)) - 149;  // subnormal: u * 2^-149
+  return max(-127, fl2 - 8);
+}
+
+// Four lanes (a DPP quad) per block, 8 values (one 16-byte load) a lane.
+// PACKED: codes in the packed activation layout; the padding rows up to a
+// multiple of 16 (`rows_out`) get zero codes and no scale.
+template <bool PACKED>
+__global__ void __launch_bounds__(256) quant_mx_kernel(const uint16_t* __restrict__ x, uint32_t R, uint32_t rows_out,
+                                                       uint32_t C, uint8_t* __restrict__ q, uint8_t* __restrict__ s) {
+  const uint32_t t = blockIdx.x * 256u + threadIdx.x;
+  const uint32_t kpr = C / 8u;                   // 8-value pieces per row
+  const uint32_t row = t / kpr;
+  const uint32_t k = (t - row * kpr) * 8u;
+  const bool ok = row < R;
+  const u32x4 v = ok ? *reinterpret_cast<const u32x4*>(x + (size_t)row * C + k) : u32x4{0, 0, 0, 0};
+  float m = abs_bf16_max8(v, 0.0f);
+  m = fmaxf(m, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(m), 0xB1, 0xF, 0xF, false)));
+  m = fmaxf(m, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(m), 0x4E, 0xF, 0xF, false)));
+  const int e = mx_exponent(m);
+  const float f = __uint_as_float((uint32_t)(127 - e) << 23);   // 2^-e, a normal binary32
+  uint32_t c0 = 0u, c1 = 0u;
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float a = clamp448(__fmul_rn(__uint_as_float(w[i] << 16), f));
+    const float b = clamp448(__fmul_rn(__uint_as_float(w[i] & 0xffff0000u), f));
+    if (i < 2)
+      c0 = (i == 0) ? e4m3_pk2<false>(a, b, c0) : e4m3_pk2<true>(a, b, c0);
+    else
+      c1 = (i == 2) ? e4m3_pk2<false>(a, b, c1) : e4m3_pk2<true>(a, b, c1);
+  }
+  if (row < (PACKED ? rows_out : R)) {
+    const size_t off = PACKED ? packed_offset(row, k, C / 128u) : (size_t)row * C + k;
+    *reinterpret_cast<u32x2*>(q + off) = ok ? u32x2{c0, c1} : u32x2{0u, 0u};
+  }
+  if (ok && (k & 31u) == 0u) s[(size_t)row * (C / 32u) + k / 32u] = (uint8_t)(e + 127);
+}
+
+hipError_t launch_quant_mx(const void* x, int64_t R, int64_t C, void* q, uint8_t* s, bool packed, hipStream_t st) {
+  const int64_t rows_out = packed ? (R + 15) / 16 * 16 : R;
+  const int64_t threads = rows_out * (C / 8);
+  const dim3 grid((unsigned)((threads + 255) / 256)), block(256);
+  if (packed)
+    quant_mx_kernel<true><<<grid, block, 0, st>>>(static_cast<const uint16_t*>(x), (uint32_t)R, (uint32_t)rows_out,
+                                                  (uint32_t)C, static_cast<uint8_t*>(q), s);
+  else
+    quant_mx_kernel<false><<<grid, block, 0, st>>>(static_cast<const uint16_t*>(x), (uint32_t)R, (uint32_t)rows_out,
+                                                   (uint32_t)C, static_cast<uint8_t*>(q), s);
+  return hipGetLastError();
+}
+
 // The E4M3 encoder alone: two values per thread, clamped, by the conversion
 // instruction every FP8 quantizer uses.
 __global__ void __launch_bounds__(256) encode_e4m3_kernel(const float* __restrict__ x, uint32_t n,

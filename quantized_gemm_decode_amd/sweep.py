@@ -167,7 +167,7 @@ class Timer:
         xm = self.x[:M].contiguous()
         if self.layout >= 3:
             a_q = ql.act_buffer(plan)
-            a_s = torch.empty(ql.act_scale_shape(fmt, M, self.K), dtype=torch.float32, device="cuda")
+            a_s = torch.empty(ql.act_scale_shape(fmt, M, self.K), dtype=ql.scale_dtype(fmt), device="cuda")
         elif self.layout == 2:
             a_q, a_s = ql.quantize_act_packed(fmt, xm)
         else:

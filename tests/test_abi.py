@@ -11,6 +11,7 @@ import os
 import re
 
 import pytest
+import torch
 
 import quantized_gemm_decode_amd as ql
 from quantized_gemm_decode_amd import _lib
@@ -288,3 +289,37 @@ def test_glu_table_entries(tmp_path):
         assert p.config["rows_per_wave"] == 16 and p.facts["epilogue"] == 0
     finally:
         ql.qlinear_table_clear()
+
+
+def test_mxfp8_plans_are_validated_on_host():
+    good = dict(w_layout=1, a_mode=2, waves_n=4, waves_k=1, prefetch=2)
+    assert _plan_status(ql.MXFP8, 8, 4096, 4096, **good) == QL_OK
+    assert _plan_status(ql.MXFP8, 8, 4096, 4096, **dict(good, a_mode=3)) == QL_OK
+    assert _plan_status(ql.MXFP8, 8, 4096, 4160, **good) == QL_E_INVALID             # K % 128
+    assert _plan_status(ql.MXFP8, 8, 4096, 4096, **dict(good, w_layout=0, a_mode=0)) == QL_E_UNSUPPORTED
+    assert _plan_status(ql.MXFP8, 8, 4096, 4096, **dict(good, a_mode=1)) == QL_E_UNSUPPORTED
+    assert _plan_status(ql.MXFP8, 8, 4096, 4096, **dict(good, a_mode=4)) == QL_E_UNSUPPORTED   # no fused quantizer
+    assert _plan_status(ql.MXFP8, 128, 4096, 4096, **dict(good, algo=ql.ALGO_TILED, tile_m=128,
+                                                          tile_n=128)) == QL_E_UNSUPPORTED
+    assert _plan_status(ql.MXFP8, 65, 4096, 4096, **good) == QL_E_UNSUPPORTED
+    # shapes whose registers would spill are not instantiated
+    assert _plan_status(ql.MXFP8, 32, 4096, 4096, **dict(good, waves_n=2, waves_k=4, prefetch=2,
+                                                         rows_per_wave=32)) == QL_E_UNSUPPORTED
+    # the heuristic keeps MXFP8 on the decode kernel up to 64 tokens
+    ql.qlinear_table_clear()
+    try:
+        for M in (1, 24, 50, 64):
+            p = ql.qlinear_plan_layouts(ql.MXFP8, M, 4096, 4096, 1, 1)
+            assert p.config["algo"] == ql.ALGO_DECODE and p.config["a_mode"] == 2, M
+        with pytest.raises(ql.QLinearError):
+            ql.qlinear_plan_layouts(ql.MXFP8, 8, 4096, 4096, 0, 0)     # row-major operands
+    finally:
+        ql.load_default_table()
+    h = ctypes.c_void_p()
+    c = ql.QLConfig(**ql.make_config(**dict(good, rows_per_wave=32)))
+    assert ql.lib().qlinear_plan_glu_with_config(ql.MXFP8, 4, 1024, 512, ctypes.byref(c),
+                                                 ctypes.byref(h)) == QL_E_UNSUPPORTED
+    assert ql.act_scale_shape(ql.MXFP8, 5, 512) == (5, 16) and ql.weight_scale_shape(ql.MXFP8, 7, 256) == (7, 8)
+    assert ql.scale_dtype(ql.MXFP8) == torch.uint8 and ql.scale_dtype(ql.BLOCK_FP8) == torch.float32
+    null = ctypes.c_void_p(0)
+    assert ql.lib().qlinear_quantize_act(ql.MXFP8, null, 4, 4160, null, null, null) == QL_E_INVALID

@@ -1,0 +1,194 @@
+"""GPU parity of the MXFP8 path against the oracle's MX statement
+(oracle/mx.py): the quantizer bit-exact (E4M3 codes and E8M0 bytes, row-major
+and packed), the GEMM inside the oracle's acceptance rule -- within one bf16
+ulp of the correctly rounded product, or inside the binary32 forward-error
+bound over the block-scaled products -- for every instantiated shape,
+split-K and Swap-AB, and at the full decode shapes."""
+
+import itertools
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import quantized_gemm_decode_amd as ql
+from oracle import mx
+from tests.gpu_util import dev_bf16, host_bf16_bits, pack_ref, requires_gpu
+from workloads import bf16_bits, make_inputs
+
+pytestmark = [pytest.mark.gpu, requires_gpu]
+
+# swap x (waves_n, waves_k) x rows per wave x batch x activation mode (2 packed from L2, 3 staged in LDS)
+MXV = list(itertools.product([0, 1], [(4, 1), (2, 2), (1, 4), (8, 1), (1, 8), (2, 4), (16, 1), (1, 16), (4, 4)],
+                             [16, 32, 64], [1, 2], [2, 3]))
+SPLITS = [1, 2, 4, 8]
+MS = [1, 5, 13, 20, 29, 32, 40, 64]
+
+
+def _quant(xb, packed=False):
+    x = dev_bf16(xb)
+    q, s = (ql.quantize_act_packed if packed else ql.quantize_act)(ql.MXFP8, x)
+    torch.cuda.synchronize()
+    return q.view(torch.uint8).cpu().numpy(), s.cpu().numpy()
+
+
+def _weights(r):
+    w_q = torch.from_numpy(np.ascontiguousarray(r["w_q"], dtype=np.uint8)).cuda().view(torch.float8_e4m3fn)
+    return ql.pack_weight(w_q), torch.from_numpy(np.ascontiguousarray(r["s_w"], dtype=np.uint8)).cuda()
+
+
+def _acts(r):
+    a_p = torch.from_numpy(pack_ref(r["a_q"])).cuda().view(torch.float8_e4m3fn)
+    return a_p, torch.from_numpy(np.ascontiguousarray(r["s_a"], dtype=np.uint8)).cuda()
+
+
+def _mx_check(r, y_bits, split, waves_k):
+    K = r["a_q"].shape[1]
+    d = oracle.summation_depth(K, split=split, waves_k=waves_k)
+    B = mx.mx_tolerance_bound(r["a_q"], r["s_a"], r["w_q"], r["s_w"], d, oracle.MATRIX_CORE_ETA)
+    return oracle.check_fp8_parity(y_bits, r["y_ref"], r["y_true"], B)
+
+
+def _run(plan, a_p, a_s, w_p, w_s):
+    y = torch.full((plan.M, plan.N), float("nan"), dtype=torch.bfloat16, device="cuda")
+    ws = plan.new_workspace()
+    ql.qlinear_run(plan, a_p, a_s, w_p, w_s, y, ws)
+    torch.cuda.synchronize()
+    return host_bf16_bits(y), ws
+
+
+@pytest.mark.parametrize("M,K", [(1, 4096), (5, 128), (32, 12288), (17, 1024), (3, 25600), (64, 4096)])
+def test_mx_act_quantizer_bit_exact(M, K):
+    x, _ = make_inputs(K, 8, M, 0.02, seed=M + K)
+    xb = bf16_bits(x)
+    cq, cs = mx.mx_quantize(xb)
+    q, s = _quant(xb)
+    assert np.array_equal(q.reshape(M, K), cq) and np.array_equal(s, cs)
+    qp, sp = _quant(xb, packed=True)
+    n = ql.qlinear_packed_act_bytes(M, K)
+    assert np.array_equal(qp[:n], pack_ref(cq)) and np.array_equal(sp, cs)
+
+
+def test_mx_quantizer_special_blocks():
+    """All-zero and negative-zero blocks, bf16 subnormals, tiny normals (the
+    -127 clamp), amax on and just below a power of two, values that clamp to
+    448, a huge outlier beside small values, and random signs."""
+    K = 256
+    rows = np.zeros((8, K), np.float64)
+    rows[1, :] = -0.0
+    rows[2, :32] = np.linspace(1, 127, 32) * 2.0 ** -133          # bf16 subnormals
+    rows[2, 32:64] = -(2.0 ** -126) * np.linspace(1, 1.9, 32)     # tiny normals
+    rows[3, :32] = np.linspace(-1.0, 1.0, 32)                     # amax exactly 2^0
+    rows[3, 32:64] = np.linspace(-0.99609375, 0.5, 32)            # amax just below
+    rows[3, 64:96] = np.linspace(-1.9, 1.75, 32)                  # 1.9 * 256 clamps to 448
+    rows[4, :] = np.sin(np.arange(K)) * 1e-3
+    rows[4, 5] = 1e30
+    rows[5, :] = np.random.default_rng(1).standard_normal(K) * 3e4
+    rows[6, ::3] = 448.0
+    rows[6, 1::3] = -2.0 ** -20
+    rows[7, :] = np.random.default_rng(2).standard_normal(K)
+    xb = torch.from_numpy(rows.astype(np.float32)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    xb[1, :] = 0x8000
+    cq, cs = mx.mx_quantize(xb)
+    for packed in (False, True):
+        q, s = _quant(xb, packed)
+        assert np.array_equal(s, cs), packed
+        got = q[:ql.qlinear_packed_act_bytes(8, K)] if packed else q.reshape(8, K)
+        assert np.array_equal(got, pack_ref(cq) if packed else cq), packed
+    assert cs[0, 0] == 0 and np.all(cq[1] == 0x80)
+
+
+@pytest.mark.parametrize("N,K", [(300, 512), (4096, 4096), (1000, 12288)])
+def test_mx_weight_quantizer_bit_exact(N, K):
+    _, w = make_inputs(K, N, 1, 0.02, seed=N)
+    wb = bf16_bits(w)
+    w_q, w_s = ql.quantize_weight(ql.MXFP8, w.cuda())
+    torch.cuda.synchronize()
+    rows = np.unique(np.random.default_rng(N).integers(0, N, 64))
+    cq, cs = mx.mx_quantize(wb[rows])
+    assert np.array_equal(w_q.view(torch.uint8).cpu().numpy()[rows], cq)
+    assert np.array_equal(w_s.cpu().numpy()[rows], cs)
+
+
+@pytest.mark.parametrize("vi", range(len(MXV)))
+def test_every_mx_instantiation_matches_oracle(vi):
+    swap, (wn, wk), rows, pf, amode = MXV[vi]
+    M = MS[vi % len(MS)]
+    K = [1024, 1152, 2048][vi % 3]
+    N = 300 + 16 * (vi % 7)                      # several tiles + a ragged tail
+    split = SPLITS[(vi // 2) % len(SPLITS)]
+    cfg = dict(swap_ab=swap, split_k=split, waves_n=wn, waves_k=wk, rows_per_wave=rows, prefetch=pf,
+               a_mode=amode, w_layout=1)
+    try:
+        plan = ql.qlinear_plan_with_config(ql.MXFP8, M, N, K, cfg)
+    except ql.QLinearError as e:
+        assert e.status == 2, e
+        pytest.skip("configuration not instantiated: %s" % e)
+    x, w = make_inputs(K, N, M, 0.02, seed=7000 + vi)
+    r = mx.mx_reference(bf16_bits(x), bf16_bits(w))
+    w_p, w_s = _weights(r)
+    a_p, a_s = _acts(r)
+    y, ws = _run(plan, a_p, a_s, w_p, w_s)
+    st = _mx_check(r, y, plan.facts["chunks"], wk)
+    assert st["ok"] and st["frac_within_ulp"] >= 0.95, (cfg, st)
+    if ws is not None:
+        assert int(torch.count_nonzero(ws)) == 0, "split-K workspace not left all-zero"
+
+
+@pytest.mark.parametrize("lab,N,K", [("qkv", 6144, 4096), ("o", 4096, 4096), ("gate_up", 24576, 4096),
+                                     ("down", 4096, 12288)])
+@pytest.mark.parametrize("M", [1, 8, 32])
+def test_mx_planner_plans_at_full_size(lab, N, K, M):
+    """The planner's forward at the 8B decode shapes, weights quantized on the
+    GPU; codes and scales checked whole, outputs on 64 sampled columns."""
+    ql.load_default_table()
+    x, w = make_inputs(K, N, M, 0.02, seed=17 + M)
+    xb, wb = bf16_bits(x), bf16_bits(w)
+    plan = ql.qlinear_plan_layouts(ql.MXFP8, M, N, K, 1, 1)
+    w_q, w_s = ql.quantize_weight(ql.MXFP8, w.cuda())
+    a_p = ql.act_buffer(plan)
+    a_s = torch.empty(ql.act_scale_shape(ql.MXFP8, M, K), dtype=torch.uint8, device="cuda")
+    y = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
+    ql.qlinear_forward(plan, x.cuda(), a_p, a_s, ql.pack_weight(w_q), w_s, y, plan.new_workspace())
+    torch.cuda.synchronize()
+    cols = np.sort(np.random.default_rng(M + N).choice(N, 64, replace=False))
+    r = mx.mx_reference(xb, wb[cols])
+    n = ql.qlinear_packed_act_bytes(M, K)
+    assert np.array_equal(a_p[:n].view(torch.uint8).cpu().numpy(), pack_ref(r["a_q"]))
+    assert np.array_equal(a_s.cpu().numpy(), r["s_a"])
+    st = _mx_check(r, host_bf16_bits(y)[:, cols], plan.facts["chunks"], plan.config["waves_k"])
+    assert st["ok"] and st["frac_within_ulp"] >= 0.95, (plan.config, st)
+
+
+def test_mx_forward_equals_quantize_then_run_and_graph_replays():
+    M, N, K = 12, 2048, 4096
+    x, w = make_inputs(K, N, M, 0.02, seed=99)
+    r = mx.mx_reference(bf16_bits(x), bf16_bits(w))
+    w_p, w_s = _weights(r)
+    plan = ql.qlinear_plan_with_config(ql.MXFP8, M, N, K, dict(swap_ab=1, split_k=1, waves_n=2, waves_k=2,
+                                                               rows_per_wave=16, prefetch=2, a_mode=3, w_layout=1))
+    a_p, a_s = _acts(r)
+    y_run, _ = _run(plan, a_p, a_s, w_p, w_s)
+    xd = x.cuda()
+    a_q = ql.act_buffer(plan)
+    s_q = torch.empty(ql.act_scale_shape(ql.MXFP8, M, K), dtype=torch.uint8, device="cuda")
+    y = torch.zeros(M, N, dtype=torch.bfloat16, device="cuda")
+    ql.qlinear_forward(plan, xd, a_q, s_q, w_p, w_s, y)
+    torch.cuda.synchronize()
+    assert np.array_equal(host_bf16_bits(y), y_run)              # same codes, same kernel, split 1
+    st = _mx_check(r, y_run, 1, 2)
+    assert st["ok"], st
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        ql.qlinear_graph_begin(s)
+        ql.qlinear_forward(plan, xd, a_q, s_q, w_p, w_s, y, stream=s)
+        g = ql.qlinear_graph_end(s)
+    for i in range(3):
+        y.fill_(0)
+        a_q.view(torch.uint8).fill_(0)
+        torch.cuda.synchronize()
+        g.launch(s)
+        s.synchronize()
+        assert np.array_equal(host_bf16_bits(y), y_run), i
+        _ = torch.randn(1000, device="cuda").sum()      # unrelated eager work between replays
