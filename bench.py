@@ -42,6 +42,8 @@ def algorithmic_bytes(fmt, M, N, K):
     """Bytes the method must move for one GEMM (weights, scales, activations, output)."""
     if fmt == 2:   # Block_FP8
         return N * K + 4 * (-(-N // 128)) * (K // 128) + M * K + 4 * M * (K // 128) + 2 * M * N
+    if fmt == 3:   # MXFP8: one E8M0 byte per 32 codes on both operands
+        return N * K + N * (K // 32) + M * K + M * (K // 32) + 2 * M * N
     return N * K + 4 * N + M * K + 4 * M + 2 * M * N
 
 
@@ -52,6 +54,8 @@ def fused_kernel_bytes(fmt, M, N, K):
 
 
 def quantizer_bytes(fmt, M, K):
+    if fmt == 3:
+        return 2 * M * K + M * K + M * (K // 32)
     return 2 * M * K + M * K + (4 * M * (K // 128) if fmt == 2 else 4 * M)
 
 
@@ -300,6 +304,8 @@ def main(argv=None):
         w_q, w_s = ql.quantize_weight(fmt, wd)
         if args.layout != "rowmajor":
             w_q = ql.pack_weight(w_q)          # offline, like the quantization itself
+            if fmt == ql.MXFP8:
+                w_s = ql.pack_mx_scales(w_s)   # MXFP8 plans read the scales in lane order
         del wd
         copies = max(2, -(-(1 << 30) // (N * K)))
         wq_all = torch.empty((copies,) + tuple(w_q.shape), dtype=w_q.dtype, device=dev)
@@ -320,7 +326,7 @@ def main(argv=None):
         pts.append(dict(lab=lab, N=N, K=K, M=M, plan=plan, cfg=cfg, facts=facts,
                         x=sh["x"][:M].contiguous(),
                         a_q=ql.act_buffer(plan, dev),
-                        a_s=torch.empty(ql.act_scale_shape(fmt, M, K), dtype=ql.scale_dtype(fmt), device=dev),
+                        a_s=ql.act_scale_buffer(plan, dev),
                         y=torch.empty(M, N, dtype=torch.bfloat16, device=dev),
                         wsp=plan.new_workspace(dev), fused=fused,
                         bytes=algorithmic_bytes(fmt, M, N, K), qbytes=quantizer_bytes(fmt, M, K),
@@ -496,7 +502,7 @@ def glu_pass(ql, wl, pts, shapes, stream, args):
             plan = p["plan"] if kind == "plain" else ql.qlinear_plan_glu(fmt, M, N, K, 2)
             y = torch.empty(M, N if kind == "plain" else N // 2, dtype=torch.bfloat16, device="cuda")
             a_q = ql.act_buffer(plan)
-            a_s = torch.empty(ql.act_scale_shape(fmt, M, K), dtype=ql.scale_dtype(fmt), device="cuda")
+            a_s = ql.act_scale_buffer(plan)
             wsp = plan.new_workspace()
             with torch.cuda.stream(stream):
                 ql.qlinear_graph_begin(stream)
@@ -573,15 +579,23 @@ def cpu_baseline(wl, shapes, budget_s):
     b_total = 0
     for (lab, N, K) in wl.shapes:
         x, w = make_inputs(K, N, max(wl.ms), wl.sigma_w, seed=wl.seed)
-        w_q, s_w = oracle.quantize_weight(fmt, bf16_bits(w))          # offline step: not timed
+        if fmt == 3:
+            w_q, s_w = oracle.mx_quantize(bf16_bits(w))                 # offline step: not timed
+        else:
+            w_q, s_w = oracle.quantize_weight(fmt, bf16_bits(w))      # offline step: not timed
         for M in wl.ms:
             if 2.0 * M * N * K > 50e9:
                 continue       # a single fp64 GEMM of minutes: outside the bounded sample
             xb = bf16_bits(x[:M])
             t0 = time.perf_counter()
-            a_q, s_a = oracle.quantize_act(fmt, xb)
-            S = oracle.contract_exact(fmt, a_q, w_q)
-            oracle.epilogue(fmt, S, s_a, s_w)
+            if fmt == 3:
+                a_q, s_a = oracle.mx_quantize(xb)
+                y = oracle.mx_contract_exact(a_q, s_a, w_q, s_w)
+                oracle.bf16_bits_from_f32(oracle.f32(y))
+            else:
+                a_q, s_a = oracle.quantize_act(fmt, xb)
+                S = oracle.contract_exact(fmt, a_q, w_q)
+                oracle.epilogue(fmt, S, s_a, s_w)
             dt = time.perf_counter() - t0
             t_total += dt
             b_total += algorithmic_bytes(fmt, M, N, K)

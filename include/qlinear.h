@@ -190,7 +190,9 @@ ql_status qlinear_quantize_act(int32_t fmt, const void* x_bf16, int64_t M, int64
  * byte h*1024 + l*16 + j = A_q[16t + l%16][128kb + 64h + 16*(l/16) + j], zero
  * for tokens >= M and K beyond K.  Every activation load of the GEMM then
  * reads one contiguous kilobyte.  a_packed holds qlinear_packed_act_bytes(M, K)
- * bytes; a_scale is as for qlinear_quantize_act.  Same codes, same scales.
+ * bytes; a_scale is as for qlinear_quantize_act -- except MXFP8, whose scales
+ * are then written in the lane-order layout of qlinear_pack_mx_scales
+ * (qlinear_packed_mx_scale_bytes(M, K) bytes).  Same codes, same scales.
  */
 int64_t qlinear_packed_act_bytes(int64_t M, int64_t K);
 ql_status qlinear_quantize_act_packed(int32_t fmt, const void* x_bf16, int64_t M, int64_t K,
@@ -229,6 +231,20 @@ ql_status qlinear_quantize_weight(int32_t fmt, const void* w_bf16, int64_t N, in
  */
 int64_t qlinear_packed_weight_bytes(int64_t N, int64_t K);
 ql_status qlinear_pack_weight(const void* w_q, int64_t N, int64_t K, void* w_packed, void* stream);
+
+/*
+ * MXFP8 scales in lane order, the layout MXFP8 plans read for weights and
+ * activations alike: the E8M0 bytes of 16 rows x one 128-wide K block take
+ * 64 bytes at (t * K/128 + kb) * 64, byte l = s[16t + l%16][4kb + l/16] (the
+ * scale byte lane l hands the matrix core with that K block; see QL_MXFP8),
+ * 0 for rows >= R.  One wave then reads a K block's scales as 64 contiguous
+ * bytes.  qlinear_pack_mx_scales reads row-major scales [R, K/32] (as
+ * qlinear_quantize_weight writes them; K % 128 == 0) and writes
+ * qlinear_packed_mx_scale_bytes(R, K) bytes; the packed MXFP8 activation
+ * quantizer writes this layout directly.  Enqueue-only.
+ */
+int64_t qlinear_packed_mx_scale_bytes(int64_t R, int64_t K);
+ql_status qlinear_pack_mx_scales(const void* scales, int64_t R, int64_t K, void* packed, void* stream);
 
 /*
  * Offline sweep table ([Summary] "Hybrid dispatch addresses runtime
@@ -316,7 +332,8 @@ void qlinear_plan_destroy(ql_plan plan);
  * hands the E8M0 bytes to the scaled matrix-core instruction, which applies
  * them to every 32-wide block of products, and rounds the fp32 sum to bf16.
  * MXFP8 plans use the decode algorithm (M <= 64) with packed weights and
- * packed activations (a_mode 2 or 3).
+ * packed activations (a_mode 2 or 3), and read both scales in the lane
+ * order of qlinear_pack_mx_scales.
  * a_q is in the plan's activation layout: row-major [M, K], or packed when
  * the plan's a_mode is 2 or 3; w_q in the plan's weight layout (w_layout).
  * Enqueue-only; workspace may be NULL when qlinear_workspace_bytes is 0.

@@ -131,11 +131,22 @@ def quantize_act(fmt, x, stream=None):
     return a_q, a_s
 
 
+def packed_act_scale_shape(fmt, M, K):
+    """Shape of s_a as the packed quantizer writes it (MXFP8: flat lane-order bytes)."""
+    return (max(qlinear_packed_mx_scale_bytes(M, K), 16),) if fmt == MXFP8 else act_scale_shape(fmt, M, K)
+
+
+def act_scale_buffer(plan, device="cuda"):
+    """s_a buffer for a forward with this plan (packed MXFP8 scales when it reads packed activations)."""
+    shape = (packed_act_scale_shape if plan.config["a_mode"] >= 2 else act_scale_shape)(plan.fmt, plan.M, plan.K)
+    return torch.empty(shape, dtype=scale_dtype(plan.fmt), device=device)
+
+
 def quantize_act_packed(fmt, x, stream=None):
     """Allocate (packed A_q as a flat code buffer, s_a) and run the packed-layout quantizer."""
     M, K = x.shape
     a_p = torch.empty(max(qlinear_packed_act_bytes(M, K), 16), dtype=code_dtype(fmt), device=x.device)
-    a_s = torch.empty(act_scale_shape(fmt, M, K), dtype=scale_dtype(fmt), device=x.device)
+    a_s = torch.empty(packed_act_scale_shape(fmt, M, K), dtype=scale_dtype(fmt), device=x.device)
     qlinear_quantize_act_packed(fmt, x, a_p, a_s, stream)
     return a_p, a_s
 
@@ -171,6 +182,24 @@ def qlinear_pack_weight(w_q, w_packed, stream=None):
     N, K = w_q.shape
     _check(lib().qlinear_pack_weight(_ptr(w_q, "w_q", CODE_DTYPES), N, K, _ptr(w_packed, "w_packed", CODE_DTYPES),
                                      _stream(stream)), "qlinear_pack_weight")
+
+
+def qlinear_packed_mx_scale_bytes(R, K):
+    return int(lib().qlinear_packed_mx_scale_bytes(R, K))
+
+
+def qlinear_pack_mx_scales(s, K, out, stream=None):
+    R = s.shape[0]
+    _check(lib().qlinear_pack_mx_scales(_ptr(s, "scales", torch.uint8), R, K, _ptr(out, "packed", torch.uint8),
+                                        _stream(stream)), "qlinear_pack_mx_scales")
+
+
+def pack_mx_scales(s, stream=None):
+    """Row-major MXFP8 scales [R, K/32] -> a new flat buffer in lane order."""
+    R, KS = s.shape
+    out = torch.empty(max(qlinear_packed_mx_scale_bytes(R, KS * 32), 16), dtype=torch.uint8, device=s.device)
+    qlinear_pack_mx_scales(s, KS * 32, out, stream)
+    return out
 
 
 def pack_weight(w_q, stream=None):

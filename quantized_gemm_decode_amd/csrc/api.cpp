@@ -506,6 +506,21 @@ ql_status qlinear_quantize_weight(int32_t fmt, const void* w_bf16, int64_t N, in
   return e == hipSuccess ? QL_OK : hip_fail(e, "weight quantizer launch");
 }
 
+int64_t qlinear_packed_mx_scale_bytes(int64_t R, int64_t K) {
+  if (R < 0 || K < 0) return 0;
+  return ((R + 15) / 16) * (K / 128) * 64;
+}
+
+ql_status qlinear_pack_mx_scales(const void* scales, int64_t R, int64_t K, void* packed, void* stream) {
+  ql_status st = check_sizes(QL_MXFP8, R, K, "R");
+  if (st != QL_OK) return st;
+  if (R == 0 || K == 0) return QL_OK;
+  if (!scales || !packed) return fail(QL_E_INVALID, "NULL pointer");
+  if (!aligned16(scales) || !aligned16(packed)) return fail(QL_E_ALIGN, "pointers must be 16-byte aligned");
+  hipError_t e = qlk::launch_pack_mx_scales(scales, R, K, packed, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? QL_OK : hip_fail(e, "MXFP8 scale packing launch");
+}
+
 ql_status qlinear_table_load(const char* path, int64_t* n_entries) {
   if (!path) return fail(QL_E_INVALID, "path is NULL");
   std::ifstream f(path);

@@ -20,9 +20,9 @@ enum {
 
 struct DecodeArgs {
   const uint8_t* a;    // A_q [M, K] codes
-  const float* sa;     // s_a [M] or [M, G]; MXFP8: E8M0 bytes [M, K/32]
+  const float* sa;     // s_a [M] or [M, G]; MXFP8: E8M0 bytes in lane order, 64 per (16 rows, K block)
   const uint8_t* w;    // W_q [N, K] codes
-  const float* sw;     // s_w [N] or [ceil(N/128), G]; MXFP8: E8M0 bytes [N, K/32]
+  const float* sw;     // s_w [N] or [ceil(N/128), G]; MXFP8: as s_a, over the weight rows
   uint16_t* y;         // Y [M, N] bf16
   void* ws;            // split-K partial sums [M, N] (int32 or fp32), all-zero between runs
   unsigned* counters;  // split-K arrival counters [n_tiles], all-zero between runs
@@ -101,6 +101,9 @@ hipError_t launch_fill_zero_bf16(void* y, int64_t count, hipStream_t st);
 // or packed tiles when `packed`) and E8M0 scale bytes [R, C/32].
 hipError_t launch_quant_mx(const void* x, int64_t R, int64_t C, void* q, uint8_t* s, bool packed,
                            hipStream_t st);
+// MXFP8 scales [R, K/32] -> lane order: 64 bytes per (16-row group t, K
+// block kb) at (t*G + kb)*64, byte l = s[16t + l%16][4kb + l/16], 0 past R.
+hipError_t launch_pack_mx_scales(const void* s, int64_t R, int64_t K, void* packed, hipStream_t st);
 // codes[i] = E4M3 code of x[i] clamped to [-448, 448], round to nearest even.
 hipError_t launch_encode_e4m3(const float* x, int64_t n, void* q, hipStream_t st);
 // Row-major W_q[N,K] -> packed 2 KB tiles (zero padding to 16 rows / 128 K).

@@ -191,25 +191,24 @@ __global__ void __launch_bounds__(NW * 64) qgemm_decode_kernel(DecodeArgs p) {
   float sa0[PF][MT][4], sa1[PF][MT][4];
   float sw0[PF][RG], sw1[PF][RG];
 
-  // MXFP8 scales are bytes, K/32 = 4G a row
-  const __amdgpu_buffer_rsrc_t rsa =
-      make_rsrc(p.sa, (FMT == FMT_BLOCK || FMT == FMT_MX ? M * (uint32_t)p.G : M) * 4u);
+  // MXFP8 scales are bytes in lane order: 64 per (16-row group, K block)
+  const __amdgpu_buffer_rsrc_t rsa = make_rsrc(
+      p.sa, FMT == FMT_MX ? MT16 * (uint32_t)p.G * 64u : (FMT == FMT_BLOCK ? M * (uint32_t)p.G : M) * 4u);
   const __amdgpu_buffer_rsrc_t rsw = make_rsrc(
-      p.sw, (FMT == FMT_MX ? N * (uint32_t)p.G : FMT == FMT_BLOCK ? ((N + 127u) / 128u) * (uint32_t)p.G : N) * 4u);
-  // MXFP8: the scale byte lane l hands the matrix core with K block kb is that
-  // of row l%16 (token, or weight row) and 32-wide block 4*kb + l/16, at
-  // row*K/32 + 4*kb + l/16.  Rows past the end read as zeros (their operand
-  // rows are zero too).
+      p.sw, FMT == FMT_MX ? NT16 * (uint32_t)p.G * 64u
+                          : (FMT == FMT_BLOCK ? ((N + 127u) / 128u) * (uint32_t)p.G : N) * 4u);
+  // MXFP8: the scale byte lane l hands the matrix core with K block kb (that
+  // of row l%16 of the operand's 16-row group and 32-wide block 4*kb + l/16)
+  // is byte l of the group's 64 for that block, so a wave reads 64
+  // contiguous bytes.  Padding rows hold 0 (their operand rows are zero).
   uint32_t xsa[MT], xsw[RG];
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt) {
-    const uint32_t m = (uint32_t)(mt * 16 + r16);
-    xsa[mt] = m < M ? m * (uint32_t)p.G * 4u + (uint32_t)g : OOB;
-  }
+  for (int mt = 0; mt < MT; ++mt)
+    xsa[mt] = (uint32_t)mt < MT16 ? (uint32_t)mt * (uint32_t)p.G * 64u + (uint32_t)lane : OOB;
 #pragma unroll
   for (int rg = 0; rg < RG; ++rg) {
-    const uint32_t row = (uint32_t)(grow(rg) + r16);
-    xsw[rg] = row < N ? row * (uint32_t)p.G * 4u + (uint32_t)g : OOB;
+    const uint32_t t = (uint32_t)(grow(rg) / 16);
+    xsw[rg] = (t < NT16 && rowok(rg, 0)) ? t * (uint32_t)p.G * 64u + (uint32_t)lane : OOB;
   }
 
   // Issue one batch of PF K blocks.  A K block past this wave's range, or
@@ -283,7 +282,7 @@ __global__ void __launch_bounds__(NW * 64) qgemm_decode_kernel(DecodeArgs p) {
       }
       if constexpr (FMT == FMT_MX) {
         // scale bytes ride in the float slots as raw bits (no arithmetic touches them)
-        const uint32_t sofs = (uint32_t)kb * 4u;
+        const uint32_t sofs = (uint32_t)kb * 64u;
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) sab[q][mt][0] = __int_as_float(bload_u8(rsa, ok ? xsa[mt] + sofs : OOB));
 #pragma unroll

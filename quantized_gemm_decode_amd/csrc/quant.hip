@@ -273,8 +273,9 @@ __device__ __forceinline__ int mx_exponent(float amax) {
 }
 
 // Four lanes (a DPP quad) per block, 8 values (one 16-byte load) a lane.
-// PACKED: codes in the packed activation layout; the padding rows up to a
-// multiple of 16 (`rows_out`) get zero codes and no scale.
+// PACKED: codes in the packed activation layout and scales in lane order
+// (byte (row/16 * G + k/128)*64 + row%16 + 16*((k%128)/32)); the padding
+// rows up to a multiple of 16 (`rows_out`) get zero codes and zero scales.
 template <bool PACKED>
 __global__ void __launch_bounds__(256) quant_mx_kernel(const uint16_t* __restrict__ x, uint32_t R, uint32_t rows_out,
                                                        uint32_t C, uint8_t* __restrict__ q, uint8_t* __restrict__ s) {
@@ -304,7 +305,33 @@ __global__ void __launch_bounds__(256) quant_mx_kernel(const uint16_t* __restric
     const size_t off = PACKED ? packed_offset(row, k, C / 128u) : (size_t)row * C + k;
     *reinterpret_cast<u32x2*>(q + off) = ok ? u32x2{c0, c1} : u32x2{0u, 0u};
   }
-  if (ok && (k & 31u) == 0u) s[(size_t)row * (C / 32u) + k / 32u] = (uint8_t)(e + 127);
+  if ((k & 31u) == 0u) {
+    if (PACKED && row < rows_out)
+      s[((size_t)(row >> 4) * (C / 128u) + (k >> 7)) * 64u + (row & 15u) + 16u * ((k >> 5) & 3u)] =
+          ok ? (uint8_t)(e + 127) : (uint8_t)0;
+    else if (!PACKED && ok)
+      s[(size_t)row * (C / 32u) + k / 32u] = (uint8_t)(e + 127);
+  }
+}
+
+// One thread per byte of the lane-order MXFP8 scale layout.
+__global__ void __launch_bounds__(256) pack_mx_scales_kernel(const uint8_t* __restrict__ s, uint32_t R, uint32_t G,
+                                                             uint32_t total, uint8_t* __restrict__ out) {
+  const uint32_t i = blockIdx.x * 256u + threadIdx.x;
+  if (i >= total) return;
+  const uint32_t l = i & 63u;
+  const uint32_t kb = (i >> 6) % G;
+  const uint32_t t = (i >> 6) / G;
+  const uint32_t row = t * 16u + (l & 15u);
+  out[i] = row < R ? s[(size_t)row * (G * 4u) + kb * 4u + (l >> 4)] : (uint8_t)0;
+}
+
+hipError_t launch_pack_mx_scales(const void* s, int64_t R, int64_t K, void* packed, hipStream_t st) {
+  const int64_t G = K / 128;
+  const int64_t total = (R + 15) / 16 * G * 64;
+  pack_mx_scales_kernel<<<dim3((unsigned)((total + 255) / 256)), dim3(256), 0, st>>>(
+      static_cast<const uint8_t*>(s), (uint32_t)R, (uint32_t)G, (uint32_t)total, static_cast<uint8_t*>(packed));
+  return hipGetLastError();
 }
 
 hipError_t launch_quant_mx(const void* x, int64_t R, int64_t C, void* q, uint8_t* s, bool packed, hipStream_t st) {

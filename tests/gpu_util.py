@@ -77,3 +77,20 @@ def pack_ref(q):
         for g in range(4):
             out[:, :, h, 16 * g:16 * g + 16, :] = arr[:, :, :, 64 * h + 16 * g:64 * h + 16 * g + 16].transpose(0, 2, 1, 3)
     return out.reshape(-1)
+
+
+def pack_mx_scales_ref(s, K):
+    """The lane-order MXFP8 scale layout, restated from its definition: the 64
+    bytes of (16-row group t, K block kb) at (t*G + kb)*64, byte l =
+    S[16t + l%16][4kb + l//16], zero past the last row."""
+    s = np.ascontiguousarray(s, dtype=np.uint8)
+    R = s.shape[0]
+    T, G = -(-R // 16), K // 128
+    out = np.zeros((T, G, 64), np.uint8)
+    for t in range(T):
+        for kb in range(G):
+            for l in range(64):
+                row = 16 * t + l % 16
+                if row < R:
+                    out[t, kb, l] = s[row, 4 * kb + l // 16]
+    return out.reshape(-1)

@@ -323,3 +323,13 @@ def test_mxfp8_plans_are_validated_on_host():
     assert ql.scale_dtype(ql.MXFP8) == torch.uint8 and ql.scale_dtype(ql.BLOCK_FP8) == torch.float32
     null = ctypes.c_void_p(0)
     assert ql.lib().qlinear_quantize_act(ql.MXFP8, null, 4, 4160, null, null, null) == QL_E_INVALID
+
+
+def test_mx_scale_layout_sizes():
+    assert ql.qlinear_packed_mx_scale_bytes(1, 4096) == 32 * 64
+    assert ql.qlinear_packed_mx_scale_bytes(17, 256) == 2 * 2 * 64
+    assert ql.qlinear_packed_mx_scale_bytes(0, 256) == 0
+    null = ctypes.c_void_p(0)
+    assert ql.lib().qlinear_pack_mx_scales(null, 4, 4160, null, null) == QL_E_INVALID   # K % 128
+    assert ql.lib().qlinear_pack_mx_scales(null, 4, 256, null, null) == QL_E_INVALID    # NULL
+    assert ql.lib().qlinear_pack_mx_scales(null, 0, 256, null, null) == QL_OK          # empty

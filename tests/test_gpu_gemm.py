@@ -413,6 +413,8 @@ def test_every_table_entry_matches_oracle(entry):
     plan = ql.qlinear_plan_with_config(fmt, M, N, K, cfg)
     y = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
     w_use = ql.pack_weight(w_q) if cfg["w_layout"] else w_q
+    if fmt == ql.MXFP8:
+        w_s = ql.pack_mx_scales(w_s)
     if entry[16]:
         a_f = ql.act_buffer(plan)
         s_f = torch.empty_like(a_s)
@@ -421,7 +423,9 @@ def test_every_table_entry_matches_oracle(entry):
         assert torch.equal(s_f, a_s)
     else:
         if cfg["a_mode"] >= 2:
-            a_q, _ = ql.quantize_act_packed(fmt, xm.cuda())
+            a_q, a_p_s = ql.quantize_act_packed(fmt, xm.cuda())
+            if fmt == ql.MXFP8:
+                a_s = a_p_s
         ql.qlinear_run(plan, a_q, a_s, w_use, w_s, y, plan.new_workspace())
         torch.cuda.synchronize()
     yb = host_bf16_bits(y)
@@ -432,8 +436,15 @@ def test_every_table_entry_matches_oracle(entry):
     else:
         cols = np.sort(rng.choice(N, 64, replace=False))
     rows = np.sort(rng.choice(M, 256, replace=False)) if M > 256 else np.arange(M)
-    r = oracle.reference(fmt, bf16_bits(xm[torch.from_numpy(rows)]), bf16_bits(w[torch.from_numpy(cols)]))
     ysel = yb[np.ix_(rows, cols)]
+    if fmt == ql.MXFP8:
+        r = oracle.mx_reference(bf16_bits(xm[torch.from_numpy(rows)]), bf16_bits(w[torch.from_numpy(cols)]))
+        d = oracle.summation_depth(K, split=plan.facts["chunks"], waves_k=16)
+        B = oracle.mx_tolerance_bound(r["a_q"], r["s_a"], r["w_q"], r["s_w"], d, oracle.MATRIX_CORE_ETA)
+        st = oracle.check_fp8_parity(ysel, r["y_ref"], r["y_true"], B)
+        assert st["ok"] and st["frac_within_ulp"] >= 0.95, (cfg, st)
+        return
+    r = oracle.reference(fmt, bf16_bits(xm[torch.from_numpy(rows)]), bf16_bits(w[torch.from_numpy(cols)]))
     if fmt == ql.W8A8_INT8:
         assert np.array_equal(ysel, r["y_ref"]), cfg
     else:

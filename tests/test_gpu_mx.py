@@ -14,7 +14,7 @@ import torch
 import oracle
 import quantized_gemm_decode_amd as ql
 from oracle import mx
-from tests.gpu_util import dev_bf16, host_bf16_bits, pack_ref, requires_gpu
+from tests.gpu_util import dev_bf16, host_bf16_bits, pack_mx_scales_ref, pack_ref, requires_gpu
 from workloads import bf16_bits, make_inputs
 
 pytestmark = [pytest.mark.gpu, requires_gpu]
@@ -34,13 +34,15 @@ def _quant(xb, packed=False):
 
 
 def _weights(r):
+    K = r["w_q"].shape[1]
     w_q = torch.from_numpy(np.ascontiguousarray(r["w_q"], dtype=np.uint8)).cuda().view(torch.float8_e4m3fn)
-    return ql.pack_weight(w_q), torch.from_numpy(np.ascontiguousarray(r["s_w"], dtype=np.uint8)).cuda()
+    return ql.pack_weight(w_q), torch.from_numpy(pack_mx_scales_ref(r["s_w"], K)).cuda()
 
 
 def _acts(r):
+    K = r["a_q"].shape[1]
     a_p = torch.from_numpy(pack_ref(r["a_q"])).cuda().view(torch.float8_e4m3fn)
-    return a_p, torch.from_numpy(np.ascontiguousarray(r["s_a"], dtype=np.uint8)).cuda()
+    return a_p, torch.from_numpy(pack_mx_scales_ref(r["s_a"], K)).cuda()
 
 
 def _mx_check(r, y_bits, split, waves_k):
@@ -67,7 +69,8 @@ def test_mx_act_quantizer_bit_exact(M, K):
     assert np.array_equal(q.reshape(M, K), cq) and np.array_equal(s, cs)
     qp, sp = _quant(xb, packed=True)
     n = ql.qlinear_packed_act_bytes(M, K)
-    assert np.array_equal(qp[:n], pack_ref(cq)) and np.array_equal(sp, cs)
+    ns = ql.qlinear_packed_mx_scale_bytes(M, K)
+    assert np.array_equal(qp[:n], pack_ref(cq)) and np.array_equal(sp[:ns], pack_mx_scales_ref(cs, K))
 
 
 def test_mx_quantizer_special_blocks():
@@ -93,7 +96,10 @@ def test_mx_quantizer_special_blocks():
     cq, cs = mx.mx_quantize(xb)
     for packed in (False, True):
         q, s = _quant(xb, packed)
-        assert np.array_equal(s, cs), packed
+        if packed:
+            assert np.array_equal(s[:ql.qlinear_packed_mx_scale_bytes(8, K)], pack_mx_scales_ref(cs, K))
+        else:
+            assert np.array_equal(s, cs)
         got = q[:ql.qlinear_packed_act_bytes(8, K)] if packed else q.reshape(8, K)
         assert np.array_equal(got, pack_ref(cq) if packed else cq), packed
     assert cs[0, 0] == 0 and np.all(cq[1] == 0x80)
@@ -109,6 +115,16 @@ def test_mx_weight_quantizer_bit_exact(N, K):
     cq, cs = mx.mx_quantize(wb[rows])
     assert np.array_equal(w_q.view(torch.uint8).cpu().numpy()[rows], cq)
     assert np.array_equal(w_s.cpu().numpy()[rows], cs)
+
+
+@pytest.mark.parametrize("R,K", [(37, 384), (16, 128), (1, 4096), (300, 1024)])
+def test_mx_scale_packing_matches_the_layout_definition(R, K):
+    s = np.random.default_rng(R).integers(0, 255, (R, K // 32), dtype=np.uint8)
+    out = ql.pack_mx_scales(torch.from_numpy(s).cuda())
+    torch.cuda.synchronize()
+    n = ql.qlinear_packed_mx_scale_bytes(R, K)
+    assert n == -(-R // 16) * (K // 128) * 64
+    assert np.array_equal(out.cpu().numpy()[:n], pack_mx_scales_ref(s, K))
 
 
 @pytest.mark.parametrize("vi", range(len(MXV)))
@@ -148,15 +164,17 @@ def test_mx_planner_plans_at_full_size(lab, N, K, M):
     plan = ql.qlinear_plan_layouts(ql.MXFP8, M, N, K, 1, 1)
     w_q, w_s = ql.quantize_weight(ql.MXFP8, w.cuda())
     a_p = ql.act_buffer(plan)
-    a_s = torch.empty(ql.act_scale_shape(ql.MXFP8, M, K), dtype=torch.uint8, device="cuda")
+    a_s = ql.act_scale_buffer(plan)
     y = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
-    ql.qlinear_forward(plan, x.cuda(), a_p, a_s, ql.pack_weight(w_q), w_s, y, plan.new_workspace())
+    ql.qlinear_forward(plan, x.cuda(), a_p, a_s, ql.pack_weight(w_q), ql.pack_mx_scales(w_s), y,
+                       plan.new_workspace())
     torch.cuda.synchronize()
     cols = np.sort(np.random.default_rng(M + N).choice(N, 64, replace=False))
     r = mx.mx_reference(xb, wb[cols])
     n = ql.qlinear_packed_act_bytes(M, K)
     assert np.array_equal(a_p[:n].view(torch.uint8).cpu().numpy(), pack_ref(r["a_q"]))
-    assert np.array_equal(a_s.cpu().numpy(), r["s_a"])
+    ns = ql.qlinear_packed_mx_scale_bytes(M, K)
+    assert np.array_equal(a_s.cpu().numpy()[:ns], pack_mx_scales_ref(r["s_a"], K))
     st = _mx_check(r, host_bf16_bits(y)[:, cols], plan.facts["chunks"], plan.config["waves_k"])
     assert st["ok"] and st["frac_within_ulp"] >= 0.95, (plan.config, st)
 
@@ -172,7 +190,7 @@ def test_mx_forward_equals_quantize_then_run_and_graph_replays():
     y_run, _ = _run(plan, a_p, a_s, w_p, w_s)
     xd = x.cuda()
     a_q = ql.act_buffer(plan)
-    s_q = torch.empty(ql.act_scale_shape(ql.MXFP8, M, K), dtype=torch.uint8, device="cuda")
+    s_q = ql.act_scale_buffer(plan)
     y = torch.zeros(M, N, dtype=torch.bfloat16, device="cuda")
     ql.qlinear_forward(plan, xd, a_q, s_q, w_p, w_s, y)
     torch.cuda.synchronize()
