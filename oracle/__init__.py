@@ -9,7 +9,7 @@ plus the dynamic activation quantizer and the offline weight quantizer, for
 the three formats of the pages (FP8_Dynamic, W8A8_INT8, Block_FP8), and the
 SiLU-and-mul epilogue of a merged gate/up projection (``glu``), and the
 MXFP8 linear (E4M3 elements with E8M0 scales per 32 values along K, the
-scales applied inside the product; ``mx``).
+scales applied inside the product) and its MXFP4-weight variant (``mx``).
 
 Who may use it: only ``tests/``, ``__graft_entry__.smoke()`` and the
 ``cpu_baseline`` leg of ``bench.py``.  The product path (the HIP library and
@@ -45,7 +45,8 @@ from .linear import (contract_exact, contract_abs, epilogue, reference, MATRIX_C
                      emulate_fp32_accumulation)
 from .glu import silu, glu_values, glu_reference, SILU_SLOPE_MAX
 from .mx import (MX_BLOCK, mx_shared_exponent, mx_quantize, mx_dequantize, mx_contract_exact,
-                 mx_contract_abs, mx_tolerance_bound, mx_reference)
+                 mx_contract_abs, mx_tolerance_bound, mx_reference, e2m1_encode, e2m1_decode,
+                 mx4_shared_exponent, mx4_quantize, mx4_contract_exact, mx4_tolerance_bound, mx4_reference)
 
 __all__ = [
     "bf16_bits_from_f32", "bf16_bits_to_f32", "ulp_bf16", "f32",
@@ -57,5 +58,6 @@ __all__ = [
     "silu", "glu_values", "glu_reference", "SILU_SLOPE_MAX",
     "contract_split_order", "contract_swap_ab", "emulate_fp32_accumulation",
     "MX_BLOCK", "mx_shared_exponent", "mx_quantize", "mx_dequantize", "mx_contract_exact",
-    "mx_contract_abs", "mx_tolerance_bound", "mx_reference",
+    "mx_contract_abs", "mx_tolerance_bound", "mx_reference", "e2m1_encode", "e2m1_decode",
+    "mx4_shared_exponent", "mx4_quantize", "mx4_contract_exact", "mx4_tolerance_bound", "mx4_reference",
 ]

@@ -1,5 +1,6 @@
-"""MXFP8 quantized linear (E4M3 elements, one E8M0 scale per 32 values along K)
--- test infrastructure only.
+"""MXFP8 quantized linear (E4M3 elements, one E8M0 scale per 32 values along K),
+and MXFP4 weights (E2M1 elements) beside MXFP8 activations -- test
+infrastructure only.
 
 Source.  Noticias, "¿Qué son vLLM y Helion?", lists the quantized linear
 formats that vLLM's linear backends serve: FP8 and INT8 (the three formats of
@@ -31,6 +32,13 @@ output is bf16(Y).  Exactness: every E4M3 product is a multiple of 2**-18 with
 magnitude < 2**17.7, so each P_b (32 products) is exact in binary64; the
 sum over blocks of P_b times a power of two is taken with ``math.fsum``,
 which returns the correctly rounded binary64 value of the exact sum.
+
+MXFP4 (the same specification, E2M1 elements: 1 sign, 2 exponent bits with
+bias 1, 1 mantissa bit; magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6): the shared
+exponent is floor(log2(amax)) - 2 (6 = 1.5 * 2**2), elements are w / 2**e
+clamped to +-6 and rounded to nearest E2M1, ties to even.  Here it quantizes
+the weights only; the activations stay MXFP8 (the decode stream is the
+weights, and 4-bit activations would cost accuracy for no bandwidth).
 """
 
 import math
@@ -125,6 +133,99 @@ def mx_tolerance_bound(a_codes, a_scales, w_codes, w_scales, depth, eta):
     over the products with their block scales applied."""
     gamma = depth * U32 / (1.0 - depth * U32) + eta
     return gamma * mx_contract_abs(a_codes, a_scales, w_codes, w_scales) * (1.0 + 4.0 * U32)
+
+
+# ----------------------------------------------------------------------------
+# MXFP4 weights (OCP MX v1.0, E2M1 elements) beside MXFP8 activations.
+# ----------------------------------------------------------------------------
+
+E2M1_MAX = 6.0
+E2M1_EMAX = 2          # exponent of E2M1's largest normal, 6 = 1.5 * 2**2
+
+
+def e2m1_decode(codes):
+    """Values of E2M1 codes (low 4 bits: sign, 2 exponent bits with bias 1,
+    1 mantissa bit; exponent field 0 holds the subnormal m * 0.5)."""
+    c = np.asarray(codes, dtype=np.int64) & 0xF
+    sign = np.where(c & 0x8, -1.0, 1.0)
+    ex, m = (c >> 1) & 0x3, c & 0x1
+    mag = np.where(ex == 0, 0.5 * m, (1.0 + 0.5 * m) * np.ldexp(1.0, ex - 1))
+    return sign * mag
+
+
+def e2m1_encode(v):
+    """E2M1 codes (uint8, low nibble) of values in [-6, 6], round to nearest,
+    ties to even (the even code has mantissa bit 0); the sign of -0.0 kept."""
+    v = np.asarray(v, dtype=np.float64)
+    if np.any(np.isnan(v)) or np.any(np.abs(v) > E2M1_MAX):
+        raise ValueError("e2m1_encode expects finite inputs already clamped to +-6")
+    table = e2m1_decode(np.arange(8))                  # the 8 magnitudes, increasing
+    a = np.abs(v)[..., None]
+    d = np.abs(a - table)
+    best = d.min(axis=-1, keepdims=True)
+    cand = d == best                                   # one nearest value, or two at a tie
+    even = (np.arange(8) & 1) == 0
+    code = np.where(np.any(cand & even, axis=-1), np.argmax(cand & even, axis=-1), np.argmax(cand, axis=-1))
+    return (code | np.where(np.signbit(v), 0x8, 0)).astype(np.uint8)
+
+
+def mx4_shared_exponent(amax):
+    """e = floor(log2(amax)) - 2, clamped to [-127, 127]; -127 where amax == 0."""
+    a = np.asarray(amax, dtype=np.float64)
+    _, ex = np.frexp(a)
+    e = np.where(a == 0, -E8M0_BIAS, (ex - 1) - E2M1_EMAX)
+    return np.clip(e, -E8M0_BIAS, E8M0_BIAS).astype(np.int64)
+
+
+def mx4_quantize(w_bits):
+    """Quantize bf16 rows to MXFP4: E2M1 codes (one per element, uint8 [R, C])
+    and E8M0 scales [R, C/32]; elements are w / 2**e clamped to +-6."""
+    w = bf16_bits_to_f32(w_bits).astype(np.float64)
+    R, C = w.shape
+    if C % MX_BLOCK:
+        raise ValueError("MXFP4 needs the row length to be a multiple of 32")
+    blocks = w.reshape(R, C // MX_BLOCK, MX_BLOCK)
+    amax = np.max(np.abs(blocks), axis=2) if C else np.zeros((R, 0))
+    e = mx4_shared_exponent(amax)
+    t = np.clip(blocks * np.ldexp(1.0, -e)[:, :, None], -E2M1_MAX, E2M1_MAX)
+    return e2m1_encode(t.reshape(R, C)), (e + E8M0_BIAS).astype(np.uint8)
+
+
+def mx4_contract_exact(a_codes, a_scales, w_codes, w_scales):
+    """y_true of MXFP8 activations times MXFP4 weights, correctly rounded to
+    binary64: every product is a multiple of 2**-10 below 2**11.4, so each
+    32-product block sum is exact, and the blocks are added with fsum."""
+    a = e4m3_decode(a_codes)
+    w = e2m1_decode(w_codes)
+    M, K = a.shape
+    nb = K // MX_BLOCK
+    P = np.stack([a[:, b * MX_BLOCK:(b + 1) * MX_BLOCK] @ w[:, b * MX_BLOCK:(b + 1) * MX_BLOCK].T
+                  for b in range(nb)]) if nb else np.zeros((0, M, w.shape[0]))
+    terms = np.ldexp(P, _scale_exponents(a_scales, w_scales))
+    flat = terms.reshape(nb, -1)
+    return np.array([math.fsum(flat[:, i]) for i in range(flat.shape[1])],
+                    dtype=np.float64).reshape(M, w.shape[0])
+
+
+def mx4_tolerance_bound(a_codes, a_scales, w_codes, w_scales, depth, eta):
+    """The MXFP8 bound with E2M1 weight values."""
+    a = np.abs(e4m3_decode(a_codes))
+    w = np.abs(e2m1_decode(w_codes))
+    nb = a.shape[1] // MX_BLOCK
+    P = np.stack([a[:, b * MX_BLOCK:(b + 1) * MX_BLOCK] @ w[:, b * MX_BLOCK:(b + 1) * MX_BLOCK].T
+                  for b in range(nb)])
+    absS = np.sum(np.ldexp(P, _scale_exponents(a_scales, w_scales)), axis=0)
+    gamma = depth * U32 / (1.0 - depth * U32) + eta
+    return gamma * absS * (1.0 + 4.0 * U32)
+
+
+def mx4_reference(x_bits, w_bits):
+    """MXFP8 activations (mx_quantize) times MXFP4 weights (mx4_quantize)."""
+    a_q, s_a = mx_quantize(x_bits)
+    w_q, s_w = mx4_quantize(w_bits)
+    y_true = mx4_contract_exact(a_q, s_a, w_q, s_w)
+    return dict(a_q=a_q, s_a=s_a, w_q=w_q, s_w=s_w, y_true=y_true,
+                y_ref=bf16_bits_from_f32(f32(y_true)))
 
 
 def mx_reference(x_bits, w_bits):

@@ -122,3 +122,21 @@ def mx_quantize_block(values, negzero):
         t = max(F(-448), min(F(448), v / F(2) ** e))
         out.append((re4m3(t), v < 0 or (v == 0 and nz)))
     return out, e
+
+
+def re2m1(x):
+    """Round to E2M1 (2 significand bits, smallest normal exponent 0, so the
+    subnormal quantum is 1/2), ties to even."""
+    return round_float(F(x), 2, 0)
+
+
+def mx4_quantize_block(values, negzero):
+    """One MXFP4 block: e = floor(log2 amax) - 2 clamped to [-127, 127] (-127 for
+    an all-zero block); elements v / 2**e clamped to +-6, rounded to E2M1."""
+    amax = max((abs(v) for v in values), default=F(0))
+    e = -127 if amax == 0 else max(-127, min(127, floor_log2(amax) - 2))
+    out = []
+    for v, nz in zip(values, negzero):
+        t = max(F(-6), min(F(6), v / F(2) ** e))
+        out.append((re2m1(t), v < 0 or (v == 0 and nz)))
+    return out, e

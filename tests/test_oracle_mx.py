@@ -186,3 +186,98 @@ def test_tolerance_accepts_binary32_order_and_rejects_a_dropped_block():
     drop = (acc - (a[:, 64:96] @ wd[:, 64:96].T).astype(np.float32)).astype(np.float32)
     st = oracle.check_fp8_parity(oracle.bf16_bits_from_f32(drop), r["y_ref"], r["y_true"], B)
     assert not st["ok"] and st["n_fail"] > 0.5 * M * N, st
+
+
+# ---------------------------------------------------------------- MXFP4 weights
+
+def test_e2m1_codec_matches_generic_rounding():
+    """Every multiple of 1/256 in [-6, 6] and random values: the encoder's code
+    decodes to the exact-rational round-to-nearest-even E2M1 value, sign kept."""
+    v = np.concatenate([np.arange(-1536, 1537) / 256.0, np.random.default_rng(4).uniform(-6, 6, 4000), [-0.0]])
+    codes = oracle.e2m1_encode(v)
+    dec = oracle.e2m1_decode(codes)
+    for x, c, d in zip(v, codes, dec):
+        want = X.re2m1(F(float(x)))
+        assert F(float(d)) == want or (want == 0 and d == 0), (x, c)
+        assert bool(c & 0x8) == bool(np.signbit(x)), x
+    assert list(oracle.e2m1_decode(np.arange(8))) == [0, 0.5, 1, 1.5, 2, 3, 4, 6]
+
+
+def test_mx4_shared_exponent_from_the_bit_fields_for_every_bf16():
+    bits = np.arange(1, 0x7F80, dtype=np.uint32)
+    ex, m = (bits >> 7) & 0xFF, bits & 0x7F
+    lead = np.array([int(v).bit_length() - 1 for v in m])
+    fl2 = np.where(ex > 0, ex.astype(np.int64) - 127, lead - 133)
+    amax = (bits << 16).astype(np.uint32).view(np.float32).astype(np.float64)
+    assert np.array_equal(mx.mx4_shared_exponent(amax), np.maximum(fl2 - 2, -127))
+
+
+def test_mx4_quantizer_matches_exact_rational_blocks():
+    rng = np.random.default_rng(5)
+    rows = np.stack([rng.standard_normal(96) * s for s in (1.0, 1e-3, 0.02, 1e-37, 3e4)])
+    rows[1, :32] = 0.0
+    wb = _bf(rows.astype(np.float32))
+    wb[1, 40] = 0x8000
+    codes, scales = mx.mx4_quantize(wb)
+    dec = oracle.e2m1_decode(codes)
+    for r in range(wb.shape[0]):
+        for b in range(3):
+            blk = wb[r, 32 * b:32 * b + 32]
+            want, e = X.mx4_quantize_block([_frac_of_bits(u) for u in blk], [int(u) == 0x8000 for u in blk])
+            assert int(scales[r, b]) == e + 127
+            for j, (val, neg) in enumerate(want):
+                assert F(float(abs(dec[r, 32 * b + j]))) == abs(val)
+                assert bool(codes[r, 32 * b + j] & 0x8) == neg, (r, b, j)
+
+
+def test_mx4_largest_element_of_every_block_lies_in_4_6():
+    _, w = make_inputs(4096, 64, 1, 0.02, seed=8)
+    codes, _ = mx.mx4_quantize(bf16_bits(w))
+    big = np.abs(oracle.e2m1_decode(codes)).reshape(64, -1, 32).max(axis=2)
+    assert np.all((big >= 4) & (big <= 6))
+
+
+def test_mx4_contraction_equals_exact_rational_sum():
+    rng = np.random.default_rng(14)
+    M, N, K = 3, 4, 128
+    a = rng.integers(0, 256, (M, K), dtype=np.uint8)
+    a[(a & 0x7F) == 0x7F] = 0x30
+    w = rng.integers(0, 16, (N, K), dtype=np.uint8)
+    sa = rng.integers(100, 160, (M, K // 32), dtype=np.uint8)
+    sw = rng.integers(60, 200, (N, K // 32), dtype=np.uint8)
+    y = mx.mx4_contract_exact(a, sa, w, sw)
+    e2m1 = {c: (-1 if c & 8 else 1) * [F(0), F(1, 2), F(1), F(3, 2), F(2), F(3), F(4), F(6)][c & 7] for c in range(16)}
+    for m in range(M):
+        for n in range(N):
+            s = sum(X.E4M3[int(a[m, k])] * e2m1[int(w[n, k])] * F(2) ** (int(sa[m, k // 32]) + int(sw[n, k // 32]) - 254)
+                    for k in range(K))
+            assert y[m, n] == float(s), (m, n)
+
+
+def test_mx4_closed_form_constant_inputs():
+    """X = 1.0 (MXFP8: code 256 at 2**-8) and W = bf16(0.02) = 1.28125 * 2**-6:
+    W's exponent is -6 - 2 = -8, w / 2**-8 = 5.125 rounds to 6 (code 7), so
+    every product is 6 * 2**-8 and Y = K * 0.0234375."""
+    M, N, K = 2, 3, 256
+    r = mx.mx4_reference(np.full((M, K), 0x3F80, np.uint16), np.full((N, K), 0x3CA4, np.uint16))
+    assert np.all(r["w_q"] == 7) and np.all(r["s_w"] == 119)
+    assert np.all(r["y_true"] == K * 0.0234375)
+
+
+def test_mx4_tolerance_accepts_binary32_order_and_rejects_a_dropped_block():
+    M, N, K = 8, 64, 2048
+    x, w = make_inputs(K, N, M, 0.02, seed=15)
+    r = mx.mx4_reference(bf16_bits(x), bf16_bits(w))
+    B = mx.mx4_tolerance_bound(r["a_q"], r["s_a"], r["w_q"], r["s_w"], oracle.summation_depth(K, 2, 4),
+                               oracle.MATRIX_CORE_ETA)
+    a = mx.mx_dequantize(r["a_q"], r["s_a"])
+    wd = (oracle.e2m1_decode(r["w_q"]).reshape(N, -1, 32)
+          * np.ldexp(1.0, r["s_w"].astype(int) - 127)[:, :, None]).reshape(N, K)
+    acc = np.zeros((M, N), np.float32)
+    for kb in range(K // 128):
+        acc = (acc + (a[:, kb * 128:(kb + 1) * 128] @ wd[:, kb * 128:(kb + 1) * 128].T).astype(np.float32)).astype(np.float32)
+    st = oracle.check_fp8_parity(oracle.bf16_bits_from_f32(acc), r["y_ref"], r["y_true"], B)
+    assert st["ok"] and st["frac_within_ulp"] > 0.99, st
+    drop = (acc - (a[:, 64:96] @ wd[:, 64:96].T).astype(np.float32)).astype(np.float32)
+    st = oracle.check_fp8_parity(oracle.bf16_bits_from_f32(drop), r["y_ref"], r["y_true"], B)
+    assert not st["ok"] and st["n_fail"] > 0.5 * M * N, st
