@@ -44,6 +44,8 @@ def algorithmic_bytes(fmt, M, N, K):
         return N * K + 4 * (-(-N // 128)) * (K // 128) + M * K + 4 * M * (K // 128) + 2 * M * N
     if fmt == 3:   # MXFP8: one E8M0 byte per 32 codes on both operands
         return N * K + N * (K // 32) + M * K + M * (K // 32) + 2 * M * N
+    if fmt == 4:   # MXFP4 weights (half a byte a value), MXFP8 activations
+        return N * K // 2 + N * (K // 32) + M * K + M * (K // 32) + 2 * M * N
     return N * K + 4 * N + M * K + 4 * M + 2 * M * N
 
 
@@ -54,7 +56,7 @@ def fused_kernel_bytes(fmt, M, N, K):
 
 
 def quantizer_bytes(fmt, M, K):
-    if fmt == 3:
+    if fmt in (3, 4):
         return 2 * M * K + M * K + M * (K // 32)
     return 2 * M * K + M * K + (4 * M * (K // 128) if fmt == 2 else 4 * M)
 
@@ -302,10 +304,10 @@ def main(argv=None):
         x, w = make_inputs(K, N, max(wl.ms), wl.sigma_w, seed=wl.seed)
         wd = w.to(dev)
         w_q, w_s = ql.quantize_weight(fmt, wd)
-        if args.layout != "rowmajor":
-            w_q = ql.pack_weight(w_q)          # offline, like the quantization itself
-            if fmt == ql.MXFP8:
-                w_s = ql.pack_mx_scales(w_s)   # MXFP8 plans read the scales in lane order
+        if args.layout != "rowmajor":           # offline, like the quantization itself
+            w_q = ql.pack_weight_fp4(w_q) if fmt == ql.MXFP4 else ql.pack_weight(w_q)
+            if fmt in ql.MX_FORMATS:
+                w_s = ql.pack_mx_scales(w_s)   # MX plans read the scales in lane order
         del wd
         copies = max(2, -(-(1 << 30) // (N * K)))
         wq_all = torch.empty((copies,) + tuple(w_q.shape), dtype=w_q.dtype, device=dev)
@@ -461,7 +463,7 @@ def main(argv=None):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp8_e4m3" if fmt != 1 else "int8",
+        "dtype": {1: "int8", 4: "fp8_e4m3 x fp4_e2m1"}.get(fmt, "fp8_e4m3"),
         "data": "synthetic (seeded N(0,1) activations with 1%% x20 outlier channels, N(0,%g) weights)" % wl.sigma_w,
         "config": {"workload": wl.name, "format": ql.FORMAT_NAMES[fmt],
                    "shapes": ["%s %dx%d" % s for s in wl.shapes], "token_counts": list(wl.ms),
@@ -579,7 +581,9 @@ def cpu_baseline(wl, shapes, budget_s):
     b_total = 0
     for (lab, N, K) in wl.shapes:
         x, w = make_inputs(K, N, max(wl.ms), wl.sigma_w, seed=wl.seed)
-        if fmt == 3:
+        if fmt == 4:
+            w_q, s_w = oracle.mx4_quantize(bf16_bits(w))                # offline step: not timed
+        elif fmt == 3:
             w_q, s_w = oracle.mx_quantize(bf16_bits(w))                 # offline step: not timed
         else:
             w_q, s_w = oracle.quantize_weight(fmt, bf16_bits(w))      # offline step: not timed
@@ -588,9 +592,9 @@ def cpu_baseline(wl, shapes, budget_s):
                 continue       # a single fp64 GEMM of minutes: outside the bounded sample
             xb = bf16_bits(x[:M])
             t0 = time.perf_counter()
-            if fmt == 3:
+            if fmt in (3, 4):
                 a_q, s_a = oracle.mx_quantize(xb)
-                y = oracle.mx_contract_exact(a_q, s_a, w_q, s_w)
+                y = (oracle.mx4_contract_exact if fmt == 4 else oracle.mx_contract_exact)(a_q, s_a, w_q, s_w)
                 oracle.bf16_bits_from_f32(oracle.f32(y))
             else:
                 a_q, s_a = oracle.quantize_act(fmt, xb)

@@ -20,6 +20,8 @@
  *   QL_BLOCK_FP8    E4M3 with 1x128 activation groups and 128x128 weight blocks
  *   QL_MXFP8        E4M3 with one E8M0 (power-of-two) scale per 32 values along K,
  *                   activations and weights alike
+ *   QL_MXFP4        MXFP4 weights (E2M1 values, two a byte, one E8M0 scale per 32)
+ *                   with MXFP8 activations
  * Quantization rule (the pages give none; the plain reading): symmetric
  * absmax, s = fl(amax / Q) with Q = 127 (int8) or 448 (E4M3); code =
  * round-half-even(fl(x / s)) clamped to [-Q, Q]; an all-zero group gets s = 1.
@@ -29,7 +31,10 @@
  * e = floor(log2(amax)) - 8 clamped to [-127, 127] (-127 for an all-zero
  * block), scale byte e + 127, code = E4M3 round-to-nearest-even of
  * x * 2^-e clamped to [-448, 448].  The matrix core applies the scales inside
- * the product: Y = bf16(sum_k 2^(ea+ew) a_k w_k), no scale epilogue.
+ * the product: Y = bf16(sum_k 2^(ea+ew) a_k w_k), no scale epilogue.  MXFP4
+ * weights: the same rule with E2M1 elements (values 0, 0.5, 1, 1.5, 2, 3, 4,
+ * 6; e = floor(log2(amax)) - 2, clamp to [-6, 6], round to nearest, ties to
+ * the even code); W_q holds them two a byte, low nibble = even K, [N, K/2].
  *
  * Data layouts (all row-major, caller-owned device memory):
  *   X      bf16   [M, K]                 activations (input of the quantizer)
@@ -77,7 +82,8 @@ typedef enum {
   QL_FP8_DYNAMIC = 0,
   QL_W8A8_INT8 = 1,
   QL_BLOCK_FP8 = 2,
-  QL_MXFP8 = 3
+  QL_MXFP8 = 3,
+  QL_MXFP4 = 4
 } ql_format;
 
 typedef enum {
@@ -212,7 +218,8 @@ ql_status qlinear_encode_e4m3(const float* x, int64_t n, void* codes, void* stre
  * Offline weight quantizer: per output channel (rows of W) or per 128x128
  * block for Block_FP8 (the last block row may be ragged).
  *   w_bf16 [N, K] in;  w_q [N, K] out;  w_scale fp32 [N] or [ceil(N/128), K/128]
- *   out (MXFP8: E8M0 bytes [N, K/32], the activation rule applied to rows of W).
+ *   out (MXFP8: E8M0 bytes [N, K/32], the activation rule applied to rows of W;
+ *   MXFP4: w_q is [N, K/2] bytes of E2M1 pairs, w_scale E8M0 bytes [N, K/32]).
  * Same rounding contract as the activation quantizer.
  */
 ql_status qlinear_quantize_weight(int32_t fmt, const void* w_bf16, int64_t N, int64_t K,
@@ -244,6 +251,18 @@ ql_status qlinear_pack_weight(const void* w_q, int64_t N, int64_t K, void* w_pac
  * quantizer writes this layout directly.  Enqueue-only.
  */
 int64_t qlinear_packed_mx_scale_bytes(int64_t R, int64_t K);
+
+/*
+ * MXFP4 weight packing: 1 KB per (16-row group t, 128-wide K block kb) at
+ * (t * K/128 + kb) * 1024; lane l's 16 bytes at l*16 hold row 16t + l%16, K
+ * [128kb + 32*(l/16), +32) as E2M1 pairs (low nibble first) -- the 32 values
+ * lane l hands the scaled matrix core as its E2M1 operand, which pairs them
+ * with the same K of the E4M3 operand's packed pieces.  Reads w_q [N, K/2]
+ * (K % 128 == 0), writes qlinear_packed_weight_bytes_fp4(N, K) bytes, zero
+ * past N.  The scales are packed with qlinear_pack_mx_scales.  Enqueue-only.
+ */
+int64_t qlinear_packed_weight_bytes_fp4(int64_t N, int64_t K);
+ql_status qlinear_pack_weight_fp4(const void* w_q, int64_t N, int64_t K, void* w_packed, void* stream);
 ql_status qlinear_pack_mx_scales(const void* scales, int64_t R, int64_t K, void* packed, void* stream);
 
 /*
@@ -331,9 +350,11 @@ void qlinear_plan_destroy(ql_plan plan);
  * group's partial inside the K loop and rounds the fp32 sum to bf16; MXFP8
  * hands the E8M0 bytes to the scaled matrix-core instruction, which applies
  * them to every 32-wide block of products, and rounds the fp32 sum to bf16.
- * MXFP8 plans use the decode algorithm (M <= 64) with packed weights and
- * packed activations (a_mode 2 or 3), and read both scales in the lane
- * order of qlinear_pack_mx_scales.
+ * MXFP8 and MXFP4 plans use the decode algorithm (M <= 64) with packed
+ * weights (MXFP4: qlinear_pack_weight_fp4) and packed activations (a_mode 2
+ * or 3), and read both scales in the lane order of qlinear_pack_mx_scales.
+ * MXFP4 plans take MXFP8 activations (qlinear_quantize_act_packed with
+ * fmt = QL_MXFP4 writes them).
  * a_q is in the plan's activation layout: row-major [M, K], or packed when
  * the plan's a_mode is 2 or 3; w_q in the plan's weight layout (w_layout).
  * Enqueue-only; workspace may be NULL when qlinear_workspace_bytes is 0.

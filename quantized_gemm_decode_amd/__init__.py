@@ -4,8 +4,9 @@
 
 Formats: FP8_Dynamic (OCP E4M3, per-token / per-channel), W8A8_INT8
 (per-token / per-channel), Block_FP8 (1x128 activation groups, 128x128
-weight blocks) and MXFP8 (E4M3 with one E8M0 scale byte per 32 values along
-K, applied by the matrix core).  All arithmetic runs in the hand-written gfx950 HIP kernels
+weight blocks), MXFP8 (E4M3 with one E8M0 scale byte per 32 values along
+K, applied by the matrix core) and MXFP4 (E2M1 weights two a byte, same
+scales, MXFP8 activations).  All arithmetic runs in the hand-written gfx950 HIP kernels
 of ``libqlinear.so`` behind the C ABI of ``include/qlinear.h``; this module
 only marshals torch tensors (device memory) and streams into that ABI, with
 the same function names.  There is no CPU or PyTorch fallback: if the
@@ -20,9 +21,11 @@ import torch
 from . import _lib
 from ._lib import QLConfig, QLPlanFacts
 
-FP8_DYNAMIC, W8A8_INT8, BLOCK_FP8, MXFP8 = 0, 1, 2, 3
-FORMATS = (FP8_DYNAMIC, W8A8_INT8, BLOCK_FP8, MXFP8)
-FORMAT_NAMES = {FP8_DYNAMIC: "FP8_Dynamic", W8A8_INT8: "W8A8_INT8", BLOCK_FP8: "Block_FP8", MXFP8: "MXFP8"}
+FP8_DYNAMIC, W8A8_INT8, BLOCK_FP8, MXFP8, MXFP4 = 0, 1, 2, 3, 4
+FORMATS = (FP8_DYNAMIC, W8A8_INT8, BLOCK_FP8, MXFP8, MXFP4)
+FORMAT_NAMES = {FP8_DYNAMIC: "FP8_Dynamic", W8A8_INT8: "W8A8_INT8", BLOCK_FP8: "Block_FP8", MXFP8: "MXFP8",
+                MXFP4: "MXFP4"}
+MX_FORMATS = (MXFP8, MXFP4)
 ALGO_DECODE, ALGO_TILED = 0, 1
 SOURCES = {0: "table", 1: "heuristic", 2: "custom"}
 DEFAULT_TABLE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "tables", "decode_table.txt")
@@ -75,23 +78,33 @@ SCALE_DTYPES = (torch.float32, torch.uint8)      # binary32 scales, or MXFP8's E
 # ----------------------------------------------------------------- shapes
 
 def act_scale_shape(fmt, M, K):
-    if fmt == MXFP8:
+    if fmt in MX_FORMATS:
         return (M, K // 32)
     return (M, K // 128) if fmt == BLOCK_FP8 else (M,)
 
 
 def weight_scale_shape(fmt, N, K):
-    if fmt == MXFP8:
+    if fmt in MX_FORMATS:
         return (N, K // 32)
     return (-(-N // 128), K // 128) if fmt == BLOCK_FP8 else (N,)
 
 
 def scale_dtype(fmt):
-    return torch.uint8 if fmt == MXFP8 else torch.float32
+    return torch.uint8 if fmt in MX_FORMATS else torch.float32
 
 
 def code_dtype(fmt):
+    """Activation code dtype (MXFP4 plans take E4M3 activations)."""
     return torch.int8 if fmt == W8A8_INT8 else torch.float8_e4m3fn
+
+
+def weight_code_shape(fmt, N, K):
+    """Row-major W_q shape: MXFP4 holds two E2M1 values a byte."""
+    return (N, K // 2) if fmt == MXFP4 else (N, K)
+
+
+def weight_code_dtype(fmt):
+    return torch.uint8 if fmt == MXFP4 else code_dtype(fmt)
 
 
 # ----------------------------------------------------------------- quantizers
@@ -133,7 +146,7 @@ def quantize_act(fmt, x, stream=None):
 
 def packed_act_scale_shape(fmt, M, K):
     """Shape of s_a as the packed quantizer writes it (MXFP8: flat lane-order bytes)."""
-    return (max(qlinear_packed_mx_scale_bytes(M, K), 16),) if fmt == MXFP8 else act_scale_shape(fmt, M, K)
+    return (max(qlinear_packed_mx_scale_bytes(M, K), 16),) if fmt in MX_FORMATS else act_scale_shape(fmt, M, K)
 
 
 def act_scale_buffer(plan, device="cuda"):
@@ -160,7 +173,7 @@ def act_buffer(plan, device="cuda"):
 def quantize_weight(fmt, w, stream=None):
     """Allocate (W_q, s_w) and run the weight quantizer."""
     N, K = w.shape
-    w_q = torch.empty(N, K, dtype=code_dtype(fmt), device=w.device)
+    w_q = torch.empty(weight_code_shape(fmt, N, K), dtype=weight_code_dtype(fmt), device=w.device)
     w_s = torch.empty(weight_scale_shape(fmt, N, K), dtype=scale_dtype(fmt), device=w.device)
     qlinear_quantize_weight(fmt, w, w_q, w_s, stream)
     return w_q, w_s
@@ -199,6 +212,19 @@ def pack_mx_scales(s, stream=None):
     R, KS = s.shape
     out = torch.empty(max(qlinear_packed_mx_scale_bytes(R, KS * 32), 16), dtype=torch.uint8, device=s.device)
     qlinear_pack_mx_scales(s, KS * 32, out, stream)
+    return out
+
+
+def qlinear_packed_weight_bytes_fp4(N, K):
+    return int(lib().qlinear_packed_weight_bytes_fp4(N, K))
+
+
+def pack_weight_fp4(w_q, stream=None):
+    """MXFP4 row-major E2M1 pairs [N, K/2] -> a new flat buffer of packed 1 KB tiles."""
+    N, K = w_q.shape[0], w_q.shape[1] * 2
+    out = torch.empty(max(qlinear_packed_weight_bytes_fp4(N, K), 16), dtype=torch.uint8, device=w_q.device)
+    _check(lib().qlinear_pack_weight_fp4(_ptr(w_q, "w_q", torch.uint8), N, K, _ptr(out, "w_packed", torch.uint8),
+                                         _stream(stream)), "qlinear_pack_weight_fp4")
     return out
 
 

@@ -32,6 +32,8 @@ SIGNATURES = {
     "qlinear_encode_e4m3": (c_i32, [c_vp, c_i64, c_vp, c_vp]),
     "qlinear_pack_weight": (c_i32, [c_vp, c_i64, c_i64, c_vp, c_vp]),
     "qlinear_packed_mx_scale_bytes": (c_i64, [c_i64, c_i64]),
+    "qlinear_packed_weight_bytes_fp4": (c_i64, [c_i64, c_i64]),
+    "qlinear_pack_weight_fp4": (c_i32, [c_vp, c_i64, c_i64, c_vp, c_vp]),
     "qlinear_pack_mx_scales": (c_i32, [c_vp, c_i64, c_i64, c_vp, c_vp]),
     "qlinear_table_load": (c_i32, [c_cp, ctypes.POINTER(c_i64)]),
     "qlinear_table_clear": (None, []),

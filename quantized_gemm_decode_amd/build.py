@@ -17,7 +17,7 @@ CSRC = os.path.join(PKG, "csrc")
 OBJ = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libqlinear.so")
 
-SOURCES = ["quant.hip", "decode_fp8.hip", "decode_int8.hip", "decode_block.hip", "decode_mx.hip", "tiled_fp8.hip",
+SOURCES = ["quant.hip", "decode_fp8.hip", "decode_int8.hip", "decode_block.hip", "decode_mx.hip", "decode_mx4.hip", "tiled_fp8.hip",
            "tiled_int8.hip", "tiled_block.hip", "api.cpp"]
 
 HIPCC_FLAGS = [

@@ -51,11 +51,13 @@ constexpr int64_t kLdsLimit = 160 * 1024 - 256;
 constexpr int64_t kFusedMaxValues = 16384;
 constexpr int kBuckets[] = {1, 2, 4, 8, 16, 24, 32};
 
-bool valid_fmt(int32_t f) { return f == QL_FP8_DYNAMIC || f == QL_W8A8_INT8 || f == QL_BLOCK_FP8 || f == QL_MXFP8; }
+bool valid_fmt(int32_t f) { return f >= QL_FP8_DYNAMIC && f <= QL_MXFP4; }
+bool is_mx(int32_t f) { return f == QL_MXFP8 || f == QL_MXFP4; }
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool is_pow2(int64_t v) { return v > 0 && (v & (v - 1)) == 0; }
 int kernel_fmt(int32_t f) {
-  return f == QL_W8A8_INT8 ? qlk::FMT_INT8 : f == QL_BLOCK_FP8 ? qlk::FMT_BLOCK : f == QL_MXFP8 ? qlk::FMT_MX : qlk::FMT_FP8;
+  return f == QL_W8A8_INT8 ? qlk::FMT_INT8 : f == QL_BLOCK_FP8 ? qlk::FMT_BLOCK : f == QL_MXFP8 ? qlk::FMT_MX
+       : f == QL_MXFP4 ? qlk::FMT_MX4 : qlk::FMT_FP8;
 }
 
 ql_status check_sizes(int32_t fmt, int64_t R, int64_t K, const char* rname) {
@@ -63,7 +65,7 @@ ql_status check_sizes(int32_t fmt, int64_t R, int64_t K, const char* rname) {
   if (R < 0 || K < 0) return fail(QL_E_INVALID, "negative size (%s=%lld, K=%lld)", rname, (long long)R, (long long)K);
   if (K % 16) return fail(QL_E_INVALID, "K=%lld is not a multiple of 16", (long long)K);
   if (fmt == QL_BLOCK_FP8 && K % 128) return fail(QL_E_INVALID, "Block_FP8 needs K %% 128 == 0 (K=%lld)", (long long)K);
-  if (fmt == QL_MXFP8 && K % 128) return fail(QL_E_INVALID, "MXFP8 needs K %% 128 == 0 (K=%lld)", (long long)K);
+  if (is_mx(fmt) && K % 128) return fail(QL_E_INVALID, "MXFP8 / MXFP4 need K %% 128 == 0 (K=%lld)", (long long)K);
   if (R * K > (int64_t(1) << 30)) return fail(QL_E_UNSUPPORTED, "%s*K=%lld exceeds 2^30", rname, (long long)(R * K));
   return QL_OK;
 }
@@ -161,7 +163,7 @@ ql_config heuristic_tiled(int32_t layout, bool a_packed, int64_t M, int64_t N, i
 
 ql_config heuristic_config(int32_t fmt, int32_t layout, bool a_packed, int64_t M, int64_t N, int64_t K) {
   // MXFP8 has no tiled kernel: its decode kernel serves up to 64 tokens
-  if (M > 32 && !(fmt == QL_MXFP8 && M <= 64)) return heuristic_tiled(layout, a_packed, M, N, K);
+  if (M > 32 && !(is_mx(fmt) && M <= 64)) return heuristic_tiled(layout, a_packed, M, N, K);
   ql_config c{};
   c.w_layout = layout;
   c.algo = QL_ALGO_DECODE;
@@ -262,12 +264,12 @@ ql_status build_plan(int32_t fmt, int64_t M, int64_t N, int64_t K, const ql_conf
     if (cfg.w_layout != 1 || cfg.rows_per_wave != 32 || (cfg.a_mode != 2 && cfg.a_mode != 4))
       return fail(QL_E_UNSUPPORTED, "SiLU-and-mul plans need packed weights, rows_per_wave 32 and a_mode 2 or 4");
   }
-  if (fmt == QL_MXFP8) {
-    if (glu) return fail(QL_E_UNSUPPORTED, "MXFP8 plans have no SiLU-and-mul epilogue");
+  if (is_mx(fmt)) {
+    if (glu) return fail(QL_E_UNSUPPORTED, "MXFP8 / MXFP4 plans have no SiLU-and-mul epilogue");
     if (cfg.algo != QL_ALGO_DECODE || M > 64)
-      return fail(QL_E_UNSUPPORTED, "MXFP8 runs on the decode algorithm (M <= 64)");
+      return fail(QL_E_UNSUPPORTED, "MXFP8 / MXFP4 run on the decode algorithm (M <= 64)");
     if (cfg.w_layout != 1 || (cfg.a_mode != 2 && cfg.a_mode != 3))
-      return fail(QL_E_UNSUPPORTED, "MXFP8 plans need packed weights and packed activations (a_mode 2 or 3)");
+      return fail(QL_E_UNSUPPORTED, "MXFP8 / MXFP4 plans need packed weights and packed activations (a_mode 2 or 3)");
   }
   if (cfg.algo == QL_ALGO_TILED) return build_tiled_plan(fmt, M, N, K, cfg, source, out);
   if (cfg.algo != QL_ALGO_DECODE) return fail(QL_E_INVALID, "unknown algo %d", cfg.algo);
@@ -338,6 +340,7 @@ ql_status build_plan(int32_t fmt, int64_t M, int64_t N, int64_t K, const ql_conf
     case qlk::FMT_INT8: pe = qlk::decode_dispatch_int8(p->key, dim3(1), dim3(1), (size_t)p->lds, nullptr, dummy, true); break;
     case qlk::FMT_BLOCK: pe = qlk::decode_dispatch_block(p->key, dim3(1), dim3(1), (size_t)p->lds, nullptr, dummy, true); break;
     case qlk::FMT_MX: pe = qlk::decode_dispatch_mx(p->key, dim3(1), dim3(1), (size_t)p->lds, nullptr, dummy, true); break;
+    case qlk::FMT_MX4: pe = qlk::decode_dispatch_mx4(p->key, dim3(1), dim3(1), (size_t)p->lds, nullptr, dummy, true); break;
     default: pe = qlk::decode_dispatch_fp8(p->key, dim3(1), dim3(1), (size_t)p->lds, nullptr, dummy, true); break;
   }
   if (pe == hipErrorInvalidDeviceFunction) {
@@ -427,6 +430,7 @@ ql_status launch_gemm(const ql_plan_s* p, const void* a_q, const void* a_scale, 
     case qlk::FMT_INT8: e = qlk::decode_dispatch_int8(p->key, grid, block, (size_t)p->lds, s, a, false); break;
     case qlk::FMT_BLOCK: e = qlk::decode_dispatch_block(p->key, grid, block, (size_t)p->lds, s, a, false); break;
     case qlk::FMT_MX: e = qlk::decode_dispatch_mx(p->key, grid, block, (size_t)p->lds, s, a, false); break;
+    case qlk::FMT_MX4: e = qlk::decode_dispatch_mx4(p->key, grid, block, (size_t)p->lds, s, a, false); break;
     default: e = qlk::decode_dispatch_fp8(p->key, grid, block, (size_t)p->lds, s, a, false); break;
   }
   return e == hipSuccess ? QL_OK : hip_fail(e, "decode GEMM launch");
@@ -464,7 +468,7 @@ static ql_status quantize_act(int32_t fmt, const void* x_bf16, int64_t M, int64_
   if (!aligned16(x_bf16) || !aligned16(a_q) || !aligned16(a_scale)) return fail(QL_E_ALIGN, "pointers must be 16-byte aligned");
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e;
-  if (fmt == QL_MXFP8)
+  if (is_mx(fmt))   // MXFP4 plans take MXFP8 activations
     e = qlk::launch_quant_mx(x_bf16, M, K, a_q, static_cast<uint8_t*>(a_scale), packed, s);
   else if (fmt == QL_BLOCK_FP8)
     e = qlk::launch_quant_groups(x_bf16, M, K, a_q, static_cast<float*>(a_scale), packed, s);
@@ -499,11 +503,28 @@ ql_status qlinear_quantize_weight(int32_t fmt, const void* w_bf16, int64_t N, in
   hipError_t e;
   if (fmt == QL_MXFP8)
     e = qlk::launch_quant_mx(w_bf16, N, K, w_q, static_cast<uint8_t*>(w_scale), false, s);
+  else if (fmt == QL_MXFP4)
+    e = qlk::launch_quant_mx4(w_bf16, N, K, w_q, static_cast<uint8_t*>(w_scale), s);
   else if (fmt == QL_BLOCK_FP8)
     e = qlk::launch_quant_wblocks(w_bf16, N, K, w_q, static_cast<float*>(w_scale), s);
   else
     e = qlk::launch_quant_rows(kernel_fmt(fmt), w_bf16, N, K, w_q, static_cast<float*>(w_scale), false, s);
   return e == hipSuccess ? QL_OK : hip_fail(e, "weight quantizer launch");
+}
+
+int64_t qlinear_packed_weight_bytes_fp4(int64_t N, int64_t K) {
+  if (N < 0 || K < 0) return 0;
+  return ((N + 15) / 16) * (K / 128) * 1024;
+}
+
+ql_status qlinear_pack_weight_fp4(const void* w_q, int64_t N, int64_t K, void* w_packed, void* stream) {
+  ql_status st = check_sizes(QL_MXFP4, N, K, "N");
+  if (st != QL_OK) return st;
+  if (N == 0 || K == 0) return QL_OK;
+  if (!w_q || !w_packed) return fail(QL_E_INVALID, "NULL pointer");
+  if (!aligned16(w_q) || !aligned16(w_packed)) return fail(QL_E_ALIGN, "pointers must be 16-byte aligned");
+  hipError_t e = qlk::launch_pack_weight_fp4(w_q, N, K, w_packed, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? QL_OK : hip_fail(e, "MXFP4 weight packing launch");
 }
 
 int64_t qlinear_packed_mx_scale_bytes(int64_t R, int64_t K) {

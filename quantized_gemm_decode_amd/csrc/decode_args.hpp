@@ -9,7 +9,8 @@ namespace qlk {
 
 // Format selector of the kernels (matches ql_format's order).  FMT_MX:
 // MXFP8, E4M3 codes with one E8M0 scale byte per 32 values along K.
-enum { FMT_FP8 = 0, FMT_INT8 = 1, FMT_BLOCK = 2, FMT_MX = 3 };
+// FMT_MX4: MXFP4 weights (E2M1, two a byte) with MXFP8 activations.
+enum { FMT_FP8 = 0, FMT_INT8 = 1, FMT_BLOCK = 2, FMT_MX = 3, FMT_MX4 = 4 };
 
 // How the decode kernel reads the weights.
 enum {
@@ -77,6 +78,8 @@ hipError_t decode_dispatch_block(const DecodeKey& k, dim3 grid, dim3 block, size
                                  hipStream_t s, const DecodeArgs& a, bool probe_only);
 hipError_t decode_dispatch_mx(const DecodeKey& k, dim3 grid, dim3 block, size_t lds,
                               hipStream_t s, const DecodeArgs& a, bool probe_only);
+hipError_t decode_dispatch_mx4(const DecodeKey& k, dim3 grid, dim3 block, size_t lds,
+                               hipStream_t s, const DecodeArgs& a, bool probe_only);
 
 // Tiled kernel launchers (tiled_*.hip); `probe_only` also raises the
 // kernel's dynamic LDS limit to `lds`.
@@ -104,6 +107,13 @@ hipError_t launch_quant_mx(const void* x, int64_t R, int64_t C, void* q, uint8_t
 // MXFP8 scales [R, K/32] -> lane order: 64 bytes per (16-row group t, K
 // block kb) at (t*G + kb)*64, byte l = s[16t + l%16][4kb + l/16], 0 past R.
 hipError_t launch_pack_mx_scales(const void* s, int64_t R, int64_t K, void* packed, hipStream_t st);
+// MXFP4 weights: w bf16 [N, K] -> E2M1 codes two a byte (low nibble = even K),
+// row-major [N, K/2], and E8M0 scale bytes [N, K/32].
+hipError_t launch_quant_mx4(const void* w, int64_t N, int64_t K, void* q, uint8_t* s, hipStream_t st);
+// Row-major E2M1 bytes [N, K/2] -> 1 KB tiles per (16-row group t, 128-wide
+// K block kb) at (t*G + kb)*1024; lane l's 16 bytes at l*16 are row
+// 16t + l%16, K [128kb + 32(l/16), +32), zero past N.
+hipError_t launch_pack_weight_fp4(const void* w_q, int64_t N, int64_t K, void* w_packed, hipStream_t st);
 // codes[i] = E4M3 code of x[i] clamped to [-448, 448], round to nearest even.
 hipError_t launch_encode_e4m3(const float* x, int64_t n, void* q, hipStream_t st);
 // Row-major W_q[N,K] -> packed 2 KB tiles (zero padding to 16 rows / 128 K).

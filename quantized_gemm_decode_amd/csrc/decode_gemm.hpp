@@ -78,6 +78,9 @@ __global__ void __launch_bounds__(NW * 64) qgemm_decode_kernel(DecodeArgs p) {
   static_assert(!FUSED || (MT == 1 && WP), "fused quantization: one token tile, packed weights");
   static_assert(!GLU || (RG == 2 && WP), "SiLU-and-mul: a gate and an up row group per wave, packed weights");
   static_assert(FMT != FMT_MX || (!FUSED && !GLU), "MXFP8: quantized activations in, plain bf16 out");
+  static_assert(FMT != FMT_MX4 || (!FUSED && !GLU && WP), "MXFP4: packed weights, quantized activations");
+  constexpr bool MXS = FMT == FMT_MX || FMT == FMT_MX4;   // E8M0 block scales in the matrix instruction
+  constexpr uint32_t WTILE = FMT == FMT_MX4 ? 1024u : 2048u;   // packed weight tile bytes
   using Acc = typename AccOf<FMT>::T;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   __shared__ int s_last;
@@ -108,7 +111,7 @@ __global__ void __launch_bounds__(NW * 64) qgemm_decode_kernel(DecodeArgs p) {
     return GLU ? (uint32_t)obase + x < IH : (uint32_t)grow(rg) + x < N;
   };
   const uint32_t NT16 = (N + 15u) / 16u;  // 16-row groups (tiles along N of the packed layout)
-  const __amdgpu_buffer_rsrc_t rw = make_rsrc(p.w, WP ? NT16 * (uint32_t)p.G * 2048u : N * K);
+  const __amdgpu_buffer_rsrc_t rw = make_rsrc(p.w, WP ? NT16 * (uint32_t)p.G * WTILE : N * K);
   const uint32_t MT16 = (M + 15u) / 16u;
   const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.a, (AL >= 2) ? MT16 * (uint32_t)p.G * 2048u : M * K);
 
@@ -138,11 +141,12 @@ __global__ void __launch_bounds__(NW * 64) qgemm_decode_kernel(DecodeArgs p) {
   // WP (packed tiles): tile (t, kb) is 2 KB at (t*G + kb)*2048 holding exactly
   // the two 16-byte pieces every lane feeds the matrix core, lane l's `lo` at
   // l*16 and `hi` at 1024 + l*16; padding rows / K are zeros in the tile.
+  // MXFP4: 1 KB tiles, one 16-byte piece a lane (32 E2M1 values).
   uint32_t wbase_p[RG];
 #pragma unroll
   for (int rg = 0; rg < RG; ++rg) {
     const uint32_t t = (uint32_t)(grow(rg) / 16);
-    wbase_p[rg] = (t < NT16 && rowok(rg, 0)) ? t * (uint32_t)p.G * 2048u + (uint32_t)lane * 16u : OOB;
+    wbase_p[rg] = (t < NT16 && rowok(rg, 0)) ? t * (uint32_t)p.G * WTILE + (uint32_t)lane * 16u : OOB;
   }
   // LDS slots of the transpose: 2 per wave, each RG x 2 KB, after the
   // staged activations.
@@ -193,10 +197,10 @@ __global__ void __launch_bounds__(NW * 64) qgemm_decode_kernel(DecodeArgs p) {
 
   // MXFP8 scales are bytes in lane order: 64 per (16-row group, K block)
   const __amdgpu_buffer_rsrc_t rsa = make_rsrc(
-      p.sa, FMT == FMT_MX ? MT16 * (uint32_t)p.G * 64u : (FMT == FMT_BLOCK ? M * (uint32_t)p.G : M) * 4u);
+      p.sa, MXS ? MT16 * (uint32_t)p.G * 64u : (FMT == FMT_BLOCK ? M * (uint32_t)p.G : M) * 4u);
   const __amdgpu_buffer_rsrc_t rsw = make_rsrc(
-      p.sw, FMT == FMT_MX ? NT16 * (uint32_t)p.G * 64u
-                          : (FMT == FMT_BLOCK ? ((N + 127u) / 128u) * (uint32_t)p.G : N) * 4u);
+      p.sw, MXS ? NT16 * (uint32_t)p.G * 64u
+                : (FMT == FMT_BLOCK ? ((N + 127u) / 128u) * (uint32_t)p.G : N) * 4u);
   // MXFP8: the scale byte lane l hands the matrix core with K block kb (that
   // of row l%16 of the operand's 16-row group and 32-wide block 4*kb + l/16)
   // is byte l of the group's 64 for that block, so a wave reads 64
@@ -227,11 +231,14 @@ __global__ void __launch_bounds__(NW * 64) qgemm_decode_kernel(DecodeArgs p) {
       const bool lo_ok = glo < rem;
       const bool hi_ok = glo + 64u < rem;
       if constexpr (WP) {
-        const uint32_t tofs = (uint32_t)kb * 2048u;
+        const uint32_t tofs = (uint32_t)kb * WTILE;
 #pragma unroll
         for (int rg = 0; rg < RG; ++rg) {
           wb[q][rg].lo = bload16_nt(rw, ok ? wbase_p[rg] + tofs : OOB);
-          wb[q][rg].hi = bload16_nt(rw, ok ? wbase_p[rg] + tofs + 1024u : OOB);
+          if constexpr (FMT == FMT_MX4)
+            wb[q][rg].hi = u32x4{0u, 0u, 0u, 0u};
+          else
+            wb[q][rg].hi = bload16_nt(rw, ok ? wbase_p[rg] + tofs + 1024u : OOB);
         }
       } else if constexpr (WL) {
         const bool c_ok = c16 < rem;
@@ -280,7 +287,7 @@ __global__ void __launch_bounds__(NW * 64) qgemm_decode_kernel(DecodeArgs p) {
           swb[q][rg] = bload_f32(rsw, (ok && row0 < N) ? ((row0 >> 7) * Gu + (uint32_t)kb) * 4u : OOB);
         }
       }
-      if constexpr (FMT == FMT_MX) {
+      if constexpr (MXS) {
         // scale bytes ride in the float slots as raw bits (no arithmetic touches them)
         const uint32_t sofs = (uint32_t)kb * 64u;
 #pragma unroll
@@ -366,6 +373,10 @@ __global__ void __launch_bounds__(NW * 64) qgemm_decode_kernel(DecodeArgs p) {
             const int xw = __float_as_int(swb[q][rg]);
             acc[rg][mt] = SWAP ? mma_f8_mx(wf[rg], af[mt], acc[rg][mt], xw, xa)
                                : mma_f8_mx(af[mt], wf[rg], acc[rg][mt], xa, xw);
+          } else if constexpr (FMT == FMT_MX4) {
+            const int xa = __float_as_int(sab[q][mt][0]);
+            const int xw = __float_as_int(swb[q][rg]);
+            acc[rg][mt] = mma_f8f4_mx<SWAP>(af[mt], wf[rg].lo, acc[rg][mt], xa, xw);
           } else {
             const f32x4 z = {0.f, 0.f, 0.f, 0.f};
             const f32x4 part = SWAP ? mma_f8(wf[rg], af[mt], z) : mma_f8(af[mt], wf[rg], z);
@@ -538,7 +549,7 @@ __global__ void __launch_bounds__(NW * 64) qgemm_decode_kernel(DecodeArgs p) {
   // Scales of the per-token formats, loaded now so that their latency hides
   // under the weight stream instead of stalling the epilogue.
   float esa[MT][4], esw[RG][4];
-  if constexpr (FMT != FMT_BLOCK && FMT != FMT_MX) {
+  if constexpr (FMT != FMT_BLOCK && !MXS) {
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
@@ -562,7 +573,10 @@ __global__ void __launch_bounds__(NW * 64) qgemm_decode_kernel(DecodeArgs p) {
   // before the weight batches, and vmcnt counts in issue order) while the
   // weight batches stay in flight, then make LDS visible workgroup-wide.
   if constexpr (ALDS && !FUSED) {
-    constexpr int NW_LOADS = 2 * PF * 2 * RG;  // weight loads of the two batches: all issued after the copies
+    // loads of the two batches, all issued after the copies: 2*RG weight loads
+    // per K block (a lower bound where scale loads follow; MXFP4 weights take
+    // one load per row group, then RG + MT scale loads, 2*RG + MT in all)
+    constexpr int NW_LOADS = 2 * PF * (FMT == FMT_MX4 ? 2 * RG + MT : 2 * RG);
     static_assert(NW_LOADS <= 63, "vmcnt holds 6 bits");
     __builtin_amdgcn_s_waitcnt((NW_LOADS & 15) | (7 << 4) | (15 << 8) | ((NW_LOADS >> 4) << 14));
     lds_barrier();
@@ -685,7 +699,7 @@ __global__ void __launch_bounds__(NW * 64) qgemm_decode_kernel(DecodeArgs p) {
         float t[2];
 #pragma unroll
         for (int rg = 0; rg < 2; ++rg) {
-          if constexpr (FMT == FMT_BLOCK || FMT == FMT_MX) {
+          if constexpr (FMT == FMT_BLOCK || MXS) {
             t[rg] = acc[rg][mt][r];
           } else {
             float accf;
@@ -716,7 +730,7 @@ __global__ void __launch_bounds__(NW * 64) qgemm_decode_kernel(DecodeArgs p) {
         nn[r] = (uint32_t)grow(rg) + (SWAP ? (uint32_t)(4 * g + r) : (uint32_t)r16);
         mm[r] = SWAP ? (uint32_t)(mt * 16 + r16) : (uint32_t)(mt * 16 + 4 * g + r);
         const bool ok = mm[r] < M && nn[r] < N;
-        if constexpr (FMT == FMT_BLOCK || FMT == FMT_MX) {
+        if constexpr (FMT == FMT_BLOCK || MXS) {
           out[r] = bf16_rne(acc[rg][mt][r]);
           if (ok && p.acc_out)
             reinterpret_cast<float*>(p.acc_out)[(size_t)mm[r] * N + nn[r]] = acc[rg][mt][r];
@@ -766,7 +780,8 @@ constexpr bool decode_config_fits() {
   }
   // two batches of PF blocks of (RG weight + MT activation) fragments, 8 VGPRs each
   const int buffers = 2 * PF_ * (RG_ + MT_) * 8;
-  const int scales = FMT == FMT_BLOCK ? 2 * PF_ * (4 * MT_ + RG_) : FMT == FMT_MX ? 2 * PF_ * (MT_ + RG_) : 0;
+  const int scales =
+      FMT == FMT_BLOCK ? 2 * PF_ * (4 * MT_ + RG_) : (FMT == FMT_MX || FMT == FMT_MX4) ? 2 * PF_ * (MT_ + RG_) : 0;
   const int accs = RG_ * MT_ * 4;
   const int budget = NW_ >= 16 ? 128 : 256;
   // Block_FP8 keeps per-block partial products and scale factors live as well
@@ -790,12 +805,27 @@ constexpr bool mx_spills() {
   return false;
 }
 
+// The MXFP4 shapes that spill (same check): its weight fragments are half as
+// large, so only some shapes holding activations in registers remain.
+template <int NW_, int MT_, int RG_, int PF_, int AL>
+constexpr bool mx4_spills() {
+  if (AL != 2) return false;
+  if (NW_ == 8)
+    return (MT_ == 1 && RG_ == 4 && PF_ == 2) || (MT_ == 2 && RG_ == 2 && PF_ == 2) ||
+           (MT_ == 4 && (PF_ == 2 || RG_ == 2));
+  if (NW_ == 16) return MT_ == 2 && RG_ == 2;
+  return false;
+}
+
 // Fused quantization adds 32/NW 16-byte X pieces a lane to the buffers in
 // flight; it serves one token tile and packed weights.
 template <int FMT, int NW_, int SW, int MT_, int RG_, int PF_, int AL, int WM_>
 constexpr bool decode_variant_ok() {
   if constexpr (FMT == FMT_MX) {
     if (mx_spills<NW_, MT_, RG_, PF_, AL>()) return false;
+  }
+  if constexpr (FMT == FMT_MX4) {
+    if (mx4_spills<NW_, MT_, RG_, PF_, AL>()) return false;
   }
   if constexpr (AL == 4) {
     if (MT_ != 1 || WM_ != W_PACKED) return false;
@@ -808,8 +838,9 @@ constexpr bool decode_variant_ok() {
 template <int FMT, int NW_, int SW, int MT_, int RG_, int PF_, int AL, int WM_, int GLU = 0>
 hipError_t decode_try(const DecodeKey& k, dim3 grid, dim3 block, size_t lds, hipStream_t s, const DecodeArgs& a,
                       bool probe_only, bool* hit) {
-  // MXFP8 is served with packed weights and packed activations only
-  constexpr bool mx_ok = FMT != FMT_MX || (GLU == 0 && WM_ == W_PACKED && (AL == 2 || AL == 3));
+  // MXFP8 / MXFP4 are served with packed weights and packed activations only
+  constexpr bool mx_ok =
+      (FMT != FMT_MX && FMT != FMT_MX4) || (GLU == 0 && WM_ == W_PACKED && (AL == 2 || AL == 3));
   if constexpr (mx_ok && decode_variant_ok<FMT, NW_, SW, MT_, RG_, PF_, AL, WM_>()) {
     if (k.swap == SW && k.mt == MT_ && k.rg == RG_ && k.nw == NW_ && k.pf == PF_ && k.alds == AL && k.wm == WM_ &&
         k.glu == GLU) {

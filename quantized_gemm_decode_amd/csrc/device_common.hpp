@@ -83,6 +83,23 @@ __device__ __forceinline__ f32x4 mma_f8_mx(const Frag& a, const Frag& b, f32x4 c
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, c, 0, 0, 0, sa, 0, sb);
 }
 
+// E4M3 activations x E2M1 weights (MXFP4) -> fp32 with E8M0 block scales.
+// The E2M1 operand is 16 bytes a lane: K [32*(l/16), +32) of row l%16 of the
+// 128-wide step, two values a byte, low nibble first -- the same K as the
+// E4M3 operand's `lo` / `hi` pieces in their order, and scaled by the same
+// lane's scale byte (checked on gfx950 with one-hot operands).  W_FIRST: the
+// weights are the first operand (Swap-AB).
+template <bool W_FIRST>
+__device__ __forceinline__ f32x4 mma_f8f4_mx(const Frag& a, u32x4 w, f32x4 c, int sa, int sw) {
+  i32x8 av = {(int)a.lo.x, (int)a.lo.y, (int)a.lo.z, (int)a.lo.w,
+              (int)a.hi.x, (int)a.hi.y, (int)a.hi.z, (int)a.hi.w};
+  i32x8 wv = {(int)w.x, (int)w.y, (int)w.z, (int)w.w, 0, 0, 0, 0};
+  if constexpr (W_FIRST)
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wv, av, c, 4, 0, 0, sw, 0, sa);
+  else
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, wv, c, 0, 4, 0, sa, 0, sw);
+}
+
 // binary32 -> bfloat16, round to nearest even; NaN stays a quiet NaN.
 __device__ __forceinline__ uint32_t bf16_rne(float f) {
   uint32_t u = __float_as_uint(f);

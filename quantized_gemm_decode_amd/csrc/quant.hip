@@ -264,12 +264,14 @@ hipError_t launch_quant_wblocks(const void* w, int64_t N, int64_t K, void* q, fl
 // of two; a product below the binary32 normals is far below E4M3's smallest
 // subnormal, so its rounding cannot change the code) clamped to +-448 and
 // rounded to E4M3.
+// EMAX: exponent of the element format's largest normal (E4M3 8, E2M1 2).
+template <int EMAX>
 __device__ __forceinline__ int mx_exponent(float amax) {
   const uint32_t u = __float_as_uint(amax);   // amax >= 0, finite
   if (u == 0u) return -127;
   const int fl2 = u >= 0x00800000u ? (int)(u >> 23) - 127   // normal
                                    : (31 - (int)__clz(u)) - 149;  // subnormal: u * 2^-149
-  return max(-127, fl2 - 8);
+  return max(-127, fl2 - EMAX);
 }
 
 // Four lanes (a DPP quad) per block, 8 values (one 16-byte load) a lane.
@@ -288,7 +290,7 @@ __global__ void __launch_bounds__(256) quant_mx_kernel(const uint16_t* __restric
   float m = abs_bf16_max8(v, 0.0f);
   m = fmaxf(m, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(m), 0xB1, 0xF, 0xF, false)));
   m = fmaxf(m, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(m), 0x4E, 0xF, 0xF, false)));
-  const int e = mx_exponent(m);
+  const int e = mx_exponent<8>(m);
   const float f = __uint_as_float((uint32_t)(127 - e) << 23);   // 2^-e, a normal binary32
   uint32_t c0 = 0u, c1 = 0u;
   const uint32_t w[4] = {v.x, v.y, v.z, v.w};
@@ -312,6 +314,77 @@ __global__ void __launch_bounds__(256) quant_mx_kernel(const uint16_t* __restric
     else if (!PACKED && ok)
       s[(size_t)row * (C / 32u) + k / 32u] = (uint8_t)(e + 127);
   }
+}
+
+// MXFP4 weights: as quant_mx_kernel with E2M1 elements -- e = floor(log2(amax))
+// - 2 (6 = 1.5 * 2^2), elements w * 2^-e clamped to +-6 and rounded to the
+// nearest of 0, 0.5, 1, 1.5, 2, 3, 4, 6, ties to the even code (mantissa bit
+// 0): the code counts the rounding boundaries below |t|, a boundary that |t|
+// meets exactly counting only when the code above it is even.  Codes two a
+// byte, low nibble first, row-major [R, C/2].
+__device__ __forceinline__ uint32_t e2m1_code(float t) {
+  const float a = fabsf(t);
+  const uint32_t c = (uint32_t)(a > 0.25f) + (uint32_t)(a >= 0.75f) + (uint32_t)(a > 1.25f) +
+                     (uint32_t)(a >= 1.75f) + (uint32_t)(a > 2.5f) + (uint32_t)(a >= 3.5f) + (uint32_t)(a > 5.0f);
+  return c | ((__float_as_uint(t) >> 28) & 0x8u);
+}
+
+__global__ void __launch_bounds__(256) quant_mx4_kernel(const uint16_t* __restrict__ w, uint32_t R, uint32_t C,
+                                                        uint8_t* __restrict__ q, uint8_t* __restrict__ s) {
+  const uint32_t t = blockIdx.x * 256u + threadIdx.x;
+  const uint32_t kpr = C / 8u;
+  const uint32_t row = t / kpr;
+  const uint32_t k = (t - row * kpr) * 8u;
+  const bool ok = row < R;
+  const u32x4 v = ok ? *reinterpret_cast<const u32x4*>(w + (size_t)row * C + k) : u32x4{0, 0, 0, 0};
+  float m = abs_bf16_max8(v, 0.0f);
+  m = fmaxf(m, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(m), 0xB1, 0xF, 0xF, false)));
+  m = fmaxf(m, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(m), 0x4E, 0xF, 0xF, false)));
+  const int e = mx_exponent<2>(m);
+  const float f = __uint_as_float((uint32_t)(127 - e) << 23);   // 2^-e, a normal binary32 (e <= 125)
+  uint32_t codes = 0u;
+  const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float a = __builtin_amdgcn_fmed3f(__fmul_rn(__uint_as_float(wv[i] << 16), f), -6.0f, 6.0f);
+    const float b = __builtin_amdgcn_fmed3f(__fmul_rn(__uint_as_float(wv[i] & 0xffff0000u), f), -6.0f, 6.0f);
+    codes |= (e2m1_code(a) | (e2m1_code(b) << 4)) << (8 * i);
+  }
+  if (ok) {
+    *reinterpret_cast<uint32_t*>(q + (size_t)row * (C / 2u) + k / 2u) = codes;
+    if ((k & 31u) == 0u) s[(size_t)row * (C / 32u) + k / 32u] = (uint8_t)(e + 127);
+  }
+}
+
+hipError_t launch_quant_mx4(const void* w, int64_t N, int64_t K, void* q, uint8_t* s, hipStream_t st) {
+  const int64_t threads = N * (K / 8);
+  quant_mx4_kernel<<<dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, st>>>(
+      static_cast<const uint16_t*>(w), (uint32_t)N, (uint32_t)K, static_cast<uint8_t*>(q), s);
+  return hipGetLastError();
+}
+
+// One thread per 16-byte piece of the packed MXFP4 weight layout.
+__global__ void __launch_bounds__(256) pack_weight_fp4_kernel(const uint8_t* __restrict__ w, uint32_t N,
+                                                              uint32_t K, uint32_t G, uint32_t total,
+                                                              uint8_t* __restrict__ out) {
+  const uint32_t i = blockIdx.x * 256u + threadIdx.x;   // piece index
+  if (i >= total) return;
+  const uint32_t l = i & 63u;
+  const uint32_t kb = (i >> 6) % G;
+  const uint32_t t = (i >> 6) / G;
+  const uint32_t row = t * 16u + (l & 15u);
+  u32x4 v = {0u, 0u, 0u, 0u};
+  if (row < N) v = *reinterpret_cast<const u32x4*>(w + (size_t)row * (K / 2u) + kb * 64u + (l >> 4) * 16u);
+  *reinterpret_cast<u32x4*>(out + (size_t)i * 16u) = v;
+}
+
+hipError_t launch_pack_weight_fp4(const void* w_q, int64_t N, int64_t K, void* w_packed, hipStream_t st) {
+  const int64_t G = K / 128;
+  const int64_t total = (N + 15) / 16 * G * 64;
+  pack_weight_fp4_kernel<<<dim3((unsigned)((total + 255) / 256)), dim3(256), 0, st>>>(
+      static_cast<const uint8_t*>(w_q), (uint32_t)N, (uint32_t)K, (uint32_t)G, (uint32_t)total,
+      static_cast<uint8_t*>(w_packed));
+  return hipGetLastError();
 }
 
 // One thread per byte of the lane-order MXFP8 scale layout.

@@ -152,9 +152,9 @@ class Timer:
         self.fmt, self.N, self.K, self.layout = fmt, N, K, layout
         w_q, w_s = ql.quantize_weight(fmt, w.cuda())
         if layout >= 1:
-            w_q = ql.pack_weight(w_q)
-            if fmt == ql.MXFP8:
-                w_s = ql.pack_mx_scales(w_s)      # MXFP8 plans read the scales in lane order
+            w_q = ql.pack_weight_fp4(w_q) if fmt == ql.MXFP4 else ql.pack_weight(w_q)
+            if fmt in ql.MX_FORMATS:
+                w_s = ql.pack_mx_scales(w_s)      # MX plans read the scales in lane order
         self.copies = min(max_copies, max(2, -(-(1 << 30) // (N * K))))
         self.wq = torch.empty((self.copies,) + tuple(w_q.shape), dtype=w_q.dtype, device="cuda")
         self.ws = torch.empty((self.copies,) + tuple(w_s.shape), dtype=w_s.dtype, device="cuda")
@@ -326,8 +326,8 @@ def main(argv=None):
                     lms = [m for m in ms if layout != 3 or fused_ok(wl.fmt, m, K)]
                     if layout == 4 and (lab != "gate_up" or N % 32):
                         continue        # SiLU-and-mul plans: the merged gate/up projection only
-                    if wl.fmt == ql.MXFP8 and layout != 2:
-                        continue        # MXFP8 plans take packed weights and packed activations only
+                    if wl.fmt in ql.MX_FORMATS and layout != 2:
+                        continue        # MX plans take packed weights and packed activations only
                     if not lms:
                         continue
                     timer = Timer(wl.fmt, N, K, x, w, stream, layout=layout)

@@ -94,3 +94,26 @@ def pack_mx_scales_ref(s, K):
                 if row < R:
                     out[t, kb, l] = s[row, 4 * kb + l // 16]
     return out.reshape(-1)
+
+
+def fp4_bytes(codes):
+    """E2M1 codes [N, K] (one a byte) -> row-major pairs [N, K/2], low nibble = even K."""
+    c = np.asarray(codes, dtype=np.uint8) & 0xF
+    return (c[:, 0::2] | (c[:, 1::2] << 4)).astype(np.uint8)
+
+
+def pack_fp4_ref(codes):
+    """The packed MXFP4 weight layout, restated from its definition: 1 KB per
+    (16-row group t, K block kb) at (t*G + kb)*1024; lane l's 16 bytes hold row
+    16t + l%16, K [128kb + 32(l//16), +32) as pairs; zero past the last row."""
+    b = fp4_bytes(codes)
+    N, K = b.shape[0], b.shape[1] * 2
+    T, G = -(-N // 16), K // 128
+    out = np.zeros((T, G, 64, 16), np.uint8)
+    for t in range(T):
+        for kb in range(G):
+            for l in range(64):
+                row = 16 * t + l % 16
+                if row < N:
+                    out[t, kb, l] = b[row, 64 * kb + 16 * (l // 16):64 * kb + 16 * (l // 16) + 16]
+    return out.reshape(-1)

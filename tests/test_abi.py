@@ -333,3 +333,17 @@ def test_mx_scale_layout_sizes():
     assert ql.lib().qlinear_pack_mx_scales(null, 4, 4160, null, null) == QL_E_INVALID   # K % 128
     assert ql.lib().qlinear_pack_mx_scales(null, 4, 256, null, null) == QL_E_INVALID    # NULL
     assert ql.lib().qlinear_pack_mx_scales(null, 0, 256, null, null) == QL_OK          # empty
+
+
+def test_mxfp4_plans_and_sizes():
+    good = dict(w_layout=1, a_mode=2, waves_n=4, waves_k=1, prefetch=2)
+    assert _plan_status(ql.MXFP4, 8, 4096, 4096, **good) == QL_OK
+    assert _plan_status(ql.MXFP4, 8, 4096, 4160, **good) == QL_E_INVALID                # K % 128
+    assert _plan_status(ql.MXFP4, 8, 4096, 4096, **dict(good, w_layout=0, a_mode=0)) == QL_E_UNSUPPORTED
+    assert _plan_status(ql.MXFP4, 8, 4096, 4096, **dict(good, a_mode=4)) == QL_E_UNSUPPORTED
+    assert ql.qlinear_packed_weight_bytes_fp4(17, 256) == 2 * 2 * 1024
+    assert ql.weight_code_shape(ql.MXFP4, 10, 256) == (10, 128) and ql.weight_code_dtype(ql.MXFP4) == torch.uint8
+    assert ql.code_dtype(ql.MXFP4) == torch.float8_e4m3fn          # activations stay E4M3
+    null = ctypes.c_void_p(0)
+    assert ql.lib().qlinear_pack_weight_fp4(null, 4, 4160, null, null) == QL_E_INVALID
+    assert ql.lib().qlinear_quantize_weight(ql.MXFP4, null, 4, 4160, null, null, null) == QL_E_INVALID

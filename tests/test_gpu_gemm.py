@@ -413,7 +413,9 @@ def test_every_table_entry_matches_oracle(entry):
     plan = ql.qlinear_plan_with_config(fmt, M, N, K, cfg)
     y = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
     w_use = ql.pack_weight(w_q) if cfg["w_layout"] else w_q
-    if fmt == ql.MXFP8:
+    if fmt == ql.MXFP4:
+        w_use = ql.pack_weight_fp4(w_q)
+    if fmt in ql.MX_FORMATS:
         w_s = ql.pack_mx_scales(w_s)
     if entry[16]:
         a_f = ql.act_buffer(plan)
@@ -424,7 +426,7 @@ def test_every_table_entry_matches_oracle(entry):
     else:
         if cfg["a_mode"] >= 2:
             a_q, a_p_s = ql.quantize_act_packed(fmt, xm.cuda())
-            if fmt == ql.MXFP8:
+            if fmt in ql.MX_FORMATS:
                 a_s = a_p_s
         ql.qlinear_run(plan, a_q, a_s, w_use, w_s, y, plan.new_workspace())
         torch.cuda.synchronize()
@@ -437,10 +439,12 @@ def test_every_table_entry_matches_oracle(entry):
         cols = np.sort(rng.choice(N, 64, replace=False))
     rows = np.sort(rng.choice(M, 256, replace=False)) if M > 256 else np.arange(M)
     ysel = yb[np.ix_(rows, cols)]
-    if fmt == ql.MXFP8:
-        r = oracle.mx_reference(bf16_bits(xm[torch.from_numpy(rows)]), bf16_bits(w[torch.from_numpy(cols)]))
+    if fmt in ql.MX_FORMATS:
+        ref, bound = ((oracle.mx4_reference, oracle.mx4_tolerance_bound) if fmt == ql.MXFP4
+                      else (oracle.mx_reference, oracle.mx_tolerance_bound))
+        r = ref(bf16_bits(xm[torch.from_numpy(rows)]), bf16_bits(w[torch.from_numpy(cols)]))
         d = oracle.summation_depth(K, split=plan.facts["chunks"], waves_k=16)
-        B = oracle.mx_tolerance_bound(r["a_q"], r["s_a"], r["w_q"], r["s_w"], d, oracle.MATRIX_CORE_ETA)
+        B = bound(r["a_q"], r["s_a"], r["w_q"], r["s_w"], d, oracle.MATRIX_CORE_ETA)
         st = oracle.check_fp8_parity(ysel, r["y_ref"], r["y_true"], B)
         assert st["ok"] and st["frac_within_ulp"] >= 0.95, (cfg, st)
         return

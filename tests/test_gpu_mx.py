@@ -14,7 +14,7 @@ import torch
 import oracle
 import quantized_gemm_decode_amd as ql
 from oracle import mx
-from tests.gpu_util import dev_bf16, host_bf16_bits, pack_mx_scales_ref, pack_ref, requires_gpu
+from tests.gpu_util import dev_bf16, fp4_bytes, host_bf16_bits, pack_fp4_ref, pack_mx_scales_ref, pack_ref, requires_gpu
 from workloads import bf16_bits, make_inputs
 
 pytestmark = [pytest.mark.gpu, requires_gpu]
@@ -210,3 +210,112 @@ def test_mx_forward_equals_quantize_then_run_and_graph_replays():
         s.synchronize()
         assert np.array_equal(host_bf16_bits(y), y_run), i
         _ = torch.randn(1000, device="cuda").sum()      # unrelated eager work between replays
+
+
+# ---------------------------------------------------------------- MXFP4 weights
+
+def _weights4(r):
+    K = r["w_q"].shape[1]
+    return (torch.from_numpy(pack_fp4_ref(r["w_q"])).cuda(),
+            torch.from_numpy(pack_mx_scales_ref(r["s_w"], K)).cuda())
+
+
+def _mx4_check(r, y_bits, split, waves_k):
+    K = r["a_q"].shape[1]
+    d = oracle.summation_depth(K, split=split, waves_k=waves_k)
+    B = mx.mx4_tolerance_bound(r["a_q"], r["s_a"], r["w_q"], r["s_w"], d, oracle.MATRIX_CORE_ETA)
+    return oracle.check_fp8_parity(y_bits, r["y_ref"], r["y_true"], B)
+
+
+@pytest.mark.parametrize("N,K", [(300, 512), (4096, 4096), (1000, 12288)])
+def test_mx4_weight_quantizer_bit_exact(N, K):
+    _, w = make_inputs(K, N, 1, 0.02, seed=N + 1)
+    w_q, w_s = ql.quantize_weight(ql.MXFP4, w.cuda())
+    torch.cuda.synchronize()
+    assert tuple(w_q.shape) == (N, K // 2)
+    rows = np.unique(np.random.default_rng(N).integers(0, N, 64))
+    cq, cs = mx.mx4_quantize(bf16_bits(w)[rows])
+    assert np.array_equal(w_q.cpu().numpy()[rows], fp4_bytes(cq))
+    assert np.array_equal(w_s.cpu().numpy()[rows], cs)
+
+
+def test_mx4_weight_quantizer_rounding_ties_and_special_blocks():
+    """Blocks whose amax is 4 (scale 2^0), so w / 2^e hits every E2M1 rounding
+    tie exactly (0.25, 0.75, ..., 5) and their neighbours; an all-zero block,
+    negative zeros, bf16 subnormals, a huge outlier."""
+    K = 256
+    rows = np.zeros((4, K), np.float64)
+    ties = [0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0]
+    vals = []
+    for t in ties:
+        vals += [t, -t, t * (1 - 2 ** -7), t * (1 + 2 ** -7)]
+    rows[0, :32] = ([4.0] + vals + [0.0] * 32)[:32]
+    rows[0, 32:64] = ([-4.0] + vals[::-1] + [0.0] * 32)[:32]
+    rows[0, 64:96] = [5.0, 5.5, 6.0, 5.9] * 8           # amax 6: scale 2^0; 5.0 is the 4 / 6 tie (-> 4)
+    rows[1, 32:64] = -0.0
+    rows[2, :32] = np.linspace(1, 127, 32) * 2.0 ** -133
+    rows[3, :] = np.sin(np.arange(K)) * 1e-3
+    rows[3, 7] = 1e30
+    wb = torch.from_numpy(rows.astype(np.float32)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    wb[1, 32:64] = 0x8000
+    w_q, w_s = ql.quantize_weight(ql.MXFP4, dev_bf16(wb))
+    torch.cuda.synchronize()
+    cq, cs = mx.mx4_quantize(wb)
+    assert np.array_equal(w_q.cpu().numpy(), fp4_bytes(cq))
+    assert np.array_equal(w_s.cpu().numpy(), cs)
+
+
+@pytest.mark.parametrize("N,K", [(37, 384), (16, 128), (300, 1024)])
+def test_mx4_weight_packing_matches_the_layout_definition(N, K):
+    codes = np.random.default_rng(N).integers(0, 16, (N, K), dtype=np.uint8)
+    out = ql.pack_weight_fp4(torch.from_numpy(fp4_bytes(codes)).cuda())
+    torch.cuda.synchronize()
+    n = ql.qlinear_packed_weight_bytes_fp4(N, K)
+    assert n == -(-N // 16) * (K // 128) * 1024
+    assert np.array_equal(out.cpu().numpy()[:n], pack_fp4_ref(codes))
+
+
+@pytest.mark.parametrize("vi", range(len(MXV)))
+def test_every_mx4_instantiation_matches_oracle(vi):
+    swap, (wn, wk), rows, pf, amode = MXV[vi]
+    M = MS[(vi + 3) % len(MS)]
+    K = [1024, 1152, 2048][(vi + 1) % 3]
+    N = 300 + 16 * (vi % 7)
+    split = SPLITS[(vi // 2) % len(SPLITS)]
+    cfg = dict(swap_ab=swap, split_k=split, waves_n=wn, waves_k=wk, rows_per_wave=rows, prefetch=pf,
+               a_mode=amode, w_layout=1)
+    try:
+        plan = ql.qlinear_plan_with_config(ql.MXFP4, M, N, K, cfg)
+    except ql.QLinearError as e:
+        assert e.status == 2, e
+        pytest.skip("configuration not instantiated: %s" % e)
+    x, w = make_inputs(K, N, M, 0.02, seed=9000 + vi)
+    r = mx.mx4_reference(bf16_bits(x), bf16_bits(w))
+    w_p, w_s = _weights4(r)
+    a_p, a_s = _acts(r)
+    y, ws = _run(plan, a_p, a_s, w_p, w_s)
+    st = _mx4_check(r, y, plan.facts["chunks"], wk)
+    assert st["ok"] and st["frac_within_ulp"] >= 0.95, (cfg, st)
+    if ws is not None:
+        assert int(torch.count_nonzero(ws)) == 0, "split-K workspace not left all-zero"
+
+
+@pytest.mark.parametrize("lab,N,K", [("qkv", 6144, 4096), ("o", 4096, 4096), ("gate_up", 24576, 4096),
+                                     ("down", 4096, 12288)])
+@pytest.mark.parametrize("M", [1, 8, 32])
+def test_mx4_planner_plans_at_full_size(lab, N, K, M):
+    ql.load_default_table()
+    x, w = make_inputs(K, N, M, 0.02, seed=23 + M)
+    xb, wb = bf16_bits(x), bf16_bits(w)
+    plan = ql.qlinear_plan_layouts(ql.MXFP4, M, N, K, 1, 1)
+    w_q, w_s = ql.quantize_weight(ql.MXFP4, w.cuda())
+    a_p = ql.act_buffer(plan)
+    a_s = ql.act_scale_buffer(plan)
+    y = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
+    ql.qlinear_forward(plan, x.cuda(), a_p, a_s, ql.pack_weight_fp4(w_q), ql.pack_mx_scales(w_s), y,
+                       plan.new_workspace())
+    torch.cuda.synchronize()
+    cols = np.sort(np.random.default_rng(M + N + 1).choice(N, 64, replace=False))
+    r = mx.mx4_reference(xb, wb[cols])
+    st = _mx4_check(r, host_bf16_bits(y)[:, cols], plan.facts["chunks"], plan.config["waves_k"])
+    assert st["ok"] and st["frac_within_ulp"] >= 0.95, (plan.config, st)

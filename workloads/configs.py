@@ -9,8 +9,9 @@ intermediate 25600) models, plus a 14B-class set beyond the threshold.
 
 from dataclasses import dataclass
 
-FP8_DYNAMIC, W8A8_INT8, BLOCK_FP8, MXFP8 = 0, 1, 2, 3
-FMT_NAMES = {FP8_DYNAMIC: "FP8_Dynamic", W8A8_INT8: "W8A8_INT8", BLOCK_FP8: "Block_FP8", MXFP8: "MXFP8"}
+FP8_DYNAMIC, W8A8_INT8, BLOCK_FP8, MXFP8, MXFP4 = 0, 1, 2, 3, 4
+FMT_NAMES = {FP8_DYNAMIC: "FP8_Dynamic", W8A8_INT8: "W8A8_INT8", BLOCK_FP8: "Block_FP8", MXFP8: "MXFP8",
+             MXFP4: "MXFP4"}
 DECODE_M = (1, 2, 4, 8, 16, 24, 32)
 
 
@@ -40,6 +41,9 @@ CONFIGS = (
     Workload("mxfp8_8b", MXFP8,
              (("qkv", 6144, 4096), ("o", 4096, 4096), ("gate_up", 24576, 4096), ("down", 4096, 12288)),
              DECODE_M, notes="MX block-scaled E4M3 on the 8B shapes"),
+    Workload("mxfp4_8b", MXFP4,
+             (("qkv", 6144, 4096), ("o", 4096, 4096), ("gate_up", 24576, 4096), ("down", 4096, 12288)),
+             DECODE_M, notes="MXFP4 weights, MXFP8 activations, on the 8B shapes"),
     Workload("fp8_dynamic_14b_large_m", FP8_DYNAMIC,
              (("qkv", 7168, 5120), ("gate_up", 34816, 5120), ("down", 5120, 17408)),
              (64, 256, 1024, 4096)),
@@ -49,7 +53,7 @@ CONFIGS = (
 def decode_workloads(include_mx=False):
     """The workloads whose token counts stay within the decode range (M <= 32);
     the MXFP8 one only on request (its plans take packed operands only)."""
-    return [c for c in CONFIGS if max(c.ms) <= 32 and (include_mx or c.fmt != MXFP8)]
+    return [c for c in CONFIGS if max(c.ms) <= 32 and (include_mx or c.fmt not in (MXFP8, MXFP4))]
 
 
 def config_by_name(name):
