@@ -148,8 +148,9 @@ typedef struct {
                             1 = packed tiles (qlinear_pack_weight) */
   int32_t tile_m;        /* TILED: workgroup tile rows (tokens): 64, 128 or 256 */
   int32_t tile_n;        /* TILED: workgroup tile columns (weight rows): 128 or 256;
-                            tile_m * tile_n <= 32768 with 4 waves, or 256 x 256 with 8 waves
-                            (packed operands, LDS-DMA ring of 2 stages, per-token formats).  TILED reads swap_ab, split_k,
+                            tiles up to 128 x 128 run 4 waves, 128 x 256 and 256 x 128 run 8,
+                            and 256 x 256 runs 8 (packed operands, LDS-DMA ring of 2 stages,
+                            per-token formats).  TILED reads swap_ab, split_k,
                             a_mode (0 or 2), w_layout, prefetch and the tile; the other
                             fields are ignored */
 } ql_config;

@@ -13,9 +13,10 @@
 // they stay in the same library, with the same split_k / swap_ab switches.
 //
 // Structure (256 threads = 4 waves in a 2 x 2 grid, wave tile TM x TN; the
-// 256 x 256 tile runs 512 threads = 8 waves in a 2 x 4 grid, wave tile
-// 128 x 64, so the LDS bytes a wave reads per flop drop by a quarter and the
-// L2 bytes per flop by half against 128 x 128):
+// 128 x 256, 256 x 128 and 256 x 256 tiles run 512 threads = 8 waves in a
+// 2 x 4 grid -- twice the waves to hide the operand loads, and for 256 x 256
+// a 128 x 64 wave tile, so the LDS bytes a wave reads per flop drop by a
+// quarter and the L2 bytes per flop by half against 128 x 128):
 //   * K advances in 128-wide blocks.  Per block, every thread loads its
 //     16-byte pieces of the A tile (BM x 128) and the B tile (BN x 128) from
 //     global memory into registers, and writes them into one of two LDS
@@ -53,10 +54,12 @@ struct TiledAcc<FMT_INT8> {
   typedef i32x4 T;
 };
 
-// Waves along N of a tile's wave grid (along M there are always 2).
+// Waves along N of a tile's wave grid (along M there are always 2): 8-wave
+// workgroups from 128 x 256 up (measured on the 14B shapes at M = 1024 and
+// 4096: the long-K down projection ran 11-19 % faster than with 4 waves).
 template <int BM, int BN>
 constexpr int tiled_waves_n() {
-  return BM * BN >= 256 * 256 ? 4 : 2;
+  return BM * BN >= 128 * 256 ? 4 : 2;
 }
 
 template <int FMT, bool SWAP, int BM, int BN, int WM, int PF, bool AP, int NS>
@@ -494,8 +497,9 @@ __global__ void __launch_bounds__((64 * 2 * tiled_waves_n<BM, BN>())) qgemm_tile
 }
 
 // Tile shapes instantiated per format: a wave holds (BM/32) x (BN/32) 16x16
-// accumulator tiles (4 waves), at most 128 registers; the 8-wave 256 x 256
-// tile holds 8 x 4 and exists for the LDS-DMA ring of 2 stages only.
+// accumulator tiles (4 waves) or (BM/32) x (BN/64) (8 waves), at most 128
+// registers; the 256 x 256 tile holds 8 x 4 and exists for the LDS-DMA ring
+// of 2 stages only.
 // Block_FP8 in the standard orientation also keeps four token scales per
 // accumulator tile row live, so its largest tiles are left out as well.
 template <int FMT, int SW, int BM, int BN, int PF, int NS>
