@@ -148,9 +148,9 @@ typedef struct {
                             1 = packed tiles (qlinear_pack_weight) */
   int32_t tile_m;        /* TILED: workgroup tile rows (tokens): 64, 128 or 256 */
   int32_t tile_n;        /* TILED: workgroup tile columns (weight rows): 128 or 256;
-                            tiles up to 128 x 128 run 4 waves, 128 x 256 and 256 x 128 run 8,
-                            and 256 x 256 runs 8 (packed operands, LDS-DMA ring of 2 stages,
-                            per-token formats).  TILED reads swap_ab, split_k,
+                            every tile runs 8 waves (Block_FP8 below 128 x 256: 4); 256 x 256
+                            needs packed operands, the LDS-DMA ring of 2 stages and a
+                            per-token format.  TILED reads swap_ab, split_k,
                             a_mode (0 or 2), w_layout, prefetch and the tile; the other
                             fields are ignored */
 } ql_config;

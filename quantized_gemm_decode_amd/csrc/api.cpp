@@ -713,7 +713,8 @@ ql_status qlinear_plan_info(ql_plan p, ql_config* cfg, ql_plan_facts* facts) {
     facts->chunks = p->chunks;
     facts->chunk_k = p->chunk_kb * 128;
     facts->workgroups = p->n_tiles * p->chunks;
-    facts->threads = p->tiled ? (p->cfg.tile_m * p->cfg.tile_n >= 128 * 256 ? 512 : 256) : p->key.nw * 64;
+    facts->threads = p->tiled ? ((p->fmt != QL_BLOCK_FP8 || p->cfg.tile_m * p->cfg.tile_n >= 128 * 256) ? 512 : 256)
+                              : p->key.nw * 64;
     facts->lds_bytes = (int32_t)p->lds;
     facts->workspace_bytes = p->ws_bytes;
     facts->epilogue = p->glu ? 1 : 0;

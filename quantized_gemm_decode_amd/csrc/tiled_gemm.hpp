@@ -12,11 +12,10 @@
 // threshold ([Summary] "Hybrid dispatch addresses runtime overhead"); here
 // they stay in the same library, with the same split_k / swap_ab switches.
 //
-// Structure (256 threads = 4 waves in a 2 x 2 grid, wave tile TM x TN; the
-// 128 x 256, 256 x 128 and 256 x 256 tiles run 512 threads = 8 waves in a
-// 2 x 4 grid -- twice the waves to hide the operand loads, and for 256 x 256
-// a 128 x 64 wave tile, so the LDS bytes a wave reads per flop drop by a
-// quarter and the L2 bytes per flop by half against 128 x 128):
+// Structure (512 threads = 8 waves in a 2 x 4 grid, wave tile TM x TN =
+// BM/2 x BN/4 -- Block_FP8 below 128 x 256: 256 threads, 4 waves in a 2 x 2
+// grid; the 256 x 256 tile's 128 x 64 wave tile reads a quarter fewer LDS
+// bytes per flop, and half the L2 bytes per flop, of 128 x 128):
 //   * K advances in 128-wide blocks.  Per block, every thread loads its
 //     16-byte pieces of the A tile (BM x 128) and the B tile (BN x 128) from
 //     global memory into registers, and writes them into one of two LDS
@@ -55,16 +54,18 @@ struct TiledAcc<FMT_INT8> {
 };
 
 // Waves along N of a tile's wave grid (along M there are always 2): 8-wave
-// workgroups from 128 x 256 up (measured on the 14B shapes at M = 1024 and
-// 4096: the long-K down projection ran 11-19 % faster than with 4 waves).
-template <int BM, int BN>
+// workgroups, whose extra waves hide the operand loads (measured on the 14B
+// shapes: 10-13 % faster at M = 256 with 64 x 128 and 128 x 128 tiles, 11-19 %
+// on the long-K down projection at M >= 1024 with 128 x 256).  Block_FP8
+// keeps 4 waves below 128 x 256: its per-row scales would spill there.
+template <int FMT, int BM, int BN>
 constexpr int tiled_waves_n() {
-  return BM * BN >= 128 * 256 ? 4 : 2;
+  return (FMT != FMT_BLOCK || BM * BN >= 128 * 256) ? 4 : 2;
 }
 
 template <int FMT, bool SWAP, int BM, int BN, int WM, int PF, bool AP, int NS>
-__global__ void __launch_bounds__((64 * 2 * tiled_waves_n<BM, BN>())) qgemm_tiled_kernel(DecodeArgs p) {
-  constexpr int WGN = tiled_waves_n<BM, BN>();
+__global__ void __launch_bounds__((64 * 2 * tiled_waves_n<FMT, BM, BN>())) qgemm_tiled_kernel(DecodeArgs p) {
+  constexpr int WGN = tiled_waves_n<FMT, BM, BN>();
   constexpr int NW = 2 * WGN;              // waves per workgroup
   constexpr int NT = 64 * NW;              // threads
   constexpr int TM = BM / 2, TN = BN / WGN;  // wave tile
@@ -496,8 +497,8 @@ __global__ void __launch_bounds__((64 * 2 * tiled_waves_n<BM, BN>())) qgemm_tile
   }
 }
 
-// Tile shapes instantiated per format: a wave holds (BM/32) x (BN/32) 16x16
-// accumulator tiles (4 waves) or (BM/32) x (BN/64) (8 waves), at most 128
+// Tile shapes instantiated per format: a wave holds (BM/32) x (BN/64) 16x16
+// accumulator tiles (8 waves) or (BM/32) x (BN/32) (4 waves), at most 128
 // registers; the 256 x 256 tile holds 8 x 4 and exists for the LDS-DMA ring
 // of 2 stages only.
 // Block_FP8 in the standard orientation also keeps four token scales per
@@ -524,7 +525,7 @@ hipError_t tiled_try(const TiledKey& k, dim3 grid, size_t lds, hipStream_t s, co
         return hipFuncSetAttribute(reinterpret_cast<const void*>(fn), hipFuncAttributeMaxDynamicSharedMemorySize,
                                    (int)lds);
       }
-      fn<<<grid, dim3(64 * 2 * tiled_waves_n<BM, BN>()), lds, s>>>(a);
+      fn<<<grid, dim3(64 * 2 * tiled_waves_n<FMT, BM, BN>()), lds, s>>>(a);
       return hipGetLastError();
     }
   }
