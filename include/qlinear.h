@@ -351,9 +351,11 @@ void qlinear_plan_destroy(ql_plan plan);
  * group's partial inside the K loop and rounds the fp32 sum to bf16; MXFP8
  * hands the E8M0 bytes to the scaled matrix-core instruction, which applies
  * them to every 32-wide block of products, and rounds the fp32 sum to bf16.
- * MXFP8 and MXFP4 plans use the decode algorithm (M <= 64) with packed
- * weights (MXFP4: qlinear_pack_weight_fp4) and packed activations (a_mode 2
- * or 3), and read both scales in the lane order of qlinear_pack_mx_scales.
+ * MXFP8 and MXFP4 plans read packed weights (MXFP4: qlinear_pack_weight_fp4)
+ * and packed activations (a_mode 2 or 3; the tiled algorithm a_mode 2), and
+ * both scales in the lane order of qlinear_pack_mx_scales.  MXFP4 runs on
+ * the decode algorithm (M <= 64); MXFP8 also on the tiled one with the
+ * register ring (w_lds 0; no 256 x 256 tile).
  * MXFP4 plans take MXFP8 activations (qlinear_quantize_act_packed with
  * fmt = QL_MXFP4 writes them).
  * a_q is in the plan's activation layout: row-major [M, K], or packed when

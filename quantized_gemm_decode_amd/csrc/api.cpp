@@ -162,7 +162,7 @@ ql_config heuristic_tiled(int32_t layout, bool a_packed, int64_t M, int64_t N, i
 }
 
 ql_config heuristic_config(int32_t fmt, int32_t layout, bool a_packed, int64_t M, int64_t N, int64_t K) {
-  // MXFP8 has no tiled kernel: its decode kernel serves up to 64 tokens
+  // the MX formats' decode kernel serves up to 64 tokens (MXFP4 has no tiled kernel)
   if (M > 32 && !(is_mx(fmt) && M <= 64)) return heuristic_tiled(layout, a_packed, M, N, K);
   ql_config c{};
   c.w_layout = layout;
@@ -234,6 +234,7 @@ ql_status build_tiled_plan(int32_t fmt, int64_t M, int64_t N, int64_t K, const q
   hipError_t pe;
   switch (p->tkey.fmt) {
     case qlk::FMT_INT8: pe = qlk::tiled_dispatch_int8(p->tkey, dim3(1), (size_t)p->lds, nullptr, dummy, true); break;
+    case qlk::FMT_MX: pe = qlk::tiled_dispatch_mx(p->tkey, dim3(1), (size_t)p->lds, nullptr, dummy, true); break;
     case qlk::FMT_BLOCK: pe = qlk::tiled_dispatch_block(p->tkey, dim3(1), (size_t)p->lds, nullptr, dummy, true); break;
     default: pe = qlk::tiled_dispatch_fp8(p->tkey, dim3(1), (size_t)p->lds, nullptr, dummy, true); break;
   }
@@ -266,8 +267,10 @@ ql_status build_plan(int32_t fmt, int64_t M, int64_t N, int64_t K, const ql_conf
   }
   if (is_mx(fmt)) {
     if (glu) return fail(QL_E_UNSUPPORTED, "MXFP8 / MXFP4 plans have no SiLU-and-mul epilogue");
-    if (cfg.algo != QL_ALGO_DECODE || M > 64)
-      return fail(QL_E_UNSUPPORTED, "MXFP8 / MXFP4 run on the decode algorithm (M <= 64)");
+    if (fmt == QL_MXFP4 && (cfg.algo != QL_ALGO_DECODE || M > 64))
+      return fail(QL_E_UNSUPPORTED, "MXFP4 runs on the decode algorithm (M <= 64)");
+    if (cfg.algo == QL_ALGO_TILED && cfg.w_lds)
+      return fail(QL_E_UNSUPPORTED, "MXFP8 tiled plans run the register ring (w_lds 0)");
     if (cfg.w_layout != 1 || (cfg.a_mode != 2 && cfg.a_mode != 3))
       return fail(QL_E_UNSUPPORTED, "MXFP8 / MXFP4 plans need packed weights and packed activations (a_mode 2 or 3)");
   }
@@ -420,6 +423,7 @@ ql_status launch_gemm(const ql_plan_s* p, const void* a_q, const void* a_scale, 
     const dim3 tgrid((unsigned)(p->n_tiles * p->chunks));
     switch (p->tkey.fmt) {
       case qlk::FMT_INT8: e = qlk::tiled_dispatch_int8(p->tkey, tgrid, (size_t)p->lds, s, a, false); break;
+      case qlk::FMT_MX: e = qlk::tiled_dispatch_mx(p->tkey, tgrid, (size_t)p->lds, s, a, false); break;
       case qlk::FMT_BLOCK: e = qlk::tiled_dispatch_block(p->tkey, tgrid, (size_t)p->lds, s, a, false); break;
       default: e = qlk::tiled_dispatch_fp8(p->tkey, tgrid, (size_t)p->lds, s, a, false); break;
     }

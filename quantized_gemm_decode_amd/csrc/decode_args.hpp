@@ -89,6 +89,8 @@ hipError_t tiled_dispatch_int8(const TiledKey& k, dim3 grid, size_t lds, hipStre
                                bool probe_only);
 hipError_t tiled_dispatch_block(const TiledKey& k, dim3 grid, size_t lds, hipStream_t s, const DecodeArgs& a,
                                 bool probe_only);
+hipError_t tiled_dispatch_mx(const TiledKey& k, dim3 grid, size_t lds, hipStream_t s, const DecodeArgs& a,
+                             bool probe_only);
 
 // Quantizer launchers (quant.hip).
 // `packed`: codes in the packed activation layout (2 KB tiles of 16 rows x

@@ -114,8 +114,11 @@ __global__ void __launch_bounds__((64 * 2 * tiled_waves_n<FMT, BM, BN>())) qgemm
   const uint32_t MT16 = (M + 15u) / 16u;
   const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.a, AP ? MT16 * G * 2048u : M * K);
   const __amdgpu_buffer_rsrc_t rw = make_rsrc(p.w, WP ? NT16 * G * 2048u : N * K);
-  const __amdgpu_buffer_rsrc_t rsa = make_rsrc(p.sa, (FMT == FMT_BLOCK ? M * G : M) * 4u);
-  const __amdgpu_buffer_rsrc_t rsw = make_rsrc(p.sw, (FMT == FMT_BLOCK ? ((N + 127u) / 128u) * G : N) * 4u);
+  // MXFP8 scales: E8M0 bytes in lane order, 64 per (16-row group, K block)
+  const __amdgpu_buffer_rsrc_t rsa =
+      make_rsrc(p.sa, FMT == FMT_MX ? MT16 * G * 64u : (FMT == FMT_BLOCK ? M * G : M) * 4u);
+  const __amdgpu_buffer_rsrc_t rsw =
+      make_rsrc(p.sw, FMT == FMT_MX ? NT16 * G * 64u : (FMT == FMT_BLOCK ? ((N + 127u) / 128u) * G : N) * 4u);
 
   // ---- global -> registers for one K block (zeros outside the matrices)
   // a ring of PF register slots: K block b of the chunk lives in slot b % PF
@@ -176,9 +179,11 @@ __global__ void __launch_bounds__((64 * 2 * tiled_waves_n<FMT, BM, BN>())) qgemm
   };
 
   // ---- Block_FP8 scale factors of one K block for this lane's elements
-  // (non-swapped: 4 token rows per 16x16 tile; swapped: 1 token per tile)
-  constexpr int SA_N = FMT == FMT_BLOCK ? (SWAP ? IM : IM * 4) : 1;
-  constexpr int SW_N = FMT == FMT_BLOCK ? IN : 1;
+  // (non-swapped: 4 token rows per 16x16 tile; swapped: 1 token per tile);
+  // MXFP8: the E8M0 byte this lane hands the matrix core with each A and B
+  // fragment (kept as raw bits in the float slots)
+  constexpr int SA_N = FMT == FMT_BLOCK ? (SWAP ? IM : IM * 4) : FMT == FMT_MX ? IM : 1;
+  constexpr int SW_N = (FMT == FMT_BLOCK || FMT == FMT_MX) ? IN : 1;
   float sa_nx[PF][SA_N], sw_nx[PF][SW_N];
   auto load_scales = [&](int kb, int sl) {
     if constexpr (FMT == FMT_BLOCK) {
@@ -194,6 +199,19 @@ __global__ void __launch_bounds__((64 * 2 * tiled_waves_n<FMT, BM, BN>())) qgemm
       for (int j = 0; j < IN; ++j) {
         const uint32_t nb = n0 + (uint32_t)(wx * TN + 16 * j);
         sw_nx[sl][j] = bload_f32(rsw, (kb < kb1 && nb < N) ? ((nb >> 7) * G + (uint32_t)kb) * 4u : OOB);
+      }
+    } else if constexpr (FMT == FMT_MX) {
+#pragma unroll
+      for (int i = 0; i < IM; ++i) {
+        const uint32_t t = m0 / 16u + (uint32_t)(wy * IM + i);
+        sa_nx[sl][i] = __int_as_float(
+            bload_u8(rsa, (kb < kb1 && t < MT16) ? (t * G + (uint32_t)kb) * 64u + (uint32_t)lane : OOB));
+      }
+#pragma unroll
+      for (int j = 0; j < IN; ++j) {
+        const uint32_t t = n0 / 16u + (uint32_t)(wx * IN + j);
+        sw_nx[sl][j] = __int_as_float(
+            bload_u8(rsw, (kb < kb1 && t < NT16) ? (t * G + (uint32_t)kb) * 64u + (uint32_t)lane : OOB));
       }
     } else {
       (void)kb;
@@ -219,6 +237,9 @@ __global__ void __launch_bounds__((64 * 2 * tiled_waves_n<FMT, BM, BN>())) qgemm
       }
     } else if constexpr (FMT == FMT_FP8) {
       acc[i][j] = SWAP ? mma_f8(b, a, acc[i][j]) : mma_f8(a, b, acc[i][j]);
+    } else if constexpr (FMT == FMT_MX) {
+      const int xa = __float_as_int(sa_c[i]), xw = __float_as_int(sw_c[j]);
+      acc[i][j] = SWAP ? mma_f8_mx(b, a, acc[i][j], xw, xa) : mma_f8_mx(a, b, acc[i][j], xa, xw);
     } else {
       const f32x4 z = {0.f, 0.f, 0.f, 0.f};
       const f32x4 part = SWAP ? mma_f8(b, a, z) : mma_f8(a, b, z);
@@ -429,9 +450,10 @@ __global__ void __launch_bounds__((64 * 2 * tiled_waves_n<FMT, BM, BN>())) qgemm
   // s_w per output column this lane holds: IM x (1 or 4) and IN x (4 or 1)
   // values, loaded once (not per element, which would keep hundreds of
   // loads in flight next to the accumulators).
-  constexpr int EA = FMT == FMT_BLOCK ? 1 : (SWAP ? 1 : 4), EW = FMT == FMT_BLOCK ? 1 : (SWAP ? 4 : 1);
+  constexpr bool SCALED_IN_K = FMT == FMT_BLOCK || FMT == FMT_MX;   // no scale epilogue
+  constexpr int EA = SCALED_IN_K ? 1 : (SWAP ? 1 : 4), EW = SCALED_IN_K ? 1 : (SWAP ? 4 : 1);
   float ea[IM][EA], ew[IN][EW];
-  if constexpr (FMT != FMT_BLOCK) {
+  if constexpr (!SCALED_IN_K) {
 #pragma unroll
     for (int i = 0; i < IM; ++i)
 #pragma unroll
@@ -457,7 +479,7 @@ __global__ void __launch_bounds__((64 * 2 * tiled_waves_n<FMT, BM, BN>())) qgemm
       for (int r = 0; r < 4; ++r) {
         const uint32_t m = elem_m(i, r), n = elem_n(j, r);
         const bool ok = m < M && n < N;
-        if constexpr (FMT == FMT_BLOCK) {
+        if constexpr (SCALED_IN_K) {
           out[r] = bf16_rne(acc[i][j][r]);
           if (ok && p.acc_out) reinterpret_cast<float*>(p.acc_out)[(size_t)m * N + n] = acc[i][j][r];
         } else {
@@ -505,9 +527,13 @@ __global__ void __launch_bounds__((64 * 2 * tiled_waves_n<FMT, BM, BN>())) qgemm
 // accumulator tile row live, so its largest tiles are left out as well.
 template <int FMT, int SW, int BM, int BN, int PF, int NS>
 constexpr bool tiled_config_fits() {
-  if (BM * BN == 256 * 256) return NS == 2 && FMT != FMT_BLOCK;
-  if (NS > 0) return FMT != FMT_BLOCK && NS * (BM + BN) * 128 <= 160 * 1024 && BM * BN <= 128 * 256;
+  // the LDS-DMA ring has no per-block scale path: Block_FP8 and MXFP8 use the register ring
+  if (BM * BN == 256 * 256) return NS == 2 && FMT != FMT_BLOCK && FMT != FMT_MX;
+  if (NS > 0) return FMT != FMT_BLOCK && FMT != FMT_MX && NS * (BM + BN) * 128 <= 160 * 1024 && BM * BN <= 128 * 256;
   if (FMT == FMT_BLOCK && !SW && BM * BN > 128 * 128) return false;
+  // MXFP8's scale bytes ride in the ring too: a two-block ring on the largest
+  // register-ring tiles spills (checked against the compiler's resource report)
+  if (FMT == FMT_MX && BM * BN >= 128 * 256 && PF > 1) return false;
   if (PF * (BM + BN) > 768) return false;  // ring of PF K blocks: at most 96 VGPRs a lane
   if (FMT == FMT_BLOCK && BM * BN > 128 * 128 && PF > 1) return false;
   return BM * BN <= 128 * 256;

@@ -299,8 +299,10 @@ def test_mxfp8_plans_are_validated_on_host():
     assert _plan_status(ql.MXFP8, 8, 4096, 4096, **dict(good, w_layout=0, a_mode=0)) == QL_E_UNSUPPORTED
     assert _plan_status(ql.MXFP8, 8, 4096, 4096, **dict(good, a_mode=1)) == QL_E_UNSUPPORTED
     assert _plan_status(ql.MXFP8, 8, 4096, 4096, **dict(good, a_mode=4)) == QL_E_UNSUPPORTED   # no fused quantizer
-    assert _plan_status(ql.MXFP8, 128, 4096, 4096, **dict(good, algo=ql.ALGO_TILED, tile_m=128,
-                                                          tile_n=128)) == QL_E_UNSUPPORTED
+    tiled = dict(good, algo=ql.ALGO_TILED, tile_m=128, tile_n=128)
+    assert _plan_status(ql.MXFP8, 128, 4096, 4096, **tiled) == QL_OK                   # register ring
+    assert _plan_status(ql.MXFP8, 128, 4096, 4096, **dict(tiled, w_lds=1)) == QL_E_UNSUPPORTED   # LDS-DMA ring
+    assert _plan_status(ql.MXFP4, 128, 4096, 4096, **tiled) == QL_E_UNSUPPORTED        # MXFP4: decode only
     assert _plan_status(ql.MXFP8, 65, 4096, 4096, **good) == QL_E_UNSUPPORTED
     # shapes whose registers would spill are not instantiated
     assert _plan_status(ql.MXFP8, 32, 4096, 4096, **dict(good, waves_n=2, waves_k=4, prefetch=2,

@@ -319,3 +319,54 @@ def test_mx4_planner_plans_at_full_size(lab, N, K, M):
     r = mx.mx4_reference(xb, wb[cols])
     st = _mx4_check(r, host_bf16_bits(y)[:, cols], plan.facts["chunks"], plan.config["waves_k"])
     assert st["ok"] and st["frac_within_ulp"] >= 0.95, (plan.config, st)
+
+
+# ---------------------------------------------------------------- MXFP8 beyond the decode range
+
+TILED_MX = list(itertools.product([0, 1], [(64, 128), (64, 256), (128, 128), (128, 256), (256, 128)], [1, 2, 4],
+                                  [1, 2]))
+
+
+@pytest.mark.parametrize("vi", range(len(TILED_MX)))
+def test_every_mx_tiled_instantiation_matches_oracle(vi):
+    swap, (bm, bn), pf, split = TILED_MX[vi]
+    M = [40, 100, 200, 257][vi % 4]
+    K = [1024, 1152][vi % 2]
+    N = 300 + 16 * (vi % 5)
+    cfg = dict(algo=ql.ALGO_TILED, swap_ab=swap, split_k=split, tile_m=bm, tile_n=bn, prefetch=pf, w_lds=0,
+               a_mode=2, w_layout=1)
+    try:
+        plan = ql.qlinear_plan_with_config(ql.MXFP8, M, N, K, cfg)
+    except ql.QLinearError as e:
+        assert e.status == 2, e
+        pytest.skip("configuration not instantiated: %s" % e)
+    x, w = make_inputs(K, N, M, 0.02, seed=11000 + vi)
+    r = mx.mx_reference(bf16_bits(x), bf16_bits(w))
+    w_p, w_s = _weights(r)
+    a_p, a_s = _acts(r)
+    y, ws = _run(plan, a_p, a_s, w_p, w_s)
+    st = _mx_check(r, y, plan.facts["chunks"], 1)
+    assert st["ok"] and st["frac_within_ulp"] >= 0.95, (cfg, st)
+    if ws is not None:
+        assert int(torch.count_nonzero(ws)) == 0, "split-K workspace not left all-zero"
+
+
+@pytest.mark.parametrize("M", [128, 1024])
+def test_mx_planner_large_m_plans(M):
+    """Beyond 64 tokens the planner sends MXFP8 to the tiled kernel; the 14B
+    QKV shape, 64 sampled columns (and 128 sampled rows at M = 1024)."""
+    N, K = 7168, 5120
+    x, w = make_inputs(K, N, M, 0.02, seed=M)
+    plan = ql.qlinear_plan_layouts(ql.MXFP8, M, N, K, 1, 1)
+    assert plan.config["algo"] == ql.ALGO_TILED
+    w_q, w_s = ql.quantize_weight(ql.MXFP8, w.cuda())
+    y = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
+    ql.qlinear_forward(plan, x.cuda(), ql.act_buffer(plan), ql.act_scale_buffer(plan), ql.pack_weight(w_q),
+                       ql.pack_mx_scales(w_s), y, plan.new_workspace())
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(M)
+    cols = np.sort(rng.choice(N, 64, replace=False))
+    rows = np.sort(rng.choice(M, min(M, 128), replace=False))
+    r = mx.mx_reference(bf16_bits(x[torch.from_numpy(rows)]), bf16_bits(w[torch.from_numpy(cols)]))
+    st = _mx_check(r, host_bf16_bits(y)[np.ix_(rows, cols)], plan.facts["chunks"], 1)
+    assert st["ok"] and st["frac_within_ulp"] >= 0.95, (plan.config, st)
