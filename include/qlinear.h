@@ -99,7 +99,8 @@ typedef enum {
 /* Algorithm family of a plan. */
 typedef enum {
   QL_ALGO_DECODE = 0, /* weight-streaming kernel for M <= 64 (decode token counts; the planner's
-                          heuristic uses it up to 32, the sweep table may pick it up to 64) */
+                          heuristic uses it up to 32 -- 64 for the MX formats -- and the sweep
+                          table may pick it up to 64) */
   QL_ALGO_TILED = 1   /* LDS-tiled matrix-core GEMM for larger M */
 } ql_algo;
 
@@ -151,8 +152,8 @@ typedef struct {
                             every tile runs 8 waves (Block_FP8 below 128 x 256: 4); 256 x 256
                             needs packed operands, the LDS-DMA ring of 2 stages and a
                             per-token format.  TILED reads swap_ab, split_k,
-                            a_mode (0 or 2), w_layout, prefetch and the tile; the other
-                            fields are ignored */
+                            a_mode (0 or 2), w_layout, w_lds, prefetch and the tile; the
+                            other fields are ignored */
 } ql_config;
 
 /* Derived launch facts of a plan (read-only). */
