@@ -1,0 +1,88 @@
+"""Host logic of the offline sweep (CPU only): the tie-break that picks a
+table entry, the table line it writes (read back through the C ABI), and the
+candidate generators' limits."""
+
+import pytest
+
+import quantized_gemm_decode_amd as ql
+from quantized_gemm_decode_amd import sweep
+
+
+def _cfg(**kw):
+    return ql.make_config(**kw)
+
+
+def test_choose_prefers_the_simpler_variant_within_two_percent():
+    std = (10.15, _cfg(swap_ab=0, split_k=1))
+    swap = (10.05, _cfg(swap_ab=1, split_k=1))
+    split2 = (10.0, _cfg(swap_ab=1, split_k=2))
+    split8 = (10.1, _cfg(swap_ab=0, split_k=8))
+    assert sweep.choose([split2, swap, std, split8]) is std            # all within 2 % of 10.0
+    assert sweep.choose([split2, swap]) is swap
+    assert sweep.choose([split8, split2]) is split2                     # same variant: smaller split
+
+
+def test_choose_takes_the_fastest_beyond_two_percent():
+    fast = (9.0, _cfg(swap_ab=1, split_k=4))
+    std = (9.5, _cfg(swap_ab=0, split_k=1))                             # 5.6 % slower
+    assert sweep.choose([std, fast]) is fast
+    assert sweep.choose([std, fast], tie=0.1) is std
+
+
+def test_table_line_round_trips_through_the_c_abi(tmp_path):
+    cfg = dict(swap_ab=1, split_k=4, waves_n=2, waves_k=2, rows_per_wave=32, prefetch=1, a_mode=2, w_layout=1)
+    line = sweep.table_line(ql.FP8_DYNAMIC, 8, 4096, 4096, cfg, 6.125)
+    fields = line.split()
+    assert len(fields) == 17 and fields[-1] == "6.125"
+    fwd = sweep.table_line(ql.FP8_DYNAMIC, 2, 4096, 4096, dict(cfg, a_mode=4, split_k=1), 5.5, kind="fwd")
+    assert fwd.endswith(" fwd")
+    path = tmp_path / "t.txt"
+    path.write_text("# test table\n" + line + "\n" + fwd + "\n")
+    try:
+        assert ql.qlinear_table_load(str(path)) == 2
+        got = ql.qlinear_plan_layouts(ql.FP8_DYNAMIC, 8, 4096, 4096, 1, 1)
+        assert got.facts["source"] == "table"
+        for k, v in cfg.items():
+            assert got.config[k] == v, k
+        f = ql.qlinear_plan_layouts(ql.FP8_DYNAMIC, 2, 4096, 4096, 1, 2)     # forward plan
+        assert f.facts["source"] == "table" and f.config["a_mode"] == 4
+    finally:
+        ql.load_default_table()
+
+
+def test_decode_candidates_plan_or_are_not_instantiated():
+    """Every phase-1 decode candidate of a packed layout is a valid config:
+    the planner accepts it or reports it as not instantiated (status 2)."""
+    n_ok = 0
+    for layout in (1, 2):
+        for cfg in sweep.phase1_candidates(ql.FP8_DYNAMIC, 8, 4096, 4096, layout):
+            try:
+                ql.qlinear_plan_with_config(ql.FP8_DYNAMIC, 8, 4096, 4096, cfg)
+                n_ok += 1
+            except ql.QLinearError as e:
+                assert e.status == 2, (cfg, e)
+    assert n_ok > 50
+
+
+def test_fused_candidates_respect_the_fused_limits():
+    assert sweep.fused_ok(ql.FP8_DYNAMIC, 4, 4096) and not sweep.fused_ok(ql.FP8_DYNAMIC, 8, 4096)
+    assert not sweep.fused_ok(ql.W8A8_INT8, 1, 4160)                   # K % 512
+    assert sweep.fused_ok(ql.BLOCK_FP8, 16, 12288) and not sweep.fused_ok(ql.BLOCK_FP8, 24, 4096)
+    cands = list(sweep.phase1_candidates(ql.FP8_DYNAMIC, 2, 4096, 4096, 3))
+    assert cands and all(c["a_mode"] == 4 and c["w_layout"] == 1 for c in cands)
+
+
+def test_tiled_candidates_cover_the_tiles_and_rings():
+    cands = list(sweep.tiled_candidates(1024, 4096, 4096, 2))
+    tiles = {(c["tile_m"], c["tile_n"]) for c in cands}
+    assert (256, 256) in tiles and (128, 256) in tiles and (64, 128) in tiles
+    assert all(c["w_lds"] == 1 and c["prefetch"] == 2 for c in cands if (c["tile_m"], c["tile_n"]) == (256, 256))
+    assert not [c for c in sweep.tiled_candidates(1024, 4096, 4096, 0) if c["w_lds"]]   # DMA ring: packed only
+    small = list(sweep.tiled_candidates(40, 4096, 4096, 2))
+    assert all(c["tile_m"] <= 80 or c["tile_m"] == 64 for c in small)
+
+
+@pytest.mark.parametrize("M", [33, 64])
+def test_decode_candidates_up_to_64_tokens(M):
+    cands = list(sweep.decode_m64_candidates(M, 4096, 4096, 2))
+    assert cands and all(c["w_layout"] == 1 and c["a_mode"] in (0, 2) for c in cands)
