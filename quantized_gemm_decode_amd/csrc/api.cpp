@@ -161,6 +161,8 @@ ql_config heuristic_tiled(int32_t layout, bool a_packed, int64_t M, int64_t N, i
   return c;
 }
 
+// The last-resort decode plan: 4 waves side by side on N, split-K up to about
+// 1024 workgroups (instantiated for every format and operand layout).
 ql_config heuristic_config(int32_t fmt, int32_t layout, bool a_packed, int64_t M, int64_t N, int64_t K) {
   // the MX formats' decode kernel serves up to 64 tokens (MXFP4 has no tiled kernel)
   if (M > 32 && !(is_mx(fmt) && M <= 64)) return heuristic_tiled(layout, a_packed, M, N, K);
@@ -184,6 +186,75 @@ ql_config heuristic_config(int32_t fmt, int32_t layout, bool a_packed, int64_t M
   c.w_lds = 0;
   (void)fmt;
   return c;
+}
+
+// Plans without a table entry, in order of preference (the caller takes the
+// first one that is instantiated).  Over the tabulated shapes the sweep
+// settles on one K range per workgroup (split 1), shared by the workgroup's
+// waves, and on a wave shape that follows the number of 16-row groups: one
+// group per 4-wave workgroup up to 256 groups (about one workgroup per
+// compute unit), 2 x 2 waves up to 1024 (4 x 1 with Swap-AB beyond 512
+// groups at M > 8), and 32 rows a wave beyond 1024 or when K spans 96 or
+// more 128-wide blocks.  Split-K adds three memory round trips (partial
+// sums, arrival counter, read-back) to the launch, so it is used only when a
+// few row groups stream a long K.
+// A forward plan at M <= 2 tries the quantizer fused into the GEMM first.
+// The last candidate is heuristic_config's, which every format instantiates.
+std::vector<ql_config> heuristic_candidates(int32_t fmt, int32_t layout, int a_class, int64_t M, int64_t N,
+                                            int64_t K) {
+  std::vector<ql_config> out;
+  if (M > 32 && !(is_mx(fmt) && M <= 64)) {
+    out.push_back(heuristic_tiled(layout, a_class != 0, M, N, K));
+    return out;
+  }
+  const int64_t groups = (N + 15) / 16;
+  const int64_t G = (K + 127) / 128;
+  ql_config b{};
+  b.algo = QL_ALGO_DECODE;
+  b.w_layout = layout;
+  b.w_lds = layout == 0 ? 1 : 0;
+  b.a_mode = a_class != 0 ? 2 : 0;
+  int64_t split = 1;
+  while (groups * split < 128 && split * 2 <= 256 && G / (split * 2) >= 64) split *= 2;
+  b.split_k = (int32_t)split;
+  b.rows_per_wave = 16;
+  b.prefetch = 2;
+  int first_swap = 0;
+  if (groups <= 256) {
+    b.waves_n = 1;
+    b.waves_k = 4;
+  } else if (groups > 1024 || G >= 96) {
+    // many row groups, or a long K: 32 rows a wave halve the activation reads per weight byte
+    b.waves_n = 1;
+    b.waves_k = 4;
+    b.rows_per_wave = 32;
+    b.prefetch = layout == 1 ? 1 : 2;   // row-major weights run 2- and 4-block batches only
+  } else if (groups <= 512 || M <= 8) {
+    b.waves_n = 2;
+    b.waves_k = 2;
+  } else {
+    // 512..1024 groups and two token tiles' worth of activations: four waves on one K range
+    b.waves_n = 4;
+    b.waves_k = 1;
+    first_swap = 1;
+  }
+  if (a_class == 2 && M <= 2) {
+    ql_config f = b;
+    f.a_mode = 4;
+    f.split_k = 1;
+    f.waves_n = 1;
+    f.waves_k = groups <= 256 ? 16 : 4;
+    f.rows_per_wave = 16;
+    f.prefetch = 1;
+    out.push_back(f);
+  }
+  for (int i = 0; i < 2; ++i) {
+    ql_config c = b;
+    c.swap_ab = i ^ first_swap;
+    out.push_back(c);
+  }
+  out.push_back(heuristic_config(fmt, layout, a_class != 0, M, N, K));
+  return out;
 }
 
 constexpr int64_t kTiledLdsLimit = 160 * 1024 - 256;  // as kLdsLimit
@@ -606,7 +677,10 @@ static ql_status plan_for_layout(int32_t fmt, int32_t layout, int a_class, int64
   // a forward plan without its own entry: the packed-activation plan
   if (a_class == 2 && table_lookup(fmt, layout, 1, M, N, K, &c))
     return build_plan(fmt, M, N, K, c, QL_SRC_TABLE, out_plan);
-  return build_plan(fmt, M, N, K, heuristic_config(fmt, layout, a_class != 0, M, N, K), QL_SRC_HEURISTIC, out_plan);
+  ql_status st = QL_E_UNSUPPORTED;
+  for (const ql_config& h : heuristic_candidates(fmt, layout, a_class, M, N, K))
+    if ((st = build_plan(fmt, M, N, K, h, QL_SRC_HEURISTIC, out_plan)) == QL_OK) break;
+  return st;
 }
 
 ql_status qlinear_plan(int32_t fmt, int64_t M, int64_t N, int64_t K, ql_plan* out_plan) {

@@ -175,11 +175,56 @@ def test_packed_weight_sizes():
 
 
 def test_heuristic_plans_cover_every_decode_workload():
+    """Without a table every decode workload point still gets an instantiated
+    plan for every operand layout, one K range per workgroup (split 1) and at
+    least one workgroup per 64 weight rows."""
     from workloads import decode_points, decode_workloads
-    for cfg in decode_workloads():
-        for (_, N, K, M) in decode_points(cfg):
-            p = ql.qlinear_plan(cfg.fmt, M, N, K)
-            assert p.facts["workgroups"] >= 256
+    ql.qlinear_table_clear()
+    try:
+        for cfg in decode_workloads(include_mx=True):
+            layouts = [(1, 1), (1, 2)] if cfg.fmt in ql.MX_FORMATS else [(0, 0), (1, 0), (1, 1), (1, 2)]
+            for (_, N, K, M) in decode_points(cfg):
+                for lay in layouts:
+                    p = ql.qlinear_plan_layouts(cfg.fmt, M, N, K, *lay)
+                    assert p.config["split_k"] == 1, (cfg.name, N, K, M, lay, p.config)
+                    assert p.facts["workgroups"] >= N // 64, (cfg.name, N, K, M, lay, p.config)
+    finally:
+        ql.load_default_table()
+
+
+@pytest.mark.parametrize("N,K,small_m,large_m", [
+    (2048, 2048, (1, 4, 16, 0), (1, 4, 16, 0)), (4096, 14336, (1, 4, 16, 0), (1, 4, 16, 0)),
+    (5120, 5120, (2, 2, 16, 0), (2, 2, 16, 0)), (7168, 5120, (2, 2, 16, 0), (2, 2, 16, 0)),
+    (5120, 17408, (1, 4, 32, 0), (1, 4, 32, 0)), (14336, 4096, (2, 2, 16, 0), (4, 1, 16, 1)),
+    (34816, 5120, (1, 4, 32, 0), (1, 4, 32, 0))])
+def test_heuristic_wave_shape_follows_the_row_groups(N, K, small_m, large_m):
+    """Table-free decode plans: one 16-row group per 4-wave workgroup up to 256
+    groups, 2 x 2 waves up to 1024 (4 x 1 with Swap-AB beyond 512 groups at
+    M > 8), 32 rows a wave beyond 1024 groups or for a long K; split 1; a
+    forward plan at M = 1 fuses the quantizer where the fused kernel fits.
+    (waves_n, waves_k, rows_per_wave, swap_ab) for M <= 8 and for M > 8."""
+    ql.qlinear_table_clear()
+    try:
+        for M in (1, 8, 16, 32):
+            c = ql.qlinear_plan_layouts(ql.FP8_DYNAMIC, M, N, K, 1, 1).config
+            want = small_m if M <= 8 else large_m
+            assert (c["waves_n"], c["waves_k"], c["rows_per_wave"], c["swap_ab"]) == want, (M, c)
+            assert c["split_k"] == 1 and c["a_mode"] == 2, (M, c)
+        f = ql.qlinear_plan_layouts(ql.FP8_DYNAMIC, 1, N, K, 1, 2).config
+        fits = K <= 16384 and K % 512 == 0
+        assert (f["a_mode"] == 4) == fits, f
+    finally:
+        ql.load_default_table()
+
+
+def test_heuristic_splits_only_few_row_groups_over_a_long_k():
+    ql.qlinear_table_clear()
+    try:
+        assert ql.qlinear_plan_layouts(ql.W8A8_INT8, 8, 64, 65536, 1, 1).config["split_k"] == 8
+        assert ql.qlinear_plan_layouts(ql.W8A8_INT8, 8, 64, 4096, 1, 1).config["split_k"] == 1
+        assert ql.qlinear_plan_layouts(ql.W8A8_INT8, 8, 4096, 65536, 1, 1).config["split_k"] == 1
+    finally:
+        ql.load_default_table()
 
 
 def test_fused_quantization_plans_are_validated_on_host():
