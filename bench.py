@@ -51,8 +51,9 @@ def algorithmic_bytes(fmt, M, N, K):
 
 def fused_kernel_bytes(fmt, M, N, K):
     """Bytes one fused-quantization GEMM launch must move: weights and their
-    scales, bf16 X in, the codes and scales it hands back, and Y."""
-    return N * K + 4 * N + 2 * M * K + M * K + 4 * M + 2 * M * N
+    scales, bf16 X in, the codes and scales it hands back, and Y -- the
+    unfused launch's bytes (codes and scales written instead of read) plus X."""
+    return algorithmic_bytes(fmt, M, N, K) + 2 * M * K
 
 
 def quantizer_bytes(fmt, M, K):
@@ -106,11 +107,11 @@ def recorded_traffic(workload, layout):
 
 
 def is_fused_instantiation(name):
-    """A qgemm_decode_kernel<FMT, SWAP, MT, RG, NW, PF, AL, WM> name with AL = 4."""
+    """A qgemm_decode_kernel<FMT, SWAP, MT, RG, NW, PF, AL, WM, GLU> name with AL = 4."""
     if "qgemm_decode_kernel<" not in name:
         return False
     args = name.split("qgemm_decode_kernel<", 1)[1].split(">", 1)[0].split(",")
-    return len(args) == 8 and args[6].strip() == "4"
+    return len(args) == 9 and args[6].strip() == "4"
 
 
 def pmc_summary(workload, layout, fetch_csv, write_csv):
