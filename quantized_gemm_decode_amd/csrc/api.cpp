@@ -138,8 +138,9 @@ struct ql_graph_s {
 
 namespace {
 
-// Tiled (M > 32): tile rows follow M, 128 weight rows per tile; split K
-// only while the tiles alone cannot give every CU two workgroups.
+// The last-resort tiled plan (M > 32): tile rows follow M, 128 weight rows
+// per tile; split K only while the tiles alone cannot give every CU two
+// workgroups.
 ql_config heuristic_tiled(int32_t layout, bool a_packed, int64_t M, int64_t N, int64_t K) {
   ql_config c{};
   c.algo = QL_ALGO_TILED;
@@ -188,6 +189,69 @@ ql_config heuristic_config(int32_t fmt, int32_t layout, bool a_packed, int64_t M
   return c;
 }
 
+// Tiled plans without a table entry, in order of preference.  Over the
+// probed shapes the fastest tile is the largest of 256 x 256 (2-stage LDS-DMA
+// ring), 128 x 256, 128 x 128 and 64 x 128 that still gives about 200 tiles
+// or more; below that the 64 x 128 tile, with split-K 4 when there are at
+// most 64 tiles and split 2 at most 128 tiles over a K of 64 or more blocks.
+// Block_FP8 applies its scales inside the K loop and keeps more registers
+// live: it runs best with 1-block batches on 128 x 128 (Swap-AB) from about
+// 400 such tiles, else on 64 x 128 (1-block batches from 400 tiles, 2 below,
+// split-K 4 up to 64 tiles and 2 up to 128, or 4 over a K of 64 or more
+// blocks).  Tiles a format or operand layout does not instantiate (the ring
+// needs packed operands; MXFP8 runs neither the ring nor 256 x 256) are
+// skipped by the caller, down to heuristic_tiled's plan.
+std::vector<ql_config> tiled_candidates(int32_t fmt, int32_t layout, bool a_packed, int64_t M, int64_t N,
+                                        int64_t K) {
+  struct Tile {
+    int bm, bn, pf, ring;
+  };
+  static const Tile kTiles[] = {{256, 256, 2, 1}, {128, 256, 1, 0}, {128, 128, 2, 0}, {64, 128, 2, 0}};
+  const int64_t G = (K + 127) / 128;
+  std::vector<ql_config> out;
+  auto make = [&](int bm, int bn, int pf, int ring, int swap, int64_t split) {
+    ql_config c{};
+    c.algo = QL_ALGO_TILED;
+    c.w_layout = layout;
+    c.a_mode = a_packed ? 2 : 0;
+    c.swap_ab = swap;
+    c.waves_n = 4;
+    c.waves_k = 1;
+    c.rows_per_wave = 16;
+    c.tile_m = bm;
+    c.tile_n = bn;
+    c.prefetch = pf;
+    c.w_lds = ring;
+    while (split > 1 && G / split < 4) split /= 2;
+    c.split_k = (int32_t)split;
+    return c;
+  };
+  auto count = [&](int bm, int bn) { return ((M + bm - 1) / bm) * ((N + bn - 1) / bn); };
+  if (fmt == QL_BLOCK_FP8) {
+    const int64_t t64 = count(64, 128);
+    const int64_t split = t64 <= 64 ? 4 : (t64 <= 128 ? (G >= 64 ? 4 : 2) : 1);
+    const ql_config small = make(64, 128, t64 >= 400 ? 1 : 2, 0, 0, split);
+    if (M >= 64 && count(128, 128) >= 400) out.push_back(make(128, 128, 1, 0, 1, 1));
+    out.push_back(small);
+    out.push_back(heuristic_tiled(layout, a_packed, M, N, K));
+    return out;
+  }
+  bool chosen = false;
+  for (const Tile& t : kTiles) {
+    if (t.bm > 64 && t.bm > 2 * M) continue;   // mostly padding rows
+    const int64_t tiles = ((M + t.bm - 1) / t.bm) * ((N + t.bn - 1) / t.bn);
+    const bool last = t.bm == 64;
+    if (!chosen && tiles < 200 && !last) continue;
+    int64_t split = 1;
+    if (t.bm == 64 && tiles <= 64) split = 4;
+    else if (t.bm == 64 && tiles <= 128 && G >= 64) split = 2;
+    out.push_back(make(t.bm, t.bn, t.pf, t.ring, 0, split));
+    chosen = true;
+  }
+  out.push_back(heuristic_tiled(layout, a_packed, M, N, K));
+  return out;
+}
+
 // Plans without a table entry, in order of preference (the caller takes the
 // first one that is instantiated).  Over the tabulated shapes the sweep
 // settles on one K range per workgroup (split 1), shared by the workgroup's
@@ -203,10 +267,7 @@ ql_config heuristic_config(int32_t fmt, int32_t layout, bool a_packed, int64_t M
 std::vector<ql_config> heuristic_candidates(int32_t fmt, int32_t layout, int a_class, int64_t M, int64_t N,
                                             int64_t K) {
   std::vector<ql_config> out;
-  if (M > 32 && !(is_mx(fmt) && M <= 64)) {
-    out.push_back(heuristic_tiled(layout, a_class != 0, M, N, K));
-    return out;
-  }
+  if (M > 32 && !(is_mx(fmt) && M <= 64)) return tiled_candidates(fmt, layout, a_class != 0, M, N, K);
   const int64_t groups = (N + 15) / 16;
   const int64_t G = (K + 127) / 128;
   ql_config b{};

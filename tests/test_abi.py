@@ -394,3 +394,45 @@ def test_mxfp4_plans_and_sizes():
     null = ctypes.c_void_p(0)
     assert ql.lib().qlinear_pack_weight_fp4(null, 4, 4160, null, null) == QL_E_INVALID
     assert ql.lib().qlinear_quantize_weight(ql.MXFP4, null, 4, 4160, null, null, null) == QL_E_INVALID
+
+
+@pytest.mark.parametrize("N,K,M,tile,split", [
+    (4096, 4096, 64, (64, 128), 4), (4096, 4096, 256, (64, 128), 1), (4096, 4096, 1024, (128, 128), 1),
+    (4096, 4096, 4096, (256, 256), 1), (14336, 4096, 64, (64, 128), 1), (14336, 4096, 256, (128, 128), 1),
+    (14336, 4096, 1024, (256, 256), 1), (4096, 14336, 256, (64, 128), 2), (28672, 4096, 256, (128, 256), 1),
+    (2048, 8192, 64, (64, 128), 4), (2048, 8192, 4096, (128, 256), 1)])
+def test_tiled_heuristic_takes_the_largest_tile_that_fills_the_chip(N, K, M, tile, split):
+    """Table-free tiled plans: the largest of 256 x 256, 128 x 256, 128 x 128
+    and 64 x 128 that gives about 200 tiles, else 64 x 128 with split-K 4
+    (<= 64 tiles) or 2 (<= 128 tiles over a K of 64 or more blocks).  Row-major
+    operands cannot run the 256 x 256 ring and take the next tile; MXFP8 runs
+    the register ring only."""
+    ql.qlinear_table_clear()
+    try:
+        c = ql.qlinear_plan_layouts(ql.FP8_DYNAMIC, M, N, K, 1, 1).config
+        assert c["algo"] == ql.ALGO_TILED and (c["tile_m"], c["tile_n"]) == tile and c["split_k"] == split, c
+        assert c["w_lds"] == (1 if tile == (256, 256) else 0), c
+        r = ql.qlinear_plan_layouts(ql.FP8_DYNAMIC, M, N, K, 0, 0).config
+        assert r["algo"] == ql.ALGO_TILED and r["w_lds"] == 0, r
+        if tile != (256, 256):
+            assert (r["tile_m"], r["tile_n"]) == tile, r
+        x = ql.qlinear_plan_layouts(ql.MXFP8, M, N, K, 1, 1).config
+        if M > 64:
+            assert x["algo"] == ql.ALGO_TILED and x["w_lds"] == 0 and (x["tile_m"], x["tile_n"]) != (256, 256), x
+    finally:
+        ql.load_default_table()
+
+
+@pytest.mark.parametrize("N,K,M,cfg", [
+    (4096, 4096, 64, (64, 128, 2, 0, 4)), (4096, 4096, 256, (64, 128, 2, 0, 2)), (4096, 4096, 1024, (64, 128, 1, 0, 1)),
+    (4096, 4096, 4096, (128, 128, 1, 1, 1)), (4096, 14336, 256, (64, 128, 2, 0, 4)),
+    (28672, 4096, 64, (64, 128, 2, 0, 1)), (14336, 4096, 1024, (128, 128, 1, 1, 1))])
+def test_tiled_heuristic_block_fp8(N, K, M, cfg):
+    """Block_FP8 table-free tiled plans (tile_m, tile_n, prefetch, swap_ab, split_k):
+    128 x 128 with 1-block batches and Swap-AB from 400 such tiles, else 64 x 128."""
+    ql.qlinear_table_clear()
+    try:
+        c = ql.qlinear_plan_layouts(ql.BLOCK_FP8, M, N, K, 1, 1).config
+        assert (c["tile_m"], c["tile_n"], c["prefetch"], c["swap_ab"], c["split_k"]) == cfg, c
+    finally:
+        ql.load_default_table()
