@@ -259,11 +259,11 @@ std::vector<ql_config> tiled_candidates(int32_t fmt, int32_t layout, bool a_pack
 // group per 4-wave workgroup up to 256 groups (about one workgroup per
 // compute unit), 2 x 2 waves up to 1024 (4 x 1 with Swap-AB beyond 512
 // groups at M > 8), and 32 rows a wave beyond 1024 or when K spans 96 or
-// more 128-wide blocks.  Split-K adds three memory round trips (partial
-// sums, arrival counter, read-back) to the launch, so it is used only when a
-// few row groups stream a long K.
-// A forward plan at M <= 2 tries the quantizer fused into the GEMM first.
-// The last candidate is heuristic_config's, which every format instantiates.
+// more 128-wide blocks (for the MX formats only at M > 16).  Split-K adds
+// three memory round trips (partial sums, arrival counter, read-back) to the
+// launch, so it is used only when a few row groups stream a long K.  A
+// forward plan at M <= 2 tries the quantizer fused into the GEMM first.  The
+// last candidate is heuristic_config's, which every format instantiates.
 std::vector<ql_config> heuristic_candidates(int32_t fmt, int32_t layout, int a_class, int64_t M, int64_t N,
                                             int64_t K) {
   std::vector<ql_config> out;
@@ -284,8 +284,9 @@ std::vector<ql_config> heuristic_candidates(int32_t fmt, int32_t layout, int a_c
   if (groups <= 256) {
     b.waves_n = 1;
     b.waves_k = 4;
-  } else if (groups > 1024 || G >= 96) {
+  } else if (groups > 1024 || (G >= 96 && (!is_mx(fmt) || M > 16))) {
     // many row groups, or a long K: 32 rows a wave halve the activation reads per weight byte
+    // (MX formats, whose scale loads add to the per-block work, gain only from two token tiles)
     b.waves_n = 1;
     b.waves_k = 4;
     b.rows_per_wave = 32;

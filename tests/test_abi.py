@@ -210,6 +210,12 @@ def test_heuristic_wave_shape_follows_the_row_groups(N, K, small_m, large_m):
             want = small_m if M <= 8 else large_m
             assert (c["waves_n"], c["waves_k"], c["rows_per_wave"], c["swap_ab"]) == want, (M, c)
             assert c["split_k"] == 1 and c["a_mode"] == 2, (M, c)
+        if (N, K) == (5120, 17408):   # the MX formats keep 2 x 2 waves on a long K up to 16 tokens
+            for fmt in (ql.MXFP8, ql.MXFP4):
+                c = ql.qlinear_plan_layouts(fmt, 16, N, K, 1, 1).config
+                assert (c["waves_n"], c["waves_k"], c["rows_per_wave"]) == (2, 2, 16), c
+                c = ql.qlinear_plan_layouts(fmt, 32, N, K, 1, 1).config
+                assert (c["waves_n"], c["waves_k"], c["rows_per_wave"]) == (1, 4, 32), c
         f = ql.qlinear_plan_layouts(ql.FP8_DYNAMIC, 1, N, K, 1, 2).config
         fits = K <= 16384 and K % 512 == 0
         assert (f["a_mode"] == 4) == fits, f
