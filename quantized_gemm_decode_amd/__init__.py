@@ -14,6 +14,7 @@ library is missing, or a tensor is not on the GPU, calls raise.
 """
 
 import ctypes
+import math
 import os
 
 import torch
@@ -286,6 +287,44 @@ class Plan:
     def workspace_bytes(self):
         return int(lib().qlinear_workspace_bytes(self.handle))
 
+    def operand_bytes(self):
+        """Least bytes each operand of a run / forward with this plan must hold
+        (the kernels read and write by the plan's shape, not the tensors')."""
+        if getattr(self, "_operand_bytes", None) is None:
+            cfg, facts = self.info()
+            fmt, M, N, K = self.fmt, self.M, self.N, self.K
+            mx = fmt in MX_FORMATS
+            packed_a = cfg["a_mode"] >= 2
+            sbytes = 1 if mx else 4
+            if cfg["w_layout"] == 1:
+                w = qlinear_packed_weight_bytes_fp4(N, K) if fmt == MXFP4 else qlinear_packed_weight_bytes(N, K)
+            else:
+                w = N * K // 2 if fmt == MXFP4 else N * K
+            self._operand_bytes = dict(
+                x=2 * M * K,
+                a_q=qlinear_packed_act_bytes(M, K) if packed_a else M * K,
+                a_scale=(qlinear_packed_mx_scale_bytes(M, K) if mx and packed_a
+                         else math.prod(act_scale_shape(fmt, M, K)) * sbytes),
+                w_q=w,
+                w_scale=(qlinear_packed_mx_scale_bytes(N, K) if mx and cfg["w_layout"] == 1
+                         else math.prod(weight_scale_shape(fmt, N, K)) * sbytes),
+                y=2 * M * (N // 2 if facts["epilogue"] == 1 else N),
+                acc_out=4 * M * N,
+                workspace=facts["workspace_bytes"])
+            if M == 0 or N == 0 or K == 0:     # a no-op, or (K == 0) a run that only zeroes Y
+                self._operand_bytes = {k: (v if k == "y" else 0) for k, v in self._operand_bytes.items()}
+        return self._operand_bytes
+
+    def check_operands(self, **tensors):
+        """Raise ValueError for any operand smaller than the plan needs."""
+        need = self.operand_bytes()
+        for name, t in tensors.items():
+            if not isinstance(t, torch.Tensor):
+                continue      # None, or not a tensor (the pointer check reports it)
+            have = t.numel() * t.element_size()
+            if have < need[name]:
+                raise ValueError("%s holds %d bytes; this plan needs at least %d" % (name, have, need[name]))
+
     def new_workspace(self, device="cuda"):
         """Zero-initialised workspace (zeroed once; runs keep it all-zero)."""
         n = self.workspace_bytes
@@ -359,6 +398,7 @@ def qlinear_plan_with_config(fmt, M, N, K, cfg):
 # ----------------------------------------------------------------- GEMM
 
 def qlinear_run(plan, a_q, a_scale, w_q, w_scale, y, workspace=None, stream=None):
+    plan.check_operands(a_q=a_q, a_scale=a_scale, w_q=w_q, w_scale=w_scale, y=y, workspace=workspace)
     _check(lib().qlinear_run(plan.handle, _ptr(a_q, "a_q", CODE_DTYPES), _ptr(a_scale, "a_scale", SCALE_DTYPES),
                              _ptr(w_q, "w_q", CODE_DTYPES), _ptr(w_scale, "w_scale", SCALE_DTYPES),
                              _ptr(y, "y", torch.bfloat16), _ptr(workspace, "workspace", required=False),
@@ -366,6 +406,8 @@ def qlinear_run(plan, a_q, a_scale, w_q, w_scale, y, workspace=None, stream=None
 
 
 def qlinear_run_debug_acc(plan, a_q, a_scale, w_q, w_scale, y, acc_out, workspace=None, stream=None):
+    plan.check_operands(a_q=a_q, a_scale=a_scale, w_q=w_q, w_scale=w_scale, y=y, acc_out=acc_out,
+                        workspace=workspace)
     _check(lib().qlinear_run_debug_acc(plan.handle, _ptr(a_q, "a_q", CODE_DTYPES),
                                        _ptr(a_scale, "a_scale", SCALE_DTYPES), _ptr(w_q, "w_q", CODE_DTYPES),
                                        _ptr(w_scale, "w_scale", SCALE_DTYPES), _ptr(y, "y", torch.bfloat16),
@@ -375,6 +417,7 @@ def qlinear_run_debug_acc(plan, a_q, a_scale, w_q, w_scale, y, acc_out, workspac
 
 
 def qlinear_forward(plan, x, a_q, a_scale, w_q, w_scale, y, workspace=None, stream=None):
+    plan.check_operands(x=x, a_q=a_q, a_scale=a_scale, w_q=w_q, w_scale=w_scale, y=y, workspace=workspace)
     _check(lib().qlinear_forward(plan.handle, _ptr(x, "x", torch.bfloat16), _ptr(a_q, "a_q", CODE_DTYPES),
                                  _ptr(a_scale, "a_scale", SCALE_DTYPES), _ptr(w_q, "w_q", CODE_DTYPES),
                                  _ptr(w_scale, "w_scale", SCALE_DTYPES), _ptr(y, "y", torch.bfloat16),

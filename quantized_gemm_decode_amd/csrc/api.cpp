@@ -511,8 +511,8 @@ ql_status launch_gemm(const ql_plan_s* p, const void* a_q, const void* a_scale, 
   if (p->M == 0 || p->N == 0) return QL_OK;
   if (!y) return fail(QL_E_INVALID, "y is NULL");
   if (!aligned16(y)) return fail(QL_E_ALIGN, "y is not 16-byte aligned");
-  if (p->K == 0) {
-    hipError_t e = qlk::launch_fill_zero_bf16(y, p->M * p->N, s);
+  if (p->K == 0) {   // Y = 0 (SiLU-and-mul plans: silu(0) * 0 over the [M, N/2] output)
+    hipError_t e = qlk::launch_fill_zero_bf16(y, p->M * (p->glu ? p->N / 2 : p->N), s);
     return e == hipSuccess ? QL_OK : hip_fail(e, "zero fill");
   }
   if (fused) {

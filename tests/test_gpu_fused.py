@@ -155,7 +155,7 @@ def test_fused_graph_replays_match_eager(fmt):
                                                          w_layout=1))
     xd = dev_bf16(xb)
     a_p = ql.act_buffer(plan)
-    a_s = torch.empty(M, dtype=torch.float32, device="cuda")
+    a_s = ql.act_scale_buffer(plan)      # Block_FP8: the [M, K/128] group scales
     y = torch.zeros(M, N, dtype=torch.bfloat16, device="cuda")
     ws = plan.new_workspace()
     ql.qlinear_forward(plan, xd, a_p, a_s, w_p, w_s, y, ws)

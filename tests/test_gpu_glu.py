@@ -109,3 +109,19 @@ def test_glu_plan_on_the_gate_up_shape(fmt, M):
     h_ref, h_true, bound = oracle.glu_reference(fmt, r, split=plan.facts["chunks"])
     st = oracle.check_fp8_parity(h[:, cols], h_ref, h_true, bound)
     assert st["ok"] and st["frac_within_ulp"] >= 0.95, (plan.config, st)
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_glu_plan_with_k_zero_writes_only_its_output(fmt):
+    """K = 0: the SiLU-and-mul output [M, N/2] becomes silu(0) * 0 = 0 and the
+    run writes nothing past it (the sentinel after Y keeps its value)."""
+    M, N = 4, 64
+    plan = ql.qlinear_plan_glu(fmt, M, N, 0, 1)
+    buf = torch.full((2 * M * (N // 2),), 3.0, dtype=torch.bfloat16, device="cuda")
+    y = buf[:M * (N // 2)].view(M, N // 2)
+    e = torch.empty(16, dtype=torch.uint8, device="cuda")
+    f = torch.empty(16, dtype=torch.float32, device="cuda")
+    ql.qlinear_run(plan, e, f, e, f, y)
+    torch.cuda.synchronize()
+    assert int(torch.count_nonzero(y)) == 0
+    assert bool(torch.all(buf[M * (N // 2):] == 3.0))
