@@ -72,6 +72,13 @@ def _ptr(t, name, dtype=None, required=True):
     return ctypes.c_void_p(t.data_ptr())
 
 
+def _need(t, name, nbytes):
+    """Refuse an output (or input) tensor smaller than the call will touch."""
+    if isinstance(t, torch.Tensor) and t.numel() * t.element_size() < nbytes:
+        raise ValueError("%s holds %d bytes; this call needs at least %d"
+                         % (name, t.numel() * t.element_size(), nbytes))
+
+
 CODE_DTYPES = (torch.int8, torch.uint8, torch.float8_e4m3fn)
 SCALE_DTYPES = (torch.float32, torch.uint8)      # binary32 scales, or MXFP8's E8M0 bytes
 
@@ -112,6 +119,8 @@ def weight_code_dtype(fmt):
 
 def qlinear_quantize_act(fmt, x, a_q, a_scale, stream=None):
     M, K = x.shape
+    _need(a_q, "a_q", M * K)
+    _need(a_scale, "a_scale", math.prod(act_scale_shape(fmt, M, K)) * (1 if fmt in MX_FORMATS else 4))
     _check(lib().qlinear_quantize_act(fmt, _ptr(x, "x", torch.bfloat16), M, K, _ptr(a_q, "a_q", CODE_DTYPES),
                                       _ptr(a_scale, "a_scale", SCALE_DTYPES), _stream(stream)),
            "qlinear_quantize_act")
@@ -123,6 +132,9 @@ def qlinear_packed_act_bytes(M, K):
 
 def qlinear_quantize_act_packed(fmt, x, a_packed, a_scale, stream=None):
     M, K = x.shape
+    _need(a_packed, "a_packed", qlinear_packed_act_bytes(M, K))
+    _need(a_scale, "a_scale", qlinear_packed_mx_scale_bytes(M, K) if fmt in MX_FORMATS
+          else 4 * math.prod(act_scale_shape(fmt, M, K)))
     _check(lib().qlinear_quantize_act_packed(fmt, _ptr(x, "x", torch.bfloat16), M, K,
                                              _ptr(a_packed, "a_packed", CODE_DTYPES),
                                              _ptr(a_scale, "a_scale", SCALE_DTYPES), _stream(stream)),
@@ -131,6 +143,8 @@ def qlinear_quantize_act_packed(fmt, x, a_packed, a_scale, stream=None):
 
 def qlinear_quantize_weight(fmt, w, w_q, w_scale, stream=None):
     N, K = w.shape
+    _need(w_q, "w_q", math.prod(weight_code_shape(fmt, N, K)))
+    _need(w_scale, "w_scale", math.prod(weight_scale_shape(fmt, N, K)) * (1 if fmt in MX_FORMATS else 4))
     _check(lib().qlinear_quantize_weight(fmt, _ptr(w, "w", torch.bfloat16), N, K, _ptr(w_q, "w_q", CODE_DTYPES),
                                          _ptr(w_scale, "w_scale", SCALE_DTYPES), _stream(stream)),
            "qlinear_quantize_weight")
@@ -184,6 +198,7 @@ def quantize_weight(fmt, w, stream=None):
 
 def qlinear_encode_e4m3(x, codes, stream=None):
     """The library's E4M3 encoder: codes = E4M3(clamp(x, -448, 448)), round to nearest even."""
+    _need(codes, "codes", x.numel())
     _check(lib().qlinear_encode_e4m3(_ptr(x, "x", torch.float32), x.numel(), _ptr(codes, "codes", CODE_DTYPES),
                                      _stream(stream)), "qlinear_encode_e4m3")
 
@@ -194,6 +209,7 @@ def qlinear_packed_weight_bytes(N, K):
 
 def qlinear_pack_weight(w_q, w_packed, stream=None):
     N, K = w_q.shape
+    _need(w_packed, "w_packed", qlinear_packed_weight_bytes(N, K))
     _check(lib().qlinear_pack_weight(_ptr(w_q, "w_q", CODE_DTYPES), N, K, _ptr(w_packed, "w_packed", CODE_DTYPES),
                                      _stream(stream)), "qlinear_pack_weight")
 
@@ -204,6 +220,8 @@ def qlinear_packed_mx_scale_bytes(R, K):
 
 def qlinear_pack_mx_scales(s, K, out, stream=None):
     R = s.shape[0]
+    _need(s, "scales", R * (K // 32))
+    _need(out, "packed", qlinear_packed_mx_scale_bytes(R, K))
     _check(lib().qlinear_pack_mx_scales(_ptr(s, "scales", torch.uint8), R, K, _ptr(out, "packed", torch.uint8),
                                         _stream(stream)), "qlinear_pack_mx_scales")
 

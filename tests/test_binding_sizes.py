@@ -52,3 +52,29 @@ def test_short_operands_are_refused():
         with pytest.raises(ValueError, match=name):
             plan.check_operands(**short)
     assert _bytes(ok["y"]) == 2 * M * N
+
+
+def test_quantizer_and_packer_outputs_are_checked():
+    """Outputs sized from the input's shape: one byte short is refused before
+    any pointer is formed (CPU tensors suffice for the size check)."""
+    M, K, N = 5, 256, 40
+    x = torch.empty(M, K, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="a_q"):
+        ql.qlinear_quantize_act(ql.FP8_DYNAMIC, x, torch.empty(M * K - 1, dtype=torch.uint8),
+                                torch.empty(M, dtype=torch.float32))
+    with pytest.raises(ValueError, match="a_scale"):
+        ql.qlinear_quantize_act(ql.BLOCK_FP8, x, torch.empty(M * K, dtype=torch.uint8),
+                                torch.empty(M, dtype=torch.float32))
+    with pytest.raises(ValueError, match="a_packed"):
+        ql.qlinear_quantize_act_packed(ql.W8A8_INT8, x, torch.empty(M * K, dtype=torch.uint8),
+                                       torch.empty(M, dtype=torch.float32))
+    w = torch.empty(N, K, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="w_scale"):
+        ql.qlinear_quantize_weight(ql.MXFP8, w, torch.empty(N, K, dtype=torch.uint8),
+                                   torch.empty(N * K // 32 - 1, dtype=torch.uint8))
+    with pytest.raises(ValueError, match="w_packed"):
+        ql.qlinear_pack_weight(torch.empty(N, K, dtype=torch.int8), torch.empty(N * K, dtype=torch.int8))
+    with pytest.raises(ValueError, match="packed"):
+        ql.qlinear_pack_mx_scales(torch.empty(N, K // 32, dtype=torch.uint8), K, torch.empty(16, dtype=torch.uint8))
+    with pytest.raises(ValueError, match="codes"):
+        ql.qlinear_encode_e4m3(torch.empty(100), torch.empty(99, dtype=torch.uint8))
