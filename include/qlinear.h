@@ -186,7 +186,10 @@ const char* qlinear_last_error(void);
  * Bit-exact contract: amax exact in fp32, IEEE division, round-half-even,
  * clamp, E4M3 round-to-nearest-even, fp32 subnormals kept (MXFP8: the
  * shared exponent from amax's bits, an exact power-of-two scaling, E4M3
- * round-to-nearest-even).
+ * round-to-nearest-even).  An all-zero row (or group) gets scale 1 and zero
+ * codes (MXFP8: E8M0 byte 0).  X must be finite: for a row (or group)
+ * holding an infinity or NaN the scale and codes are outside the contract;
+ * the other rows are unaffected.
  */
 ql_status qlinear_quantize_act(int32_t fmt, const void* x_bf16, int64_t M, int64_t K,
                                void* a_q, void* a_scale, void* stream);
