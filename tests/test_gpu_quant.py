@@ -115,6 +115,30 @@ def test_quantizer_empty_inputs_are_no_ops():
     assert a_q.shape == (0, 256)
 
 
+@pytest.mark.parametrize("fmt", FMTS)
+def test_non_finite_rows_leave_the_other_rows_exact(fmt):
+    """A row holding +inf, -inf and NaN is outside the quantizer's contract;
+    every other row's codes and scales stay bit-exact, and the packed layout
+    still holds the row-major codes of every row."""
+    M, K = 6, 512
+    x, _ = make_inputs(K, 1, M, 0.02, seed=77, with_weight=False)
+    xb = np.array(bf16_bits(x), dtype=np.uint16)
+    bad = 2
+    xb[bad, 5], xb[bad, 300], xb[bad, 301] = 0x7F80, 0xFF80, 0x7FC0
+    good = [m for m in range(M) if m != bad]
+    q_ref, s_ref = oracle.quantize_act(fmt, xb[good])
+    a_q, a_s = ql.quantize_act(fmt, dev_bf16(xb))
+    a_p, a_ps = ql.quantize_act_packed(fmt, dev_bf16(xb))
+    torch.cuda.synchronize()
+    q = host_codes(fmt, a_q)
+    assert np.array_equal(q[good], q_ref)
+    s_bits = a_s.cpu().numpy().view(np.uint32)
+    assert np.array_equal(s_bits[good], np.asarray(s_ref, np.float32).view(np.uint32))
+    n = ql.qlinear_packed_act_bytes(M, K)
+    assert np.array_equal(a_p[:n].view(torch.uint8).cpu().numpy(), pack_ref(np.asarray(q).view(np.uint8)))
+    assert np.array_equal(a_ps.cpu().numpy().view(np.uint32)[good], s_bits[good])
+
+
 def _e4m3_probe_inputs():
     """Every bf16 value; every binary32 within 64 ulp of each E4M3 value and of
     each midpoint between neighbouring values (both signs); values beyond the
