@@ -1,0 +1,47 @@
+"""The offline tuning path end to end on the GPU: sweep one small shape,
+write its table line, load it back, and check that the planner then returns
+the swept configuration and that this plan matches the oracle."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import quantized_gemm_decode_amd as ql
+from quantized_gemm_decode_amd import sweep
+from tests.gpu_util import fp8_check, host_bf16_bits, requires_gpu
+from workloads import bf16_bits, make_inputs
+
+pytestmark = [pytest.mark.gpu, requires_gpu]
+
+
+@pytest.mark.parametrize("fmt", [ql.FP8_DYNAMIC, ql.W8A8_INT8])
+def test_sweep_one_shape_then_plan_from_its_table(fmt, tmp_path):
+    M, N, K = 4, 384, 1024
+    x, w = make_inputs(K, N, M, 0.02, seed=5)
+    s = torch.cuda.Stream()
+    timer = sweep.Timer(fmt, N, K, x, w, s, layout=2, max_copies=8)
+    res = sweep.sweep_point(timer, fmt, M, N, K, log=lambda *a: None)
+    assert len(res) > 10 and all(u > 0 for u, _ in res)
+    us, cfg = res[0]
+    assert us <= min(u for u, _ in res) * 1.02 + 1e-9          # the tie rule keeps the choice within 2 %
+    path = tmp_path / "table.txt"
+    path.write_text(sweep.table_line(fmt, M, N, K, cfg, us) + "\n")
+    try:
+        assert ql.qlinear_table_load(str(path)) == 1
+        plan = ql.qlinear_plan_layouts(fmt, M, N, K, 1, 1)
+        assert plan.facts["source"] == "table"
+        got = plan.config
+        assert all(got[k] == v for k, v in ql.make_config(**cfg).items()), (got, cfg)
+        r = oracle.reference(fmt, bf16_bits(x), bf16_bits(w))
+        w_q, w_s = ql.quantize_weight(fmt, w.cuda())
+        a_q, a_s = ql.act_buffer(plan), ql.act_scale_buffer(plan)
+        y = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
+        ql.qlinear_forward(plan, x.cuda(), a_q, a_s, ql.pack_weight(w_q), w_s, y, plan.new_workspace())
+        torch.cuda.synchronize()
+        if fmt == ql.W8A8_INT8:
+            assert np.array_equal(host_bf16_bits(y), r["y_ref"])
+        else:
+            assert fp8_check(fmt, r, host_bf16_bits(y), plan.facts["chunks"])["ok"]
+    finally:
+        ql.load_default_table()
