@@ -25,6 +25,7 @@ along under "per_point".
 """
 
 import argparse
+import itertools
 import json
 import os
 import sys
@@ -427,9 +428,15 @@ def main(argv=None):
     achieved = tot_bytes / (tot_us * 1e-6) / 1e9
     traffic, traffic_note = recorded_traffic(wl.name, args.layout)
     if max(wl.ms) <= 32:
+        ceil_gbs = stream_ceiling(ql, per_point, stream, reps)
         roofline = {"kernel": "qgemm_decode_kernel", "bound": "hbm", "achieved": round(achieved, 1),
                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                     "traffic": traffic, "algorithmic_bytes": int(tot_bytes), "traffic_source": traffic_note,
+                    "stream_ceiling": {"achieved": round(ceil_gbs, 1), "frac": round(ceil_gbs / HBM_PEAK_GBS, 4),
+                                       "kernel_vs_ceiling": round(achieved / ceil_gbs, 4),
+                                       "note": "a plain streaming read of each point's kernel bytes "
+                                               "(qlinear_stream_read, best of 5 grids x 2 load depths), timed like the GEMMs; "
+                                               "per point under ceiling_us"},
                     "note": "algorithmic bytes of one launch of each of the %d GEMM kernels (a fused-"
                             "quantization launch also reads bf16 X and writes the codes and scales) / sum of "
                             "their per-launch durations (HIP events around graph replays of back-to-back "
@@ -483,6 +490,52 @@ def main(argv=None):
         with open(args.out, "w") as f:
             f.write(line + "\n")
     return 0
+
+
+def stream_ceiling(ql, per_point, stream, reps):
+    """The streaming-read ceiling of every point: the fastest plain read
+    (qlinear_stream_read, best of 5 grids x 2 load depths) of the point's kernel bytes,
+    timed as the GEMM is -- HIP events around graph replays of R back-to-back
+    launches on distinct offsets of a 1 GiB buffer, so the Infinity Cache
+    cannot serve it.  Sets per_point[i]["ceiling_us"]; returns the ceiling's
+    GB/s over all points (their bytes / their ceiling times)."""
+    import numpy as np
+    import torch
+    pool = torch.ones(1 << 30, dtype=torch.uint8, device="cuda")
+    sink = torch.empty(4096, dtype=torch.int32, device="cuda")
+    best = {}
+    for q in per_point:
+        nb = q["kernel_bytes"] // 16 * 16
+        if nb not in best:
+            span = -(-nb // 4096) * 4096
+            R = max(2, min(64, (1 << 30) // span))
+            times = []
+            for wg, lif in itertools.product((256, 512, 1024, 2048, 4096), (4, 8)):
+                with torch.cuda.stream(stream):
+                    ql.qlinear_graph_begin(stream)
+                    for c in range(R):
+                        ql.qlinear_stream_read(pool[c * span:], nb, wg, sink, loads_in_flight=lif, stream=stream)
+                    g = ql.qlinear_graph_end(stream)
+                for _ in range(3):
+                    g.launch(stream)
+                stream.synchronize()
+                samples = []
+                for _ in range(reps):
+                    e0 = torch.cuda.Event(enable_timing=True)
+                    e1 = torch.cuda.Event(enable_timing=True)
+                    e0.record(stream)
+                    g.launch(stream)
+                    e1.record(stream)
+                    e1.synchronize()
+                    samples.append(e0.elapsed_time(e1) * 1e3 / R)
+                times.append(float(np.median(samples)))
+                del g
+            best[nb] = min(times)
+        q["ceiling_us"] = round(best[nb], 3)
+    del pool
+    tot_b = sum(q["kernel_bytes"] for q in per_point)
+    tot_us = sum(best[q["kernel_bytes"] // 16 * 16] for q in per_point)
+    return tot_b / (tot_us * 1e-6) / 1e9
 
 
 def glu_pass(ql, wl, pts, shapes, stream, args):

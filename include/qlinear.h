@@ -220,6 +220,24 @@ ql_status qlinear_quantize_act_packed(int32_t fmt, const void* x_bf16, int64_t M
 ql_status qlinear_encode_e4m3(const float* x, int64_t n, void* codes, void* stream);
 
 /*
+ * Measurement aid, not part of the linear: read `bytes` bytes of device
+ * memory at `src` once with 16-byte nontemporal loads -- workgroup w of
+ * `workgroups` (256 threads each; 0 = 1024) reads the w-th contiguous slice,
+ * `loads_in_flight` (4 or 8; 0 = 8) loads per lane in flight.  Its time for
+ * a buffer the size of a GEMM's operands is the streaming-read ceiling a
+ * weight-streaming kernel is held against on this device (launch and ramp
+ * included, as for the GEMM).  With `check` nonzero every workgroup also
+ * writes the wrapping 32-bit sum of the words it read to sink[w] (a test of
+ * the read); with `check` zero the kernel writes nothing in practice (a lane
+ * writes its sum to sink[w] only if it equals a fixed constant, which keeps
+ * the loads from being elided).  bytes % 16 == 0 and bytes <= 2^36; src and
+ * sink device memory, 16-byte aligned; sink holds 4 * workgroups bytes.
+ * Enqueue-only.
+ */
+ql_status qlinear_stream_read(const void* src, int64_t bytes, int32_t workgroups, int32_t loads_in_flight,
+                              int32_t check, void* sink, void* stream);
+
+/*
  * Offline weight quantizer: per output channel (rows of W) or per 128x128
  * block for Block_FP8 (the last block row may be ragged).
  *   w_bf16 [N, K] in;  w_q [N, K] out;  w_scale fp32 [N] or [ceil(N/128), K/128]

@@ -203,6 +203,16 @@ def qlinear_encode_e4m3(x, codes, stream=None):
                                      _stream(stream)), "qlinear_encode_e4m3")
 
 
+def qlinear_stream_read(src, nbytes, workgroups, sink, loads_in_flight=8, check=False, stream=None):
+    """Measurement aid: read nbytes of src once (the streaming-read ceiling of a
+    buffer that size); with check, sink gets one wrapping 32-bit word sum per
+    workgroup."""
+    _need(src, "src", nbytes)
+    _need(sink, "sink", 4 * (workgroups or 1024))
+    _check(lib().qlinear_stream_read(_ptr(src, "src"), int(nbytes), int(workgroups), int(loads_in_flight),
+                                     int(bool(check)), _ptr(sink, "sink"), _stream(stream)), "qlinear_stream_read")
+
+
 def qlinear_packed_weight_bytes(N, K):
     return int(lib().qlinear_packed_weight_bytes(N, K))
 

@@ -18,7 +18,7 @@ OBJ = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libqlinear.so")
 
 SOURCES = ["quant.hip", "decode_fp8.hip", "decode_int8.hip", "decode_block.hip", "decode_mx.hip", "decode_mx4.hip", "tiled_fp8.hip",
-           "tiled_int8.hip", "tiled_block.hip", "tiled_mx.hip", "api.cpp"]
+           "tiled_int8.hip", "tiled_block.hip", "tiled_mx.hip", "stream_read.hip", "api.cpp"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

@@ -769,6 +769,23 @@ ql_status qlinear_encode_e4m3(const float* x, int64_t n, void* codes, void* stre
   return e == hipSuccess ? QL_OK : hip_fail(e, "E4M3 encoder launch");
 }
 
+ql_status qlinear_stream_read(const void* src, int64_t bytes, int32_t workgroups, int32_t loads_in_flight,
+                              int32_t check, void* sink, void* stream) {
+  if (bytes < 0 || bytes % 16 || bytes > (int64_t(1) << 36))
+    return fail(QL_E_INVALID, "bytes=%lld must be a multiple of 16 in [0, 2^36]", (long long)bytes);
+  if (workgroups == 0) workgroups = 1024;
+  if (workgroups < 1 || workgroups > 65536) return fail(QL_E_INVALID, "workgroups=%d outside [1, 65536]", workgroups);
+  if (loads_in_flight == 0) loads_in_flight = 8;
+  if (loads_in_flight != 4 && loads_in_flight != 8)
+    return fail(QL_E_INVALID, "loads_in_flight=%d must be 4 or 8", loads_in_flight);
+  if (!src || !sink) return fail(QL_E_INVALID, "NULL pointer");
+  if (!aligned16(src) || !aligned16(sink)) return fail(QL_E_ALIGN, "pointers must be 16-byte aligned");
+  hipError_t e = qlk::launch_stream_read(src, (uint64_t)bytes, workgroups, loads_in_flight, check != 0,
+                                         static_cast<uint32_t*>(sink),
+                                         static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? QL_OK : hip_fail(e, "stream read launch");
+}
+
 int64_t qlinear_packed_weight_bytes(int64_t N, int64_t K) {
   if (N < 0 || K < 0) return 0;
   return ((N + 15) / 16) * ((K + 127) / 128) * 2048;

@@ -102,6 +102,10 @@ hipError_t launch_quant_groups(const void* x, int64_t M, int64_t K, void* q, flo
 hipError_t launch_quant_wblocks(const void* w, int64_t N, int64_t K, void* q, float* s,
                                 hipStream_t st);
 hipError_t launch_fill_zero_bf16(void* y, int64_t count, hipStream_t st);
+// plain streaming read of `bytes` (a multiple of 16), a contiguous slice per workgroup with `unroll`
+// (4 or 8) loads in flight per lane; `check`: one 32-bit word sum per workgroup into sink
+hipError_t launch_stream_read(const void* src, uint64_t bytes, int workgroups, int unroll, bool check,
+                              uint32_t* sink, hipStream_t s);
 // MXFP8 rows: x bf16 [R, C] (C % 32 == 0) -> E4M3 codes (row-major [R, C],
 // or packed tiles when `packed`) and E8M0 scale bytes [R, C/32].
 hipError_t launch_quant_mx(const void* x, int64_t R, int64_t C, void* q, uint8_t* s, bool packed,

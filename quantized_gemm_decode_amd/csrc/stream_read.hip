@@ -1,0 +1,75 @@
+// A plain streaming read of device memory: the time a buffer of a GEMM's
+// operand size takes to cross from HBM with nothing else to do, on this
+// device.  A weight-streaming GEMM is measured against it (the HBM peak is
+// not reachable by any kernel at the sizes of decode GEMMs, where launch and
+// ramp take a fixed share).  Each workgroup reads a contiguous slice in
+// 16-byte nontemporal loads, 4 or 8 in flight per lane.  In its checking
+// mode each workgroup writes the wrapping 32-bit sum of the words it read, so
+// a test can check that every byte was read exactly once; the timing mode
+// writes nothing in practice.
+#include "decode_args.hpp"
+#include "device_common.hpp"
+
+namespace qlk {
+
+constexpr int kStreamThreads = 256;
+
+// Workgroup w reads the contiguous slice [w*per, min(n16, (w+1)*per)) of
+// 16-byte pieces, UNROLL pieces in flight per lane (a workgroup load covers
+// 4 KB, so UNROLL consecutive 4 KB spans are in flight per workgroup).
+// CHECK: every workgroup reduces its lanes' sums and writes one word.
+// Otherwise a lane writes its own sum only if it equals a fixed constant:
+// the loads stay live, and the kernel's end waits for no writes (a plain
+// read, as the ceiling should be).
+constexpr uint32_t kStreamMagic = 0x9E3779B9u;
+
+template <int UNROLL, bool CHECK>
+__global__ void __launch_bounds__(kStreamThreads) stream_read_kernel(const u32x4* __restrict__ p, uint64_t n16,
+                                                                      uint32_t* __restrict__ sink) {
+  const uint64_t per = (n16 + gridDim.x - 1) / gridDim.x;
+  const uint64_t b = (uint64_t)blockIdx.x * per;
+  const uint64_t e = b + per < n16 ? b + per : n16;
+  uint32_t acc = 0;
+  for (uint64_t i = b + threadIdx.x; i < e; i += (uint64_t)kStreamThreads * UNROLL) {
+    u32x4 v[UNROLL];
+#pragma unroll
+    for (int u = 0; u < UNROLL; ++u) {
+      const uint64_t j = i + (uint64_t)u * kStreamThreads;
+      v[u] = j < e ? __builtin_nontemporal_load(p + j) : u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int u = 0; u < UNROLL; ++u) acc += v[u].x + v[u].y + v[u].z + v[u].w;
+  }
+  if constexpr (CHECK) {
+    __shared__ uint32_t part[kStreamThreads / 64];
+    for (int o = 32; o > 0; o >>= 1) acc += (uint32_t)__shfl_xor((int)acc, o, 64);
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    if (lane == 0) part[wave] = acc;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      uint32_t s = 0;
+      for (int w = 0; w < kStreamThreads / 64; ++w) s += part[w];
+      sink[blockIdx.x] = s;
+    }
+  } else {
+    if (acc == kStreamMagic) sink[blockIdx.x] = acc;
+  }
+}
+
+hipError_t launch_stream_read(const void* src, uint64_t bytes, int workgroups, int unroll, bool check,
+                              uint32_t* sink, hipStream_t s) {
+  const u32x4* p = reinterpret_cast<const u32x4*>(src);
+  const dim3 grid((unsigned)workgroups), block(kStreamThreads);
+  const uint64_t n16 = bytes / 16u;
+  if (unroll == 4 && check)
+    hipLaunchKernelGGL((stream_read_kernel<4, true>), grid, block, 0, s, p, n16, sink);
+  else if (unroll == 4)
+    hipLaunchKernelGGL((stream_read_kernel<4, false>), grid, block, 0, s, p, n16, sink);
+  else if (check)
+    hipLaunchKernelGGL((stream_read_kernel<8, true>), grid, block, 0, s, p, n16, sink);
+  else
+    hipLaunchKernelGGL((stream_read_kernel<8, false>), grid, block, 0, s, p, n16, sink);
+  return hipGetLastError();
+}
+
+}  // namespace qlk
