@@ -125,3 +125,36 @@ def test_glu_plan_with_k_zero_writes_only_its_output(fmt):
     torch.cuda.synchronize()
     assert int(torch.count_nonzero(y)) == 0
     assert bool(torch.all(buf[M * (N // 2):] == 3.0))
+
+
+def _glu_case(i):
+    import random
+    rng = random.Random(700 + i)
+    fmt = FMTS[i % 3]
+    M = rng.choice([1, 2, 3, 5, 9, 16, 17, 24, 32])
+    I = 16 * rng.randint(1, 64)
+    K = 128 * rng.randint(1, 24) if fmt == ql.BLOCK_FP8 else 16 * rng.randint(8, 200)
+    return fmt, M, I, K, rng.choice([1, 2])
+
+
+GLU_CASES = [_glu_case(i) for i in range(24)]
+
+
+@pytest.mark.parametrize("fmt,M,I,K,a_packed", GLU_CASES,
+                         ids=["f%d_M%d_I%d_K%d_a%d" % c for c in GLU_CASES])
+def test_glu_table_free_plans_match_oracle(fmt, M, I, K, a_packed):
+    """SiLU-and-mul plans for shapes the table lacks (the heuristic's plan,
+    reshaped to the SiLU-and-mul kernels): gate/up weights [2I, K] against the
+    oracle, with quantized activations in (a_packed 1) or X in (2)."""
+    ql.qlinear_table_clear()
+    try:
+        plan = ql.qlinear_plan_glu(fmt, M, 2 * I, K, a_packed)
+    finally:
+        ql.load_default_table()
+    x, w = make_inputs(K, 2 * I, M, 0.02, seed=M * 7 + I + K)
+    xb = bf16_bits(x)
+    r = oracle.reference(fmt, xb, bf16_bits(w))
+    h, ws = _run_glu(plan, fmt, r, xb)
+    _check(fmt, r, h, plan, plan.config["waves_k"])
+    if ws is not None:
+        assert int(torch.count_nonzero(ws)) == 0
