@@ -267,8 +267,29 @@ std::vector<ql_config> tiled_candidates(int32_t fmt, int32_t layout, bool a_pack
 std::vector<ql_config> heuristic_candidates(int32_t fmt, int32_t layout, int a_class, int64_t M, int64_t N,
                                             int64_t K) {
   std::vector<ql_config> out;
-  if (M > 32 && !(is_mx(fmt) && M <= 64)) return tiled_candidates(fmt, layout, a_class != 0, M, N, K);
   const int64_t groups = (N + 15) / 16;
+  if (M > 32 && !(is_mx(fmt) && M <= 64)) {
+    // Up to 64 tokens the weight-streaming kernel with four token tiles beats
+    // the tiled one while the weights are few enough rows (measured 0.71-0.95x
+    // the tiled plan up to 448 row groups, even at 896, 1.4x at 1792);
+    // Block_FP8 has no four-token-tile instantiation.
+    std::vector<ql_config> out;
+    if (M <= 64 && fmt != QL_BLOCK_FP8 && layout == 1 && groups <= 512) {
+      ql_config d{};
+      d.algo = QL_ALGO_DECODE;
+      d.w_layout = 1;
+      d.a_mode = a_class != 0 ? 2 : 0;
+      d.swap_ab = 1;
+      d.split_k = 1;
+      d.rows_per_wave = 16;
+      d.prefetch = 2;
+      d.waves_n = groups <= 256 ? 1 : 2;
+      d.waves_k = groups <= 256 ? 4 : 2;
+      out.push_back(d);
+    }
+    for (const ql_config& c : tiled_candidates(fmt, layout, a_class != 0, M, N, K)) out.push_back(c);
+    return out;
+  }
   const int64_t G = (K + 127) / 128;
   ql_config b{};
   b.algo = QL_ALGO_DECODE;

@@ -293,10 +293,11 @@ def test_decode_plans_reach_64_tokens():
     assert _plan_status(ql.FP8_DYNAMIC, 65, 4096, 4096, **cfg) == QL_E_UNSUPPORTED
     p = ql.qlinear_plan_with_config(ql.FP8_DYNAMIC, 50, 4096, 4096, cfg)
     assert p.config["algo"] == ql.ALGO_DECODE and p.facts["threads"] == 256
-    # without a table entry the planner still sends M > 32 to the tiled kernel
+    # without a table entry M > 32 streams the weights while they are at most 512 row groups
     ql.qlinear_table_clear()
     try:
-        assert ql.qlinear_plan_layouts(ql.FP8_DYNAMIC, 50, 4096, 4096, 1, 1).config["algo"] == ql.ALGO_TILED
+        assert ql.qlinear_plan_layouts(ql.FP8_DYNAMIC, 50, 4096, 4096, 1, 1).config["algo"] == ql.ALGO_DECODE
+        assert ql.qlinear_plan_layouts(ql.FP8_DYNAMIC, 50, 16384, 4096, 1, 1).config["algo"] == ql.ALGO_TILED
     finally:
         ql.load_default_table()
 
@@ -403,10 +404,10 @@ def test_mxfp4_plans_and_sizes():
 
 
 @pytest.mark.parametrize("N,K,M,tile,split", [
-    (4096, 4096, 64, (64, 128), 4), (4096, 4096, 256, (64, 128), 1), (4096, 4096, 1024, (128, 128), 1),
+    (4096, 4096, 96, (64, 128), 4), (4096, 4096, 256, (64, 128), 1), (4096, 4096, 1024, (128, 128), 1),
     (4096, 4096, 4096, (256, 256), 1), (14336, 4096, 64, (64, 128), 1), (14336, 4096, 256, (128, 128), 1),
     (14336, 4096, 1024, (256, 256), 1), (4096, 14336, 256, (64, 128), 2), (28672, 4096, 256, (128, 256), 1),
-    (2048, 8192, 64, (64, 128), 4), (2048, 8192, 4096, (128, 256), 1)])
+    (2048, 8192, 96, (64, 128), 4), (2048, 8192, 4096, (128, 256), 1)])
 def test_tiled_heuristic_takes_the_largest_tile_that_fills_the_chip(N, K, M, tile, split):
     """Table-free tiled plans: the largest of 256 x 256, 128 x 256, 128 x 128
     and 64 x 128 that gives about 200 tiles, else 64 x 128 with split-K 4
@@ -440,5 +441,24 @@ def test_tiled_heuristic_block_fp8(N, K, M, cfg):
     try:
         c = ql.qlinear_plan_layouts(ql.BLOCK_FP8, M, N, K, 1, 1).config
         assert (c["tile_m"], c["tile_n"], c["prefetch"], c["swap_ab"], c["split_k"]) == cfg, c
+    finally:
+        ql.load_default_table()
+
+
+@pytest.mark.parametrize("N,K,waves", [(4096, 4096, (1, 4)), (2048, 8192, (1, 4)), (7168, 5120, (2, 2))])
+def test_table_free_plans_up_to_64_tokens_stream_the_weights(N, K, waves):
+    """32 < M <= 64 with packed weights and at most 512 row groups: the
+    weight-streaming kernel with four token tiles; more rows, row-major
+    weights or Block_FP8: the tiled kernel."""
+    ql.qlinear_table_clear()
+    try:
+        for M in (33, 40, 64):
+            for fmt in (ql.FP8_DYNAMIC, ql.W8A8_INT8):
+                c = ql.qlinear_plan_layouts(fmt, M, N, K, 1, 1).config
+                assert c["algo"] == ql.ALGO_DECODE and (c["waves_n"], c["waves_k"]) == waves, c
+                assert ql.qlinear_plan_layouts(fmt, M, N, K, 0, 0).config["algo"] == ql.ALGO_TILED
+            assert ql.qlinear_plan_layouts(ql.BLOCK_FP8, M, N, K, 1, 1).config["algo"] == ql.ALGO_TILED
+        assert ql.qlinear_plan_layouts(ql.FP8_DYNAMIC, 64, 28672, 4096, 1, 1).config["algo"] == ql.ALGO_TILED
+        assert ql.qlinear_plan_layouts(ql.FP8_DYNAMIC, 65, 4096, 4096, 1, 1).config["algo"] == ql.ALGO_TILED
     finally:
         ql.load_default_table()
