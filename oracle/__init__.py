@@ -31,20 +31,24 @@ Pins.  Every function here is checked in ``tests/test_oracle_*.py`` against
 something other than itself: an independent exact-rational (Fraction)
 implementation on tiny inputs, closed forms, layout one-hot probes, the OCP
 OFP8 specification's E4M3 values, torch's CPU float8 cast, the bf16 bit
-fields (MX shared exponents, exhaustively), and invariants of the method (variant order independence, quantizer bounds).  No function is
-"parity unpinned".
+fields (MX shared exponents, exhaustively), and invariants of the method (variant order independence, quantizer bounds).  The
+FP8 tolerance's matrix-core allowance (``matrix_core``) is pinned against a
+brute-force restatement of its model and, on the GPU, against the matrix
+instruction itself on adversarial operands.  No function is "parity
+unpinned".
 """
 
 from .fpbits import (bf16_bits_from_f32, bf16_bits_to_f32, ulp_bf16, f32)
 from .e4m3 import e4m3_encode, e4m3_decode, E4M3_MAX
 from .quant import (FMT_FP8_DYNAMIC, FMT_W8A8_INT8, FMT_BLOCK_FP8, FORMATS,
                     qmax_of, quantize_act, quantize_weight, dequant_codes)
-from .linear import (contract_exact, contract_abs, epilogue, reference, MATRIX_CORE_ETA,
-                     tolerance_bound, summation_depth, check_fp8_parity,
+from .linear import (contract_exact, contract_abs, epilogue, reference, Fp8Bound, accumulator_bound,
+                     tolerance_bound, summation_depth, check_fp8_parity, parity_statistics,
                      contract_split_order, contract_swap_ab,
                      emulate_fp32_accumulation)
 from .glu import silu, glu_values, glu_reference, SILU_SLOPE_MAX
-from .mx import (MX_BLOCK, mx_shared_exponent, mx_quantize, mx_dequantize, mx_contract_exact,
+from .matrix_core import allowance_pairs, allowance_full, e4m3_exponent, e2m1_exponent
+from .mx import (MxBound, MX_BLOCK, mx_shared_exponent, mx_quantize, mx_dequantize, mx_contract_exact,
                  mx_contract_abs, mx_tolerance_bound, mx_reference, e2m1_encode, e2m1_decode,
                  mx4_shared_exponent, mx4_quantize, mx4_contract_exact, mx4_tolerance_bound, mx4_reference)
 
@@ -54,7 +58,8 @@ __all__ = [
     "FMT_FP8_DYNAMIC", "FMT_W8A8_INT8", "FMT_BLOCK_FP8", "FORMATS",
     "qmax_of", "quantize_act", "quantize_weight", "dequant_codes",
     "contract_exact", "contract_abs", "epilogue", "reference",
-    "tolerance_bound", "summation_depth", "MATRIX_CORE_ETA", "check_fp8_parity",
+    "tolerance_bound", "summation_depth", "Fp8Bound", "accumulator_bound", "check_fp8_parity",
+    "parity_statistics", "allowance_pairs", "allowance_full", "e4m3_exponent", "e2m1_exponent", "MxBound",
     "silu", "glu_values", "glu_reference", "SILU_SLOPE_MAX",
     "contract_split_order", "contract_swap_ab", "emulate_fp32_accumulation",
     "MX_BLOCK", "mx_shared_exponent", "mx_quantize", "mx_dequantize", "mx_contract_exact",

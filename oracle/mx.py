@@ -126,13 +126,51 @@ def mx_contract_abs(a_codes, a_scales, w_codes, w_scales):
     return np.sum(np.ldexp(P, E), axis=0) if P.shape[0] else np.zeros(P.shape[1:])
 
 
-def mx_tolerance_bound(a_codes, a_scales, w_codes, w_scales, depth, eta):
-    """B[m, n] = (gamma_d + eta) * sum |scaled products| * (1 + 4u): the same
-    forward-error bound as the per-token FP8 formats (binary32 sums of depth
-    d plus the matrix instruction's per-instruction allowance eta), taken
-    over the products with their block scales applied."""
-    gamma = depth * U32 / (1.0 - depth * U32) + eta
-    return gamma * mx_contract_abs(a_codes, a_scales, w_codes, w_scales) * (1.0 + 4.0 * U32)
+class MxBound:
+    """The FP8 bound for an MX product, per element:
+
+        B[m, n] = (gamma_d * sum_b 2**(ea+ew) sum_{k in b} |a_k w_k| + allowance) * (1 + 4u)
+
+    -- binary32 sums of depth d, plus the matrix instruction's cut of small
+    products (``matrix_core``), both over the products with their block
+    scales applied (the scaled instruction multiplies exact products by exact
+    powers of two, then adds them as the unscaled one does; the block scale
+    shifts the alignment exponent).  ``fp4``: E2M1 weights.  The allowance
+    is evaluated only where asked (``at``)."""
+
+    def __init__(self, a_codes, a_scales, w_codes, w_scales, depth, matrix_core=True, fp4=False):
+        from .matrix_core import e2m1_exponent, e4m3_exponent
+        ea = np.asarray(a_scales, np.int64) - E8M0_BIAS
+        ew = np.asarray(w_scales, np.int64) - E8M0_BIAS
+        a = e4m3_decode(a_codes)
+        w = e2m1_decode(w_codes) if fp4 else e4m3_decode(w_codes)
+        self.av = a * np.repeat(np.ldexp(1.0, ea), MX_BLOCK, axis=1)
+        self.wv = w * np.repeat(np.ldexp(1.0, ew), MX_BLOCK, axis=1)
+        self.ea = (e4m3_exponent(a_codes) + np.repeat(ea, MX_BLOCK, axis=1)).astype(np.int16)
+        self.ew = ((e2m1_exponent(w_codes) if fp4 else e4m3_exponent(w_codes))
+                   + np.repeat(ew, MX_BLOCK, axis=1)).astype(np.int16)
+        self.matrix_core = matrix_core
+        gamma = depth * U32 / (1.0 - depth * U32)
+        self.base = gamma * (np.abs(self.av) @ np.abs(self.wv).T) * (1.0 + 4.0 * U32)
+        self.shape = self.base.shape
+
+    def at(self, mi, ni):
+        from .matrix_core import allowance_pairs
+        mi, ni = np.asarray(mi, np.int64), np.asarray(ni, np.int64)
+        b = self.base[mi, ni]
+        if self.matrix_core and mi.size:
+            b = b + allowance_pairs(self.av, self.ea, self.wv, self.ew, mi, ni).sum(axis=1) * (1.0 + 4.0 * U32)
+        return b
+
+    def full(self):
+        M, N = self.shape
+        mi, ni = np.meshgrid(np.arange(M), np.arange(N), indexing="ij")
+        return self.at(mi.reshape(-1), ni.reshape(-1)).reshape(M, N)
+
+
+def mx_tolerance_bound(a_codes, a_scales, w_codes, w_scales, depth, matrix_core=True):
+    """``MxBound`` for every element, float64 [M, N]."""
+    return MxBound(a_codes, a_scales, w_codes, w_scales, depth, matrix_core).full()
 
 
 # ----------------------------------------------------------------------------
@@ -207,16 +245,9 @@ def mx4_contract_exact(a_codes, a_scales, w_codes, w_scales):
                     dtype=np.float64).reshape(M, w.shape[0])
 
 
-def mx4_tolerance_bound(a_codes, a_scales, w_codes, w_scales, depth, eta):
-    """The MXFP8 bound with E2M1 weight values."""
-    a = np.abs(e4m3_decode(a_codes))
-    w = np.abs(e2m1_decode(w_codes))
-    nb = a.shape[1] // MX_BLOCK
-    P = np.stack([a[:, b * MX_BLOCK:(b + 1) * MX_BLOCK] @ w[:, b * MX_BLOCK:(b + 1) * MX_BLOCK].T
-                  for b in range(nb)])
-    absS = np.sum(np.ldexp(P, _scale_exponents(a_scales, w_scales)), axis=0)
-    gamma = depth * U32 / (1.0 - depth * U32) + eta
-    return gamma * absS * (1.0 + 4.0 * U32)
+def mx4_tolerance_bound(a_codes, a_scales, w_codes, w_scales, depth, matrix_core=True):
+    """The MXFP8 bound with E2M1 weight values, for every element."""
+    return MxBound(a_codes, a_scales, w_codes, w_scales, depth, matrix_core, fp4=True).full()
 
 
 def mx4_reference(x_bits, w_bits):

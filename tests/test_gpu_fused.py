@@ -15,7 +15,7 @@ import torch
 
 import oracle
 import quantized_gemm_decode_amd as ql
-from tests.gpu_util import dev_bf16, fp8_check, host_bf16_bits, pack_ref, requires_gpu
+from tests.gpu_util import dev_bf16, fp8_check, fp8_ok, host_bf16_bits, MIN_FRAC_WITHIN_ULP, pack_ref, requires_gpu
 from workloads import bf16_bits, make_inputs
 
 pytestmark = [pytest.mark.gpu, requires_gpu]
@@ -57,7 +57,7 @@ def _check(fmt, r, plan, a_p, a_s, y, label, waves_k=16):
         assert bad.size == 0, (label, bad[:5])
     else:
         st = fp8_check(fmt, r, y, plan.facts["chunks"], waves_k)
-        assert st["ok"] and st["frac_within_ulp"] >= 0.95, (label, st)
+        assert st["ok"] and st["frac_within_ulp"] >= MIN_FRAC_WITHIN_ULP, (label, st)
 
 
 def _weights(fmt, r):
@@ -118,7 +118,7 @@ def test_fused_special_rows(fmt):
         assert np.array_equal(y, r["y_ref"])
     else:
         st = fp8_check(fmt, r, y, 2, 2)
-        assert st["ok"], st
+        assert fp8_ok(st), st
 
 
 @pytest.mark.parametrize("fmt", FMTS)
@@ -141,7 +141,7 @@ def test_fused_equals_two_launch_forward(fmt, M, N, K):
     if fmt == ql.W8A8_INT8:
         assert np.array_equal(yf, yu) and np.array_equal(yf, r["y_ref"])
     else:
-        assert fp8_check(fmt, r, yf, 1, 4)["ok"] and fp8_check(fmt, r, yu, 1, 4)["ok"]
+        assert fp8_ok(fp8_check(fmt, r, yf, 1, 4)) and fp8_ok(fp8_check(fmt, r, yu, 1, 4))
 
 
 @pytest.mark.parametrize("fmt", FMTS)
@@ -175,7 +175,7 @@ def test_fused_graph_replays_match_eager(fmt):
         if fmt == ql.W8A8_INT8:
             assert torch.equal(y, eager), i
         else:
-            assert fp8_check(fmt, r, host_bf16_bits(y), 4)["ok"], i
+            assert fp8_ok(fp8_check(fmt, r, host_bf16_bits(y), 4)), i
         n = ql.qlinear_packed_act_bytes(M, K)
         assert np.array_equal(a_p[:n].view(torch.uint8).cpu().numpy(), pack_ref(_codes_u8(fmt, r["a_q"]))), i
         assert int(torch.count_nonzero(ws)) == 0

@@ -11,7 +11,7 @@ import torch
 
 import oracle
 import quantized_gemm_decode_amd as ql
-from tests.gpu_util import dev_bf16, host_bf16_bits, pack_ref, requires_gpu
+from tests.gpu_util import dev_bf16, host_bf16_bits, MIN_FRAC_WITHIN_ULP, pack_ref, requires_gpu
 from workloads import bf16_bits, make_inputs
 
 pytestmark = [pytest.mark.gpu, requires_gpu]
@@ -53,7 +53,7 @@ def _run_glu(plan, fmt, r, xb):
 def _check(fmt, r, h, plan, waves_k):
     h_ref, h_true, bound = oracle.glu_reference(fmt, r, split=plan.facts["chunks"], waves_k=waves_k)
     st = oracle.check_fp8_parity(h, h_ref, h_true, bound)
-    assert st["ok"] and st["frac_within_ulp"] >= 0.95, (plan.config, st)
+    assert st["ok"] and st["frac_within_ulp"] >= MIN_FRAC_WITHIN_ULP, (plan.config, st)
 
 
 @pytest.mark.parametrize("fmt", FMTS)
@@ -108,7 +108,7 @@ def test_glu_plan_on_the_gate_up_shape(fmt, M):
     r = oracle.reference(fmt, xb, bf16_bits(w[torch.from_numpy(rows)]))
     h_ref, h_true, bound = oracle.glu_reference(fmt, r, split=plan.facts["chunks"])
     st = oracle.check_fp8_parity(h[:, cols], h_ref, h_true, bound)
-    assert st["ok"] and st["frac_within_ulp"] >= 0.95, (plan.config, st)
+    assert st["ok"] and st["frac_within_ulp"] >= MIN_FRAC_WITHIN_ULP, (plan.config, st)
 
 
 @pytest.mark.parametrize("fmt", FMTS)

@@ -14,7 +14,8 @@ import torch
 import oracle
 import quantized_gemm_decode_amd as ql
 from oracle import mx
-from tests.gpu_util import dev_bf16, fp4_bytes, host_bf16_bits, pack_fp4_ref, pack_mx_scales_ref, pack_ref, requires_gpu
+from tests.gpu_util import (dev_bf16, fp4_bytes, host_bf16_bits, MIN_FRAC_WITHIN_ULP, pack_fp4_ref,
+                            pack_mx_scales_ref, pack_ref, requires_gpu)
 from workloads import bf16_bits, make_inputs
 
 pytestmark = [pytest.mark.gpu, requires_gpu]
@@ -48,7 +49,7 @@ def _acts(r):
 def _mx_check(r, y_bits, split, waves_k):
     K = r["a_q"].shape[1]
     d = oracle.summation_depth(K, split=split, waves_k=waves_k)
-    B = mx.mx_tolerance_bound(r["a_q"], r["s_a"], r["w_q"], r["s_w"], d, oracle.MATRIX_CORE_ETA)
+    B = mx.MxBound(r["a_q"], r["s_a"], r["w_q"], r["s_w"], d)
     return oracle.check_fp8_parity(y_bits, r["y_ref"], r["y_true"], B)
 
 
@@ -147,7 +148,7 @@ def test_every_mx_instantiation_matches_oracle(vi):
     a_p, a_s = _acts(r)
     y, ws = _run(plan, a_p, a_s, w_p, w_s)
     st = _mx_check(r, y, plan.facts["chunks"], wk)
-    assert st["ok"] and st["frac_within_ulp"] >= 0.95, (cfg, st)
+    assert st["ok"] and st["frac_within_ulp"] >= MIN_FRAC_WITHIN_ULP, (cfg, st)
     if ws is not None:
         assert int(torch.count_nonzero(ws)) == 0, "split-K workspace not left all-zero"
 
@@ -176,7 +177,7 @@ def test_mx_planner_plans_at_full_size(lab, N, K, M):
     ns = ql.qlinear_packed_mx_scale_bytes(M, K)
     assert np.array_equal(a_s.cpu().numpy()[:ns], pack_mx_scales_ref(r["s_a"], K))
     st = _mx_check(r, host_bf16_bits(y)[:, cols], plan.facts["chunks"], plan.config["waves_k"])
-    assert st["ok"] and st["frac_within_ulp"] >= 0.95, (plan.config, st)
+    assert st["ok"] and st["frac_within_ulp"] >= MIN_FRAC_WITHIN_ULP, (plan.config, st)
 
 
 def test_mx_forward_equals_quantize_then_run_and_graph_replays():
@@ -196,7 +197,7 @@ def test_mx_forward_equals_quantize_then_run_and_graph_replays():
     torch.cuda.synchronize()
     assert np.array_equal(host_bf16_bits(y), y_run)              # same codes, same kernel, split 1
     st = _mx_check(r, y_run, 1, 2)
-    assert st["ok"], st
+    assert st["ok"] and st["frac_within_ulp"] >= MIN_FRAC_WITHIN_ULP, st
     s = torch.cuda.Stream()
     with torch.cuda.stream(s):
         ql.qlinear_graph_begin(s)
@@ -223,7 +224,7 @@ def _weights4(r):
 def _mx4_check(r, y_bits, split, waves_k):
     K = r["a_q"].shape[1]
     d = oracle.summation_depth(K, split=split, waves_k=waves_k)
-    B = mx.mx4_tolerance_bound(r["a_q"], r["s_a"], r["w_q"], r["s_w"], d, oracle.MATRIX_CORE_ETA)
+    B = mx.MxBound(r["a_q"], r["s_a"], r["w_q"], r["s_w"], d, fp4=True)
     return oracle.check_fp8_parity(y_bits, r["y_ref"], r["y_true"], B)
 
 
@@ -295,7 +296,7 @@ def test_every_mx4_instantiation_matches_oracle(vi):
     a_p, a_s = _acts(r)
     y, ws = _run(plan, a_p, a_s, w_p, w_s)
     st = _mx4_check(r, y, plan.facts["chunks"], wk)
-    assert st["ok"] and st["frac_within_ulp"] >= 0.95, (cfg, st)
+    assert st["ok"] and st["frac_within_ulp"] >= MIN_FRAC_WITHIN_ULP, (cfg, st)
     if ws is not None:
         assert int(torch.count_nonzero(ws)) == 0, "split-K workspace not left all-zero"
 
@@ -318,7 +319,7 @@ def test_mx4_planner_plans_at_full_size(lab, N, K, M):
     cols = np.sort(np.random.default_rng(M + N + 1).choice(N, 64, replace=False))
     r = mx.mx4_reference(xb, wb[cols])
     st = _mx4_check(r, host_bf16_bits(y)[:, cols], plan.facts["chunks"], plan.config["waves_k"])
-    assert st["ok"] and st["frac_within_ulp"] >= 0.95, (plan.config, st)
+    assert st["ok"] and st["frac_within_ulp"] >= MIN_FRAC_WITHIN_ULP, (plan.config, st)
 
 
 # ---------------------------------------------------------------- MXFP8 beyond the decode range
@@ -346,7 +347,7 @@ def test_every_mx_tiled_instantiation_matches_oracle(vi):
     a_p, a_s = _acts(r)
     y, ws = _run(plan, a_p, a_s, w_p, w_s)
     st = _mx_check(r, y, plan.facts["chunks"], 1)
-    assert st["ok"] and st["frac_within_ulp"] >= 0.95, (cfg, st)
+    assert st["ok"] and st["frac_within_ulp"] >= MIN_FRAC_WITHIN_ULP, (cfg, st)
     if ws is not None:
         assert int(torch.count_nonzero(ws)) == 0, "split-K workspace not left all-zero"
 
@@ -369,4 +370,4 @@ def test_mx_planner_large_m_plans(M):
     rows = np.sort(rng.choice(M, min(M, 128), replace=False))
     r = mx.mx_reference(bf16_bits(x[torch.from_numpy(rows)]), bf16_bits(w[torch.from_numpy(cols)]))
     st = _mx_check(r, host_bf16_bits(y)[np.ix_(rows, cols)], plan.facts["chunks"], 1)
-    assert st["ok"] and st["frac_within_ulp"] >= 0.95, (plan.config, st)
+    assert st["ok"] and st["frac_within_ulp"] >= MIN_FRAC_WITHIN_ULP, (plan.config, st)

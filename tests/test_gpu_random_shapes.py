@@ -18,7 +18,7 @@ import torch
 
 import oracle
 import quantized_gemm_decode_amd as ql
-from tests.gpu_util import fp8_check, host_bf16_bits, host_codes, pack_ref, requires_gpu
+from tests.gpu_util import fp8_check, fp8_ok, host_bf16_bits, host_codes, pack_ref, requires_gpu
 from workloads import bf16_bits, make_inputs
 
 pytestmark = [pytest.mark.gpu, requires_gpu]
@@ -66,7 +66,7 @@ def test_random_shape_forward_matches_oracle(fmt, M, N, K, layout):
         assert np.array_equal(host_bf16_bits(y), r["y_ref"]), label
     else:
         st = fp8_check(fmt, r, host_bf16_bits(y), plan.facts["chunks"])
-        assert st["ok"], (label, st)
+        assert fp8_ok(st), (label, st)
 
 
 # ---------------------------------------------------------------- MXFP8 / MXFP4
@@ -109,7 +109,6 @@ def test_random_shape_mx_forward_matches_oracle(fmt, M, N, K, layout):
                           pack_mx_scales_ref(r["s_a"], K)), label
     waves_k = cfg["waves_k"] if cfg["algo"] == ql.ALGO_DECODE else 1
     d = oracle.summation_depth(K, split=plan.facts["chunks"], waves_k=waves_k)
-    bound = (mx.mx_tolerance_bound if fmt == ql.MXFP8 else mx.mx4_tolerance_bound)(
-        r["a_q"], r["s_a"], r["w_q"], r["s_w"], d, oracle.MATRIX_CORE_ETA)
+    bound = mx.MxBound(r["a_q"], r["s_a"], r["w_q"], r["s_w"], d, fp4=fmt == ql.MXFP4)
     st = oracle.check_fp8_parity(host_bf16_bits(y), r["y_ref"], r["y_true"], bound)
-    assert st["ok"], (label, st)
+    assert fp8_ok(st), (label, st)

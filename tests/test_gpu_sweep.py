@@ -9,7 +9,7 @@ import torch
 import oracle
 import quantized_gemm_decode_amd as ql
 from quantized_gemm_decode_amd import sweep
-from tests.gpu_util import fp8_check, host_bf16_bits, requires_gpu
+from tests.gpu_util import fp8_check, fp8_ok, host_bf16_bits, requires_gpu
 from workloads import bf16_bits, make_inputs
 
 pytestmark = [pytest.mark.gpu, requires_gpu]
@@ -42,6 +42,6 @@ def test_sweep_one_shape_then_plan_from_its_table(fmt, tmp_path):
         if fmt == ql.W8A8_INT8:
             assert np.array_equal(host_bf16_bits(y), r["y_ref"])
         else:
-            assert fp8_check(fmt, r, host_bf16_bits(y), plan.facts["chunks"])["ok"]
+            assert fp8_ok(fp8_check(fmt, r, host_bf16_bits(y), plan.facts["chunks"]))
     finally:
         ql.load_default_table()

@@ -13,7 +13,7 @@ import pytest
 
 import oracle
 import quantized_gemm_decode_amd as ql
-from tests.gpu_util import fp8_check, requires_gpu
+from tests.gpu_util import fp8_check, fp8_ok, requires_gpu
 from workloads import bf16_bits, config_by_name, make_inputs
 
 HERE = os.path.dirname(os.path.abspath(__file__))
@@ -71,4 +71,4 @@ def test_c_consumer_runs_one_linear(tmp_path, wname, fmt, M, N, K):
             chunks = ql.qlinear_plan(fmt, M, N, K).facts["chunks"]
         finally:
             ql.load_default_table()
-        assert fp8_check(fmt, ref, y, chunks)["ok"]
+        assert fp8_ok(fp8_check(fmt, ref, y, chunks))

@@ -330,8 +330,8 @@ def test_tolerance_accepts_emulated_fp32_orders_and_rejects_dropped_tile(fmt):
         order = rng.permutation(len(bounds) - 1).tolist()
         yb = oracle.emulate_fp32_accumulation(fmt, r["a_q"], r["w_q"], r["s_a"], r["s_w"], bounds, order, rng)
         d = oracle.summation_depth(K, split=len(bounds) - 1)
-        for eta in (0.0, oracle.MATRIX_CORE_ETA):      # binary32-only bound, and with the matrix-core term
-            B = oracle.tolerance_bound(fmt, r["a_q"], r["w_q"], r["s_a"], r["s_w"], d, eta=eta)
+        for mc in (False, True):      # binary32-only bound, and with the matrix-core allowance
+            B = oracle.tolerance_bound(fmt, r["a_q"], r["w_q"], r["s_a"], r["s_w"], d, matrix_core=mc)
             st = oracle.check_fp8_parity(yb, r["y_ref"], r["y_true"], B)
             assert st["ok"], st
     # a kernel that drops one 128-wide K tile must fail on nearly every element

@@ -174,7 +174,7 @@ def test_tolerance_accepts_binary32_order_and_rejects_a_dropped_block():
     x, w = make_inputs(K, N, M, 0.02, seed=13)
     r = mx.mx_reference(bf16_bits(x), bf16_bits(w))
     depth = oracle.summation_depth(K, split=2, waves_k=4)
-    B = mx.mx_tolerance_bound(r["a_q"], r["s_a"], r["w_q"], r["s_w"], depth, oracle.MATRIX_CORE_ETA)
+    B = mx.mx_tolerance_bound(r["a_q"], r["s_a"], r["w_q"], r["s_w"], depth)
     a = mx.mx_dequantize(r["a_q"], r["s_a"])
     wd = mx.mx_dequantize(r["w_q"], r["s_w"])
     # binary32 evaluation: exact 128-K steps, added in binary32 in K order
@@ -268,8 +268,7 @@ def test_mx4_tolerance_accepts_binary32_order_and_rejects_a_dropped_block():
     M, N, K = 8, 64, 2048
     x, w = make_inputs(K, N, M, 0.02, seed=15)
     r = mx.mx4_reference(bf16_bits(x), bf16_bits(w))
-    B = mx.mx4_tolerance_bound(r["a_q"], r["s_a"], r["w_q"], r["s_w"], oracle.summation_depth(K, 2, 4),
-                               oracle.MATRIX_CORE_ETA)
+    B = mx.mx4_tolerance_bound(r["a_q"], r["s_a"], r["w_q"], r["s_w"], oracle.summation_depth(K, 2, 4))
     a = mx.mx_dequantize(r["a_q"], r["s_a"])
     wd = (oracle.e2m1_decode(r["w_q"]).reshape(N, -1, 32)
           * np.ldexp(1.0, r["s_w"].astype(int) - 127)[:, :, None]).reshape(N, K)
