@@ -115,11 +115,11 @@ def is_fused_instantiation(name):
     return len(args) == 9 and args[6].strip() == "4"
 
 
-def pmc_summary(workload, layout, fetch_csv, write_csv):
-    """Summarise two rocprofv3 --pmc runs of --profile-pass into the traffic record."""
+def pmc_summary(wls, layout, fetch_csv, write_csv):
+    """Summarise two rocprofv3 --pmc runs of --profile-pass into one traffic
+    record per workload; returns {workload name: text}."""
     import csv
-    from workloads import config_by_name, decode_points
-    wl = config_by_name(workload)
+    from workloads import decode_points
 
     def load(path):
         rows = list(csv.DictReader(open(path)))
@@ -134,36 +134,44 @@ def pmc_summary(workload, layout, fetch_csv, write_csv):
     kf, kw = cal / fetch_copy, cal / write_copy
     gem = [(float(a["Counter_Value"]), float(b["Counter_Value"]), a["Kernel_Name"].split("(")[0])
            for a, b in zip(fr, wr) if "qgemm" in a["Kernel_Name"]]
-    pts = decode_points(wl)
-    gem = gem[-3 * len(pts):]
-    lines = ["# HBM traffic of the decode GEMM kernels, workload %s, %s" % (workload, LAYOUT_NAMES[layout]),
-             "# commands (run from /tmp with TMPDIR=/tmp):",
-             "#   rocprofv3 --pmc FETCH_SIZE -f csv -d <dir_f> -o fetch -- python3 <repo>/bench.py --workload %s "
-             "--layout %s --profile-pass" % (workload, layout),
-             "#   rocprofv3 --pmc WRITE_SIZE -f csv -d <dir_w> -o write -- python3 <repo>/bench.py --workload %s "
-             "--layout %s --profile-pass" % (workload, layout),
-             "#   python3 bench.py --workload %s --layout %s --pmc-summary <dir_f>/fetch_counter_collection.csv "
-             "<dir_w>/write_counter_collection.csv" % (workload, layout),
-             "# calibration: a 256 MiB device copy reads FETCH_SIZE %.1f KiB and WRITE_SIZE %.1f KiB per dispatch"
-             % (fetch_copy, write_copy),
-             "#   -> bytes = FETCH_SIZE * %.4f KiB, WRITE_SIZE * %.4f KiB" % (kf, kw),
-             "# per GEMM: mean of 3 dispatches on distinct weight copies (a fused-quantization launch's",
-             "# algorithmic bytes include bf16 X in and the codes and scales out)",
-             "# shape    M    algorithmic_B   fetched_B  written_B  traffic/alg"]
-    tot_a = tot_t = 0
-    for i, (lab, N, K, M) in enumerate(pts):
-        g = gem[3 * i:3 * i + 3]
-        fb = sum(x[0] for x in g) / 3 * 1024 * kf
-        wb = sum(x[1] for x in g) / 3 * 1024 * kw
-        ab = (fused_kernel_bytes if is_fused_instantiation(g[0][2]) else algorithmic_bytes)(wl.fmt, M, N, K)
-        tot_a += ab
-        tot_t += fb + wb
-        lines.append("# %-8s %-4d %13d %11.0f %10.0f  %.4f" % (lab, M, ab, fb, wb, (fb + wb) / ab))
-    lines += ["kernel_sources_sha256 %s" % kernel_sources_digest(),
-              "algorithmic_bytes_per_step %d" % tot_a,
-              "traffic_bytes_per_step %d" % round(tot_t),
-              "traffic_over_algorithmic %.4f" % (tot_t / tot_a)]
-    return "\n".join(lines) + "\n"
+    n_all = sum(3 * len(decode_points(wl)) for wl in wls)
+    gem = gem[-n_all:]
+    names = ",".join(wl.name for wl in wls) if len(wls) > 1 or wls[0].name not in DECODE_SET else wls[0].name
+    if [wl.name for wl in wls] == list(DECODE_SET):
+        names = "decode"
+    out, at = {}, 0
+    for wl in wls:
+        pts = decode_points(wl)
+        lines = ["# HBM traffic of the decode GEMM kernels, workload %s, %s" % (wl.name, LAYOUT_NAMES[layout]),
+                 "# commands (run from /tmp with TMPDIR=/tmp):",
+                 "#   rocprofv3 --pmc FETCH_SIZE -f csv -d <dir_f> -o fetch -- python3 <repo>/bench.py --workload %s "
+                 "--layout %s --profile-pass" % (names, layout),
+                 "#   rocprofv3 --pmc WRITE_SIZE -f csv -d <dir_w> -o write -- python3 <repo>/bench.py --workload %s "
+                 "--layout %s --profile-pass" % (names, layout),
+                 "#   python3 bench.py --workload %s --layout %s --pmc-summary <dir_f>/fetch_counter_collection.csv "
+                 "<dir_w>/write_counter_collection.csv" % (names, layout),
+                 "# calibration: a 256 MiB device copy reads FETCH_SIZE %.1f KiB and WRITE_SIZE %.1f KiB per "
+                 "dispatch" % (fetch_copy, write_copy),
+                 "#   -> bytes = FETCH_SIZE * %.4f KiB, WRITE_SIZE * %.4f KiB" % (kf, kw),
+                 "# per GEMM: mean of 3 dispatches on distinct weight copies (a fused-quantization launch's",
+                 "# algorithmic bytes include bf16 X in and the codes and scales out)",
+                 "# shape    M    algorithmic_B   fetched_B  written_B  traffic/alg"]
+        tot_a = tot_t = 0
+        for (lab, N, K, M) in pts:
+            g = gem[at:at + 3]
+            at += 3
+            fb = sum(x[0] for x in g) / 3 * 1024 * kf
+            wb = sum(x[1] for x in g) / 3 * 1024 * kw
+            ab = (fused_kernel_bytes if is_fused_instantiation(g[0][2]) else algorithmic_bytes)(wl.fmt, M, N, K)
+            tot_a += ab
+            tot_t += fb + wb
+            lines.append("# %-8s %-4d %13d %11.0f %10.0f  %.4f" % (lab, M, ab, fb, wb, (fb + wb) / ab))
+        lines += ["kernel_sources_sha256 %s" % kernel_sources_digest(),
+                  "algorithmic_bytes_per_step %d" % tot_a,
+                  "traffic_bytes_per_step %d" % round(tot_t),
+                  "traffic_over_algorithmic %.4f" % (tot_t / tot_a)]
+        out[wl.name] = "\n".join(lines) + "\n"
+    return out
 
 
 def trace_summary(workload, layout, trace_csv, stats_csv, bench_json, ref_json=None):
@@ -176,11 +184,13 @@ def trace_summary(workload, layout, trace_csv, stats_csv, bench_json, ref_json=N
     for line in open(bench_json):
         if line.startswith("{"):
             bench = json.loads(line)
-    pp = bench["per_point"]
-    # The per-point timing phase ends the run: for each point a block of
-    # (3 warm-up + kernel-reps timed) graph replays of R GEMM launches, in
-    # point order (the unfused points' quantizer runs between blocks and is
-    # skipped).  Slice the GEMM launches by those counts from the end.
+    blocks = bench["workloads"]
+    pp = [dict(q, workload=b["workload"]) for b in blocks for q in b["per_point"]]
+    # After the timed steps, each workload's per-point phase launches, for
+    # each point, (3 warm-up + kernel-reps timed) graph replays of R GEMM
+    # launches, in point order; quantizer and streaming-read timings follow
+    # but launch no GEMM.  So the GEMM launches of the per-point phases are
+    # the last ones of the run: slice them by those counts from the end.
     reps = bench.get("kernel_reps", 5)
     gemm = [r for r in rows if "qgemm" in r["Kernel_Name"]]
     sizes = [(3 + reps) * p["R"] for p in pp]
@@ -189,7 +199,8 @@ def trace_summary(workload, layout, trace_csv, stats_csv, bench_json, ref_json=N
     for n in sizes:
         runs.append((tail[at:at + n], n * reps // (3 + reps)))
         at += n
-    lines = ["# rocprofv3 kernel trace of the GEMM kernels, workload %s, %s" % (workload, LAYOUT_NAMES[layout]),
+    lines = ["# rocprofv3 kernel trace of the GEMM kernels, workload %s, %s"
+             % (bench["config"]["workload"], LAYOUT_NAMES[layout]),
              "# command (from /tmp with TMPDIR=/tmp):",
              "#   rocprofv3 --kernel-trace --stats -f csv -d <dir> -o bench -- python3 <repo>/bench.py --workload %s "
              "--layout %s --steps %d --warmup %d --kernel-reps %d --no-cpu-baseline"
@@ -199,7 +210,8 @@ def trace_summary(workload, layout, trace_csv, stats_csv, bench_json, ref_json=N
              % (workload, layout),
              "# per point: rocprof = mean kernel duration over the timed replays (last kernel-reps x R launches);",
              "# hip_events = the same run's HIP-event time per launch (median of replays / R)",
-             "# shape    M    kernel_instantiation                                   rocprof_us  hip_events_us  ratio"]
+             "# workload               shape    M    kernel_instantiation                                   "
+             "rocprof_us  hip_events_us  ratio"]
     tot_r = tot_e = 0.0
     per_us = []
     for p, (run, n_timed) in zip(pp, runs):
@@ -209,7 +221,8 @@ def trace_summary(workload, layout, trace_csv, stats_csv, bench_json, ref_json=N
         tot_r += us
         tot_e += p["us"]
         per_us.append(us)
-        lines.append("# %-8s %-4d %-54s %9.3f %13.3f  %.3f" % (p["shape"], p["M"], name, us, p["us"], p["us"] / us))
+        lines.append("# %-22s %-8s %-4d %-54s %9.3f %13.3f  %.3f" % (p["workload"], p["shape"], p["M"], name, us,
+                                                                   p["us"], p["us"] / us))
     lines.append("# sum over the %d points: rocprof %.2f us, hip events %.2f us (ratio %.3f)" % (len(pp), tot_r, tot_e,
                                                                                               tot_e / tot_r))
     rl = bench["roofline"]
@@ -224,8 +237,8 @@ def trace_summary(workload, layout, trace_csv, stats_csv, bench_json, ref_json=N
                  % (what, ach, rl["unit"], rl["achieved"], rl["unit"]))
     if ref_json:
         ref = json.loads(open(ref_json).read().strip().splitlines()[-1])
-        ref_pp = {(q["shape"], q["M"]): q["us"] for q in ref["per_point"]}
-        tot_ref = sum(ref_pp.get((p["shape"], p["M"]), float("nan")) for p in pp)
+        ref_pp = {(b["workload"], q["shape"], q["M"]): q["us"] for b in ref["workloads"] for q in b["per_point"]}
+        tot_ref = sum(ref_pp.get((p["workload"], p["shape"], p["M"]), float("nan")) for p in pp)
         lines.append("# the same bench without the profiler (%s): roofline.achieved %.1f %s; its per-launch "
                      "times sum to %.2f us, %.3f x the rocprof kernel durations above"
                      % (os.path.basename(ref_json), ref["roofline"]["achieved"], ref["roofline"]["unit"], tot_ref,
@@ -241,7 +254,10 @@ def parse_args(argv=None):
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="fp8_dynamic_8b")
+    ap.add_argument("--workload", default="decode",
+                    help="'decode' (default): the INT8 4096x2048 linear, the FP8_Dynamic and Block_FP8 8B-class "
+                         "sweeps and the W8A8_INT8 32B-class sweep, timed together; or one or more workload "
+                         "names, comma-separated (e.g. fp8_dynamic_14b_large_m, mxfp8_8b)")
     ap.add_argument("--layout", choices=("fused", "packed", "packedw", "rowmajor"), default="fused",
                     help="fused: packed weights (qlinear_pack_weight, offline) and each point's forward plan, "
                          "with the quantizer fused into the GEMM where the sweep found that faster; packed: "
@@ -249,7 +265,7 @@ def parse_args(argv=None):
                          "packed weights only; rowmajor: row-major both")
     ap.add_argument("--kernel-reps", type=int, default=30, help="graph replays per point for kernel timing")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-budget-s", type=float, default=20.0)
+    ap.add_argument("--cpu-budget-s", type=float, default=24.0, help="CPU oracle seconds, split over the workloads")
     ap.add_argument("--table", default=None, help="sweep table path (default: the packaged table)")
     ap.add_argument("--out", default=None, help="also write the JSON line to this file")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -267,46 +283,52 @@ def parse_args(argv=None):
     return ap.parse_args(argv)
 
 
-def main(argv=None):
-    args = parse_args(argv)
-    if args.gpus != 1:
-        print("bench.py measures one GPU only (--gpus %d requested); the linear shards "
-              "column-wise across GPUs with no exchange, so per-GPU work is one GPU's share." % args.gpus,
-              file=sys.stderr)
-        return 2
+# The decode workloads a default run measures together: the INT8 single
+# linear (4096x2048 at M = 8), the FP8_Dynamic and Block_FP8 8B-class sweeps
+# and the W8A8_INT8 32B-class sweep -- the fp8 / int8 decode shapes of the metric.
+DECODE_SET = ("int8_linear_4096x2048", "fp8_dynamic_8b", "block_fp8_8b", "int8_32b")
 
-    if args.trace_summary:
-        sys.stdout.write(trace_summary(args.workload, args.layout, *args.trace_summary, ref_json=args.trace_ref))
-        return 0
-    if args.pmc_summary:
-        sys.stdout.write(pmc_summary(args.workload, args.layout, *args.pmc_summary))
-        return 0
 
-    import numpy as np
-    import torch
+def resolve_workloads(name):
+    from workloads import config_by_name
+    names = DECODE_SET if name == "decode" else tuple(name.split(","))
+    return [config_by_name(n) for n in names]
 
-    import quantized_gemm_decode_amd as ql
-    from workloads import config_by_name, decode_points, make_inputs
 
-    if not os.path.exists(os.path.join(ROOT, "quantized_gemm_decode_amd", "libqlinear.so")):
-        from quantized_gemm_decode_amd import build as b
-        b.build()
-    torch.cuda.set_device(0)
-    n_table = ql.qlinear_table_load(args.table) if args.table else ql.load_default_table()
+def environment(ql, torch):
+    """Versions of what the numbers were measured on."""
+    import hashlib
+    env = {"torch": torch.__version__, "hip": getattr(torch.version, "hip", None)}
+    try:
+        prop = torch.cuda.get_device_properties(0)
+        env["gpu"] = prop.name
+        env["gcn_arch"] = getattr(prop, "gcnArchName", None)
+        env["compute_units"] = prop.multi_processor_count
+    except Exception as e:      # informational only
+        env["gpu"] = "unknown (%s)" % e
+    for path in ("/opt/rocm/.info/version", "/opt/rocm/.info/version-dev"):
+        if os.path.exists(path):
+            env["rocm"] = open(path).read().strip()
+            break
+    env["library_version"] = int(ql.lib().qlinear_version())
+    table = os.path.join(PKG, "tables", "decode_table.txt")
+    if os.path.exists(table):
+        env["table_sha256_16"] = hashlib.sha256(open(table, "rb").read()).hexdigest()[:16]
+    env["kernel_sources_sha256_16"] = kernel_sources_digest()[:16]
+    return env
 
-    wl = config_by_name(args.workload)
+
+def prepare_workload(ql, torch, wl, layout, dev):
+    """Weights (quantized on the GPU, packed offline, >= 1 GiB of copies per
+    shape), activations and one plan + buffers per point."""
+    from workloads import decode_points, make_inputs
     fmt = wl.fmt
-    points = decode_points(wl)
-    dev = "cuda"
-    stream = torch.cuda.Stream()
-
-    # ------------------------------------------------ inputs, weights, copies
     shapes = {}
     for (lab, N, K) in wl.shapes:
         x, w = make_inputs(K, N, max(wl.ms), wl.sigma_w, seed=wl.seed)
         wd = w.to(dev)
         w_q, w_s = ql.quantize_weight(fmt, wd)
-        if args.layout != "rowmajor":           # offline, like the quantization itself
+        if layout != "rowmajor":              # offline, like the quantization itself
             w_q = ql.pack_weight_fp4(w_q) if fmt == ql.MXFP4 else ql.pack_weight(w_q)
             if fmt in ql.MX_FORMATS:
                 w_s = ql.pack_mx_scales(w_s)   # MX plans read the scales in lane order
@@ -318,12 +340,10 @@ def main(argv=None):
         ws_all[:] = w_s
         shapes[lab] = dict(N=N, K=K, x=x.to(dev), wq=wq_all, ws=ws_all, copies=copies)
     torch.cuda.synchronize()
-
-    # ------------------------------------------------ per-point plans and buffers
     pts = []
-    for (lab, N, K, M) in points:
+    for (lab, N, K, M) in decode_points(wl):
         sh = shapes[lab]
-        w_layout, a_packed = LAYOUT_PLAN[args.layout]
+        w_layout, a_packed = LAYOUT_PLAN[layout]
         plan = ql.qlinear_plan_layouts(fmt, M, N, K, w_layout, a_packed)
         cfg, facts = plan.info()
         fused = cfg["algo"] == ql.ALGO_DECODE and cfg["a_mode"] == 4
@@ -335,50 +355,65 @@ def main(argv=None):
                         wsp=plan.new_workspace(dev), fused=fused,
                         bytes=algorithmic_bytes(fmt, M, N, K), qbytes=quantizer_bytes(fmt, M, K),
                         kbytes=fused_kernel_bytes(fmt, M, N, K) if fused else algorithmic_bytes(fmt, M, N, K)))
+    return dict(wl=wl, fmt=fmt, shapes=shapes, pts=pts)
 
-    if args.profile_pass:
-        return profile_pass(ql, fmt, pts, shapes, stream)
-    if args.glu:
-        return glu_pass(ql, wl, pts, shapes, stream, args)
 
-    # ------------------------------------------------ step graphs (quantize + GEMM per point)
-    n_graphs = 8
+def step_graphs(ql, W, stream, n_graphs=8):
+    """hipGraphs of one step of a workload (every point's quantize + GEMM),
+    each graph on its own weight copies."""
     graphs = []
-    with torch.cuda.stream(stream):
-        for gi in range(n_graphs):
-            ql.qlinear_graph_begin(stream)
-            for pi, p in enumerate(pts):
-                sh = shapes[p["lab"]]
-                c = (gi * len(pts) + pi) % sh["copies"]
-                ql.qlinear_forward(p["plan"], p["x"], p["a_q"], p["a_s"], sh["wq"][c], sh["ws"][c], p["y"],
-                                   p["wsp"], stream=stream)
-            graphs.append(ql.qlinear_graph_end(stream))
-    stream.synchronize()
+    pts, shapes = W["pts"], W["shapes"]
+    for gi in range(n_graphs):
+        ql.qlinear_graph_begin(stream)
+        for pi, p in enumerate(pts):
+            sh = shapes[p["lab"]]
+            c = (gi * len(pts) + pi) % sh["copies"]
+            ql.qlinear_forward(p["plan"], p["x"], p["a_q"], p["a_s"], sh["wq"][c], sh["ws"][c], p["y"],
+                               p["wsp"], stream=stream)
+        graphs.append(ql.qlinear_graph_end(stream))
+    return graphs
 
-    for i in range(args.warmup):
-        graphs[i % n_graphs].launch(stream)
-    stream.synchronize()
+
+def time_steps(torch, graph_sets, steps, stream):
+    """HIP-event ms per step, a step replaying one graph of every workload."""
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
+    stream.synchronize()
     t0.record(stream)
-    wall0 = time.perf_counter()
-    for i in range(args.steps):
-        graphs[i % n_graphs].launch(stream)
+    for i in range(steps):
+        for gs in graph_sets:
+            gs[i % len(gs)].launch(stream)
     t1.record(stream)
     stream.synchronize()
-    wall = time.perf_counter() - wall0
-    step_ms = t0.elapsed_time(t1) / args.steps
-    step_bytes = sum(p["bytes"] + p["qbytes"] for p in pts)
-    value = step_bytes / (step_ms * 1e-3) / 1e9
+    return t0.elapsed_time(t1) / steps
 
-    # ------------------------------------------------ per-point GEMM kernel timing (HIP events)
-    # R back-to-back launches of the point's GEMM kernel: qlinear_run, or for a
-    # fused plan qlinear_forward (which is that one kernel launch)
-    reps = args.kernel_reps
+
+def graph_us(torch, np, g, R, reps, stream):
+    """Median / p10 / p90 per-launch µs of a graph of R launches (HIP events)."""
+    for _ in range(3):
+        g.launch(stream)
+    stream.synchronize()
+    samples = []
+    for _ in range(reps):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        g.launch(stream)
+        e1.record(stream)
+        e1.synchronize()
+        samples.append(e0.elapsed_time(e1) * 1e3 / R)
+    return float(np.median(samples)), float(np.percentile(samples, 10)), float(np.percentile(samples, 90))
+
+
+def point_timing(ql, torch, np, W, stream, reps):
+    """Per point: a hipGraph of R back-to-back launches of the point's GEMM
+    kernel (qlinear_run, or for a fused plan qlinear_forward, which is that one
+    kernel) on distinct weight copies; then, for an unfused point, R launches
+    of its activation quantizer alone."""
+    fmt = W["fmt"]
     per_point = []
-    tot_bytes = tot_us = tot_flops = 0.0
-    for p in pts:
-        sh = shapes[p["lab"]]
+    for p in W["pts"]:
+        sh = W["shapes"][p["lab"]]
         R = min(sh["copies"], 64)
         with torch.cuda.stream(stream):
             ql.qlinear_graph_begin(stream)
@@ -390,75 +425,182 @@ def main(argv=None):
                     ql.qlinear_run(p["plan"], p["a_q"], p["a_s"], sh["wq"][c], sh["ws"][c], p["y"], p["wsp"],
                                    stream=stream)
             g = ql.qlinear_graph_end(stream)
-            if p["fused"]:
-                pass
-            elif p["cfg"]["a_mode"] >= 2:
-                ql.qlinear_quantize_act_packed(fmt, p["x"], p["a_q"], p["a_s"], stream=stream)
-            else:
-                ql.qlinear_quantize_act(fmt, p["x"], p["a_q"], p["a_s"], stream=stream)
-        for _ in range(3):
-            g.launch(stream)
-        stream.synchronize()
-        samples = []
-        for _ in range(reps):
-            e0 = torch.cuda.Event(enable_timing=True)
-            e1 = torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-            g.launch(stream)
-            e1.record(stream)
-            e1.synchronize()
-            samples.append(e0.elapsed_time(e1) * 1e3 / R)
-        us = float(np.median(samples))
+            if not p["fused"]:        # the codes the GEMM reads
+                quantize_into(ql, fmt, p, stream)
+        us, p10, p90 = graph_us(torch, np, g, R, reps, stream)
+        del g
         gbs = p["kbytes"] / (us * 1e-6) / 1e9
         flops = 2.0 * p["M"] * p["N"] * p["K"]
-        tot_bytes += p["kbytes"]
-        tot_flops += flops
-        tot_us += us
-        per_point.append(dict(shape=p["lab"], M=p["M"], N=p["N"], K=p["K"], us=round(us, 3),
-                              us_p10=round(float(np.percentile(samples, 10)), 3),
-                              us_p90=round(float(np.percentile(samples, 90)), 3),
-                              GBs=round(gbs, 1), frac=round(gbs / HBM_PEAK_GBS, 4),
-                              TFLOPs=round(flops / (us * 1e-6) / 1e12, 1), algo=p["cfg"]["algo"],
-                              variant=("split-k" if p["facts"]["chunks"] > 1 else
-                                       ("swap-ab" if p["cfg"]["swap_ab"] else "standard")),
-                              split=p["facts"]["chunks"], swap_ab=p["cfg"]["swap_ab"],
-                              fused_quant=p["fused"], kernel_bytes=int(p["kbytes"]), R=R,
-                              source=p["facts"]["source"]))
+        rec = dict(shape=p["lab"], M=p["M"], N=p["N"], K=p["K"], us=round(us, 3), us_p10=round(p10, 3),
+                   us_p90=round(p90, 3), GBs=round(gbs, 1), frac=round(gbs / HBM_PEAK_GBS, 4),
+                   TFLOPs=round(flops / (us * 1e-6) / 1e12, 1), algo=p["cfg"]["algo"],
+                   variant=("split-k" if p["facts"]["chunks"] > 1 else
+                            ("swap-ab" if p["cfg"]["swap_ab"] else "standard")),
+                   split=p["facts"]["chunks"], swap_ab=p["cfg"]["swap_ab"],
+                   fused_quant=p["fused"], kernel_bytes=int(p["kbytes"]), R=R, source=p["facts"]["source"])
+        per_point.append(rec)
+    # the separate quantizer launches (unfused points), after every GEMM timing
+    for p, rec in zip(W["pts"], per_point):
+        if p["fused"]:
+            continue
+        R = 64
+        with torch.cuda.stream(stream):
+            ql.qlinear_graph_begin(stream)
+            for _ in range(R):
+                quantize_into(ql, fmt, p, stream)
+            g = ql.qlinear_graph_end(stream)
+        rec["quant_us"] = round(graph_us(torch, np, g, R, reps, stream)[0], 3)
         del g
-    achieved = tot_bytes / (tot_us * 1e-6) / 1e9
-    traffic, traffic_note = recorded_traffic(wl.name, args.layout)
-    if max(wl.ms) <= 32:
-        ceil_gbs = stream_ceiling(ql, per_point, stream, reps)
-        roofline = {"kernel": "qgemm_decode_kernel", "bound": "hbm", "achieved": round(achieved, 1),
-                    "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                    "traffic": traffic, "algorithmic_bytes": int(tot_bytes), "traffic_source": traffic_note,
-                    "stream_ceiling": {"achieved": round(ceil_gbs, 1), "frac": round(ceil_gbs / HBM_PEAK_GBS, 4),
-                                       "kernel_vs_ceiling": round(achieved / ceil_gbs, 4),
-                                       "note": "a plain streaming read of each point's kernel bytes "
-                                               "(qlinear_stream_read, best of 5 grids x 2 load depths), timed like the GEMMs; "
-                                               "per point under ceiling_us"},
-                    "note": "algorithmic bytes of one launch of each of the %d GEMM kernels (a fused-"
-                            "quantization launch also reads bf16 X and writes the codes and scales) / sum of "
-                            "their per-launch durations (HIP events around graph replays of back-to-back "
-                            "launches); traffic is the HBM bytes those same %d launches moved"
-                            % (len(pts), len(pts))}
-    else:
-        # token counts in the hundreds and thousands: the tiled kernel is matrix-core bound
-        big = [q for q in per_point if q["M"] >= 1024]
-        fl = sum(2.0 * q["M"] * q["N"] * q["K"] for q in big)
-        t = sum(q["us"] for q in big) * 1e-6
-        tflops = fl / t / 1e12
-        roofline = {"kernel": "qgemm_tiled_kernel", "bound": "mfma", "achieved": round(tflops, 1),
-                    "peak": MFMA_FP8_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(tflops / MFMA_FP8_PEAK_TFLOPS, 4),
-                    "traffic": traffic, "traffic_source": traffic_note,
-                    "note": "2*M*N*K of one launch of each M >= 1024 GEMM / sum of their per-launch durations; "
-                            "the M = 64 and 256 points are HBM- or ridge-bound and are reported per point"}
+    return per_point
 
-    # ------------------------------------------------ CPU oracle baseline (bounded sample)
+
+def quantize_into(ql, fmt, p, stream):
+    if p["cfg"]["a_mode"] >= 2:
+        ql.qlinear_quantize_act_packed(fmt, p["x"], p["a_q"], p["a_s"], stream=stream)
+    else:
+        ql.qlinear_quantize_act(fmt, p["x"], p["a_q"], p["a_s"], stream=stream)
+
+
+def hbm_roofline(per_point, traffic, traffic_note, ceil_gbs):
+    tot_b = sum(q["kernel_bytes"] for q in per_point)
+    tot_us = sum(q["us"] for q in per_point)
+    achieved = tot_b / (tot_us * 1e-6) / 1e9
+    r = {"kernel": "qgemm_decode_kernel", "bound": "hbm", "achieved": round(achieved, 1),
+         "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+         "traffic": traffic, "algorithmic_bytes": int(tot_b), "traffic_source": traffic_note,
+         "note": "algorithmic bytes of one launch of each of the %d GEMM kernels (a fused-quantization "
+                 "launch also reads bf16 X and writes the codes and scales) / sum of their per-launch "
+                 "durations (HIP events around graph replays of back-to-back launches); traffic is the HBM "
+                 "bytes those same %d launches moved" % (len(per_point), len(per_point))}
+    if ceil_gbs is not None:
+        r["stream_ceiling"] = {"achieved": round(ceil_gbs, 1), "frac": round(ceil_gbs / HBM_PEAK_GBS, 4),
+                               "kernel_vs_ceiling": round(achieved / ceil_gbs, 4),
+                               "note": "a plain streaming read of each point's kernel bytes (qlinear_stream_read, "
+                                       "best of 5 grids x 2 load depths), timed like the GEMMs; per point under "
+                                       "ceiling_us"}
+    return r
+
+
+def main(argv=None):
+    args = parse_args(argv)
+    if args.gpus != 1:
+        print("bench.py measures one GPU only (--gpus %d requested); the linear shards "
+              "column-wise across GPUs with no exchange, so per-GPU work is one GPU's share." % args.gpus,
+              file=sys.stderr)
+        return 2
+
+    wls = resolve_workloads(args.workload)
+    if args.trace_summary:
+        sys.stdout.write(trace_summary(args.workload, args.layout, *args.trace_summary, ref_json=args.trace_ref))
+        return 0
+    if args.pmc_summary:
+        for name, text in pmc_summary(wls, args.layout, *args.pmc_summary).items():
+            path = traffic_file(name, args.layout)
+            with open(path, "w") as f:
+                f.write(text)
+            print("wrote", path)
+        return 0
+
+    import numpy as np
+    import torch
+
+    import quantized_gemm_decode_amd as ql
+
+    if not os.path.exists(os.path.join(ROOT, "quantized_gemm_decode_amd", "libqlinear.so")):
+        from quantized_gemm_decode_amd import build as b
+        b.build()
+    torch.cuda.set_device(0)
+    n_table = ql.qlinear_table_load(args.table) if args.table else ql.load_default_table()
+    dev = "cuda"
+    stream = torch.cuda.Stream()
+
+    Ws = [prepare_workload(ql, torch, wl, args.layout, dev) for wl in wls]
+    if args.profile_pass:
+        return profile_pass(ql, Ws, stream)
+    if args.glu:
+        W = Ws[0]
+        return glu_pass(ql, W["wl"], W["pts"], W["shapes"], stream, args)
+
+    # ------------------------------------------------ the timed steps
+    with torch.cuda.stream(stream):
+        graph_sets = [step_graphs(ql, W, stream) for W in Ws]
+    stream.synchronize()
+    for i in range(args.warmup):
+        for gs in graph_sets:
+            gs[i % len(gs)].launch(stream)
+    stream.synchronize()
+    wall0 = time.perf_counter()
+    step_ms = time_steps(torch, graph_sets, args.steps, stream)
+    wall = time.perf_counter() - wall0
+    step_bytes = sum(p["bytes"] + p["qbytes"] for W in Ws for p in W["pts"])
+    value = step_bytes / (step_ms * 1e-3) / 1e9
+    # the same K steps twice more (spread of repeated runs), then each workload alone
+    repeats = [step_ms] + [time_steps(torch, graph_sets, args.steps, stream) for _ in range(2)]
+    alone = [time_steps(torch, [gs], args.steps, stream) for gs in graph_sets]
+    del graph_sets
+
+    # ------------------------------------------------ per workload: kernels, ceiling, roofline, CPU oracle
+    blocks = []
+    all_pp = []
+    traffic_sum, traffic_ok, notes = 0, True, set()
+    cpu_budget = args.cpu_budget_s / len(Ws)
+    for W, ms in zip(Ws, alone):
+        wl = W["wl"]
+        pp = point_timing(ql, torch, np, W, stream, args.kernel_reps)
+        traffic, traffic_note = recorded_traffic(wl.name, args.layout)
+        if traffic is None:
+            traffic_ok = False
+        else:
+            traffic_sum += traffic
+        notes.add(traffic_note)
+        if max(wl.ms) <= 32:
+            ceil_gbs = stream_ceiling(ql, pp, stream, max(10, args.kernel_reps // 3))
+            roofline = hbm_roofline(pp, traffic, traffic_note, ceil_gbs)
+        else:
+            # token counts in the hundreds and thousands: the tiled kernel is matrix-core bound
+            big = [q for q in pp if q["M"] >= 1024]
+            fl = sum(2.0 * q["M"] * q["N"] * q["K"] for q in big)
+            t = sum(q["us"] for q in big) * 1e-6
+            tflops = fl / t / 1e12
+            roofline = {"kernel": "qgemm_tiled_kernel", "bound": "mfma", "achieved": round(tflops, 1),
+                        "peak": MFMA_FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
+                        "frac": round(tflops / MFMA_FP8_PEAK_TFLOPS, 4),
+                        "traffic": traffic, "traffic_source": traffic_note,
+                        "note": "2*M*N*K of one launch of each M >= 1024 GEMM / sum of their per-launch durations; "
+                                "the M = 64 and 256 points are HBM- or ridge-bound and are reported per point"}
+        cpu = None if args.no_cpu_baseline else cpu_baseline(wl, cpu_budget)
+        wbytes = sum(p["bytes"] + p["qbytes"] for p in W["pts"])
+        qus = [q["quant_us"] for q in pp if "quant_us" in q]
+        blocks.append({
+            "workload": wl.name, "format": ql.FORMAT_NAMES[W["fmt"]],
+            "shapes": ["%s %dx%d" % s for s in wl.shapes], "token_counts": list(wl.ms),
+            "gemms_per_step": len(pp), "ms_per_step": round(ms, 4),
+            "value": round(wbytes / (ms * 1e-3) / 1e9, 1), "unit": "GB/s",
+            "fused_quant_points": sum(1 for p in W["pts"] if p["fused"]),
+            "quantizer_us_total": round(sum(qus), 3),
+            "roofline": roofline, "cpu_baseline": cpu, "per_point": pp})
+        all_pp += pp
+        W.clear()
+        torch.cuda.empty_cache()
+
+    if all(max(b["token_counts"]) <= 32 for b in blocks):
+        roofline = hbm_roofline(all_pp, traffic_sum if traffic_ok else None,
+                                "; ".join(sorted(notes)), None)
+        ceil_b = sum(q["kernel_bytes"] for q in all_pp)
+        ceil_us = sum(q["ceiling_us"] for q in all_pp)
+        ceil_gbs = ceil_b / (ceil_us * 1e-6) / 1e9
+        roofline["stream_ceiling"] = {"achieved": round(ceil_gbs, 1), "frac": round(ceil_gbs / HBM_PEAK_GBS, 4),
+                                      "kernel_vs_ceiling": round(roofline["achieved"] / ceil_gbs, 4)}
+    else:
+        roofline = blocks[0]["roofline"]
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(wl, shapes, args.cpu_budget_s)
-
+        cb = [b["cpu_baseline"] for b in blocks]
+        secs = sum(c["seconds"] for c in cb)
+        cpu = {"value": round(sum(c["bytes"] for c in cb) / secs / 1e9, 3), "unit": "GB/s",
+               "cores": cb[0]["cores"], "kind": "oracle",
+               "sample": "; ".join(c["sample"] for c in cb)}
+    fmts = sorted({b["format"] for b in blocks})
     out = {
         "metric": METRIC,
         "value": round(value, 1),
@@ -468,20 +610,23 @@ def main(argv=None):
         "warmup": args.warmup,
         "kernel_reps": args.kernel_reps,
         "ms_per_step": round(step_ms, 4),
+        "ms_per_step_repeats": [round(r, 4) for r in repeats],
+        "repeat_spread": round((max(repeats) - min(repeats)) / min(repeats), 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": {1: "int8", 4: "fp8_e4m3 x fp4_e2m1"}.get(fmt, "fp8_e4m3"),
-        "data": "synthetic (seeded N(0,1) activations with 1%% x20 outlier channels, N(0,%g) weights)" % wl.sigma_w,
-        "config": {"workload": wl.name, "format": ql.FORMAT_NAMES[fmt],
-                   "shapes": ["%s %dx%d" % s for s in wl.shapes], "token_counts": list(wl.ms),
-                   "gemms_per_step": len(pts), "graph_replay": True, "table_entries": n_table,
+        "dtype": "+".join(sorted({DTYPES.get(b["format"], "fp8_e4m3") for b in blocks})),
+        "data": "synthetic (seeded N(0,1) activations with 1% x20 outlier channels, N(0,0.02) weights "
+                "(N(0,0.015) for the 32B-class shapes))",
+        "config": {"workload": "+".join(b["workload"] for b in blocks), "formats": fmts,
+                   "gemms_per_step": len(all_pp), "graph_replay": True, "table_entries": n_table,
                    "weight_layout": args.layout,
-                   "fused_quant_points": sum(1 for p in pts if p["fused"]),
-                   "us_per_gemm_step_avg": round(step_ms * 1e3 / len(pts), 3)},
+                   "fused_quant_points": sum(b["fused_quant_points"] for b in blocks),
+                   "us_per_gemm_step_avg": round(step_ms * 1e3 / len(all_pp), 3)},
         "roofline": roofline,
         "cpu_baseline": cpu,
-        "per_point": per_point,
+        "env": environment(ql, torch),
+        "workloads": blocks,
         "wall_s": round(wall, 3),
     }
     line = json.dumps(out)
@@ -490,6 +635,9 @@ def main(argv=None):
         with open(args.out, "w") as f:
             f.write(line + "\n")
     return 0
+
+
+DTYPES = {"W8A8_INT8": "int8", "MXFP4": "fp8_e4m3 x fp4_e2m1"}
 
 
 def stream_ceiling(ql, per_point, stream, reps):
@@ -593,21 +741,23 @@ def glu_pass(ql, wl, pts, shapes, stream, args):
     return 0
 
 
-def profile_pass(ql, fmt, pts, shapes, stream):
+def profile_pass(ql, Ws, stream):
     """Eager launches in a fixed order for per-dispatch hardware counters.
 
-    Order: for every point, 3 x (quantize, GEMM) on weight copies 0, 1, 2;
-    then 3 plain copies of 256 MiB (read 256 MiB, write 256 MiB), whose
-    counter readings calibrate the byte counters."""
+    Order: for every workload, for every point, 3 x (quantize, GEMM) on weight
+    copies 0, 1, 2; then 3 plain copies of 256 MiB (read 256 MiB, write
+    256 MiB), whose counter readings calibrate the byte counters."""
     import torch
     with torch.cuda.stream(stream):
-        for p in pts:
-            sh = shapes[p["lab"]]
-            for c in range(3):
-                ql.qlinear_forward(p["plan"], p["x"], p["a_q"], p["a_s"], sh["wq"][c], sh["ws"][c], p["y"],
-                                   p["wsp"], stream=stream)
-            stream.synchronize()
-            print("point %s M=%d N=%d K=%d bytes=%d" % (p["lab"], p["M"], p["N"], p["K"], p["bytes"]), flush=True)
+        for W in Ws:
+            for p in W["pts"]:
+                sh = W["shapes"][p["lab"]]
+                for c in range(3):
+                    ql.qlinear_forward(p["plan"], p["x"], p["a_q"], p["a_s"], sh["wq"][c], sh["ws"][c], p["y"],
+                                       p["wsp"], stream=stream)
+                stream.synchronize()
+                print("point %s %s M=%d N=%d K=%d bytes=%d" % (W["wl"].name, p["lab"], p["M"], p["N"], p["K"],
+                                                              p["bytes"]), flush=True)
         src = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")
         dst = torch.empty_like(src)
         src.fill_(1)
@@ -619,9 +769,8 @@ def profile_pass(ql, fmt, pts, shapes, stream):
     return 0
 
 
-def cpu_baseline(wl, shapes, budget_s):
+def cpu_baseline(wl, budget_s):
     """Time the CPU oracle (as it stands) on a bounded sample of the same workload."""
-    import numpy as np
     import torch
 
     import oracle
@@ -641,7 +790,7 @@ def cpu_baseline(wl, shapes, budget_s):
             w_q, s_w = oracle.mx_quantize(bf16_bits(w))                 # offline step: not timed
         else:
             w_q, s_w = oracle.quantize_weight(fmt, bf16_bits(w))      # offline step: not timed
-        for M in wl.ms:
+        for M in (wl.ms if len(wl.ms) < 3 else (wl.ms[0], wl.ms[-1])):
             if 2.0 * M * N * K > 50e9:
                 continue       # a single fp64 GEMM of minutes: outside the bounded sample
             xb = bf16_bits(x[:M])
@@ -665,7 +814,8 @@ def cpu_baseline(wl, shapes, budget_s):
     return {"value": round(b_total / t_total / 1e9, 3), "unit": "GB/s", "cores": n, "kind": "oracle",
             "sample": "%s: activation quantizer + exact fp64 contraction + epilogue on %s (weights "
                       "pre-quantized, untimed); %.1f s of CPU time" % (wl.name, ", ".join(sample), t_total),
-            "us_per_gemm": round(t_total / len(sample) * 1e6, 1)}
+            "us_per_gemm": round(t_total / len(sample) * 1e6, 1), "seconds": round(t_total, 3),
+            "bytes": int(b_total)}
 
 
 if __name__ == "__main__":

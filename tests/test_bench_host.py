@@ -65,9 +65,37 @@ def test_pmc_summary_applies_the_copy_calibration(tmp_path, monkeypatch):
     _csv(tmp_path / "f.csv", fetch)
     _csv(tmp_path / "w.csv", write)
     monkeypatch.setattr(bench, "kernel_sources_digest", lambda: "0" * 64)
-    out = bench.pmc_summary(wl.name, "fused", str(tmp_path / "f.csv"), str(tmp_path / "w.csv"))
+    out = bench.pmc_summary([wl], "fused", str(tmp_path / "f.csv"), str(tmp_path / "w.csv"))[wl.name]
     kv = dict(l.split() for l in out.splitlines() if l and not l.startswith("#"))
     want = 4100.0 * 1024 * 2 + 64.0 * 1024
     assert int(kv["traffic_bytes_per_step"]) == round(want)
     assert int(kv["algorithmic_bytes_per_step"]) == bench.algorithmic_bytes(wl.fmt, M, N, K)
     assert kv["kernel_sources_sha256"] == "0" * 64
+
+
+def test_default_workloads_are_the_fp8_int8_decode_sweeps():
+    """The default run measures the single INT8 linear and the three M = 1..32
+    sweeps (FP8_Dynamic 8B, Block_FP8 8B, W8A8_INT8 32B) together."""
+    wls = bench.resolve_workloads(bench.parse_args([]).workload)
+    assert [w.name for w in wls] == list(bench.DECODE_SET)
+    assert [w.fmt for w in wls] == [ql.W8A8_INT8, ql.FP8_DYNAMIC, ql.BLOCK_FP8, ql.W8A8_INT8]
+    assert sum(len(decode_points(w)) for w in wls) == 85
+    assert all(max(w.ms) <= 32 for w in wls)
+
+
+def test_pmc_summary_splits_dispatches_by_workload(tmp_path, monkeypatch):
+    """Two workloads profiled in one pass: each gets its own record, from its
+    own dispatches in order."""
+    wls = [config_by_name("int8_linear_4096x2048"), config_by_name("int8_linear_4096x2048")]
+    gemm = "void qlk::qgemm_decode_kernel<1, false, 1, 1, 4, 2, 2, 2, false>(qlk::DecodeArgs)"
+    copy = "void copy_kernel(unsigned char const*, unsigned char*)"
+    fetch = [(gemm, 1000.0)] * 3 + [(gemm, 3000.0)] * 3 + [(copy, 131072.0)] * 3
+    write = [(gemm, 0.0)] * 6 + [(copy, 262144.0)] * 3
+    _csv(tmp_path / "f.csv", fetch)
+    _csv(tmp_path / "w.csv", write)
+    monkeypatch.setattr(bench, "kernel_sources_digest", lambda: "0" * 64)
+    wls2 = [wls[0], type(wls[1])(**{**wls[1].__dict__, "name": "other"})]
+    out = bench.pmc_summary(wls2, "fused", str(tmp_path / "f.csv"), str(tmp_path / "w.csv"))
+    kv = {n: dict(l.split() for l in t.splitlines() if l and not l.startswith("#")) for n, t in out.items()}
+    assert int(kv[wls2[0].name]["traffic_bytes_per_step"]) == 1000 * 1024 * 2
+    assert int(kv["other"]["traffic_bytes_per_step"]) == 3000 * 1024 * 2
