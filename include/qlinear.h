@@ -411,6 +411,26 @@ ql_status qlinear_forward(ql_plan plan, const void* x_bf16, void* a_q, void* a_s
                           void* workspace, void* stream);
 
 /*
+ * For callers that cannot allocate device memory -- code running under
+ * hipGraph capture, tight serving loops, harnesses that forbid hipMalloc:
+ * qlinear_forward without the workspace argument.  A split-K plan's partial
+ * sums and arrival counters live in a scratch array inside the library, one
+ * per GPU (16 MiB = 16777216 bytes, held until the process
+ * ends); nothing is allocated by this call, or by the library for it.  The
+ * first call on a GPU clears that GPU's array with a fill kernel on `stream`
+ * (make it outside graph capture, or capture it: the fill is an ordinary
+ * node); every run leaves the array all-zero again.  All such calls on one
+ * GPU share its array, so calls that overlap in time on one GPU (concurrent
+ * streams, or graph replays in flight on two streams) race and must not be
+ * made.  A plan whose workspace (qlinear_workspace_bytes) exceeds the scratch
+ * is rejected with QL_E_UNSUPPORTED before anything is enqueued.  Otherwise
+ * arguments, results and errors are those of qlinear_forward.
+ */
+ql_status qlinear_forward_noalloc(ql_plan plan, const void* x_bf16, void* a_q, void* a_scale,
+                                  const void* w_q, const void* w_scale, void* y_bf16,
+                                  void* stream);
+
+/*
  * hipGraph dispatch for the small-M path ([Summary] "Hybrid dispatch
  * addresses runtime overhead": the tuned kernels run only under graph
  * replay, which removes the host launch cost).  qlinear_graph_begin starts

@@ -453,6 +453,21 @@ def qlinear_forward(plan, x, a_q, a_scale, w_q, w_scale, y, workspace=None, stre
            "qlinear_forward")
 
 
+def qlinear_forward_noalloc(plan, x, a_q, a_scale, w_q, w_scale, y, stream=None):
+    """qlinear_forward with the split-K workspace taken from the library's
+    per-GPU scratch (no allocation; calls on one GPU must not overlap)."""
+    plan.check_operands(x=x, a_q=a_q, a_scale=a_scale, w_q=w_q, w_scale=w_scale, y=y)
+    _check(lib().qlinear_forward_noalloc(plan.handle, _ptr(x, "x", torch.bfloat16), _ptr(a_q, "a_q", CODE_DTYPES),
+                                         _ptr(a_scale, "a_scale", SCALE_DTYPES), _ptr(w_q, "w_q", CODE_DTYPES),
+                                         _ptr(w_scale, "w_scale", SCALE_DTYPES), _ptr(y, "y", torch.bfloat16),
+                                         _stream(stream)),
+           "qlinear_forward_noalloc")
+
+
+# Bytes of the per-GPU scratch behind qlinear_forward_noalloc (stated in include/qlinear.h).
+NOALLOC_SCRATCH_BYTES = 16 << 20
+
+
 # ----------------------------------------------------------------- graphs
 
 class Graph:

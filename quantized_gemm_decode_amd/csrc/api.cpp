@@ -594,6 +594,68 @@ ql_status launch_gemm(const ql_plan_s* p, const void* a_q, const void* a_scale, 
   return e == hipSuccess ? QL_OK : hip_fail(e, "decode GEMM launch");
 }
 
+ql_status quantize_act(int32_t fmt, const void* x_bf16, int64_t M, int64_t K, void* a_q, void* a_scale,
+                       bool packed, void* stream) {
+  ql_status st = check_sizes(fmt, M, K, "M");
+  if (st != QL_OK) return st;
+  if (packed && qlinear_packed_act_bytes(M, K) > (int64_t(1) << 30))
+    return fail(QL_E_UNSUPPORTED, "packed activations exceed 2^30 bytes");
+  if (M == 0 || K == 0) return QL_OK;
+  if (!x_bf16 || !a_q || !a_scale) return fail(QL_E_INVALID, "NULL pointer");
+  if (!aligned16(x_bf16) || !aligned16(a_q) || !aligned16(a_scale)) return fail(QL_E_ALIGN, "pointers must be 16-byte aligned");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e;
+  if (is_mx(fmt))   // MXFP4 plans take MXFP8 activations
+    e = qlk::launch_quant_mx(x_bf16, M, K, a_q, static_cast<uint8_t*>(a_scale), packed, s);
+  else if (fmt == QL_BLOCK_FP8)
+    e = qlk::launch_quant_groups(x_bf16, M, K, a_q, static_cast<float*>(a_scale), packed, s);
+  else
+    e = qlk::launch_quant_rows(kernel_fmt(fmt), x_bf16, M, K, a_q, static_cast<float*>(a_scale), packed, s);
+  return e == hipSuccess ? QL_OK : hip_fail(e, "activation quantizer launch");
+}
+
+// Split-K workspace for callers that cannot allocate (qlinear_forward_noalloc):
+// one array per GPU, held until the process ends, shared by every such call
+// on that GPU.  In host code `scratch` names a host-side stand-in; the
+// device address comes from hipGetSymbolAddress, once per device.
+constexpr int64_t kScratchBytes = int64_t(16) << 20;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's scratch address; on the first call on a device the
+// array is also cleared on `s` (a fill kernel, so a graph being captured
+// records an ordinary node) -- the kernels leave it all-zero after each run.
+ql_status device_scratch(hipStream_t s, void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(QL_E_UNSUPPORTED, "device %d beyond the scratch table", dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    e = qlk::launch_fill_zero_bf16(ptr, kScratchBytes / 2, s);
+    if (e != hipSuccess) return hip_fail(e, "scratch clear");
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return QL_OK;
+}
+
+ql_status forward_impl(ql_plan p, const void* x_bf16, void* a_q, void* a_scale, const void* w_q,
+                       const void* w_scale, void* y, void* workspace, void* stream) {
+  if (!p->tiled && p->cfg.a_mode == 4)
+    return launch_gemm(p, nullptr, nullptr, w_q, w_scale, y, workspace, nullptr, static_cast<hipStream_t>(stream),
+                       true, x_bf16, a_q, static_cast<float*>(a_scale));
+  ql_status st = quantize_act(p->fmt, x_bf16, p->M, p->K, a_q, a_scale, p->cfg.a_mode >= 2, stream);
+  if (st != QL_OK) return st;
+  return launch_gemm(p, a_q, a_scale, w_q, w_scale, y, workspace, nullptr, static_cast<hipStream_t>(stream));
+}
+
 }  // namespace
 
 extern "C" {
@@ -614,26 +676,6 @@ const char* qlinear_status_string(int32_t s) {
 }
 
 const char* qlinear_last_error(void) { return g_err.c_str(); }
-
-static ql_status quantize_act(int32_t fmt, const void* x_bf16, int64_t M, int64_t K, void* a_q, void* a_scale,
-                              bool packed, void* stream) {
-  ql_status st = check_sizes(fmt, M, K, "M");
-  if (st != QL_OK) return st;
-  if (packed && qlinear_packed_act_bytes(M, K) > (int64_t(1) << 30))
-    return fail(QL_E_UNSUPPORTED, "packed activations exceed 2^30 bytes");
-  if (M == 0 || K == 0) return QL_OK;
-  if (!x_bf16 || !a_q || !a_scale) return fail(QL_E_INVALID, "NULL pointer");
-  if (!aligned16(x_bf16) || !aligned16(a_q) || !aligned16(a_scale)) return fail(QL_E_ALIGN, "pointers must be 16-byte aligned");
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e;
-  if (is_mx(fmt))   // MXFP4 plans take MXFP8 activations
-    e = qlk::launch_quant_mx(x_bf16, M, K, a_q, static_cast<uint8_t*>(a_scale), packed, s);
-  else if (fmt == QL_BLOCK_FP8)
-    e = qlk::launch_quant_groups(x_bf16, M, K, a_q, static_cast<float*>(a_scale), packed, s);
-  else
-    e = qlk::launch_quant_rows(kernel_fmt(fmt), x_bf16, M, K, a_q, static_cast<float*>(a_scale), packed, s);
-  return e == hipSuccess ? QL_OK : hip_fail(e, "activation quantizer launch");
-}
 
 ql_status qlinear_quantize_act(int32_t fmt, const void* x_bf16, int64_t M, int64_t K, void* a_q,
                                void* a_scale, void* stream) {
@@ -920,12 +962,21 @@ ql_status qlinear_run_debug_acc(ql_plan p, const void* a_q, const void* a_scale,
 ql_status qlinear_forward(ql_plan p, const void* x_bf16, void* a_q, void* a_scale, const void* w_q,
                           const void* w_scale, void* y, void* workspace, void* stream) {
   if (!p) return fail(QL_E_INVALID, "plan is NULL");
-  if (!p->tiled && p->cfg.a_mode == 4)
-    return launch_gemm(p, nullptr, nullptr, w_q, w_scale, y, workspace, nullptr, static_cast<hipStream_t>(stream),
-                       true, x_bf16, a_q, static_cast<float*>(a_scale));
-  ql_status st = quantize_act(p->fmt, x_bf16, p->M, p->K, a_q, a_scale, p->cfg.a_mode >= 2, stream);
-  if (st != QL_OK) return st;
-  return launch_gemm(p, a_q, a_scale, w_q, w_scale, y, workspace, nullptr, static_cast<hipStream_t>(stream));
+  return forward_impl(p, x_bf16, a_q, a_scale, w_q, w_scale, y, workspace, stream);
+}
+
+ql_status qlinear_forward_noalloc(ql_plan p, const void* x_bf16, void* a_q, void* a_scale, const void* w_q,
+                                  const void* w_scale, void* y, void* stream) {
+  if (!p) return fail(QL_E_INVALID, "plan is NULL");
+  void* ws = nullptr;
+  if (p->ws_bytes > 0) {
+    if (p->ws_bytes > kScratchBytes)
+      return fail(QL_E_UNSUPPORTED, "plan needs %lld bytes of split-K workspace; the no-allocation scratch holds %lld",
+                  (long long)p->ws_bytes, (long long)kScratchBytes);
+    ql_status st = device_scratch(static_cast<hipStream_t>(stream), &ws);
+    if (st != QL_OK) return st;
+  }
+  return forward_impl(p, x_bf16, a_q, a_scale, w_q, w_scale, y, ws, stream);
 }
 
 ql_status qlinear_graph_begin(void* stream) {
