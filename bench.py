@@ -203,7 +203,7 @@ def trace_summary(workload, layout, trace_csv, stats_csv, bench_json, ref_json=N
              % (bench["config"]["workload"], LAYOUT_NAMES[layout]),
              "# command (from /tmp with TMPDIR=/tmp):",
              "#   rocprofv3 --kernel-trace --stats -f csv -d <dir> -o bench -- python3 <repo>/bench.py --workload %s "
-             "--layout %s --steps %d --warmup %d --kernel-reps %d --no-cpu-baseline"
+             "--layout %s --steps %d --warmup %d --kernel-reps %d --no-cpu-baseline --no-ceiling"
              % (workload, layout, bench["steps"], bench["warmup"], bench.get("kernel_reps", 5)),
              "#   python3 bench.py --workload %s --layout %s --trace-summary <dir>/bench_kernel_trace.csv "
              "<dir>/bench_kernel_stats.csv <stdout of the command above> [--trace-ref <json of a plain run>]"
@@ -265,6 +265,8 @@ def parse_args(argv=None):
                          "packed weights only; rowmajor: row-major both")
     ap.add_argument("--kernel-reps", type=int, default=30, help="graph replays per point for kernel timing")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-ceiling", action="store_true",
+                    help="skip the streaming-read ceiling (for profiled runs: it launches thousands of kernels)")
     ap.add_argument("--cpu-budget-s", type=float, default=24.0, help="CPU oracle seconds, split over the workloads")
     ap.add_argument("--table", default=None, help="sweep table path (default: the packaged table)")
     ap.add_argument("--out", default=None, help="also write the JSON line to this file")
@@ -279,7 +281,9 @@ def parse_args(argv=None):
                          "copies, then a plain 256 MiB device copy 3 times (the counters' calibration), and exit")
     ap.add_argument("--glu", action="store_true",
                     help="time the workload's gate_up points two ways -- the forward plan writing Y [M, N], and "
-                         "the SiLU-and-mul plan writing silu(gate)*up [M, N/2] -- print one JSON line, and exit")
+                         "the SiLU-and-mul plan writing silu(gate)*up [M, N/2] -- and the gate_up -> down chain "
+                         "two ways (down quantizing H in a pass of its own, or down quantizing its K chunk with the "
+                         "per-token amax the SiLU-and-mul epilogue folded); print one JSON line, and exit")
     return ap.parse_args(argv)
 
 
@@ -518,8 +522,11 @@ def main(argv=None):
     if args.profile_pass:
         return profile_pass(ql, Ws, stream)
     if args.glu:
-        W = Ws[0]
-        return glu_pass(ql, W["wl"], W["pts"], W["shapes"], stream, args)
+        # one JSON line per workload that has a gate_up projection
+        for W in Ws:
+            if any(p["lab"] == "gate_up" for p in W["pts"]):
+                glu_pass(ql, W["wl"], W["pts"], W["shapes"], stream, args)
+        return 0
 
     # ------------------------------------------------ the timed steps
     with torch.cuda.stream(stream):
@@ -554,7 +561,7 @@ def main(argv=None):
             traffic_sum += traffic
         notes.add(traffic_note)
         if max(wl.ms) <= 32:
-            ceil_gbs = stream_ceiling(ql, pp, stream, max(10, args.kernel_reps // 3))
+            ceil_gbs = None if args.no_ceiling else stream_ceiling(ql, pp, stream, max(10, args.kernel_reps // 3))
             roofline = hbm_roofline(pp, traffic, traffic_note, ceil_gbs)
         else:
             # token counts in the hundreds and thousands: the tiled kernel is matrix-core bound
@@ -586,11 +593,12 @@ def main(argv=None):
     if all(max(b["token_counts"]) <= 32 for b in blocks):
         roofline = hbm_roofline(all_pp, traffic_sum if traffic_ok else None,
                                 "; ".join(sorted(notes)), None)
-        ceil_b = sum(q["kernel_bytes"] for q in all_pp)
-        ceil_us = sum(q["ceiling_us"] for q in all_pp)
-        ceil_gbs = ceil_b / (ceil_us * 1e-6) / 1e9
-        roofline["stream_ceiling"] = {"achieved": round(ceil_gbs, 1), "frac": round(ceil_gbs / HBM_PEAK_GBS, 4),
-                                      "kernel_vs_ceiling": round(roofline["achieved"] / ceil_gbs, 4)}
+        if not args.no_ceiling:
+            ceil_b = sum(q["kernel_bytes"] for q in all_pp)
+            ceil_us = sum(q["ceiling_us"] for q in all_pp)
+            ceil_gbs = ceil_b / (ceil_us * 1e-6) / 1e9
+            roofline["stream_ceiling"] = {"achieved": round(ceil_gbs, 1), "frac": round(ceil_gbs / HBM_PEAK_GBS, 4),
+                                          "kernel_vs_ceiling": round(roofline["achieved"] / ceil_gbs, 4)}
     else:
         roofline = blocks[0]["roofline"]
     cpu = None
@@ -686,14 +694,53 @@ def stream_ceiling(ql, per_point, stream, reps):
     return tot_b / (tot_us * 1e-6) / 1e9
 
 
+def _graph_median_us(torch, np, stream, g, R, reps, before=None):
+    for _ in range(3):
+        if before:
+            before()
+        g.launch(stream)
+    stream.synchronize()
+    samples = []
+    for _ in range(reps):
+        if before:
+            before()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        g.launch(stream)
+        e1.record(stream)
+        e1.synchronize()
+        samples.append(e0.elapsed_time(e1) * 1e3 / R)
+    return round(float(np.median(samples)), 3)
+
+
+def _cfg_str(cfg):
+    return "swap%d split%d waves%dx%d rows%d pf%d amode%d" % (
+        cfg["swap_ab"], cfg["split_k"], cfg["waves_n"], cfg["waves_k"], cfg["rows_per_wave"], cfg["prefetch"],
+        cfg["a_mode"])
+
+
+def _launches(cfg):
+    """Kernel launches of one forward: one when the quantizer runs inside the GEMM."""
+    return 1 if cfg["a_mode"] in (4, 5) else 2
+
+
 def glu_pass(ql, wl, pts, shapes, stream, args):
-    """Per-launch times of the gate_up points as a plain forward (Y [M, N]) and
-    with the SiLU-and-mul epilogue (silu(gate)*up, [M, N/2]), HIP events around
-    graph replays of R launches on distinct weight copies, as for the bench's
-    per-point timing."""
+    """The gated MLP's gate_up point, three ways, each timed as graph replays
+    of R back-to-back forwards on distinct weight copies (HIP events):
+
+      plain: the gate_up forward writing Y [M, N];
+      glu:   the SiLU-and-mul plan writing H = silu(gate)*up [M, N/2];
+      and the gate_up -> down chain, twice: 'chain_two_pass' = the SiLU-and-mul
+      forward, then down's forward plan (its own quantizer launch, or the
+      quantizer fused in where it fits the row); 'chain' = the SiLU-and-mul
+      forward folding the per-token amax of H, then down's given-amax plan
+      (each workgroup quantizes its K chunk of H in the GEMM launch)."""
     import numpy as np
     import torch
     fmt = wl.fmt
+    per_token = fmt in (ql.FP8_DYNAMIC, ql.W8A8_INT8)
+    downs = {p["M"]: p for p in pts if p["lab"] == "down"}
     out = []
     for p in pts:
         if p["lab"] != "gate_up":
@@ -702,40 +749,61 @@ def glu_pass(ql, wl, pts, shapes, stream, args):
         M, N, K = p["M"], p["N"], p["K"]
         R = min(sh["copies"], 64)
         res = {"M": M}
+        glu_plan = ql.qlinear_plan_glu(fmt, M, N, K, 2)
+        h = torch.empty(M, N // 2, dtype=torch.bfloat16, device="cuda")
+        a_q, a_s = ql.act_buffer(glu_plan), ql.act_scale_buffer(glu_plan)
+        wsp = glu_plan.new_workspace()
         for kind in ("plain", "glu"):
-            plan = p["plan"] if kind == "plain" else ql.qlinear_plan_glu(fmt, M, N, K, 2)
-            y = torch.empty(M, N if kind == "plain" else N // 2, dtype=torch.bfloat16, device="cuda")
-            a_q = ql.act_buffer(plan)
-            a_s = ql.act_scale_buffer(plan)
-            wsp = plan.new_workspace()
+            plan = p["plan"] if kind == "plain" else glu_plan
+            y = torch.empty(M, N, dtype=torch.bfloat16, device="cuda") if kind == "plain" else h
+            aq, as_ = (ql.act_buffer(plan), ql.act_scale_buffer(plan)) if kind == "plain" else (a_q, a_s)
+            ws = plan.new_workspace() if kind == "plain" else wsp
             with torch.cuda.stream(stream):
                 ql.qlinear_graph_begin(stream)
                 for c in range(R):
-                    ql.qlinear_forward(plan, p["x"], a_q, a_s, sh["wq"][c], sh["ws"][c], y, wsp, stream=stream)
+                    ql.qlinear_forward(plan, p["x"], aq, as_, sh["wq"][c], sh["ws"][c], y, ws, stream=stream)
                 g = ql.qlinear_graph_end(stream)
-            for _ in range(3):
-                g.launch(stream)
-            stream.synchronize()
-            samples = []
-            for _ in range(args.kernel_reps):
-                e0 = torch.cuda.Event(enable_timing=True)
-                e1 = torch.cuda.Event(enable_timing=True)
-                e0.record(stream)
-                g.launch(stream)
-                e1.record(stream)
-                e1.synchronize()
-                samples.append(e0.elapsed_time(e1) * 1e3 / R)
-            cfg = plan.config
-            res[kind + "_us"] = round(float(np.median(samples)), 3)
-            res[kind + "_fused_quant"] = cfg["a_mode"] == 4
-            res[kind + "_config"] = "swap%d split%d waves%dx%d rows%d pf%d amode%d" % (
-                cfg["swap_ab"], cfg["split_k"], cfg["waves_n"], cfg["waves_k"], cfg["rows_per_wave"],
-                cfg["prefetch"], cfg["a_mode"])
+            res[kind + "_us"] = _graph_median_us(torch, np, stream, g, R, args.kernel_reps)
+            res[kind + "_fused_quant"] = plan.config["a_mode"] == 4
+            res[kind + "_config"] = _cfg_str(plan.config)
             del g
+        d = downs.get(M)
+        if d is not None and d["K"] == N // 2:
+            dsh = shapes["down"]
+            Rc = min(R, dsh["copies"])
+            y2 = torch.empty(M, d["N"], dtype=torch.bfloat16, device="cuda")
+            two = ql.qlinear_plan_layouts(fmt, M, d["N"], d["K"], 1, 2)
+            chains = [("chain_two_pass", two)]
+            if per_token:
+                chains.append(("chain", ql.qlinear_plan_layouts(fmt, M, d["N"], d["K"], 1, 3)))
+            amax = ql.amax_buffer(M)
+            for kind, dplan in chains:
+                da_q, da_s = ql.act_buffer(dplan), ql.act_scale_buffer(dplan)
+                dws = dplan.new_workspace()
+                with torch.cuda.stream(stream):
+                    ql.qlinear_graph_begin(stream)
+                    for c in range(Rc):
+                        if kind == "chain":
+                            ql.qlinear_forward_glu_amax(glu_plan, p["x"], a_q, a_s, sh["wq"][c], sh["ws"][c], h, amax,
+                                                        wsp, stream=stream)
+                            ql.qlinear_forward_amax(dplan, h, amax, da_q, da_s, dsh["wq"][c], dsh["ws"][c], y2, dws,
+                                                    stream=stream)
+                        else:
+                            ql.qlinear_forward(glu_plan, p["x"], a_q, a_s, sh["wq"][c], sh["ws"][c], h, wsp,
+                                               stream=stream)
+                            ql.qlinear_forward(dplan, h, da_q, da_s, dsh["wq"][c], dsh["ws"][c], y2, dws,
+                                               stream=stream)
+                    g = ql.qlinear_graph_end(stream)
+                res[kind + "_us"] = _graph_median_us(torch, np, stream, g, Rc, args.kernel_reps)
+                res[kind + "_launches"] = _launches(glu_plan.config) + _launches(dplan.config)
+                res[kind + "_down_config"] = _cfg_str(dplan.config)
+                del g
         out.append(res)
     gu = [p for p in pts if p["lab"] == "gate_up"]
     print(json.dumps({"metric": "µs per gate_up forward: plain (Y [M, N]) vs SiLU-and-mul epilogue (silu(gate)*up, "
-                                "[M, N/2])", "unit": "us", "workload": wl.name,
+                                "[M, N/2]); µs per gate_up -> down chain: down quantizing H in its own pass vs "
+                                "down quantizing its K chunk with the per-token amax the SiLU-and-mul epilogue "
+                                "folded", "unit": "us", "workload": wl.name,
                       "shape": "gate_up %dx%d" % (gu[0]["N"], gu[0]["K"]) if gu else None,
                       "data": "synthetic", "kernel_reps": args.kernel_reps, "per_point": out}), flush=True)
     return 0

@@ -12,6 +12,8 @@
  *   [Summary]  English summary, yuxiaoba.github.io/tech/en/helion-linear/
  *   [Noticias] "Helion entra al backend lineal de vLLM y supera a CUTLASS en
  *              Hopper", noticias.mechatronicstore.cl
+ *   [Deep dive] "Optimizing vLLM Linear Backend Performance using Helion
+ *              Kernel DSL", explore.n1n.ai
  *
  * Formats ([Summary] "Put algorithm selection inside the search space", last
  * paragraph; [Noticias] "El backend lineal de Helion / Alcance"):
@@ -305,9 +307,14 @@ ql_status qlinear_table_load(const char* path, int64_t* n_entries);
 void qlinear_table_clear(void);
 
 /*
- * Plan one GEMM shape.  Looks up the sweep table with M rounded up to the
- * next tuned token bucket {1,2,4,8,16,24,32} (M > 32: the nearest tuned M at
- * or above, else the largest); without an entry a built-in heuristic is used
+ * Plan one GEMM shape: the runtime half of the pages' hybrid dispatch -- a
+ * per-shape configuration searched offline, with the algorithmic switches
+ * (split_k, swap_ab) inside the search space, and looked up per token-count
+ * bucket at run time ([Summary] "Put algorithm selection inside the search
+ * space" and "Hybrid dispatch addresses runtime overhead": token counts 1, 2,
+ * 4, 8, 16, 24, 32 tuned separately).  Looks up the sweep table with M rounded
+ * up to the next tuned token bucket {1,2,4,8,16,24,32} (M > 32: the nearest
+ * tuned M at or above, else the largest); without an entry a built-in heuristic is used
  * (facts.source tells which).  The environment variable QLINEAR_FORCE =
  * "algo,swap,split,wn,wk,rows,prefetch,amode,wlds,wlayout,tile_m,tile_n"
  * overrides both (its operand layouts must match the call).  Without a table
@@ -325,7 +332,11 @@ ql_status qlinear_plan_packed(int32_t fmt, int64_t M, int64_t N, int64_t K, ql_p
  * 1 = packed weights; a_packed 0 = row-major A_q (qlinear_quantize_act),
  * 1 = packed A_q (qlinear_quantize_act_packed; the plan's a_mode is 2 or 3),
  * 2 = a forward plan for packed weights (the table's "fwd" entry, else the
- * packed-A_q plan): a_mode 2, 3 or 4, to be run with qlinear_forward only.
+ * packed-A_q plan): a_mode 2, 3 or 4, to be run with qlinear_forward only;
+ * 3 = a forward plan for an input whose per-token amax is given (FP8_Dynamic
+ * and W8A8_INT8, packed weights; the table's "amx" entry, else a_mode 5 when
+ * M <= 16 and K % 128 == 0, else the packed-A_q plan), to be run with
+ * qlinear_forward_amax.
  */
 ql_status qlinear_plan_layouts(int32_t fmt, int64_t M, int64_t N, int64_t K, int32_t w_layout,
                                int32_t a_packed, ql_plan* out_plan);
@@ -409,6 +420,44 @@ ql_status qlinear_run_debug_acc(ql_plan plan, const void* a_q, const void* a_sca
 ql_status qlinear_forward(ql_plan plan, const void* x_bf16, void* a_q, void* a_scale,
                           const void* w_q, const void* w_scale, void* y_bf16,
                           void* workspace, void* stream);
+
+/*
+ * The gated MLP of a decode step as a chain: gate_up with the SiLU-and-mul
+ * epilogue, then down, whose input H must be quantized per token.  The
+ * deep-dive page lists fused epilogues -- activations, and quantization of the
+ * output for the next layer -- among what a GEMM's write-back can carry
+ * ([Deep dive] "Understanding Helion").  A per-token scale needs the whole
+ * row's amax, which no single workgroup of gate_up sees; so the SiLU-and-mul
+ * epilogue folds max |bf16(h)| of each token into a small buffer with atomic
+ * maxima (exact: a maximum does not depend on the order), and down's
+ * workgroups each quantize only their own K chunk of H with the rule of
+ * qlinear_quantize_act (s = fl(amax / Q), code = round(fl(h / s)), the same
+ * codes and scales bit for bit), in the GEMM launch itself: no separate
+ * quantizer launch and no second pass over H.
+ *
+ * h_amax / x_amax: M + 1 32-bit words, 16-byte aligned, caller-owned, all
+ * zero before the first producer runs: words 0..M-1 hold the binary32 bit
+ * patterns of the token maxima, word M an arrival counter.  The consumer
+ * (qlinear_forward_amax) leaves them all zero again, so one buffer serves
+ * every layer in turn; a producer must be followed by exactly one consumer
+ * before the next producer.
+ *
+ * qlinear_forward_glu_amax: qlinear_forward of a SiLU-and-mul plan
+ * (qlinear_plan_glu, FP8_Dynamic or W8A8_INT8) that also accumulates the
+ * per-token amax of its output H [M, N/2] into h_amax.  K must be > 0.
+ * qlinear_forward_amax: qlinear_forward of a plan from qlinear_plan_layouts
+ * (..., a_packed = 3) for X whose amax words are x_amax.  An a_mode 5 plan is
+ * one launch that reads X (bf16, the whole of it across the grid, each
+ * workgroup its K chunk) and writes a_q / a_scale as qlinear_quantize_act_packed
+ * would; any other plan runs the quantizer and the GEMM and then clears the
+ * words.  Either way x_amax is all zero afterwards.  Enqueue-only.
+ */
+ql_status qlinear_forward_glu_amax(ql_plan plan, const void* x_bf16, void* a_q, void* a_scale,
+                                   const void* w_q, const void* w_scale, void* h_bf16, void* h_amax,
+                                   void* workspace, void* stream);
+ql_status qlinear_forward_amax(ql_plan plan, const void* x_bf16, void* x_amax, void* a_q, void* a_scale,
+                               const void* w_q, const void* w_scale, void* y_bf16, void* workspace,
+                               void* stream);
 
 /*
  * For callers that cannot allocate device memory -- code running under

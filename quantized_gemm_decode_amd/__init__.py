@@ -453,6 +453,41 @@ def qlinear_forward(plan, x, a_q, a_scale, w_q, w_scale, y, workspace=None, stre
            "qlinear_forward")
 
 
+def amax_buffer(M, device="cuda"):
+    """Zeroed per-token amax words (M maxima + the consumer's counter) for
+    qlinear_forward_glu_amax / qlinear_forward_amax; reusable, the consumer
+    leaves it zeroed."""
+    return torch.zeros(-(-(M + 1) // 4) * 4, dtype=torch.int32, device=device)
+
+
+def _need_amax(plan, t, name):
+    _need(t, name, 4 * (plan.M + 1))
+
+
+def qlinear_forward_glu_amax(plan, x, a_q, a_scale, w_q, w_scale, h, h_amax, workspace=None, stream=None):
+    """SiLU-and-mul forward that also folds max |h| per token into h_amax."""
+    plan.check_operands(x=x, a_q=a_q, a_scale=a_scale, w_q=w_q, w_scale=w_scale, y=h, workspace=workspace)
+    _need_amax(plan, h_amax, "h_amax")
+    _check(lib().qlinear_forward_glu_amax(plan.handle, _ptr(x, "x", torch.bfloat16), _ptr(a_q, "a_q", CODE_DTYPES),
+                                          _ptr(a_scale, "a_scale", SCALE_DTYPES), _ptr(w_q, "w_q", CODE_DTYPES),
+                                          _ptr(w_scale, "w_scale", SCALE_DTYPES), _ptr(h, "h", torch.bfloat16),
+                                          _ptr(h_amax, "h_amax", torch.int32),
+                                          _ptr(workspace, "workspace", required=False), _stream(stream)),
+           "qlinear_forward_glu_amax")
+
+
+def qlinear_forward_amax(plan, x, x_amax, a_q, a_scale, w_q, w_scale, y, workspace=None, stream=None):
+    """Forward of X whose per-token amax words are x_amax (left zeroed)."""
+    plan.check_operands(x=x, a_q=a_q, a_scale=a_scale, w_q=w_q, w_scale=w_scale, y=y, workspace=workspace)
+    _need_amax(plan, x_amax, "x_amax")
+    _check(lib().qlinear_forward_amax(plan.handle, _ptr(x, "x", torch.bfloat16), _ptr(x_amax, "x_amax", torch.int32),
+                                      _ptr(a_q, "a_q", CODE_DTYPES), _ptr(a_scale, "a_scale", SCALE_DTYPES),
+                                      _ptr(w_q, "w_q", CODE_DTYPES), _ptr(w_scale, "w_scale", SCALE_DTYPES),
+                                      _ptr(y, "y", torch.bfloat16), _ptr(workspace, "workspace", required=False),
+                                      _stream(stream)),
+           "qlinear_forward_amax")
+
+
 def qlinear_forward_noalloc(plan, x, a_q, a_scale, w_q, w_scale, y, stream=None):
     """qlinear_forward with the split-K workspace taken from the library's
     per-GPU scratch (no allocation; calls on one GPU must not overlap)."""

@@ -54,6 +54,8 @@ SIGNATURES = {
     "qlinear_run_debug_acc": (c_i32, [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp]),
     "qlinear_forward": (c_i32, [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp]),
     "qlinear_forward_noalloc": (c_i32, [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp]),
+    "qlinear_forward_glu_amax": (c_i32, [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp]),
+    "qlinear_forward_amax": (c_i32, [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp]),
     "qlinear_graph_begin": (c_i32, [c_vp]),
     "qlinear_graph_end": (c_i32, [c_vp, ctypes.POINTER(c_vp)]),
     "qlinear_graph_launch": (c_i32, [c_vp, c_vp]),

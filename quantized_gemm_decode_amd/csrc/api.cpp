@@ -78,7 +78,8 @@ struct TableEntry {
   ql_config cfg;
   double us;
   int us_class;  // 2: a forward-only entry (its time covers quantize + GEMM); 3: a SiLU-and-mul forward
-                 // entry (qlinear_plan_glu); else act_class(a_mode)
+                 // entry (qlinear_plan_glu); 4: a forward entry for inputs whose per-token amax is
+                 // given (qlinear_forward_amax); else act_class(a_mode)
 };
 
 std::mutex g_table_mu;
@@ -91,9 +92,11 @@ int64_t bucket_of(int64_t M) {
 }
 
 // Activation class of a configuration: 0 row-major A_q (a_mode 0, 1), 1 packed
-// A_q (2, 3), 2 forward-only plans (fused quantization, 4).  A class-2 table
-// entry is the best plan for quantize + GEMM, fused or not.
-int act_class(int32_t a_mode) { return a_mode == 4 ? 2 : (a_mode >= 2 ? 1 : 0); }
+// A_q (2, 3), 2 forward-only plans (fused quantization, 4), 4 forward plans
+// of an input whose per-token amax is given (5).  A class-2 table entry is
+// the best plan for quantize + GEMM, fused or not; a class-4 entry the best
+// for the same with the amax given (a_mode 5, or a packed-A plan).
+int act_class(int32_t a_mode) { return a_mode == 5 ? 4 : a_mode == 4 ? 2 : (a_mode >= 2 ? 1 : 0); }
 
 bool table_lookup(int32_t fmt, int32_t layout, int a_class, int64_t M, int64_t N, int64_t K, ql_config* out) {
   std::lock_guard<std::mutex> lk(g_table_mu);
@@ -321,6 +324,20 @@ std::vector<ql_config> heuristic_candidates(int32_t fmt, int32_t layout, int a_c
     b.waves_k = 1;
     first_swap = 1;
   }
+  if (a_class == 4 && M <= 16 && K % 128 == 0 && layout == 1 && (fmt == QL_FP8_DYNAMIC || fmt == QL_W8A8_INT8)) {
+    // the given amax lets a workgroup quantize just its K chunk: split so that
+    // M x chunk stays within the 16384 values a workgroup holds
+    ql_config f = b;
+    int64_t sp = 1;
+    while (M * ((G + sp - 1) / sp) * 128 > kFusedMaxValues && sp < 256) sp *= 2;
+    f.a_mode = 5;
+    f.split_k = (int32_t)sp;
+    f.waves_n = 1;
+    f.waves_k = groups <= 256 ? 16 : 4;
+    f.rows_per_wave = 16;
+    f.prefetch = 1;
+    out.push_back(f);
+  }
   if (a_class == 2 && M <= 2) {
     ql_config f = b;
     f.a_mode = 4;
@@ -439,7 +456,11 @@ ql_status build_plan(int32_t fmt, int64_t M, int64_t N, int64_t K, const ql_conf
   if (cfg.rows_per_wave != 16 && cfg.rows_per_wave != 32 && cfg.rows_per_wave != 64)
     return fail(QL_E_INVALID, "rows_per_wave must be 16, 32 or 64");
   if (cfg.prefetch != 1 && cfg.prefetch != 2 && cfg.prefetch != 4) return fail(QL_E_INVALID, "prefetch must be 1, 2 or 4");
-  if (cfg.a_mode < 0 || cfg.a_mode > 4) return fail(QL_E_INVALID, "a_mode must be 0, 1, 2, 3 or 4");
+  if (cfg.a_mode < 0 || cfg.a_mode > 5) return fail(QL_E_INVALID, "a_mode must be 0, 1, 2, 3, 4 or 5");
+  if (cfg.a_mode == 5 && (fmt != QL_FP8_DYNAMIC && fmt != QL_W8A8_INT8))
+    return fail(QL_E_UNSUPPORTED, "a_mode 5 (per-token amax given) serves FP8_Dynamic and W8A8_INT8");
+  if (cfg.a_mode == 5 && (glu || M > 16 || K % 128))
+    return fail(QL_E_UNSUPPORTED, "a_mode 5 needs M <= 16, K %% 128 == 0 and a plain (not SiLU-and-mul) epilogue");
   if (cfg.a_mode >= 2 && !cfg.w_layout) return fail(QL_E_UNSUPPORTED, "packed activations need packed weights");
   if (cfg.a_mode == 4 && fmt != QL_BLOCK_FP8 && (M > 16 || M * K > kFusedMaxValues || K % 512))
     return fail(QL_E_UNSUPPORTED, "fused per-token quantization needs M <= 16, M*K <= %lld and K %% 512 == 0",
@@ -463,7 +484,7 @@ ql_status build_plan(int32_t fmt, int64_t M, int64_t N, int64_t K, const ql_conf
   p->chunks = p->G > 0 ? (p->G + p->chunk_kb - 1) / p->chunk_kb : 1;
   p->mt = M <= 16 ? 1 : (M <= 32 ? 2 : 4);
   // Block_FP8 fused quantization reads only its K chunk: M * chunk values
-  if (cfg.a_mode == 4 && fmt == QL_BLOCK_FP8 && (M > 16 || M * p->chunk_kb * 128 > kFusedMaxValues)) {
+  if ((cfg.a_mode == 4 && fmt == QL_BLOCK_FP8 || cfg.a_mode == 5) && (M > 16 || M * p->chunk_kb * 128 > kFusedMaxValues)) {
     const long long chunk = (long long)p->chunk_kb * 128;
     delete p;
     return fail(QL_E_UNSUPPORTED, "fused group quantization needs M <= 16 and M * chunk <= %lld (chunk %lld)",
@@ -475,7 +496,7 @@ ql_status build_plan(int32_t fmt, int64_t M, int64_t N, int64_t K, const ql_conf
   p->bn = glu ? cfg.waves_n * 16 : cfg.waves_n * rg * 16;
   p->n_tiles = (int)(((glu ? N / 2 : N) + p->bn - 1) / p->bn);
   const int64_t lds_a = (cfg.a_mode == 1 || cfg.a_mode == 3) ? (int64_t)p->chunk_kb * p->mt * 2048
-                       : cfg.a_mode == 4 ? 512 + M * ((int64_t)p->chunk_kb * 128 + 64) +
+                       : cfg.a_mode >= 4 ? 512 + M * ((int64_t)p->chunk_kb * 128 + 64) +
                                                (fmt == QL_BLOCK_FP8 ? M * (int64_t)p->chunk_kb * 4 : 0)
                                          : 0;
   const int64_t lds_w = (cfg.w_lds && !cfg.w_layout) ? (int64_t)nw * 2 * rg * 2048 : 0;
@@ -522,12 +543,17 @@ bool parse_force(ql_config* c) {
 
 // x / aq_out / sa_out: the fused plans' input X and their quantizer outputs
 // (a_q and a_scale are then unused).
+// amax: the per-token amax words of X and their counter (activation mode 5,
+// required), or the SiLU-and-mul epilogue's amax output (optional).
 ql_status launch_gemm(const ql_plan_s* p, const void* a_q, const void* a_scale, const void* w_q,
                       const void* w_scale, void* y, void* workspace, void* acc_out, hipStream_t s,
                       bool from_forward = false, const void* x = nullptr, void* aq_out = nullptr,
-                      float* sa_out = nullptr) {
-  const bool fused = !p->tiled && p->cfg.a_mode == 4;
+                      float* sa_out = nullptr, uint32_t* amax = nullptr) {
+  const bool fused = !p->tiled && (p->cfg.a_mode == 4 || p->cfg.a_mode == 5);
   if (fused && !from_forward) return fail(QL_E_INVALID, "a fused-quantization plan runs through qlinear_forward");
+  if (!p->tiled && p->cfg.a_mode == 5 && !amax)
+    return fail(QL_E_INVALID, "an a_mode 5 plan runs through qlinear_forward_amax (it reads the given amax)");
+  if (amax && !aligned16(amax)) return fail(QL_E_ALIGN, "amax is not 16-byte aligned");
   if (p->glu && acc_out) return fail(QL_E_UNSUPPORTED, "raw accumulators are not kept by a SiLU-and-mul plan");
   if (p->M == 0 || p->N == 0) return QL_OK;
   if (!y) return fail(QL_E_INVALID, "y is NULL");
@@ -563,6 +589,7 @@ ql_status launch_gemm(const ql_plan_s* p, const void* a_q, const void* a_scale, 
   a.x = static_cast<const uint16_t*>(x);
   a.aq_out = static_cast<uint8_t*>(aq_out);
   a.sa_out = sa_out;
+  a.amax = amax;
   a.M = (int)p->M;
   a.N = (int)p->N;
   a.K = (int)p->K;
@@ -647,13 +674,14 @@ ql_status device_scratch(hipStream_t s, void** out) {
 }
 
 ql_status forward_impl(ql_plan p, const void* x_bf16, void* a_q, void* a_scale, const void* w_q,
-                       const void* w_scale, void* y, void* workspace, void* stream) {
-  if (!p->tiled && p->cfg.a_mode == 4)
+                       const void* w_scale, void* y, void* workspace, void* stream, uint32_t* amax = nullptr) {
+  if (!p->tiled && (p->cfg.a_mode == 4 || p->cfg.a_mode == 5))
     return launch_gemm(p, nullptr, nullptr, w_q, w_scale, y, workspace, nullptr, static_cast<hipStream_t>(stream),
-                       true, x_bf16, a_q, static_cast<float*>(a_scale));
+                       true, x_bf16, a_q, static_cast<float*>(a_scale), amax);
   ql_status st = quantize_act(p->fmt, x_bf16, p->M, p->K, a_q, a_scale, p->cfg.a_mode >= 2, stream);
   if (st != QL_OK) return st;
-  return launch_gemm(p, a_q, a_scale, w_q, w_scale, y, workspace, nullptr, static_cast<hipStream_t>(stream));
+  return launch_gemm(p, a_q, a_scale, w_q, w_scale, y, workspace, nullptr, static_cast<hipStream_t>(stream), false,
+                     nullptr, nullptr, nullptr, amax);
 }
 
 }  // namespace
@@ -765,9 +793,9 @@ ql_status qlinear_table_load(const char* path, int64_t* n_entries) {
     std::string kind;
     e.us_class = act_class(e.cfg.a_mode);
     if (is >> kind) {
-      if (kind != "fwd" && kind != "glu")
+      if (kind != "fwd" && kind != "glu" && kind != "amx")
         return fail(QL_E_TABLE, "%s:%d: unknown entry kind '%s'", path, lineno, kind.c_str());
-      e.us_class = kind == "glu" ? 3 : 2;
+      e.us_class = kind == "glu" ? 3 : kind == "amx" ? 4 : 2;
     }
     if (!valid_fmt(e.fmt) || M < 1 || N < 1 || K < 1) return fail(QL_E_TABLE, "%s:%d: bad key", path, lineno);
     e.M = M;
@@ -794,15 +822,27 @@ static ql_status plan_for_layout(int32_t fmt, int32_t layout, int a_class, int64
   ql_config c;
   if (parse_force(&c)) {
     const int fc = act_class(c.a_mode);
-    if (c.w_layout != layout || (a_class == 2 ? fc == 0 : fc != a_class))
-      return fail(QL_E_INVALID, "QLINEAR_FORCE names other operand layouts");
+    const bool ok = a_class == 2 ? (fc == 1 || fc == 2) : a_class == 4 ? (fc == 1 || fc == 4) : fc == a_class;
+    if (c.w_layout != layout || !ok) return fail(QL_E_INVALID, "QLINEAR_FORCE names other operand layouts");
     return build_plan(fmt, M, N, K, c, QL_SRC_CUSTOM, out_plan);
   }
-  if (table_lookup(fmt, layout, a_class, M, N, K, &c)) return build_plan(fmt, M, N, K, c, QL_SRC_TABLE, out_plan);
-  // a forward plan without its own entry: the packed-activation plan
-  if (a_class == 2 && table_lookup(fmt, layout, 1, M, N, K, &c))
-    return build_plan(fmt, M, N, K, c, QL_SRC_TABLE, out_plan);
+  // a table entry that no longer builds (an instantiation removed since the
+  // sweep) falls through to the heuristic instead of failing the plan
+  if (table_lookup(fmt, layout, a_class, M, N, K, &c) && build_plan(fmt, M, N, K, c, QL_SRC_TABLE, out_plan) == QL_OK)
+    return QL_OK;
   ql_status st = QL_E_UNSUPPORTED;
+  // a given-amax forward plan without its own entry: a_mode 5 by the heuristic, else the packed-A plan
+  if (a_class == 4) {
+    for (const ql_config& h : heuristic_candidates(fmt, layout, 4, M, N, K))
+      if (h.a_mode == 5 && build_plan(fmt, M, N, K, h, QL_SRC_HEURISTIC, out_plan) == QL_OK) return QL_OK;
+    a_class = 1;
+    if (table_lookup(fmt, layout, 1, M, N, K, &c) && build_plan(fmt, M, N, K, c, QL_SRC_TABLE, out_plan) == QL_OK)
+      return QL_OK;
+  }
+  // a forward plan without its own entry: the packed-activation plan
+  if (a_class == 2 && table_lookup(fmt, layout, 1, M, N, K, &c) &&
+      build_plan(fmt, M, N, K, c, QL_SRC_TABLE, out_plan) == QL_OK)
+    return QL_OK;
   for (const ql_config& h : heuristic_candidates(fmt, layout, a_class, M, N, K))
     if ((st = build_plan(fmt, M, N, K, h, QL_SRC_HEURISTIC, out_plan)) == QL_OK) break;
   return st;
@@ -818,9 +858,11 @@ ql_status qlinear_plan_packed(int32_t fmt, int64_t M, int64_t N, int64_t K, ql_p
 
 ql_status qlinear_plan_layouts(int32_t fmt, int64_t M, int64_t N, int64_t K, int32_t w_layout, int32_t a_packed,
                                ql_plan* out_plan) {
-  if (a_packed < 0 || a_packed > 2) return fail(QL_E_INVALID, "a_packed must be 0, 1 or 2");
+  if (a_packed < 0 || a_packed > 3) return fail(QL_E_INVALID, "a_packed must be 0, 1, 2 or 3");
   if (a_packed && !w_layout) return fail(QL_E_UNSUPPORTED, "packed activations need packed weights");
-  return plan_for_layout(fmt, w_layout, a_packed, M, N, K, out_plan);
+  if (a_packed == 3 && fmt != QL_FP8_DYNAMIC && fmt != QL_W8A8_INT8)
+    return fail(QL_E_UNSUPPORTED, "given-amax forward plans serve FP8_Dynamic and W8A8_INT8");
+  return plan_for_layout(fmt, w_layout, a_packed == 3 ? 4 : a_packed, M, N, K, out_plan);
 }
 
 ql_status qlinear_encode_e4m3(const float* x, int64_t n, void* codes, void* stream) {
@@ -963,6 +1005,35 @@ ql_status qlinear_forward(ql_plan p, const void* x_bf16, void* a_q, void* a_scal
                           const void* w_scale, void* y, void* workspace, void* stream) {
   if (!p) return fail(QL_E_INVALID, "plan is NULL");
   return forward_impl(p, x_bf16, a_q, a_scale, w_q, w_scale, y, workspace, stream);
+}
+
+ql_status qlinear_forward_glu_amax(ql_plan p, const void* x_bf16, void* a_q, void* a_scale, const void* w_q,
+                                   const void* w_scale, void* h_bf16, void* h_amax, void* workspace, void* stream) {
+  if (!p) return fail(QL_E_INVALID, "plan is NULL");
+  if (!p->glu) return fail(QL_E_INVALID, "qlinear_forward_glu_amax takes a SiLU-and-mul plan");
+  if (p->fmt != QL_FP8_DYNAMIC && p->fmt != QL_W8A8_INT8)
+    return fail(QL_E_UNSUPPORTED, "the per-token amax of H serves FP8_Dynamic and W8A8_INT8");
+  if (!h_amax && p->M > 0 && p->N > 0 && p->K > 0) return fail(QL_E_INVALID, "h_amax is NULL");
+  if (p->K == 0) return fail(QL_E_UNSUPPORTED, "K = 0: H is zero, its amax is not accumulated");
+  return forward_impl(p, x_bf16, a_q, a_scale, w_q, w_scale, h_bf16, workspace, stream, static_cast<uint32_t*>(h_amax));
+}
+
+ql_status qlinear_forward_amax(ql_plan p, const void* x_bf16, void* x_amax, void* a_q, void* a_scale, const void* w_q,
+                               const void* w_scale, void* y, void* workspace, void* stream) {
+  if (!p) return fail(QL_E_INVALID, "plan is NULL");
+  if (p->glu) return fail(QL_E_INVALID, "qlinear_forward_amax takes a plain (not SiLU-and-mul) plan");
+  if (p->fmt != QL_FP8_DYNAMIC && p->fmt != QL_W8A8_INT8)
+    return fail(QL_E_UNSUPPORTED, "the given per-token amax serves FP8_Dynamic and W8A8_INT8");
+  if (p->M == 0) return QL_OK;
+  if (!x_amax) return fail(QL_E_INVALID, "x_amax is NULL");
+  if (!aligned16(x_amax)) return fail(QL_E_ALIGN, "x_amax is not 16-byte aligned");
+  if (!p->tiled && p->cfg.a_mode == 5 && p->N > 0 && p->K > 0)
+    return forward_impl(p, x_bf16, a_q, a_scale, w_q, w_scale, y, workspace, stream, static_cast<uint32_t*>(x_amax));
+  // any other plan: the quantizer finds the amax itself; then clear the words for the next producer
+  ql_status st = forward_impl(p, x_bf16, a_q, a_scale, w_q, w_scale, y, workspace, stream);
+  if (st != QL_OK) return st;
+  hipError_t e = qlk::launch_fill_zero_bf16(x_amax, 2 * (p->M + 1), static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? QL_OK : hip_fail(e, "amax clear");
 }
 
 ql_status qlinear_forward_noalloc(ql_plan p, const void* x_bf16, void* a_q, void* a_scale, const void* w_q,

@@ -33,6 +33,11 @@ struct DecodeArgs {
   const uint16_t* x;   // X [M, K] bf16
   uint8_t* aq_out;     // packed A_q, ceil(M/16) x G tiles of 2 KB
   float* sa_out;       // s_a [M]
+  // per-token amax words of X (binary32 bit patterns of max |x| per row),
+  // then one arrival counter: written by a SiLU-and-mul plan's epilogue
+  // (atomic max over its output H) when non-null; read -- and reset to zero
+  // by the last workgroup -- by an activation-mode-5 plan
+  uint32_t* amax;
   int M, N, K;
   int G;               // number of 128-wide K blocks, ceil(K / 128)
   int split;           // number of K chunks (workgroups per output tile)
@@ -51,7 +56,8 @@ struct DecodeKey {
   int nw;    // waves per workgroup (4, 8 or 16)
   int pf;    // K blocks per prefetch batch
   int alds;  // activations: 0 row-major from L2, 1 row-major staged in LDS, 2 packed from L2,
-             // 3 packed staged in LDS, 4 quantized from X inside the kernel (fused)
+             // 3 packed staged in LDS, 4 quantized from X inside the kernel (fused), 5 the same
+             // with the per-token amax given (each workgroup reads only its K chunk of X)
   int wm;    // weight mode: W_DIRECT / W_LDS_TRANSPOSE / W_PACKED
   int glu;   // 1: merged gate/up weight, SiLU-and-mul epilogue, output [M, N/2]
 };

@@ -70,12 +70,16 @@ __device__ __forceinline__ uint32_t epilogue_scaled(float accf, float sa, float 
 // output columns, so both values of an output element meet in one lane.
 template <int FMT, bool SWAP, int MT, int RG, int NW, int PF, int AL, int WM, bool GLU>
 __global__ void __launch_bounds__(NW * 64) qgemm_decode_kernel(DecodeArgs p) {
-  constexpr bool FUSED = AL == 4;                     // activations quantized here from bf16 X
+  constexpr bool FUSED = AL == 4 || AL == 5;          // activations quantized here from bf16 X
+  // the workgroup reads only its K chunk of X: Block_FP8 (1 x 128 groups are
+  // local) and activation mode 5 (per-token amax given by the producer of X)
+  constexpr bool CHUNKED = FUSED && (FMT == FMT_BLOCK || AL == 5);
   constexpr bool ALDS = AL == 1 || AL == 3 || FUSED;  // activations read from LDS
   constexpr bool AP = AL == 2;                        // packed activations, read per K block like packed weights
   constexpr bool WL = WM == W_LDS_TRANSPOSE;
   constexpr bool WP = WM == W_PACKED;
   static_assert(!FUSED || (MT == 1 && WP), "fused quantization: one token tile, packed weights");
+  static_assert(AL != 5 || ((FMT == FMT_FP8 || FMT == FMT_INT8) && !GLU), "given amax: per-token formats");
   static_assert(!GLU || (RG == 2 && WP), "SiLU-and-mul: a gate and an up row group per wave, packed weights");
   static_assert(FMT != FMT_MX || (!FUSED && !GLU), "MXFP8: quantized activations in, plain bf16 out");
   static_assert(FMT != FMT_MX4 || (!FUSED && !GLU && WP), "MXFP4: packed weights, quantized activations");
@@ -433,11 +437,25 @@ __global__ void __launch_bounds__(NW * 64) qgemm_decode_kernel(DecodeArgs p) {
   // lanes of a row of the wave hold one group.
   constexpr int XP = FUSED ? 32 / NW : 1;
   u32x4 xv[XP];
+  uint32_t xam[XP];                              // activation mode 5: the amax word of each piece's row
   const uint32_t upr = K / 512u;                 // per-token: wave pieces per token row
-  const uint32_t ppr = (uint32_t)nkc * 16u;      // Block_FP8: pieces per row of the chunk
+  const uint32_t ppr = (uint32_t)nkc * 16u;      // chunked: pieces per row of the chunk
+  if constexpr (AL == 5) {
+    // the row amax words first (older than the X and weight loads, so the
+    // wait for X covers them), as agent-scope loads: the producer's atomic
+    // maxima are performed at the device's coherence point
+#pragma unroll
+    for (int i = 0; i < XP; ++i) {
+      const uint32_t P = (uint32_t)(tid + NW * 64 * i);
+      const uint32_t m = P / ppr;
+      xam[i] = (uint32_t)(wave * 64 + NW * 64 * i) < M * ppr && m < M
+                   ? __hip_atomic_load(p.amax + m, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                   : 0u;
+    }
+  }
   if constexpr (FUSED) {
     const __amdgpu_buffer_rsrc_t rx = make_rsrc(p.x, M * K * 2u);
-    const uint32_t npc = FMT == FMT_BLOCK ? M * ppr : M * K / 8u;
+    const uint32_t npc = CHUNKED ? M * ppr : M * K / 8u;
     // a wave issues only the loads whose pieces exist (a wave-uniform test;
     // the wait below counts the weight loads, which are all younger)
 #pragma unroll
@@ -446,7 +464,7 @@ __global__ void __launch_bounds__(NW * 64) qgemm_decode_kernel(DecodeArgs p) {
       xv[i] = u32x4{0u, 0u, 0u, 0u};
       if ((uint32_t)(wave * 64 + NW * 64 * i) < npc) {
         uint32_t off;
-        if constexpr (FMT == FMT_BLOCK) {
+        if constexpr (CHUNKED) {
           const uint32_t m = P / ppr, w = P - m * ppr;
           off = (m * K + (uint32_t)kb0 * 128u + w * 8u) * 2u;
         } else {
@@ -461,7 +479,10 @@ __global__ void __launch_bounds__(NW * 64) qgemm_decode_kernel(DecodeArgs p) {
 
   // Two batches in flight: the loop enters and repeats with the same pair of
   // buffers outstanding (batch b in wb0, b+1 in wb1), and each buffer is
-  // refilled right after it has been consumed.
+  // refilled right after it has been consumed.  (Four batches during a fused
+  // prologue, so that the weight stream would not idle while X is read and
+  // quantized, made the FP8 and INT8 fused launches 3-24 % slower: the
+  // prologue's cost is its quantization arithmetic, not a weight stall.)
   issue(wb0, ab0, sa0, sw0, 0);
   issue(wb1, ab1, sa1, sw1, 1);
 
@@ -495,6 +516,36 @@ __global__ void __launch_bounds__(NW * 64) qgemm_decode_kernel(DecodeArgs p) {
         p.sa_out[m * (uint32_t)p.G + (uint32_t)kb0 + kbl] = ssb[m * (uint32_t)p.chunk_kb + kbl];
       }
     }
+  } else if constexpr (AL == 5) {
+    constexpr int NW_LOADS = 2 * PF * 2 * RG;  // weight loads of the two batches, issued after X
+    static_assert(NW_LOADS <= 63, "vmcnt holds 6 bits");
+    __builtin_amdgcn_s_waitcnt((NW_LOADS & 15) | (7 << 4) | (15 << 8) | ((NW_LOADS >> 4) << 14));
+    float* ssc = reinterpret_cast<float*>(smem + FA_SC);
+    const uint32_t npc = M * ppr;
+#pragma unroll
+    for (int i = 0; i < XP; ++i) {
+      const uint32_t P = (uint32_t)(tid + NW * 64 * i);
+      if ((uint32_t)(wave * 64 + NW * 64 * i) >= npc) continue;   // no piece of this wave
+      if (P < npc) {
+        const uint32_t m = P / ppr, w = P - m * ppr;
+        const float sc = scale_of<FMT>(__uint_as_float(xam[i]));
+        *reinterpret_cast<u32x2*>(smem + FA0 + m * (uint32_t)CH + w * 8u) = quant8<FMT>(xv[i], sc, recip_of(sc));
+        if (w == 0u) ssc[m] = sc;
+      }
+    }
+    lds_barrier();
+    // Every wave of this workgroup has its amax words (the wait above), so
+    // count the workgroup; the last of the grid resets the words and the
+    // counter for the next producer.
+    if (tid == 0) {
+      const unsigned prev = __hip_atomic_fetch_add(p.amax + M, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (prev == gridDim.x - 1u) {
+        for (uint32_t m = 0; m < M; ++m)
+          __hip_atomic_exchange(p.amax + m, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_exchange(p.amax + M, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+    if (p.aq_out && tile == 0 && chunk == 0 && (uint32_t)tid < M) p.sa_out[tid] = ssc[tid];
   } else if constexpr (FUSED) {
     constexpr int NW_LOADS = 2 * PF * 2 * RG;  // weight loads of the two batches, issued after X
     static_assert(NW_LOADS <= 63, "vmcnt holds 6 bits");
@@ -690,12 +741,15 @@ __global__ void __launch_bounds__(NW * 64) qgemm_decode_kernel(DecodeArgs p) {
   // an output element are the binary32 epilogue values of the two rows;
   // h = g / (1 + exp(-g)) * u, rounded to bf16 once, stored to Y [M, N/2].
   if constexpr (GLU) {
+    // |bf16(h)| of each stored element, for the per-token amax of H
+    float habs[MT][4];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const uint32_t x = SWAP ? (uint32_t)(4 * g + r) : (uint32_t)r16;
         const uint32_t m = SWAP ? (uint32_t)(mt * 16 + r16) : (uint32_t)(mt * 16 + 4 * g + r);
+        habs[mt][r] = 0.0f;
         float t[2];
 #pragma unroll
         for (int rg = 0; rg < 2; ++rg) {
@@ -711,7 +765,38 @@ __global__ void __launch_bounds__(NW * 64) qgemm_decode_kernel(DecodeArgs p) {
           }
         }
         const float h = __fmul_rn(__fdiv_rn(t[0], 1.0f + expf(-t[0])), t[1]);
-        if (m < M && rowok(0, x)) p.y[(size_t)m * IH + (uint32_t)obase + x] = (uint16_t)bf16_rne(h);
+        if (m < M && rowok(0, x)) {
+          const uint32_t hb = bf16_rne(h);
+          p.y[(size_t)m * IH + (uint32_t)obase + x] = (uint16_t)hb;
+          habs[mt][r] = bf16_to_f32(hb & 0x7fffu);
+        }
+      }
+    }
+    // Per-token amax of H for a consumer that quantizes it (activation mode
+    // 5): the largest |h| of each token over this wave's columns, then an
+    // atomic maximum on its binary32 bit pattern (non-negative, so the
+    // integer order is the numeric one; exact whatever the order).
+    if (p.amax) {
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        if constexpr (SWAP) {
+          // lane: token 16mt + r16, columns 4g..4g+3 -> fold r, then the four lane groups
+          float v = fmaxf(fmaxf(habs[mt][0], habs[mt][1]), fmaxf(habs[mt][2], habs[mt][3]));
+          v = fmaxf(v, __shfl_xor(v, 16));
+          v = fmaxf(v, __shfl_xor(v, 32));
+          const uint32_t m = (uint32_t)(mt * 16 + r16);
+          if (g == 0 && m < M)
+            __hip_atomic_fetch_max(p.amax + m, __float_as_uint(v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        } else {
+          // lane: column r16, tokens 16mt + 4g + r -> fold the 16 columns of the DPP row
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float v = row16_max_nonneg(habs[mt][r]);
+            const uint32_t m = (uint32_t)(mt * 16 + 4 * g + r);
+            if (r16 == 0 && m < M)
+              __hip_atomic_fetch_max(p.amax + m, __float_as_uint(v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          }
+        }
       }
     }
     return;
@@ -827,7 +912,10 @@ constexpr bool decode_variant_ok() {
   if constexpr (FMT == FMT_MX4) {
     if (mx4_spills<NW_, MT_, RG_, PF_, AL>()) return false;
   }
-  if constexpr (AL == 4) {
+  if constexpr (AL == 5) {
+    if (FMT != FMT_FP8 && FMT != FMT_INT8) return false;
+  }
+  if constexpr (AL == 4 || AL == 5) {
     if (MT_ != 1 || WM_ != W_PACKED) return false;
     const int estimate = 2 * PF_ * (RG_ + MT_) * 8 + RG_ * MT_ * 4 + 40 + 4 * (32 / NW_);
     return estimate <= (NW_ >= 16 ? 128 : 256) && decode_config_fits<FMT, NW_, SW, MT_, RG_, PF_>();
@@ -873,14 +961,14 @@ hipError_t decode_dispatch(const DecodeKey& k, dim3 grid, dim3 block, size_t lds
   QL_TRY(4, SW, MT_, RG_, PF_, AL, 0) QL_TRY(4, SW, MT_, RG_, PF_, AL, 1) QL_TRY(4, SW, MT_, RG_, PF_, AL, 2)
 #define QL_TRY_AL(SW, MT_, RG_, PF_)                                                      \
   QL_TRY_WL(SW, MT_, RG_, PF_, 0) QL_TRY_WL(SW, MT_, RG_, PF_, 1) QL_TRY(4, SW, MT_, RG_, PF_, 2, 2) \
-  QL_TRY(4, SW, MT_, RG_, PF_, 3, 2) QL_TRY(4, SW, MT_, RG_, PF_, 4, 2)
+  QL_TRY(4, SW, MT_, RG_, PF_, 3, 2) QL_TRY(4, SW, MT_, RG_, PF_, 4, 2) QL_TRY(4, SW, MT_, RG_, PF_, 5, 2)
 #define QL_TRY_PF(SW, MT_, RG_) QL_TRY_AL(SW, MT_, RG_, 2) QL_TRY_AL(SW, MT_, RG_, 4)
 #define QL_TRY_RG(SW, MT_) QL_TRY_PF(SW, MT_, 1) QL_TRY_PF(SW, MT_, 2)
   // packed weights, activations (row-major or packed) from L2: wider workgroups,
   // longer rows, 1-block batches
 #define QL_TRY_PA(NW_, SW, MT_, RG_, PF_)                                                      \
   QL_TRY(NW_, SW, MT_, RG_, PF_, 0, 2) QL_TRY(NW_, SW, MT_, RG_, PF_, 2, 2) QL_TRY(NW_, SW, MT_, RG_, PF_, 3, 2) \
-  QL_TRY(NW_, SW, MT_, RG_, PF_, 4, 2)
+  QL_TRY(NW_, SW, MT_, RG_, PF_, 4, 2) QL_TRY(NW_, SW, MT_, RG_, PF_, 5, 2)
 #define QL_TRY_P(NW_, SW, MT_, RG_) QL_TRY_PA(NW_, SW, MT_, RG_, 1) QL_TRY_PA(NW_, SW, MT_, RG_, 2)
 #define QL_TRY_PN(SW, MT_)                                                                    \
   QL_TRY_PA(4, SW, MT_, 1, 1) QL_TRY_PA(4, SW, MT_, 2, 1) QL_TRY_P(4, SW, MT_, 4)             \

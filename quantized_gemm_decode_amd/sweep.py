@@ -52,7 +52,9 @@ if ROOT not in sys.path:
 
 from workloads import config_by_name, decode_workloads, make_inputs  # noqa: E402
 
-SPLITS = (1, 2, 4, 8, 16, 32)
+# split_k over the pages' powers of two 1..256 (clamped to the K blocks; only
+# distinct chunk counts are timed)
+SPLITS = (1, 2, 4, 8, 16, 32, 64, 128, 256)
 WAVES = ((4, 1), (2, 2), (1, 4))
 # packed weights also run 8- and 16-wave workgroups and 64 rows per wave
 WAVES_PACKED = WAVES + ((1, 8), (2, 4), (1, 16))
@@ -89,6 +91,11 @@ def fused_ok(fmt, M, K):
     return M <= 16 and M * K <= 16384 and K % 512 == 0
 
 
+def amax_mode_ok(fmt, M, K):
+    """Shapes the given-amax prologue (a_mode 5) can serve."""
+    return fmt in (ql.FP8_DYNAMIC, ql.W8A8_INT8) and M <= 16 and K % 128 == 0
+
+
 def decode_m64_candidates(M, N, K, layout):
     """Weight-streaming configurations with four token tiles (32 < M <= 64,
     packed weights, activations from L2)."""
@@ -116,6 +123,23 @@ def phase1_candidates(fmt, M, N, K, layout=0):
                 (2, 4) if fused_ok(fmt, M, K) else (2,)):
             yield dict(swap_ab=swap, split_k=split, waves_n=wn, waves_k=wk, rows_per_wave=32, prefetch=pf,
                        a_mode=amode, w_lds=0, w_layout=1)
+        return
+    if layout == 5:
+        # given-amax forward plans: each workgroup quantizes its own K chunk (M x chunk <= 16384 values)
+        if not amax_mode_ok(fmt, M, K):
+            return
+        seen = set()
+        for (wn, wk), rows, split in itertools.product(WAVES_PACKED, (16, 32, 64), SPLITS):
+            ch = _effective_chunks(K, split)
+            G = -(-K // 128)
+            if M * -(-G // min(split, G)) * 128 > 16384:
+                continue
+            key = (wn, wk, rows, ch)
+            if key in seen:
+                continue
+            seen.add(key)
+            yield dict(swap_ab=1, split_k=split, waves_n=wn, waves_k=wk, rows_per_wave=rows, prefetch=2, a_mode=5,
+                       w_lds=0, w_layout=1)
         return
     if layout == 3:
         seen = set()
@@ -146,7 +170,8 @@ class Timer:
 
     layout 0: row-major W_q and A_q; 1: packed W_q, row-major A_q; 2: packed W_q and A_q;
     3: packed W_q, whole forward (quantizer + GEMM, or the fused launch) timed;
-    4: as 3 for SiLU-and-mul plans of a merged gate/up weight (output [M, N/2])."""
+    4: as 3 for SiLU-and-mul plans of a merged gate/up weight (output [M, N/2]);
+    5: as 3 for an input whose per-token amax is given (qlinear_forward_amax)."""
 
     def __init__(self, fmt, N, K, x, w, stream, layout=0, max_copies=48):
         self.fmt, self.N, self.K, self.layout = fmt, N, K, layout
@@ -176,9 +201,19 @@ class Timer:
             a_q, a_s = ql.quantize_act(fmt, xm)
         y = torch.empty(M, self.N // 2 if self.layout == 4 else self.N, dtype=torch.bfloat16, device="cuda")
         wsp = plan.new_workspace()
+        R = self.copies
+        if self.layout == 5:
+            # one amax buffer per launch of the graph (each consumer clears its
+            # own), refilled before every replay
+            mag = (xm.view(torch.int16).to(torch.int32) & 0x7FFF) << 16
+            words = torch.zeros(R, -(-(M + 1) // 4) * 4, dtype=torch.int32, device="cuda")
+            words[:, :M] = mag.max(dim=1).values
+            amax0 = words.clone()
 
         def one(c, stream=None):
-            if self.layout >= 3:
+            if self.layout == 5:
+                ql.qlinear_forward_amax(plan, xm, words[c], a_q, a_s, self.wq[c], self.ws[c], y, wsp, stream=stream)
+            elif self.layout >= 3:
                 ql.qlinear_forward(plan, xm, a_q, a_s, self.wq[c], self.ws[c], y, wsp, stream=stream)
             else:
                 ql.qlinear_run(plan, a_q, a_s, self.wq[c], self.ws[c], y, wsp, stream=stream)
@@ -186,7 +221,8 @@ class Timer:
         # not later inside a captured graph
         one(0)
         torch.cuda.synchronize()
-        R = self.copies
+        if self.layout == 5:
+            words.copy_(amax0)
         with torch.cuda.stream(s):
             ql.qlinear_graph_begin(s)
             for c in range(R):
@@ -196,6 +232,9 @@ class Timer:
         s.synchronize()
         ts = []
         for _ in range(reps):
+            if self.layout == 5:
+                with torch.cuda.stream(s):
+                    words.copy_(amax0)
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record(s)
             g.launch(s)
@@ -234,7 +273,7 @@ def sweep_point(timer, fmt, M, N, K, log=print, top=6):
     results = []
     ref = None
     cands = list(phase1_candidates(fmt, M, N, K, timer.layout))
-    if timer.layout == 3:
+    if timer.layout in (3, 5):
         # the unfused contender: the packed-activation plan (table entry or heuristic)
         cands.insert(0, dict(ql.qlinear_plan_layouts(fmt, M, N, K, 1, 1).config))
     for cfg in cands:
@@ -295,15 +334,55 @@ def table_line(fmt, M, N, K, cfg, us, kind=""):
         (" " + kind) if kind else "")
 
 
+def _entry_key(line):
+    """(format, M, N, K, weight layout, activation class, kind) of a table line:
+    the key the planner looks entries up by."""
+    f = line.split()
+    a_mode = int(f[11])
+    kind = f[17] if len(f) > 17 else ""
+    return (f[0], f[1], f[2], f[3], f[13], "packed" if a_mode >= 2 else "rowmajor", kind)
+
+
+def merge_tables(base, update, out):
+    """Write `out`: the entries of `base`, each replaced by the entry of
+    `update` with the same key where there is one, plus `update`'s new keys.
+    Returns the number of entries taken from `update`."""
+    def entries(path):
+        return [l.rstrip("\n") for l in open(path) if l.strip() and not l.startswith("#")]
+    new = {}
+    for l in entries(update):
+        new[_entry_key(l)] = l
+    lines, used = [], set()
+    for l in open(base):
+        if l.strip() and not l.startswith("#"):
+            k = _entry_key(l)
+            if k in new:
+                l = new[k] + "\n"
+                used.add(k)
+        lines.append(l if l.endswith("\n") else l + "\n")
+    added = [new[k] + "\n" for k in new if k not in used]
+    body = [l for l in lines if not l.startswith("# sweep wall time")]
+    tail = [l for l in lines if l.startswith("# sweep wall time")]
+    with open(out, "w") as f:
+        f.writelines(body + added + ["# merged %d entries of a sweep (%s)\n" % (len(new), os.path.basename(update))]
+                     + tail)
+    return len(new)
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description="offline per-shape sweep")
     ap.add_argument("--workloads", default=",".join(c.name for c in decode_workloads()))
     ap.add_argument("--out", default=ql.DEFAULT_TABLE)
     ap.add_argument("--ms", default=None, help="comma list overriding the token counts")
-    ap.add_argument("--layouts", default="0,1,2,3,4",
+    ap.add_argument("--shapes", default=None, help="comma list of shape labels to sweep (default: every shape)")
+    ap.add_argument("--merge", default=None, metavar="TABLE",
+                    help="after the sweep, write TABLE with this sweep's entries replacing its entries of the "
+                         "same (format, M, N, K, operand layouts, kind)")
+    ap.add_argument("--layouts", default="0,1,2,3,4,5",
                     help="operand layouts to tune: 0 row-major W and A, 1 packed W, 2 packed W and A, "
                          "3 forward plans (packed W; fused quantization or not), 4 SiLU-and-mul forward plans "
-                         "of the gate_up shapes")
+                         "of the gate_up shapes, 5 given-amax forward plans of the down shapes (the input is the "
+                         "SiLU-and-mul output, whose per-token amax the gate_up epilogue folds)")
     args = ap.parse_args(argv)
     torch.cuda.set_device(0)
     stream = torch.cuda.Stream()
@@ -321,11 +400,16 @@ def main(argv=None):
             wl = config_by_name(name)
             ms = [int(m) for m in args.ms.split(",")] if args.ms else list(wl.ms)
             for (lab, N, K) in wl.shapes:
+                if args.shapes and lab not in args.shapes.split(","):
+                    continue
                 x, w = make_inputs(K, N, max(ms), wl.sigma_w, seed=wl.seed)
                 for layout in [int(v) for v in args.layouts.split(",")]:
-                    lms = [m for m in ms if layout != 3 or fused_ok(wl.fmt, m, K)]
+                    lms = [m for m in ms if (layout != 3 or fused_ok(wl.fmt, m, K))
+                           and (layout != 5 or amax_mode_ok(wl.fmt, m, K))]
                     if layout == 4 and (lab != "gate_up" or N % 32):
                         continue        # SiLU-and-mul plans: the merged gate/up projection only
+                    if layout == 5 and lab != "down":
+                        continue        # given-amax plans: the projection fed by the SiLU-and-mul output
                     if wl.fmt in ql.MX_FORMATS and layout != 2:
                         continue        # MX plans take packed weights and packed activations only
                     if not lms:
@@ -335,7 +419,8 @@ def main(argv=None):
                         t0 = time.time()
                         res = sweep_point(timer, wl.fmt, M, N, K)
                         us, cfg = res[0]
-                        f.write(table_line(wl.fmt, M, N, K, cfg, us, kind={3: "fwd", 4: "glu"}.get(layout, ""))
+                        f.write(table_line(wl.fmt, M, N, K, cfg, us,
+                                           kind={3: "fwd", 4: "glu", 5: "amx"}.get(layout, ""))
                                 + "\n")
                         f.flush()
                         n += 1
@@ -345,6 +430,9 @@ def main(argv=None):
                     torch.cuda.empty_cache()
         f.write("# sweep wall time %.0f s\n" % (time.time() - t_start))
     print("wrote %d entries to %s" % (n, args.out))
+    if args.merge:
+        k = merge_tables(args.merge, args.out, args.merge)
+        print("merged: %d entries of %s replaced or added in %s" % (k, args.out, args.merge))
 
 
 if __name__ == "__main__":

@@ -245,7 +245,7 @@ def test_fused_quantization_plans_are_validated_on_host():
     assert _plan_status(ql.FP8_DYNAMIC, 17, 4096, 512, **fused) == QL_E_UNSUPPORTED  # one token tile
     assert _plan_status(ql.FP8_DYNAMIC, 1, 4096, 4352, **fused) == QL_E_UNSUPPORTED  # K % 512
     assert _plan_status(ql.FP8_DYNAMIC, 1, 4096, 4096, a_mode=4) == QL_E_UNSUPPORTED  # needs packed weights
-    assert _plan_status(ql.FP8_DYNAMIC, 1, 4096, 4096, a_mode=5, w_layout=1) == QL_E_INVALID
+    assert _plan_status(ql.FP8_DYNAMIC, 1, 4096, 4096, a_mode=6, w_layout=1) == QL_E_INVALID
     # a fused plan quantizes X itself, so it only runs through qlinear_forward
     p = ql.qlinear_plan_with_config(ql.FP8_DYNAMIC, 2, 1024, 4096, fused)
     assert p.facts["lds_bytes"] >= 512 + 2 * (4096 + 64)
@@ -462,3 +462,31 @@ def test_table_free_plans_up_to_64_tokens_stream_the_weights(N, K, waves):
         assert ql.qlinear_plan_layouts(ql.FP8_DYNAMIC, 65, 4096, 4096, 1, 1).config["algo"] == ql.ALGO_TILED
     finally:
         ql.load_default_table()
+
+
+def test_given_amax_plans_are_validated_on_host():
+    """a_mode 5 (the per-token amax of X given): per-token formats, one token
+    tile, whole 128-wide K blocks, M x chunk within the 16384 values a
+    workgroup quantizes, packed weights."""
+    m5 = dict(w_layout=1, a_mode=5, waves_n=1, waves_k=4)
+    assert _plan_status(ql.FP8_DYNAMIC, 1, 4096, 12288, **m5) == QL_OK
+    assert _plan_status(ql.W8A8_INT8, 16, 4096, 12288, split_k=16, **m5) == QL_OK   # 16 x 768 values
+    assert _plan_status(ql.W8A8_INT8, 16, 4096, 12288, split_k=8, **m5) == QL_E_UNSUPPORTED   # 16 x 1536
+    assert _plan_status(ql.FP8_DYNAMIC, 17, 4096, 512, **m5) == QL_E_UNSUPPORTED
+    assert _plan_status(ql.FP8_DYNAMIC, 1, 4096, 4160, **m5) == QL_E_UNSUPPORTED     # K % 128
+    assert _plan_status(ql.BLOCK_FP8, 1, 4096, 4096, **m5) == QL_E_UNSUPPORTED
+    assert _plan_status(ql.MXFP8, 1, 4096, 4096, **m5) == QL_E_UNSUPPORTED
+    assert _plan_status(ql.FP8_DYNAMIC, 1, 4096, 4096, a_mode=5) == QL_E_UNSUPPORTED  # needs packed weights
+
+
+def test_given_amax_planning():
+    """qlinear_plan_layouts(..., a_packed = 3): a_mode 5 up to 16 tokens over
+    whole K blocks (split so that M x chunk fits), else the packed-A plan."""
+    for M in (1, 4, 16):                      # an untabulated shape: the heuristic's plan
+        p = ql.qlinear_plan_layouts(ql.FP8_DYNAMIC, M, 3072, 12288, 1, 3)
+        assert p.config["a_mode"] == 5 and p.facts["source"] == "heuristic"
+        assert M * p.facts["chunk_k"] <= 16384
+    assert ql.qlinear_plan_layouts(ql.W8A8_INT8, 24, 3072, 12288, 1, 3).config["a_mode"] in (2, 3)
+    assert ql.qlinear_plan_layouts(ql.W8A8_INT8, 4, 3072, 4160, 1, 3).config["a_mode"] in (2, 3)
+    with pytest.raises(ql.QLinearError):
+        ql.qlinear_plan_layouts(ql.BLOCK_FP8, 4, 4096, 4096, 1, 3)

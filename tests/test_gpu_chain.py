@@ -1,0 +1,165 @@
+"""The gated MLP as a chain: gate_up (SiLU-and-mul epilogue folding the
+per-token amax of H) -> down (a_mode 5: each workgroup quantizes its own K
+chunk of H with the given amax, in the GEMM launch).
+
+Checked against the oracle: H within the SiLU-and-mul rule; the amax words
+equal max |H| per token of the GPU's own H, bit for bit; down's codes and
+scales equal ``oracle.quantize_act`` of that H bit for bit; down's Y is
+bit-exact (INT8) or within the FP8 rule against the oracle linear on that H;
+the amax words are all zero after the consumer.
+"""
+
+import itertools
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import quantized_gemm_decode_amd as ql
+from tests.gpu_util import fp8_check, fp8_ok, host_bf16_bits, pack_ref, requires_gpu
+from workloads import bf16_bits, make_inputs
+
+pytestmark = [pytest.mark.gpu, requires_gpu]
+FMTS = [ql.FP8_DYNAMIC, ql.W8A8_INT8]
+
+
+def _amax_words(h_bits):
+    """max |h| per row of bf16 bit patterns, as binary32 bit patterns."""
+    mag = (h_bits.astype(np.uint32) & 0x7FFF) << 16
+    return mag.max(axis=1).astype(np.uint32)
+
+
+def _weights(fmt, N, K, seed, sigma=0.02):
+    _, w = make_inputs(K, N, 1, sigma, seed=seed)
+    w_q, w_s = ql.quantize_weight(fmt, w.cuda())
+    return w, ql.pack_weight(w_q), w_s
+
+
+def _consume(fmt, plan, hd, amax, w_p, w_s):
+    a_q = ql.act_buffer(plan)
+    a_s = torch.empty(plan.M, dtype=torch.float32, device="cuda")
+    y = torch.full((plan.M, plan.N), float("nan"), dtype=torch.bfloat16, device="cuda")
+    ql.qlinear_forward_amax(plan, hd, amax, a_q, a_s, w_p, w_s, y, plan.new_workspace())
+    torch.cuda.synchronize()
+    return a_q, a_s, y
+
+
+def _check_consumer(fmt, plan, h_bits, w_down, a_q, a_s, y, label):
+    M, K = h_bits.shape
+    r = oracle.reference(fmt, h_bits, bf16_bits(w_down))
+    codes = np.asarray(r["a_q"]).view(np.uint8) if fmt != ql.W8A8_INT8 else np.asarray(r["a_q"]).astype(np.int8).view(np.uint8)
+    n = ql.qlinear_packed_act_bytes(M, K)
+    assert np.array_equal(a_q.view(torch.uint8)[:n].cpu().numpy(), pack_ref(codes)), label
+    assert np.array_equal(a_s.cpu().numpy(), np.asarray(r["s_a"], np.float32)), label
+    yb = host_bf16_bits(y)
+    if fmt == ql.W8A8_INT8:
+        assert np.array_equal(yb, r["y_ref"]), label
+    else:
+        st = fp8_check(fmt, r, yb, plan.facts["chunks"])
+        assert fp8_ok(st), (label, st)
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("M", [1, 3, 8, 16, 24])
+def test_chain_matches_oracle(fmt, M):
+    I, K, N2 = 640, 1024, 384                      # gate_up [2I, K], down [N2, I]
+    x, w_gu = make_inputs(K, 2 * I, M, 0.02, seed=M + 10 * fmt)
+    w_down, wd_p, wd_s = _weights(fmt, N2, I, seed=M + 7)
+    wg_q, wg_s = ql.quantize_weight(fmt, w_gu.cuda())
+    glu = ql.qlinear_plan_glu(fmt, M, 2 * I, K, 2)
+    h = torch.full((M, I), float("nan"), dtype=torch.bfloat16, device="cuda")
+    amax = ql.amax_buffer(M)
+    ql.qlinear_forward_glu_amax(glu, x.cuda(), ql.act_buffer(glu),
+                                torch.empty(M, dtype=torch.float32, device="cuda"), ql.pack_weight(wg_q), wg_s, h,
+                                amax, glu.new_workspace())
+    torch.cuda.synchronize()
+    h_bits = host_bf16_bits(h)
+    # H itself against the oracle's SiLU-and-mul rule
+    r = oracle.reference(fmt, bf16_bits(x), bf16_bits(w_gu))
+    h_ref, h_true, bound = oracle.glu_reference(fmt, r, split=glu.facts["chunks"])
+    st = oracle.check_fp8_parity(h_bits, h_ref, h_true, bound)
+    assert fp8_ok(st), st
+    # the amax words: max |H| per token of this H, exactly; the counter word zero
+    words = amax.cpu().numpy().view(np.uint32)
+    assert np.array_equal(words[:M], _amax_words(h_bits))
+    assert words[M] == 0
+    down = ql.qlinear_plan_layouts(fmt, M, N2, I, 1, 3)
+    assert (down.config["a_mode"] == 5) == (M <= 16)
+    a_q, a_s, y = _consume(fmt, down, h, amax, wd_p, wd_s)
+    _check_consumer(fmt, down, h_bits, w_down, a_q, a_s, y, (fmt, M, down.config))
+    assert int(torch.count_nonzero(amax)) == 0, "the consumer leaves the amax words zero"
+
+
+def _given_amax(x_bits, M):
+    buf = ql.amax_buffer(M)
+    host = np.zeros(buf.numel(), np.uint32)
+    host[:M] = _amax_words(x_bits)
+    buf.copy_(torch.from_numpy(host.view(np.int32)))
+    return buf
+
+
+# a_mode 5 instantiations: waves (n x k), rows per wave, batch, swap
+MODE5 = list(itertools.product([(1, 4), (2, 2), (4, 1), (1, 8), (2, 4), (1, 16), (4, 4)], [16, 32, 64], [1, 2],
+                               [0, 1]))
+
+
+def _mode5_available(fmt, M, N, K, cfg):
+    try:
+        return ql.qlinear_plan_with_config(fmt, M, N, K, cfg)
+    except ql.QLinearError as e:
+        assert e.status == 2, e
+        return None
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("M", [2, 13])
+@pytest.mark.parametrize("split", [1, 4])
+def test_every_mode5_instantiation(fmt, M, split):
+    """Every instantiated a_mode 5 shape, on a ragged N with several tiles,
+    against the oracle, twice in a row (the second run must find the words
+    the first one cleared, refilled)."""
+    N, K = 600, 1152                      # 13 x 1152 values fit one workgroup at split 1
+    x, _ = make_inputs(K, N, M, 0.02, seed=M * 31 + split, with_weight=False)
+    xb = bf16_bits(x)
+    w_full, w_p, w_s = _weights(fmt, N, K, seed=M + split)
+    ran = 0
+    for (wn, wk), rows, pf, swap in MODE5:
+        cfg = dict(swap_ab=swap, split_k=split, waves_n=wn, waves_k=wk, rows_per_wave=rows, prefetch=pf, a_mode=5,
+                   w_lds=0, w_layout=1)
+        plan = _mode5_available(fmt, M, N, K, cfg)
+        if plan is None:
+            continue
+        for _ in range(2):
+            amax = _given_amax(xb, M)
+            a_q, a_s, y = _consume(fmt, plan, x.cuda(), amax, w_p, w_s)
+            _check_consumer(fmt, plan, xb, w_full, a_q, a_s, y, cfg)
+            assert int(torch.count_nonzero(amax)) == 0
+        ran += 1
+    assert ran >= 20, ran
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_consumer_without_mode5_clears_the_words(fmt):
+    """A plan that quantizes separately (M > 16) still leaves the words zero."""
+    M, N, K = 24, 256, 512
+    x, _ = make_inputs(K, N, M, 0.02, seed=5, with_weight=False)
+    w_full, w_p, w_s = _weights(fmt, N, K, seed=6)
+    plan = ql.qlinear_plan_layouts(fmt, M, N, K, 1, 3)
+    assert plan.config["a_mode"] != 5
+    amax = _given_amax(bf16_bits(x), M)
+    a_q, a_s, y = _consume(fmt, plan, x.cuda(), amax, w_p, w_s)
+    _check_consumer(fmt, plan, bf16_bits(x), w_full, a_q, a_s, y, plan.config)
+    assert int(torch.count_nonzero(amax)) == 0
+
+
+def test_mode5_plan_refuses_plain_forward():
+    plan = ql.qlinear_plan_layouts(ql.FP8_DYNAMIC, 4, 256, 512, 1, 3)
+    assert plan.config["a_mode"] == 5
+    x = torch.zeros(4, 512, dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(ql.QLinearError) as e:
+        ql.qlinear_forward(plan, x, ql.act_buffer(plan), torch.empty(4, device="cuda"),
+                           torch.zeros(ql.qlinear_packed_weight_bytes(256, 512), dtype=torch.uint8,
+                                       device="cuda").view(torch.float8_e4m3fn),
+                           torch.ones(256, device="cuda"), torch.empty(4, 256, dtype=torch.bfloat16, device="cuda"))
+    assert e.value.status == 1

@@ -18,6 +18,7 @@ import oracle
 import quantized_gemm_decode_amd as ql
 from tests.gpu_util import (MIN_FRAC_WITHIN_ULP, dev_bf16, dev_codes, dev_f32, fp8_check, fp8_ok, host_bf16_bits,
                             host_codes, pack_ref, requires_gpu, run_gemm)
+from tests.instantiations import cases
 from workloads import CONFIGS, bf16_bits, config_by_name, decode_points, decode_workloads, make_inputs
 
 pytestmark = [pytest.mark.gpu, requires_gpu]
@@ -70,25 +71,30 @@ SPLITS = [1, 2, 4, 8]
 WAVES_K = [1, 2, 4]
 
 
-@pytest.mark.parametrize("fmt", FMTS)
-@pytest.mark.parametrize("M", [5, 29])
-@pytest.mark.parametrize("vi", range(len(VARIANTS)))
-def test_every_instantiation_matches_oracle(fmt, M, vi):
+def _variant_args(fmt, M, vi):
     swap, rows, pf, alds, wmode = VARIANTS[vi]
     split = SPLITS[(vi + M) % len(SPLITS)]
     wk = WAVES_K[(vi // 2 + M) % len(WAVES_K)]
     N = 300 if rows == 16 else 520                      # several tiles + a ragged tail
     K = 1152 if fmt == ql.BLOCK_FP8 or vi % 3 else 1040  # 1040: ragged last K block
-    r = _ref(fmt, M, N, K, seed=vi * 7 + M)
     cfg = dict(swap_ab=swap, split_k=split, waves_n=4 // wk, waves_k=wk, rows_per_wave=rows, prefetch=pf,
                a_mode=alds, w_lds=int(wmode == 1), w_layout=int(wmode == 2))
-    try:
-        plan = ql.qlinear_plan_with_config(fmt, M, N, K, cfg)
-    except ql.QLinearError as e:
-        spill = (M > 16 and rows == 32 and pf == 4 or (fmt == ql.BLOCK_FP8 and M > 16 and pf == 4 and not swap)
-                 or alds >= 2)   # 4-wave packed-activation shapes exist for the register-fitting ones only
-        assert e.status == 2 and (spill or "LDS" in str(e)), e
-        pytest.skip("configuration not available: %s" % e)
+    return fmt, M, N, K, cfg
+
+
+# the instantiated points of fmt x M x VARIANTS (shapes that would spill or
+# exceed the LDS are not instantiated; the manifest test watches the list)
+VARIANT_CASES = cases("gemm_variants", [(f, M, vi) for f in FMTS for M in (5, 29) for vi in range(len(VARIANTS))],
+                      _variant_args)
+
+
+@pytest.mark.parametrize("fmt,M,vi", VARIANT_CASES)
+def test_every_instantiation_matches_oracle(fmt, M, vi):
+    _, _, N, K, cfg = _variant_args(fmt, M, vi)
+    wmode = VARIANTS[vi][4]
+    alds = cfg["a_mode"]
+    r = _ref(fmt, M, N, K, seed=vi * 7 + M)
+    plan = ql.qlinear_plan_with_config(fmt, M, N, K, cfg)
     a_q, s_a, w_q, s_w = _dev(fmt, r)
     if wmode == 2:
         w_q = ql.pack_weight(w_q)
@@ -104,24 +110,28 @@ def test_every_instantiation_matches_oracle(fmt, M, vi):
 WIDE = list(itertools.product([4, 8, 16], [16, 32, 64], [1, 2], [0, 1], [0, 2, 3]))   # ... x activation mode
 
 
-@pytest.mark.parametrize("fmt", FMTS)
-@pytest.mark.parametrize("M", [5, 29, 61])
-@pytest.mark.parametrize("wi", range(len(WIDE)))
-def test_wide_workgroup_instantiations_match_oracle(fmt, M, wi):
+def _wide_args(fmt, M, wi):
     nw, rows, pf, swap, amode = WIDE[wi]
     wks = [k for k in (1, 2, 4, 8, 16) if k <= nw]
     wk = wks[(wi + M) % len(wks)]
     split = SPLITS[(wi + 2 * M) % len(SPLITS)]
     N = 300 + 16 * wi                                    # several tiles + a ragged tail
     K = 1152 if fmt == ql.BLOCK_FP8 or wi % 3 else 1040  # 1040: ragged last K block
-    r = _ref(fmt, M, N, K, seed=1000 + wi * 7 + M)
     cfg = dict(swap_ab=swap, split_k=split, waves_n=nw // wk, waves_k=wk, rows_per_wave=rows, prefetch=pf,
                a_mode=amode, w_lds=0, w_layout=1)
-    try:
-        plan = ql.qlinear_plan_with_config(fmt, M, N, K, cfg)
-    except ql.QLinearError as e:
-        assert e.status == 2, e
-        pytest.skip("configuration not available: %s" % e)
+    return fmt, M, N, K, cfg
+
+
+WIDE_CASES = cases("gemm_wide", [(f, M, wi) for f in FMTS for M in (5, 29, 61) for wi in range(len(WIDE))],
+                   _wide_args)
+
+
+@pytest.mark.parametrize("fmt,M,wi", WIDE_CASES)
+def test_wide_workgroup_instantiations_match_oracle(fmt, M, wi):
+    _, _, N, K, cfg = _wide_args(fmt, M, wi)
+    wk, amode = cfg["waves_k"], cfg["a_mode"]
+    r = _ref(fmt, M, N, K, seed=1000 + wi * 7 + M)
+    plan = ql.qlinear_plan_with_config(fmt, M, N, K, cfg)
     a_q, s_a, w_q, s_w = _dev(fmt, r)
     if amode >= 2:
         a_q = _dev_packed_act(fmt, r)
@@ -377,7 +387,7 @@ def _table_entries():
             continue
         v = [int(t) for t in f[:16]]
         kind = f[17] if len(f) > 17 else ""
-        out.append(tuple(v) + ({"": 0, "fwd": 1, "glu": 2}[kind],))
+        out.append(tuple(v) + ({"": 0, "fwd": 1, "glu": 2, "amx": 3}[kind],))
     return out
 
 
@@ -397,7 +407,7 @@ def _shape_config(fmt, N, K):
 
 @pytest.mark.parametrize("entry", _table_entries(),
                          ids=lambda e: "f%d-M%d-N%d-K%d-L%d%s" % (e[0], e[1], e[2], e[3], e[13],
-                                                                  ["", "-fwd", "-glu"][e[16]]))
+                                                                  ["", "-fwd", "-glu", "-amx"][e[16]]))
 def test_every_table_entry_matches_oracle(entry):
     """Each configuration the shipped sweep table selects, run at its own
     (format, M, N, K) and weight layout, against the oracle on sampled columns
@@ -418,7 +428,18 @@ def test_every_table_entry_matches_oracle(entry):
         w_use = ql.pack_weight_fp4(w_q)
     if fmt in ql.MX_FORMATS:
         w_s = ql.pack_mx_scales(w_s)
-    if entry[16]:
+    if entry[16] == 3:
+        # given-amax forward: the amax words of X from the host, cleared by the run
+        a_f = ql.act_buffer(plan)
+        s_f = torch.empty_like(a_s)
+        amax = ql.amax_buffer(M)
+        words = np.zeros(amax.numel(), np.uint32)
+        words[:M] = ((bf16_bits(xm).astype(np.uint32) & 0x7FFF) << 16).max(axis=1)
+        amax.copy_(torch.from_numpy(words.view(np.int32)))
+        ql.qlinear_forward_amax(plan, xm.cuda(), amax, a_f, s_f, w_use, w_s, y, plan.new_workspace())
+        torch.cuda.synchronize()
+        assert torch.equal(s_f, a_s) and int(torch.count_nonzero(amax)) == 0
+    elif entry[16]:
         a_f = ql.act_buffer(plan)
         s_f = torch.empty_like(a_s)
         ql.qlinear_forward(plan, xm.cuda(), a_f, s_f, w_use, w_s, y, plan.new_workspace())
@@ -508,3 +529,24 @@ def test_concurrent_plans_on_two_streams_match_serial_runs():
             else:
                 assert fp8_ok(fp8_check(fmt, r, yb, plan.facts["chunks"], 2)), it
         assert int(torch.count_nonzero(wss[ci])) == 0
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("split", [64, 128, 256])
+def test_split_k_up_to_256(fmt, split):
+    """The pages' split_k range reaches 256: a long-K, small-N shape (256 K
+    blocks, so chunks of 4, 2 and 1 blocks) in row-major and packed layouts;
+    INT8 bit-exact, FP8 within the bound, workspace left all-zero."""
+    M, N, K = 5, 200, 32768
+    r = _ref(fmt, M, N, K, seed=split + fmt)
+    a_q, s_a, w_q, s_w = _dev(fmt, r)
+    for packed in (0, 1):
+        cfg = dict(swap_ab=int(split == 128), split_k=split, waves_n=4 if packed else 2,
+                   waves_k=1 if packed else 2, rows_per_wave=16, prefetch=2, a_mode=2 if packed else 0, w_lds=0,
+                   w_layout=packed)
+        plan = ql.qlinear_plan_with_config(fmt, M, N, K, cfg)
+        assert plan.facts["chunks"] == split
+        y, acc, ws = run_gemm(plan, _dev_packed_act(fmt, r) if packed else a_q, s_a,
+                              ql.pack_weight(w_q) if packed else w_q, s_w)
+        _assert_parity(fmt, r, y, acc, split, label=str(cfg), waves_k=cfg["waves_k"])
+        assert int(torch.count_nonzero(ws)) == 0, "split-K workspace not left all-zero"

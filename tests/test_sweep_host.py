@@ -86,3 +86,38 @@ def test_tiled_candidates_cover_the_tiles_and_rings():
 def test_decode_candidates_up_to_64_tokens(M):
     cands = list(sweep.decode_m64_candidates(M, 4096, 4096, 2))
     assert cands and all(c["w_layout"] == 1 and c["a_mode"] in (0, 2) for c in cands)
+
+
+def test_merge_replaces_entries_of_the_same_key(tmp_path):
+    """A partial re-sweep replaces exactly the entries the planner would look
+    up by the same key (format, M, N, K, weight layout, activation class,
+    kind) and keeps every other line."""
+    base = tmp_path / "base.txt"
+    upd = tmp_path / "upd.txt"
+    base.write_text("# header\n"
+                    "0 8 4096 12288 0 1 1 1 4 16 2 2 0 1 0 0 10.000\n"          # packed A: replaced
+                    "0 8 4096 12288 0 1 1 1 4 16 2 0 0 1 0 0 11.000\n"          # row-major A: kept
+                    "0 8 4096 12288 0 1 1 1 4 16 2 4 0 1 0 0 9.000 fwd\n"       # forward: replaced
+                    "1 8 4096 12288 0 1 1 1 4 16 2 2 0 1 0 0 12.000\n"          # other format: kept
+                    "# sweep wall time 5 s\n")
+    upd.write_text("0 8 4096 12288 0 1 64 1 4 16 2 3 0 1 0 0 8.000\n"
+                   "0 8 4096 12288 0 1 2 1 4 16 2 2 0 1 0 0 8.500 fwd\n"
+                   "0 16 4096 12288 0 1 8 1 4 16 2 2 0 1 0 0 9.500\n")
+    out = tmp_path / "out.txt"
+    assert sweep.merge_tables(str(base), str(upd), str(out)) == 3
+    lines = [l for l in out.read_text().splitlines() if l and not l.startswith("#")]
+    assert lines == ["0 8 4096 12288 0 1 64 1 4 16 2 3 0 1 0 0 8.000",
+                     "0 8 4096 12288 0 1 1 1 4 16 2 0 0 1 0 0 11.000",
+                     "0 8 4096 12288 0 1 2 1 4 16 2 2 0 1 0 0 8.500 fwd",
+                     "1 8 4096 12288 0 1 1 1 4 16 2 2 0 1 0 0 12.000",
+                     "0 16 4096 12288 0 1 8 1 4 16 2 2 0 1 0 0 9.500"]
+    assert out.read_text().rstrip().endswith("# sweep wall time 5 s")
+
+
+def test_split_candidates_reach_256_clamped_to_the_k_blocks():
+    cands = list(sweep.phase1_candidates(ql.FP8_DYNAMIC, 8, 4096, 32768, layout=2))
+    chunks = {sweep._effective_chunks(32768, c["split_k"]) for c in cands}
+    assert {64, 128, 256} <= chunks
+    short = {sweep._effective_chunks(1024, c["split_k"])
+             for c in sweep.phase1_candidates(ql.FP8_DYNAMIC, 8, 4096, 1024, layout=2)}
+    assert max(short) == 8
