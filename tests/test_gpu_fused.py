@@ -16,6 +16,7 @@ import torch
 import oracle
 import quantized_gemm_decode_amd as ql
 from tests.gpu_util import dev_bf16, fp8_check, fp8_ok, host_bf16_bits, MIN_FRAC_WITHIN_ULP, pack_ref, requires_gpu
+from tests.instantiations import cases
 from workloads import bf16_bits, make_inputs
 
 pytestmark = [pytest.mark.gpu, requires_gpu]
@@ -66,23 +67,27 @@ def _weights(fmt, r):
     return ql.pack_weight(w_q), torch.from_numpy(np.asarray(r["s_w"], np.float32)).cuda()
 
 
-@pytest.mark.parametrize("fmt", FMTS)
-@pytest.mark.parametrize("vi", range(len(FVARIANTS)))
-def test_every_fused_instantiation_matches_oracle(fmt, vi):
+def _fused_args(fmt, vi):
     nw, wk, rows, pf, swap = FVARIANTS[vi]
     M, K = SHAPES[vi % len(SHAPES)]
     split = SPLITS[(vi // 2) % len(SPLITS)]
     N = 300 + 16 * (vi % 7)                      # several tiles + a ragged tail
+    cfg = dict(swap_ab=swap, split_k=split, waves_n=nw // wk, waves_k=wk, rows_per_wave=rows, prefetch=pf,
+               a_mode=4, w_layout=1)
+    return fmt, M, N, K, cfg
+
+
+FUSED_CASES = cases("fused", [(f, vi) for f in FMTS for vi in range(len(FVARIANTS))], _fused_args)
+
+
+@pytest.mark.parametrize("fmt,vi", FUSED_CASES)
+def test_every_fused_instantiation_matches_oracle(fmt, vi):
+    _, M, N, K, cfg = _fused_args(fmt, vi)
+    wk = cfg["waves_k"]
     x, w = make_inputs(K, N, M, 0.02, seed=4000 + vi)
     xb = bf16_bits(x)
     r = oracle.reference(fmt, xb, bf16_bits(w))
-    cfg = dict(swap_ab=swap, split_k=split, waves_n=nw // wk, waves_k=wk, rows_per_wave=rows, prefetch=pf,
-               a_mode=4, w_layout=1)
-    try:
-        plan = ql.qlinear_plan_with_config(fmt, M, N, K, cfg)
-    except ql.QLinearError as e:
-        assert e.status == 2, e
-        pytest.skip("configuration not instantiated: %s" % e)
+    plan = ql.qlinear_plan_with_config(fmt, M, N, K, cfg)
     w_p, w_s = _weights(fmt, r)
     a_p, a_s, y, ws = _forward(plan, fmt, xb, w_p, w_s)
     _check(fmt, r, plan, a_p, a_s, y, str(cfg), waves_k=wk)

@@ -12,6 +12,7 @@ import torch
 import oracle
 import quantized_gemm_decode_amd as ql
 from tests.gpu_util import dev_bf16, host_bf16_bits, MIN_FRAC_WITHIN_ULP, pack_ref, requires_gpu
+from tests.instantiations import cases
 from workloads import bf16_bits, make_inputs
 
 pytestmark = [pytest.mark.gpu, requires_gpu]
@@ -56,24 +57,29 @@ def _check(fmt, r, h, plan, waves_k):
     assert st["ok"] and st["frac_within_ulp"] >= MIN_FRAC_WITHIN_ULP, (plan.config, st)
 
 
-@pytest.mark.parametrize("fmt", FMTS)
-@pytest.mark.parametrize("vi", range(len(GVARIANTS)))
-def test_every_glu_instantiation_matches_oracle(fmt, vi):
+def _glu_args(fmt, vi):
     swap, (wn, wk), pf, amode = GVARIANTS[vi]
     M = [1, 3, 13][vi % 3] if amode == 4 else [5, 20, 29][vi % 3]
     I = [304, 528][vi % 2]                            # several tiles + a ragged last one
     K = 1024 if amode == 4 or fmt == ql.BLOCK_FP8 else 1040
     split = SPLITS[(vi // 2) % len(SPLITS)]
-    x, w = make_inputs(K, 2 * I, M, 0.02, seed=6000 + vi * 3 + fmt)
-    xb = bf16_bits(x)
-    r = oracle.reference(fmt, xb, bf16_bits(w))
     cfg = dict(swap_ab=swap, split_k=split, waves_n=wn, waves_k=wk, rows_per_wave=32, prefetch=pf, a_mode=amode,
                w_layout=1)
-    try:
-        plan = ql.qlinear_plan_glu_with_config(fmt, M, 2 * I, K, cfg)
-    except ql.QLinearError as e:
-        assert e.status == 2, e
-        pytest.skip("configuration not instantiated: %s" % e)
+    return fmt, M, 2 * I, K, cfg
+
+
+GLU_CASES = cases("glu", [(f, vi) for f in FMTS for vi in range(len(GVARIANTS))], _glu_args,
+                  ql.qlinear_plan_glu_with_config)
+
+
+@pytest.mark.parametrize("fmt,vi", GLU_CASES)
+def test_every_glu_instantiation_matches_oracle(fmt, vi):
+    _, M, N2, K, cfg = _glu_args(fmt, vi)
+    wk = cfg["waves_k"]
+    x, w = make_inputs(K, N2, M, 0.02, seed=6000 + vi * 3 + fmt)
+    xb = bf16_bits(x)
+    r = oracle.reference(fmt, xb, bf16_bits(w))
+    plan = ql.qlinear_plan_glu_with_config(fmt, M, N2, K, cfg)
     assert plan.facts["epilogue"] == 1
     h, ws = _run_glu(plan, fmt, r, xb)
     _check(fmt, r, h, plan, wk)

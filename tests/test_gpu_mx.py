@@ -16,6 +16,7 @@ import quantized_gemm_decode_amd as ql
 from oracle import mx
 from tests.gpu_util import (dev_bf16, fp4_bytes, host_bf16_bits, MIN_FRAC_WITHIN_ULP, pack_fp4_ref,
                             pack_mx_scales_ref, pack_ref, requires_gpu)
+from tests.instantiations import cases
 from workloads import bf16_bits, make_inputs
 
 pytestmark = [pytest.mark.gpu, requires_gpu]
@@ -128,8 +129,7 @@ def test_mx_scale_packing_matches_the_layout_definition(R, K):
     assert np.array_equal(out.cpu().numpy()[:n], pack_mx_scales_ref(s, K))
 
 
-@pytest.mark.parametrize("vi", range(len(MXV)))
-def test_every_mx_instantiation_matches_oracle(vi):
+def _mx_args(vi):
     swap, (wn, wk), rows, pf, amode = MXV[vi]
     M = MS[vi % len(MS)]
     K = [1024, 1152, 2048][vi % 3]
@@ -137,11 +137,17 @@ def test_every_mx_instantiation_matches_oracle(vi):
     split = SPLITS[(vi // 2) % len(SPLITS)]
     cfg = dict(swap_ab=swap, split_k=split, waves_n=wn, waves_k=wk, rows_per_wave=rows, prefetch=pf,
                a_mode=amode, w_layout=1)
-    try:
-        plan = ql.qlinear_plan_with_config(ql.MXFP8, M, N, K, cfg)
-    except ql.QLinearError as e:
-        assert e.status == 2, e
-        pytest.skip("configuration not instantiated: %s" % e)
+    return ql.MXFP8, M, N, K, cfg
+
+
+MX_CASES = cases("mxfp8", [(vi,) for vi in range(len(MXV))], _mx_args)
+
+
+@pytest.mark.parametrize("vi", [c[0] for c in MX_CASES])
+def test_every_mx_instantiation_matches_oracle(vi):
+    _, M, N, K, cfg = _mx_args(vi)
+    wk = cfg["waves_k"]
+    plan = ql.qlinear_plan_with_config(ql.MXFP8, M, N, K, cfg)
     x, w = make_inputs(K, N, M, 0.02, seed=7000 + vi)
     r = mx.mx_reference(bf16_bits(x), bf16_bits(w))
     w_p, w_s = _weights(r)
@@ -276,8 +282,7 @@ def test_mx4_weight_packing_matches_the_layout_definition(N, K):
     assert np.array_equal(out.cpu().numpy()[:n], pack_fp4_ref(codes))
 
 
-@pytest.mark.parametrize("vi", range(len(MXV)))
-def test_every_mx4_instantiation_matches_oracle(vi):
+def _mx4_args(vi):
     swap, (wn, wk), rows, pf, amode = MXV[vi]
     M = MS[(vi + 3) % len(MS)]
     K = [1024, 1152, 2048][(vi + 1) % 3]
@@ -285,11 +290,17 @@ def test_every_mx4_instantiation_matches_oracle(vi):
     split = SPLITS[(vi // 2) % len(SPLITS)]
     cfg = dict(swap_ab=swap, split_k=split, waves_n=wn, waves_k=wk, rows_per_wave=rows, prefetch=pf,
                a_mode=amode, w_layout=1)
-    try:
-        plan = ql.qlinear_plan_with_config(ql.MXFP4, M, N, K, cfg)
-    except ql.QLinearError as e:
-        assert e.status == 2, e
-        pytest.skip("configuration not instantiated: %s" % e)
+    return ql.MXFP4, M, N, K, cfg
+
+
+MX4_CASES = cases("mxfp4", [(vi,) for vi in range(len(MXV))], _mx4_args)
+
+
+@pytest.mark.parametrize("vi", [c[0] for c in MX4_CASES])
+def test_every_mx4_instantiation_matches_oracle(vi):
+    _, M, N, K, cfg = _mx4_args(vi)
+    wk = cfg["waves_k"]
+    plan = ql.qlinear_plan_with_config(ql.MXFP4, M, N, K, cfg)
     x, w = make_inputs(K, N, M, 0.02, seed=9000 + vi)
     r = mx.mx4_reference(bf16_bits(x), bf16_bits(w))
     w_p, w_s = _weights4(r)
@@ -328,19 +339,23 @@ TILED_MX = list(itertools.product([0, 1], [(64, 128), (64, 256), (128, 128), (12
                                   [1, 2]))
 
 
-@pytest.mark.parametrize("vi", range(len(TILED_MX)))
-def test_every_mx_tiled_instantiation_matches_oracle(vi):
+def _mx_tiled_args(vi):
     swap, (bm, bn), pf, split = TILED_MX[vi]
     M = [40, 100, 200, 257][vi % 4]
     K = [1024, 1152][vi % 2]
     N = 300 + 16 * (vi % 5)
     cfg = dict(algo=ql.ALGO_TILED, swap_ab=swap, split_k=split, tile_m=bm, tile_n=bn, prefetch=pf, w_lds=0,
                a_mode=2, w_layout=1)
-    try:
-        plan = ql.qlinear_plan_with_config(ql.MXFP8, M, N, K, cfg)
-    except ql.QLinearError as e:
-        assert e.status == 2, e
-        pytest.skip("configuration not instantiated: %s" % e)
+    return ql.MXFP8, M, N, K, cfg
+
+
+MX_TILED_CASES = cases("mxfp8_tiled", [(vi,) for vi in range(len(TILED_MX))], _mx_tiled_args)
+
+
+@pytest.mark.parametrize("vi", [c[0] for c in MX_TILED_CASES])
+def test_every_mx_tiled_instantiation_matches_oracle(vi):
+    _, M, N, K, cfg = _mx_tiled_args(vi)
+    plan = ql.qlinear_plan_with_config(ql.MXFP8, M, N, K, cfg)
     x, w = make_inputs(K, N, M, 0.02, seed=11000 + vi)
     r = mx.mx_reference(bf16_bits(x), bf16_bits(w))
     w_p, w_s = _weights(r)

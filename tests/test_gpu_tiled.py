@@ -18,6 +18,7 @@ import quantized_gemm_decode_amd as ql
 from tests.gpu_util import (dev_codes, dev_f32, fp8_check, fp8_ok, host_bf16_bits, host_codes,
                             MIN_FRAC_WITHIN_ULP, requires_gpu, run_gemm)
 from tests.test_gpu_gemm import _assert_parity, _dev_packed_act
+from tests.instantiations import cases
 from workloads import bf16_bits, config_by_name, make_inputs
 
 pytestmark = [pytest.mark.gpu, requires_gpu]
@@ -32,22 +33,26 @@ def _ref(fmt, M, N, K, seed):
     return oracle.reference(fmt, bf16_bits(x), bf16_bits(w))
 
 
-@pytest.mark.parametrize("fmt", FMTS)
-@pytest.mark.parametrize("M", [40, 200])
-@pytest.mark.parametrize("vi", range(len(TVARIANTS)))
-def test_every_tiled_instantiation_matches_oracle(fmt, M, vi):
+def _tiled_args(fmt, M, vi):
     swap, (bm, bn), (packed, apacked), pf = TVARIANTS[vi]
     split = [1, 2, 4][(vi + M) % 3]
     N = 300 if bn == 128 else 520                         # several tiles + a ragged tail
     K = 1152 if fmt == ql.BLOCK_FP8 or vi % 2 else 1040   # 1040: ragged last K block (9 blocks: ring wraps)
-    r = _ref(fmt, M, N, K, seed=3000 + vi * 5 + M)
     cfg = dict(algo=ql.ALGO_TILED, swap_ab=swap, split_k=split, tile_m=bm, tile_n=bn, w_layout=packed, prefetch=pf,
                a_mode=2 * apacked)
-    try:
-        plan = ql.qlinear_plan_with_config(fmt, M, N, K, cfg)
-    except ql.QLinearError as e:
-        assert e.status == 2, e
-        pytest.skip("tile not instantiated for this format: %s" % e)
+    return fmt, M, N, K, cfg
+
+
+TILED_CASES = cases("tiled", [(f, M, vi) for f in FMTS for M in (40, 200) for vi in range(len(TVARIANTS))],
+                    _tiled_args)
+
+
+@pytest.mark.parametrize("fmt,M,vi", TILED_CASES)
+def test_every_tiled_instantiation_matches_oracle(fmt, M, vi):
+    _, _, N, K, cfg = _tiled_args(fmt, M, vi)
+    packed, apacked = cfg["w_layout"], cfg["a_mode"] // 2
+    r = _ref(fmt, M, N, K, seed=3000 + vi * 5 + M)
+    plan = ql.qlinear_plan_with_config(fmt, M, N, K, cfg)
     a_q, s_a, w_q, s_w = (dev_codes(fmt, r["a_q"]), dev_f32(r["s_a"]), dev_codes(fmt, r["w_q"]), dev_f32(r["s_w"]))
     if packed:
         w_q = ql.pack_weight(w_q)
