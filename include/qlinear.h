@@ -435,12 +435,16 @@ ql_status qlinear_forward(ql_plan plan, const void* x_bf16, void* a_q, void* a_s
  * codes and scales bit for bit), in the GEMM launch itself: no separate
  * quantizer launch and no second pass over H.
  *
- * h_amax / x_amax: M + 1 32-bit words, 16-byte aligned, caller-owned, all
- * zero before the first producer runs: words 0..M-1 hold the binary32 bit
- * patterns of the token maxima, word M an arrival counter.  The consumer
- * (qlinear_forward_amax) leaves them all zero again, so one buffer serves
- * every layer in turn; a producer must be followed by exactly one consumer
- * before the next producer.
+ * h_amax / x_amax: QL_AMAX_BUFFER_BYTES bytes (any M <= 32), 16-byte
+ * aligned, caller-owned, all zero before the first producer runs.  Atomics
+ * on one cache line serialize, so the maxima are spread over 64 replicas of
+ * one 128-byte line each: word 32 r + m holds the binary32 bit pattern of
+ * the largest |h| of token m among the producer waves that chose replica r
+ * (the token's amax is the maximum over r); the consumer's arrival counters
+ * follow (16 group counters and one counter of groups, a line each).  The
+ * consumer (qlinear_forward_amax) leaves the whole buffer zero again, so one
+ * buffer serves every layer in turn; a producer must be followed by exactly
+ * one consumer before the next producer, and the two run in stream order.
  *
  * qlinear_forward_glu_amax: qlinear_forward of a SiLU-and-mul plan
  * (qlinear_plan_glu, FP8_Dynamic or W8A8_INT8) that also accumulates the
@@ -449,9 +453,12 @@ ql_status qlinear_forward(ql_plan plan, const void* x_bf16, void* a_q, void* a_s
  * (..., a_packed = 3) for X whose amax words are x_amax.  An a_mode 5 plan is
  * one launch that reads X (bf16, the whole of it across the grid, each
  * workgroup its K chunk) and writes a_q / a_scale as qlinear_quantize_act_packed
- * would; any other plan runs the quantizer and the GEMM and then clears the
- * words.  Either way x_amax is all zero afterwards.  Enqueue-only.
+ * would; any other decode plan runs the quantizer and the GEMM, whose first
+ * workgroup clears the buffer (a large-M plan adds a fill launch).  Either
+ * way x_amax is all zero afterwards.  Enqueue-only.
  */
+#define QL_AMAX_BUFFER_BYTES 10368
+
 ql_status qlinear_forward_glu_amax(ql_plan plan, const void* x_bf16, void* a_q, void* a_scale,
                                    const void* w_q, const void* w_scale, void* h_bf16, void* h_amax,
                                    void* workspace, void* stream);

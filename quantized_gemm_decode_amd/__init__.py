@@ -453,15 +453,28 @@ def qlinear_forward(plan, x, a_q, a_scale, w_q, w_scale, y, workspace=None, stre
            "qlinear_forward")
 
 
-def amax_buffer(M, device="cuda"):
-    """Zeroed per-token amax words (M maxima + the consumer's counter) for
-    qlinear_forward_glu_amax / qlinear_forward_amax; reusable, the consumer
-    leaves it zeroed."""
-    return torch.zeros(-(-(M + 1) // 4) * 4, dtype=torch.int32, device=device)
+# QL_AMAX_BUFFER_BYTES of qlinear.h: 64 replica lines of 32 words (token m
+# of replica r at word 32 r + m), then 17 counter lines
+AMAX_BUFFER_BYTES = 10368
+AMAX_REPLICAS, AMAX_LINE = 64, 32
+
+
+def amax_buffer(M=None, device="cuda"):
+    """Zeroed per-token amax buffer for qlinear_forward_glu_amax /
+    qlinear_forward_amax (any M <= 32); reusable, the consumer leaves it zeroed."""
+    return torch.zeros(AMAX_BUFFER_BYTES // 4, dtype=torch.int32, device=device)
+
+
+def amax_of_buffer(buf, M):
+    """The per-token maxima a buffer holds (the maximum over its replicas),
+    as binary32 bit patterns (uint32 numpy array of M values)."""
+    import numpy as np
+    w = buf.cpu().numpy().view(np.uint32)
+    return w[:AMAX_REPLICAS * AMAX_LINE].reshape(AMAX_REPLICAS, AMAX_LINE)[:, :M].max(axis=0)
 
 
 def _need_amax(plan, t, name):
-    _need(t, name, 4 * (plan.M + 1))
+    _need(t, name, AMAX_BUFFER_BYTES)
 
 
 def qlinear_forward_glu_amax(plan, x, a_q, a_scale, w_q, w_scale, h, h_amax, workspace=None, stream=None):

@@ -1027,12 +1027,13 @@ ql_status qlinear_forward_amax(ql_plan p, const void* x_bf16, void* x_amax, void
   if (p->M == 0) return QL_OK;
   if (!x_amax) return fail(QL_E_INVALID, "x_amax is NULL");
   if (!aligned16(x_amax)) return fail(QL_E_ALIGN, "x_amax is not 16-byte aligned");
-  if (!p->tiled && p->cfg.a_mode == 5 && p->N > 0 && p->K > 0)
+  // a decode plan with work to do takes the buffer: a_mode 5 reads it, any
+  // other finds the amax itself and its first workgroup clears the buffer
+  if (!p->tiled && p->N > 0 && p->K > 0)
     return forward_impl(p, x_bf16, a_q, a_scale, w_q, w_scale, y, workspace, stream, static_cast<uint32_t*>(x_amax));
-  // any other plan: the quantizer finds the amax itself; then clear the words for the next producer
   ql_status st = forward_impl(p, x_bf16, a_q, a_scale, w_q, w_scale, y, workspace, stream);
   if (st != QL_OK) return st;
-  hipError_t e = qlk::launch_fill_zero_bf16(x_amax, 2 * (p->M + 1), static_cast<hipStream_t>(stream));
+  hipError_t e = qlk::launch_fill_zero_bf16(x_amax, qlk::AMAX_WORDS * 2, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? QL_OK : hip_fail(e, "amax clear");
 }
 

@@ -7,6 +7,21 @@
 
 namespace qlk {
 
+// The per-token amax buffer (32-bit words).  Device-scope atomics on one
+// cache line serialize, and every wave of a SiLU-and-mul grid folds its
+// tokens' maxima into the buffer, so the maxima are spread over
+// AMAX_REPLICAS lines of AMAX_LINE words (token m of replica r at word
+// r * AMAX_LINE + m, M <= 32): a producer wave picks one replica, a
+// consumer takes the maximum over all of them.  The consumer's arrival
+// counters follow, one line each: AMAX_GROUPS group counters (workgroup b
+// counts in group b % AMAX_GROUPS), then the counter of completed groups.
+constexpr uint32_t AMAX_LINE = 32;
+constexpr uint32_t AMAX_REPLICAS = 64;
+constexpr uint32_t AMAX_GROUPS = 16;
+constexpr uint32_t AMAX_CTR0 = AMAX_REPLICAS * AMAX_LINE;
+constexpr uint32_t AMAX_TOP = AMAX_CTR0 + AMAX_GROUPS * AMAX_LINE;
+constexpr uint32_t AMAX_WORDS = AMAX_TOP + AMAX_LINE;
+
 // Format selector of the kernels (matches ql_format's order).  FMT_MX:
 // MXFP8, E4M3 codes with one E8M0 scale byte per 32 values along K.
 // FMT_MX4: MXFP4 weights (E2M1, two a byte) with MXFP8 activations.
@@ -33,10 +48,10 @@ struct DecodeArgs {
   const uint16_t* x;   // X [M, K] bf16
   uint8_t* aq_out;     // packed A_q, ceil(M/16) x G tiles of 2 KB
   float* sa_out;       // s_a [M]
-  // per-token amax words of X (binary32 bit patterns of max |x| per row),
-  // then one arrival counter: written by a SiLU-and-mul plan's epilogue
-  // (atomic max over its output H) when non-null; read -- and reset to zero
-  // by the last workgroup -- by an activation-mode-5 plan
+  // per-token amax buffer of X (layout below): written by a SiLU-and-mul
+  // plan's epilogue (atomic max over its output H) when non-null; read --
+  // and reset to zero by the last workgroup -- by an activation-mode-5 plan;
+  // cleared by any other decode plan that is given it
   uint32_t* amax;
   int M, N, K;
   int G;               // number of 128-wide K blocks, ceil(K / 128)

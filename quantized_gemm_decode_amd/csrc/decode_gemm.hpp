@@ -92,6 +92,15 @@ __global__ void __launch_bounds__(NW * 64) qgemm_decode_kernel(DecodeArgs p) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  // A plan other than activation mode 5 given its input's amax buffer (the
+  // consumer end of the gate_up -> down chain, quantizing X by itself):
+  // nothing here reads the buffer, so workgroup 0 clears it for the next
+  // producer.
+  if constexpr (!GLU && AL != 5) {
+    if (p.amax && blockIdx.x == 0)
+      for (uint32_t v = (uint32_t)tid; v < AMAX_WORDS / 4u; v += (uint32_t)(NW * 64))
+        reinterpret_cast<u32x4*>(p.amax)[v] = u32x4{0u, 0u, 0u, 0u};
+  }
   const int WK = p.waves_k;
   const int wn = wave / WK;
   const int wk = wave - wn * WK;
@@ -437,21 +446,26 @@ __global__ void __launch_bounds__(NW * 64) qgemm_decode_kernel(DecodeArgs p) {
   // lanes of a row of the wave hold one group.
   constexpr int XP = FUSED ? 32 / NW : 1;
   u32x4 xv[XP];
-  uint32_t xam[XP];                              // activation mode 5: the amax word of each piece's row
   const uint32_t upr = K / 512u;                 // per-token: wave pieces per token row
   const uint32_t ppr = (uint32_t)nkc * 16u;      // chunked: pieces per row of the chunk
+  // Activation mode 5: every replica's maxima of the M tokens, AMW words a
+  // thread, loaded first (older than the X and weight loads, so the wait for
+  // X covers them).  The producer was an earlier kernel of the stream, whose
+  // atomics were complete and visible device-wide when it ended, so plain
+  // loads see them.  The maxima over the replicas are folded in LDS
+  // (FA_RED, zeroed here) after that wait.
+  constexpr int AMW = AL == 5 ? (int)((AMAX_REPLICAS * 16u + NW * 64 - 1) / (NW * 64)) : 1;
+  uint32_t amw[AMW];
   if constexpr (AL == 5) {
-    // the row amax words first (older than the X and weight loads, so the
-    // wait for X covers them), as agent-scope loads: the producer's atomic
-    // maxima are performed at the device's coherence point
+    const __amdgpu_buffer_rsrc_t ram = make_rsrc(p.amax, AMAX_WORDS * 4u);
+    const uint32_t nwords = AMAX_REPLICAS * M;
 #pragma unroll
-    for (int i = 0; i < XP; ++i) {
-      const uint32_t P = (uint32_t)(tid + NW * 64 * i);
-      const uint32_t m = P / ppr;
-      xam[i] = (uint32_t)(wave * 64 + NW * 64 * i) < M * ppr && m < M
-                   ? __hip_atomic_load(p.amax + m, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
-                   : 0u;
+    for (int i = 0; i < AMW; ++i) {
+      const uint32_t j = (uint32_t)(tid + NW * 64 * i);
+      const uint32_t r = j / M;
+      amw[i] = __float_as_uint(bload_f32(ram, j < nwords ? (r * AMAX_LINE + (j - r * M)) * 4u : OOB));
     }
+    if (tid < (int)AMAX_LINE) reinterpret_cast<uint32_t*>(smem + FA_RED)[tid] = 0u;
   }
   if constexpr (FUSED) {
     const __amdgpu_buffer_rsrc_t rx = make_rsrc(p.x, M * K * 2u);
@@ -521,6 +535,17 @@ __global__ void __launch_bounds__(NW * 64) qgemm_decode_kernel(DecodeArgs p) {
     static_assert(NW_LOADS <= 63, "vmcnt holds 6 bits");
     __builtin_amdgcn_s_waitcnt((NW_LOADS & 15) | (7 << 4) | (15 << 8) | ((NW_LOADS >> 4) << 14));
     float* ssc = reinterpret_cast<float*>(smem + FA_SC);
+    uint32_t* amx = reinterpret_cast<uint32_t*>(smem + FA_RED);
+    lds_barrier();   // the zeroed token maxima
+    {
+      const uint32_t nwords = AMAX_REPLICAS * M;
+#pragma unroll
+      for (int i = 0; i < AMW; ++i) {
+        const uint32_t j = (uint32_t)(tid + NW * 64 * i);
+        if (j < nwords) __hip_atomic_fetch_max(amx + (j % M), amw[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      }
+    }
+    lds_barrier();
     const uint32_t npc = M * ppr;
 #pragma unroll
     for (int i = 0; i < XP; ++i) {
@@ -528,21 +553,37 @@ __global__ void __launch_bounds__(NW * 64) qgemm_decode_kernel(DecodeArgs p) {
       if ((uint32_t)(wave * 64 + NW * 64 * i) >= npc) continue;   // no piece of this wave
       if (P < npc) {
         const uint32_t m = P / ppr, w = P - m * ppr;
-        const float sc = scale_of<FMT>(__uint_as_float(xam[i]));
+        const float sc = scale_of<FMT>(__uint_as_float(amx[m]));
         *reinterpret_cast<u32x2*>(smem + FA0 + m * (uint32_t)CH + w * 8u) = quant8<FMT>(xv[i], sc, recip_of(sc));
         if (w == 0u) ssc[m] = sc;
       }
     }
     lds_barrier();
-    // Every wave of this workgroup has its amax words (the wait above), so
-    // count the workgroup; the last of the grid resets the words and the
-    // counter for the next producer.
-    if (tid == 0) {
-      const unsigned prev = __hip_atomic_fetch_add(p.amax + M, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      if (prev == gridDim.x - 1u) {
-        for (uint32_t m = 0; m < M; ++m)
-          __hip_atomic_exchange(p.amax + m, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_exchange(p.amax + M, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    // Every wave of this workgroup has read the buffer (the wait above), so
+    // count the workgroup: in its group's counter, and the workgroup that
+    // completes a group in the counter of groups.  The one that completes
+    // the last group -- every workgroup of the grid has then read the
+    // maxima -- zeroes the replicas (wave 0); each counter is reset by the
+    // workgroup that completed it.
+    if (wave == 0) {
+      uint32_t last = 0;
+      if (lane == 0) {
+        const uint32_t grp = blockIdx.x % AMAX_GROUPS;
+        const uint32_t members = (gridDim.x - grp + AMAX_GROUPS - 1u) / AMAX_GROUPS;
+        uint32_t* gctr = p.amax + AMAX_CTR0 + grp * AMAX_LINE;
+        if (__hip_atomic_fetch_add(gctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == members - 1u) {
+          __hip_atomic_exchange(gctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          const uint32_t ngroups = min(gridDim.x, AMAX_GROUPS);
+          if (__hip_atomic_fetch_add(p.amax + AMAX_TOP, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+              ngroups - 1u) {
+            __hip_atomic_exchange(p.amax + AMAX_TOP, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            last = 1;
+          }
+        }
+      }
+      if (__builtin_amdgcn_readfirstlane(last)) {
+        for (uint32_t v = (uint32_t)lane; v < AMAX_CTR0 / 4u; v += 64u)
+          reinterpret_cast<u32x4*>(p.amax)[v] = u32x4{0u, 0u, 0u, 0u};
       }
     }
     if (p.aq_out && tile == 0 && chunk == 0 && (uint32_t)tid < M) p.sa_out[tid] = ssc[tid];
@@ -777,6 +818,8 @@ __global__ void __launch_bounds__(NW * 64) qgemm_decode_kernel(DecodeArgs p) {
     // atomic maximum on its binary32 bit pattern (non-negative, so the
     // integer order is the numeric one; exact whatever the order).
     if (p.amax) {
+      // this wave's replica of the maxima (spreads the atomics over lines)
+      uint32_t* am = p.amax + ((uint32_t)blockIdx.x * (uint32_t)(NW / WK) + (uint32_t)wn) % AMAX_REPLICAS * AMAX_LINE;
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
         if constexpr (SWAP) {
@@ -786,7 +829,7 @@ __global__ void __launch_bounds__(NW * 64) qgemm_decode_kernel(DecodeArgs p) {
           v = fmaxf(v, __shfl_xor(v, 32));
           const uint32_t m = (uint32_t)(mt * 16 + r16);
           if (g == 0 && m < M)
-            __hip_atomic_fetch_max(p.amax + m, __float_as_uint(v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_fetch_max(am + m, __float_as_uint(v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         } else {
           // lane: column r16, tokens 16mt + 4g + r -> fold the 16 columns of the DPP row
 #pragma unroll
@@ -794,7 +837,7 @@ __global__ void __launch_bounds__(NW * 64) qgemm_decode_kernel(DecodeArgs p) {
             const float v = row16_max_nonneg(habs[mt][r]);
             const uint32_t m = (uint32_t)(mt * 16 + 4 * g + r);
             if (r16 == 0 && m < M)
-              __hip_atomic_fetch_max(p.amax + m, __float_as_uint(v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+              __hip_atomic_fetch_max(am + m, __float_as_uint(v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
           }
         }
       }

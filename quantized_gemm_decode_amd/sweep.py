@@ -205,8 +205,9 @@ class Timer:
         if self.layout == 5:
             # one amax buffer per launch of the graph (each consumer clears its
             # own), refilled before every replay
+            # (the maxima in replica 0; the consumer reads every replica)
             mag = (xm.view(torch.int16).to(torch.int32) & 0x7FFF) << 16
-            words = torch.zeros(R, -(-(M + 1) // 4) * 4, dtype=torch.int32, device="cuda")
+            words = torch.zeros(R, ql.AMAX_BUFFER_BYTES // 4, dtype=torch.int32, device="cuda")
             words[:, :M] = mag.max(dim=1).values
             amax0 = words.clone()
 

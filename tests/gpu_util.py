@@ -131,3 +131,25 @@ def pack_fp4_ref(codes):
                 if row < N:
                     out[t, kb, l] = b[row, 64 * kb + 16 * (l // 16):64 * kb + 16 * (l // 16) + 16]
     return out.reshape(-1)
+
+
+def amax_words(x_bits):
+    """max |x| per row of bf16 bit patterns, as binary32 bit patterns."""
+    return ((np.asarray(x_bits).astype(np.uint32) & 0x7FFF) << 16).max(axis=1).astype(np.uint32)
+
+
+def filled_amax_buffer(maxima, seed=0):
+    """An amax buffer holding the given per-token maxima the way producer
+    waves leave it: each token's maximum in one random replica, the other
+    replicas holding smaller (or zero) non-negative values."""
+    rng = np.random.default_rng(seed)
+    buf = ql.amax_buffer()
+    words = np.zeros(buf.numel(), np.uint32)
+    rep = words[:ql.AMAX_REPLICAS * ql.AMAX_LINE].reshape(ql.AMAX_REPLICAS, ql.AMAX_LINE)
+    for m, v in enumerate(np.asarray(maxima, np.uint32)):
+        below = rng.integers(0, int(v) + 1, ql.AMAX_REPLICAS, dtype=np.uint64).astype(np.uint32)
+        below[rng.random(ql.AMAX_REPLICAS) < 0.5] = 0
+        rep[:, m] = below
+        rep[rng.integers(ql.AMAX_REPLICAS), m] = v
+    buf.copy_(torch.from_numpy(words.view(np.int32)))
+    return buf

@@ -490,3 +490,24 @@ def test_given_amax_planning():
     assert ql.qlinear_plan_layouts(ql.W8A8_INT8, 4, 3072, 4160, 1, 3).config["a_mode"] in (2, 3)
     with pytest.raises(ql.QLinearError):
         ql.qlinear_plan_layouts(ql.BLOCK_FP8, 4, 4096, 4096, 1, 3)
+
+
+def test_amax_buffer_layout_matches_the_header():
+    """The amax buffer: 64 replica lines of 32 words, then 17 counter lines;
+    the binding's size and layout constants are the header's (and the
+    kernels', which index it with the same numbers)."""
+    text = open(HEADER).read()
+    m = re.search(r"#define\s+QL_AMAX_BUFFER_BYTES\s+(\d+)", text)
+    assert m and int(m.group(1)) == ql.AMAX_BUFFER_BYTES
+    assert ql.AMAX_BUFFER_BYTES == (ql.AMAX_REPLICAS * ql.AMAX_LINE + 17 * ql.AMAX_LINE) * 4
+    args = open(os.path.join(ROOT, "quantized_gemm_decode_amd", "csrc", "decode_args.hpp")).read()
+    assert re.search(r"AMAX_REPLICAS\s*=\s*%d;" % ql.AMAX_REPLICAS, args)
+    assert re.search(r"AMAX_LINE\s*=\s*%d;" % ql.AMAX_LINE, args)
+    assert re.search(r"AMAX_GROUPS\s*=\s*16;", args)
+    buf = ql.amax_buffer(device="cpu")
+    assert buf.numel() * 4 == ql.AMAX_BUFFER_BYTES and not buf.any()
+    words = buf.numpy().view("uint32")
+    words[3 * ql.AMAX_LINE + 2] = 7
+    words[40 * ql.AMAX_LINE + 2] = 9
+    words[5] = 1
+    assert list(ql.amax_of_buffer(buf, 3)) == [0, 0, 9]

@@ -17,17 +17,11 @@ import torch
 
 import oracle
 import quantized_gemm_decode_amd as ql
-from tests.gpu_util import fp8_check, fp8_ok, host_bf16_bits, pack_ref, requires_gpu
+from tests.gpu_util import amax_words, filled_amax_buffer, fp8_check, fp8_ok, host_bf16_bits, pack_ref, requires_gpu
 from workloads import bf16_bits, make_inputs
 
 pytestmark = [pytest.mark.gpu, requires_gpu]
 FMTS = [ql.FP8_DYNAMIC, ql.W8A8_INT8]
-
-
-def _amax_words(h_bits):
-    """max |h| per row of bf16 bit patterns, as binary32 bit patterns."""
-    mag = (h_bits.astype(np.uint32) & 0x7FFF) << 16
-    return mag.max(axis=1).astype(np.uint32)
 
 
 def _weights(fmt, N, K, seed, sigma=0.02):
@@ -80,10 +74,13 @@ def test_chain_matches_oracle(fmt, M):
     h_ref, h_true, bound = oracle.glu_reference(fmt, r, split=glu.facts["chunks"])
     st = oracle.check_fp8_parity(h_bits, h_ref, h_true, bound)
     assert fp8_ok(st), st
-    # the amax words: max |H| per token of this H, exactly; the counter word zero
+    # the maxima over the replicas: max |H| per token of this H, exactly; the
+    # counters zero; nothing written past the M tokens of any replica
     words = amax.cpu().numpy().view(np.uint32)
-    assert np.array_equal(words[:M], _amax_words(h_bits))
-    assert words[M] == 0
+    assert np.array_equal(ql.amax_of_buffer(amax, M), amax_words(h_bits))
+    reps = words[:ql.AMAX_REPLICAS * ql.AMAX_LINE].reshape(ql.AMAX_REPLICAS, ql.AMAX_LINE)
+    assert not reps[:, M:].any() and not words[ql.AMAX_REPLICAS * ql.AMAX_LINE:].any()
+    assert np.count_nonzero(reps[:, :M].any(axis=1)) > 1, "the producer waves spread over replicas"
     down = ql.qlinear_plan_layouts(fmt, M, N2, I, 1, 3)
     assert (down.config["a_mode"] == 5) == (M <= 16)
     a_q, a_s, y = _consume(fmt, down, h, amax, wd_p, wd_s)
@@ -91,12 +88,8 @@ def test_chain_matches_oracle(fmt, M):
     assert int(torch.count_nonzero(amax)) == 0, "the consumer leaves the amax words zero"
 
 
-def _given_amax(x_bits, M):
-    buf = ql.amax_buffer(M)
-    host = np.zeros(buf.numel(), np.uint32)
-    host[:M] = _amax_words(x_bits)
-    buf.copy_(torch.from_numpy(host.view(np.int32)))
-    return buf
+def _given_amax(x_bits, M, seed=0):
+    return filled_amax_buffer(amax_words(x_bits), seed=seed)
 
 
 # a_mode 5 instantiations: waves (n x k), rows per wave, batch, swap
@@ -130,8 +123,8 @@ def test_every_mode5_instantiation(fmt, M, split):
         plan = _mode5_available(fmt, M, N, K, cfg)
         if plan is None:
             continue
-        for _ in range(2):
-            amax = _given_amax(xb, M)
+        for rep in range(2):
+            amax = _given_amax(xb, M, seed=rep)
             a_q, a_s, y = _consume(fmt, plan, x.cuda(), amax, w_p, w_s)
             _check_consumer(fmt, plan, xb, w_full, a_q, a_s, y, cfg)
             assert int(torch.count_nonzero(amax)) == 0

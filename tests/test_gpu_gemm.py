@@ -16,8 +16,8 @@ import torch
 
 import oracle
 import quantized_gemm_decode_amd as ql
-from tests.gpu_util import (MIN_FRAC_WITHIN_ULP, dev_bf16, dev_codes, dev_f32, fp8_check, fp8_ok, host_bf16_bits,
-                            host_codes, pack_ref, requires_gpu, run_gemm)
+from tests.gpu_util import (MIN_FRAC_WITHIN_ULP, amax_words, dev_bf16, dev_codes, dev_f32, filled_amax_buffer, fp8_check,
+                            fp8_ok, host_bf16_bits, host_codes, pack_ref, requires_gpu, run_gemm)
 from tests.instantiations import cases
 from workloads import CONFIGS, bf16_bits, config_by_name, decode_points, decode_workloads, make_inputs
 
@@ -432,10 +432,7 @@ def test_every_table_entry_matches_oracle(entry):
         # given-amax forward: the amax words of X from the host, cleared by the run
         a_f = ql.act_buffer(plan)
         s_f = torch.empty_like(a_s)
-        amax = ql.amax_buffer(M)
-        words = np.zeros(amax.numel(), np.uint32)
-        words[:M] = ((bf16_bits(xm).astype(np.uint32) & 0x7FFF) << 16).max(axis=1)
-        amax.copy_(torch.from_numpy(words.view(np.int32)))
+        amax = filled_amax_buffer(amax_words(bf16_bits(xm)), seed=M + N)
         ql.qlinear_forward_amax(plan, xm.cuda(), amax, a_f, s_f, w_use, w_s, y, plan.new_workspace())
         torch.cuda.synchronize()
         assert torch.equal(s_f, a_s) and int(torch.count_nonzero(amax)) == 0
