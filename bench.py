@@ -279,6 +279,10 @@ def parse_args(argv=None):
     ap.add_argument("--profile-pass", action="store_true",
                     help="for hardware-counter runs: launch each point's quantize+GEMM eagerly on 3 weight "
                          "copies, then a plain 256 MiB device copy 3 times (the counters' calibration), and exit")
+    ap.add_argument("--library-ref", action="store_true",
+                    help="FP8_Dynamic workloads: time each point's GEMM kernel next to torch._scaled_mm "
+                         "(the vendor library, rowwise scales: the same per-token x per-channel scaling) on the "
+                         "same codes and weight copies; print one JSON line per workload, and exit")
     ap.add_argument("--glu", action="store_true",
                     help="time the workload's gate_up points two ways -- the forward plan writing Y [M, N], and "
                          "the SiLU-and-mul plan writing silu(gate)*up [M, N/2] -- and the gate_up -> down chain "
@@ -521,6 +525,10 @@ def main(argv=None):
     Ws = [prepare_workload(ql, torch, wl, args.layout, dev) for wl in wls]
     if args.profile_pass:
         return profile_pass(ql, Ws, stream)
+    if args.library_ref:
+        for W in Ws:
+            library_ref_pass(ql, torch, np, W, stream, args.kernel_reps)
+        return 0
     if args.glu:
         # one JSON line per workload that has a gate_up projection
         for W in Ws:
@@ -807,6 +815,92 @@ def glu_pass(ql, wl, pts, shapes, stream, args):
                       "shape": "gate_up %dx%d" % (gu[0]["N"], gu[0]["K"]) if gu else None,
                       "data": "synthetic", "kernel_reps": args.kernel_reps, "per_point": out}), flush=True)
     return 0
+
+
+def library_ref_pass(ql, torch, np, W, stream, reps):
+    """Per point: this library's GEMM kernel (as in point_timing) and
+    torch._scaled_mm -- the vendor GEMM library, row-wise scales, bf16 out --
+    on the same activation codes and the same number of distinct weight
+    copies (row-major codes, as that library takes them), both timed as
+    graphs of back-to-back launches with HIP events.  A reference for the
+    compute-bound points, not part of the product path."""
+    wl = W["wl"]
+    if W["fmt"] != ql.FP8_DYNAMIC:
+        print(json.dumps({"workload": wl.name, "skipped": "the reference takes FP8_Dynamic (row-wise) only"}))
+        return
+    from workloads import make_inputs
+    ours = {(q["shape"], q["M"]): q for q in point_timing(ql, torch, np, W, stream, reps)}
+    out = []
+    rm = {}
+    for p in W["pts"]:
+        sh = W["shapes"][p["lab"]]
+        M, N, K = p["M"], p["N"], p["K"]
+        if p["lab"] not in rm:
+            rm.clear()
+            _, w = make_inputs(K, N, max(wl.ms), wl.sigma_w, seed=wl.seed)   # the weights prepare_workload made
+            w_q, w_s = ql.quantize_weight(ql.FP8_DYNAMIC, w.to("cuda"))
+            copies = sh["copies"]
+            wq_all = torch.empty((copies,) + tuple(w_q.shape), dtype=w_q.dtype, device="cuda")
+            wq_all[:] = w_q
+            rm[p["lab"]] = (wq_all, w_s.view(1, N).contiguous(), copies)
+        wq_all, sb, copies = rm[p["lab"]]
+        a_q, a_s = ql.quantize_act(ql.FP8_DYNAMIC, p["x"])
+        sa = a_s.view(M, 1).contiguous()
+        torch.cuda.synchronize()
+        R = min(copies, 64)
+        y = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
+        def lib_mm(c):
+            torch._scaled_mm(a_q, wq_all[c].t(), scale_a=sa, scale_b=sb, out_dtype=torch.bfloat16, out=y)
+        try:
+            with torch.cuda.stream(stream):
+                y_ref = torch._scaled_mm(a_q, wq_all[0].t(), scale_a=sa, scale_b=sb, out_dtype=torch.bfloat16)
+                lib_mm(0)
+            stream.synchronize()
+            # captured like this library's launches; trusted only if a replay reproduces the eager output
+            y.zero_()
+            torch.cuda.synchronize()
+            with torch.cuda.stream(stream):
+                ql.qlinear_graph_begin(stream)
+                for c in range(R):
+                    lib_mm(c)
+                g = ql.qlinear_graph_end(stream)
+            g.launch(stream)
+            stream.synchronize()
+            captured = bool(torch.equal(y, y_ref))
+        except RuntimeError as e:
+            out.append(dict(shape=p["lab"], M=M, N=N, K=K, us=ours[(p["lab"], M)]["us"], library_error=str(e)[:160]))
+            continue
+        samples = []
+        for _ in range(reps):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            if captured:
+                g.launch(stream)
+            else:                 # eager launches (host launch overhead included)
+                with torch.cuda.stream(stream):
+                    for c in range(R):
+                        lib_mm(c)
+            e1.record(stream)
+            e1.synchronize()
+            samples.append(e0.elapsed_time(e1) * 1e3 / R)
+        del g
+        lib_us = float(np.median(samples))
+        q = ours[(p["lab"], M)]
+        flops = 2.0 * M * N * K
+        # the two compute the same linear: largest difference relative to max |Y|
+        with torch.cuda.stream(stream):
+            ql.qlinear_forward(p["plan"], p["x"], p["a_q"], p["a_s"], sh["wq"][0], sh["ws"][0], y, p["wsp"],
+                               stream=stream)
+        stream.synchronize()
+        rel = float((y.float() - y_ref.float()).abs().max() / y_ref.float().abs().max().clamp_min(1e-30))
+        out.append(dict(shape=p["lab"], M=M, N=N, K=K, us=q["us"], TFLOPs=round(flops / (q["us"] * 1e-6) / 1e12, 1),
+                        library_us=round(lib_us, 3), library_TFLOPs=round(flops / (lib_us * 1e-6) / 1e12, 1),
+                        ratio=round(lib_us / q["us"], 3), algo=p["cfg"]["algo"], R=R, library_graph=captured,
+                        max_rel_diff=round(rel, 5)))
+    print(json.dumps({"metric": "µs per GEMM: this library's plan vs torch._scaled_mm (the vendor GEMM library, "
+                                "row-wise scales) on the same codes; ratio = library / this", "workload": wl.name,
+                      "data": "synthetic", "kernel_reps": reps, "per_point": out}), flush=True)
 
 
 def profile_pass(ql, Ws, stream):
