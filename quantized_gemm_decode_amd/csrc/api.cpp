@@ -168,7 +168,7 @@ ql_config heuristic_tiled(int32_t layout, bool a_packed, int64_t M, int64_t N, i
 // The last-resort decode plan: 4 waves side by side on N, split-K up to about
 // 1024 workgroups (instantiated for every format and operand layout).
 ql_config heuristic_config(int32_t fmt, int32_t layout, bool a_packed, int64_t M, int64_t N, int64_t K) {
-  // the MX formats' decode kernel serves up to 64 tokens (MXFP4 has no tiled kernel)
+  // the MX formats' decode kernel serves up to 64 tokens
   if (M > 32 && !(is_mx(fmt) && M <= 64)) return heuristic_tiled(layout, a_packed, M, N, K);
   ql_config c{};
   c.w_layout = layout;
@@ -390,7 +390,8 @@ ql_status build_tiled_plan(int32_t fmt, int64_t M, int64_t N, int64_t K, const q
   p->bn = cfg.tile_n;
   p->tiles_n = (int)((N + cfg.tile_n - 1) / cfg.tile_n);
   p->n_tiles = (int)((M + cfg.tile_m - 1) / cfg.tile_m) * p->tiles_n;
-  p->lds = (cfg.w_lds ? cfg.prefetch : 2) * (int64_t)(cfg.tile_m + cfg.tile_n) * 128;
+  // a stage: the A tile's tile_m rows and the B tile's tile_n rows of one K block (MXFP4: 64 bytes a row)
+  p->lds = (cfg.w_lds ? cfg.prefetch : 2) * ((int64_t)cfg.tile_m * 128 + (int64_t)cfg.tile_n * (fmt == QL_MXFP4 ? 64 : 128));
   if (p->lds > kTiledLdsLimit) {
     delete p;
     return fail(QL_E_UNSUPPORTED, "tile needs more LDS than a workgroup has");
@@ -406,6 +407,7 @@ ql_status build_tiled_plan(int32_t fmt, int64_t M, int64_t N, int64_t K, const q
   switch (p->tkey.fmt) {
     case qlk::FMT_INT8: pe = qlk::tiled_dispatch_int8(p->tkey, dim3(1), (size_t)p->lds, nullptr, dummy, true); break;
     case qlk::FMT_MX: pe = qlk::tiled_dispatch_mx(p->tkey, dim3(1), (size_t)p->lds, nullptr, dummy, true); break;
+    case qlk::FMT_MX4: pe = qlk::tiled_dispatch_mx4(p->tkey, dim3(1), (size_t)p->lds, nullptr, dummy, true); break;
     case qlk::FMT_BLOCK: pe = qlk::tiled_dispatch_block(p->tkey, dim3(1), (size_t)p->lds, nullptr, dummy, true); break;
     default: pe = qlk::tiled_dispatch_fp8(p->tkey, dim3(1), (size_t)p->lds, nullptr, dummy, true); break;
   }
@@ -438,10 +440,8 @@ ql_status build_plan(int32_t fmt, int64_t M, int64_t N, int64_t K, const ql_conf
   }
   if (is_mx(fmt)) {
     if (glu) return fail(QL_E_UNSUPPORTED, "MXFP8 / MXFP4 plans have no SiLU-and-mul epilogue");
-    if (fmt == QL_MXFP4 && (cfg.algo != QL_ALGO_DECODE || M > 64))
-      return fail(QL_E_UNSUPPORTED, "MXFP4 runs on the decode algorithm (M <= 64)");
     if (cfg.algo == QL_ALGO_TILED && cfg.w_lds)
-      return fail(QL_E_UNSUPPORTED, "MXFP8 tiled plans run the register ring (w_lds 0)");
+      return fail(QL_E_UNSUPPORTED, "MXFP8 / MXFP4 tiled plans run the register ring (w_lds 0)");
     if (cfg.w_layout != 1 || (cfg.a_mode != 2 && cfg.a_mode != 3))
       return fail(QL_E_UNSUPPORTED, "MXFP8 / MXFP4 plans need packed weights and packed activations (a_mode 2 or 3)");
   }
@@ -605,6 +605,7 @@ ql_status launch_gemm(const ql_plan_s* p, const void* a_q, const void* a_scale, 
     switch (p->tkey.fmt) {
       case qlk::FMT_INT8: e = qlk::tiled_dispatch_int8(p->tkey, tgrid, (size_t)p->lds, s, a, false); break;
       case qlk::FMT_MX: e = qlk::tiled_dispatch_mx(p->tkey, tgrid, (size_t)p->lds, s, a, false); break;
+      case qlk::FMT_MX4: e = qlk::tiled_dispatch_mx4(p->tkey, tgrid, (size_t)p->lds, s, a, false); break;
       case qlk::FMT_BLOCK: e = qlk::tiled_dispatch_block(p->tkey, tgrid, (size_t)p->lds, s, a, false); break;
       default: e = qlk::tiled_dispatch_fp8(p->tkey, tgrid, (size_t)p->lds, s, a, false); break;
     }

@@ -79,7 +79,7 @@ struct DecodeKey {
 
 // Compile-time shape of one tiled (M > 32) kernel instantiation.
 struct TiledKey {
-  int fmt;   // FMT_FP8 / FMT_INT8 / FMT_BLOCK
+  int fmt;   // FMT_FP8 / FMT_INT8 / FMT_BLOCK / FMT_MX / FMT_MX4
   int swap;  // weights as the matrix core's first operand
   int bm;    // output tile rows (tokens): 64, 128 or 256
   int bn;    // output tile columns (weight rows): 128 or 256
@@ -112,6 +112,8 @@ hipError_t tiled_dispatch_block(const TiledKey& k, dim3 grid, size_t lds, hipStr
                                 bool probe_only);
 hipError_t tiled_dispatch_mx(const TiledKey& k, dim3 grid, size_t lds, hipStream_t s, const DecodeArgs& a,
                              bool probe_only);
+hipError_t tiled_dispatch_mx4(const TiledKey& k, dim3 grid, size_t lds, hipStream_t s, const DecodeArgs& a,
+                              bool probe_only);
 
 // Quantizer launchers (quant.hip).
 // `packed`: codes in the packed activation layout (2 KB tiles of 16 rows x

@@ -70,10 +70,15 @@ __global__ void __launch_bounds__((64 * 2 * tiled_waves_n<FMT, BM, BN>())) qgemm
   constexpr int NT = 64 * NW;              // threads
   constexpr int TM = BM / 2, TN = BN / WGN;  // wave tile
   constexpr int IM = TM / 16, IN = TN / 16;
-  constexpr int STAGE = (BM + BN) * 128;   // bytes of one LDS stage
+  // MXFP4: E2M1 weights, 64 bytes a row per K block (1 KB packed tiles)
+  constexpr bool MXS = FMT == FMT_MX || FMT == FMT_MX4;   // E8M0 block scales in the matrix instruction
+  constexpr int WB = FMT == FMT_MX4 ? 64 : 128;          // weight bytes per row per K block
+  constexpr int WT = 16 * WB;                            // bytes of one packed weight tile
+  constexpr int STAGE = BM * 128 + BN * WB;  // bytes of one LDS stage
   constexpr int PA = BM * 8 / NT;          // 16-byte A pieces per thread per K block
-  constexpr int PB = BN * 8 / NT;
+  constexpr int PB = BN * (WB / 16) / NT;
   constexpr bool WP = WM == W_PACKED;
+  static_assert(FMT != FMT_MX4 || (WP && AP && NS == 0), "MXFP4: packed operands, register ring");
   using Acc = typename TiledAcc<FMT>::T;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   __shared__ int s_last;
@@ -113,12 +118,12 @@ __global__ void __launch_bounds__((64 * 2 * tiled_waves_n<FMT, BM, BN>())) qgemm
 
   const uint32_t MT16 = (M + 15u) / 16u;
   const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.a, AP ? MT16 * G * 2048u : M * K);
-  const __amdgpu_buffer_rsrc_t rw = make_rsrc(p.w, WP ? NT16 * G * 2048u : N * K);
+  const __amdgpu_buffer_rsrc_t rw = make_rsrc(p.w, WP ? NT16 * G * (uint32_t)WT : N * K);
   // MXFP8 scales: E8M0 bytes in lane order, 64 per (16-row group, K block)
   const __amdgpu_buffer_rsrc_t rsa =
-      make_rsrc(p.sa, FMT == FMT_MX ? MT16 * G * 64u : (FMT == FMT_BLOCK ? M * G : M) * 4u);
+      make_rsrc(p.sa, MXS ? MT16 * G * 64u : (FMT == FMT_BLOCK ? M * G : M) * 4u);
   const __amdgpu_buffer_rsrc_t rsw =
-      make_rsrc(p.sw, FMT == FMT_MX ? NT16 * G * 64u : (FMT == FMT_BLOCK ? ((N + 127u) / 128u) * G : N) * 4u);
+      make_rsrc(p.sw, MXS ? NT16 * G * 64u : (FMT == FMT_BLOCK ? ((N + 127u) / 128u) * G : N) * 4u);
 
   // ---- global -> registers for one K block (zeros outside the matrices)
   // a ring of PF register slots: K block b of the chunk lives in slot b % PF
@@ -141,8 +146,9 @@ __global__ void __launch_bounds__((64 * 2 * tiled_waves_n<FMT, BM, BN>())) qgemm
     for (int i = 0; i < PB; ++i) {
       const uint32_t q = (uint32_t)(i * NT + tid);
       if constexpr (WP) {
-        const uint32_t t = n0 / 16u + (q >> 7);
-        pb[sl][i] = bload16(rw, (in && t < NT16) ? (t * G + (uint32_t)kb) * 2048u + (q & 127u) * 16u : OOB);
+        constexpr uint32_t QT = (uint32_t)WT / 16u;   // 16-byte pieces of a tile
+        const uint32_t t = n0 / 16u + q / QT;
+        pb[sl][i] = bload16(rw, (in && t < NT16) ? (t * G + (uint32_t)kb) * (uint32_t)WT + (q % QT) * 16u : OOB);
       } else {
         const uint32_t n = n0 + (q >> 3), k = kofs + (q & 7u) * 16u;
         pb[sl][i] = bload16(rw, (in && n < N && k < K) ? n * K + k : OOB);
@@ -182,8 +188,8 @@ __global__ void __launch_bounds__((64 * 2 * tiled_waves_n<FMT, BM, BN>())) qgemm
   // (non-swapped: 4 token rows per 16x16 tile; swapped: 1 token per tile);
   // MXFP8: the E8M0 byte this lane hands the matrix core with each A and B
   // fragment (kept as raw bits in the float slots)
-  constexpr int SA_N = FMT == FMT_BLOCK ? (SWAP ? IM : IM * 4) : FMT == FMT_MX ? IM : 1;
-  constexpr int SW_N = (FMT == FMT_BLOCK || FMT == FMT_MX) ? IN : 1;
+  constexpr int SA_N = FMT == FMT_BLOCK ? (SWAP ? IM : IM * 4) : MXS ? IM : 1;
+  constexpr int SW_N = (FMT == FMT_BLOCK || MXS) ? IN : 1;
   float sa_nx[PF][SA_N], sw_nx[PF][SW_N];
   auto load_scales = [&](int kb, int sl) {
     if constexpr (FMT == FMT_BLOCK) {
@@ -200,7 +206,7 @@ __global__ void __launch_bounds__((64 * 2 * tiled_waves_n<FMT, BM, BN>())) qgemm
         const uint32_t nb = n0 + (uint32_t)(wx * TN + 16 * j);
         sw_nx[sl][j] = bload_f32(rsw, (kb < kb1 && nb < N) ? ((nb >> 7) * G + (uint32_t)kb) * 4u : OOB);
       }
-    } else if constexpr (FMT == FMT_MX) {
+    } else if constexpr (MXS) {
 #pragma unroll
       for (int i = 0; i < IM; ++i) {
         const uint32_t t = m0 / 16u + (uint32_t)(wy * IM + i);
@@ -240,6 +246,9 @@ __global__ void __launch_bounds__((64 * 2 * tiled_waves_n<FMT, BM, BN>())) qgemm
     } else if constexpr (FMT == FMT_MX) {
       const int xa = __float_as_int(sa_c[i]), xw = __float_as_int(sw_c[j]);
       acc[i][j] = SWAP ? mma_f8_mx(b, a, acc[i][j], xw, xa) : mma_f8_mx(a, b, acc[i][j], xa, xw);
+    } else if constexpr (FMT == FMT_MX4) {
+      const int xa = __float_as_int(sa_c[i]), xw = __float_as_int(sw_c[j]);
+      acc[i][j] = mma_f8f4_mx<SWAP>(a, b.lo, acc[i][j], xa, xw);
     } else {
       const f32x4 z = {0.f, 0.f, 0.f, 0.f};
       const f32x4 part = SWAP ? mma_f8(b, a, z) : mma_f8(a, b, z);
@@ -256,14 +265,21 @@ __global__ void __launch_bounds__((64 * 2 * tiled_waves_n<FMT, BM, BN>())) qgemm
   // column) of matrix-core instructions, so LDS reads overlap the math.
   auto compute = [&](int buf, const float (&sa_c)[SA_N], const float (&sw_c)[SW_N]) {
     const uint8_t* as = smem + buf * STAGE + (wy * IM) * 2048 + lane * 16;
-    const uint8_t* bs = smem + buf * STAGE + BM * 128 + (wx * IN) * 2048 + lane * 16;
+    const uint8_t* bs = smem + buf * STAGE + BM * 128 + (wx * IN) * WT + lane * 16;
+    // a B fragment: the two 16-byte pieces of a 2 KB tile, or MXFP4's one of a 1 KB tile
+    auto bfrag = [&](int j) -> Frag {
+      Frag f;
+      f.lo = *reinterpret_cast<const u32x4*>(bs + j * WT);
+      if constexpr (FMT == FMT_MX4)
+        f.hi = u32x4{0u, 0u, 0u, 0u};
+      else
+        f.hi = *reinterpret_cast<const u32x4*>(bs + j * WT + 1024);
+      return f;
+    };
     if constexpr (IM > IN) {
       Frag bf[IN];
 #pragma unroll
-      for (int j = 0; j < IN; ++j) {
-        bf[j].lo = *reinterpret_cast<const u32x4*>(bs + j * 2048);
-        bf[j].hi = *reinterpret_cast<const u32x4*>(bs + j * 2048 + 1024);
-      }
+      for (int j = 0; j < IN; ++j) bf[j] = bfrag(j);
 #pragma unroll
       for (int i = 0; i < IM; ++i) {
         Frag af;
@@ -281,9 +297,7 @@ __global__ void __launch_bounds__((64 * 2 * tiled_waves_n<FMT, BM, BN>())) qgemm
       }
 #pragma unroll
       for (int j = 0; j < IN; ++j) {
-        Frag bf;
-        bf.lo = *reinterpret_cast<const u32x4*>(bs + j * 2048);
-        bf.hi = *reinterpret_cast<const u32x4*>(bs + j * 2048 + 1024);
+        const Frag bf = bfrag(j);
 #pragma unroll
         for (int i = 0; i < IM; ++i) mma_tile(af[i], bf, i, j, sa_c, sw_c);
       }
@@ -450,7 +464,7 @@ __global__ void __launch_bounds__((64 * 2 * tiled_waves_n<FMT, BM, BN>())) qgemm
   // s_w per output column this lane holds: IM x (1 or 4) and IN x (4 or 1)
   // values, loaded once (not per element, which would keep hundreds of
   // loads in flight next to the accumulators).
-  constexpr bool SCALED_IN_K = FMT == FMT_BLOCK || FMT == FMT_MX;   // no scale epilogue
+  constexpr bool SCALED_IN_K = FMT == FMT_BLOCK || MXS;   // no scale epilogue
   constexpr int EA = SCALED_IN_K ? 1 : (SWAP ? 1 : 4), EW = SCALED_IN_K ? 1 : (SWAP ? 4 : 1);
   float ea[IM][EA], ew[IN][EW];
   if constexpr (!SCALED_IN_K) {
@@ -528,12 +542,13 @@ __global__ void __launch_bounds__((64 * 2 * tiled_waves_n<FMT, BM, BN>())) qgemm
 template <int FMT, int SW, int BM, int BN, int PF, int NS>
 constexpr bool tiled_config_fits() {
   // the LDS-DMA ring has no per-block scale path: Block_FP8 and MXFP8 use the register ring
-  if (BM * BN == 256 * 256) return NS == 2 && FMT != FMT_BLOCK && FMT != FMT_MX;
-  if (NS > 0) return FMT != FMT_BLOCK && FMT != FMT_MX && NS * (BM + BN) * 128 <= 160 * 1024 && BM * BN <= 128 * 256;
+  constexpr bool MXS = FMT == FMT_MX || FMT == FMT_MX4;
+  if (BM * BN == 256 * 256) return NS == 2 && FMT != FMT_BLOCK && !MXS;
+  if (NS > 0) return FMT != FMT_BLOCK && !MXS && NS * (BM + BN) * 128 <= 160 * 1024 && BM * BN <= 128 * 256;
   if (FMT == FMT_BLOCK && !SW && BM * BN > 128 * 128) return false;
   // MXFP8's scale bytes ride in the ring too: a two-block ring on the largest
   // register-ring tiles spills (checked against the compiler's resource report)
-  if (FMT == FMT_MX && BM * BN >= 128 * 256 && PF > 1) return false;
+  if (MXS && BM * BN >= 128 * 256 && PF > 1) return false;
   if (PF * (BM + BN) > 768) return false;  // ring of PF K blocks: at most 96 VGPRs a lane
   if (FMT == FMT_BLOCK && BM * BN > 128 * 128 && PF > 1) return false;
   return BM * BN <= 128 * 256;
@@ -542,7 +557,8 @@ constexpr bool tiled_config_fits() {
 template <int FMT, int SW, int BM, int BN, int WM_, int PF, int AP, int NS>
 hipError_t tiled_try(const TiledKey& k, dim3 grid, size_t lds, hipStream_t s, const DecodeArgs& a, bool probe_only,
                      bool* hit) {
-  if constexpr (tiled_config_fits<FMT, SW, BM, BN, PF, NS>()) {
+  // MXFP4: packed E2M1 weights and packed activations only
+  if constexpr (tiled_config_fits<FMT, SW, BM, BN, PF, NS>() && (FMT != FMT_MX4 || (WM_ == W_PACKED && AP == 1))) {
     if (k.swap == SW && k.bm == BM && k.bn == BN && k.wm == WM_ && k.pf == PF && k.ap == AP && k.ns == NS) {
       *hit = true;
       auto fn = qgemm_tiled_kernel<FMT, SW != 0, BM, BN, WM_, PF, AP != 0, NS>;

@@ -386,3 +386,57 @@ def test_mx_planner_large_m_plans(M):
     r = mx.mx_reference(bf16_bits(x[torch.from_numpy(rows)]), bf16_bits(w[torch.from_numpy(cols)]))
     st = _mx_check(r, host_bf16_bits(y)[np.ix_(rows, cols)], plan.facts["chunks"], 1)
     assert st["ok"] and st["frac_within_ulp"] >= MIN_FRAC_WITHIN_ULP, (plan.config, st)
+
+
+# ---------------------------------------------------------------- MXFP4 beyond the decode range
+
+def _mx4_tiled_args(vi):
+    swap, (bm, bn), pf, split = TILED_MX[vi]
+    M = [40, 100, 200, 257][(vi + 1) % 4]
+    K = [1024, 1152][(vi + 1) % 2]
+    N = 300 + 16 * (vi % 5)                        # several tiles + a ragged tail
+    cfg = dict(algo=ql.ALGO_TILED, swap_ab=swap, split_k=split, tile_m=bm, tile_n=bn, prefetch=pf, w_lds=0,
+               a_mode=2, w_layout=1)
+    return ql.MXFP4, M, N, K, cfg
+
+
+MX4_TILED_CASES = cases("mxfp4_tiled", [(vi,) for vi in range(len(TILED_MX))], _mx4_tiled_args)
+
+
+@pytest.mark.parametrize("vi", [c[0] for c in MX4_TILED_CASES])
+def test_every_mx4_tiled_instantiation_matches_oracle(vi):
+    """E2M1 weights through the tiled kernel (1 KB weight tiles in the LDS
+    stage), every instantiated tile, ring depth, Swap-AB and split-K."""
+    _, M, N, K, cfg = _mx4_tiled_args(vi)
+    plan = ql.qlinear_plan_with_config(ql.MXFP4, M, N, K, cfg)
+    x, w = make_inputs(K, N, M, 0.02, seed=12000 + vi)
+    r = mx.mx4_reference(bf16_bits(x), bf16_bits(w))
+    w_p, w_s = _weights4(r)
+    a_p, a_s = _acts(r)
+    y, ws = _run(plan, a_p, a_s, w_p, w_s)
+    st = _mx4_check(r, y, plan.facts["chunks"], 1)
+    assert st["ok"] and st["frac_within_ulp"] >= MIN_FRAC_WITHIN_ULP, (cfg, st)
+    if ws is not None:
+        assert int(torch.count_nonzero(ws)) == 0, "split-K workspace not left all-zero"
+
+
+@pytest.mark.parametrize("M", [65, 256, 1024])
+def test_mx4_planner_large_m_plans(M):
+    """Beyond 64 tokens the planner sends MXFP4 to the tiled kernel; the 14B
+    QKV shape through the forward (MXFP8 quantizer + GEMM), 64 sampled
+    columns and up to 128 sampled rows."""
+    N, K = 7168, 5120
+    x, w = make_inputs(K, N, M, 0.02, seed=M + 5)
+    plan = ql.qlinear_plan_layouts(ql.MXFP4, M, N, K, 1, 1)
+    assert plan.config["algo"] == ql.ALGO_TILED
+    w_q, w_s = ql.quantize_weight(ql.MXFP4, w.cuda())
+    y = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
+    ql.qlinear_forward(plan, x.cuda(), ql.act_buffer(plan), ql.act_scale_buffer(plan), ql.pack_weight_fp4(w_q),
+                       ql.pack_mx_scales(w_s), y, plan.new_workspace())
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(M)
+    cols = np.sort(rng.choice(N, 64, replace=False))
+    rows = np.sort(rng.choice(M, min(M, 128), replace=False))
+    r = mx.mx4_reference(bf16_bits(x[torch.from_numpy(rows)]), bf16_bits(w[torch.from_numpy(cols)]))
+    st = _mx4_check(r, host_bf16_bits(y)[np.ix_(rows, cols)], plan.facts["chunks"], 1)
+    assert st["ok"] and st["frac_within_ulp"] >= MIN_FRAC_WITHIN_ULP, (plan.config, st)

@@ -47,6 +47,12 @@ CONFIGS = (
     Workload("fp8_dynamic_14b_large_m", FP8_DYNAMIC,
              (("qkv", 7168, 5120), ("gate_up", 34816, 5120), ("down", 5120, 17408)),
              (64, 256, 1024, 4096)),
+    Workload("mxfp8_14b_large_m", MXFP8,
+             (("qkv", 7168, 5120), ("gate_up", 34816, 5120), ("down", 5120, 17408)),
+             (64, 256, 1024, 4096), notes="MXFP8 beyond the decode range (tiled kernel from M = 65)"),
+    Workload("mxfp4_14b_large_m", MXFP4,
+             (("qkv", 7168, 5120), ("gate_up", 34816, 5120), ("down", 5120, 17408)),
+             (64, 256, 1024, 4096), notes="MXFP4 weights beyond the decode range (tiled kernel from M = 65)"),
 )
 
 
