@@ -323,7 +323,21 @@ def environment(ql, torch):
     if os.path.exists(table):
         env["table_sha256_16"] = hashlib.sha256(open(table, "rb").read()).hexdigest()[:16]
     env["kernel_sources_sha256_16"] = kernel_sources_digest()[:16]
+    env["clocks"] = current_clocks()
     return env
+
+
+def current_clocks():
+    """The GPU's current clock levels as rocm-smi reports them (read-only;
+    None where the tool is missing or refuses)."""
+    import subprocess
+    try:
+        r = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True, text=True, timeout=20)
+        data = json.loads(r.stdout[r.stdout.index("{"):]) if "{" in r.stdout else {}
+    except (OSError, ValueError, subprocess.SubprocessError):
+        return None
+    card = next(iter(data.values()), {}) if isinstance(data, dict) else {}
+    return {k.strip(" :"): v for k, v in card.items() if isinstance(v, str) and "clk" in k.lower()} or None
 
 
 def prepare_workload(ql, torch, wl, layout, dev):
