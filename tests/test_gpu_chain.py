@@ -156,3 +156,56 @@ def test_mode5_plan_refuses_plain_forward():
                                        device="cuda").view(torch.float8_e4m3fn),
                            torch.ones(256, device="cuda"), torch.empty(4, 256, dtype=torch.bfloat16, device="cuda"))
     assert e.value.status == 1
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("M", [2, 24])
+def test_chain_graph_replays(fmt, M):
+    """gate_up (amax fold) -> down (mode 5 at M <= 16, else the quantizer and
+    a GEMM that clears the buffer) captured once and replayed four times with
+    unrelated eager work between: every replay gives the eager outputs, and
+    leaves the amax buffer zero for the next."""
+    I, K, N2 = 640, 1024, 384
+    x, w_gu = make_inputs(K, 2 * I, M, 0.02, seed=M + 100 * fmt)
+    _, wd_p, wd_s = _weights(fmt, N2, I, seed=M + 9)
+    wg_q, wg_s = ql.quantize_weight(fmt, w_gu.cuda())
+    wg_p = ql.pack_weight(wg_q)
+    glu = ql.qlinear_plan_glu(fmt, M, 2 * I, K, 2)
+    down = ql.qlinear_plan_layouts(fmt, M, N2, I, 1, 3)
+    xd = x.cuda()
+    h = torch.empty(M, I, dtype=torch.bfloat16, device="cuda")
+    y = torch.empty(M, N2, dtype=torch.bfloat16, device="cuda")
+    amax = ql.amax_buffer(M)
+    bufs = dict(ga=ql.act_buffer(glu), gs=torch.empty(M, dtype=torch.float32, device="cuda"), gw=glu.new_workspace(),
+                da=ql.act_buffer(down), ds=torch.empty(M, dtype=torch.float32, device="cuda"), dw=down.new_workspace())
+
+    def chain(stream=None):
+        ql.qlinear_forward_glu_amax(glu, xd, bufs["ga"], bufs["gs"], wg_p, wg_s, h, amax, bufs["gw"], stream=stream)
+        ql.qlinear_forward_amax(down, h, amax, bufs["da"], bufs["ds"], wd_p, wd_s, y, bufs["dw"], stream=stream)
+
+    chain()
+    torch.cuda.synchronize()
+    h_eager, y_eager = h.clone(), y.clone()
+    assert int(torch.count_nonzero(amax)) == 0
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        ql.qlinear_graph_begin(s)
+        chain(stream=s)
+        g = ql.qlinear_graph_end(s)
+    for i in range(4):
+        h.fill_(0)
+        y.fill_(0)
+        torch.cuda.synchronize()
+        g.launch(s)
+        s.synchronize()
+        if fmt == ql.W8A8_INT8:
+            assert torch.equal(h, h_eager) and torch.equal(y, y_eager), i
+        else:
+            # the same plans on the same inputs: only a split-K summation order can differ
+            # (fp32 atomics), and with it a last bit of H, a code of down's input, a bit of Y
+            if glu.facts["chunks"] == 1:
+                assert torch.equal(h, h_eager), i
+            ref = y_eager.float().abs().max()
+            assert float((y.float() - y_eager.float()).abs().max()) <= 2 ** -6 * float(ref), i
+        assert int(torch.count_nonzero(amax)) == 0, i
+        _ = torch.randn(1000, device="cuda").sum()      # unrelated eager work between replays
