@@ -406,6 +406,32 @@ __global__ void __launch_bounds__(NW * 64) qgemm_decode_kernel(DecodeArgs p) {
     }
   };
 
+  // ---- scales of the per-token formats for the epilogue, issued before any
+  // other load: they depend on nothing, so their latency passes while the
+  // first weight batches are on their way, also where a wave has only a few
+  // K blocks to stream (measured 2-4 % faster on such points than issuing
+  // them after the first batches).  Issued first, they are older than every
+  // load the explicit waits below count.  Fused plans load them after their
+  // prologue (below).
+  float esa[MT][4], esw[RG][4];
+  if constexpr (FMT != FMT_BLOCK && !MXS && !FUSED) {
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const uint32_t m = SWAP ? (uint32_t)(mt * 16 + r16) : (uint32_t)(mt * 16 + 4 * g + r);
+        esa[mt][r] = (SWAP && r > 0) ? 0.f : bload_f32(rsa, m < M ? m * 4u : OOB);
+      }
+#pragma unroll
+    for (int rg = 0; rg < RG; ++rg)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const uint32_t n = (uint32_t)grow(rg) + (SWAP ? (uint32_t)(4 * g + r) : (uint32_t)r16);
+        esw[rg][r] = (!SWAP && r > 0) ? 0.f : bload_f32(rsw, n < N ? n * 4u : OOB);
+      }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+
   // ---- stage this chunk's activations in LDS first, with LDS-DMA buffer
   // loads (no registers; their completion is awaited below, after the first
   // weight batches are in flight): one 1 KB block b per (K block kbl, token
@@ -638,19 +664,16 @@ __global__ void __launch_bounds__(NW * 64) qgemm_decode_kernel(DecodeArgs p) {
     }
   }
 
-  // Scales of the per-token formats, loaded now so that their latency hides
-  // under the weight stream instead of stalling the epilogue.
-  float esa[MT][4], esw[RG][4];
-  if constexpr (FMT != FMT_BLOCK && !MXS) {
+  // Fused plans: the token scales the prologue computed and the weight
+  // scales, for the epilogue.  (Issued before X instead, the weight-scale
+  // loads made the fused launches up to 16 % slower.)
+  if constexpr (FMT != FMT_BLOCK && !MXS && FUSED) {
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const uint32_t m = SWAP ? (uint32_t)(mt * 16 + r16) : (uint32_t)(mt * 16 + 4 * g + r);
-        if constexpr (FUSED)
-          esa[mt][r] = m < M ? reinterpret_cast<const float*>(smem + FA_SC)[m] : 0.f;
-        else
-          esa[mt][r] = (SWAP && r > 0) ? 0.f : bload_f32(rsa, m < M ? m * 4u : OOB);
+        esa[mt][r] = m < M ? reinterpret_cast<const float*>(smem + FA_SC)[m] : 0.f;
       }
 #pragma unroll
     for (int rg = 0; rg < RG; ++rg)
