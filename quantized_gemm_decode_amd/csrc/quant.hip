@@ -48,16 +48,22 @@ __device__ __forceinline__ size_t packed_offset(uint32_t row, uint32_t k, uint32
          ((row & 15u) + 16u * ((kk >> 4) & 3u)) * 16u + (kk & 15u);
 }
 
-// One row per workgroup; the row stays in registers (VPT 16-byte vectors per
-// thread) between the amax pass and the quantize pass.  PACKED writes the
-// packed activation layout instead of row-major codes: the grid then also
-// covers the padding rows up to a multiple of 16 and the padding K up to a
-// multiple of 128, which get zero codes (and no scale).
-template <int FMT, int VPT, bool PACKED, int NT>
+// PARTS workgroups per row; the row stays in registers (VPT 16-byte vectors
+// per thread) between the amax pass and the quantize pass.  Each of a row's
+// workgroups reads the whole row and reduces its amax (a few operations per
+// value), then quantizes only its own 1/PARTS of the row (some ninety
+// operations per 8 values): on a long row that arithmetic, not the loads,
+// bounds the launch, and one compute unit per row left most of the chip
+// idle.  PACKED writes the packed activation layout instead of row-major
+// codes: the grid then also covers the padding rows up to a multiple of 16
+// and the padding K up to a multiple of 128, which get zero codes (and no
+// scale).
+template <int FMT, int VPT, bool PACKED, int NT, int PARTS = 1>
 __global__ void __launch_bounds__(NT) quant_rows_reg_kernel(const uint16_t* __restrict__ x, uint32_t R, uint32_t C,
                                                             uint8_t* __restrict__ q, float* __restrict__ s) {
   __shared__ float red[NT / 64];
-  const uint32_t row = blockIdx.x;
+  const uint32_t row = blockIdx.x / PARTS;
+  const uint32_t part = blockIdx.x - row * PARTS;
   const bool real = row < R;
   const uint16_t* xr = x + (size_t)row * C;
   const uint32_t G = (C + 127u) / 128u;
@@ -73,15 +79,19 @@ __global__ void __launch_bounds__(NT) quant_rows_reg_kernel(const uint16_t* __re
   amax = block_max<NT>(amax, red);
   const float sc = scale_of<FMT>(amax);
   const float rc = recip_of(sc);
+  // this workgroup's vectors of the row: [v_lo, v_hi) of the CW/8 written
+  const uint32_t nv = CW / 8u;
+  const uint32_t v_lo = PARTS == 1 ? 0u : nv * part / PARTS, v_hi = PARTS == 1 ? nv : nv * (part + 1u) / PARTS;
 #pragma unroll
   for (int i = 0; i < VPT; ++i) {
-    const uint32_t e = (uint32_t)(i * NT + threadIdx.x) * 8u;
-    if (e < CW) {
+    const uint32_t vi = (uint32_t)(i * NT) + threadIdx.x;
+    if (vi >= v_lo && vi < v_hi) {
+      const uint32_t e = vi * 8u;
       const size_t off = PACKED ? packed_offset(row, e, G) : (size_t)row * C + e;
       *reinterpret_cast<u32x2*>(q + off) = quant8<FMT>(v[i], sc, rc);
     }
   }
-  if (threadIdx.x == 0 && real) s[row] = sc;
+  if (threadIdx.x == 0 && real && part == 0) s[row] = sc;
 }
 
 // Rows too long for registers: two streaming passes (the second re-reads from cache).
@@ -198,14 +208,30 @@ static hipError_t rows_dispatch_nt(const void* x, int64_t R, int64_t C, void* q,
   uint8_t* qp = static_cast<uint8_t*>(q);
   const int64_t vecs = (C + 7) / 8;
   const int64_t vpt = (vecs + NT - 1) / NT;
-  const dim3 grid((unsigned)(PACKED ? (R + 15) / 16 * 16 : R)), block(NT);
+  const int64_t rows = PACKED ? (R + 15) / 16 * 16 : R;
+  const dim3 grid((unsigned)rows), block(NT);
   const uint32_t r = (uint32_t)R, c = (uint32_t)C;
-  if (vpt <= 1)
+  // the few rows of decode activations (at most 64): a row's quantization
+  // split over 2 workgroups for 1024 < C <= 2048 values, 4 up to 16384, 8 up
+  // to 32768, 16 up to 65536 (measured: each doubling of the parts up to
+  // these shortened the launch; the amax pass every part repeats is cheap)
+  const bool split = NT == 1024 && R <= 64;
+  if (vpt <= 1 && split && vecs > 256)
+    quant_rows_reg_kernel<FMT, 1, PACKED, NT, 4><<<dim3((unsigned)(rows * 4)), block, 0, st>>>(xp, r, c, qp, s);
+  else if (vpt <= 1 && split && vecs > 128)
+    quant_rows_reg_kernel<FMT, 1, PACKED, NT, 2><<<dim3((unsigned)(rows * 2)), block, 0, st>>>(xp, r, c, qp, s);
+  else if (vpt <= 1)
     quant_rows_reg_kernel<FMT, 1, PACKED, NT><<<grid, block, 0, st>>>(xp, r, c, qp, s);
+  else if (vpt <= 2 && split)
+    quant_rows_reg_kernel<FMT, 2, PACKED, NT, 4><<<dim3((unsigned)(rows * 4)), block, 0, st>>>(xp, r, c, qp, s);
   else if (vpt <= 2)
     quant_rows_reg_kernel<FMT, 2, PACKED, NT><<<grid, block, 0, st>>>(xp, r, c, qp, s);
+  else if (vpt <= 4 && split)
+    quant_rows_reg_kernel<FMT, 4, PACKED, NT, 8><<<dim3((unsigned)(rows * 8)), block, 0, st>>>(xp, r, c, qp, s);
   else if (vpt <= 4)
     quant_rows_reg_kernel<FMT, 4, PACKED, NT><<<grid, block, 0, st>>>(xp, r, c, qp, s);
+  else if (vpt <= 8 && split)
+    quant_rows_reg_kernel<FMT, 8, PACKED, NT, 16><<<dim3((unsigned)(rows * 16)), block, 0, st>>>(xp, r, c, qp, s);
   else if (vpt <= 8)
     quant_rows_reg_kernel<FMT, 8, PACKED, NT><<<grid, block, 0, st>>>(xp, r, c, qp, s);
   else if constexpr (NT == QT) {
