@@ -483,7 +483,7 @@ def quantize_into(ql, fmt, p, stream):
         ql.qlinear_quantize_act(fmt, p["x"], p["a_q"], p["a_s"], stream=stream)
 
 
-def hbm_roofline(per_point, traffic, traffic_note, ceil_gbs):
+def hbm_roofline(per_point, traffic, traffic_note, ceil_gbs, cu_gbs=None):
     tot_b = sum(q["kernel_bytes"] for q in per_point)
     tot_us = sum(q["us"] for q in per_point)
     achieved = tot_b / (tot_us * 1e-6) / 1e9
@@ -500,7 +500,19 @@ def hbm_roofline(per_point, traffic, traffic_note, ceil_gbs):
                                "note": "a plain streaming read of each point's kernel bytes (qlinear_stream_read, "
                                        "best of 5 grids x 2 load depths), timed like the GEMMs; per point under "
                                        "ceiling_us"}
+    if cu_gbs is not None:
+        r["cu_ceiling"] = cu_ceiling_block(per_point, achieved, cu_gbs)
     return r
+
+
+def cu_ceiling_block(per_point, achieved, cu_gbs):
+    return {"achieved": round(cu_gbs, 1), "frac": round(cu_gbs / HBM_PEAK_GBS, 4),
+            "kernel_vs_ceiling": round(achieved / cu_gbs, 4),
+            "note": "one workgroup per compute unit reading its share of the weights from HBM and, "
+                    "interleaved, every token's activations (bf16 X for a fused-quantization point) -- the "
+                    "bytes each compute unit of an unsplit weight-streaming GEMM must load "
+                    "(qlinear_stream_read_bcast, best of 2 thread counts x 2 load depths), timed like the "
+                    "GEMMs; the point's algorithmic bytes over that time; per point under cu_ceiling_us"}
 
 
 def main(argv=None):
@@ -584,7 +596,8 @@ def main(argv=None):
         notes.add(traffic_note)
         if max(wl.ms) <= 32:
             ceil_gbs = None if args.no_ceiling else stream_ceiling(ql, pp, stream, max(10, args.kernel_reps // 3))
-            roofline = hbm_roofline(pp, traffic, traffic_note, ceil_gbs)
+            cu_gbs = None if args.no_ceiling else cu_ceiling(ql, pp, stream, max(10, args.kernel_reps // 3))
+            roofline = hbm_roofline(pp, traffic, traffic_note, ceil_gbs, cu_gbs)
         else:
             # token counts in the hundreds and thousands: the tiled kernel is matrix-core bound
             big = [q for q in pp if q["M"] >= 1024]
@@ -621,6 +634,8 @@ def main(argv=None):
             ceil_gbs = ceil_b / (ceil_us * 1e-6) / 1e9
             roofline["stream_ceiling"] = {"achieved": round(ceil_gbs, 1), "frac": round(ceil_gbs / HBM_PEAK_GBS, 4),
                                           "kernel_vs_ceiling": round(roofline["achieved"] / ceil_gbs, 4)}
+            cu_us = sum(q["cu_ceiling_us"] for q in all_pp)
+            roofline["cu_ceiling"] = cu_ceiling_block(all_pp, roofline["achieved"], ceil_b / (cu_us * 1e-6) / 1e9)
     else:
         roofline = blocks[0]["roofline"]
     cpu = None
@@ -713,6 +728,49 @@ def stream_ceiling(ql, per_point, stream, reps):
     del pool
     tot_b = sum(q["kernel_bytes"] for q in per_point)
     tot_us = sum(best[q["kernel_bytes"] // 16 * 16] for q in per_point)
+    return tot_b / (tot_us * 1e-6) / 1e9
+
+
+def cu_ceiling(ql, per_point, stream, reps):
+    """The per-compute-unit ceiling of every point: 256 workgroups (one per
+    compute unit) each reading its share of the N x K weight codes from HBM and,
+    interleaved, the whole activation block (M x K codes, or M x K bf16 X for a
+    fused-quantization point) -- what each compute unit of a weight-streaming
+    GEMM without a K split must load (qlinear_stream_read_bcast, best of 2
+    thread counts x 2 load depths).  Timed as the GEMM is: HIP events around
+    graph replays of R back-to-back launches on distinct weight offsets of a
+    1 GiB buffer, one activation block shared by all of them.  Sets
+    per_point[i]["cu_ceiling_us"]; returns the points' algorithmic bytes over
+    the sum of these times (GB/s)."""
+    import numpy as np
+    import torch
+    pool = torch.ones(1 << 30, dtype=torch.uint8, device="cuda")
+    sink = torch.empty(256, dtype=torch.int32, device="cuda")
+    best = {}
+    for q in per_point:
+        wb = q["N"] * q["K"] // 16 * 16
+        ab = (2 if q["fused_quant"] else 1) * q["M"] * q["K"] // 16 * 16
+        key = (wb, ab)
+        if key not in best:
+            act = torch.ones(max(ab, 16), dtype=torch.uint8, device="cuda")
+            span = -(-wb // 4096) * 4096
+            R = max(2, min(64, (1 << 30) // span))
+            times = []
+            for thr, lif in itertools.product((512, 1024), (2, 4)):
+                with torch.cuda.stream(stream):
+                    ql.qlinear_graph_begin(stream)
+                    for c in range(R):
+                        ql.qlinear_stream_read_bcast(pool[c * span:], wb, act, ab, sink, workgroups=256,
+                                                     threads=thr, loads_in_flight=lif, stream=stream)
+                    g = ql.qlinear_graph_end(stream)
+                times.append(_graph_median_us(torch, np, stream, g, R, reps))
+                del g
+            best[key] = min(times)
+            del act
+        q["cu_ceiling_us"] = round(best[key], 3)
+    del pool
+    tot_b = sum(q["kernel_bytes"] for q in per_point)
+    tot_us = sum(q["cu_ceiling_us"] for q in per_point)
     return tot_b / (tot_us * 1e-6) / 1e9
 
 

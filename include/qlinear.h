@@ -240,6 +240,26 @@ ql_status qlinear_stream_read(const void* src, int64_t bytes, int32_t workgroups
                               int32_t check, void* sink, void* stream);
 
 /*
+ * Measurement aid for the same purpose, one level finer: the ceiling of a
+ * weight-streaming decomposition without a K split, in which every
+ * workgroup owns a share of the weight rows over all of K and therefore
+ * multiplies them with every token's activations.  Workgroup w (of
+ * `workgroups`, 0 = 256, i.e. one per compute unit; `threads` 256, 512 or
+ * 1024, 0 = 1024) reads the w-th contiguous slice of src, as
+ * qlinear_stream_read does, and, interleaved with it, all bcast_bytes of
+ * bcast -- the activation block every such workgroup must load (from L2
+ * once one workgroup has brought it in).  `loads_in_flight` (2 or 4; 0 = 4)
+ * pieces of each stream per lane.  `check` as for qlinear_stream_read: then
+ * sink[w] = wrapping 32-bit sum of the words of slice w plus those of
+ * bcast.  bytes % 16 == 0 and bytes <= 2^36; bcast_bytes % 16 == 0 and
+ * bcast_bytes <= 2^30; device pointers, 16-byte aligned (bcast may be NULL
+ * when bcast_bytes is 0); sink holds 4 * workgroups bytes.  Enqueue-only.
+ */
+ql_status qlinear_stream_read_bcast(const void* src, int64_t bytes, const void* bcast, int64_t bcast_bytes,
+                                    int32_t workgroups, int32_t threads, int32_t loads_in_flight, int32_t check,
+                                    void* sink, void* stream);
+
+/*
  * Offline weight quantizer: per output channel (rows of W) or per 128x128
  * block for Block_FP8 (the last block row may be ragged).
  *   w_bf16 [N, K] in;  w_q [N, K] out;  w_scale fp32 [N] or [ceil(N/128), K/128]

@@ -213,6 +213,22 @@ def qlinear_stream_read(src, nbytes, workgroups, sink, loads_in_flight=8, check=
                                      int(bool(check)), _ptr(sink, "sink"), _stream(stream)), "qlinear_stream_read")
 
 
+def qlinear_stream_read_bcast(src, nbytes, bcast, bcast_bytes, sink, workgroups=256, threads=1024,
+                              loads_in_flight=4, check=False, stream=None):
+    """Measurement aid: every workgroup reads its slice of nbytes of src and all
+    bcast_bytes of bcast (the bytes each compute unit of an unsplit
+    weight-streaming GEMM loads); with check, sink gets one wrapping 32-bit
+    word sum per workgroup."""
+    _need(src, "src", nbytes)
+    if bcast_bytes:
+        _need(bcast, "bcast", bcast_bytes)
+    _need(sink, "sink", 4 * (workgroups or 256))
+    _check(lib().qlinear_stream_read_bcast(_ptr(src, "src"), int(nbytes),
+                                           _ptr(bcast, "bcast") if bcast_bytes else None, int(bcast_bytes),
+                                           int(workgroups), int(threads), int(loads_in_flight), int(bool(check)),
+                                           _ptr(sink, "sink"), _stream(stream)), "qlinear_stream_read_bcast")
+
+
 def qlinear_packed_weight_bytes(N, K):
     return int(lib().qlinear_packed_weight_bytes(N, K))
 

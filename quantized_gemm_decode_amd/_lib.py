@@ -31,6 +31,7 @@ SIGNATURES = {
     "qlinear_packed_weight_bytes": (c_i64, [c_i64, c_i64]),
     "qlinear_encode_e4m3": (c_i32, [c_vp, c_i64, c_vp, c_vp]),
     "qlinear_stream_read": (c_i32, [c_vp, c_i64, c_i32, c_i32, c_i32, c_vp, c_vp]),
+    "qlinear_stream_read_bcast": (c_i32, [c_vp, c_i64, c_vp, c_i64, c_i32, c_i32, c_i32, c_i32, c_vp, c_vp]),
     "qlinear_pack_weight": (c_i32, [c_vp, c_i64, c_i64, c_vp, c_vp]),
     "qlinear_packed_mx_scale_bytes": (c_i64, [c_i64, c_i64]),
     "qlinear_packed_weight_bytes_fp4": (c_i64, [c_i64, c_i64]),

@@ -892,6 +892,30 @@ ql_status qlinear_stream_read(const void* src, int64_t bytes, int32_t workgroups
   return e == hipSuccess ? QL_OK : hip_fail(e, "stream read launch");
 }
 
+ql_status qlinear_stream_read_bcast(const void* src, int64_t bytes, const void* bcast, int64_t bcast_bytes,
+                                    int32_t workgroups, int32_t threads, int32_t loads_in_flight, int32_t check,
+                                    void* sink, void* stream) {
+  if (bytes < 0 || bytes % 16 || bytes > (int64_t(1) << 36))
+    return fail(QL_E_INVALID, "bytes=%lld must be a multiple of 16 in [0, 2^36]", (long long)bytes);
+  if (bcast_bytes < 0 || bcast_bytes % 16 || bcast_bytes > (int64_t(1) << 30))
+    return fail(QL_E_INVALID, "bcast_bytes=%lld must be a multiple of 16 in [0, 2^30]", (long long)bcast_bytes);
+  if (workgroups == 0) workgroups = 256;
+  if (workgroups < 1 || workgroups > 65536) return fail(QL_E_INVALID, "workgroups=%d outside [1, 65536]", workgroups);
+  if (threads == 0) threads = 1024;
+  if (threads != 256 && threads != 512 && threads != 1024)
+    return fail(QL_E_INVALID, "threads=%d must be 256, 512 or 1024", threads);
+  if (loads_in_flight == 0) loads_in_flight = 4;
+  if (loads_in_flight != 2 && loads_in_flight != 4)
+    return fail(QL_E_INVALID, "loads_in_flight=%d must be 2 or 4", loads_in_flight);
+  if (!src || !sink || (bcast_bytes && !bcast)) return fail(QL_E_INVALID, "NULL pointer");
+  if (!aligned16(src) || !aligned16(sink) || (bcast && !aligned16(bcast)))
+    return fail(QL_E_ALIGN, "pointers must be 16-byte aligned");
+  hipError_t e = qlk::launch_stream_read_bcast(src, (uint64_t)bytes, bcast, (uint64_t)bcast_bytes, workgroups,
+                                               threads, loads_in_flight, check != 0, static_cast<uint32_t*>(sink),
+                                               static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? QL_OK : hip_fail(e, "broadcast read launch");
+}
+
 int64_t qlinear_packed_weight_bytes(int64_t N, int64_t K) {
   if (N < 0 || K < 0) return 0;
   return ((N + 15) / 16) * ((K + 127) / 128) * 2048;

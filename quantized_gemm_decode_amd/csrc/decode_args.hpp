@@ -129,6 +129,11 @@ hipError_t launch_fill_zero_bf16(void* y, int64_t count, hipStream_t st);
 // (4 or 8) loads in flight per lane; `check`: one 32-bit word sum per workgroup into sink
 hipError_t launch_stream_read(const void* src, uint64_t bytes, int workgroups, int unroll, bool check,
                               uint32_t* sink, hipStream_t s);
+// the same slices of `src` plus, interleaved, all of `bcast` in every workgroup; `threads` 256, 512
+// or 1024, `unroll` (2 or 4) loads of each stream in flight per lane
+hipError_t launch_stream_read_bcast(const void* src, uint64_t bytes, const void* bcast, uint64_t bcast_bytes,
+                                    int workgroups, int threads, int unroll, bool check, uint32_t* sink,
+                                    hipStream_t s);
 // MXFP8 rows: x bf16 [R, C] (C % 32 == 0) -> E4M3 codes (row-major [R, C],
 // or packed tiles when `packed`) and E8M0 scale bytes [R, C/32].
 hipError_t launch_quant_mx(const void* x, int64_t R, int64_t C, void* q, uint8_t* s, bool packed,

@@ -98,10 +98,11 @@ def amax_mode_ok(fmt, M, K):
 
 def decode_m64_candidates(M, N, K, layout):
     """Weight-streaming configurations with four token tiles (32 < M <= 64,
-    packed weights, activations from L2)."""
+    packed weights; packed activations read per K block or staged in LDS for
+    layout 2, row-major ones for layout 1)."""
     seen = set()
     for (wn, wk), rows, split, amode in itertools.product(((4, 1), (2, 2), (1, 4), (2, 4), (1, 8)), (16, 32, 64),
-                                                         SPLITS, (2, 0) if layout == 2 else (0,)):
+                                                         SPLITS, (2, 3) if layout == 2 else (0,)):
         key = (wn, wk, rows, _effective_chunks(K, split), amode)
         if key in seen:
             continue

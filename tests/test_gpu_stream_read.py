@@ -47,3 +47,41 @@ def test_stream_read_arguments_are_checked():
         ql.qlinear_stream_read(src, 64, 32, sink)         # sink too small for the grid
     with pytest.raises(ql.QLinearError):
         ql.qlinear_stream_read(src, 64, 4, sink, loads_in_flight=3)
+
+
+@pytest.mark.parametrize("nbytes,bbytes", [(0, 0), (16, 0), (0, 4096), (1040, 48), (16 * ((1 << 20) + 3), 131072),
+                                           (50 << 20, 393216)])
+@pytest.mark.parametrize("workgroups", [1, 3, 256])
+@pytest.mark.parametrize("threads,lif", [(256, 2), (512, 4), (1024, 2), (1024, 4)])
+def test_stream_read_bcast_reads_its_slice_and_the_whole_block(nbytes, bbytes, workgroups, threads, lif):
+    """Workgroup w's checking sum is that of its slice of src (the slices of
+    qlinear_stream_read) plus that of every word of the broadcast block."""
+    g = torch.Generator().manual_seed(nbytes % 9973 + bbytes + workgroups)
+    host = torch.randint(0, 256, (nbytes + 64,), dtype=torch.uint8, generator=g)
+    bhost = torch.randint(0, 256, (bbytes + 64,), dtype=torch.uint8, generator=g)
+    src, bc = host.cuda(), bhost.cuda()
+    sink = torch.full((workgroups,), 0xDEAD, dtype=torch.int32, device="cuda")
+    ql.qlinear_stream_read_bcast(src, nbytes, bc, bbytes, sink, workgroups=workgroups, threads=threads,
+                                 loads_in_flight=lif, check=True)
+    torch.cuda.synchronize()
+    got = sink.cpu().numpy().view(np.uint32).astype(np.uint64)
+    words = host[:nbytes].numpy().view(np.uint32).astype(np.uint64)
+    bsum = int(bhost[:bbytes].numpy().view(np.uint32).astype(np.uint64).sum())
+    n16 = nbytes // 16
+    per = -(-n16 // workgroups)
+    for w in range(workgroups):
+        lo, hi = min(n16, w * per) * 4, min(n16, (w + 1) * per) * 4
+        assert int(got[w]) == (int(words[lo:hi].sum()) + bsum) & 0xFFFFFFFF, w
+
+
+def test_stream_read_bcast_arguments_are_checked():
+    src = torch.empty(64, dtype=torch.uint8, device="cuda")
+    sink = torch.empty(16, dtype=torch.int32, device="cuda")
+    with pytest.raises(ql.QLinearError):
+        ql.qlinear_stream_read_bcast(src, 64, src, 24, sink, workgroups=4)      # broadcast not a multiple of 16
+    with pytest.raises(ql.QLinearError):
+        ql.qlinear_stream_read_bcast(src, 64, src, 32, sink, workgroups=4, threads=128)
+    with pytest.raises(ql.QLinearError):
+        ql.qlinear_stream_read_bcast(src, 64, src, 32, sink, workgroups=4, loads_in_flight=8)
+    with pytest.raises(ValueError):
+        ql.qlinear_stream_read_bcast(src, 64, src, 128, sink, workgroups=4)     # beyond the broadcast source

@@ -84,8 +84,13 @@ def test_tiled_candidates_cover_the_tiles_and_rings():
 
 @pytest.mark.parametrize("M", [33, 64])
 def test_decode_candidates_up_to_64_tokens(M):
+    # the candidates read the activations in the layout the timer hands them:
+    # packed (read per K block or staged in LDS) for layout 2, row-major for layout 1
     cands = list(sweep.decode_m64_candidates(M, 4096, 4096, 2))
-    assert cands and all(c["w_layout"] == 1 and c["a_mode"] in (0, 2) for c in cands)
+    assert cands and all(c["w_layout"] == 1 and c["a_mode"] in (2, 3) for c in cands)
+    assert {c["a_mode"] for c in cands} == {2, 3}
+    cands = list(sweep.decode_m64_candidates(M, 4096, 4096, 1))
+    assert cands and all(c["w_layout"] == 1 and c["a_mode"] == 0 for c in cands)
 
 
 def test_merge_replaces_entries_of_the_same_key(tmp_path):
