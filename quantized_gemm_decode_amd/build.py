@@ -27,6 +27,8 @@ HIPCC_FLAGS = [
     # IEEE division and fp32 subnormals are part of the quantizer's contract
     "-fhip-fp32-correctly-rounded-divide-sqrt", "-fno-gpu-flush-denormals-to-zero",
     "-fno-fast-math",
+    # the decode kernel's first 9 arguments (14 words) are preloaded into SGPRs at wave launch
+    "-mllvm", "-amdgpu-kernarg-preload-count=9",
     "-I" + os.path.join(ROOT, "include"),
     "-Wno-unused-command-line-argument",
 ]

@@ -483,6 +483,10 @@ ql_status build_plan(int32_t fmt, int64_t M, int64_t N, int64_t K, const ql_conf
   p->chunk_kb = p->G > 0 ? (p->G + split - 1) / split : 0;
   p->chunks = p->G > 0 ? (p->G + p->chunk_kb - 1) / p->chunk_kb : 1;
   p->mt = M <= 16 ? 1 : (M <= 32 ? 2 : 4);
+  if (p->chunk_kb >= qlk::kShapeChunkLimit) {
+    delete p;
+    return fail(QL_E_UNSUPPORTED, "a decode K chunk holds fewer than 2^18 blocks of 128 (raise split_k)");
+  }
   // Block_FP8 fused quantization reads only its K chunk: M * chunk values
   if ((cfg.a_mode == 4 && fmt == QL_BLOCK_FP8 || cfg.a_mode == 5) && (M > 16 || M * p->chunk_kb * 128 > kFusedMaxValues)) {
     const long long chunk = (long long)p->chunk_kb * 128;

@@ -62,6 +62,14 @@ struct DecodeArgs {
   int tiles_n;         // tiled kernel: output tiles along N
 };
 
+// The decode kernel's packed launch word: waves_k (5 bits), split (9 bits),
+// chunk_kb (18 bits); the planner keeps every decode plan inside these
+// ranges (waves_k <= 16, split <= 256, chunk_kb < 2^18).
+constexpr int kShapeChunkLimit = 1 << 18;
+inline int decode_shape_word(const DecodeArgs& a) {
+  return (a.waves_k & 31) | ((a.split & 511) << 5) | (a.chunk_kb << 14);
+}
+
 // Compile-time shape of one decode kernel instantiation.
 struct DecodeKey {
   int fmt;   // FMT_FP8 / FMT_INT8 / FMT_BLOCK

@@ -68,9 +68,35 @@ __device__ __forceinline__ uint32_t epilogue_scaled(float accf, float sa, float 
 // [N/2, N) up) and the output is silu(gate) * up, [M, N/2]: a wave's two
 // 16-row groups are gate rows c.. and the up rows N/2 + c.. of the same
 // output columns, so both values of an output element meet in one lane.
+//
+// Arguments: the operands and sizes the prologue needs come first, as 14
+// words the hardware preloads into SGPRs at wave launch (the library is
+// built with a kernel-argument preload count of 9), so the first weight and
+// scale loads do not wait for a read of the kernel-argument segment; the
+// full argument block follows and supplies what only later code uses.
+// `a_or_x` is X for the fused-quantization modes and A_q otherwise; `shape`
+// packs waves_k (5 bits), split (9 bits) and chunk_kb (18 bits).
 template <int FMT, bool SWAP, int MT, int RG, int NW, int PF, int AL, int WM, bool GLU>
-__global__ void __launch_bounds__(NW * 64) qgemm_decode_kernel(DecodeArgs p) {
+__global__ void __launch_bounds__(NW * 64)
+    qgemm_decode_kernel(const void* a_or_x, const uint8_t* w_in, const float* sa_in, const float* sw_in,
+                        uint32_t* amax_in, int M_in, int N_in, int K_in, int shape, DecodeArgs args) {
   constexpr bool FUSED = AL == 4 || AL == 5;          // activations quantized here from bf16 X
+  DecodeArgs p = args;
+  if constexpr (FUSED)
+    p.x = static_cast<const uint16_t*>(a_or_x);
+  else
+    p.a = static_cast<const uint8_t*>(a_or_x);
+  p.w = w_in;
+  p.sa = sa_in;
+  p.sw = sw_in;
+  p.amax = amax_in;
+  p.M = M_in;
+  p.N = N_in;
+  p.K = K_in;
+  p.G = (K_in + 127) / 128;
+  p.waves_k = shape & 31;
+  p.split = (shape >> 5) & 511;
+  p.chunk_kb = shape >> 14;
   // the workgroup reads only its K chunk of X: Block_FP8 (1 x 128 groups are
   // local) and activation mode 5 (per-token amax given by the producer of X)
   constexpr bool CHUNKED = FUSED && (FMT == FMT_BLOCK || AL == 5);
@@ -1007,7 +1033,9 @@ hipError_t decode_try(const DecodeKey& k, dim3 grid, dim3 block, size_t lds, hip
                                      (int)lds);
         return hipSuccess;
       }
-      fn<<<grid, block, lds, s>>>(a);
+      constexpr bool FUSED = AL == 4 || AL == 5;
+      fn<<<grid, block, lds, s>>>(FUSED ? static_cast<const void*>(a.x) : static_cast<const void*>(a.a), a.w, a.sa,
+                                  a.sw, a.amax, a.M, a.N, a.K, decode_shape_word(a), a);
       return hipGetLastError();
     }
   }
