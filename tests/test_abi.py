@@ -84,6 +84,11 @@ def test_host_validation_status_codes():
     assert _plan_status(ql.FP8_DYNAMIC, 32, 4096, 25600, split_k=1, a_mode=1) == QL_E_UNSUPPORTED
     assert _plan_status(ql.FP8_DYNAMIC, 32, 4096, 25600, split_k=1, a_mode=0) == QL_OK
     assert "LDS" in ql.lib().qlinear_last_error().decode() or True
+    # a decode K chunk must hold fewer than 2^18 blocks of 128 (the kernel's packed launch word)
+    assert _plan_status(ql.FP8_DYNAMIC, 1, 16, 2 ** 25, split_k=1, a_mode=0) == QL_E_UNSUPPORTED
+    assert "2^18" in ql.lib().qlinear_last_error().decode()
+    assert _plan_status(ql.FP8_DYNAMIC, 1, 16, 2 ** 25, split_k=2, a_mode=0) == QL_OK
+    assert _plan_status(ql.FP8_DYNAMIC, 1, 16, 2 ** 25 - 128, split_k=1, a_mode=0) == QL_OK
 
 
 def test_quantizer_rejects_bad_arguments_on_host():
