@@ -155,7 +155,14 @@ typedef struct {
                             needs packed operands, the LDS-DMA ring of 2 stages and a
                             per-token format.  TILED reads swap_ab, split_k,
                             a_mode (0 or 2), w_layout, w_lds, prefetch and the tile; the
-                            other fields are ignored */
+                            other fields are ignored.
+                            DECODE: 0, or the rows of N one workgroup owns -- a multiple of 8
+                            in [8, 120], at most waves_n * rows_per_wave -- so that N can be
+                            spread evenly over the compute units (N = 6144: 256 workgroups of
+                            24 rows instead of 192 of 32); the rows of a workgroup's last row
+                            group beyond its tile are neither loaded nor stored.  FP8_Dynamic
+                            and W8A8_INT8 linears with weights read directly (w_lds 0), not
+                            SiLU-and-mul plans */
 } ql_config;
 
 /* Derived launch facts of a plan (read-only). */

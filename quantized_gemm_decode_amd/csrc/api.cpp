@@ -470,6 +470,16 @@ ql_status build_plan(int32_t fmt, int64_t M, int64_t N, int64_t K, const ql_conf
   if (cfg.w_lds != 0 && cfg.w_lds != 1) return fail(QL_E_INVALID, "w_lds must be 0 or 1");
   if (cfg.w_layout != 0 && cfg.w_layout != 1) return fail(QL_E_INVALID, "w_layout must be 0 or 1");
   if (cfg.w_layout == 1 && cfg.w_lds) return fail(QL_E_INVALID, "w_lds applies to row-major weights only");
+  // tile_n of a decode plan: the rows of N one workgroup owns, 0 = all its waves cover
+  if (cfg.tile_n != 0) {
+    if (cfg.tile_n < 8 || cfg.tile_n % 8 || cfg.tile_n > qlk::kRowTileMax ||
+        cfg.tile_n > cfg.waves_n * cfg.rows_per_wave)
+      return fail(QL_E_INVALID, "a decode row tile (tile_n) is a multiple of 8 in [8, %d] and at most "
+                  "waves_n * rows_per_wave", qlk::kRowTileMax);
+    if (glu || (fmt != QL_FP8_DYNAMIC && fmt != QL_W8A8_INT8) || cfg.w_lds)
+      return fail(QL_E_UNSUPPORTED, "decode row tiles serve FP8_Dynamic / W8A8_INT8 linears with weights read "
+                  "directly (no SiLU-and-mul, no LDS transpose)");
+  }
 
   ql_plan_s* p = new ql_plan_s();
   p->fmt = fmt;
@@ -485,7 +495,7 @@ ql_status build_plan(int32_t fmt, int64_t M, int64_t N, int64_t K, const ql_conf
   p->mt = M <= 16 ? 1 : (M <= 32 ? 2 : 4);
   if (p->chunk_kb >= qlk::kShapeChunkLimit) {
     delete p;
-    return fail(QL_E_UNSUPPORTED, "a decode K chunk holds fewer than 2^18 blocks of 128 (raise split_k)");
+    return fail(QL_E_UNSUPPORTED, "a decode K chunk holds fewer than 2^14 blocks of 128 (raise split_k)");
   }
   // Block_FP8 fused quantization reads only its K chunk: M * chunk values
   if ((cfg.a_mode == 4 && fmt == QL_BLOCK_FP8 || cfg.a_mode == 5) && (M > 16 || M * p->chunk_kb * 128 > kFusedMaxValues)) {
@@ -497,7 +507,7 @@ ql_status build_plan(int32_t fmt, int64_t M, int64_t N, int64_t K, const ql_conf
   const int rg = cfg.rows_per_wave / 16;
   p->glu = glu;
   // GLU: a tile's waves side by side cover 16 output columns each
-  p->bn = glu ? cfg.waves_n * 16 : cfg.waves_n * rg * 16;
+  p->bn = glu ? cfg.waves_n * 16 : (cfg.tile_n ? cfg.tile_n : cfg.waves_n * rg * 16);
   p->n_tiles = (int)(((glu ? N / 2 : N) + p->bn - 1) / p->bn);
   const int64_t lds_a = (cfg.a_mode == 1 || cfg.a_mode == 3) ? (int64_t)p->chunk_kb * p->mt * 2048
                        : cfg.a_mode >= 4 ? 512 + M * ((int64_t)p->chunk_kb * 128 + 64) +
@@ -603,6 +613,7 @@ ql_status launch_gemm(const ql_plan_s* p, const void* a_q, const void* a_scale, 
   a.waves_k = p->cfg.waves_k;
   a.n_tiles = p->n_tiles;
   a.tiles_n = p->tiles_n;
+  a.row_tile = p->tiled ? 0 : p->cfg.tile_n;
   hipError_t e;
   if (p->tiled) {
     const dim3 tgrid((unsigned)(p->n_tiles * p->chunks));

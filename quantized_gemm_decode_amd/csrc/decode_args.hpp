@@ -60,14 +60,19 @@ struct DecodeArgs {
   int waves_k;         // waves of a workgroup that share one K chunk
   int n_tiles;         // output tiles along N (decode) / all output tiles (tiled)
   int tiles_n;         // tiled kernel: output tiles along N
+  int row_tile;        // decode: rows of N a workgroup owns (a multiple of 8, <= 120), 0 = what its waves cover
 };
 
 // The decode kernel's packed launch word: waves_k (5 bits), split (9 bits),
-// chunk_kb (18 bits); the planner keeps every decode plan inside these
-// ranges (waves_k <= 16, split <= 256, chunk_kb < 2^18).
-constexpr int kShapeChunkLimit = 1 << 18;
+// chunk_kb (14 bits), row_tile / 8 (4 bits); the planner keeps every decode
+// plan inside these ranges (waves_k <= 16, split <= 256, chunk_kb < 2^14,
+// row_tile a multiple of 8 up to 120).
+constexpr int kShapeChunkLimit = 1 << 14;
+constexpr int kRowTileMax = 120;
 inline int decode_shape_word(const DecodeArgs& a) {
-  return (a.waves_k & 31) | ((a.split & 511) << 5) | (a.chunk_kb << 14);
+  const unsigned w = (unsigned)(a.waves_k & 31) | ((unsigned)(a.split & 511) << 5) |
+                     ((unsigned)(a.chunk_kb & 16383) << 14) | ((unsigned)((a.row_tile / 8) & 15) << 28);
+  return (int)w;
 }
 
 // Compile-time shape of one decode kernel instantiation.

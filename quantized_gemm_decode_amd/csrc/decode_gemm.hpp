@@ -75,7 +75,8 @@ __device__ __forceinline__ uint32_t epilogue_scaled(float accf, float sa, float 
 // scale loads do not wait for a read of the kernel-argument segment; the
 // full argument block follows and supplies what only later code uses.
 // `a_or_x` is X for the fused-quantization modes and A_q otherwise; `shape`
-// packs waves_k (5 bits), split (9 bits) and chunk_kb (18 bits).
+// packs waves_k (5 bits), split (9 bits), chunk_kb (14 bits) and the row
+// tile in units of 8 rows (4 bits; 0: the workgroup's waves_n * 16 * RG).
 template <int FMT, bool SWAP, int MT, int RG, int NW, int PF, int AL, int WM, bool GLU>
 __global__ void __launch_bounds__(NW * 64)
     qgemm_decode_kernel(const void* a_or_x, const uint8_t* w_in, const float* sa_in, const float* sw_in,
@@ -96,7 +97,13 @@ __global__ void __launch_bounds__(NW * 64)
   p.G = (K_in + 127) / 128;
   p.waves_k = shape & 31;
   p.split = (shape >> 5) & 511;
-  p.chunk_kb = shape >> 14;
+  p.chunk_kb = (shape >> 14) & 16383;
+  // Row tile: a workgroup owns rows [tile * BN, tile * BN + BN) of N.  By
+  // default BN is what its waves cover; a plan may give it fewer, any
+  // multiple of 8 (for example 24 rows, so that N = 6144 spreads over 256
+  // compute units instead of 192 workgroups of 32 rows), and the rows of its
+  // last row group beyond the tile are neither loaded nor stored.
+  const int row_tile = (int)(((uint32_t)shape >> 28) * 8u);
   // the workgroup reads only its K chunk of X: Block_FP8 (1 x 128 groups are
   // local) and activation mode 5 (per-token amax given by the producer of X)
   constexpr bool CHUNKED = FUSED && (FMT == FMT_BLOCK || AL == 5);
@@ -130,7 +137,7 @@ __global__ void __launch_bounds__(NW * 64)
   const int WK = p.waves_k;
   const int wn = wave / WK;
   const int wk = wave - wn * WK;
-  const int BN = (NW / WK) * RG * 16;
+  const int BN = (!GLU && row_tile) ? row_tile : (NW / WK) * RG * 16;
   const int tile = blockIdx.x / p.split;
   const int chunk = blockIdx.x - tile * p.split;
   const int kb0 = chunk * p.chunk_kb;
@@ -141,13 +148,15 @@ __global__ void __launch_bounds__(NW * 64)
   const int row_base = tile * BN + wn * RG * 16;
 
   const uint32_t M = (uint32_t)p.M, N = (uint32_t)p.N, K = (uint32_t)p.K;
+  // rows this workgroup may load and store (GLU plans use obase / IH instead)
+  const uint32_t row_end = min(N, (uint32_t)(tile * BN + BN));
   // GLU: output columns obase.. of this wave; weight rows of its row groups
   const uint32_t IH = N / 2u;
   const int obase = tile * (NW / WK) * 16 + wn * 16;
   auto grow = [&](int rg) -> int { return GLU ? (rg == 0 ? obase : (int)IH + obase) : row_base + rg * 16; };
   // is the element at offset x of row group rg a real output?
   auto rowok = [&](int rg, uint32_t x) -> bool {
-    return GLU ? (uint32_t)obase + x < IH : (uint32_t)grow(rg) + x < N;
+    return GLU ? (uint32_t)obase + x < IH : (uint32_t)grow(rg) + x < row_end;
   };
   const uint32_t NT16 = (N + 15u) / 16u;  // 16-row groups (tiles along N of the packed layout)
   const __amdgpu_buffer_rsrc_t rw = make_rsrc(p.w, WP ? NT16 * (uint32_t)p.G * WTILE : N * K);
@@ -162,7 +171,7 @@ __global__ void __launch_bounds__(NW * 64)
 #pragma unroll
   for (int rg = 0; rg < RG; ++rg) {
     const uint32_t row = (uint32_t)(grow(rg) + r16);
-    wbase[rg] = row < N ? row * K + glo : OOB;
+    wbase[rg] = row < row_end ? row * K + glo : OOB;
   }
   // WL (coalesced weight stream): the two loads of a (row group, K block)
   // each cover 8 whole rows x 128 bytes -- lane l takes row 8*i + l/8 and
@@ -175,17 +184,27 @@ __global__ void __launch_bounds__(NW * 64)
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const uint32_t row = (uint32_t)(grow(rg) + 8 * i + (lane >> 3));
-      wbase_c[rg][i] = row < N ? row * K + c16 : OOB;
+      wbase_c[rg][i] = row < row_end ? row * K + c16 : OOB;
     }
   // WP (packed tiles): tile (t, kb) is 2 KB at (t*G + kb)*2048 holding exactly
   // the two 16-byte pieces every lane feeds the matrix core, lane l's `lo` at
   // l*16 and `hi` at 1024 + l*16; padding rows / K are zeros in the tile.
-  // MXFP4: 1 KB tiles, one 16-byte piece a lane (32 E2M1 values).
+  // MXFP4: 1 KB tiles, one 16-byte piece a lane (32 E2M1 values).  A row
+  // group that starts inside a tile (a row tile that is not a multiple of
+  // 16) reads each lane's row from the tile that holds it: row r sits in
+  // tile r/16 at the lane slot of row r%16 (for an aligned group, the lane's
+  // own slot).
   uint32_t wbase_p[RG];
 #pragma unroll
   for (int rg = 0; rg < RG; ++rg) {
-    const uint32_t t = (uint32_t)(grow(rg) / 16);
-    wbase_p[rg] = (t < NT16 && rowok(rg, 0)) ? t * (uint32_t)p.G * WTILE + (uint32_t)lane * 16u : OOB;
+    if constexpr (GLU || FMT == FMT_MX4) {
+      const uint32_t t = (uint32_t)(grow(rg) / 16);
+      wbase_p[rg] = (t < NT16 && rowok(rg, 0)) ? t * (uint32_t)p.G * WTILE + (uint32_t)lane * 16u : OOB;
+    } else {
+      const uint32_t row = (uint32_t)(grow(rg) + r16);
+      wbase_p[rg] = row < row_end ? (row / 16u) * (uint32_t)p.G * WTILE + ((row & 15u) + 16u * (uint32_t)g) * 16u
+                                  : OOB;
+    }
   }
   // LDS slots of the transpose: 2 per wave, each RG x 2 KB, after the
   // staged activations.
@@ -906,7 +925,7 @@ __global__ void __launch_bounds__(NW * 64)
       for (int r = 0; r < 4; ++r) {
         nn[r] = (uint32_t)grow(rg) + (SWAP ? (uint32_t)(4 * g + r) : (uint32_t)r16);
         mm[r] = SWAP ? (uint32_t)(mt * 16 + r16) : (uint32_t)(mt * 16 + 4 * g + r);
-        const bool ok = mm[r] < M && nn[r] < N;
+        const bool ok = mm[r] < M && nn[r] < row_end;
         if constexpr (FMT == FMT_BLOCK || MXS) {
           out[r] = bf16_rne(acc[rg][mt][r]);
           if (ok && p.acc_out)
@@ -928,13 +947,13 @@ __global__ void __launch_bounds__(NW * 64)
           }
         }
       }
-      if (vec4 && mm[0] < M && nn[3] < N) {
+      if (vec4 && mm[0] < M && nn[3] < row_end) {
         u32x2 v = {out[0] | (out[1] << 16), out[2] | (out[3] << 16)};
         *reinterpret_cast<u32x2*>(p.y + (size_t)mm[0] * N + nn[0]) = v;
       } else {
 #pragma unroll
         for (int r = 0; r < 4; ++r)
-          if (mm[r] < M && nn[r] < N) p.y[(size_t)mm[r] * N + nn[r]] = (uint16_t)out[r];
+          if (mm[r] < M && nn[r] < row_end) p.y[(size_t)mm[r] * N + nn[r]] = (uint16_t)out[r];
       }
     }
   }

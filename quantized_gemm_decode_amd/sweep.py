@@ -111,7 +111,43 @@ def decode_m64_candidates(M, N, K, layout):
                    w_lds=0, w_layout=1)
 
 
+def row_tiles(fmt, N, layout):
+    """Decode row tiles (tile_n) that spread N over the 256 compute units
+    more evenly than the waves' 16-row groups do: the smallest multiple of 8
+    rows that gives at most 256 workgroups, and the next one (FP8_Dynamic /
+    W8A8_INT8 linears; 16, 32 and 64 are what plain plans already cover)."""
+    if fmt not in (ql.FP8_DYNAMIC, ql.W8A8_INT8) or layout == 4:
+        return []
+    rt = -(-(-(-N // 256)) // 8) * 8
+    if rt in (16, 32, 64) and N % (256 * rt) == 0:
+        return []                         # plain plans already give every compute unit the same rows
+    return [r for r in (rt, rt + 8) if r not in (16, 32, 64) and r <= 120]
+
+
+def row_tile_candidates(fmt, M, N, K, layout):
+    """Decode configurations with a row tile: waves whose row groups cover
+    the tile with less than 32 rows to spare, in the activation modes of the
+    layout (phase 1 form: swap_ab 1, 2-block batches)."""
+    amodes = {0: (0,), 1: (1, 0), 2: (3, 2), 3: (4,), 5: (5,)}[layout]
+    seen = set()
+    for rt in row_tiles(fmt, N, layout):
+        for (wn, rows), wk, split, amode in itertools.product(((1, 16), (1, 32), (1, 64), (2, 16), (2, 32), (4, 16)),
+                                                              (1, 2, 4, 8, 16), SPLITS, amodes):
+            if not rt <= wn * rows < rt + 32 or wn * wk not in (4, 8, 16):
+                continue
+            if layout == 0 and (wn * wk != 4 or rows > 32):
+                continue                  # row-major weights: 4-wave workgroups, up to 32 rows a wave
+            key = (rt, wn, wk, rows, _effective_chunks(K, split), amode)
+            if key in seen:
+                continue
+            seen.add(key)
+            yield dict(swap_ab=1, split_k=split, waves_n=wn, waves_k=wk, rows_per_wave=rows, prefetch=2,
+                       a_mode=amode, w_lds=0, w_layout=1 if layout >= 1 else 0, tile_n=rt)
+
+
 def phase1_candidates(fmt, M, N, K, layout=0):
+    if M <= 32:
+        yield from row_tile_candidates(fmt, M, N, K, layout)
     if M > 32:
         yield from tiled_candidates(M, N, K, layout)
         if M <= 64 and layout >= 1:

@@ -84,11 +84,31 @@ def test_host_validation_status_codes():
     assert _plan_status(ql.FP8_DYNAMIC, 32, 4096, 25600, split_k=1, a_mode=1) == QL_E_UNSUPPORTED
     assert _plan_status(ql.FP8_DYNAMIC, 32, 4096, 25600, split_k=1, a_mode=0) == QL_OK
     assert "LDS" in ql.lib().qlinear_last_error().decode() or True
-    # a decode K chunk must hold fewer than 2^18 blocks of 128 (the kernel's packed launch word)
-    assert _plan_status(ql.FP8_DYNAMIC, 1, 16, 2 ** 25, split_k=1, a_mode=0) == QL_E_UNSUPPORTED
-    assert "2^18" in ql.lib().qlinear_last_error().decode()
-    assert _plan_status(ql.FP8_DYNAMIC, 1, 16, 2 ** 25, split_k=2, a_mode=0) == QL_OK
-    assert _plan_status(ql.FP8_DYNAMIC, 1, 16, 2 ** 25 - 128, split_k=1, a_mode=0) == QL_OK
+    # a decode K chunk must hold fewer than 2^14 blocks of 128 (the kernel's packed launch word)
+    assert _plan_status(ql.FP8_DYNAMIC, 1, 16, 2 ** 21, split_k=1, a_mode=0) == QL_E_UNSUPPORTED
+    assert "2^14" in ql.lib().qlinear_last_error().decode()
+    assert _plan_status(ql.FP8_DYNAMIC, 1, 16, 2 ** 21, split_k=2, a_mode=0) == QL_OK
+    assert _plan_status(ql.FP8_DYNAMIC, 1, 16, 2 ** 21 - 128, split_k=1, a_mode=0) == QL_OK
+
+
+def test_decode_row_tile_validation():
+    """tile_n of a decode plan: a multiple of 8 in [8, 120] within the waves' rows, FP8_Dynamic /
+    W8A8_INT8 with weights read directly; the workgroup count follows the tile."""
+    packed = dict(waves_n=1, waves_k=4, rows_per_wave=32, w_layout=1, a_mode=2)
+    assert _plan_status(ql.FP8_DYNAMIC, 8, 6144, 4096, tile_n=24, **packed) == QL_OK
+    assert _plan_status(ql.W8A8_INT8, 8, 6144, 4096, tile_n=8, **packed) == QL_OK
+    assert _plan_status(ql.FP8_DYNAMIC, 8, 6144, 4096, tile_n=12, **packed) == QL_E_INVALID    # not a multiple of 8
+    assert _plan_status(ql.FP8_DYNAMIC, 8, 6144, 4096, tile_n=40, **packed) == QL_E_INVALID    # beyond 32 rows
+    assert _plan_status(ql.FP8_DYNAMIC, 8, 6144, 4096, tile_n=128, waves_n=4, waves_k=1, rows_per_wave=32,
+                        w_layout=1, a_mode=2) == QL_E_INVALID                                  # beyond 120
+    assert _plan_status(ql.BLOCK_FP8, 8, 6144, 4096, tile_n=24, **packed) == QL_E_UNSUPPORTED
+    assert _plan_status(ql.MXFP8, 8, 6144, 4096, tile_n=24, **packed) == QL_E_UNSUPPORTED
+    assert _plan_status(ql.FP8_DYNAMIC, 8, 6144, 4096, tile_n=24, waves_n=1, waves_k=4, rows_per_wave=32,
+                        w_lds=1) == QL_E_UNSUPPORTED                                           # LDS transpose
+    p = ql.qlinear_plan_with_config(ql.FP8_DYNAMIC, 8, 6144, 4096, dict(tile_n=24, **packed))
+    assert p.facts["workgroups"] == 256 and p.config["tile_n"] == 24
+    p = ql.qlinear_plan_with_config(ql.FP8_DYNAMIC, 8, 1000, 4096, dict(tile_n=24, split_k=2, **packed))
+    assert p.facts["workgroups"] == 42 * 2
 
 
 def test_quantizer_rejects_bad_arguments_on_host():

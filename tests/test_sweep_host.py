@@ -64,6 +64,28 @@ def test_decode_candidates_plan_or_are_not_instantiated():
     assert n_ok > 50
 
 
+def test_row_tile_candidates():
+    """Row tiles are offered where N does not split evenly over 256 compute
+    units in 16-row groups, for FP8_Dynamic / W8A8_INT8 only, and every
+    candidate plans or is reported as not instantiated."""
+    assert sweep.row_tiles(ql.FP8_DYNAMIC, 6144, 2) == [24]
+    assert sweep.row_tiles(ql.W8A8_INT8, 10240, 2) == [40, 48]
+    assert sweep.row_tiles(ql.FP8_DYNAMIC, 4096, 2) == [] and sweep.row_tiles(ql.FP8_DYNAMIC, 8192, 2) == []
+    assert sweep.row_tiles(ql.BLOCK_FP8, 6144, 2) == [] and sweep.row_tiles(ql.FP8_DYNAMIC, 6144, 4) == []
+    n_ok = 0
+    for layout in (0, 1, 2, 3, 5):
+        cands = list(sweep.row_tile_candidates(ql.W8A8_INT8, 8, 5120, 8192, layout))
+        assert cands and all(c["tile_n"] == 24 and c["waves_n"] * c["rows_per_wave"] >= 24 for c in cands)
+        for cfg in cands:
+            try:
+                ql.qlinear_plan_with_config(ql.W8A8_INT8, 8, 5120, 8192, cfg)
+                n_ok += 1
+            except ql.QLinearError as e:
+                assert e.status == 2, (cfg, e)
+    assert n_ok > 50
+    assert all(c.get("tile_n", 0) == 0 for c in sweep.phase1_candidates(ql.FP8_DYNAMIC, 8, 4096, 4096, 2))
+
+
 def test_fused_candidates_respect_the_fused_limits():
     assert sweep.fused_ok(ql.FP8_DYNAMIC, 4, 4096) and not sweep.fused_ok(ql.FP8_DYNAMIC, 8, 4096)
     assert not sweep.fused_ok(ql.W8A8_INT8, 1, 4160)                   # K % 512
