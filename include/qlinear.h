@@ -160,9 +160,9 @@ typedef struct {
                             in [8, 120], at most waves_n * rows_per_wave -- so that N can be
                             spread evenly over the compute units (N = 6144: 256 workgroups of
                             24 rows instead of 192 of 32); the rows of a workgroup's last row
-                            group beyond its tile are neither loaded nor stored.  FP8_Dynamic
-                            and W8A8_INT8 linears with weights read directly (w_lds 0), not
-                            SiLU-and-mul plans */
+                            group beyond its tile are neither loaded nor stored.  FP8_Dynamic,
+                            W8A8_INT8 and Block_FP8 linears with weights read directly (w_lds
+                            0), not SiLU-and-mul plans */
 } ql_config;
 
 /* Derived launch facts of a plan (read-only). */

@@ -476,9 +476,9 @@ ql_status build_plan(int32_t fmt, int64_t M, int64_t N, int64_t K, const ql_conf
         cfg.tile_n > cfg.waves_n * cfg.rows_per_wave)
       return fail(QL_E_INVALID, "a decode row tile (tile_n) is a multiple of 8 in [8, %d] and at most "
                   "waves_n * rows_per_wave", qlk::kRowTileMax);
-    if (glu || (fmt != QL_FP8_DYNAMIC && fmt != QL_W8A8_INT8) || cfg.w_lds)
-      return fail(QL_E_UNSUPPORTED, "decode row tiles serve FP8_Dynamic / W8A8_INT8 linears with weights read "
-                  "directly (no SiLU-and-mul, no LDS transpose)");
+    if (glu || is_mx(fmt) || cfg.w_lds)
+      return fail(QL_E_UNSUPPORTED, "decode row tiles serve FP8_Dynamic / W8A8_INT8 / Block_FP8 linears with "
+                  "weights read directly (no SiLU-and-mul, no LDS transpose, no MX)");
   }
 
   ql_plan_s* p = new ql_plan_s();

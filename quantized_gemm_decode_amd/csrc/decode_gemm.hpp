@@ -341,8 +341,12 @@ __global__ void __launch_bounds__(NW * 64)
         }
 #pragma unroll
         for (int rg = 0; rg < RG; ++rg) {
-          const uint32_t row0 = (uint32_t)grow(rg);
-          swb[q][rg] = bload_f32(rsw, (ok && row0 < N) ? ((row0 >> 7) * Gu + (uint32_t)kb) * 4u : OOB);
+          // the 128-row block of this lane's row(s): its one row (standard
+          // orientation) or its four rows 4g..4g+3, which never straddle a
+          // 128-row boundary (groups start at multiples of 8); a row group
+          // of a row tile may straddle one, so the block is taken per lane
+          const uint32_t rs = (uint32_t)grow(rg) + (SWAP ? 4u * (uint32_t)g : (uint32_t)r16);
+          swb[q][rg] = bload_f32(rsw, (ok && rs < N) ? ((rs >> 7) * Gu + (uint32_t)kb) * 4u : OOB);
         }
       }
       if constexpr (MXS) {

@@ -113,15 +113,19 @@ def decode_m64_candidates(M, N, K, layout):
 
 def row_tiles(fmt, N, layout):
     """Decode row tiles (tile_n) that spread N over the 256 compute units
-    more evenly than the waves' 16-row groups do: the smallest multiple of 8
-    rows that gives at most 256 workgroups, and the next one (FP8_Dynamic /
-    W8A8_INT8 linears; 16, 32 and 64 are what plain plans already cover)."""
-    if fmt not in (ql.FP8_DYNAMIC, ql.W8A8_INT8) or layout == 4:
+    more evenly than the waves' 16-row groups do (FP8_Dynamic, W8A8_INT8 and
+    Block_FP8 linears; 16, 32 and 64 rows are what plain plans already
+    cover): the smallest multiple of 8 rows that gives at most 256
+    workgroups and the next one, and every multiple of 8 up to 120 that
+    gives a whole number of workgroups per compute unit.  None where a plain
+    plan already does that."""
+    if fmt not in (ql.FP8_DYNAMIC, ql.W8A8_INT8, ql.BLOCK_FP8) or layout == 4:
         return []
-    rt = -(-(-(-N // 256)) // 8) * 8
-    if rt in (16, 32, 64) and N % (256 * rt) == 0:
+    if any(N % (256 * r) == 0 for r in (16, 32, 64)):
         return []                         # plain plans already give every compute unit the same rows
-    return [r for r in (rt, rt + 8) if r not in (16, 32, 64) and r <= 120]
+    rt = -(-(-(-N // 256)) // 8) * 8
+    even = [r for r in range(24, 121, 8) if (-(-N // r)) % 256 == 0]
+    return sorted({r for r in [rt, rt + 8] + even if r not in (16, 32, 64) and r <= 120})
 
 
 def row_tile_candidates(fmt, M, N, K, layout):

@@ -93,7 +93,7 @@ def test_host_validation_status_codes():
 
 def test_decode_row_tile_validation():
     """tile_n of a decode plan: a multiple of 8 in [8, 120] within the waves' rows, FP8_Dynamic /
-    W8A8_INT8 with weights read directly; the workgroup count follows the tile."""
+    W8A8_INT8 / Block_FP8 with weights read directly; the workgroup count follows the tile."""
     packed = dict(waves_n=1, waves_k=4, rows_per_wave=32, w_layout=1, a_mode=2)
     assert _plan_status(ql.FP8_DYNAMIC, 8, 6144, 4096, tile_n=24, **packed) == QL_OK
     assert _plan_status(ql.W8A8_INT8, 8, 6144, 4096, tile_n=8, **packed) == QL_OK
@@ -101,7 +101,7 @@ def test_decode_row_tile_validation():
     assert _plan_status(ql.FP8_DYNAMIC, 8, 6144, 4096, tile_n=40, **packed) == QL_E_INVALID    # beyond 32 rows
     assert _plan_status(ql.FP8_DYNAMIC, 8, 6144, 4096, tile_n=128, waves_n=4, waves_k=1, rows_per_wave=32,
                         w_layout=1, a_mode=2) == QL_E_INVALID                                  # beyond 120
-    assert _plan_status(ql.BLOCK_FP8, 8, 6144, 4096, tile_n=24, **packed) == QL_E_UNSUPPORTED
+    assert _plan_status(ql.BLOCK_FP8, 8, 6144, 4096, tile_n=24, **packed) == QL_OK
     assert _plan_status(ql.MXFP8, 8, 6144, 4096, tile_n=24, **packed) == QL_E_UNSUPPORTED
     assert _plan_status(ql.FP8_DYNAMIC, 8, 6144, 4096, tile_n=24, waves_n=1, waves_k=4, rows_per_wave=32,
                         w_lds=1) == QL_E_UNSUPPORTED                                           # LDS transpose

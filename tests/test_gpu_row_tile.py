@@ -4,8 +4,10 @@ groups, so its last row group is partly masked and, for a tile that is not a
 multiple of 16, starts inside a packed 16-row weight tile.
 
 Every output is written exactly once (Y starts as NaN), INT8 accumulators and
-outputs are bit-exact, FP8 outputs pass the oracle's acceptance rule; ragged N
-(a partial last tile), ragged K, split-K and every activation mode are covered.
+outputs are bit-exact, FP8_Dynamic and Block_FP8 outputs pass the oracle's
+acceptance rule (Block_FP8: row groups that straddle a 128-row weight-scale
+block); ragged N (a partial last tile), ragged K, split-K and every
+activation mode are covered.
 """
 
 import itertools
@@ -27,10 +29,12 @@ TILES = [(8, 16, 1, 4, 2), (24, 32, 1, 4, 2), (40, 64, 1, 4, 1), (24, 16, 2, 2, 
          (56, 32, 2, 4, 1)]
 # (weight layout, activation mode): row-major W and A; packed W, packed A per block; packed A staged in LDS
 LAYOUTS = [(0, 0), (1, 0), (1, 2), (1, 3)]
-# row-major weights are instantiated for 4-wave workgroups of up to 32 rows a wave only
-CASES = [c for c in itertools.product([ql.FP8_DYNAMIC, ql.W8A8_INT8], [3, 17, 32], range(len(TILES)), [0, 1],
-                                      range(len(LAYOUTS)))
-         if LAYOUTS[c[4]][0] == 1 or (TILES[c[2]][1] <= 32 and TILES[c[2]][2] * TILES[c[2]][3] == 4)]
+# row-major weights are instantiated for 4-wave workgroups of up to 32 rows a wave only, and
+# Block_FP8 with two token tiles for up to 32 rows a wave (its per-block scales take registers)
+CASES = [c for c in itertools.product([ql.FP8_DYNAMIC, ql.W8A8_INT8, ql.BLOCK_FP8], [3, 17, 32], range(len(TILES)),
+                                      [0, 1], range(len(LAYOUTS)))
+         if (LAYOUTS[c[4]][0] == 1 or (TILES[c[2]][1] <= 32 and TILES[c[2]][2] * TILES[c[2]][3] == 4))
+         and not (c[0] == ql.BLOCK_FP8 and c[1] > 16 and TILES[c[2]][1] == 64)]
 
 
 def _ref(fmt, M, N, K, seed):
@@ -44,7 +48,7 @@ def test_row_tile_plans_match_oracle(fmt, M, ti, swap, li):
     w_layout, a_mode = LAYOUTS[li]
     split = [1, 2][(ti + li + M) % 2]
     N = 1000                                              # 1000 % rt != 0 for most tiles: a partial last tile
-    K = 1040 if (ti + swap) % 2 else 1152                 # 1040: ragged last K block
+    K = 1040 if (ti + swap) % 2 and fmt != ql.BLOCK_FP8 else 1152   # 1040: ragged last K block
     cfg = dict(swap_ab=swap, split_k=split, waves_n=wn, waves_k=wk, rows_per_wave=rows, prefetch=pf,
                a_mode=a_mode, w_lds=0, w_layout=w_layout, tile_n=rt)
     plan = ql.qlinear_plan_with_config(fmt, M, N, K, cfg)
@@ -61,7 +65,7 @@ def test_row_tile_plans_match_oracle(fmt, M, ti, swap, li):
         assert int(torch.count_nonzero(ws)) == 0, "split-K workspace not left all-zero"
 
 
-@pytest.mark.parametrize("fmt", [ql.FP8_DYNAMIC, ql.W8A8_INT8])
+@pytest.mark.parametrize("fmt", [ql.FP8_DYNAMIC, ql.W8A8_INT8, ql.BLOCK_FP8])
 @pytest.mark.parametrize("rt,rows,wn,wk", [(24, 32, 1, 4), (40, 64, 1, 8), (8, 16, 1, 8)])
 def test_row_tile_fused_quantization_matches_oracle(fmt, rt, rows, wn, wk):
     """The quantizer fused into the GEMM launch (a_mode 4) with a row tile:

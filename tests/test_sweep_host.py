@@ -71,7 +71,10 @@ def test_row_tile_candidates():
     assert sweep.row_tiles(ql.FP8_DYNAMIC, 6144, 2) == [24]
     assert sweep.row_tiles(ql.W8A8_INT8, 10240, 2) == [40, 48]
     assert sweep.row_tiles(ql.FP8_DYNAMIC, 4096, 2) == [] and sweep.row_tiles(ql.FP8_DYNAMIC, 8192, 2) == []
-    assert sweep.row_tiles(ql.BLOCK_FP8, 6144, 2) == [] and sweep.row_tiles(ql.FP8_DYNAMIC, 6144, 4) == []
+    assert sweep.row_tiles(ql.BLOCK_FP8, 6144, 2) == [24] and sweep.row_tiles(ql.FP8_DYNAMIC, 6144, 4) == []
+    assert sweep.row_tiles(ql.MXFP8, 6144, 2) == []
+    assert sweep.row_tiles(ql.W8A8_INT8, 51200, 2) == [40]          # 1280 workgroups: 5 a compute unit
+    assert sweep.row_tiles(ql.W8A8_INT8, 24576, 2) == []             # 768 x 32 rows: 3 a compute unit
     n_ok = 0
     for layout in (0, 1, 2, 3, 5):
         cands = list(sweep.row_tile_candidates(ql.W8A8_INT8, 8, 5120, 8192, layout))
