@@ -79,3 +79,24 @@ def test_row_tile_fused_quantization_matches_oracle(fmt, rt, rows, wn, wk):
     w_p, w_s = _weights(fmt, r)
     a_p, a_s, y, _ = _forward(plan, fmt, bf16_bits(x), w_p, w_s)
     _check_fused(fmt, r, plan, a_p, a_s, y, str(cfg))
+
+
+@pytest.mark.parametrize("fmt", [ql.FP8_DYNAMIC, ql.W8A8_INT8])
+@pytest.mark.parametrize("rt,rows,wn,wk,split", [(24, 32, 1, 4, 1), (40, 64, 1, 8, 4), (8, 16, 1, 4, 1)])
+def test_row_tile_given_amax_matches_oracle(fmt, rt, rows, wn, wk, split):
+    """A given-amax plan (a_mode 5: each workgroup quantizes its own K chunk
+    with the per-token amax its producer folded) with a row tile: codes,
+    scales and outputs as the oracle's, the amax words cleared, twice in a row."""
+    from tests.test_gpu_chain import _check_consumer, _consume, _given_amax, _weights as _chain_weights
+    M, N, K = 9, 1000, 1152
+    x, _ = make_inputs(K, N, M, 0.02, seed=400 + rt + split, with_weight=False)
+    xb = bf16_bits(x)
+    w_full, w_p, w_s = _chain_weights(fmt, N, K, seed=rt + split)
+    cfg = dict(swap_ab=0, split_k=split, waves_n=wn, waves_k=wk, rows_per_wave=rows, prefetch=1, a_mode=5,
+               w_lds=0, w_layout=1, tile_n=rt)
+    plan = ql.qlinear_plan_with_config(fmt, M, N, K, cfg)
+    for rep in range(2):
+        amax = _given_amax(xb, M, seed=rep)
+        a_q, a_s, y = _consume(fmt, plan, x.cuda(), amax, w_p, w_s)
+        _check_consumer(fmt, plan, xb, w_full, a_q, a_s, y, str(cfg))
+        assert int(torch.count_nonzero(amax)) == 0
